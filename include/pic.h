@@ -1,0 +1,199 @@
+/*
+ * pic.h -- C ABI of the position-independent KV splicing library (libpic.so, gfx950).
+ *
+ * The library runs the link phase of LegoLink / seam-window selective recompute for
+ * one attention layer on one GPU:
+ *
+ *   1. pic_build_index     host planner: chunk offsets, the recompute index (the first
+ *                          min(k, L_c) tokens of every chunk except chunk 0, then every
+ *                          query token) and the launch schedule of the three kernels.
+ *   2. pic_rope_delta      in place, rotates the cached K of every chunk from its local
+ *                          RoPE positions to its global offset with one direct rotation
+ *                          R(delta_c) per row.
+ *   3. pic_splice          copies the fresh K/V of the recomputed rows into the spliced
+ *                          buffers at their global positions.
+ *   4. pic_selective_attn  causal attention of the recomputed rows (global positions)
+ *                          over every spliced key j <= p_r, GQA, flash-style on MFMA.
+ *
+ * Sources (page title and section):
+ *   [EPIC]  "EPIC: Efficient Position-Independent Caching for Serving Large Language
+ *           Models" walkthrough: worked 4+5+5+3 example; link_legolink Steps 1-3.
+ *   [RoPE-C] 10100.com article on RoPE and prefix caching: 2.2 (RoPE rotates pairs of
+ *           neighbouring dimensions by position-proportional angles), 3.3 (scheme C,
+ *           rotary correction by the delta rotation, one direct kernel rather than two
+ *           stacked rotations), footnote 3 (inv_freq = base^(-2i/D)).
+ *   [HYPIC] joto.ai article on HYPIC: 2.2 seam window (k = w = 8 per internal segment).
+ *   [KV-scratch] "KV cache 从零实现：两层 Decoder、位置偏移与正确性验证": offset mask
+ *           allowed[i, j] = [j <= P + i].
+ *
+ * Conventions shared by every call
+ *   - Ownership: the caller owns every buffer, host and device (EPIC's explicit-cache
+ *     API leaves cache lifetime to the user).  The library allocates no memory and
+ *     keeps no state between calls, so calls are reentrant.
+ *   - Streams: device calls are asynchronous on the caller's HIP stream (hipStream_t
+ *     passed as void*, NULL = legacy default stream).  No call synchronises.
+ *   - Errors: every argument check runs before any launch.  On a non-zero status
+ *     nothing was launched and no buffer was touched.  PIC_EDEVICE reports a HIP
+ *     launch error; faults inside kernels surface at the caller's next synchronise.
+ *   - Layouts: token-major.  K/V buffers are [n_tokens, h_kv, head_dim]; request b
+ *     owns rows req_tok_ptr[b] .. req_tok_ptr[b+1]-1; within a request the chunks'
+ *     cached rows come first in chunk order, then q_b query rows.  Fresh K/V are
+ *     [n_rows, h_kv, head_dim], Q and O are [n_rows, h_q, head_dim], all in the order
+ *     of the recompute index (ascending position within each request, requests in
+ *     order).  Elements are dense, innermost dimension contiguous.
+ *   - RoPE: pair i of a head (i < D/2) is (2i, 2i+1) for PIC_ROPE_ADJACENT (the
+ *     [RoPE-C] 2.2 wording) or (i, i + D/2) for PIC_ROPE_HALF (the HF layout of
+ *     footnote 3); theta_i = base^(-2i/D); pair (a, b) at angle phi becomes
+ *     (a cos phi - b sin phi, a sin phi + b cos phi).
+ */
+#ifndef PIC_H
+#define PIC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  PIC_OK = 0,
+  PIC_EINVAL = -1,       /* bad argument (null pointer, negative size, bad shape) */
+  PIC_ENOSPC = -2,       /* caller buffer too small; the needed size is reported */
+  PIC_EUNSUPPORTED = -3, /* valid but not implemented (e.g. head_dim outside the set) */
+  PIC_EDEVICE = -4       /* HIP runtime error at launch */
+};
+
+/* Element types of K, V, Q, O (storage; arithmetic is fp32 on the device). */
+enum { PIC_F32 = 0, PIC_BF16 = 1 };
+
+/* RoPE pair layouts. */
+enum { PIC_ROPE_ADJACENT = 0, PIC_ROPE_HALF = 1 };
+
+/* ------------------------------------------------------------------------------
+ * Plan: one int32 array written by pic_build_index.  A header of
+ * PIC_PLAN_HEADER_WORDS words, then sections at the word offsets the header gives.
+ * ---------------------------------------------------------------------------- */
+#define PIC_PLAN_MAGIC 0x31434950 /* "PIC1" */
+#define PIC_PLAN_HEADER_WORDS 32
+#define PIC_ATTN_TILE_M 64 /* (row, head) pairs per attention tile */
+#define PIC_ROPE_TILE_ROWS 32
+
+enum {
+  PIC_H_MAGIC = 0,
+  PIC_H_WORDS,        /* total words of the plan */
+  PIC_H_N_REQ,        /* requests */
+  PIC_H_N_CHUNKS,     /* chunks over all requests */
+  PIC_H_N_ROWS,       /* recomputed rows over all requests (sum of R_b) */
+  PIC_H_N_TOKENS,     /* spliced tokens over all requests (sum of N_b) */
+  PIC_H_K,            /* recompute count per chunk c >= 1 */
+  PIC_H_POS_BASE,     /* local RoPE position of each chunk's first cached row */
+  PIC_H_H_Q,
+  PIC_H_H_KV,
+  PIC_H_TILE_ROWS,    /* recompute rows per attention tile = PIC_ATTN_TILE_M / (h_q/h_kv) */
+  PIC_H_N_ROPE_TILES,
+  PIC_H_N_ATTN_TILES,
+  PIC_H_N_ATTN_ITEMS,
+  PIC_H_N_MERGE,
+  PIC_H_N_PARTIALS,   /* split-KV partial slots the attention workspace must hold */
+  PIC_H_MAX_TOKENS,   /* largest N_b */
+  PIC_H_O_REQ_CHUNK_PTR, /* [n_req+1] copy of the input CSR */
+  PIC_H_O_CHUNK_OFF,  /* [n_chunks+n_req] per request b: off_0..off_{n_b} (last = ctx_b) */
+  PIC_H_O_REQ_TOK_PTR,/* [n_req+1] first K/V row of each request; last = n_tokens */
+  PIC_H_O_REQ_ROW_PTR,/* [n_req+1] first recomputed row of each request; last = n_rows */
+  PIC_H_O_ROWS,       /* [n_rows] request-local global position p_r of each recomputed row */
+  PIC_H_O_ROW_TOK,    /* [n_rows] K/V buffer row of each recomputed row (req_tok_ptr[b] + p_r) */
+  PIC_H_O_ROPE_TILES, /* [n_rope_tiles][4]: first K row, row count, delta, chunk index */
+  PIC_H_O_ATTN_TILES, /* [n_attn_tiles][8]: req, first row, row count, req_tok_ptr[req],
+                         p_first, p_last, 0, 0 */
+  PIC_H_O_ATTN_ITEMS, /* [n_attn_items][8]: tile, kv head, key_begin, key_end,
+                         partial slot (-1: writes O directly), 0, 0, 0 */
+  PIC_H_O_MERGE,      /* [n_merge][4]: tile, kv head, first slot, slot count */
+  PIC_H_RESERVED0,
+  PIC_H_RESERVED1,
+  PIC_H_RESERVED2,
+  PIC_H_RESERVED3,
+  PIC_H_RESERVED4
+};
+
+/*
+ * pic_build_index -- host planner (integer, exact).                 [EPIC] Step 1-2
+ *
+ * Requests b = 0..n_req-1 hold chunks req_chunk_ptr[b] .. req_chunk_ptr[b+1]-1 with
+ * lengths chunk_lens[] (>= 0) and q_lens[b] (>= 0) query tokens.  off_0 = 0,
+ * off_{c+1} = off_c + L_c, ctx = off_n, N_b = ctx + q_b.  The recompute index of a
+ * request lists, for c = 1..n_b-1 and j < min(k, L_c), position off_c + j, then
+ * positions ctx .. N_b-1 (k >= 0; k = 0 keeps only the query rows).  Chunk 0 is never
+ * recomputed.  pos_base is the local position of the first cached row of every chunk
+ * (0 after a plain compile; delta_c = off_c - pos_base may be negative).
+ * h_q/h_kv fix the GQA group G = h_q / h_kv (must divide PIC_ATTN_TILE_M).  n_cu is
+ * the compute-unit count used to size split-KV (<= 0 selects 256).
+ *
+ * plan: caller-owned int32 host array of plan_cap words, or NULL to query the size.
+ * *plan_words receives the size the plan needs.  Returns PIC_ENOSPC (plan untouched)
+ * when plan_cap is too small, PIC_EINVAL on bad input (negative values, a request
+ * without chunks, h_q % h_kv != 0, totals beyond int32).
+ */
+int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr, const int32_t *chunk_lens,
+                    const int32_t *q_lens, int32_t k, int32_t pos_base, int32_t h_q,
+                    int32_t h_kv, int32_t n_cu, int32_t *plan, int64_t plan_cap,
+                    int64_t *plan_words);
+
+/*
+ * pic_rope_delta -- rotary correction of cached K in place.          [RoPE-C] 3.3
+ *
+ * For every rope tile of the plan (every chunk with delta_c != 0, cached rows that
+ * are not recomputed), each pair of each head of each row is rotated by the angle
+ * delta_c * theta_i: one direct rotation, fp32 arithmetic with a double-float
+ * angle (theta_i from fp64 on the host, exact product, Cody-Waite reduction),
+ * result rounded to the storage type (RNE).  Rows that the splice overwrites are
+ * skipped; V is never touched.
+ *
+ * plan_host / plan_dev: the same plan on the host and on the device.  k: device
+ * buffer [n_tokens, h_kv, head_dim] of dtype.  head_dim even, head_dim % 8 == 0 for
+ * PIC_ROPE_ADJACENT and head_dim % 16 == 0 for PIC_ROPE_HALF, 8 <= head_dim <= 256.
+ */
+int pic_rope_delta(const int32_t *plan_host, const int32_t *plan_dev, void *k, int32_t dtype,
+                   int32_t head_dim, int32_t rope_layout, double rope_base, void *stream);
+
+/*
+ * pic_splice -- overwrite the recomputed rows with their fresh K/V.  [EPIC] Step 3
+ *
+ * For every recomputed row r: k[row_tok[r]] = k_fresh[r], v[row_tok[r]] = v_fresh[r]
+ * (bit copies, all h_kv heads).  k, v: device [n_tokens, h_kv, head_dim];
+ * k_fresh, v_fresh: device [n_rows, h_kv, head_dim]; head_dim % 8 == 0.
+ */
+int pic_splice(const int32_t *plan_host, const int32_t *plan_dev, void *k, void *v,
+               const void *k_fresh, const void *v_fresh, int32_t dtype, int32_t head_dim,
+               void *stream);
+
+/* Bytes of fp32 workspace pic_selective_attn needs for split-KV partials (0 if the
+ * plan has no split tile).  Returns 0 on a bad plan as well; check with the call. */
+size_t pic_attn_workspace_bytes(const int32_t *plan_host, int32_t head_dim);
+
+/*
+ * pic_selective_attn -- causal attention of the recomputed rows.   [EPIC] Step 3
+ *                                                      [KV-scratch] offset mask
+ * For recomputed row r of request b at position p = rows[r] and query head h
+ * (kv head g = h / (h_q/h_kv)):
+ *   O[r, h] = sum_{j <= p} softmax_j(Q[r, h] . K[tok_b + j, g] * scale) V[tok_b + j, g]
+ * over the spliced K/V of request b only.  q: device [n_rows, h_q, head_dim] (already
+ * rotated at p); k, v: spliced device buffers; out: device [n_rows, h_q, head_dim]
+ * of dtype.  scale > 0 (normally 1/sqrt(head_dim)).  bf16 runs bf16 MFMA with fp32
+ * accumulation and an fp32 online softmax; f32 runs fp32 MFMA.  head_dim in {64, 128}
+ * for bf16, {16, 32, 64, 128} for f32.  workspace: device, >= pic_attn_workspace_bytes
+ * (may be NULL when that is 0); contents on entry are ignored.
+ */
+int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_dev, const void *q,
+                       const void *k, const void *v, void *out, int32_t dtype,
+                       int32_t head_dim, float scale, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* Short static description of a status code. */
+const char *pic_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PIC_H */

@@ -1,0 +1,375 @@
+"""Plain CPU oracle for position-independent KV splicing (fp64, NumPy).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import or call anything here.  The
+GPU library never routes through this module, and this module imports nothing from
+the GPU package: the two sides share no code.
+
+Every function is the slow, obvious definition of one step of the link phase of
+LegoLink / seam-window recompute, written from these pages:
+
+* [EPIC] "EPIC: Efficient Position-Independent Caching for Serving Large Language
+  Models" (Chinese walkthrough on juhe.plus): the worked 4+5+5+3 example, the
+  ``link_legolink`` listing (Step 1 recompute positions, Step 2 global positions,
+  Step 3 splice and attention), the method/complexity table and the Step 5 k sweep.
+* [RoPE-C] 10100.com article on why RoPE breaks prefix caching: section 2.2 (RoPE
+  rotates each adjacent dimension pair by an angle proportional to the position),
+  section 3.3 (scheme C, rotary correction by a delta rotation) and footnote 3
+  (HF Llama ``inv_freq``).
+* [HYPIC] joto.ai article on HYPIC: section 2.2 (seam window of w tokens at the
+  head of every internal segment, default w = 8).
+* [KV-scratch] "KV cache 从零实现：两层 Decoder、位置偏移与正确性验证": section on the
+  offset causal mask (allowed[i, j] = [j <= P + i]) and the equivalence-testing
+  method (fp64 re-runs, error injection).
+
+Readings of places where the pages are silent, garbled or disagree:
+
+1. RoPE pairs: [RoPE-C] 2.2 rotates pairs of neighbouring dimensions, so the default
+   layout pairs (2i, 2i+1).  The HF Llama code cited in footnote 3 pairs (i, i+D/2);
+   that layout is offered as ``layout="half"``.  Both rotate pair i by angle p*theta_i.
+2. Frequencies: theta_i = base ** (-2i / D), i = 0 .. D/2-1 ([RoPE-C] footnote 3).
+3. Rotation sign (the formula was lost in extraction): R(phi) = [[cos, -sin], [sin, cos]]
+   acting on (x_a, x_b), so R(a) R(b) = R(a + b) and <R(m) q, R(n) k> depends on n - m
+   only, as [RoPE-C] 2.2 and 3.3 state.
+4. Cached K of a chunk sits at local positions pos_base .. pos_base + L - 1 (pos_base
+   = 0 for plain compile, [EPIC] compile_chunk); the correction angle of chunk c is
+   delta_c = off_c - pos_base.
+5. Fresh Q/K of recomputed rows arrive already rotated at their global positions
+   ([EPIC] Step 3: ``compute_qkv`` is called with the global positions); V never
+   carries RoPE.
+6. Mask: causal including self, j <= p_r ([EPIC] Step 3 listing applies a causal mask;
+   [KV-scratch] offset mask).  The worked example's looser wording (the seven rows
+   see all 17 positions) is read as: all keys that exist, filtered by that mask.
+7. Scale 1/sqrt(D); no bias, soft-cap or dropout.
+8. GQA: query head h reads KV head h // (Hq / Hkv) (contiguous groups).
+9. Every recomputed row produces an output (seam outputs feed the next layer in the
+   per-layer loop); the query rows are the last q of them.
+10. Zero-length chunks are legal and contribute nothing; q = 0 is legal.
+"""
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Step 1 / Step 2 of [EPIC] link_legolink: offsets and recompute positions.
+# ---------------------------------------------------------------------------
+
+
+def chunk_offsets(chunk_lens):
+    """Global start of every chunk, plus the total context length at the end.
+
+    [EPIC] Step 1 walk-through: the running ``offset`` goes 0 -> 4 -> 9 -> 14 for
+    chunks of 4, 5, 5 tokens, and total_ctx_len is the last value.
+    """
+    offs = [0]
+    for length in chunk_lens:
+        offs.append(offs[-1] + int(length))
+    return offs
+
+
+def recompute_positions(chunk_lens, q_len, k):
+    """LegoLink-k recompute set, in ascending order.
+
+    [EPIC] link_legolink Step 1: skip chunk 0; for every later chunk append its
+    first min(k, L_c) global positions; then append every query position
+    ctx .. ctx + q - 1.  [HYPIC] 2.2 uses the same rule with k = w.
+    """
+    offs = chunk_offsets(chunk_lens)
+    rows = []
+    for c, length in enumerate(chunk_lens):
+        if c == 0:
+            continue
+        for j in range(min(int(k), int(length))):
+            rows.append(offs[c] + j)
+    ctx = offs[-1]
+    for j in range(int(q_len)):
+        rows.append(ctx + j)
+    return rows
+
+
+def recompute_set_by_membership(chunk_lens, q_len, k):
+    """Second, independent formulation of the recompute set (used as a pin).
+
+    Position j of the spliced prompt is recomputed iff it is a query position, or
+    it lies in a chunk other than the first and is among that chunk's first k tokens.
+    Scans positions one by one instead of chunks.
+    """
+    total_ctx = sum(int(x) for x in chunk_lens)
+    n_total = total_ctx + int(q_len)
+    out = []
+    for j in range(n_total):
+        if j >= total_ctx:
+            out.append(j)
+            continue
+        # find the chunk holding j by walking from the start
+        start = 0
+        for c, length in enumerate(chunk_lens):
+            if start <= j < start + int(length):
+                if c >= 1 and j - start < int(k):
+                    out.append(j)
+                break
+            start += int(length)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# RoPE definition ([RoPE-C] 2.2 and footnote 3).
+# ---------------------------------------------------------------------------
+
+
+def rope_theta(head_dim, base):
+    """theta_i = base ** (-2 i / D) for i = 0 .. D/2 - 1, in fp64."""
+    assert head_dim % 2 == 0
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(np.float64(base), -2.0 * i / np.float64(head_dim))
+
+
+def rope_pair_index(head_dim, layout="adjacent"):
+    """Dimension indices (a_i, b_i) of pair i.
+
+    "adjacent": (2i, 2i+1) -- the wording of [RoPE-C] 2.2.
+    "half":     (i, i+D/2) -- the HF Llama layout referenced in footnote 3.
+    """
+    half = head_dim // 2
+    i = np.arange(half)
+    if layout == "adjacent":
+        return 2 * i, 2 * i + 1
+    if layout == "half":
+        return i, i + half
+    raise ValueError("unknown layout %r" % (layout,))
+
+
+def rope_rotate(x, positions, base, layout="adjacent"):
+    """Rotate every pair of every row of ``x`` by angle positions[t] * theta_i.
+
+    x: [T, H, D] (any float dtype; computed in fp64).  positions: [T] integers
+    (may be negative: rotating by -p undoes rotating by p).  Returns a new fp64 array.
+    Pair (a, b) maps to (a cos phi - b sin phi, a sin phi + b cos phi).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    t_count, _, head_dim = x.shape
+    theta = rope_theta(head_dim, base)
+    ia, ib = rope_pair_index(head_dim, layout)
+    pos = np.asarray(positions, dtype=np.float64).reshape(t_count, 1)
+    phi = pos * theta[None, :]  # [T, D/2], fp64 angle
+    c = np.cos(phi)[:, None, :]
+    s = np.sin(phi)[:, None, :]
+    a = x[:, :, ia]
+    b = x[:, :, ib]
+    out = np.empty_like(x)
+    out[:, :, ia] = a * c - b * s
+    out[:, :, ib] = a * s + b * c
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Scheme C rotary correction ([RoPE-C] 3.3): cached K moved from local to global.
+# ---------------------------------------------------------------------------
+
+
+def rope_delta(cached_k_chunks, base, layout="adjacent", pos_base=0):
+    """Concatenate the cached K of every chunk, each rotated by R(delta_c).
+
+    cached_k_chunks: list of [L_c, Hkv, D] arrays whose rows carry RoPE at local
+    positions pos_base .. pos_base + L_c - 1.  delta_c = off_c - pos_base, one
+    direct rotation per row (not two stacked ones).  Returns [ctx, Hkv, D] fp64.
+    """
+    lens = [int(np.asarray(a).shape[0]) for a in cached_k_chunks]
+    offs = chunk_offsets(lens)
+    parts = []
+    for c, kc in enumerate(cached_k_chunks):
+        kc = np.asarray(kc, dtype=np.float64)
+        delta = offs[c] - int(pos_base)
+        parts.append(rope_rotate(kc, np.full(kc.shape[0], delta), base, layout))
+    if not parts:
+        raise ValueError("at least one chunk is required")
+    return np.concatenate(parts, axis=0)
+
+
+def concat_chunks(chunks):
+    """Plain concatenation along tokens (V carries no RoPE, [RoPE-C] 3.2/3.3)."""
+    return np.concatenate([np.asarray(a, dtype=np.float64) for a in chunks], axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Step 3 of [EPIC]: splice and selective attention.
+# ---------------------------------------------------------------------------
+
+
+def splice(k_ctx, v_ctx, k_fresh, v_fresh, rows, n_total):
+    """Build the full-length spliced K/V ([EPIC] Step 3: K_exp, V_exp).
+
+    Rows 0..ctx-1 start as the (corrected) cached rows; rows ctx..N-1 do not exist
+    in the cache and are filled only by fresh rows.  Then K_exp[rows] = K_new and
+    V_exp[rows] = V_new.  Rows that no fresh row covers stay NaN so a missing
+    overwrite cannot pass unnoticed.
+    """
+    k_ctx = np.asarray(k_ctx, dtype=np.float64)
+    v_ctx = np.asarray(v_ctx, dtype=np.float64)
+    ctx = k_ctx.shape[0]
+    shape = (n_total,) + k_ctx.shape[1:]
+    kx = np.full(shape, np.nan)
+    vx = np.full(shape, np.nan)
+    kx[:ctx] = k_ctx
+    vx[:ctx] = v_ctx
+    rows = np.asarray(rows, dtype=np.int64)
+    kx[rows] = np.asarray(k_fresh, dtype=np.float64)
+    vx[rows] = np.asarray(v_fresh, dtype=np.float64)
+    return kx, vx
+
+
+def contiguous_runs(rows):
+    """Split an ascending position list into runs of consecutive positions.
+
+    Returns (first_position, first_row_index, length) triples.
+    """
+    runs = []
+    r = 0
+    rows = list(rows)
+    while r < len(rows):
+        s = r
+        while r + 1 < len(rows) and rows[r + 1] == rows[r] + 1:
+            r += 1
+        runs.append((rows[s], s, r - s + 1))
+        r += 1
+    return runs
+
+
+def offset_mask(past_len, new_len):
+    """allowed[i, j] = [j <= P + i] over keys 0 .. P + C - 1 ([KV-scratch] mask)."""
+    qpos = past_len + np.arange(new_len)
+    kpos = np.arange(past_len + new_len)
+    return kpos[None, :] <= qpos[:, None]
+
+
+def _softmax_rows(scores):
+    m = np.max(scores, axis=-1, keepdims=True)
+    e = np.exp(scores - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def selective_attn(q, kx, vx, rows, scale=None):
+    """Causal attention of the recomputed rows over the spliced K/V.
+
+    q: [R, Hq, D] (row r at global position rows[r]); kx, vx: [N, Hkv, D].
+    For each query head h (KV head h // G) and each contiguous run of rows starting
+    at position P: scores = Q K^T * scale over keys 0 .. P+m-1, masked with the
+    offset mask, softmax, times V ([EPIC] Step 3; [KV-scratch] offset mask).
+    Returns O: [R, Hq, D] fp64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kx = np.asarray(kx, dtype=np.float64)
+    vx = np.asarray(vx, dtype=np.float64)
+    n_rows, hq, head_dim = q.shape
+    hkv = kx.shape[1]
+    assert hq % hkv == 0
+    group = hq // hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    out = np.zeros((n_rows, hq, head_dim))
+    for start_pos, first_row, m in contiguous_runs(rows):
+        allowed = offset_mask(start_pos, m)
+        n_keys = start_pos + m
+        for h in range(hq):
+            g = h // group
+            qr = q[first_row:first_row + m, h, :]
+            kk = kx[:n_keys, g, :]
+            vv = vx[:n_keys, g, :]
+            scores = (qr @ kk.T) * scale
+            scores = np.where(allowed, scores, -np.inf)
+            out[first_row:first_row + m, h, :] = _softmax_rows(scores) @ vv
+    return out
+
+
+def full_causal_attn(q_all, k_all, v_all, scale=None):
+    """Brute force: dense causal attention over every position (tiny inputs only).
+
+    q_all: [N, Hq, D]; k_all, v_all: [N, Hkv, D].  Builds the explicit N x N mask
+    j <= i for each head independently of ``selective_attn``.
+    """
+    q_all = np.asarray(q_all, dtype=np.float64)
+    k_all = np.asarray(k_all, dtype=np.float64)
+    v_all = np.asarray(v_all, dtype=np.float64)
+    n_total, hq, head_dim = q_all.shape
+    hkv = k_all.shape[1]
+    group = hq // hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    out = np.zeros_like(q_all)
+    for h in range(hq):
+        g = h // group
+        for i in range(n_total):
+            s = np.array([np.dot(q_all[i, h], k_all[j, g]) * scale for j in range(i + 1)])
+            w = np.exp(s - s.max())
+            w = w / w.sum()
+            acc = np.zeros(head_dim)
+            for j in range(i + 1):
+                acc += w[j] * v_all[j, g]
+            out[i, h] = acc
+    return out
+
+
+def attn_rows_direct(q_rows, kx, vx, positions, heads, scale=None):
+    """Attention output of selected (row, head) pairs, one at a time.
+
+    Used for sampled parity at full size: q_rows[s] is the query vector [D] of
+    sample s at global position positions[s] for query head heads[s]; kx/vx carry
+    all group heads.  Same definition as ``selective_attn``.
+    """
+    kx = np.asarray(kx, dtype=np.float64)
+    vx = np.asarray(vx, dtype=np.float64)
+    head_dim = kx.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    out = []
+    for qv, p, g in zip(q_rows, positions, heads):
+        kk = kx[: int(p) + 1, int(g), :]
+        vv = vx[: int(p) + 1, int(g), :]
+        s = (kk @ np.asarray(qv, dtype=np.float64)) * scale
+        w = np.exp(s - s.max())
+        w = w / w.sum()
+        out.append(w @ vv)
+    return np.stack(out)
+
+
+# ---------------------------------------------------------------------------
+# Composition of one request ([EPIC] link_legolink, one layer).
+# ---------------------------------------------------------------------------
+
+
+def link_request(cached_k_chunks, cached_v_chunks, q_len, k, k_fresh, v_fresh, q_fresh,
+                 base, layout="adjacent", pos_base=0, scale=None):
+    """Run the whole link for one request and one layer.
+
+    Returns dict(rows, offsets, kx, vx, out).  k_fresh/v_fresh/q_fresh are in the
+    order of ``rows`` (ascending positions).
+    """
+    lens = [int(np.asarray(a).shape[0]) for a in cached_k_chunks]
+    offs = chunk_offsets(lens)
+    rows = recompute_positions(lens, q_len, k)
+    n_total = offs[-1] + int(q_len)
+    k_ctx = rope_delta(cached_k_chunks, base, layout, pos_base)
+    v_ctx = concat_chunks(cached_v_chunks)
+    kx, vx = splice(k_ctx, v_ctx, k_fresh, v_fresh, rows, n_total)
+    out = selective_attn(q_fresh, kx, vx, rows, scale)
+    return {"rows": rows, "offsets": offs, "kx": kx, "vx": vx, "out": out}
+
+
+# ---------------------------------------------------------------------------
+# Shared-chunk pool (paged storage): gather one chunk back to contiguous rows.
+# ---------------------------------------------------------------------------
+
+
+def gather_paged_chunk(pool, block_ids, length):
+    """Rows 0..length-1 of a chunk stored in fixed-size pool blocks.
+
+    pool: [n_blocks, block_size, H, D]; block_ids: the chunk's blocks in order.
+    Token t lives in block block_ids[t // block_size], slot t % block_size.
+    """
+    pool = np.asarray(pool)
+    bs = pool.shape[1]
+    rows = [pool[int(block_ids[t // bs]), t % bs] for t in range(int(length))]
+    if not rows:
+        return np.zeros((0,) + pool.shape[2:], dtype=np.float64)
+    return np.stack(rows).astype(np.float64)

@@ -1,0 +1,175 @@
+"""Seeded synthetic workloads for position-independent KV splicing.
+
+This module only draws random numbers and chunk lengths.  It holds none of the
+method's arithmetic (no offsets, recompute sets, rotations or attention), so both
+the GPU path and the CPU oracle can take their inputs from it without sharing any
+of the computation.
+
+The shapes follow the pages' workloads: RAG prompts assembled from independently
+cached documents plus a user query (EPIC walkthrough, worked example and Step 5;
+HYPIC section 2.2: segments usually longer than 512 tokens, seam window w = 8;
+prompts of tens to hundreds of segments reaching ~100k tokens).  No dataset is
+used: values are N(0, 1) draws (optionally scaled) rounded to the I/O dtype with
+round-to-nearest-even.
+
+Recipe (all draws use ``torch.Generator`` on the CPU, Mersenne Twister, seeded):
+  * chunk lengths: ``numpy.random.default_rng(seed)`` integers, inclusive bounds;
+  * tensors: ``torch.randn(float32) * scale`` then ``.to(dtype)`` (RNE for bf16).
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@dataclass
+class Request:
+    chunk_lens: list
+    q_len: int
+    chunk_ids: list = None  # pool chunk id per chunk (paged workloads only)
+
+
+@dataclass
+class Workload:
+    name: str
+    dtype: str
+    h_q: int
+    h_kv: int
+    head_dim: int
+    rope_base: float
+    k: int
+    requests: list
+    value_scale: float = 1.0
+    seed: int = 0
+    # paged shared-chunk pool (None for contiguous workloads)
+    pool_lens: list = None
+    block_size: int = 16
+    pool_block_perm_seed: int = None
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def n_tokens(self):
+        return sum(sum(r.chunk_lens) + r.q_len for r in self.requests)
+
+    @property
+    def torch_dtype(self):
+        return DTYPES[self.dtype]
+
+
+def _lengths_until(rng, lo, hi, target):
+    lens = []
+    while sum(lens) < target:
+        lens.append(int(rng.integers(lo, hi + 1)))
+    return lens
+
+
+def worked_example(seed=1):
+    """4+5+5 token chunks plus a 3-token query, k = 2, fp32, 4 heads of 16 dims."""
+    return Workload("worked_example", "f32", 4, 4, 16, 10000.0, 2,
+                    [Request([4, 5, 5], 3)], seed=seed)
+
+
+def rag_single(seed=2):
+    """One RAG request: 5 chunks of 1024 tokens + 64 query tokens, GQA 32/8, k = 16."""
+    return Workload("rag_single", "bf16", 32, 8, 128, 500000.0, 16,
+                    [Request([1024] * 5, 64)], value_scale=1.0 / np.sqrt(128.0), seed=seed)
+
+
+def long_context(k=16, seed=3):
+    """Batch 1: 32 chunks of 1024 tokens + 128 query tokens (32896 tokens)."""
+    return Workload("long_context", "bf16", 32, 8, 128, 500000.0, k,
+                    [Request([1024] * 32, 128)], seed=seed * 1000 + k)
+
+
+def epic_sweep(k=16, n_req=4, seed=4):
+    """4 independent requests of ~50k tokens; chunk lengths uniform in [512, 2048]."""
+    rng = np.random.default_rng(seed * 1000 + k)
+    reqs = [Request(_lengths_until(rng, 512, 2048, 50000), 256) for _ in range(n_req)]
+    return Workload("epic_sweep", "bf16", 32, 8, 128, 500000.0, k, reqs, seed=seed * 1000 + k)
+
+
+def shared_pool(n_pool=256, n_req=8, m_lo=96, m_hi=128, q_len=128, w=8, seed=5):
+    """Paged shared-chunk pool: 256 chunks (lengths in [512, 1536]) stored once in
+    16-token blocks; 8 requests each splice 96-128 distinct pool chunks in random
+    order plus 128 query tokens; seam window w = 8; GQA 32/4."""
+    rng = np.random.default_rng(seed)
+    pool_lens = [int(x) for x in rng.integers(512, 1537, size=n_pool)]
+    reqs = []
+    for _ in range(n_req):
+        m = int(rng.integers(m_lo, m_hi + 1))
+        ids = [int(x) for x in rng.permutation(n_pool)[:m]]
+        reqs.append(Request([pool_lens[i] for i in ids], q_len, chunk_ids=ids))
+    return Workload("shared_pool", "bf16", 32, 4, 128, 500000.0, w, reqs,
+                    pool_lens=pool_lens, block_size=16, pool_block_perm_seed=seed + 7,
+                    seed=seed)
+
+
+def pool_block_table(wl):
+    """Physical block ids of every pool chunk, in a shuffled physical order.
+
+    Chunk i needs ceil(L_i / block_size) blocks; the physical ids are a seeded
+    permutation of 0 .. n_blocks-1 so a gather is a real gather.  Returns
+    (chunk_block_ptr [n_pool + 1], blocks [n_blocks]) as int32 arrays.
+    """
+    bs = wl.block_size
+    counts = [(L + bs - 1) // bs for L in wl.pool_lens]
+    ptr = np.zeros(len(counts) + 1, dtype=np.int64)
+    ptr[1:] = np.cumsum(counts)
+    n_blocks = int(ptr[-1])
+    perm = np.random.default_rng(wl.pool_block_perm_seed).permutation(n_blocks)
+    return ptr.astype(np.int32), perm.astype(np.int32)
+
+
+def draw(shape, seed, dtype, scale=1.0):
+    """N(0, 1) * scale rounded to ``dtype`` (a torch dtype); CPU tensor."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    x = torch.randn(tuple(int(s) for s in shape), generator=g, dtype=torch.float32)
+    if scale != 1.0:
+        x = x * float(scale)
+    return x.to(dtype)
+
+
+def context_tensors(wl):
+    """Cached K/V buffers for a contiguous workload.
+
+    Returns (k_buf, v_buf), each [n_tokens, Hkv, D] in the workload's dtype.  Request
+    b's rows start where request b-1's end; within a request the chunks' cached rows
+    come first in chunk order (each carrying RoPE at its own local positions, as the
+    compile step leaves it), followed by q rows that only the splice fills.
+    """
+    shape = (wl.n_tokens, wl.h_kv, wl.head_dim)
+    k_buf = draw(shape, wl.seed * 7 + 1, wl.torch_dtype, wl.value_scale)
+    v_buf = draw(shape, wl.seed * 7 + 2, wl.torch_dtype, wl.value_scale)
+    return k_buf, v_buf
+
+
+def fresh_tensors(wl, n_rows):
+    """Fresh Q/K/V of the recomputed rows: Q [n_rows, Hq, D], K/V [n_rows, Hkv, D].
+
+    ``n_rows`` is supplied by the caller (each side derives it from its own index)."""
+    q = draw((n_rows, wl.h_q, wl.head_dim), wl.seed * 7 + 3, wl.torch_dtype, wl.value_scale)
+    kf = draw((n_rows, wl.h_kv, wl.head_dim), wl.seed * 7 + 4, wl.torch_dtype, wl.value_scale)
+    vf = draw((n_rows, wl.h_kv, wl.head_dim), wl.seed * 7 + 5, wl.torch_dtype, wl.value_scale)
+    return q, kf, vf
+
+
+def pool_tensors(wl):
+    """Paged pool K/V: [n_blocks, block_size, Hkv, D] each."""
+    bs = wl.block_size
+    n_blocks = sum((L + bs - 1) // bs for L in wl.pool_lens)
+    shape = (n_blocks, bs, wl.h_kv, wl.head_dim)
+    return (draw(shape, wl.seed * 7 + 1, wl.torch_dtype, wl.value_scale),
+            draw(shape, wl.seed * 7 + 2, wl.torch_dtype, wl.value_scale))
+
+
+CONFIGS = {
+    "worked_example": worked_example,
+    "rag_single": rag_single,
+    "long_context": long_context,
+    "epic_sweep": epic_sweep,
+    "shared_pool": shared_pool,
+}

@@ -1,0 +1,438 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each pin is chosen so a plausible mistake (dropped term, wrong sign or index,
+transposed operand, off-by-one in k, top-left mask, positions restarted at 0)
+fails at least one of them; the "planted" tests at the end plant such mistakes
+into the oracle and check that a pin catches each one.  CPU only.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import pic_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Recompute index
+# ---------------------------------------------------------------------------
+
+
+def test_worked_example_index():
+    g = _golden("worked_example.json")
+    assert O.chunk_offsets(g["chunk_lens"]) == g["offsets"]
+    rows = O.recompute_positions(g["chunk_lens"], g["q_len"], g["k"])
+    assert rows == g["recompute_positions"]
+    assert len(rows) == g["n_recomputed"]
+    assert O.chunk_offsets(g["chunk_lens"])[-1] == g["total_ctx_len"]
+    assert g["total_ctx_len"] + g["q_len"] == g["n_total"]
+    assert O.recompute_set_by_membership(g["chunk_lens"], g["q_len"], g["k"]) == rows
+
+
+def test_k_sweep_counts():
+    g = _golden("k_sweep.json")
+    assert sum(g["chunk_lens"]) + g["q_len"] == g["n_total"]
+    for row in g["rows"]:
+        rows = O.recompute_positions(g["chunk_lens"], g["q_len"], row["k"])
+        assert len(rows) == row["recompute_tokens"]
+        assert round(100.0 * len(rows) / g["n_total"], 1) == row["percent"]
+
+
+def test_method_table_count_formula():
+    # EPIC method table: LegoLink-k recomputes (chunks - 1) * k + q tokens when
+    # every chunk has at least k tokens.
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        k = int(rng.integers(0, 9))
+        n = int(rng.integers(1, 7))
+        lens = [int(x) for x in rng.integers(k, k + 10, size=n)]
+        q = int(rng.integers(0, 6))
+        assert len(O.recompute_positions(lens, q, k)) == (n - 1) * k + q
+
+
+def test_membership_formulation_exhaustive():
+    import itertools
+    for n in range(1, 4):
+        for lens in itertools.product(range(0, 5), repeat=n):
+            for q in range(0, 3):
+                for k in range(0, 6):
+                    a = O.recompute_positions(list(lens), q, k)
+                    b = O.recompute_set_by_membership(list(lens), q, k)
+                    assert a == b, (lens, q, k)
+                    assert a == sorted(set(a))
+
+
+def test_chunk_zero_never_recomputed_and_queries_always():
+    rng = np.random.default_rng(1)
+    for _ in range(100):
+        lens = [int(x) for x in rng.integers(0, 12, size=int(rng.integers(1, 6)))]
+        q = int(rng.integers(0, 5))
+        k = int(rng.integers(0, 20))
+        rows = O.recompute_positions(lens, q, k)
+        ctx = sum(lens)
+        assert all(r >= lens[0] for r in rows)
+        assert [r for r in rows if r >= ctx] == list(range(ctx, ctx + q))
+
+
+# ---------------------------------------------------------------------------
+# RoPE and the delta rotation
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_rope_two_dims_is_complex_multiplication(layout):
+    # D = 2: theta_0 = 1, so RoPE at position p multiplies a + ib by e^{ip}.
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((7, 3, 2))
+    pos = rng.integers(-50, 50, size=7)
+    got = O.rope_rotate(x, pos, 10000.0, layout)
+    z = (x[..., 0] + 1j * x[..., 1]) * np.exp(1j * pos.astype(np.float64))[:, None]
+    assert np.max(np.abs(got[..., 0] - z.real)) < 1e-13
+    assert np.max(np.abs(got[..., 1] - z.imag)) < 1e-13
+
+
+def test_rope_pair_layout_and_frequency_unit_vectors():
+    # D = 4, base B: theta_1 = B^(-1/2).  Unit vector on the first member of pair 1.
+    base, p = 10000.0, 3
+    th1 = 1.0 / math.sqrt(base)
+    x = np.zeros((1, 1, 4))
+    x[0, 0, 2] = 1.0  # adjacent layout: pair 1 is (2, 3)
+    got = O.rope_rotate(x, [p], base, "adjacent")[0, 0]
+    assert np.allclose(got, [0.0, 0.0, math.cos(p * th1), math.sin(p * th1)], atol=1e-15)
+    x = np.zeros((1, 1, 4))
+    x[0, 0, 1] = 1.0  # half layout: pair 1 is (1, 3)
+    got = O.rope_rotate(x, [p], base, "half")[0, 0]
+    assert np.allclose(got, [0.0, math.cos(p * th1), 0.0, math.sin(p * th1)], atol=1e-15)
+    # pair 0 rotates at theta_0 = 1 in both layouts
+    x = np.zeros((1, 1, 4))
+    x[0, 0, 0] = 1.0
+    for layout, idx in (("adjacent", 1), ("half", 2)):
+        got = O.rope_rotate(x, [p], base, layout)[0, 0]
+        want = np.zeros(4)
+        want[0], want[idx] = math.cos(p), math.sin(p)
+        assert np.allclose(got, want, atol=1e-15)
+
+
+def test_rope_theta_matches_footnote_inv_freq():
+    # [RoPE-C] footnote 3 (HF Llama): inv_freq = 1 / base^(arange(0, D, 2) / D)
+    for d, base in ((16, 1e4), (128, 5e5), (64, 1e6)):
+        inv = 1.0 / (base ** (np.arange(0, d, 2, dtype=np.float64) / d))
+        assert np.allclose(O.rope_theta(d, base), inv, rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_rope_additivity_closed_form(layout):
+    # R(delta) RoPE(x, p) = RoPE(x, p + delta): rotating a cached row from p by delta
+    # equals rotating it directly at p + delta ([RoPE-C] 3.3), fp64 to 1e-10.
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((64, 2, 128))
+    p = rng.integers(0, 4096, size=64)
+    delta = rng.integers(-131072, 131072, size=64)
+    a = O.rope_rotate(O.rope_rotate(x, p, 5e5, layout), delta, 5e5, layout)
+    b = O.rope_rotate(x, p + delta, 5e5, layout)
+    assert np.max(np.abs(a - b)) < 1e-10
+    # inverse and identity
+    back = O.rope_rotate(O.rope_rotate(x, p, 5e5, layout), -p, 5e5, layout)
+    assert np.max(np.abs(back - x)) < 1e-10
+    assert np.array_equal(O.rope_rotate(x, np.zeros(64, dtype=np.int64), 5e5, layout), x)
+
+
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_rope_norm_and_relative_position(layout):
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((32, 1, 64))
+    k = rng.standard_normal((32, 1, 64))
+    m = rng.integers(0, 70000, size=32)
+    n = rng.integers(0, 70000, size=32)
+    s = rng.integers(-20000, 20000, size=32)
+    ia, ib = O.rope_pair_index(64, layout)
+    rq = O.rope_rotate(q, m, 5e5, layout)
+    # per-pair norm preserved
+    assert np.allclose(rq[..., ia] ** 2 + rq[..., ib] ** 2, q[..., ia] ** 2 + q[..., ib] ** 2,
+                       rtol=0, atol=1e-12)
+    # <R(m) q, R(n) k> depends on n - m only ([RoPE-C] 2.2)
+    d1 = np.sum(O.rope_rotate(q, m, 5e5, layout) * O.rope_rotate(k, n, 5e5, layout), axis=-1)
+    d2 = np.sum(O.rope_rotate(q, m + s, 5e5, layout) * O.rope_rotate(k, n + s, 5e5, layout), axis=-1)
+    assert np.max(np.abs(d1 - d2)) < 1e-10
+
+
+@pytest.mark.parametrize("pos_base", [0, 4])
+def test_rope_delta_restores_global_rotation(pos_base):
+    # Cached chunk rows = RoPE(K0, pos_base + local t); after the delta rotation they
+    # must equal RoPE(K0, global position) for every chunk, including chunk 0 when
+    # pos_base != 0 (negative delta).
+    rng = np.random.default_rng(5)
+    lens = [5, 0, 7, 3]
+    offs = O.chunk_offsets(lens)
+    k0 = rng.standard_normal((offs[-1], 2, 32))
+    cached = []
+    for c, L in enumerate(lens):
+        cached.append(O.rope_rotate(k0[offs[c]:offs[c] + L], pos_base + np.arange(L), 1e4))
+    got = O.rope_delta(cached, 1e4, pos_base=pos_base)
+    want = O.rope_rotate(k0, np.arange(offs[-1]), 1e4)
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Splice layout and offset mask
+# ---------------------------------------------------------------------------
+
+
+def test_worked_example_splice_layout():
+    g = _golden("worked_example.json")
+    lens, q, k = g["chunk_lens"], g["q_len"], g["k"]
+    rows = O.recompute_positions(lens, q, k)
+    ctx = sum(lens)
+    # tag every cached row with 1000 + position and every fresh row with 2000 + r
+    v_ctx = (1000.0 + np.arange(ctx)).reshape(ctx, 1, 1)
+    v_fresh = (2000.0 + np.arange(len(rows))).reshape(len(rows), 1, 1)
+    _, vx = O.splice(v_ctx, v_ctx, v_fresh, v_fresh, rows, g["n_total"])
+    src = g["spliced_row_source"]
+    for key, positions in src.items():
+        for p in positions:
+            val = vx[p, 0, 0]
+            if key.startswith("cached"):
+                assert val == 1000.0 + p
+            else:
+                assert val == 2000.0 + rows.index(p)
+    assert not np.isnan(vx).any()
+
+
+def test_offset_mask_examples():
+    g = _golden("offset_mask_exercise.json")
+    for ex in g["examples"]:
+        P, C = ex["past_len"], ex["new_len"]
+        m = O.offset_mask(P, C)
+        assert list(m.shape) == ex["score_shape"]
+        assert list(m.sum(axis=1)) == ex["visible_keys"]
+        top_left = np.tril(np.ones((C, P + C), dtype=bool))
+        assert list(top_left.sum(axis=1)) == ex["top_left_visible_keys"]
+        assert (P + np.arange(C)).tolist() == ex["query_positions"]
+
+
+# ---------------------------------------------------------------------------
+# Selective attention
+# ---------------------------------------------------------------------------
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def test_full_recompute_equals_brute_force():
+    # k >= every chunk length: every row after chunk 0 is fresh, so the selected rows
+    # of the causal attention over the whole prompt (independent code) must match.
+    rng = np.random.default_rng(6)
+    lens, q_len, hq, hkv, d = [3, 4, 2], 2, 4, 2, 8
+    n = sum(lens) + q_len
+    q_all, k_all, v_all = _rand(rng, n, hq, d), _rand(rng, n, hkv, d), _rand(rng, n, hkv, d)
+    rows = O.recompute_positions(lens, q_len, 10)
+    cached_k = [k_all[0:3], _rand(rng, 4, hkv, d), _rand(rng, 2, hkv, d)]
+    cached_v = [v_all[0:3], _rand(rng, 4, hkv, d), _rand(rng, 2, hkv, d)]
+    res = O.link_request(cached_k, cached_v, q_len, 10, k_all[rows], v_all[rows], q_all[rows], 1e4)
+    want = O.full_causal_attn(q_all, k_all, v_all)[rows]
+    assert np.max(np.abs(res["out"] - want)) < 1e-10
+
+
+@pytest.mark.parametrize("k", [0, 1, 2, 5])
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_consistency_invariant_any_k(k, layout):
+    # One layer with pre-RoPE K0/Q0: cached K = RoPE(K0, local), fresh = RoPE(., global).
+    # Delta rotation + splice rebuild RoPE(K0, global) exactly, so the selected rows
+    # equal full causal attention for every k.  Pins rope_delta + splice + attention.
+    rng = np.random.default_rng(7 + k)
+    lens, q_len, hq, hkv, d, base = [4, 5, 5], 3, 4, 2, 16, 1e4
+    offs = O.chunk_offsets(lens)
+    n = offs[-1] + q_len
+    q0, k0, v = _rand(rng, n, hq, d), _rand(rng, n, hkv, d), _rand(rng, n, hkv, d)
+    pos = np.arange(n)
+    q_glob = O.rope_rotate(q0, pos, base, layout)
+    k_glob = O.rope_rotate(k0, pos, base, layout)
+    rows = O.recompute_positions(lens, q_len, k)
+    cached_k = [O.rope_rotate(k0[offs[c]:offs[c + 1]], np.arange(lens[c]), base, layout)
+                for c in range(len(lens))]
+    cached_v = [v[offs[c]:offs[c + 1]] for c in range(len(lens))]
+    res = O.link_request(cached_k, cached_v, q_len, k, k_glob[rows], v[rows], q_glob[rows],
+                         base, layout)
+    assert np.max(np.abs(res["kx"] - k_glob)) < 1e-12
+    want = O.full_causal_attn(q_glob, k_glob, v)[rows]
+    assert np.max(np.abs(res["out"] - want)) < 1e-10
+
+
+def test_matches_torch_sdpa_with_explicit_mask():
+    rng = np.random.default_rng(8)
+    lens, q_len, hq, hkv, d = [6, 3, 7], 4, 6, 3, 16
+    n = sum(lens) + q_len
+    rows = O.recompute_positions(lens, q_len, 2)
+    kx, vx = _rand(rng, n, hkv, d), _rand(rng, n, hkv, d)
+    q = _rand(rng, len(rows), hq, d)
+    got = O.selective_attn(q, kx, vx, rows)
+    group = hq // hkv
+    kt = torch.from_numpy(kx).permute(1, 0, 2).repeat_interleave(group, 0)  # [Hq, N, D]
+    vt = torch.from_numpy(vx).permute(1, 0, 2).repeat_interleave(group, 0)
+    qt = torch.from_numpy(q).permute(1, 0, 2)  # [Hq, R, D]
+    mask = torch.arange(n)[None, :] <= torch.tensor(rows)[:, None]  # [R, N]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+    assert np.max(np.abs(ref.permute(1, 0, 2).numpy() - got)) < 1e-12
+
+
+def test_special_cases():
+    rng = np.random.default_rng(9)
+    d = 8
+    # A request whose only chunk is empty and one query token: row 0 sees key 0 only.
+    rows = O.recompute_positions([0], 1, 3)
+    assert rows == [0]
+    kx, vx = _rand(rng, 1, 1, d), _rand(rng, 1, 1, d)
+    out = O.selective_attn(_rand(rng, 1, 2, d), kx, vx, rows)
+    assert np.array_equal(out[0, 0], vx[0, 0]) and np.array_equal(out[0, 1], vx[0, 0])
+    # identical V rows: output is that row whatever the scores
+    lens, q_len = [5, 6], 3
+    n = sum(lens) + q_len
+    rows = O.recompute_positions(lens, q_len, 2)
+    vrow = _rand(rng, 1, 1, d)
+    vx = np.repeat(vrow, n, axis=0)
+    out = O.selective_attn(_rand(rng, len(rows), 1, d) * 5, _rand(rng, n, 1, d), vx, rows)
+    assert np.max(np.abs(out - vrow[0, 0])) < 1e-12
+
+
+def test_causality_probe_and_input_immutability():
+    # [KV-scratch] equivalence checks: changing the last token leaves earlier outputs
+    # unchanged; the inputs are not modified.
+    rng = np.random.default_rng(10)
+    lens, q_len, hq, hkv, d = [4, 4, 4], 3, 2, 1, 8
+    n = sum(lens) + q_len
+    rows = O.recompute_positions(lens, q_len, 2)
+    kx, vx, q = _rand(rng, n, hkv, d), _rand(rng, n, hkv, d), _rand(rng, len(rows), hq, d)
+    copies = [a.copy() for a in (kx, vx, q)]
+    a = O.selective_attn(q, kx, vx, rows)
+    for x, c in zip((kx, vx, q), copies):
+        assert np.array_equal(x, c)
+    kx2, vx2, q2 = kx.copy(), vx.copy(), q.copy()
+    kx2[-1] += 3.0
+    vx2[-1] -= 2.0
+    q2[-1] *= -1.0
+    b = O.selective_attn(q2, kx2, vx2, rows)
+    assert np.array_equal(a[:-1], b[:-1])
+    assert not np.allclose(a[-1], b[-1])
+
+
+def test_paged_gather_roundtrip():
+    rng = np.random.default_rng(11)
+    bs, L, h, d = 4, 10, 2, 8
+    chunk = _rand(rng, L, h, d)
+    n_blocks = 7
+    pool = np.zeros((n_blocks, bs, h, d))
+    blocks = [5, 1, 3]  # physical blocks of this chunk, in order
+    for t in range(L):
+        pool[blocks[t // bs], t % bs] = chunk[t]
+    assert np.array_equal(O.gather_paged_chunk(pool, blocks, L), chunk)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each must make a pin fail by far more than its tolerance
+# ---------------------------------------------------------------------------
+
+
+def _consistency_error(layout="adjacent", k=2):
+    rng = np.random.default_rng(12)
+    lens, q_len, hq, hkv, d, base = [4, 5, 5], 3, 4, 2, 16, 1e4
+    offs = O.chunk_offsets(lens)
+    n = offs[-1] + q_len
+    q0, k0, v = _rand(rng, n, hq, d), _rand(rng, n, hkv, d), _rand(rng, n, hkv, d)
+    pos = np.arange(n)
+    q_glob = O.rope_rotate(q0, pos, base, layout)
+    k_glob = O.rope_rotate(k0, pos, base, layout)
+    rows = O.recompute_positions(lens, q_len, k)
+    cached_k = [O.rope_rotate(k0[offs[c]:offs[c + 1]], np.arange(lens[c]), base, layout)
+                for c in range(len(lens))]
+    cached_v = [v[offs[c]:offs[c + 1]] for c in range(len(lens))]
+    res = O.link_request(cached_k, cached_v, q_len, k, k_glob[rows], v[rows], q_glob[rows],
+                         base, layout)
+    want = O.full_causal_attn(q_glob, k_glob, v)[rows]
+    return float(np.max(np.abs(res["out"] - want)))
+
+
+def test_planted_delta_zero_is_caught(monkeypatch):
+    assert _consistency_error() < 1e-10
+    monkeypatch.setattr(O, "rope_delta", lambda chunks, base, layout="adjacent", pos_base=0:
+                        O.concat_chunks(chunks))
+    assert _consistency_error() > 1e-2
+
+
+def test_planted_top_left_mask_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "offset_mask",
+                        lambda P, C: np.tril(np.ones((C, P + C), dtype=bool)))
+    assert _consistency_error() > 1e-2
+
+
+def test_planted_dropped_scale_is_caught(monkeypatch):
+    real = O.selective_attn
+    monkeypatch.setattr(O, "selective_attn", lambda q, kx, vx, rows, scale=None:
+                        real(q, kx, vx, rows, 1.0))
+    assert _consistency_error() > 1e-2
+
+
+def test_planted_fresh_rows_at_local_positions_is_caught():
+    # Fresh K/Q rotated at positions restarted from 0 (the [KV-scratch] "positions
+    # reset" injection) instead of their global positions.
+    rng = np.random.default_rng(15)
+    lens, q_len, hq, hkv, d, base = [4, 5, 5], 3, 4, 2, 16, 1e4
+    offs = O.chunk_offsets(lens)
+    n = offs[-1] + q_len
+    q0, k0, v = _rand(rng, n, hq, d), _rand(rng, n, hkv, d), _rand(rng, n, hkv, d)
+    k_glob = O.rope_rotate(k0, np.arange(n), base)
+    q_glob = O.rope_rotate(q0, np.arange(n), base)
+    rows = O.recompute_positions(lens, q_len, 2)
+    restart = np.arange(len(rows))
+    cached_k = [O.rope_rotate(k0[offs[c]:offs[c + 1]], np.arange(lens[c]), base)
+                for c in range(len(lens))]
+    cached_v = [v[offs[c]:offs[c + 1]] for c in range(len(lens))]
+    res = O.link_request(cached_k, cached_v, q_len, 2,
+                         O.rope_rotate(k0[rows], restart, base), v[rows],
+                         O.rope_rotate(q0[rows], restart, base), base)
+    want = O.full_causal_attn(q_glob, k_glob, v)[rows]
+    assert np.max(np.abs(res["out"] - want)) > 1e-2
+
+
+def test_planted_wrong_rotation_sign_is_caught(monkeypatch):
+    real = O.rope_rotate
+    monkeypatch.setattr(O, "rope_rotate", lambda x, p, base, layout="adjacent":
+                        real(x, -np.asarray(p), base, layout))
+    x = np.random.default_rng(13).standard_normal((3, 1, 2))
+    pos = np.array([1, 2, 3])
+    z = (x[..., 0] + 1j * x[..., 1]) * np.exp(1j * pos)[:, None]
+    got = O.rope_rotate(x, pos, 1e4)
+    assert np.max(np.abs(got[..., 1] - z.imag)) > 1e-2
+
+
+def test_planted_gqa_map_is_caught(monkeypatch):
+    rng = np.random.default_rng(14)
+    lens, q_len, hq, hkv, d = [3, 4, 2], 2, 4, 2, 8
+    n = sum(lens) + q_len
+    q_all, k_all, v_all = _rand(rng, n, hq, d), _rand(rng, n, hkv, d), _rand(rng, n, hkv, d)
+    rows = O.recompute_positions(lens, q_len, 10)
+    want = O.full_causal_attn(q_all, k_all, v_all)[rows]
+    good = O.selective_attn(q_all[rows], k_all, v_all, rows)
+    assert np.max(np.abs(good - want)) < 1e-10
+    # interleaved head map (h % Hkv) instead of contiguous groups (h // G)
+    k_perm = k_all[:, [0, 1], :]
+    q_perm = q_all[rows][:, [0, 2, 1, 3], :]
+    bad = O.selective_attn(q_perm, k_perm, v_all, rows)[:, [0, 2, 1, 3], :]
+    assert np.max(np.abs(bad - want)) > 1e-2
+
+
+def test_planted_k_off_by_one_is_caught():
+    g = _golden("worked_example.json")
+    assert O.recompute_positions(g["chunk_lens"], g["q_len"], g["k"] + 1) != g["recompute_positions"]
+    assert O.recompute_positions(g["chunk_lens"], g["q_len"], g["k"] - 1) != g["recompute_positions"]
