@@ -1,0 +1,225 @@
+"""Benchmark of the position-independent KV splicing hot path on one MI355X.
+
+One step = one pass of the whole link path over one batch of synthetic requests:
+host planner (recompute index + schedules) and plan upload, rotary correction of the
+cached K, splice of the fresh rows, selective attention (+ split-KV merge).  Inputs
+are resident in HBM before the timed region.  Prints ONE JSON line.
+
+Default workload: 4 independent requests of ~50k tokens each (chunks of 512-2048
+tokens, 256 query tokens), GQA 32/8, head_dim 128, bf16, k = 16.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "spliced context tokens/s + selective-attn TFLOP/s (1 GPU, % of roofline)"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+ATTN_SOURCES = ["position_independent_kv_rope_amd/csrc/pic_attn.hip"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="epic_sweep",
+                    choices=["rag_single", "long_context", "epic_sweep"])
+    ap.add_argument("--k", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=0,
+                    help="recomputed rows of request 0 the oracle times (0 = all)")
+    return ap.parse_args()
+
+
+def make_workload(name, k):
+    from position_independent_kv_rope_amd import workloads as W
+    if name == "rag_single":
+        wl = W.rag_single()
+        wl.k = k
+        return wl
+    if name == "long_context":
+        return W.long_context(k=k)
+    return W.epic_sweep(k=k)
+
+
+def src_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != src_hash(rec.get("sources", ATTN_SOURCES)):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, k_in, v_in, q, kf, vf, plan, sample_rows):
+    """Time the CPU oracle (as it stands) on request 0 of the same inputs."""
+    import torch
+    from threadpoolctl import threadpool_info
+    from oracle import pic_oracle as O
+    r = wl.requests[0]
+    tok0 = int(plan.req_tok_ptr[0])
+    row0, row1 = int(plan.req_row_ptr[0]), int(plan.req_row_ptr[1])
+    offs = O.chunk_offsets(r.chunk_lens)
+    f64 = lambda t: t.to(torch.float64).numpy()
+    kin = f64(k_in[tok0:tok0 + offs[-1]])
+    vin = f64(v_in[tok0:tok0 + offs[-1]])
+    ck = [kin[offs[c]:offs[c + 1]] for c in range(len(r.chunk_lens))]
+    cv = [vin[offs[c]:offs[c + 1]] for c in range(len(r.chunk_lens))]
+    t0 = time.perf_counter()
+    rows = O.recompute_positions(r.chunk_lens, r.q_len, wl.k)
+    k_ctx = O.rope_delta(ck, wl.rope_base)
+    v_ctx = O.concat_chunks(cv)
+    kx, vx = O.splice(k_ctx, v_ctx, f64(kf[row0:row1]), f64(vf[row0:row1]), rows,
+                      offs[-1] + r.q_len)
+    n_att = len(rows) if sample_rows <= 0 else min(sample_rows, len(rows))
+    # the last n_att rows (the longest ones) when sampling
+    sel = slice(len(rows) - n_att, len(rows))
+    O.selective_attn(f64(q[row0:row1])[sel], kx, vx, rows[sel])
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    n_tokens = offs[-1] + r.q_len
+    frac_rows = n_att / max(1, len(rows))
+    return {"value": n_tokens / dt if frac_rows == 1.0 else None, "unit": "tokens/s",
+            "cores": int(threads), "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "request 0 of the batch (%d tokens, %d of %d recomputed rows), fp64 "
+                      "NumPy oracle: index, rotation, splice and selective attention"
+                      % (n_tokens, n_att, len(rows)),
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import position_independent_kv_rope_amd as P
+    from position_independent_kv_rope_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    P.lib()
+    wl = make_workload(args.workload, args.k)
+    reqs = [r.chunk_lens for r in wl.requests]
+    qs = [r.q_len for r in wl.requests]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, n_cu=n_cu)
+    k_in, v_in = W.context_tensors(wl)
+    q_h, kf_h, vf_h = W.fresh_tensors(wl, plan.n_rows)
+    dev = "cuda"
+    k, v = k_in.to(dev), v_in.to(dev)
+    q, kf, vf = q_h.to(dev), kf_h.to(dev), vf_h.to(dev)
+    out = torch.empty_like(q)
+    ws = P.attn_workspace(plan, wl.head_dim)
+    plan_dev = torch.empty(plan.words.size, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    s = wl.torch_dtype.itemsize
+    D, hq, hkv = wl.head_dim, wl.h_q, wl.h_kv
+    rows = plan.rows.astype(np.int64)
+    attn_flops = 4.0 * D * hq * float(np.sum(rows + 1))
+    rope_rows = int(plan.rope_tiles[:, 1].sum()) if plan[P.H_N_ROPE_TILES] else 0
+    rope_bytes = 2.0 * s * hkv * D * rope_rows
+    splice_bytes = 4.0 * s * hkv * D * plan.n_rows
+    attn_bytes = 2.0 * s * hkv * D * plan.n_tokens + 2.0 * s * hq * D * plan.n_rows
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(i=None):
+        p = P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, n_cu=n_cu)
+        plan_dev.copy_(torch.from_numpy(p.words))
+        p.dev = plan_dev
+        e = ev[i] if i is not None else None
+        if e: e[0].record()
+        P.pic_rope_delta(p, k, wl.rope_base)
+        if e: e[1].record()
+        P.pic_splice(p, k, v, kf, vf)
+        if e: e[2].record()
+        P.pic_selective_attn(p, q, k, v, out, workspace=ws)
+        if e: e[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / args.steps
+
+    t_rope = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    t_splice = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    tokens = plan.n_tokens
+    value = tokens / (ms_step * 1e-3)
+    attn_tflops = attn_flops / (t_attn * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    traffic = load_traffic("attn", args.workload + "_k%d" % wl.k)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "requests": len(wl.requests), "tokens": tokens,
+                   "recomputed_rows": plan.n_rows, "k": wl.k, "h_q": hq, "h_kv": hkv,
+                   "head_dim": D, "rope_base": wl.rope_base,
+                   "parallelism": "none (1 GPU)"},
+        "attn_tflops": round(attn_tflops, 2),
+        "splice_pass_tokens_per_s": round(tokens / ((t_rope + t_splice) * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
+                     "traffic": traffic, "kernel": "selective_attn (+merge)",
+                     "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes},
+        "kernels": {
+            "rope_delta": {"ms": round(t_rope, 4), "bytes": rope_bytes,
+                           "GB_s": round(rope_bytes / (t_rope * 1e-3) / 1e9, 1),
+                           "hbm_frac": round(rope_bytes / (t_rope * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "splice": {"ms": round(t_splice, 4), "bytes": splice_bytes,
+                       "GB_s": round(splice_bytes / (t_splice * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(splice_bytes / (t_splice * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "selective_attn": {"ms": round(t_attn, 4), "flops": attn_flops,
+                               "TFLOP_s": round(attn_tflops, 2),
+                               "items": plan[P.H_N_ATTN_ITEMS], "merges": plan[P.H_N_MERGE]},
+            "host_plan_and_upload_ms": round(ms_step - t_rope - t_splice - t_attn, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, k_in, v_in, q_h, kf_h, vf_h, plan,
+                                           args.cpu_sample_rows)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

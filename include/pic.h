@@ -132,8 +132,10 @@ enum {
  *
  * plan: caller-owned int32 host array of plan_cap words, or NULL to query the size.
  * *plan_words receives the size the plan needs.  Returns PIC_ENOSPC (plan untouched)
- * when plan_cap is too small, PIC_EINVAL on bad input (negative values, a request
- * without chunks, h_q % h_kv != 0, totals beyond int32).
+ * when plan_cap is too small, PIC_EINVAL on bad input (null pointers, negative values,
+ * req_chunk_ptr not starting at 0 or decreasing, h_q % h_kv != 0, totals beyond int32)
+ * and PIC_EUNSUPPORTED when G does not divide PIC_ATTN_TILE_M or some |delta_c| > 2^24.
+ * A request may have no chunks (only query rows) or no query tokens.
  */
 int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr, const int32_t *chunk_lens,
                     const int32_t *q_lens, int32_t k, int32_t pos_base, int32_t h_q,

@@ -1,0 +1,255 @@
+"""Position-independent KV splicing on MI355X: thin Python binding of libpic.so.
+
+The functions below carry the names of the C entry points in ``include/pic.h`` and
+only marshal arguments: every step of the path runs in the HIP library.  PyTorch
+supplies device memory and the current stream.  There is no fallback: if libpic.so
+is missing or a call fails, a ``PicError`` is raised.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpic.so")
+
+PIC_OK, PIC_EINVAL, PIC_ENOSPC, PIC_EUNSUPPORTED, PIC_EDEVICE = 0, -1, -2, -3, -4
+PIC_F32, PIC_BF16 = 0, 1
+PIC_ROPE_ADJACENT, PIC_ROPE_HALF = 0, 1
+PIC_PLAN_MAGIC = 0x31434950
+PIC_ATTN_TILE_M = 64
+
+# header word indices (include/pic.h)
+(H_MAGIC, H_WORDS, H_N_REQ, H_N_CHUNKS, H_N_ROWS, H_N_TOKENS, H_K, H_POS_BASE, H_H_Q, H_H_KV,
+ H_TILE_ROWS, H_N_ROPE_TILES, H_N_ATTN_TILES, H_N_ATTN_ITEMS, H_N_MERGE, H_N_PARTIALS,
+ H_MAX_TOKENS, H_O_REQ_CHUNK_PTR, H_O_CHUNK_OFF, H_O_REQ_TOK_PTR, H_O_REQ_ROW_PTR, H_O_ROWS,
+ H_O_ROW_TOK, H_O_ROPE_TILES, H_O_ATTN_TILES, H_O_ATTN_ITEMS, H_O_MERGE) = range(27)
+
+EXPORTED = ("pic_build_index", "pic_rope_delta", "pic_splice", "pic_attn_workspace_bytes",
+            "pic_selective_attn", "pic_strerror")
+
+
+class PicError(RuntimeError):
+    def __init__(self, fn, status):
+        msg = "%s failed: %d (%s)" % (fn, status, strerror(status) if _lib else "?")
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libpic.so (built in-tree by build.py); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libpic.so not found at %s; build it with "
+                           "`python -m position_independent_kv_rope_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, p, f32, f64, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                                 ctypes.c_float, ctypes.c_double, ctypes.c_size_t)
+    L.pic_build_index.argtypes = [i32, p, p, p, i32, i32, i32, i32, i32, p, i64,
+                                  ctypes.POINTER(i64)]
+    L.pic_build_index.restype = ctypes.c_int
+    L.pic_rope_delta.argtypes = [p, p, p, i32, i32, i32, f64, p]
+    L.pic_rope_delta.restype = ctypes.c_int
+    L.pic_splice.argtypes = [p, p, p, p, p, p, i32, i32, p]
+    L.pic_splice.restype = ctypes.c_int
+    L.pic_attn_workspace_bytes.argtypes = [p, i32]
+    L.pic_attn_workspace_bytes.restype = sz
+    L.pic_selective_attn.argtypes = [p, p, p, p, p, p, i32, i32, f32, p, sz, p]
+    L.pic_selective_attn.restype = ctypes.c_int
+    L.pic_strerror.argtypes = [ctypes.c_int]
+    L.pic_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def strerror(status):
+    return lib().pic_strerror(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != PIC_OK:
+        raise PicError(fn, status)
+
+
+def _i32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None and a.size else None
+
+
+class Plan:
+    """Host plan (int32 numpy array) written by pic_build_index, plus section views."""
+
+    def __init__(self, words):
+        self.words = words
+        self.dev = None
+
+    def __getitem__(self, i):
+        return int(self.words[i])
+
+    def _sec(self, off_field, n, width=1):
+        o = self[off_field]
+        return self.words[o:o + n * width].reshape(n, width) if width > 1 else self.words[o:o + n]
+
+    @property
+    def n_rows(self):
+        return self[H_N_ROWS]
+
+    @property
+    def n_tokens(self):
+        return self[H_N_TOKENS]
+
+    @property
+    def rows(self):
+        return self._sec(H_O_ROWS, self[H_N_ROWS])
+
+    @property
+    def row_tok(self):
+        return self._sec(H_O_ROW_TOK, self[H_N_ROWS])
+
+    @property
+    def chunk_off(self):
+        return self._sec(H_O_CHUNK_OFF, self[H_N_CHUNKS] + self[H_N_REQ])
+
+    @property
+    def req_tok_ptr(self):
+        return self._sec(H_O_REQ_TOK_PTR, self[H_N_REQ] + 1)
+
+    @property
+    def req_row_ptr(self):
+        return self._sec(H_O_REQ_ROW_PTR, self[H_N_REQ] + 1)
+
+    @property
+    def rope_tiles(self):
+        return self._sec(H_O_ROPE_TILES, self[H_N_ROPE_TILES], 4)
+
+    @property
+    def attn_tiles(self):
+        return self._sec(H_O_ATTN_TILES, self[H_N_ATTN_TILES], 8)
+
+    @property
+    def attn_items(self):
+        return self._sec(H_O_ATTN_ITEMS, self[H_N_ATTN_ITEMS], 8)
+
+    @property
+    def merges(self):
+        return self._sec(H_O_MERGE, self[H_N_MERGE], 4)
+
+    def to_device(self, device="cuda"):
+        """Upload the plan (one int32 tensor) and keep it with the host copy."""
+        import torch
+        self.dev = torch.from_numpy(self.words).to(device)
+        return self.dev
+
+    def host_ptr(self):
+        return self.words.ctypes.data_as(ctypes.c_void_p)
+
+    def dev_ptr(self):
+        if self.dev is None:
+            raise RuntimeError("plan not uploaded: call Plan.to_device() first")
+        return ctypes.c_void_p(self.dev.data_ptr())
+
+
+def pic_build_index(chunk_lens_per_req, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0):
+    """Run the host planner.  chunk_lens_per_req: list (per request) of chunk-length lists."""
+    n_req = len(chunk_lens_per_req)
+    ptr = np.zeros(n_req + 1, dtype=np.int64)
+    ptr[1:] = np.cumsum([len(c) for c in chunk_lens_per_req])
+    rcp = _i32(ptr)
+    lens = _i32([x for c in chunk_lens_per_req for x in c])
+    ql = _i32(q_lens)
+    words = ctypes.c_int64(0)
+    L = lib()
+    st = L.pic_build_index(n_req, _ptr(rcp), _ptr(lens), _ptr(ql), int(k), int(pos_base),
+                           int(h_q), int(h_kv), int(n_cu), None, 0, ctypes.byref(words))
+    _check("pic_build_index", st)
+    plan = np.zeros(words.value, dtype=np.int32)
+    st = L.pic_build_index(n_req, _ptr(rcp), _ptr(lens), _ptr(ql), int(k), int(pos_base),
+                           int(h_q), int(h_kv), int(n_cu), _ptr(plan), plan.size,
+                           ctypes.byref(words))
+    _check("pic_build_index", st)
+    return Plan(plan)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return PIC_BF16
+    if t.dtype == torch.float32:
+        return PIC_F32
+    raise TypeError("unsupported dtype %s" % (t.dtype,))
+
+
+def _dev(t, name):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous device tensor" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def pic_rope_delta(plan, k, rope_base, layout=PIC_ROPE_ADJACENT, stream=None):
+    """In-place rotary correction of k ([n_tokens, h_kv, D]) on the current stream."""
+    if k.shape[0] != plan.n_tokens or k.shape[1] != plan[H_H_KV]:
+        raise ValueError("k shape %s does not match the plan" % (tuple(k.shape),))
+    st = lib().pic_rope_delta(plan.host_ptr(), plan.dev_ptr(), _dev(k, "k"), _dtype_code(k),
+                              int(k.shape[2]), int(layout), float(rope_base), _stream(stream))
+    _check("pic_rope_delta", st)
+
+
+def pic_splice(plan, k, v, k_fresh, v_fresh, stream=None):
+    """k[row_tok[r]] = k_fresh[r], v[row_tok[r]] = v_fresh[r] for every recomputed row."""
+    for t, n in ((k, plan.n_tokens), (v, plan.n_tokens), (k_fresh, plan.n_rows),
+                 (v_fresh, plan.n_rows)):
+        if t.shape[0] != n or t.dtype != k.dtype or tuple(t.shape[1:]) != tuple(k.shape[1:]):
+            raise ValueError("buffer shapes/dtypes do not match the plan")
+    st = lib().pic_splice(plan.host_ptr(), plan.dev_ptr(), _dev(k, "k"), _dev(v, "v"),
+                          _dev(k_fresh, "k_fresh"), _dev(v_fresh, "v_fresh"), _dtype_code(k),
+                          int(k.shape[2]), _stream(stream))
+    _check("pic_splice", st)
+
+
+def pic_attn_workspace_bytes(plan, head_dim):
+    return int(lib().pic_attn_workspace_bytes(plan.host_ptr(), int(head_dim)))
+
+
+def pic_selective_attn(plan, q, k, v, out, scale=None, workspace=None, stream=None):
+    """out[r, h] = causal attention of q[r, h] over the spliced k/v of its request."""
+    d = int(q.shape[2])
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if q.shape[0] != plan.n_rows or out.shape != q.shape or q.shape[1] != plan[H_H_Q]:
+        raise ValueError("q/out shapes do not match the plan")
+    if k.shape[0] != plan.n_tokens or v.shape != k.shape or k.shape[1] != plan[H_H_KV]:
+        raise ValueError("k/v shapes do not match the plan")
+    for t in (k, v, out):
+        if t.dtype != q.dtype:
+            raise ValueError("q, k, v and out must share one dtype")
+    ws, ws_bytes = None, 0
+    if workspace is not None:
+        ws, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    st = lib().pic_selective_attn(plan.host_ptr(), plan.dev_ptr(), _dev(q, "q"), _dev(k, "k"),
+                                  _dev(v, "v"), _dev(out, "out"), _dtype_code(q), d,
+                                  float(scale), ws, ws_bytes, _stream(stream))
+    _check("pic_selective_attn", st)
+
+
+def attn_workspace(plan, head_dim, device="cuda"):
+    """Allocate the split-KV workspace a plan needs (a float32 device tensor or None)."""
+    import torch
+    n = pic_attn_workspace_bytes(plan, head_dim)
+    if n == 0:
+        return None
+    return torch.empty(n // 4, dtype=torch.float32, device=device)

@@ -1,0 +1,42 @@
+// Internal declarations shared by the host planner and the device entry points of
+// libpic.so.  Nothing here is part of the public ABI (include/pic.h is).
+#pragma once
+
+#include <stdint.h>
+#include <stddef.h>
+
+#include "pic.h"
+
+namespace pic {
+
+// Validated read-only view of a host plan header.
+struct PlanHeader {
+  const int32_t *w = nullptr;
+  int32_t operator[](int i) const { return w[i]; }
+  bool valid() const {
+    return w != nullptr && w[PIC_H_MAGIC] == PIC_PLAN_MAGIC && w[PIC_H_WORDS] >= PIC_PLAN_HEADER_WORDS;
+  }
+};
+
+// Attention tile and item records as stored in the plan (8 int32 words each).
+struct AttnTile {
+  int32_t req, row_begin, n_rows, tok_base, p_first, p_last, pad0, pad1;
+};
+struct AttnItem {
+  int32_t tile, kv_head, key_begin, key_end, slot, pad0, pad1, pad2;
+};
+struct MergeEntry {
+  int32_t tile, kv_head, slot_base, n_slots;
+};
+struct RopeTile {
+  int32_t tok_begin, n_rows, delta, chunk;
+};
+
+static_assert(sizeof(AttnTile) == 32, "plan record size");
+static_assert(sizeof(AttnItem) == 32, "plan record size");
+static_assert(sizeof(MergeEntry) == 16, "plan record size");
+static_assert(sizeof(RopeTile) == 16, "plan record size");
+
+inline size_t dtype_size(int32_t dt) { return dt == PIC_BF16 ? 2 : (dt == PIC_F32 ? 4 : 0); }
+
+}  // namespace pic

@@ -1,0 +1,249 @@
+// Host planner of libpic.so: pic_build_index and pic_strerror.
+//
+// Integer work only.  It produces the recompute index of LegoLink-k (EPIC walkthrough,
+// link_legolink Step 1: skip chunk 0, take the first min(k, L_c) tokens of every later
+// chunk, then every query token; HYPIC section 2.2 applies the same rule with k = w) and
+// the launch schedules of the three device kernels:
+//   * rope tiles: runs of at most PIC_ROPE_TILE_ROWS cached rows of one chunk that keep
+//     their cached K (the recomputed rows are skipped, the splice overwrites them);
+//   * attention tiles: PIC_ATTN_TILE_M (row, head) pairs = PIC_ATTN_TILE_M / G
+//     consecutive recomputed rows of one request times the G query heads of a KV head;
+//   * attention items: (tile, kv head, key range); long tiles are split along keys so
+//     the grid fills the GPU, ordered longest first (the LPT rule HYPIC uses to balance
+//     its segment workers, section 2.3), and each split writes a partial result that a
+//     merge pass combines.
+#include <algorithm>
+#include <cstring>
+#include <numeric>
+#include <vector>
+
+#include "pic_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxI32 = 0x7fffffff;
+constexpr int32_t kKeyAlign = 64;       // attention key block
+constexpr int32_t kMinSplitKeys = 2048;  // smallest key range worth a partial result
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+}  // namespace
+
+extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
+                               const int32_t *chunk_lens, const int32_t *q_lens, int32_t k,
+                               int32_t pos_base, int32_t h_q, int32_t h_kv, int32_t n_cu,
+                               int32_t *plan, int64_t plan_cap, int64_t *plan_words) {
+  using namespace pic;
+  if (plan_words == nullptr || n_req < 0 || k < 0 || h_q <= 0 || h_kv <= 0) return PIC_EINVAL;
+  if (h_q % h_kv != 0) return PIC_EINVAL;
+  const int32_t group = h_q / h_kv;
+  if (group > PIC_ATTN_TILE_M || PIC_ATTN_TILE_M % group != 0) return PIC_EUNSUPPORTED;
+  if (n_req > 0 && (req_chunk_ptr == nullptr || q_lens == nullptr)) return PIC_EINVAL;
+  if (n_req > 0 && req_chunk_ptr[0] != 0) return PIC_EINVAL;
+  for (int32_t b = 0; b < n_req; ++b) {
+    if (req_chunk_ptr[b + 1] < req_chunk_ptr[b] || q_lens[b] < 0) return PIC_EINVAL;
+  }
+  const int32_t n_chunks = n_req > 0 ? req_chunk_ptr[n_req] : 0;
+  if (n_chunks > 0 && chunk_lens == nullptr) return PIC_EINVAL;
+  for (int32_t c = 0; c < n_chunks; ++c)
+    if (chunk_lens[c] < 0) return PIC_EINVAL;
+  if (n_cu <= 0) n_cu = 256;
+
+  // ---- offsets, token and row pointers (64-bit, then range-checked) ----
+  std::vector<int32_t> chunk_off(n_chunks + n_req);
+  std::vector<int32_t> req_tok_ptr(n_req + 1), req_row_ptr(n_req + 1);
+  int64_t tok = 0, nrows = 0, max_tokens = 0;
+  for (int32_t b = 0; b < n_req; ++b) {
+    const int32_t c0 = req_chunk_ptr[b], c1 = req_chunk_ptr[b + 1];
+    int64_t off = 0, r = 0;
+    for (int32_t c = c0; c < c1; ++c) {
+      chunk_off[c + b] = (int32_t)std::min<int64_t>(off, kMaxI32);
+      if (c > c0) r += std::min<int64_t>(k, chunk_lens[c]);
+      off += chunk_lens[c];
+      if (off > kMaxI32) return PIC_EINVAL;
+    }
+    chunk_off[c1 + b] = (int32_t)off;
+    const int64_t n_b = off + q_lens[b];
+    r += q_lens[b];
+    req_tok_ptr[b] = (int32_t)tok;
+    req_row_ptr[b] = (int32_t)nrows;
+    tok += n_b;
+    nrows += r;
+    max_tokens = std::max(max_tokens, n_b);
+    if (tok > kMaxI32 || nrows > kMaxI32) return PIC_EINVAL;
+  }
+  req_tok_ptr[n_req] = (int32_t)tok;
+  req_row_ptr[n_req] = (int32_t)nrows;
+
+  // ---- recompute index: ascending positions per request ----
+  std::vector<int32_t> rows(nrows), row_tok(nrows);
+  {
+    int64_t r = 0;
+    for (int32_t b = 0; b < n_req; ++b) {
+      const int32_t c0 = req_chunk_ptr[b], c1 = req_chunk_ptr[b + 1];
+      for (int32_t c = c0 + 1; c < c1; ++c) {
+        const int32_t off = chunk_off[c + b];
+        const int32_t m = std::min(k, chunk_lens[c]);
+        for (int32_t j = 0; j < m; ++j) rows[r++] = off + j;
+      }
+      const int32_t ctx = chunk_off[c1 + b];
+      for (int32_t j = 0; j < q_lens[b]; ++j) rows[r++] = ctx + j;
+    }
+    for (int32_t b = 0; b < n_req; ++b)
+      for (int32_t i = req_row_ptr[b]; i < req_row_ptr[b + 1]; ++i)
+        row_tok[i] = req_tok_ptr[b] + rows[i];
+  }
+
+  // ---- rope tiles: cached rows that keep their K, per chunk with delta != 0 ----
+  std::vector<RopeTile> rope;
+  for (int32_t b = 0; b < n_req; ++b) {
+    const int32_t c0 = req_chunk_ptr[b], c1 = req_chunk_ptr[b + 1];
+    for (int32_t c = c0; c < c1; ++c) {
+      const int64_t delta = (int64_t)chunk_off[c + b] - pos_base;
+      if (delta == 0) continue;
+      // the device forms delta in fp32 exactly, which holds for |delta| <= 2^24
+      if (delta > (int64_t(1) << 24) || delta < -(int64_t(1) << 24)) return PIC_EUNSUPPORTED;
+      const int32_t skip = (c > c0) ? std::min(k, chunk_lens[c]) : 0;
+      for (int32_t t = skip; t < chunk_lens[c]; t += PIC_ROPE_TILE_ROWS) {
+        RopeTile rt;
+        rt.tok_begin = req_tok_ptr[b] + chunk_off[c + b] + t;
+        rt.n_rows = std::min<int32_t>(PIC_ROPE_TILE_ROWS, chunk_lens[c] - t);
+        rt.delta = (int32_t)delta;
+        rt.chunk = c;
+        rope.push_back(rt);
+      }
+    }
+  }
+
+  // ---- attention tiles ----
+  const int32_t tile_rows = PIC_ATTN_TILE_M / group;
+  std::vector<AttnTile> tiles;
+  for (int32_t b = 0; b < n_req; ++b) {
+    for (int32_t r0 = req_row_ptr[b]; r0 < req_row_ptr[b + 1]; r0 += tile_rows) {
+      AttnTile t{};
+      t.req = b;
+      t.row_begin = r0;
+      t.n_rows = std::min(tile_rows, req_row_ptr[b + 1] - r0);
+      t.tok_base = req_tok_ptr[b];
+      t.p_first = rows[r0];
+      t.p_last = rows[r0 + t.n_rows - 1];
+      tiles.push_back(t);
+    }
+  }
+
+  // ---- split-KV sizing: aim for items no longer than half a fair share per slot ----
+  int64_t total_cost = 0;
+  for (const AttnTile &t : tiles) total_cost += (int64_t)(t.p_last + 1) * h_kv;
+  const int64_t slots = (int64_t)n_cu * 2;
+  int64_t split_len = std::max<int64_t>(kMinSplitKeys, total_cost / std::max<int64_t>(1, slots * 2));
+  split_len = round_up(split_len, kKeyAlign);
+
+  std::vector<AttnItem> items;
+  std::vector<MergeEntry> merges;
+  int64_t n_partials = 0;
+  for (int32_t ti = 0; ti < (int32_t)tiles.size(); ++ti) {
+    const int64_t keys = (int64_t)tiles[ti].p_last + 1;
+    int64_t n_split = (keys + split_len - 1) / split_len;
+    if (n_split < 1) n_split = 1;
+    const int64_t span = round_up((keys + n_split - 1) / n_split, kKeyAlign);
+    n_split = (keys + span - 1) / span;
+    for (int32_t g = 0; g < h_kv; ++g) {
+      const int64_t slot_base = n_partials;
+      for (int64_t s = 0; s < n_split; ++s) {
+        AttnItem it{};
+        it.tile = ti;
+        it.kv_head = g;
+        it.key_begin = (int32_t)(s * span);
+        it.key_end = (int32_t)std::min<int64_t>(keys, (s + 1) * span);
+        it.slot = n_split > 1 ? (int32_t)(slot_base + s) : -1;
+        items.push_back(it);
+      }
+      if (n_split > 1) {
+        merges.push_back(MergeEntry{ti, g, (int32_t)slot_base, (int32_t)n_split});
+        n_partials += n_split;
+      }
+    }
+    if (n_partials > kMaxI32 / 2) return PIC_EINVAL;
+  }
+  // longest first; ties keep (tile, head, split) order so the schedule is deterministic
+  std::stable_sort(items.begin(), items.end(), [](const AttnItem &a, const AttnItem &b) {
+    return (a.key_end - a.key_begin) > (b.key_end - b.key_begin);
+  });
+
+  // ---- layout of the plan ----
+  int64_t words = PIC_PLAN_HEADER_WORDS;
+  auto place = [&words](int64_t n) {
+    const int64_t at = words;
+    words += round_up(n, 4);  // keep 16-byte alignment of every section
+    return at;
+  };
+  const int64_t o_rcp = place(n_req + 1);
+  const int64_t o_coff = place(n_chunks + n_req);
+  const int64_t o_rtp = place(n_req + 1);
+  const int64_t o_rrp = place(n_req + 1);
+  const int64_t o_rows = place(nrows);
+  const int64_t o_rtok = place(nrows);
+  const int64_t o_rope = place((int64_t)rope.size() * 4);
+  const int64_t o_tiles = place((int64_t)tiles.size() * 8);
+  const int64_t o_items = place((int64_t)items.size() * 8);
+  const int64_t o_merge = place((int64_t)merges.size() * 4);
+  if (words > kMaxI32) return PIC_EINVAL;
+  *plan_words = words;
+  if (plan == nullptr) return PIC_OK;
+  if (plan_cap < words) return PIC_ENOSPC;
+
+  std::memset(plan, 0, sizeof(int32_t) * (size_t)words);
+  int32_t *h = plan;
+  h[PIC_H_MAGIC] = PIC_PLAN_MAGIC;
+  h[PIC_H_WORDS] = (int32_t)words;
+  h[PIC_H_N_REQ] = n_req;
+  h[PIC_H_N_CHUNKS] = n_chunks;
+  h[PIC_H_N_ROWS] = (int32_t)nrows;
+  h[PIC_H_N_TOKENS] = (int32_t)tok;
+  h[PIC_H_K] = k;
+  h[PIC_H_POS_BASE] = pos_base;
+  h[PIC_H_H_Q] = h_q;
+  h[PIC_H_H_KV] = h_kv;
+  h[PIC_H_TILE_ROWS] = tile_rows;
+  h[PIC_H_N_ROPE_TILES] = (int32_t)rope.size();
+  h[PIC_H_N_ATTN_TILES] = (int32_t)tiles.size();
+  h[PIC_H_N_ATTN_ITEMS] = (int32_t)items.size();
+  h[PIC_H_N_MERGE] = (int32_t)merges.size();
+  h[PIC_H_N_PARTIALS] = (int32_t)n_partials;
+  h[PIC_H_MAX_TOKENS] = (int32_t)max_tokens;
+  h[PIC_H_O_REQ_CHUNK_PTR] = (int32_t)o_rcp;
+  h[PIC_H_O_CHUNK_OFF] = (int32_t)o_coff;
+  h[PIC_H_O_REQ_TOK_PTR] = (int32_t)o_rtp;
+  h[PIC_H_O_REQ_ROW_PTR] = (int32_t)o_rrp;
+  h[PIC_H_O_ROWS] = (int32_t)o_rows;
+  h[PIC_H_O_ROW_TOK] = (int32_t)o_rtok;
+  h[PIC_H_O_ROPE_TILES] = (int32_t)o_rope;
+  h[PIC_H_O_ATTN_TILES] = (int32_t)o_tiles;
+  h[PIC_H_O_ATTN_ITEMS] = (int32_t)o_items;
+  h[PIC_H_O_MERGE] = (int32_t)o_merge;
+  if (n_req > 0) std::memcpy(h + o_rcp, req_chunk_ptr, sizeof(int32_t) * (n_req + 1));
+  else h[o_rcp] = 0;
+  if (!chunk_off.empty()) std::memcpy(h + o_coff, chunk_off.data(), sizeof(int32_t) * chunk_off.size());
+  std::memcpy(h + o_rtp, req_tok_ptr.data(), sizeof(int32_t) * req_tok_ptr.size());
+  std::memcpy(h + o_rrp, req_row_ptr.data(), sizeof(int32_t) * req_row_ptr.size());
+  if (nrows) {
+    std::memcpy(h + o_rows, rows.data(), sizeof(int32_t) * nrows);
+    std::memcpy(h + o_rtok, row_tok.data(), sizeof(int32_t) * nrows);
+  }
+  if (!rope.empty()) std::memcpy(h + o_rope, rope.data(), sizeof(RopeTile) * rope.size());
+  if (!tiles.empty()) std::memcpy(h + o_tiles, tiles.data(), sizeof(AttnTile) * tiles.size());
+  if (!items.empty()) std::memcpy(h + o_items, items.data(), sizeof(AttnItem) * items.size());
+  if (!merges.empty()) std::memcpy(h + o_merge, merges.data(), sizeof(MergeEntry) * merges.size());
+  return PIC_OK;
+}
+
+extern "C" const char *pic_strerror(int status) {
+  switch (status) {
+    case PIC_OK: return "ok";
+    case PIC_EINVAL: return "invalid argument";
+    case PIC_ENOSPC: return "output buffer too small";
+    case PIC_EUNSUPPORTED: return "unsupported configuration";
+    case PIC_EDEVICE: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,234 @@
+"""C-ABI surface and host planner (pic_build_index), CPU only.
+
+The planner is host code, so it runs here: its recompute index, offsets and
+buffer rows must equal the oracle's bit for bit, and its launch schedules must
+cover exactly the rows and keys the definition needs.  No kernel is launched.
+"""
+
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import position_independent_kv_rope_amd as P
+from oracle import pic_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    if not os.path.exists(P.LIB_PATH):
+        from position_independent_kv_rope_amd import build
+        build.build()
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "pic.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pic_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = _declared_symbols()
+    assert set(syms) == set(P.EXPORTED), syms
+    lib = ctypes.CDLL(P.LIB_PATH)
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_strerror_and_status_codes():
+    assert P.strerror(P.PIC_OK) == "ok"
+    for code in (P.PIC_EINVAL, P.PIC_ENOSPC, P.PIC_EUNSUPPORTED, P.PIC_EDEVICE):
+        assert P.strerror(code) != "unknown status"
+    assert P.strerror(12345) == "unknown status"
+
+
+def _build_raw(rcp, lens, ql, k, h_q=4, h_kv=4, pos_base=0, cap=None):
+    L = P.lib()
+    rcp, lens, ql = (np.asarray(a, dtype=np.int32) for a in (rcp, lens, ql))
+    words = ctypes.c_int64(0)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p) if a.size else None
+    n_req = len(ql)
+    st0 = L.pic_build_index(n_req, ptr(rcp), ptr(lens), ptr(ql), k, pos_base, h_q, h_kv, 0,
+                            None, 0, ctypes.byref(words))
+    if st0 != 0 or cap is None:
+        return st0, words.value
+    buf = np.full(max(cap, 1), 0x5A5A5A5A, dtype=np.int32)
+    st1 = L.pic_build_index(n_req, ptr(rcp), ptr(lens), ptr(ql), k, pos_base, h_q, h_kv, 0,
+                            ptr(buf), cap, ctypes.byref(words))
+    return st1, buf
+
+
+def test_build_index_error_paths():
+    assert _build_raw([0, 1], [3], [2], -1)[0] == P.PIC_EINVAL       # k < 0
+    assert _build_raw([0, 1], [-3], [2], 1)[0] == P.PIC_EINVAL       # negative length
+    assert _build_raw([0, 1], [3], [-2], 1)[0] == P.PIC_EINVAL       # negative q
+    assert _build_raw([1, 1], [3], [2], 1)[0] == P.PIC_EINVAL        # CSR not from 0
+    assert _build_raw([0, 2, 1], [3, 3], [1, 1], 1)[0] == P.PIC_EINVAL  # CSR decreasing
+    assert _build_raw([0, 1], [3], [2], 1, h_q=6, h_kv=4)[0] == P.PIC_EINVAL
+    assert _build_raw([0, 1], [3], [2], 1, h_q=12, h_kv=4)[0] == P.PIC_EUNSUPPORTED  # G=3
+    assert _build_raw([0, 1, 2], [3, 1 << 25], [1, 1], 1)[0] == P.PIC_OK  # chunk 0 of req 1
+    assert _build_raw([0, 2], [1 << 25, 3], [1], 1)[0] == P.PIC_EUNSUPPORTED  # delta > 2^24
+    st, need = _build_raw([0, 3], [4, 5, 5], [3], 2)
+    assert st == P.PIC_OK and need > 32
+    st, buf = _build_raw([0, 3], [4, 5, 5], [3], 2, cap=need - 1)
+    assert st == P.PIC_ENOSPC and np.all(buf == 0x5A5A5A5A)  # untouched
+
+
+def test_device_entry_points_reject_bad_arguments_without_launching():
+    L = P.lib()
+    plan = P.pic_build_index([[4, 5, 5]], [3], 2, 4, 4)
+    hp = plan.host_ptr()
+    bogus = np.zeros(64, dtype=np.int32)
+    bp = bogus.ctypes.data_as(ctypes.c_void_p)
+    fake = ctypes.c_void_p(0x1000)
+    assert L.pic_rope_delta(bp, fake, fake, P.PIC_F32, 16, 0, 1e4, None) == P.PIC_EINVAL
+    assert L.pic_rope_delta(hp, fake, fake, 7, 16, 0, 1e4, None) == P.PIC_EINVAL
+    assert L.pic_rope_delta(hp, fake, fake, P.PIC_F32, 15, 0, 1e4, None) == P.PIC_EINVAL
+    assert L.pic_rope_delta(hp, fake, fake, P.PIC_F32, 16, 2, 1e4, None) == P.PIC_EINVAL
+    assert L.pic_rope_delta(hp, fake, fake, P.PIC_F32, 16, 0, -1.0, None) == P.PIC_EINVAL
+    assert L.pic_rope_delta(hp, fake, fake, P.PIC_F32, 12, 0, 1e4, None) == P.PIC_EUNSUPPORTED
+    assert L.pic_rope_delta(hp, fake, None, P.PIC_F32, 16, 0, 1e4, None) == P.PIC_EINVAL
+    assert L.pic_splice(bp, fake, fake, fake, fake, fake, P.PIC_F32, 16, None) == P.PIC_EINVAL
+    assert L.pic_splice(hp, fake, fake, None, fake, fake, P.PIC_F32, 16, None) == P.PIC_EINVAL
+    assert L.pic_splice(hp, fake, fake, fake, fake, fake, P.PIC_F32, 12, None) == P.PIC_EUNSUPPORTED
+    args = (fake, fake, fake, fake)
+    assert L.pic_selective_attn(hp, fake, *args, P.PIC_F32, 16, 0.0, None, 0, None) == P.PIC_EINVAL
+    assert L.pic_selective_attn(hp, fake, *args, P.PIC_F32, 24, 0.25, None, 0, None) == P.PIC_EUNSUPPORTED
+    assert L.pic_selective_attn(hp, fake, *args, P.PIC_BF16, 16, 0.25, None, 0, None) == P.PIC_EUNSUPPORTED
+    assert L.pic_selective_attn(hp, None, *args, P.PIC_F32, 16, 0.25, None, 0, None) == P.PIC_EINVAL
+    # a split plan without workspace is refused before launch
+    big = P.pic_build_index([[1024] * 32], [128], 2, 32, 8)
+    assert P.pic_attn_workspace_bytes(big, 128) > 0
+    assert L.pic_selective_attn(big.host_ptr(), fake, *args, P.PIC_BF16, 128, 0.088, None, 0,
+                                None) == P.PIC_ENOSPC
+    assert L.pic_attn_workspace_bytes(bp, 128) == 0
+
+
+# ---------------------------------------------------------------------------
+# Planner vs oracle
+# ---------------------------------------------------------------------------
+
+
+def check_plan(reqs, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0):
+    plan = P.pic_build_index(reqs, q_lens, k, h_q, h_kv, pos_base=pos_base, n_cu=n_cu)
+    group = h_q // h_kv
+    # index, offsets and pointers: bit-exact against the oracle
+    exp_rows, exp_off, exp_tok, exp_rowptr = [], [], [0], [0]
+    for lens, q in zip(reqs, q_lens):
+        rows = O.recompute_positions(lens, q, k)
+        offs = O.chunk_offsets(lens)
+        exp_rows.append(rows)
+        exp_off += offs
+        exp_tok.append(exp_tok[-1] + offs[-1] + q)
+        exp_rowptr.append(exp_rowptr[-1] + len(rows))
+    flat_rows = [r for rr in exp_rows for r in rr]
+    assert plan.rows.tolist() == flat_rows
+    assert plan.chunk_off.tolist() == exp_off
+    assert plan.req_tok_ptr.tolist() == exp_tok
+    assert plan.req_row_ptr.tolist() == exp_rowptr
+    assert plan.row_tok.tolist() == [exp_tok[b] + r for b, rr in enumerate(exp_rows) for r in rr]
+    assert plan.n_tokens == exp_tok[-1] and plan.n_rows == len(flat_rows)
+
+    # rope tiles: exactly the cached rows that keep their K, with delta = off_c - pos_base
+    want = {}
+    for b, (lens, q) in enumerate(zip(reqs, q_lens)):
+        offs = O.chunk_offsets(lens)
+        rec = set(exp_rows[b])
+        for c, L_c in enumerate(lens):
+            delta = offs[c] - pos_base
+            for t in range(L_c):
+                if delta != 0 and offs[c] + t not in rec:
+                    want[exp_tok[b] + offs[c] + t] = delta
+    got = {}
+    for tok0, n, delta, _ in plan.rope_tiles.tolist():
+        assert 1 <= n <= 32
+        for t in range(tok0, tok0 + n):
+            assert t not in got
+            got[t] = delta
+    assert got == want
+
+    # attention tiles: every (row, head) once; items cover [0, p_last] of each tile
+    tile_rows = 64 // group
+    seen = set()
+    for ti, (req, r0, n, tokb, pf, pl, _, _) in enumerate(plan.attn_tiles.tolist()):
+        assert 1 <= n <= tile_rows and tokb == exp_tok[req]
+        assert exp_rowptr[req] <= r0 and r0 + n <= exp_rowptr[req + 1]
+        assert pf == flat_rows[r0] and pl == flat_rows[r0 + n - 1]
+        for r in range(r0, r0 + n):
+            assert r not in seen
+            seen.add(r)
+    assert seen == set(range(len(flat_rows)))
+    cover = {}
+    slots = set()
+    for tile, g, kb, ke, slot, _, _, _ in plan.attn_items.tolist():
+        assert 0 <= g < h_kv and 0 <= kb < ke
+        cover.setdefault((tile, g), []).append((kb, ke, slot))
+        if slot >= 0:
+            assert slot not in slots
+            slots.add(slot)
+    tiles = plan.attn_tiles.tolist()
+    for ti in range(len(tiles)):
+        for g in range(h_kv):
+            ranges = sorted(cover[(ti, g)])
+            assert ranges[0][0] == 0 and ranges[-1][1] == tiles[ti][5] + 1
+            for (a0, a1, _), (b0, b1, _) in zip(ranges, ranges[1:]):
+                assert a1 == b0
+            if len(ranges) == 1:
+                assert ranges[0][2] == -1
+            else:
+                assert all(s >= 0 for _, _, s in ranges)
+    merges = plan.merges.tolist()
+    assert len(merges) == sum(1 for v in cover.values() if len(v) > 1)
+    for tile, g, base, n in merges:
+        assert sorted(s for _, _, s in cover[(tile, g)]) == list(range(base, base + n))
+    assert plan[P.H_N_PARTIALS] == len(slots)
+    # items are ordered longest first
+    lengths = [ke - kb for _, _, kb, ke, _, _, _, _ in plan.attn_items.tolist()]
+    assert lengths == sorted(lengths, reverse=True)
+    return plan
+
+
+def test_plan_worked_example():
+    plan = check_plan([[4, 5, 5]], [3], 2, 4, 4)
+    assert plan.rows.tolist() == [4, 5, 9, 10, 14, 15, 16]
+
+
+def test_plan_exhaustive_small_grids():
+    for n in range(1, 4):
+        for lens in itertools.product(range(0, 5), repeat=n):
+            for q in range(0, 3):
+                for k in (0, 1, 2, 5):
+                    check_plan([list(lens)], [q], k, 4, 2)
+
+
+def test_plan_multi_request_and_pos_base():
+    check_plan([[3, 0, 4], [5], [2, 2, 2, 2], []], [2, 0, 3, 4], 1, 8, 2)
+    check_plan([[4, 5, 5], [7, 1]], [3, 2], 0, 4, 4, pos_base=4)
+    check_plan([[4, 5, 5]], [3], 2, 4, 4, pos_base=-3)
+
+
+@pytest.mark.parametrize("k", [2, 16])
+def test_plan_long_context_splits(k):
+    plan = check_plan([[1024] * 32], [128], k, 32, 8)
+    assert plan[P.H_N_MERGE] > 0  # a few hundred rows need split-KV to fill the GPU
+
+
+def test_plan_epic_sweep_sizes():
+    from position_independent_kv_rope_amd import workloads as W
+    wl = W.epic_sweep(k=16)
+    check_plan([r.chunk_lens for r in wl.requests], [r.q_len for r in wl.requests], 16, 32, 8)
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(st.lists(st.integers(0, 300), min_size=0, max_size=12), min_size=1, max_size=4),
+       st.lists(st.integers(0, 70), min_size=4, max_size=4), st.integers(0, 20),
+       st.sampled_from([(32, 8), (32, 4), (4, 4), (8, 1), (16, 16)]), st.integers(-5, 5))
+def test_plan_property(reqs, qs, k, heads, pos_base):
+    check_plan(reqs, qs[:len(reqs)], k, heads[0], heads[1], pos_base=pos_base, n_cu=8)

@@ -1,0 +1,257 @@
+"""GPU parity of the HIP path against the CPU oracle (MI355X only).
+
+Every case calls the C ABI through the binding on seeded synthetic inputs and
+compares with the oracle on the same bits: the index and the splice bit-exactly,
+floating outputs to max-abs 1e-5 (fp32 I/O) or 2e-2 (bf16 I/O) on unit-variance
+inputs.  Full-size workloads compare every rotated row and sampled attention rows.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import position_independent_kv_rope_amd as P
+from position_independent_kv_rope_amd import workloads as W
+from oracle import pic_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+LAYOUTS = {"adjacent": P.PIC_ROPE_ADJACENT, "half": P.PIC_ROPE_HALF}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    P.lib()
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t):
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+class Run:
+    """One pass of the path on the GPU, keeping every intermediate on the host."""
+
+    def __init__(self, wl, layout="adjacent", n_cu=0, pos_base=0):
+        self.wl = wl
+        reqs = [r.chunk_lens for r in wl.requests]
+        qs = [r.q_len for r in wl.requests]
+        self.plan = P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, pos_base=pos_base,
+                                      n_cu=n_cu)
+        self.plan.to_device()
+        self.k_in, self.v_in = W.context_tensors(wl)
+        self.q, self.kf, self.vf = W.fresh_tensors(wl, self.plan.n_rows)
+        dev = "cuda"
+        k = self.k_in.to(dev)
+        v = self.v_in.to(dev)
+        q, kf, vf = self.q.to(dev), self.kf.to(dev), self.vf.to(dev)
+        out = torch.full_like(q, float("nan"))
+        ws = P.attn_workspace(self.plan, wl.head_dim)
+        say(wl.name, "k=%d" % wl.k, layout, "rope_delta")
+        P.pic_rope_delta(self.plan, k, wl.rope_base, LAYOUTS[layout])
+        torch.cuda.synchronize()
+        self.k_rot = k.cpu()
+        say(wl.name, "splice")
+        P.pic_splice(self.plan, k, v, kf, vf)
+        torch.cuda.synchronize()
+        self.k_spl, self.v_spl = k.cpu(), v.cpu()
+        say(wl.name, "selective_attn items=%d merges=%d" % (self.plan[P.H_N_ATTN_ITEMS],
+                                                          self.plan[P.H_N_MERGE]))
+        P.pic_selective_attn(self.plan, q, k, v, out, workspace=ws)
+        torch.cuda.synchronize()
+        self.out = out.cpu()
+        self.layout = layout
+        self.pos_base = pos_base
+        self.dev = dict(q=q, k=k, v=v, out=out, ws=ws)
+
+    def request_slices(self, b):
+        r = self.wl.requests[b]
+        tok0 = int(self.plan.req_tok_ptr[b])
+        row0, row1 = int(self.plan.req_row_ptr[b]), int(self.plan.req_row_ptr[b + 1])
+        return r, tok0, row0, row1
+
+    def oracle_request(self, b):
+        """Oracle K after rotation, spliced K/V, and attention output of request b."""
+        r, tok0, row0, row1 = self.request_slices(b)
+        offs = O.chunk_offsets(r.chunk_lens)
+        kin = f64(self.k_in[tok0:tok0 + offs[-1]])
+        vin = f64(self.v_in[tok0:tok0 + offs[-1]])
+        chunks_k = [kin[offs[c]:offs[c + 1]] for c in range(len(r.chunk_lens))]
+        chunks_v = [vin[offs[c]:offs[c + 1]] for c in range(len(r.chunk_lens))]
+        rows = O.recompute_positions(r.chunk_lens, r.q_len, self.wl.k)
+        if chunks_k:
+            k_ctx = O.rope_delta(chunks_k, self.wl.rope_base, self.layout, self.pos_base)
+            v_ctx = O.concat_chunks(chunks_v)
+        else:
+            k_ctx = np.zeros((0, self.wl.h_kv, self.wl.head_dim))
+            v_ctx = k_ctx
+        n_total = offs[-1] + r.q_len
+        kx, vx = O.splice(k_ctx, v_ctx, f64(self.kf[row0:row1]), f64(self.vf[row0:row1]), rows,
+                          n_total)
+        return rows, k_ctx, kx, vx
+
+
+def check_run(run, sample_rows=None):
+    wl, plan = run.wl, run.plan
+    tol = TOL[wl.dtype]
+    # index: bit-exact
+    flat = []
+    for r in wl.requests:
+        flat += O.recompute_positions(r.chunk_lens, r.q_len, wl.k)
+    assert plan.rows.tolist() == flat
+    worst = {"rope": 0.0, "attn": 0.0}
+    for b in range(len(wl.requests)):
+        r, tok0, row0, row1 = run.request_slices(b)
+        rows, k_ctx, kx, vx = run.oracle_request(b)
+        ctx = sum(r.chunk_lens)
+        rec = set(rows)
+        keep = np.array([j for j in range(ctx) if j not in rec], dtype=np.int64)
+        # rotated K on the kept rows against the oracle; untouched rows bit-identical
+        got = f64(run.k_rot[tok0:tok0 + ctx])
+        if keep.size:
+            err = float(np.max(np.abs(got[keep] - k_ctx[keep])))
+            worst["rope"] = max(worst["rope"], err)
+            assert err <= tol, ("rope_delta", b, err)
+        n_total = ctx + r.q_len
+        # rows the rotation must not touch: recomputed rows (the splice overwrites them)
+        # and, with pos_base = 0, all of chunk 0 (delta_0 = 0)
+        rec_t = torch.tensor(rows, dtype=torch.long) + tok0
+        assert torch.equal(run.k_rot[rec_t], run.k_in[rec_t])
+        if run.pos_base == 0 and r.chunk_lens:
+            L0 = r.chunk_lens[0]
+            assert torch.equal(run.k_rot[tok0:tok0 + L0], run.k_in[tok0:tok0 + L0])
+        # splice: fresh rows bit-exact, V elsewhere unchanged, K elsewhere = rotated
+        rows_t = torch.tensor(rows, dtype=torch.long) + tok0
+        assert torch.equal(run.k_spl[rows_t], run.kf[row0:row1])
+        assert torch.equal(run.v_spl[rows_t], run.vf[row0:row1])
+        others = torch.tensor([tok0 + j for j in range(n_total) if j not in rec], dtype=torch.long)
+        if others.numel():
+            assert torch.equal(run.v_spl[others], run.v_in[others])
+            assert torch.equal(run.k_spl[others], run.k_rot[others])
+        # attention
+        qb = f64(run.q[row0:row1])
+        if sample_rows is None:
+            want = O.selective_attn(qb, kx, vx, rows)
+            got_o = f64(run.out[row0:row1])
+        else:
+            rng = np.random.default_rng(1234 + b)
+            n = row1 - row0
+            picks = sorted(set(rng.integers(0, n, size=min(sample_rows, n)).tolist()) |
+                           {0, n - 1})
+            heads = rng.integers(0, wl.h_q, size=len(picks))
+            g = heads // (wl.h_q // wl.h_kv)
+            want = O.attn_rows_direct([qb[i, h] for i, h in zip(picks, heads)], kx, vx,
+                                      [rows[i] for i in picks], g)
+            got_o = np.stack([f64(run.out[row0 + i, h]) for i, h in zip(picks, heads)])
+        assert np.isfinite(got_o).all()
+        err = float(np.max(np.abs(got_o - want))) if want.size else 0.0
+        worst["attn"] = max(worst["attn"], err)
+        assert err <= tol, ("selective_attn", b, err)
+    say(wl.name, "k=%d" % wl.k, "max-abs errors", worst)
+    return worst
+
+
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_worked_example_fp32(layout):
+    run = Run(W.worked_example(), layout)
+    assert run.plan.rows.tolist() == [4, 5, 9, 10, 14, 15, 16]
+    check_run(run)
+
+
+def test_rag_single_bf16():
+    check_run(Run(W.rag_single()))
+
+
+@pytest.mark.parametrize("k", [2, 16])
+def test_long_context_bf16(k):
+    run = Run(W.long_context(k=k))
+    assert run.plan[P.H_N_MERGE] > 0
+    check_run(run)
+
+
+def test_epic_sweep_full_size_sampled():
+    # the launch configuration bench.py times (n_cu = 256), sampled attention rows
+    run = Run(W.epic_sweep(k=16), n_cu=256)
+    check_run(run, sample_rows=48)
+
+
+def _custom(name, dtype, h_q, h_kv, d, base, k, reqs, seed=11, scale=1.0):
+    return W.Workload(name, dtype, h_q, h_kv, d, base, k,
+                      [W.Request(list(c), q) for c, q in reqs], value_scale=scale, seed=seed)
+
+
+EDGE_CASES = [
+    # ragged tails, zero-length chunks, q = 0 requests, k = 0, k >= chunk length
+    ("ragged_bf16", "bf16", 32, 8, 128, 5e5, 3, [([37, 0, 101, 5], 9), ([64], 0), ([3, 3], 70)]),
+    ("k0_bf16", "bf16", 32, 8, 128, 5e5, 0, [([300, 200], 17)]),
+    ("k_ge_len_bf16", "bf16", 32, 8, 128, 5e5, 40, [([20, 33, 7], 5)]),
+    ("gqa8_bf16", "bf16", 32, 4, 128, 5e5, 8, [([700, 650, 900], 128), ([513], 3)]),
+    ("mha_bf16_d64", "bf16", 8, 8, 64, 1e4, 4, [([130, 77], 12)]),
+    ("gqa2_bf16_d64", "bf16", 16, 8, 64, 1e6, 2, [([250, 250, 250], 40)]),
+    ("f32_d32", "f32", 8, 2, 32, 1e4, 2, [([40, 41, 42], 11), ([5], 2)]),
+    ("f32_d64", "f32", 16, 4, 64, 5e5, 5, [([300, 129], 33)]),
+    ("f32_d128", "f32", 32, 8, 128, 5e5, 16, [([200, 180], 20)]),
+    ("only_query_rows", "f32", 4, 4, 16, 1e4, 2, [([], 6), ([0], 3)]),
+]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
+def test_edge_cases(case):
+    name, dtype, hq, hkv, d, base, k, reqs = case
+    check_run(Run(_custom(name, dtype, hq, hkv, d, base, k, reqs)))
+
+
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_half_layout_and_pos_base(layout):
+    # LegoLink-0 style cached positions (first cached row at position 4): every chunk,
+    # chunk 0 included, is rotated by off_c - 4 (negative for chunk 0)
+    wl = _custom("pos_base", "bf16", 32, 8, 128, 5e5, 0, [([100, 90, 80], 20)])
+    check_run(Run(wl, layout, pos_base=4))
+
+
+def test_consistency_invariant_gpu():
+    # cached K = RoPE(K0, local), fresh K/Q = RoPE(., global) (made by the oracle on the
+    # CPU, rounded to fp32): the GPU link must reproduce full causal attention.
+    rng = np.random.default_rng(21)
+    lens, q_len, hq, hkv, d, base, k = [9, 14, 11, 6], 5, 8, 2, 32, 1e4, 2
+    offs = O.chunk_offsets(lens)
+    n = offs[-1] + q_len
+    q0, k0, v = (rng.standard_normal((n, h, d)) for h in (hq, hkv, hkv))
+    pos = np.arange(n)
+    kg, qg = O.rope_rotate(k0, pos, base), O.rope_rotate(q0, pos, base)
+    cached = np.concatenate([O.rope_rotate(k0[offs[c]:offs[c + 1]], np.arange(lens[c]), base)
+                             for c in range(len(lens))] + [np.zeros((q_len, hkv, d))])
+    plan = P.pic_build_index([lens], [q_len], k, hq, hkv)
+    plan.to_device()
+    rows = plan.rows.tolist()
+    t = lambda a: torch.tensor(a, dtype=torch.float32, device="cuda").contiguous()
+    kb, vb = t(cached), t(np.concatenate([v[:offs[-1]], np.zeros((q_len, hkv, d))]))
+    q, kf, vf = t(qg[rows]), t(kg[rows]), t(v[rows])
+    out = torch.empty_like(q)
+    say("consistency_invariant")
+    P.pic_rope_delta(plan, kb, base)
+    P.pic_splice(plan, kb, vb, kf, vf)
+    P.pic_selective_attn(plan, q, kb, vb, out, workspace=P.attn_workspace(plan, d))
+    torch.cuda.synchronize()
+    want = O.full_causal_attn(qg.astype(np.float32), kg.astype(np.float32),
+                              v.astype(np.float32))[rows]
+    assert np.max(np.abs(f64(kb) - kg)) < 1e-5
+    assert np.max(np.abs(f64(out) - want)) < 1e-5
+
+
+def test_attention_is_deterministic():
+    run = Run(W.long_context(k=2))
+    d = run.dev
+    again = torch.full_like(d["out"], float("nan"))
+    P.pic_selective_attn(run.plan, d["q"], d["k"], d["v"], again, workspace=d["ws"])
+    torch.cuda.synchronize()
+    assert torch.equal(again.cpu(), run.out)
