@@ -36,7 +36,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="recomputed rows of request 0 the oracle times (0 = all)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (5 launches) to calibrate "
+                         "rocprofv3 FETCH_SIZE/WRITE_SIZE against known bytes")
     return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
 def make_workload(name, k):
@@ -116,6 +131,8 @@ def main():
     import position_independent_kv_rope_amd as P
     from position_independent_kv_rope_amd import workloads as W
 
+    if args.copy_calibration:
+        return copy_calibration()
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)

@@ -77,7 +77,7 @@ enum { PIC_ROPE_ADJACENT = 0, PIC_ROPE_HALF = 1 };
  * ---------------------------------------------------------------------------- */
 #define PIC_PLAN_MAGIC 0x31434950 /* "PIC1" */
 #define PIC_PLAN_HEADER_WORDS 32
-#define PIC_ATTN_TILE_M 64 /* (row, head) pairs per attention tile */
+#define PIC_ATTN_TILE_M 128 /* query vectors (row, head) per attention tile */
 #define PIC_ROPE_TILE_ROWS 32
 
 enum {

@@ -18,7 +18,7 @@ PIC_OK, PIC_EINVAL, PIC_ENOSPC, PIC_EUNSUPPORTED, PIC_EDEVICE = 0, -1, -2, -3, -
 PIC_F32, PIC_BF16 = 0, 1
 PIC_ROPE_ADJACENT, PIC_ROPE_HALF = 0, 1
 PIC_PLAN_MAGIC = 0x31434950
-PIC_ATTN_TILE_M = 64
+PIC_ATTN_TILE_M = 128
 
 # header word indices (include/pic.h)
 (H_MAGIC, H_WORDS, H_N_REQ, H_N_CHUNKS, H_N_ROWS, H_N_TOKENS, H_K, H_POS_BASE, H_H_Q, H_H_KV,

@@ -7,21 +7,26 @@
 // query head h to KV head h / G.
 //
 // Work decomposition (the host planner builds it): an attention tile is
-// PIC_ATTN_TILE_M = 64 (row, head) pairs -- 64/G consecutive recomputed rows of one
+// PIC_ATTN_TILE_M = 128 query vectors -- 128/G consecutive recomputed rows of one
 // request times the G query heads that share one KV head -- so every K/V element
-// staged in LDS feeds 64 query vectors.  An item is (tile, kv head, key range); long
+// staged in LDS feeds 128 query vectors.  An item is (tile, kv head, key range); long
 // tiles are split along keys and a merge kernel combines the partial results with
 // their log-sum-exp weights.
 //
-// Inside a workgroup (4 waves) each wave owns 16 of the 64 query vectors.  Per block
-// of 64 keys the workgroup stages K (row-major) and V (transposed, key-contiguous)
-// into LDS, then each wave computes S^T = K Q^T with MFMA (16 keys x 16 queries per
-// instruction), runs the online softmax in the exp2 domain with the running max kept
-// per query column (the C layout puts one query per lane column, so the row statistics
-// need only two cross-lane exchanges), and accumulates O^T += V^T P^T with MFMA.  The
-// keys of a 32-key group are permuted between the two S^T instructions so that each
-// lane's softmax probabilities are exactly the 8 consecutive keys its PV operand needs.
-// bf16 uses v_mfma_f32_16x16x32_bf16 (fp32 accumulate); fp32 uses v_mfma_f32_16x16x4_f32.
+// The math is the flash-attention recurrence in transposed form: S^T = K Q^T puts one
+// query per MFMA output column, so a lane holds many keys of one query and the softmax
+// statistics need one (32x32 tiles) or two (16x16 tiles) cross-lane exchanges; then
+// O^T += V^T P^T consumes the probabilities straight from the S^T registers.  Rows of
+// the K operand are permuted so that each lane's probabilities are exactly the
+// consecutive keys its PV operand slots need.  The running max is kept in the exp2
+// domain (scores scaled by scale * log2 e).
+//
+// bf16 kernel (the hot one): 4 waves x 32 queries, v_mfma_f32_32x32x16_bf16 for both
+// products, K/V blocks of 64 keys double-buffered in LDS (row-major, 16-byte coalesced
+// staging; the next block is loaded into registers while the current one is
+// computed), V read transposed for the PV operand with ds_read_b64_tr_b16.
+// fp32 kernel: 8 waves x 16 queries, v_mfma_f32_16x16x4_f32 (fp32 operands, so fp32
+// I/O keeps fp32 accuracy), V staged transposed.
 #include <cmath>
 #include <type_traits>
 
@@ -31,63 +36,44 @@
 namespace pic {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kKB = 64;  // keys per staged block
-constexpr int kM = PIC_ATTN_TILE_M;
+constexpr int kM = PIC_ATTN_TILE_M;  // query vectors per tile
+constexpr int kKB = 64;              // keys per staged block
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 
-static_assert(kM == 16 * kWaves, "one 16-query MFMA column block per wave");
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <typename T>
-struct Cfg;
-template <>
-struct Cfg<__bf16> {
-  static constexpr int kPad = 8;  // elements of padding per LDS row (16 bytes)
-};
-template <>
-struct Cfg<float> {
-  static constexpr int kPad = 4;
-};
+__device__ __forceinline__ bool wave_any(bool p) { return __any((int)p); }
 
-// Key (within a 64-key block) held in C-tile slot i of lane group grp of sub-block sb.
-template <typename T>
-__device__ __forceinline__ int key_of(int sb, int grp, int i) {
-  if constexpr (std::is_same<T, __bf16>::value)
-    return 32 * (sb >> 1) + 8 * grp + 4 * (sb & 1) + i;
-  else
-    return 16 * sb + 4 * grp + i;
+// ================================ bf16 kernel ==================================
+
+constexpr int kBfWaves = 4;
+constexpr int kBfThreads = 64 * kBfWaves;
+static_assert(kM == 32 * kBfWaves, "one 32-query MFMA column block per wave");
+
+// Key (0..31 within a 32-key S^T tile t of the 64-key block) at C row r: rows held by
+// lane group g in accumulator slots 8h..8h+7 become keys 16(2t+h) + 8g + 0..7.
+__device__ __forceinline__ int perm_key(int t, int r) {
+  const int a = r >> 3, g = (r >> 2) & 1, b = r & 3;
+  return 16 * (2 * t + (a >> 1)) + 8 * g + 4 * (a & 1) + b;
 }
 
-__device__ __forceinline__ float wave_max_cols(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-__device__ __forceinline__ float wave_sum_cols(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void attn_kernel(
-    const T *__restrict__ q, const T *__restrict__ kbuf, const T *__restrict__ vbuf,
-    T *__restrict__ out, const int32_t *__restrict__ rows, const AttnTile *__restrict__ tiles,
-    const AttnItem *__restrict__ items, float *__restrict__ ws_o, float *__restrict__ ws_ml,
-    int h_q, int h_kv, int tile_rows, float scale_log2) {
-  constexpr int kPad = Cfg<T>::kPad;
-  constexpr int kKs = D + kPad;    // K row stride in LDS (elements)
-  constexpr int kVs = kKB + kPad;  // V^T row stride in LDS (elements)
-  constexpr int kEPU = 16 / sizeof(T);  // elements per 16-byte unit
-  constexpr int kUPR = D / kEPU;        // 16-byte units per key row of one head
-  constexpr bool kBf16 = std::is_same<T, __bf16>::value;
-  constexpr int kDB = D / 16;           // 16-wide output d blocks
-  constexpr int kQOps = kBf16 ? D / 32 : D / 4;
-
-  __shared__ __attribute__((aligned(16))) T ks[kKB * kKs];
-  __shared__ __attribute__((aligned(16))) T vt[D * kVs];
+template <int D>
+__global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ kbuf,
+    const __bf16 *__restrict__ vbuf, __bf16 *__restrict__ out, const int32_t *__restrict__ rows,
+    const AttnTile *__restrict__ tiles, const AttnItem *__restrict__ items,
+    float *__restrict__ ws_o, float *__restrict__ ws_ml, int h_q, int h_kv, int tile_rows,
+    float scale_log2) {
+  constexpr int kStride = D + 8;             // LDS row stride (elements): 16 B of padding
+  constexpr int kKS = D / 16;                // S^T contraction steps
+  constexpr int kDB = D / 32;                // 32-wide d blocks of O^T
+  constexpr int kUPR = D / 8;                // 16-byte units per key row
+  constexpr int kUPT = kKB * kUPR / kBfThreads;  // staged units per thread per tensor
+  static_assert(kUPT * kBfThreads == kKB * kUPR, "staging must tile the block");
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2][2][kKB * kStride];
 
   const AttnItem it = items[blockIdx.x];
   const AttnTile tile = tiles[it.tile];
@@ -95,10 +81,216 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   const int group = h_q / h_kv;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;  // query column of this lane in C tiles
-  const int grp = lane >> 4;  // lane group 0..3
+  const int n = lane & 31;     // query column of this lane
+  const int grp = lane >> 5;   // lane group (0, 1)
+  const int q16 = lane >> 4;   // 16-lane group for the transposing LDS read
+  const int i16 = lane & 15;
 
-  // ---- the query vector of this lane's column ----
+  const int m = 32 * wave + n;
+  const int row_local = m % tile_rows;
+  const int head = g * group + m / tile_rows;
+  const bool valid = row_local < tile.n_rows;
+  const int row = tile.row_begin + (valid ? row_local : 0);
+  const int pos = valid ? rows[row] : -1;
+
+  bf16x8 qop[kKS];
+  {
+    const __bf16 *qp = q + ((int64_t)row * h_q + head) * D + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < kKS; ++s)
+      qop[s] = valid ? *reinterpret_cast<const bf16x8 *>(qp + 16 * s) : bf16x8{};
+  }
+  int pos_min = valid ? pos : 0x7fffffff;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) pos_min = min(pos_min, __shfl_xor(pos_min, o));
+
+  f32x16 acc[kDB];
+#pragma unroll
+  for (int d = 0; d < kDB; ++d)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[d][j] = 0.f;
+  float m_run = kNegInf;
+  float l_lane = 0.f;
+
+  const int key_begin = it.key_begin;
+  const int key_end = it.key_end;
+  const int key_last = key_end - 1;
+  const int64_t tok_stride = (int64_t)h_kv * D;
+  const __bf16 *kbase = kbuf + (int64_t)tile.tok_base * tok_stride + (int64_t)g * D;
+  const __bf16 *vbase = vbuf + (int64_t)tile.tok_base * tok_stride + (int64_t)g * D;
+
+  u32x4 pk[kUPT], pv[kUPT];
+  auto load_block = [&](int kb0) {
+#pragma unroll
+    for (int r = 0; r < kUPT; ++r) {
+      const int u = threadIdx.x + kBfThreads * r;
+      const int key = u / kUPR, c = u - key * kUPR;
+      const int64_t at = (int64_t)min(kb0 + key, key_last) * tok_stride + 8 * c;
+      pk[r] = *reinterpret_cast<const u32x4 *>(kbase + at);
+      pv[r] = *reinterpret_cast<const u32x4 *>(vbase + at);
+    }
+  };
+  auto store_block = [&](int b) {
+#pragma unroll
+    for (int r = 0; r < kUPT; ++r) {
+      const int u = threadIdx.x + kBfThreads * r;
+      const int key = u / kUPR, c = u - key * kUPR;
+      *reinterpret_cast<u32x4 *>(&lds[b][0][key * kStride + 8 * c]) = pk[r];
+      *reinterpret_cast<u32x4 *>(&lds[b][1][key * kStride + 8 * c]) = pv[r];
+    }
+  };
+
+  const int n_blocks = (key_end - key_begin + kKB - 1) / kKB;
+  load_block(key_begin);
+  store_block(0);
+  __syncthreads();
+
+  for (int ib = 0; ib < n_blocks; ++ib) {
+    const int kb0 = key_begin + ib * kKB;
+    const int buf = ib & 1;
+    const bool more = ib + 1 < n_blocks;
+    if (more) load_block(kb0 + kKB);
+    const __bf16 *Ks = lds[buf][0];
+    const __bf16 *Vs = lds[buf][1];
+
+    // ---- S^T = K Q^T: two 32-key tiles ----
+    f32x16 sc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sc[t][j] = 0.f;
+      const __bf16 *kr = Ks + perm_key(t, n) * kStride + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < kKS; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kr + 16 * s);
+        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], sc[t], 0, 0, 0);
+      }
+    }
+
+    // ---- causal mask, only where a key can pass a column's position ----
+    if (kb0 + kKB - 1 > min(pos_min, key_last)) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = kb0 + perm_key(t, 8 * (j >> 2) + 4 * grp + (j & 3));
+          if (key > pos || key > key_last) sc[t][j] = kNegInf;
+        }
+    }
+
+    // ---- online softmax (exp2 domain) ----
+    float mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[t][j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const bool none = m_new == kNegInf;
+    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float base = none ? 0.f : m_new;
+    m_run = m_new;
+    float psum = 0.f;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[t][j], scale_log2, -base));
+        psum += p;
+        pb[2 * t + (j >> 3)][j & 7] = (__bf16)p;
+      }
+    l_lane = l_lane * alpha + psum;
+    if (wave_any(alpha != 1.f)) {
+#pragma unroll
+      for (int d = 0; d < kDB; ++d) acc[d] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T (V^T operand via transposing LDS reads) ----
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      // source row of this lane for the transposing read: key 16c + 8*(q16/2) + i16/4 (+4)
+      const __bf16 *vr = Vs + (16 * c + 8 * (q16 >> 1) + (i16 >> 2)) * kStride +
+                         16 * (q16 & 1) + 4 * (i16 & 3);
+#pragma unroll
+      for (int d = 0; d < kDB; ++d) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(vr + 32 * d));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(vr + 4 * kStride + 32 * d));
+        bf16x8 a;
+        __builtin_memcpy(&a, &lo, 8);
+        __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &hi, 8);
+        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[d], 0, 0, 0);
+      }
+    }
+
+    if (more) store_block(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+  const float l_row = l_lane + __shfl_xor(l_lane, 32);
+  if (!valid) return;
+  if (it.slot < 0) {
+    const float inv = 1.f / l_row;
+    __bf16 *op = out + ((int64_t)row * h_q + head) * D + 4 * grp;
+#pragma unroll
+    for (int d = 0; d < kDB; ++d)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        bf16x4 o;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) o[b] = (__bf16)(acc[d][4 * a + b] * inv);
+        *reinterpret_cast<bf16x4 *>(op + 32 * d + 8 * a) = o;
+      }
+  } else {
+    float *wo = ws_o + ((int64_t)it.slot * kM + m) * D + 4 * grp;
+#pragma unroll
+    for (int d = 0; d < kDB; ++d)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 o;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) o[b] = acc[d][4 * a + b];
+        *reinterpret_cast<f32x4 *>(wo + 32 * d + 8 * a) = o;
+      }
+    if (grp == 0) {
+      ws_ml[((int64_t)it.slot * kM + m) * 2 + 0] = m_run;
+      ws_ml[((int64_t)it.slot * kM + m) * 2 + 1] = l_row;
+    }
+  }
+}
+
+// ================================ fp32 kernel ==================================
+
+constexpr int kF32Waves = 8;
+constexpr int kF32Threads = 64 * kF32Waves;
+static_assert(kM == 16 * kF32Waves, "one 16-query MFMA column block per wave");
+
+template <int D>
+__global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ kbuf, const float *__restrict__ vbuf,
+    float *__restrict__ out, const int32_t *__restrict__ rows, const AttnTile *__restrict__ tiles,
+    const AttnItem *__restrict__ items, float *__restrict__ ws_o, float *__restrict__ ws_ml,
+    int h_q, int h_kv, int tile_rows, float scale_log2) {
+  constexpr int kKs = D + 4;      // K row stride in LDS (floats)
+  constexpr int kVs = kKB + 4;    // V^T row stride in LDS (floats)
+  constexpr int kUPR = D / 4;     // 16-byte units per key row
+  constexpr int kDB = D / 16;
+  constexpr int kQOps = D / 4;
+  __shared__ __attribute__((aligned(16))) float ks[kKB * kKs];
+  __shared__ __attribute__((aligned(16))) float vt[D * kVs];
+
+  const AttnItem it = items[blockIdx.x];
+  const AttnTile tile = tiles[it.tile];
+  const int g = it.kv_head;
+  const int group = h_q / h_kv;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
   const int m = 16 * wave + col;
   const int row_local = m % tile_rows;
   const int head = g * group + m / tile_rows;
@@ -106,21 +298,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   const int row = tile.row_begin + (valid ? row_local : 0);
   const int pos = valid ? rows[row] : -1;
 
-  typedef typename std::conditional<kBf16, bf16x8, float>::type Op;
-  Op qop[kQOps];
+  float qop[kQOps];
   {
-    const T *qp = q + ((int64_t)row * h_q + head) * D;
+    const float *qp = q + ((int64_t)row * h_q + head) * D;
 #pragma unroll
-    for (int s = 0; s < kQOps; ++s) {
-      if constexpr (kBf16) {
-        qop[s] = valid ? *reinterpret_cast<const bf16x8 *>(qp + 32 * s + 8 * grp) : bf16x8{};
-      } else {
-        qop[s] = valid ? qp[4 * s + grp] : 0.0f;
-      }
-    }
+    for (int s = 0; s < kQOps; ++s) qop[s] = valid ? qp[4 * s + grp] : 0.f;
   }
-
-  // lowest position among the wave's valid columns (masking is skipped below it)
   int pos_min = valid ? pos : 0x7fffffff;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) pos_min = min(pos_min, __shfl_xor(pos_min, o));
@@ -128,87 +311,62 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   f32x4 acc[kDB];
 #pragma unroll
   for (int d = 0; d < kDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf;  // running max of scaled scores (log2 domain), per column
-  float l_lane = 0.f;     // this lane's share of the running denominator
+  float m_run = kNegInf, l_lane = 0.f;
 
-  const int key_begin = it.key_begin;
-  const int key_end = it.key_end;  // exclusive, <= p_last + 1
-  const int key_last = key_end - 1;
-  const int64_t head_stride = (int64_t)h_kv * D;
-  const T *kbase = kbuf + (int64_t)tile.tok_base * head_stride + (int64_t)g * D;
-  const T *vbase = vbuf + (int64_t)tile.tok_base * head_stride + (int64_t)g * D;
+  const int key_begin = it.key_begin, key_end = it.key_end, key_last = key_end - 1;
+  const int64_t tok_stride = (int64_t)h_kv * D;
+  const float *kbase = kbuf + (int64_t)tile.tok_base * tok_stride + (int64_t)g * D;
+  const float *vbase = vbuf + (int64_t)tile.tok_base * tok_stride + (int64_t)g * D;
 
   for (int kb0 = key_begin; kb0 < key_end; kb0 += kKB) {
     __syncthreads();
-    // ---- stage K (row-major) ----
-    for (int u = threadIdx.x; u < kKB * kUPR; u += kThreads) {
+    for (int u = threadIdx.x; u < kKB * kUPR; u += kF32Threads) {
       const int key = u / kUPR, c = u - key * kUPR;
       const int kk = min(kb0 + key, key_last);
-      *reinterpret_cast<u32x4 *>(&ks[key * kKs + c * kEPU]) =
-          *reinterpret_cast<const u32x4 *>(kbase + (int64_t)kk * head_stride + c * kEPU);
+      *reinterpret_cast<f32x4 *>(&ks[key * kKs + 4 * c]) =
+          *reinterpret_cast<const f32x4 *>(kbase + (int64_t)kk * tok_stride + 4 * c);
     }
-    // ---- stage V transposed: 4 keys x one 16-byte unit per work item ----
-    for (int u = threadIdx.x; u < (kKB / 4) * kUPR; u += kThreads) {
+    // V transposed: 4 keys x 4 dims per work item
+    for (int u = threadIdx.x; u < (kKB / 4) * kUPR; u += kF32Threads) {
       const int quad = u / kUPR, c = u - quad * kUPR;
-      T e[4][kEPU];
+      f32x4 e[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kk = min(kb0 + 4 * quad + r, key_last);
-        const u32x4 raw = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)kk * head_stride + c * kEPU);
-        __builtin_memcpy(e[r], &raw, 16);
+        e[r] = *reinterpret_cast<const f32x4 *>(vbase + (int64_t)kk * tok_stride + 4 * c);
       }
 #pragma unroll
-      for (int j = 0; j < kEPU; ++j) {
-        T four[4] = {e[0][j], e[1][j], e[2][j], e[3][j]};
-        if constexpr (kBf16) {
-          uint64_t w;
-          __builtin_memcpy(&w, four, 8);
-          *reinterpret_cast<uint64_t *>(&vt[(c * kEPU + j) * kVs + 4 * quad]) = w;
-        } else {
-          u32x4 w;
-          __builtin_memcpy(&w, four, 16);
-          *reinterpret_cast<u32x4 *>(&vt[(c * kEPU + j) * kVs + 4 * quad]) = w;
-        }
-      }
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4 *>(&vt[(4 * c + j) * kVs + 4 * quad]) =
+            f32x4{e[0][j], e[1][j], e[2][j], e[3][j]};
     }
     __syncthreads();
 
-    // ---- S^T = K Q^T for the 4 sub-blocks of 16 keys ----
     f32x4 sc[4];
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
       sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int krow = key_of<T>(sb, col >> 2, col & 3);  // A row = C row = col here
+      const float *kr = ks + (16 * sb + col) * kKs + grp;
 #pragma unroll
-      for (int s = 0; s < kQOps; ++s) {
-        if constexpr (kBf16) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&ks[krow * kKs + 32 * s + 8 * grp]);
-          sc[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[s], sc[sb], 0, 0, 0);
-        } else {
-          const float a = ks[krow * kKs + 4 * s + grp];
-          sc[sb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qop[s], sc[sb], 0, 0, 0);
-        }
-      }
+      for (int s = 0; s < kQOps; ++s)
+        sc[sb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[4 * s], qop[s], sc[sb], 0, 0, 0);
     }
-
-    // ---- mask (only blocks that reach past some column's position or the range end) ----
     if (kb0 + kKB - 1 > min(pos_min, key_last)) {
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = kb0 + key_of<T>(sb, grp, i);
+          const int key = kb0 + 16 * sb + 4 * grp + i;
           if (key > pos || key > key_last) sc[sb][i] = kNegInf;
         }
     }
-
-    // ---- online softmax (exp2 domain) ----
     float mx = kNegInf;
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[sb][i]);
-    mx = wave_max_cols(mx);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx * scale_log2);
     const bool none = m_new == kNegInf;
     const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -226,53 +384,25 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     l_lane = l_lane * alpha + psum;
 #pragma unroll
     for (int d = 0; d < kDB; ++d) acc[d] *= alpha;
-
-    // ---- O^T += V^T P^T ----
-    if constexpr (kBf16) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 pb;
+    for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[i] = (__bf16)sc[2 * h][i];
-          pb[4 + i] = (__bf16)sc[2 * h + 1][i];
-        }
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int d = 0; d < kDB; ++d) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&vt[(16 * d + col) * kVs + 32 * h + 8 * grp]);
-          acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[d], 0, 0, 0);
+          const float a = vt[(16 * d + col) * kVs + 16 * sb + 4 * grp + i];
+          acc[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sc[sb][i], acc[d], 0, 0, 0);
         }
-      }
-    } else {
-#pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int d = 0; d < kDB; ++d) {
-            const float a = vt[(16 * d + col) * kVs + 16 * sb + 4 * grp + i];
-            acc[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sc[sb][i], acc[d], 0, 0, 0);
-          }
-    }
   }
 
-  // ---- epilogue ----
-  const float l_row = wave_sum_cols(l_lane);
+  float l_row = l_lane + __shfl_xor(l_lane, 16);
+  l_row += __shfl_xor(l_row, 32);
   if (!valid) return;
   if (it.slot < 0) {
     const float inv = 1.f / l_row;
-    T *op = out + ((int64_t)row * h_q + head) * D;
+    float *op = out + ((int64_t)row * h_q + head) * D;
 #pragma unroll
-    for (int d = 0; d < kDB; ++d) {
-      if constexpr (kBf16) {
-        bf16x4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (__bf16)(acc[d][i] * inv);
-        *reinterpret_cast<bf16x4 *>(op + 16 * d + 4 * grp) = o;
-      } else {
-        *reinterpret_cast<f32x4 *>(op + 16 * d + 4 * grp) = acc[d] * inv;
-      }
-    }
+    for (int d = 0; d < kDB; ++d) *reinterpret_cast<f32x4 *>(op + 16 * d + 4 * grp) = acc[d] * inv;
   } else {
     float *wo = ws_o + ((int64_t)it.slot * kM + m) * D;
 #pragma unroll
@@ -284,18 +414,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
   }
 }
 
+// ================================ merge ========================================
+
 // Combine the split partials of one (tile, kv head) with their log-sum-exp weights.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(
-    T *__restrict__ out, const int32_t *__restrict__ rows, const AttnTile *__restrict__ tiles,
-    const MergeEntry *__restrict__ merges, const float *__restrict__ ws_o,
-    const float *__restrict__ ws_ml, int h_q, int h_kv, int tile_rows) {
-  (void)rows;
+__global__ __launch_bounds__(256) void merge_kernel(
+    T *__restrict__ out, const AttnTile *__restrict__ tiles, const MergeEntry *__restrict__ merges,
+    const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int h_q, int h_kv,
+    int tile_rows) {
   const MergeEntry me = merges[blockIdx.x];
   const AttnTile tile = tiles[me.tile];
   const int group = h_q / h_kv;
-  constexpr int kC = D / 4;  // 4-wide chunks per query vector
-  for (int u = threadIdx.x; u < kM * kC; u += kThreads) {
+  constexpr int kC = D / 4;
+  for (int u = threadIdx.x; u < kM * kC; u += 256) {
     const int m = u / kC, c = u - m * kC;
     const int row_local = m % tile_rows;
     if (row_local >= tile.n_rows) continue;
@@ -336,14 +467,22 @@ int launch_attn(const PlanHeader &h, const int32_t *plan_dev, const void *q, con
   float *ws_o = static_cast<float *>(workspace);
   float *ws_ml = ws_o ? ws_o + (int64_t)h[PIC_H_N_PARTIALS] * kM * D : nullptr;
   const float scale_log2 = scale * kLog2e;
-  hipLaunchKernelGGL((attn_kernel<T, D>), dim3(h[PIC_H_N_ATTN_ITEMS]), dim3(kThreads), 0, s,
-                     static_cast<const T *>(q), static_cast<const T *>(k),
-                     static_cast<const T *>(v), static_cast<T *>(out), rows, tiles, items, ws_o,
-                     ws_ml, h[PIC_H_H_Q], h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], scale_log2);
+  const dim3 grid(h[PIC_H_N_ATTN_ITEMS]);
+  if constexpr (std::is_same<T, __bf16>::value) {
+    hipLaunchKernelGGL((attn_bf16_kernel<D>), grid, dim3(kBfThreads), 0, s,
+                       static_cast<const T *>(q), static_cast<const T *>(k),
+                       static_cast<const T *>(v), static_cast<T *>(out), rows, tiles, items,
+                       ws_o, ws_ml, h[PIC_H_H_Q], h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], scale_log2);
+  } else {
+    hipLaunchKernelGGL((attn_f32_kernel<D>), grid, dim3(kF32Threads), 0, s,
+                       static_cast<const T *>(q), static_cast<const T *>(k),
+                       static_cast<const T *>(v), static_cast<T *>(out), rows, tiles, items,
+                       ws_o, ws_ml, h[PIC_H_H_Q], h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], scale_log2);
+  }
   PIC_LAUNCH_CHECK();
   if (h[PIC_H_N_MERGE] > 0) {
-    hipLaunchKernelGGL((merge_kernel<T, D>), dim3(h[PIC_H_N_MERGE]), dim3(kThreads), 0, s,
-                       static_cast<T *>(out), rows, tiles, merges, ws_o, ws_ml, h[PIC_H_H_Q],
+    hipLaunchKernelGGL((merge_kernel<T, D>), dim3(h[PIC_H_N_MERGE]), dim3(256), 0, s,
+                       static_cast<T *>(out), tiles, merges, ws_o, ws_ml, h[PIC_H_H_Q],
                        h[PIC_H_H_KV], h[PIC_H_TILE_ROWS]);
     PIC_LAUNCH_CHECK();
   }

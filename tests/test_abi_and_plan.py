@@ -155,7 +155,7 @@ def check_plan(reqs, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0):
     assert got == want
 
     # attention tiles: every (row, head) once; items cover [0, p_last] of each tile
-    tile_rows = 64 // group
+    tile_rows = P.PIC_ATTN_TILE_M // group
     seen = set()
     for ti, (req, r0, n, tokb, pf, pl, _, _) in enumerate(plan.attn_tiles.tolist()):
         assert 1 <= n <= tile_rows and tokb == exp_tok[req]
