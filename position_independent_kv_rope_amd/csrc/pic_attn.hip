@@ -22,9 +22,11 @@
 // domain (scores scaled by scale * log2 e).
 //
 // bf16 kernel (the hot one): 4 waves x 32 queries, v_mfma_f32_32x32x16_bf16 for both
-// products, K/V blocks of 64 keys double-buffered in LDS (row-major, 16-byte coalesced
-// staging; the next block is loaded into registers while the current one is
-// computed), V read transposed for the PV operand with ds_read_b64_tr_b16.
+// products, K/V blocks of 64 keys double-buffered in LDS and staged by direct
+// buffer->LDS loads (the next block streams in while the current one is computed;
+// the buffer range clamps rows past the item's keys to zero), V read transposed for
+// the PV operand with ds_read_b64_tr_b16, row sums taken from the bf16 probabilities
+// with v_dot2_f32_bf16.
 // fp32 kernel: 8 waves x 16 queries, v_mfma_f32_16x16x4_f32 (fp32 operands, so fp32
 // I/O keeps fp32 accuracy), V staged transposed.
 #include <cmath>
@@ -53,6 +55,9 @@ constexpr int kBfWaves = 4;
 constexpr int kBfThreads = 64 * kBfWaves;
 static_assert(kM == 32 * kBfWaves, "one 32-query MFMA column block per wave");
 
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
 // Key (0..31 within a 32-key S^T tile t of the 64-key block) at C row r: rows held by
 // lane group g in accumulator slots 8h..8h+7 become keys 16(2t+h) + 8g + 0..7.
 __device__ __forceinline__ int perm_key(int t, int r) {
@@ -60,30 +65,49 @@ __device__ __forceinline__ int perm_key(int t, int r) {
   return 16 * (2 * t + (a >> 1)) + 8 * g + 4 * (a & 1) + b;
 }
 
+// LDS layouts: a staged block is 64 key rows of D bf16, rows unpadded, 16-byte chunks
+// XOR-swizzled per row so that the reads of one LDS cycle hit distinct banks.
+// K rows are read 16 at a time (rows {0..3, 8..11, 16..19, 24..27} + const, one chunk
+// each): the swizzle takes 16 distinct values over such a set.  V rows are read by the
+// transposing loads 4 consecutive rows at a time, two lane groups on adjacent chunk
+// pairs: XOR of chunk bits 2-3 by (row & 3) puts the four rows on four distinct
+// 64-byte bank groups.
+template <int kCPR>
+__device__ __forceinline__ int swz_k(int r) {
+  return ((r & 3) | (((r >> 3) & 3) << 2)) & (kCPR - 1);
+}
+template <int kCPR>
+__device__ __forceinline__ int swz_v(int r) {
+  return (4 * (r & 3)) & (kCPR - 1);
+}
+
 template <int D>
-__global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_kernel(
+__device__ __forceinline__ void attn_bf16_body(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ kbuf,
     const __bf16 *__restrict__ vbuf, __bf16 *__restrict__ out, const int32_t *__restrict__ rows,
     const AttnTile *__restrict__ tiles, const AttnItem *__restrict__ items,
     float *__restrict__ ws_o, float *__restrict__ ws_ml, int h_q, int h_kv, int tile_rows,
     float scale_log2) {
-  constexpr int kStride = D + 8;             // LDS row stride (elements): 16 B of padding
-  constexpr int kKS = D / 16;                // S^T contraction steps
-  constexpr int kDB = D / 32;                // 32-wide d blocks of O^T
-  constexpr int kUPR = D / 8;                // 16-byte units per key row
-  constexpr int kUPT = kKB * kUPR / kBfThreads;  // staged units per thread per tensor
-  static_assert(kUPT * kBfThreads == kKB * kUPR, "staging must tile the block");
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2][2][kKB * kStride];
+  constexpr int kRowB = D * 2;                 // bytes per staged key row
+  constexpr int kCPR = D / 8;                  // 16-byte chunks per row
+  constexpr int kTileB = kKB * kRowB;          // bytes of one staged K or V block
+  constexpr int kRPI = 1024 / kRowB;           // rows one wave fills per direct load
+  constexpr int kRounds = kKB / (kRPI * kBfWaves);  // direct loads per wave per tensor
+  constexpr int kKS = D / 16;                  // S^T contraction steps
+  constexpr int kDB = D / 32;                  // 32-wide d blocks of O^T
+  static_assert(kRounds * kRPI * kBfWaves == kKB, "direct loads must tile the block");
+  // [buffer 0: K, V][buffer 1: K, V]
+  __shared__ __attribute__((aligned(1024))) char lds[4 * kTileB];
 
   const AttnItem it = items[blockIdx.x];
   const AttnTile tile = tiles[it.tile];
   const int g = it.kv_head;
   const int group = h_q / h_kv;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31;     // query column of this lane
   const int grp = lane >> 5;   // lane group (0, 1)
-  const int q16 = lane >> 4;   // 16-lane group for the transposing LDS read
+  const int q16 = lane >> 4;   // 16-lane group of the transposing read
   const int i16 = lane & 15;
 
   const int m = 32 * wave + n;
@@ -115,43 +139,66 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_kernel(
   const int key_begin = it.key_begin;
   const int key_end = it.key_end;
   const int key_last = key_end - 1;
-  const int64_t tok_stride = (int64_t)h_kv * D;
-  const __bf16 *kbase = kbuf + (int64_t)tile.tok_base * tok_stride + (int64_t)g * D;
-  const __bf16 *vbase = vbuf + (int64_t)tile.tok_base * tok_stride + (int64_t)g * D;
+  const int tok_bytes = h_kv * D * 2;
 
-  u32x4 pk[kUPT], pv[kUPT];
-  auto load_block = [&](int kb0) {
+  // ---- direct global->LDS staging: buffer resources clamp rows >= key_end to zero ----
+  // (the resources are rebuilt where used: a lambda may not capture the resource type)
+  const int64_t head_off = ((int64_t)tile.tok_base * h_kv + g) * D;
+  const __bf16 *kh = kbuf + head_off;
+  const __bf16 *vh = vbuf + head_off;
+  const int n_records = key_end * tok_bytes;
+  int voff_k[kRounds], voff_v[kRounds];
 #pragma unroll
-    for (int r = 0; r < kUPT; ++r) {
-      const int u = threadIdx.x + kBfThreads * r;
-      const int key = u / kUPR, c = u - key * kUPR;
-      const int64_t at = (int64_t)min(kb0 + key, key_last) * tok_stride + 8 * c;
-      pk[r] = *reinterpret_cast<const u32x4 *>(kbase + at);
-      pv[r] = *reinterpret_cast<const u32x4 *>(vbase + at);
+  for (int r = 0; r < kRounds; ++r) {
+    const int R = kRPI * (kBfWaves * r + wave) + lane / kCPR;  // block row this lane fills
+    const int p = lane % kCPR;                                 // its physical chunk
+    voff_k[r] = R * tok_bytes + 16 * (p ^ swz_k<kCPR>(R));
+    voff_v[r] = R * tok_bytes + 16 * (p ^ swz_v<kCPR>(R));
+  }
+  auto issue_block = [&](int kb0, int buf) {
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void *)kh, 0, n_records, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void *)vh, 0, n_records, 0x00020000);
+    const int soff = kb0 * tok_bytes;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int dst = (2 * buf) * kTileB + (kBfWaves * r + wave) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(lds + dst), 16, voff_k[r], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(lds + dst + kTileB), 16, voff_v[r], soff, 0, 0);
     }
   };
-  auto store_block = [&](int b) {
+
+  // ---- loop-invariant LDS read offsets (bytes within a K or V block) ----
+  int koff[kKS];
+  {
+    const int r0 = perm_key(0, n);  // tile 1 is rows + 32, same swizzle
+    const int f = swz_k<kCPR>(r0);
 #pragma unroll
-    for (int r = 0; r < kUPT; ++r) {
-      const int u = threadIdx.x + kBfThreads * r;
-      const int key = u / kUPR, c = u - key * kUPR;
-      *reinterpret_cast<u32x4 *>(&lds[b][0][key * kStride + 8 * c]) = pk[r];
-      *reinterpret_cast<u32x4 *>(&lds[b][1][key * kStride + 8 * c]) = pv[r];
-    }
-  };
+    for (int s = 0; s < kKS; ++s) koff[s] = r0 * kRowB + 16 * ((2 * s + grp) ^ f);
+  }
+  int voff[kDB];
+  {
+    const int rr = 8 * (q16 >> 1) + (i16 >> 2);  // + 16c + 4h, which keeps rr & 3
+    const int f = swz_v<kCPR>(rr) >> 2;
+#pragma unroll
+    for (int d = 0; d < kDB; ++d)
+      voff[d] = rr * kRowB + 16 * (4 * (d ^ f) + 2 * (q16 & 1) + ((i16 & 3) >> 1)) +
+                8 * (i16 & 1);
+  }
 
   const int n_blocks = (key_end - key_begin + kKB - 1) / kKB;
-  load_block(key_begin);
-  store_block(0);
+  issue_block(key_begin, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int ib = 0; ib < n_blocks; ++ib) {
+  auto step = [&](int ib, auto bufc) {
+    constexpr int kBuf = decltype(bufc)::value;
     const int kb0 = key_begin + ib * kKB;
-    const int buf = ib & 1;
     const bool more = ib + 1 < n_blocks;
-    if (more) load_block(kb0 + kKB);
-    const __bf16 *Ks = lds[buf][0];
-    const __bf16 *Vs = lds[buf][1];
+    if (more) issue_block(kb0 + kKB, kBuf ^ 1);
+    const char *Kb = lds + (2 * kBuf) * kTileB;
+    const char *Vb = Kb + kTileB;
 
     // ---- S^T = K Q^T: two 32-key tiles ----
     f32x16 sc[2];
@@ -159,10 +206,9 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_kernel(
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) sc[t][j] = 0.f;
-      const __bf16 *kr = Ks + perm_key(t, n) * kStride + 8 * grp;
 #pragma unroll
       for (int s = 0; s < kKS; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kr + 16 * s);
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Kb + koff[s] + t * 32 * kRowB);
         sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], sc[t], 0, 0, 0);
       }
     }
@@ -178,7 +224,7 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_kernel(
         }
     }
 
-    // ---- online softmax (exp2 domain) ----
+    // ---- online softmax (exp2 domain); row sums from the bf16 probabilities ----
     float mx = kNegInf;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -190,17 +236,22 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_kernel(
     const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
     const float base = none ? 0.f : m_new;
     m_run = m_new;
-    float psum = 0.f;
     bf16x8 pb[4];
+    const bf16x2v ones = {(__bf16)1.f, (__bf16)1.f};
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[t][j], scale_log2, -base));
-        psum += p;
-        pb[2 * t + (j >> 3)][j & 7] = (__bf16)p;
+      for (int j = 0; j < 16; j += 2) {
+        bf16x2v pr;
+        pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][j], scale_log2, -base));
+        pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][j + 1], scale_log2, -base));
+        pb[2 * t + (j >> 3)][j & 7] = pr[0];
+        pb[2 * t + (j >> 3)][(j & 7) + 1] = pr[1];
+        if (j & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps1, false);
+        else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps0, false);
       }
-    l_lane = l_lane * alpha + psum;
+    l_lane = l_lane * alpha + (ps0 + ps1);
     if (wave_any(alpha != 1.f)) {
 #pragma unroll
       for (int d = 0; d < kDB; ++d) acc[d] *= alpha;
@@ -209,15 +260,11 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_kernel(
     // ---- O^T += V^T P^T (V^T operand via transposing LDS reads) ----
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      // source row of this lane for the transposing read: key 16c + 8*(q16/2) + i16/4 (+4)
-      const __bf16 *vr = Vs + (16 * c + 8 * (q16 >> 1) + (i16 >> 2)) * kStride +
-                         16 * (q16 & 1) + 4 * (i16 & 3);
 #pragma unroll
       for (int d = 0; d < kDB; ++d) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4 *)(vr + 32 * d));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4 *)(vr + 4 * kStride + 32 * d));
+        const char *vr = Vb + voff[d] + c * 16 * kRowB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vr);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 4 * kRowB));
         bf16x8 a;
         __builtin_memcpy(&a, &lo, 8);
         __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &hi, 8);
@@ -225,8 +272,13 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_kernel(
       }
     }
 
-    if (more) store_block(buf ^ 1);
+    if (more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  for (int ib = 0; ib < n_blocks; ib += 2) {
+    step(ib, std::integral_constant<int, 0>{});
+    if (ib + 1 < n_blocks) step(ib + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue ----
@@ -260,6 +312,17 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_kernel(
       ws_ml[((int64_t)it.slot * kM + m) * 2 + 1] = l_row;
     }
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ kbuf,
+    const __bf16 *__restrict__ vbuf, __bf16 *__restrict__ out, const int32_t *__restrict__ rows,
+    const AttnTile *__restrict__ tiles, const AttnItem *__restrict__ items,
+    float *__restrict__ ws_o, float *__restrict__ ws_ml, int h_q, int h_kv, int tile_rows,
+    float scale_log2) {
+  attn_bf16_body<D>(q, kbuf, vbuf, out, rows, tiles, items, ws_o, ws_ml, h_q, h_kv, tile_rows,
+                    scale_log2);
 }
 
 // ================================ fp32 kernel ==================================

@@ -9,9 +9,10 @@
 //   * attention tiles: PIC_ATTN_TILE_M (row, head) pairs = PIC_ATTN_TILE_M / G
 //     consecutive recomputed rows of one request times the G query heads of a KV head;
 //   * attention items: (tile, kv head, key range); long tiles are split along keys so
-//     the grid fills the GPU, ordered longest first (the LPT rule HYPIC uses to balance
-//     its segment workers, section 2.3), and each split writes a partial result that a
-//     merge pass combines.
+//     the grid fills the GPU, and each split writes a partial result that a merge pass
+//     combines.  Items are dispatched longest first (the LPT rule HYPIC uses to balance
+//     its segment workers, section 2.3) within each XCD, with the items that share K/V
+//     kept on one XCD (see xcd_order).
 #include <algorithm>
 #include <cstring>
 #include <numeric>
@@ -24,8 +25,77 @@ namespace {
 constexpr int64_t kMaxI32 = 0x7fffffff;
 constexpr int32_t kKeyAlign = 64;       // attention key block
 constexpr int32_t kMinSplitKeys = 2048;  // smallest key range worth a partial result
+constexpr int kXcd = 8;                  // MI355X dies with a private L2 each
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Dispatch order of the attention items for a GPU whose consecutive workgroups go
+// round-robin to n_xcd dies, each with its own L2 (MI355X: 8 XCDs).  Items that read
+// the same K/V (same request and KV head: a "stream") are kept on one die so they
+// share its L2: streams are assigned to dies greedily by total cost (largest first,
+// to the least loaded die), each die's items run longest first (LPT), and position i
+// of the launch takes the next item of die i % n_xcd.  When a die runs out, the
+// remaining items fill its positions in LPT order.
+std::vector<pic::AttnItem> xcd_order(std::vector<pic::AttnItem> items,
+                                     const std::vector<pic::AttnTile> &tiles, int n_xcd) {
+  using pic::AttnItem;
+  auto len = [](const AttnItem &a) { return (int64_t)a.key_end - a.key_begin; };
+  std::stable_sort(items.begin(), items.end(),
+                   [&](const AttnItem &a, const AttnItem &b) { return len(a) > len(b); });
+  if (n_xcd <= 1 || items.size() < 2) return items;
+  // stream id = (request, kv head)
+  std::vector<int64_t> key(items.size());
+  std::vector<std::pair<int64_t, int64_t>> cost;  // (stream, cost)
+  {
+    std::vector<int64_t> ids;
+    for (size_t i = 0; i < items.size(); ++i) {
+      key[i] = (int64_t)tiles[items[i].tile].req * 65536 + items[i].kv_head;
+      ids.push_back(key[i]);
+    }
+    std::sort(ids.begin(), ids.end());
+    ids.erase(std::unique(ids.begin(), ids.end()), ids.end());
+    cost.resize(ids.size());
+    for (size_t s = 0; s < ids.size(); ++s) cost[s] = {ids[s], 0};
+    for (size_t i = 0; i < items.size(); ++i) {
+      auto it = std::lower_bound(ids.begin(), ids.end(), key[i]);
+      cost[it - ids.begin()].second += len(items[i]);
+    }
+  }
+  std::vector<size_t> order(cost.size());
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](size_t a, size_t b) { return cost[a].second > cost[b].second; });
+  std::vector<int64_t> load(n_xcd, 0);
+  std::vector<std::pair<int64_t, int>> die_of;  // (stream, die)
+  for (size_t s : order) {
+    const int d = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    load[d] += cost[s].second;
+    die_of.push_back({cost[s].first, d});
+  }
+  std::sort(die_of.begin(), die_of.end());
+  std::vector<std::vector<AttnItem>> per_die(n_xcd);
+  for (size_t i = 0; i < items.size(); ++i) {  // items are already longest first
+    auto it = std::lower_bound(die_of.begin(), die_of.end(), std::make_pair(key[i], -1));
+    per_die[it->second].push_back(items[i]);
+  }
+  std::vector<AttnItem> out;
+  out.reserve(items.size());
+  std::vector<size_t> next(n_xcd, 0);
+  for (size_t pos = 0; out.size() < items.size(); ++pos) {
+    int d = (int)(pos % n_xcd);
+    if (next[d] >= per_die[d].size()) {
+      // this die is done: take the longest remaining item of any die
+      int best = -1;
+      for (int e = 0; e < n_xcd; ++e)
+        if (next[e] < per_die[e].size() &&
+            (best < 0 || len(per_die[e][next[e]]) > len(per_die[best][next[best]])))
+          best = e;
+      d = best;
+    }
+    out.push_back(per_die[d][next[d]++]);
+  }
+  return out;
+}
 
 }  // namespace
 
@@ -165,10 +235,7 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
     }
     if (n_partials > kMaxI32 / 2) return PIC_EINVAL;
   }
-  // longest first; ties keep (tile, head, split) order so the schedule is deterministic
-  std::stable_sort(items.begin(), items.end(), [](const AttnItem &a, const AttnItem &b) {
-    return (a.key_end - a.key_begin) > (b.key_end - b.key_begin);
-  });
+  items = xcd_order(std::move(items), tiles, kXcd);
 
   // ---- layout of the plan ----
   int64_t words = PIC_PLAN_HEADER_WORDS;

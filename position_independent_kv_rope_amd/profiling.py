@@ -1,0 +1,115 @@
+"""Summaries of rocprofv3 output for the kernels of libpic.so.
+
+    python -m position_independent_kv_rope_amd.profiling stats <kernel_stats.csv>
+    python -m position_independent_kv_rope_amd.profiling counters <counter_collection.csv> ...
+    python -m position_independent_kv_rope_amd.profiling traffic \
+        --fetch <bench FETCH_SIZE csv> --write <bench WRITE_SIZE csv> \
+        --copy-fetch <copy FETCH_SIZE csv> --copy-write <copy WRITE_SIZE csv> \
+        --kernel attn_bf16_kernel --out profiles/traffic_attn_<workload>.json \
+        --sources position_independent_kv_rope_amd/csrc/pic_attn.hip
+
+``traffic`` scales the per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of a kernel by
+what the same counters read for a plain device copy of known size, and records the
+sha256 of the kernel sources so a stale measurement is not reused after a change.
+"""
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SHORT = [("attn_bf16_kernel", "attn_bf16"), ("attn_f32_kernel", "attn_f32"),
+         ("merge_kernel", "merge"), ("rope_delta_kernel", "rope_delta"),
+         ("splice_kernel", "splice"), ("copyBuffer", "copy (calibration)")]
+
+
+def short_name(name):
+    for key, s in SHORT:
+        if key in name:
+            return s
+    return name[:48]
+
+
+def read_csv(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def kernel_stats(path):
+    out = []
+    for r in read_csv(path):
+        out.append({"kernel": short_name(r["Name"]), "calls": int(r["Calls"]),
+                    "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
+                    "max_us": float(r["MaxNs"]) / 1e3, "pct": float(r["Percentage"])})
+    return out
+
+
+def counters(paths):
+    """Mean per dispatch of every counter, per kernel."""
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for p in paths:
+        for r in read_csv(p):
+            agg[short_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
+
+
+def src_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(args):
+    fetch = counters([args.fetch])
+    write = counters([args.write])
+    cf = counters([args.copy_fetch])["copy (calibration)"]["FETCH_SIZE"]
+    cw = counters([args.copy_write])["copy (calibration)"]["WRITE_SIZE"]
+    copy_kib = args.copy_bytes / 1024.0
+    f_scale, w_scale = copy_kib / cf, copy_kib / cw
+    k = short_name(args.kernel)
+    fb = fetch[k]["FETCH_SIZE"] * f_scale * 1024.0
+    wb = write[k]["WRITE_SIZE"] * w_scale * 1024.0
+    rec = {"kernel": k, "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+           "bytes_per_launch": fb + wb, "fetch_scale": f_scale, "write_scale": w_scale,
+           "copy_bytes": args.copy_bytes, "sources": args.sources,
+           "source_hash": src_hash(args.sources), "command": args.command}
+    with open(args.out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    t = sub.add_parser("traffic")
+    for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--out"):
+        t.add_argument(a, required=True)
+    t.add_argument("--copy-bytes", type=float, default=float(1 << 30))
+    t.add_argument("--sources", nargs="+", default=["position_independent_kv_rope_amd/csrc/pic_attn.hip"])
+    t.add_argument("--command", default="")
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        print("| kernel | calls | avg us | min us | max us | % time |")
+        print("|---|---|---|---|---|---|")
+        for r in kernel_stats(a.csv):
+            print("| %s | %d | %.1f | %.1f | %.1f | %.2f |" % (r["kernel"], r["calls"], r["avg_us"],
+                                                             r["min_us"], r["max_us"], r["pct"]))
+    elif a.cmd == "counters":
+        for k, cs in counters(a.csv).items():
+            print("%s: %s" % (k, ", ".join("%s=%.6g" % kv for kv in sorted(cs.items()))))
+    else:
+        traffic(a)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
