@@ -23,8 +23,9 @@
 //
 // bf16 kernel (the hot one): 4 waves x 32 queries, v_mfma_f32_32x32x16_bf16 for both
 // products, K/V blocks of 64 keys double-buffered in LDS and staged by direct
-// buffer->LDS loads (the next block streams in while the current one is computed;
-// the buffer range clamps rows past the item's keys to zero), V read transposed for
+// buffer->LDS loads (the buffer range clamps rows past the item's keys to zero), K
+// one block ahead of V so that S^T of block i+1 is computed while block i's softmax
+// runs (software pipelining inside each wave), V read transposed for
 // the PV operand with ds_read_b64_tr_b16, row sums taken from the bf16 probabilities
 // with v_dot2_f32_bf16.
 // fp32 kernel: 8 waves x 16 queries, v_mfma_f32_16x16x4_f32 (fp32 operands, so fp32
@@ -96,6 +97,7 @@ __device__ __forceinline__ void attn_bf16_body(
   constexpr int kKS = D / 16;                  // S^T contraction steps
   constexpr int kDB = D / 32;                  // 32-wide d blocks of O^T
   static_assert(kRounds * kRPI * kBfWaves == kKB, "direct loads must tile the block");
+  static_assert(2 * kKS <= 16, "S^T MFMAs of a block must fit the 16 exponential pairs");
   // [buffer 0: K, V][buffer 1: K, V]
   __shared__ __attribute__((aligned(1024))) char lds[4 * kTileB];
 
@@ -155,17 +157,16 @@ __device__ __forceinline__ void attn_bf16_body(
     voff_k[r] = R * tok_bytes + 16 * (p ^ swz_k<kCPR>(R));
     voff_v[r] = R * tok_bytes + 16 * (p ^ swz_v<kCPR>(R));
   }
-  auto issue_block = [&](int kb0, int buf) {
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void *)kh, 0, n_records, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void *)vh, 0, n_records, 0x00020000);
+  // LDS: K blocks in buffers 0/1, V blocks in buffers 2/3.  K is staged one block
+  // ahead of V so that S^T of block i+1 can be computed while block i's softmax runs.
+  auto issue = [&](const __bf16 *base, const int (&voffs)[kRounds], int kb0, int buf) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, n_records, 0x00020000);
     const int soff = kb0 * tok_bytes;
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
-      const int dst = (2 * buf) * kTileB + (kBfWaves * r + wave) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(lds + dst), 16, voff_k[r], soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(lds + dst + kTileB), 16, voff_v[r], soff, 0, 0);
+      const int dst = buf * kTileB + (kBfWaves * r + wave) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16, voffs[r], soff, 0, 0);
     }
   };
 
@@ -187,21 +188,8 @@ __device__ __forceinline__ void attn_bf16_body(
                 8 * (i16 & 1);
   }
 
-  const int n_blocks = (key_end - key_begin + kKB - 1) / kKB;
-  issue_block(key_begin, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  auto step = [&](int ib, auto bufc) {
-    constexpr int kBuf = decltype(bufc)::value;
-    const int kb0 = key_begin + ib * kKB;
-    const bool more = ib + 1 < n_blocks;
-    if (more) issue_block(kb0 + kKB, kBuf ^ 1);
-    const char *Kb = lds + (2 * kBuf) * kTileB;
-    const char *Vb = Kb + kTileB;
-
-    // ---- S^T = K Q^T: two 32-key tiles ----
-    f32x16 sc[2];
+  // S^T = K Q^T for the two 32-key tiles of the block in K buffer kb.
+  auto qk = [&](const char *Kb, f32x16 (&sc)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -212,8 +200,17 @@ __device__ __forceinline__ void attn_bf16_body(
         sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], sc[t], 0, 0, 0);
       }
     }
+  };
 
-    // ---- causal mask, only where a key can pass a column's position ----
+  // Mask, online softmax and O^T += V^T P^T for the block starting at key kb0; S^T of
+  // the next block (K buffer Knext) is computed into s_nxt meanwhile, its 16 MFMAs
+  // interleaved with the 32 exponentials (after the last block the result is unused).  The running max m_run is only moved when a
+  // column's block max exceeds it by more than kLazy (log2 units), so rescaling the
+  // accumulators is rare; probabilities then stay below 2^kLazy, far inside fp32/bf16
+  // range, and the final normalisation is unchanged (acc and l share the reference).
+  auto softmax_pv = [&](f32x16 (&sc)[2], int kb0, const char *Vb, const char *Knext,
+                        f32x16 (&s_nxt)[2]) {
+    constexpr float kLazy = 8.f;
     if (kb0 + kKB - 1 > min(pos_min, key_last)) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -223,41 +220,53 @@ __device__ __forceinline__ void attn_bf16_body(
           if (key > pos || key > key_last) sc[t][j] = kNegInf;
         }
     }
-
-    // ---- online softmax (exp2 domain); row sums from the bf16 probabilities ----
     float mx = kNegInf;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[t][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
-    const bool none = m_new == kNegInf;
-    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    const float base = none ? 0.f : m_new;
-    m_run = m_new;
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    const bool upd = mx > m_run + kLazy;  // false while everything seen is masked
+    if (wave_any(upd)) {
+      const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+      m_run = upd ? mx : m_run;
+      l_lane *= alpha;
+#pragma unroll
+      for (int d = 0; d < kDB; ++d) acc[d] *= alpha;
+    }
+    const float base = m_run == kNegInf ? 0.f : m_run;
+
     bf16x8 pb[4];
     const bf16x2v ones = {(__bf16)1.f, (__bf16)1.f};
     float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        bf16x2v pr;
-        pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][j], scale_log2, -base));
-        pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][j + 1], scale_log2, -base));
-        pb[2 * t + (j >> 3)][j & 7] = pr[0];
-        pb[2 * t + (j >> 3)][(j & 7) + 1] = pr[1];
-        if (j & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps1, false);
-        else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps0, false);
-      }
-    l_lane = l_lane * alpha + (ps0 + ps1);
-    if (wave_any(alpha != 1.f)) {
+      for (int j = 0; j < 16; ++j) s_nxt[t][j] = 0.f;
 #pragma unroll
-      for (int d = 0; d < kDB; ++d) acc[d] *= alpha;
+    for (int q = 0; q < 16; ++q) {
+      if (q < 2 * kKS) {  // S^T MFMAs of the next block, one per pair; tiles alternate
+        const int t = q & 1, s = q >> 1;
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Knext + koff[s] + t * 32 * kRowB);
+        s_nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], s_nxt[t], 0, 0, 0);
+      }
+      const int t = q >> 3, j = 2 * (q & 7);
+      bf16x2v pr;
+      pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][j], scale_log2, -base));
+      pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][j + 1], scale_log2, -base));
+      pb[2 * t + (j >> 3)][j & 7] = pr[0];
+      pb[2 * t + (j >> 3)][(j & 7) + 1] = pr[1];
+      if (j & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps1, false);
+      else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps0, false);
     }
-
-    // ---- O^T += V^T P^T (V^T operand via transposing LDS reads) ----
+    // keep the schedule interleaved: per pair, its K read, one MFMA, the VALU work
+#pragma unroll
+    for (int q = 0; q < 2 * kKS; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+    }
+    l_lane += ps0 + ps1;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -271,14 +280,35 @@ __device__ __forceinline__ void attn_bf16_body(
         acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[d], 0, 0, 0);
       }
     }
+  };
 
-    if (more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  const int n_blocks = (key_end - key_begin + kKB - 1) / kKB;
+  issue(kh, voff_k, key_begin, 0);
+  issue(vh, voff_v, key_begin, 2);
+  if (n_blocks > 1) issue(kh, voff_k, key_begin + kKB, 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  qk(lds, sa);
+  __syncthreads();  // K buffer 0 is refilled next
+
+  // Block ib: S^T(ib) is in registers; stage K(ib+2) and V(ib+1), compute S^T(ib+1),
+  // then the softmax and PV of block ib.  kB = ib & 1 selects the buffers.
+  auto step = [&](int ib, auto bufc, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+    constexpr int kB = decltype(bufc)::value;
+    const int kb0 = key_begin + ib * kKB;
+    if (ib + 2 < n_blocks) issue(kh, voff_k, kb0 + 2 * kKB, kB);
+    if (ib + 1 < n_blocks) issue(vh, voff_v, kb0 + kKB, 2 + (kB ^ 1));
+    softmax_pv(s_cur, kb0, lds + (2 + kB) * kTileB, lds + (kB ^ 1) * kTileB, s_nxt);
+    if (ib + 1 < n_blocks) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
   };
 
   for (int ib = 0; ib < n_blocks; ib += 2) {
-    step(ib, std::integral_constant<int, 0>{});
-    if (ib + 1 < n_blocks) step(ib + 1, std::integral_constant<int, 1>{});
+    step(ib, std::integral_constant<int, 0>{}, sa, sb);
+    if (ib + 1 < n_blocks) step(ib + 1, std::integral_constant<int, 1>{}, sb, sa);
   }
 
   // ---- epilogue ----

@@ -26,6 +26,7 @@ constexpr int64_t kMaxI32 = 0x7fffffff;
 constexpr int32_t kKeyAlign = 64;       // attention key block
 constexpr int32_t kMinSplitKeys = 2048;  // smallest key range worth a partial result
 constexpr int kXcd = 8;                  // MI355X dies with a private L2 each
+constexpr int64_t kSegKeys = 8192;       // longest split-KV segment
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -33,9 +34,9 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // round-robin to n_xcd dies, each with its own L2 (MI355X: 8 XCDs).  Items that read
 // the same K/V (same request and KV head: a "stream") are kept on one die so they
 // share its L2: streams are assigned to dies greedily by total cost (largest first,
-// to the least loaded die), each die's items run longest first (LPT), and position i
-// of the launch takes the next item of die i % n_xcd.  When a die runs out, the
-// remaining items fill its positions in LPT order.
+// to the least loaded die), each die runs its items segment by segment, and position
+// i of the launch takes the next item of die i % n_xcd.  When a die runs out, the
+// remaining items fill its positions, longest first.
 std::vector<pic::AttnItem> xcd_order(std::vector<pic::AttnItem> items,
                                      const std::vector<pic::AttnTile> &tiles, int n_xcd) {
   using pic::AttnItem;
@@ -74,9 +75,27 @@ std::vector<pic::AttnItem> xcd_order(std::vector<pic::AttnItem> items,
   }
   std::sort(die_of.begin(), die_of.end());
   std::vector<std::vector<AttnItem>> per_die(n_xcd);
-  for (size_t i = 0; i < items.size(); ++i) {  // items are already longest first
+  std::vector<std::vector<int64_t>> per_die_key(n_xcd);
+  for (size_t i = 0; i < items.size(); ++i) {
     auto it = std::lower_bound(die_of.begin(), die_of.end(), std::make_pair(key[i], -1));
     per_die[it->second].push_back(items[i]);
+    per_die_key[it->second].push_back(key[i]);
+  }
+  // within a die: segment-major (key_begin), then stream, then longest first, so the
+  // items that read the same K/V rows run side by side
+  for (int d = 0; d < n_xcd; ++d) {
+    std::vector<size_t> idx(per_die[d].size());
+    std::iota(idx.begin(), idx.end(), 0);
+    const auto &v = per_die[d];
+    const auto &kk = per_die_key[d];
+    std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) {
+      if (v[a].key_begin != v[b].key_begin) return v[a].key_begin < v[b].key_begin;
+      if (kk[a] != kk[b]) return kk[a] < kk[b];
+      return len(v[a]) > len(v[b]);
+    });
+    std::vector<AttnItem> sorted;
+    for (size_t i : idx) sorted.push_back(v[i]);
+    per_die[d].swap(sorted);
   }
   std::vector<AttnItem> out;
   out.reserve(items.size());
@@ -201,30 +220,32 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
     }
   }
 
-  // ---- split-KV sizing: aim for items no longer than half a fair share per slot ----
+  // ---- split-KV sizing ----
+  // Keys are split on a global grid of seg_len keys.  All tiles of one (request, kv
+  // head) stream that reach a grid segment read the same K/V rows there; dispatched
+  // together on one XCD they stream those rows in lockstep, so the XCD's L2 serves
+  // the re-reads.  seg_len is also capped so that small batches still fill the GPU
+  // (items no longer than half a fair share per workgroup slot).
   int64_t total_cost = 0;
   for (const AttnTile &t : tiles) total_cost += (int64_t)(t.p_last + 1) * h_kv;
   const int64_t slots = (int64_t)n_cu * 2;
-  int64_t split_len = std::max<int64_t>(kMinSplitKeys, total_cost / std::max<int64_t>(1, slots * 2));
-  split_len = round_up(split_len, kKeyAlign);
+  int64_t seg_len = std::max<int64_t>(kMinSplitKeys, total_cost / std::max<int64_t>(1, slots * 2));
+  seg_len = round_up(std::min<int64_t>(seg_len, kSegKeys), kKeyAlign);
 
   std::vector<AttnItem> items;
   std::vector<MergeEntry> merges;
   int64_t n_partials = 0;
   for (int32_t ti = 0; ti < (int32_t)tiles.size(); ++ti) {
     const int64_t keys = (int64_t)tiles[ti].p_last + 1;
-    int64_t n_split = (keys + split_len - 1) / split_len;
-    if (n_split < 1) n_split = 1;
-    const int64_t span = round_up((keys + n_split - 1) / n_split, kKeyAlign);
-    n_split = (keys + span - 1) / span;
+    const int64_t n_split = (keys + seg_len - 1) / seg_len;
     for (int32_t g = 0; g < h_kv; ++g) {
       const int64_t slot_base = n_partials;
       for (int64_t s = 0; s < n_split; ++s) {
         AttnItem it{};
         it.tile = ti;
         it.kv_head = g;
-        it.key_begin = (int32_t)(s * span);
-        it.key_end = (int32_t)std::min<int64_t>(keys, (s + 1) * span);
+        it.key_begin = (int32_t)(s * seg_len);
+        it.key_end = (int32_t)std::min<int64_t>(keys, (s + 1) * seg_len);
         it.slot = n_split > 1 ? (int32_t)(slot_base + s) : -1;
         items.push_back(it);
       }

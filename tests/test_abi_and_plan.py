@@ -189,12 +189,12 @@ def check_plan(reqs, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0):
     for tile, g, base, n in merges:
         assert sorted(s for _, _, s in cover[(tile, g)]) == list(range(base, base + n))
     assert plan[P.H_N_PARTIALS] == len(slots)
-    # dispatch order: items of one (request, kv head) stream run longest first
+    # dispatch order: items of one (request, kv head) stream run segment by segment
     streams = {}
     for tile, g, kb, ke, _, _, _, _ in plan.attn_items.tolist():
-        streams.setdefault((tiles[tile][0], g), []).append(ke - kb)
-    for lengths in streams.values():
-        assert lengths == sorted(lengths, reverse=True)
+        streams.setdefault((tiles[tile][0], g), []).append(kb)
+    for begins in streams.values():
+        assert begins == sorted(begins)
     return plan
 
 
