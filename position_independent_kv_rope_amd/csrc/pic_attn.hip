@@ -30,6 +30,7 @@
 // with v_dot2_f32_bf16.
 // fp32 kernel: 8 waves x 16 queries, v_mfma_f32_16x16x4_f32 (fp32 operands, so fp32
 // I/O keeps fp32 accuracy), V staged transposed.
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -267,6 +268,7 @@ __device__ __forceinline__ void attn_bf16_body(
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
     }
     l_lane += ps0 + ps1;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -280,6 +282,7 @@ __device__ __forceinline__ void attn_bf16_body(
         acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[d], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   const int n_blocks = (key_end - key_begin + kKB - 1) / kKB;
@@ -509,33 +512,45 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(
 
 // ================================ merge ========================================
 
-// Combine the split partials of one (tile, kv head) with their log-sum-exp weights.
+// Combine the split partials of each (tile, kv head) with their log-sum-exp weights:
+// one thread per (merge entry, query vector, 4 output dims), a single pass over the
+// slots with an online maximum.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(
     T *__restrict__ out, const AttnTile *__restrict__ tiles, const MergeEntry *__restrict__ merges,
     const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int h_q, int h_kv,
-    int tile_rows) {
-  const MergeEntry me = merges[blockIdx.x];
-  const AttnTile tile = tiles[me.tile];
-  const int group = h_q / h_kv;
+    int tile_rows, int n_merge) {
   constexpr int kC = D / 4;
-  for (int u = threadIdx.x; u < kM * kC; u += 256) {
-    const int m = u / kC, c = u - m * kC;
+  const int group = h_q / h_kv;
+  const int64_t total = (int64_t)n_merge * kM * kC;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total;
+       u += (int64_t)gridDim.x * 256) {
+    const int e = (int)(u / (kM * kC));
+    const int rem = (int)(u - (int64_t)e * (kM * kC));
+    const int m = rem / kC, c = rem - m * kC;
+    const MergeEntry me = merges[e];
+    const AttnTile tile = tiles[me.tile];
     const int row_local = m % tile_rows;
     if (row_local >= tile.n_rows) continue;
     const int head = me.kv_head * group + m / tile_rows;
-    float mmax = kNegInf;
-    for (int s = 0; s < me.n_slots; ++s)
-      mmax = fmaxf(mmax, ws_ml[((int64_t)(me.slot_base + s) * kM + m) * 2]);
-    float den = 0.f;
+    float mmax = kNegInf, den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int s = 0; s < me.n_slots; ++s) {
       const int64_t at = (int64_t)(me.slot_base + s) * kM + m;
       const float ms = ws_ml[at * 2];
+      const float ls = ws_ml[at * 2 + 1];
+      const f32x4 os = *reinterpret_cast<const f32x4 *>(ws_o + at * D + 4 * c);
       if (ms == kNegInf) continue;
+      if (ms > mmax) {
+        const float r = __builtin_amdgcn_exp2f(mmax - ms);  // 0 when mmax is -inf
+        den *= r;
+        num *= r;
+        mmax = ms;
+      }
       const float w = __builtin_amdgcn_exp2f(ms - mmax);
-      den += w * ws_ml[at * 2 + 1];
-      num += w * *reinterpret_cast<const f32x4 *>(ws_o + at * D + 4 * c);
+      den += w * ls;
+      num += w * os;
     }
     const float inv = 1.f / den;
     T *op = out + ((int64_t)(tile.row_begin + row_local) * h_q + head) * D + 4 * c;
@@ -574,9 +589,11 @@ int launch_attn(const PlanHeader &h, const int32_t *plan_dev, const void *q, con
   }
   PIC_LAUNCH_CHECK();
   if (h[PIC_H_N_MERGE] > 0) {
-    hipLaunchKernelGGL((merge_kernel<T, D>), dim3(h[PIC_H_N_MERGE]), dim3(256), 0, s,
+    const int64_t threads = (int64_t)h[PIC_H_N_MERGE] * kM * (D / 4);
+    const unsigned blocks = (unsigned)std::min<int64_t>((threads + 255) / 256, 1 << 20);
+    hipLaunchKernelGGL((merge_kernel<T, D>), dim3(blocks), dim3(256), 0, s,
                        static_cast<T *>(out), tiles, merges, ws_o, ws_ml, h[PIC_H_H_Q],
-                       h[PIC_H_H_KV], h[PIC_H_TILE_ROWS]);
+                       h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], h[PIC_H_N_MERGE]);
     PIC_LAUNCH_CHECK();
   }
   return PIC_OK;

@@ -2,6 +2,9 @@
 
     python -m position_independent_kv_rope_amd.profiling stats <kernel_stats.csv>
     python -m position_independent_kv_rope_amd.profiling counters <counter_collection.csv> ...
+    python -m position_independent_kv_rope_amd.profiling report --kernel attn_bf16 \
+        --stats <kernel_stats.csv> --counters <csv> ... --copy-fetch <csv> --copy-write <csv> \
+        --algo-bytes B --algo-flops F --title T --cmdline "..." [--cmdline "..."]
     python -m position_independent_kv_rope_amd.profiling traffic \
         --fetch <bench FETCH_SIZE csv> --write <bench WRITE_SIZE csv> \
         --copy-fetch <copy FETCH_SIZE csv> --copy-write <copy WRITE_SIZE csv> \
@@ -84,6 +87,51 @@ def traffic(args):
     print(json.dumps(rec, indent=1))
 
 
+def report(args):
+    """Markdown summary of one kernel: trace statistics, counters, scaled HBM traffic."""
+    stats = {r["kernel"]: r for r in kernel_stats(args.stats)}
+    cs = counters(args.counters)
+    k = short_name(args.kernel)
+    st = stats[k]
+    c = cs.get(k, {})
+    copy_kib = float(1 << 30) / 1024.0
+    f_scale = copy_kib / counters([args.copy_fetch])["copy (calibration)"]["FETCH_SIZE"]
+    w_scale = copy_kib / counters([args.copy_write])["copy (calibration)"]["WRITE_SIZE"]
+    out = ["# %s" % args.title, "", "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", ""]
+    out += ["    " + cl for cl in args.cmdlines]
+    out += ["", "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+            "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in kernel_stats(args.stats):
+        out.append("| %s | %d | %.1f | %.1f | %.1f | %.2f |" % (r["kernel"], r["calls"], r["avg_us"],
+                                                                 r["min_us"], r["max_us"], r["pct"]))
+    avg_s = st["avg_us"] * 1e-6
+    out += ["", "## %s per launch" % k, ""]
+    if args.algo_flops:
+        out.append("- algorithmic flops: %.4g -> %.1f TFLOP/s at the average duration" %
+                   (args.algo_flops, args.algo_flops / avg_s / 1e12))
+    if args.algo_bytes:
+        out.append("- algorithmic bytes: %.4g -> %.1f GB/s at the average duration" %
+                   (args.algo_bytes, args.algo_bytes / avg_s / 1e9))
+    if "FETCH_SIZE" in c:
+        fb = c["FETCH_SIZE"] * f_scale * 1024
+        wb = c.get("WRITE_SIZE", 0.0) * w_scale * 1024
+        out.append("- HBM traffic from counters: fetch %.4g B + write %.4g B = %.4g B "
+                   "(FETCH_SIZE x %.3f, WRITE_SIZE x %.3f, factors from a 1 GiB device copy)"
+                   % (fb, wb, fb + wb, f_scale, w_scale))
+        if args.algo_bytes:
+            out.append("- counter traffic / algorithmic bytes: %.2f" % ((fb + wb) / args.algo_bytes))
+    if "TCC_HIT" in c and "TCC_MISS" in c:
+        out.append("- L2 hit rate: %.1f%%" % (100.0 * c["TCC_HIT"] / (c["TCC_HIT"] + c["TCC_MISS"])))
+    if c:
+        out += ["", "Raw counters (mean per dispatch): " +
+                ", ".join("%s=%.6g" % kv for kv in sorted(c.items()))]
+    text = "\n".join(out) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -97,6 +145,17 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=float, default=float(1 << 30))
     t.add_argument("--sources", nargs="+", default=["position_independent_kv_rope_amd/csrc/pic_attn.hip"])
     t.add_argument("--command", default="")
+    r = sub.add_parser("report")
+    r.add_argument("--kernel", required=True)
+    r.add_argument("--stats", required=True)
+    r.add_argument("--counters", nargs="*", default=[])
+    r.add_argument("--copy-fetch", required=True)
+    r.add_argument("--copy-write", required=True)
+    r.add_argument("--algo-bytes", type=float, default=0.0)
+    r.add_argument("--algo-flops", type=float, default=0.0)
+    r.add_argument("--title", required=True)
+    r.add_argument("--cmdline", action="append", dest="cmdlines", default=[])
+    r.add_argument("--out", default="")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print("| kernel | calls | avg us | min us | max us | % time |")
@@ -107,6 +166,8 @@ def main(argv=None):
     elif a.cmd == "counters":
         for k, cs in counters(a.csv).items():
             print("%s: %s" % (k, ", ".join("%s=%.6g" % kv for kv in sorted(cs.items()))))
+    elif a.cmd == "report":
+        report(a)
     else:
         traffic(a)
 
