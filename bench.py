@@ -215,7 +215,8 @@ def main():
         "splice_pass_tokens_per_s": round(tokens / ((t_rope + t_splice) * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
-                     "traffic": traffic, "kernel": "selective_attn (+merge)",
+                     "traffic": traffic,
+                     "kernel": "pic_selective_attn call (attn_bf16_kernel + merge_kernel)",
                      "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes},
         "kernels": {
             "rope_delta": {"ms": round(t_rope, 4), "bytes": rope_bytes,

@@ -436,3 +436,20 @@ def test_planted_k_off_by_one_is_caught():
     g = _golden("worked_example.json")
     assert O.recompute_positions(g["chunk_lens"], g["q_len"], g["k"] + 1) != g["recompute_positions"]
     assert O.recompute_positions(g["chunk_lens"], g["q_len"], g["k"] - 1) != g["recompute_positions"]
+
+
+def test_attn_rows_direct_matches_selective_attn():
+    # the one-row-at-a-time form used for sampled parity at full size is the same
+    # definition as the run-based selective_attn (and so as the brute force)
+    rng = np.random.default_rng(16)
+    lens, q_len, hq, hkv, d = [7, 9, 4], 5, 8, 2, 16
+    n = sum(lens) + q_len
+    rows = O.recompute_positions(lens, q_len, 3)
+    kx, vx = _rand(rng, n, hkv, d), _rand(rng, n, hkv, d)
+    q = _rand(rng, len(rows), hq, d)
+    full = O.selective_attn(q, kx, vx, rows)
+    picks = [(i, h) for i in range(len(rows)) for h in (0, 3, 7)]
+    got = O.attn_rows_direct([q[i, h] for i, h in picks], kx, vx, [rows[i] for i, _ in picks],
+                             [h // (hq // hkv) for _, h in picks])
+    want = np.stack([full[i, h] for i, h in picks])
+    assert np.max(np.abs(got - want)) < 1e-12
