@@ -106,14 +106,19 @@ enum {
   PIC_H_O_ROW_TOK,    /* [n_rows] K/V buffer row of each recomputed row (req_tok_ptr[b] + p_r) */
   PIC_H_O_ROPE_TILES, /* [n_rope_tiles][4]: first K row, row count, delta, chunk index */
   PIC_H_O_ATTN_TILES, /* [n_attn_tiles][8]: req, first row, row count, req_tok_ptr[req],
-                         p_first, p_last, 0, 0 */
+                         p_first, p_last, req_row_ptr[req], recomputed rows of req */
   PIC_H_O_ATTN_ITEMS, /* [n_attn_items][8]: tile, kv head, key_begin, key_end,
-                         partial slot (-1: writes O directly), 0, 0, 0 */
+                         partial slot (-1: writes O directly), 0, 0, 0.  Paged plans
+                         store a key-block range [key_begin, key_end) instead */
   PIC_H_O_MERGE,      /* [n_merge][4]: tile, kv head, first slot, slot count */
-  PIC_H_RESERVED0,
-  PIC_H_RESERVED1,
-  PIC_H_RESERVED2,
-  PIC_H_RESERVED3,
+  PIC_H_PAGED,        /* 1: chunks live in a shared paged pool (chunk_ids given) */
+  PIC_H_O_SEGS,       /* paged: [n_chunks][8] off_c, L_c, n_seam_c, pool chunk id, delta_c,
+                         request, 0, 0 */
+  PIC_H_N_KBLOCKS,    /* paged: key blocks over all requests */
+  PIC_H_O_KBLOCKS,    /* paged: [n_kblocks][4] chunk (global chunk index, or -1 for the
+                         request's fresh rows), first local key (t0, or fresh row offset),
+                         position of the first key, 0; per request the fresh blocks
+                         come first, then the pool blocks in position order */
   PIC_H_RESERVED4
 };
 
@@ -130,6 +135,12 @@ enum {
  * h_q/h_kv fix the GQA group G = h_q / h_kv (must divide PIC_ATTN_TILE_M).  n_cu is
  * the compute-unit count used to size split-KV (<= 0 selects 256).
  *
+ * chunk_ids: NULL for spliced contiguous K/V buffers.  Otherwise the chunks are stored
+ * once in a shared paged pool and chunk_ids[c] (>= 0) names the pool chunk of request
+ * chunk c (chunk_lens[c] must be its length): the plan then has no rope tiles (the pool
+ * is read-only; pic_selective_attn_paged rotates on load), and attention items walk
+ * per-request key blocks (fresh rows first, then pool rows chunk by chunk).
+ *
  * plan: caller-owned int32 host array of plan_cap words, or NULL to query the size.
  * *plan_words receives the size the plan needs.  Returns PIC_ENOSPC (plan untouched)
  * when plan_cap is too small, PIC_EINVAL on bad input (null pointers, negative values,
@@ -138,9 +149,9 @@ enum {
  * A request may have no chunks (only query rows) or no query tokens.
  */
 int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr, const int32_t *chunk_lens,
-                    const int32_t *q_lens, int32_t k, int32_t pos_base, int32_t h_q,
-                    int32_t h_kv, int32_t n_cu, int32_t *plan, int64_t plan_cap,
-                    int64_t *plan_words);
+                    const int32_t *q_lens, const int32_t *chunk_ids, int32_t k,
+                    int32_t pos_base, int32_t h_q, int32_t h_kv, int32_t n_cu, int32_t *plan,
+                    int64_t plan_cap, int64_t *plan_words);
 
 /*
  * pic_rope_delta -- rotary correction of cached K in place.          [RoPE-C] 3.3
@@ -170,8 +181,9 @@ int pic_splice(const int32_t *plan_host, const int32_t *plan_dev, void *k, void 
                const void *k_fresh, const void *v_fresh, int32_t dtype, int32_t head_dim,
                void *stream);
 
-/* Bytes of fp32 workspace pic_selective_attn needs for split-KV partials (0 if the
- * plan has no split tile).  Returns 0 on a bad plan as well; check with the call. */
+/* Bytes of workspace pic_selective_attn (split-KV partials; 0 if the plan has no split
+ * tile) or pic_selective_attn_paged (partials + per-chunk angle table) needs.  Returns 0
+ * on a bad plan as well; the attention call checks again. */
 size_t pic_attn_workspace_bytes(const int32_t *plan_host, int32_t head_dim);
 
 /*
@@ -185,12 +197,42 @@ size_t pic_attn_workspace_bytes(const int32_t *plan_host, int32_t head_dim);
  * of dtype.  scale > 0 (normally 1/sqrt(head_dim)).  bf16 runs bf16 MFMA with fp32
  * accumulation and an fp32 online softmax; f32 runs fp32 MFMA.  head_dim in {64, 128}
  * for bf16, {16, 32, 64, 128} for f32.  workspace: device, >= pic_attn_workspace_bytes
- * (may be NULL when that is 0); contents on entry are ignored.
+ * (may be NULL when that is 0); contents on entry are ignored.  A paged plan (built with
+ * chunk_ids) is rejected with PIC_EINVAL: it needs pic_selective_attn_paged.
  */
 int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_dev, const void *q,
                        const void *k, const void *v, void *out, int32_t dtype,
                        int32_t head_dim, float scale, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/*
+ * pic_selective_attn_paged -- selective attention over a shared paged chunk pool.
+ *                                  [EPIC] Step 3; [RoPE-C] 3.3; [HYPIC] 2.2
+ * Same result as pic_rope_delta + pic_splice + pic_selective_attn on the gathered
+ * chunks, without modifying the pool: chunks are stored once, carrying RoPE at local
+ * positions pos_base.., in pool_k/pool_v [pool_blocks][block_size = 16][h_kv][head_dim];
+ * pool chunk i occupies the blocks block_ids[chunk_block_ptr[i] .. chunk_block_ptr[i+1]-1]
+ * in order (the last one partially); chunk_block_ptr is device [n_pool_chunks + 1] and
+ * block_ids device int32.  The plan must come from pic_build_index with chunk_ids, all
+ * of them < n_pool_chunks (checked on the host).  Not checkable on the host and left to
+ * the caller: each listed chunk has at least ceil(L_c / 16) blocks, and block ids are
+ * < pool_blocks (a larger id reads zeros: the pool loads are range-checked).  k_fresh/v_fresh [n_rows][h_kv][head_dim] hold the recomputed rows (RoPE'd
+ * at their global positions) and are read in place; q/out as in pic_selective_attn.
+ * Cached keys of chunk c are scored in their local frame against the query rotated by
+ * -delta_c (same theta and pair layout as pic_rope_delta).  bf16 only, head_dim in
+ * {64, 128}, pool and fresh K/V each < 2 GiB.  Pool slots past a chunk's length may
+ * hold anything (NaN included).  workspace >= pic_attn_workspace_bytes(plan_host,
+ * head_dim) (partials + angle table).  Errors: PIC_EINVAL (not a paged plan, null
+ * pointers, a chunk id >= n_pool_chunks, bad scale/base/layout), PIC_EUNSUPPORTED
+ * (dtype, head_dim, block_size != 16, sizes), PIC_ENOSPC (workspace), PIC_EDEVICE.
+ */
+int pic_selective_attn_paged(const int32_t *plan_host, const int32_t *plan_dev, const void *q,
+                             const void *pool_k, const void *pool_v, int64_t pool_blocks,
+                             int32_t block_size, const int32_t *chunk_block_ptr,
+                             int32_t n_pool_chunks, const int32_t *block_ids, const void *k_fresh, const void *v_fresh,
+                             void *out, int32_t dtype, int32_t head_dim, int32_t rope_layout,
+                             double rope_base, float scale, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /* Short static description of a status code. */
 const char *pic_strerror(int status);

@@ -24,10 +24,11 @@ PIC_ATTN_TILE_M = 128
 (H_MAGIC, H_WORDS, H_N_REQ, H_N_CHUNKS, H_N_ROWS, H_N_TOKENS, H_K, H_POS_BASE, H_H_Q, H_H_KV,
  H_TILE_ROWS, H_N_ROPE_TILES, H_N_ATTN_TILES, H_N_ATTN_ITEMS, H_N_MERGE, H_N_PARTIALS,
  H_MAX_TOKENS, H_O_REQ_CHUNK_PTR, H_O_CHUNK_OFF, H_O_REQ_TOK_PTR, H_O_REQ_ROW_PTR, H_O_ROWS,
- H_O_ROW_TOK, H_O_ROPE_TILES, H_O_ATTN_TILES, H_O_ATTN_ITEMS, H_O_MERGE) = range(27)
+ H_O_ROW_TOK, H_O_ROPE_TILES, H_O_ATTN_TILES, H_O_ATTN_ITEMS, H_O_MERGE, H_PAGED, H_O_SEGS,
+ H_N_KBLOCKS, H_O_KBLOCKS) = range(31)
 
 EXPORTED = ("pic_build_index", "pic_rope_delta", "pic_splice", "pic_attn_workspace_bytes",
-            "pic_selective_attn", "pic_strerror")
+            "pic_selective_attn", "pic_selective_attn_paged", "pic_strerror")
 
 
 class PicError(RuntimeError):
@@ -38,6 +39,7 @@ class PicError(RuntimeError):
 
 
 _lib = None
+_NO_CHUNKS = ctypes.c_int32(0)
 
 
 def lib():
@@ -51,7 +53,7 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     i32, i64, p, f32, f64, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                  ctypes.c_float, ctypes.c_double, ctypes.c_size_t)
-    L.pic_build_index.argtypes = [i32, p, p, p, i32, i32, i32, i32, i32, p, i64,
+    L.pic_build_index.argtypes = [i32, p, p, p, p, i32, i32, i32, i32, i32, p, i64,
                                   ctypes.POINTER(i64)]
     L.pic_build_index.restype = ctypes.c_int
     L.pic_rope_delta.argtypes = [p, p, p, i32, i32, i32, f64, p]
@@ -62,6 +64,9 @@ def lib():
     L.pic_attn_workspace_bytes.restype = sz
     L.pic_selective_attn.argtypes = [p, p, p, p, p, p, i32, i32, f32, p, sz, p]
     L.pic_selective_attn.restype = ctypes.c_int
+    L.pic_selective_attn_paged.argtypes = [p, p, p, p, p, i64, i32, p, i32, p, p, p, p, i32, i32,
+                                           i32, f64, f32, p, sz, p]
+    L.pic_selective_attn_paged.restype = ctypes.c_int
     L.pic_strerror.argtypes = [ctypes.c_int]
     L.pic_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -143,6 +148,18 @@ class Plan:
     def merges(self):
         return self._sec(H_O_MERGE, self[H_N_MERGE], 4)
 
+    @property
+    def paged(self):
+        return bool(self[H_PAGED])
+
+    @property
+    def segments(self):
+        return self._sec(H_O_SEGS, self[H_N_CHUNKS] if self.paged else 0, 8)
+
+    @property
+    def kblocks(self):
+        return self._sec(H_O_KBLOCKS, self[H_N_KBLOCKS], 4)
+
     def to_device(self, device="cuda"):
         """Upload the plan (one int32 tensor) and keep it with the host copy."""
         import torch
@@ -158,21 +175,31 @@ class Plan:
         return ctypes.c_void_p(self.dev.data_ptr())
 
 
-def pic_build_index(chunk_lens_per_req, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0):
-    """Run the host planner.  chunk_lens_per_req: list (per request) of chunk-length lists."""
+def pic_build_index(chunk_lens_per_req, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0,
+                    chunk_ids_per_req=None):
+    """Run the host planner.  chunk_lens_per_req: list (per request) of chunk-length lists;
+    chunk_ids_per_req: pool chunk ids of the same shape for a paged pool, or None."""
     n_req = len(chunk_lens_per_req)
     ptr = np.zeros(n_req + 1, dtype=np.int64)
     ptr[1:] = np.cumsum([len(c) for c in chunk_lens_per_req])
     rcp = _i32(ptr)
     lens = _i32([x for c in chunk_lens_per_req for x in c])
     ql = _i32(q_lens)
+    ids = None
+    if chunk_ids_per_req is not None:
+        ids = _i32([x for c in chunk_ids_per_req for x in c])
+        if ids.size != lens.size:
+            raise ValueError("chunk_ids_per_req must match chunk_lens_per_req")
+    ids_p = ids.ctypes.data_as(ctypes.c_void_p) if ids is not None else None
+    if ids is not None and ids.size == 0:
+        ids_p = ctypes.cast(ctypes.pointer(_NO_CHUNKS), ctypes.c_void_p)  # paged, no chunks
     words = ctypes.c_int64(0)
     L = lib()
-    st = L.pic_build_index(n_req, _ptr(rcp), _ptr(lens), _ptr(ql), int(k), int(pos_base),
+    st = L.pic_build_index(n_req, _ptr(rcp), _ptr(lens), _ptr(ql), ids_p, int(k), int(pos_base),
                            int(h_q), int(h_kv), int(n_cu), None, 0, ctypes.byref(words))
     _check("pic_build_index", st)
     plan = np.zeros(words.value, dtype=np.int32)
-    st = L.pic_build_index(n_req, _ptr(rcp), _ptr(lens), _ptr(ql), int(k), int(pos_base),
+    st = L.pic_build_index(n_req, _ptr(rcp), _ptr(lens), _ptr(ql), ids_p, int(k), int(pos_base),
                            int(h_q), int(h_kv), int(n_cu), _ptr(plan), plan.size,
                            ctypes.byref(words))
     _check("pic_build_index", st)
@@ -253,3 +280,38 @@ def attn_workspace(plan, head_dim, device="cuda"):
     if n == 0:
         return None
     return torch.empty(n // 4, dtype=torch.float32, device=device)
+
+
+def pic_selective_attn_paged(plan, q, pool_k, pool_v, chunk_block_ptr, block_ids, k_fresh,
+                             v_fresh, out, rope_base, layout=PIC_ROPE_ADJACENT, scale=None,
+                             workspace=None, stream=None):
+    """Selective attention over a shared paged pool [blocks, 16, h_kv, D] (read-only)."""
+    import torch
+    d = int(q.shape[2])
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if not plan.paged:
+        raise ValueError("plan was not built with chunk ids (paged pool)")
+    if q.shape[0] != plan.n_rows or out.shape != q.shape or q.shape[1] != plan[H_H_Q]:
+        raise ValueError("q/out shapes do not match the plan")
+    if pool_k.dim() != 4 or pool_v.shape != pool_k.shape or pool_k.shape[2] != plan[H_H_KV]:
+        raise ValueError("pool must be [blocks, block_size, h_kv, D]")
+    for t, name in ((chunk_block_ptr, "chunk_block_ptr"), (block_ids, "block_ids")):
+        if t.dtype != torch.int32 or t.dim() != 1:
+            raise ValueError(name + " must be a 1-D int32 tensor")
+    if k_fresh.shape != (plan.n_rows, plan[H_H_KV], d) or v_fresh.shape != k_fresh.shape:
+        raise ValueError("fresh K/V must be [n_rows, h_kv, D]")
+    for t in (pool_k, pool_v, k_fresh, v_fresh, out):
+        if t.dtype != q.dtype:
+            raise ValueError("all tensors must share one dtype")
+    ws, ws_bytes = None, 0
+    if workspace is not None:
+        ws, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    st = lib().pic_selective_attn_paged(
+        plan.host_ptr(), plan.dev_ptr(), _dev(q, "q"), _dev(pool_k, "pool_k"),
+        _dev(pool_v, "pool_v"), int(pool_k.shape[0]), int(pool_k.shape[1]),
+        _dev(chunk_block_ptr, "chunk_block_ptr"), int(chunk_block_ptr.numel()) - 1,
+        _dev(block_ids, "block_ids"),
+        _dev(k_fresh, "k_fresh"), _dev(v_fresh, "v_fresh"), _dev(out, "out"), _dtype_code(q), d,
+        int(layout), float(rope_base), float(scale), ws, ws_bytes, _stream(stream))
+    _check("pic_selective_attn_paged", st)

@@ -358,6 +358,418 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_kernel(
                     scale_log2);
 }
 
+// ============================ bf16 kernel, paged pool ===========================
+//
+// Chunks are stored once in a shared pool of 16-row blocks, so cached K cannot be
+// rotated in place.  Instead each chunk's keys are scored in their local RoPE frame
+// against the query rotated the other way: <q, R(delta_c) k> = <R(-delta_c) q, k>
+// (rotations are orthogonal), once per chunk per wave.  The recomputed rows (seams and
+// queries) are read straight from the fresh buffers in the global frame, as their own
+// key blocks; the online softmax does not depend on key order.  Every staged block
+// therefore comes from one buffer, so direct buffer->LDS loads still apply: pool blocks
+// take one scalar block-table lookup per 16 rows, rows past a chunk's last block read
+// as zero, and V rows past a chunk's end are zeroed in LDS so that masked keys
+// contribute exactly nothing.
+
+constexpr int kPoolBlockRows = 16;
+
+// cos/sin(delta_c * theta_i) for every chunk c and pair i of the plan.
+__global__ __launch_bounds__(256) void paged_angles_kernel(float2 *__restrict__ angles,
+                                                           const int32_t *__restrict__ segs,
+                                                           int n_chunks, int n_pairs,
+                                                           ThetaTable theta) {
+  const int64_t total = (int64_t)n_chunks * n_pairs;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total;
+       u += (int64_t)gridDim.x * 256) {
+    const int c = (int)(u / n_pairs), i = (int)(u - (int64_t)c * n_pairs);
+    angles[u] = delta_cos_sin(segs[8 * c + 4], theta.hi[i], theta.lo[i]);
+  }
+}
+
+template <int D, bool kHalf>
+__device__ __forceinline__ void attn_bf16_paged_body(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ pool_k,
+    const __bf16 *__restrict__ pool_v, const int32_t *__restrict__ chunk_block_ptr,
+    const int32_t *__restrict__ block_ids, const __bf16 *__restrict__ k_fresh,
+    const __bf16 *__restrict__ v_fresh, __bf16 *__restrict__ out,
+    const int32_t *__restrict__ rows, const AttnTile *__restrict__ tiles,
+    const AttnItem *__restrict__ items, const int32_t *__restrict__ segs,
+    const int4 *__restrict__ kblocks, const float2 *__restrict__ angles,
+    float *__restrict__ ws_o, float *__restrict__ ws_ml, int h_q, int h_kv, int tile_rows,
+    float scale_log2, int pool_bytes) {
+  constexpr int kRowB = D * 2;
+  constexpr int kCPR = D / 8;
+  constexpr int kTileB = kKB * kRowB;
+  constexpr int kRPI = 1024 / kRowB;
+  constexpr int kRounds = kKB / (kRPI * kBfWaves);
+  constexpr int kKS = D / 16;
+  constexpr int kDB = D / 32;
+  constexpr int kPairs = D / 2;
+  static_assert(kRounds * kRPI * kBfWaves == kKB, "direct loads must tile the block");
+  static_assert(2 * kKS <= 16, "S^T MFMAs of a block must fit the 16 exponential pairs");
+  static_assert(kRPI <= kPoolBlockRows, "one direct load must stay inside a pool block");
+  __shared__ __attribute__((aligned(1024))) char lds[4 * kTileB];
+  __shared__ int kpos[2][kKB];  // key positions of fresh blocks (INT_MAX: no key)
+
+  const AttnItem it = items[blockIdx.x];
+  const AttnTile tile = tiles[it.tile];
+  const int g = it.kv_head;
+  const int group = h_q / h_kv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31;
+  const int grp = lane >> 5;
+  const int q16 = lane >> 4;
+  const int i16 = lane & 15;
+
+  const int m = 32 * wave + n;
+  const int row_local = m % tile_rows;
+  const int head = g * group + m / tile_rows;
+  const bool valid = row_local < tile.n_rows;
+  const int row = tile.row_begin + (valid ? row_local : 0);
+  const int pos = valid ? rows[row] : -1;
+  const int fresh_base = tile.pad0, n_fresh = tile.pad1;
+
+  int pos_min = valid ? pos : 0x7fffffff;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) pos_min = min(pos_min, __shfl_xor(pos_min, o));
+
+  // ---- query operand in the frame of the block being scored ----
+  bf16x8 qop[kKS];
+  int frame = -2;  // -1: global frame (fresh keys); c >= 0: local frame of chunk c
+  const __bf16 *qp = q + ((int64_t)row * h_q + head) * D + 8 * grp;
+  auto set_frame = [&](int f) {
+    if (f == frame) return;
+    frame = f;
+    bf16x8 qo[kKS];
+#pragma unroll
+    for (int s = 0; s < kKS; ++s)
+      qo[s] = valid ? *reinterpret_cast<const bf16x8 *>(qp + 16 * s) : bf16x8{};
+    if (f < 0) {
+#pragma unroll
+      for (int s = 0; s < kKS; ++s) qop[s] = qo[s];
+      return;
+    }
+    const float2 *cs = angles + (int64_t)f * kPairs;  // rotate by -delta_c
+    if constexpr (!kHalf) {
+#pragma unroll
+      for (int s = 0; s < kKS; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const float2 c = cs[8 * s + 4 * grp + j / 2];
+          const float a = (float)qo[s][j], b = (float)qo[s][j + 1];
+          qop[s][j] = (__bf16)(a * c.x + b * c.y);
+          qop[s][j + 1] = (__bf16)(b * c.x - a * c.y);
+        }
+    } else {
+#pragma unroll
+      for (int s = 0; s < kKS / 2; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float2 c = cs[16 * s + 8 * grp + j];
+          const float a = (float)qo[s][j], b = (float)qo[s + kKS / 2][j];
+          qop[s][j] = (__bf16)(a * c.x + b * c.y);
+          qop[s + kKS / 2][j] = (__bf16)(b * c.x - a * c.y);
+        }
+    }
+  };
+
+  f32x16 acc[kDB];
+#pragma unroll
+  for (int d = 0; d < kDB; ++d)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[d][j] = 0.f;
+  float m_run = kNegInf;
+  float l_lane = 0.f;
+
+  // ---- key blocks: item ranges [key_begin, key_end) then [pad0, pad1) ----
+  const int n1 = it.key_end - it.key_begin;
+  const int n_blocks = n1 + (it.pad1 - it.pad0);
+  auto desc = [&](int ib) { return kblocks[ib < n1 ? it.key_begin + ib : it.pad0 + ib - n1]; };
+
+  const int tok_bytes = h_kv * D * 2;
+  const int blk_bytes = kPoolBlockRows * tok_bytes;
+  const __bf16 *kfh = k_fresh + ((int64_t)fresh_base * h_kv + g) * D;
+  const __bf16 *vfh = v_fresh + ((int64_t)fresh_base * h_kv + g) * D;
+  int voff_f[kRounds], voff_p[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int R = kRPI * (kBfWaves * r + wave) + lane / kCPR;
+    const int pch = lane % kCPR;
+    voff_f[r] = R * tok_bytes + 16 * (pch ^ swz_k<kCPR>(R));
+    voff_p[r] = (R % kPoolBlockRows) * tok_bytes + g * kRowB + 16 * (pch ^ swz_k<kCPR>(R));
+  }
+  int voff_fv[kRounds], voff_pv[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int R = kRPI * (kBfWaves * r + wave) + lane / kCPR;
+    const int pch = lane % kCPR;
+    voff_fv[r] = R * tok_bytes + 16 * (pch ^ swz_v<kCPR>(R));
+    voff_pv[r] = (R % kPoolBlockRows) * tok_bytes + g * kRowB + 16 * (pch ^ swz_v<kCPR>(R));
+  }
+
+  // Stage one K (is_v = false) or V block into LDS buffer `buf` (direct loads).
+  auto issue = [&](int4 dsc, bool is_v, int buf) {
+    if (dsc.x < 0) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(is_v ? vfh : kfh), 0, n_fresh * tok_bytes, 0x00020000);
+      const int soff = dsc.y * tok_bytes;
+#pragma unroll
+      for (int r = 0; r < kRounds; ++r) {
+        const int dst = buf * kTileB + (kBfWaves * r + wave) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16,
+                                                 is_v ? voff_fv[r] : voff_f[r], soff, 0, 0);
+      }
+    } else {
+      const int32_t *sg = segs + 8 * dsc.x;
+      const int len = sg[1], cid = sg[3];
+      const int nb = (len + kPoolBlockRows - 1) / kPoolBlockRows;
+      const int32_t *bl = block_ids + chunk_block_ptr[cid];
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(is_v ? pool_v : pool_k), 0, pool_bytes, 0x00020000);
+#pragma unroll
+      for (int r = 0; r < kRounds; ++r) {
+        const int pb = (dsc.y + kRPI * (kBfWaves * r + wave)) / kPoolBlockRows;
+        const int soff = pb < nb ? bl[pb] * blk_bytes : pool_bytes;  // past the chunk: zeros
+        const int dst = buf * kTileB + (kBfWaves * r + wave) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16,
+                                                 is_v ? voff_pv[r] : voff_p[r], soff, 0, 0);
+      }
+    }
+  };
+  // After a V block landed: zero V rows past the chunk's end (pool blocks) and record
+  // key positions (fresh blocks).
+  auto finish_v = [&](int4 dsc, int buf) {
+    if (dsc.x < 0) {
+      if (wave == 0) {
+        const int r = dsc.y + lane;
+        kpos[buf & 1][lane] = r < n_fresh ? rows[fresh_base + r] : 0x7fffffff;
+      }
+      return;
+    }
+    const int len = segs[8 * dsc.x + 1];
+    if (dsc.y + kKB <= len) return;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int R = kRPI * (kBfWaves * r + wave) + lane / kCPR;
+      if (dsc.y + R >= len) {
+        const int dst = (2 + buf) * kTileB + (kBfWaves * r + wave) * 1024 + 16 * lane;
+        *reinterpret_cast<u32x4 *>(lds + dst) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  int koff[kKS];
+  {
+    const int r0 = perm_key(0, n);
+    const int f = swz_k<kCPR>(r0);
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) koff[s] = r0 * kRowB + 16 * ((2 * s + grp) ^ f);
+  }
+  int voff[kDB];
+  {
+    const int rr = 8 * (q16 >> 1) + (i16 >> 2);
+    const int f = swz_v<kCPR>(rr) >> 2;
+#pragma unroll
+    for (int d = 0; d < kDB; ++d)
+      voff[d] = rr * kRowB + 16 * (4 * (d ^ f) + 2 * (q16 & 1) + ((i16 & 3) >> 1)) +
+                8 * (i16 & 1);
+  }
+
+  auto qk = [&](const char *Kb, f32x16 (&sc)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sc[t][j] = 0.f;
+#pragma unroll
+      for (int s = 0; s < kKS; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Kb + koff[s] + t * 32 * kRowB);
+        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], sc[t], 0, 0, 0);
+      }
+    }
+  };
+
+  auto softmax_pv = [&](f32x16 (&sc)[2], int4 dsc, int buf, const char *Knext,
+                        f32x16 (&s_nxt)[2]) {
+    constexpr float kLazy = 8.f;
+    const char *Vb = lds + (2 + buf) * kTileB;
+    if (dsc.x < 0) {  // fresh keys: positions from LDS
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int kp = kpos[buf][perm_key(t, 8 * (j >> 2) + 4 * grp + (j & 3))];
+          if (kp > pos) sc[t][j] = kNegInf;
+        }
+    } else {
+      const int32_t *sg = segs + 8 * dsc.x;
+      const int off = sg[0], len = sg[1], seam = sg[2];
+      if (dsc.y < seam || dsc.y + kKB > len || off + dsc.y + kKB - 1 > pos_min) {
+        const int lim = min(len, pos - off + 1);  // keys t < lim are visible
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int tk = dsc.y + perm_key(t, 8 * (j >> 2) + 4 * grp + (j & 3));
+            if (tk < seam || tk >= lim) sc[t][j] = kNegInf;
+          }
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[t][j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    const bool upd = mx > m_run + kLazy;
+    if (wave_any(upd)) {
+      const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
+      m_run = upd ? mx : m_run;
+      l_lane *= alpha;
+#pragma unroll
+      for (int d = 0; d < kDB; ++d) acc[d] *= alpha;
+    }
+    const float base = m_run == kNegInf ? 0.f : m_run;
+    bf16x8 pb[4];
+    const bf16x2v ones = {(__bf16)1.f, (__bf16)1.f};
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s_nxt[t][j] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (q < 2 * kKS) {
+        const int t = q & 1, s = q >> 1;
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Knext + koff[s] + t * 32 * kRowB);
+        s_nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], s_nxt[t], 0, 0, 0);
+      }
+      const int t = q >> 3, j = 2 * (q & 7);
+      bf16x2v pr;
+      pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][j], scale_log2, -base));
+      pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][j + 1], scale_log2, -base));
+      pb[2 * t + (j >> 3)][j & 7] = pr[0];
+      pb[2 * t + (j >> 3)][(j & 7) + 1] = pr[1];
+      if (j & 2) ps1 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps1, false);
+      else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps0, false);
+    }
+#pragma unroll
+    for (int q = 0; q < 2 * kKS; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    l_lane += ps0 + ps1;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int d = 0; d < kDB; ++d) {
+        const char *vr = Vb + voff[d] + c * 16 * kRowB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vr);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 4 * kRowB));
+        bf16x8 a;
+        __builtin_memcpy(&a, &lo, 8);
+        __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &hi, 8);
+        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[d], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // ---- prologue: K(0), V(0), K(1) ----
+  int4 d0 = desc(0);
+  issue(d0, false, 0);
+  issue(d0, true, 2);
+  int4 d1 = n_blocks > 1 ? desc(1) : d0;
+  if (n_blocks > 1) issue(d1, false, 1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  finish_v(d0, 0);
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  set_frame(d0.x < 0 ? -1 : d0.x);
+  qk(lds, sa);
+  __syncthreads();
+
+  // Block ib: S^T(ib) is in registers; stage K(ib+2) and V(ib+1), compute S^T(ib+1) in
+  // block ib+1's frame, then the softmax and PV of block ib.
+  auto step = [&](int ib, auto bufc, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], int4 dc,
+                  int4 dn) {
+    constexpr int kB = decltype(bufc)::value;
+    if (ib + 2 < n_blocks) issue(desc(ib + 2), false, kB);
+    if (ib + 1 < n_blocks) {
+      issue(dn, true, 2 + (kB ^ 1));
+      set_frame(dn.x < 0 ? -1 : dn.x);
+    }
+    softmax_pv(s_cur, dc, kB, lds + (kB ^ 1) * kTileB, s_nxt);
+    if (ib + 1 < n_blocks) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      finish_v(dn, kB ^ 1);
+      __syncthreads();
+    }
+  };
+
+  int4 dc = d0, dn = d1;
+  for (int ib = 0; ib < n_blocks; ib += 2) {
+    step(ib, std::integral_constant<int, 0>{}, sa, sb, dc, dn);
+    dc = dn;
+    dn = ib + 2 < n_blocks ? desc(ib + 2) : dc;
+    if (ib + 1 < n_blocks) {
+      step(ib + 1, std::integral_constant<int, 1>{}, sb, sa, dc, dn);
+      dc = dn;
+      dn = ib + 3 < n_blocks ? desc(ib + 3) : dc;
+    }
+  }
+
+  // ---- epilogue (as in the contiguous kernel) ----
+  const float l_row = l_lane + __shfl_xor(l_lane, 32);
+  if (!valid) return;
+  if (it.slot < 0) {
+    const float inv = 1.f / l_row;
+    __bf16 *op = out + ((int64_t)row * h_q + head) * D + 4 * grp;
+#pragma unroll
+    for (int d = 0; d < kDB; ++d)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        bf16x4 o;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) o[b] = (__bf16)(acc[d][4 * a + b] * inv);
+        *reinterpret_cast<bf16x4 *>(op + 32 * d + 8 * a) = o;
+      }
+  } else {
+    float *wo = ws_o + ((int64_t)it.slot * kM + m) * D + 4 * grp;
+#pragma unroll
+    for (int d = 0; d < kDB; ++d)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 o;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) o[b] = acc[d][4 * a + b];
+        *reinterpret_cast<f32x4 *>(wo + 32 * d + 8 * a) = o;
+      }
+    if (grp == 0) {
+      ws_ml[((int64_t)it.slot * kM + m) * 2 + 0] = m_run;
+      ws_ml[((int64_t)it.slot * kM + m) * 2 + 1] = l_row;
+    }
+  }
+}
+
+template <int D, bool kHalf>
+__global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_paged_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ pool_k,
+    const __bf16 *__restrict__ pool_v, const int32_t *__restrict__ chunk_block_ptr,
+    const int32_t *__restrict__ block_ids, const __bf16 *__restrict__ k_fresh,
+    const __bf16 *__restrict__ v_fresh, __bf16 *__restrict__ out,
+    const int32_t *__restrict__ rows, const AttnTile *__restrict__ tiles,
+    const AttnItem *__restrict__ items, const int32_t *__restrict__ segs,
+    const int4 *__restrict__ kblocks, const float2 *__restrict__ angles,
+    float *__restrict__ ws_o, float *__restrict__ ws_ml, int h_q, int h_kv, int tile_rows,
+    float scale_log2, int pool_bytes) {
+  attn_bf16_paged_body<D, kHalf>(q, pool_k, pool_v, chunk_block_ptr, block_ids, k_fresh,
+                                 v_fresh, out, rows, tiles, items, segs, kblocks, angles, ws_o,
+                                 ws_ml, h_q, h_kv, tile_rows, scale_log2, pool_bytes);
+}
+
 // ================================ fp32 kernel ==================================
 
 constexpr int kF32Waves = 8;
@@ -602,11 +1014,113 @@ int launch_attn(const PlanHeader &h, const int32_t *plan_dev, const void *q, con
 }  // namespace
 }  // namespace pic
 
+namespace pic {
+namespace {
+
+// Workspace layout: partial O [slots][kM][D], partial (m, l) [slots][kM][2], then for
+// paged plans the angle table [n_chunks][D/2] float2 (16-byte aligned).
+size_t partial_bytes(const PlanHeader &h, int head_dim) {
+  return (size_t)h[PIC_H_N_PARTIALS] * kM * ((size_t)head_dim + 2) * sizeof(float);
+}
+size_t angle_offset(const PlanHeader &h, int head_dim) {
+  return (partial_bytes(h, head_dim) + 15) / 16 * 16;
+}
+
+template <int D, bool kHalf>
+int launch_paged(const PlanHeader &h, const int32_t *plan_dev, const void *q, const void *pool_k,
+                 const void *pool_v, const int32_t *cbp, const int32_t *bids, const void *kf,
+                 const void *vf, void *out, double rope_base, float scale, void *workspace,
+                 int pool_bytes, hipStream_t s) {
+  const int32_t *rows = plan_dev + h[PIC_H_O_ROWS];
+  const AttnTile *tiles = reinterpret_cast<const AttnTile *>(plan_dev + h[PIC_H_O_ATTN_TILES]);
+  const AttnItem *items = reinterpret_cast<const AttnItem *>(plan_dev + h[PIC_H_O_ATTN_ITEMS]);
+  const MergeEntry *merges = reinterpret_cast<const MergeEntry *>(plan_dev + h[PIC_H_O_MERGE]);
+  const int32_t *segs = plan_dev + h[PIC_H_O_SEGS];
+  const int4 *kblocks = reinterpret_cast<const int4 *>(plan_dev + h[PIC_H_O_KBLOCKS]);
+  char *ws = static_cast<char *>(workspace);
+  float *ws_o = reinterpret_cast<float *>(ws);
+  float *ws_ml = ws_o + (int64_t)h[PIC_H_N_PARTIALS] * kM * D;
+  float2 *angles = reinterpret_cast<float2 *>(ws + angle_offset(h, D));
+  const int n_chunks = h[PIC_H_N_CHUNKS];
+  if (n_chunks > 0) {
+    const int64_t total = (int64_t)n_chunks * (D / 2);
+    const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65535);
+    hipLaunchKernelGGL(paged_angles_kernel, dim3(blocks), dim3(256), 0, s, angles, segs,
+                       n_chunks, D / 2, make_theta(D, rope_base));
+    PIC_LAUNCH_CHECK();
+  }
+  hipLaunchKernelGGL((attn_bf16_paged_kernel<D, kHalf>), dim3(h[PIC_H_N_ATTN_ITEMS]),
+                     dim3(kBfThreads), 0, s, static_cast<const __bf16 *>(q),
+                     static_cast<const __bf16 *>(pool_k), static_cast<const __bf16 *>(pool_v),
+                     cbp, bids, static_cast<const __bf16 *>(kf), static_cast<const __bf16 *>(vf),
+                     static_cast<__bf16 *>(out), rows, tiles, items, segs, kblocks, angles, ws_o,
+                     ws_ml, h[PIC_H_H_Q], h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], scale * kLog2e,
+                     pool_bytes);
+  PIC_LAUNCH_CHECK();
+  if (h[PIC_H_N_MERGE] > 0) {
+    const int64_t threads = (int64_t)h[PIC_H_N_MERGE] * kM * (D / 4);
+    const unsigned blocks = (unsigned)std::min<int64_t>((threads + 255) / 256, 1 << 20);
+    hipLaunchKernelGGL((merge_kernel<__bf16, D>), dim3(blocks), dim3(256), 0, s,
+                       static_cast<__bf16 *>(out), tiles, merges, ws_o, ws_ml, h[PIC_H_H_Q],
+                       h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], h[PIC_H_N_MERGE]);
+    PIC_LAUNCH_CHECK();
+  }
+  return PIC_OK;
+}
+
+}  // namespace
+}  // namespace pic
+
 extern "C" size_t pic_attn_workspace_bytes(const int32_t *plan_host, int32_t head_dim) {
   using namespace pic;
   const PlanHeader h{plan_host};
   if (!h.valid() || head_dim <= 0) return 0;
-  return (size_t)h[PIC_H_N_PARTIALS] * kM * ((size_t)head_dim + 2) * sizeof(float);
+  if (!h[PIC_H_PAGED]) return partial_bytes(h, head_dim);
+  return angle_offset(h, head_dim) + (size_t)h[PIC_H_N_CHUNKS] * (head_dim / 2) * sizeof(float2);
+}
+
+extern "C" int pic_selective_attn_paged(
+    const int32_t *plan_host, const int32_t *plan_dev, const void *q, const void *pool_k,
+    const void *pool_v, int64_t pool_blocks, int32_t block_size, const int32_t *chunk_block_ptr,
+    int32_t n_pool_chunks, const int32_t *block_ids, const void *k_fresh, const void *v_fresh, void *out, int32_t dtype,
+    int32_t head_dim, int32_t rope_layout, double rope_base, float scale, void *workspace,
+    size_t workspace_bytes, void *stream) {
+  using namespace pic;
+  const PlanHeader h{plan_host};
+  if (!h.valid() || !h[PIC_H_PAGED]) return PIC_EINVAL;
+  if (dtype != PIC_BF16 && dtype != PIC_F32) return PIC_EINVAL;
+  if (rope_layout != PIC_ROPE_ADJACENT && rope_layout != PIC_ROPE_HALF) return PIC_EINVAL;
+  if (!(scale > 0.f) || !std::isfinite(scale) || head_dim <= 0 || pool_blocks < 0) return PIC_EINVAL;
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return PIC_EINVAL;
+  if (dtype != PIC_BF16 || block_size != kPoolBlockRows) return PIC_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PIC_EUNSUPPORTED;
+  const int64_t tok_bytes = (int64_t)h[PIC_H_H_KV] * head_dim * 2;
+  const int64_t pool_bytes = pool_blocks * kPoolBlockRows * tok_bytes;
+  // 32-bit buffer offsets (plus one pool block of slack past the end)
+  if (pool_bytes > 0x7fff0000LL || (int64_t)h[PIC_H_N_ROWS] * tok_bytes > 0x7fff0000LL)
+    return PIC_EUNSUPPORTED;
+  const int32_t *segs_h = plan_host + h[PIC_H_O_SEGS];
+  for (int32_t c = 0; c < h[PIC_H_N_CHUNKS]; ++c)
+    if (segs_h[8 * c + 3] >= n_pool_chunks) return PIC_EINVAL;
+  if (h[PIC_H_N_ATTN_ITEMS] == 0) return PIC_OK;
+  if (!plan_dev || !q || !pool_k || !pool_v || !chunk_block_ptr || !block_ids || !k_fresh ||
+      !v_fresh || !out)
+    return PIC_EINVAL;
+  const size_t need = pic_attn_workspace_bytes(plan_host, head_dim);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PIC_ENOSPC;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool half = rope_layout == PIC_ROPE_HALF;
+#define PIC_PAGED(D_, H_)                                                                    \
+  return launch_paged<D_, H_>(h, plan_dev, q, pool_k, pool_v, chunk_block_ptr, block_ids,     \
+                              k_fresh, v_fresh, out, rope_base, scale, workspace,             \
+                              (int)pool_bytes, s)
+  if (head_dim == 128) {
+    if (half) PIC_PAGED(128, true);
+    PIC_PAGED(128, false);
+  }
+  if (half) PIC_PAGED(64, true);
+  PIC_PAGED(64, false);
+#undef PIC_PAGED
 }
 
 extern "C" int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_dev,
@@ -615,7 +1129,7 @@ extern "C" int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_
                                   size_t workspace_bytes, void *stream) {
   using namespace pic;
   const PlanHeader h{plan_host};
-  if (!h.valid()) return PIC_EINVAL;
+  if (!h.valid() || h[PIC_H_PAGED]) return PIC_EINVAL;
   if (dtype != PIC_BF16 && dtype != PIC_F32) return PIC_EINVAL;
   if (!(scale > 0.f) || !std::isfinite(scale) || head_dim <= 0) return PIC_EINVAL;
   if (h[PIC_H_N_ATTN_ITEMS] == 0) return PIC_OK;

@@ -20,7 +20,9 @@ struct PlanHeader {
 
 // Attention tile and item records as stored in the plan (8 int32 words each).
 struct AttnTile {
-  int32_t req, row_begin, n_rows, tok_base, p_first, p_last, pad0, pad1;
+  int32_t req, row_begin, n_rows, tok_base, p_first, p_last;
+  int32_t pad0;  // first recomputed (fresh) row of the request
+  int32_t pad1;  // recomputed rows of the request
 };
 struct AttnItem {
   int32_t tile, kv_head, key_begin, key_end, slot, pad0, pad1, pad2;

@@ -40,7 +40,9 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 std::vector<pic::AttnItem> xcd_order(std::vector<pic::AttnItem> items,
                                      const std::vector<pic::AttnTile> &tiles, int n_xcd) {
   using pic::AttnItem;
-  auto len = [](const AttnItem &a) { return (int64_t)a.key_end - a.key_begin; };
+  auto len = [](const AttnItem &a) {  // second range used by paged plans
+    return (int64_t)a.key_end - a.key_begin + ((int64_t)a.pad1 - a.pad0);
+  };
   std::stable_sort(items.begin(), items.end(),
                    [&](const AttnItem &a, const AttnItem &b) { return len(a) > len(b); });
   if (n_xcd <= 1 || items.size() < 2) return items;
@@ -119,9 +121,10 @@ std::vector<pic::AttnItem> xcd_order(std::vector<pic::AttnItem> items,
 }  // namespace
 
 extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
-                               const int32_t *chunk_lens, const int32_t *q_lens, int32_t k,
-                               int32_t pos_base, int32_t h_q, int32_t h_kv, int32_t n_cu,
-                               int32_t *plan, int64_t plan_cap, int64_t *plan_words) {
+                               const int32_t *chunk_lens, const int32_t *q_lens,
+                               const int32_t *chunk_ids, int32_t k, int32_t pos_base,
+                               int32_t h_q, int32_t h_kv, int32_t n_cu, int32_t *plan,
+                               int64_t plan_cap, int64_t *plan_words) {
   using namespace pic;
   if (plan_words == nullptr || n_req < 0 || k < 0 || h_q <= 0 || h_kv <= 0) return PIC_EINVAL;
   if (h_q % h_kv != 0) return PIC_EINVAL;
@@ -135,7 +138,8 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   const int32_t n_chunks = n_req > 0 ? req_chunk_ptr[n_req] : 0;
   if (n_chunks > 0 && chunk_lens == nullptr) return PIC_EINVAL;
   for (int32_t c = 0; c < n_chunks; ++c)
-    if (chunk_lens[c] < 0) return PIC_EINVAL;
+    if (chunk_lens[c] < 0 || (chunk_ids != nullptr && chunk_ids[c] < 0)) return PIC_EINVAL;
+  const bool paged = chunk_ids != nullptr;
   if (n_cu <= 0) n_cu = 256;
 
   // ---- offsets, token and row pointers (64-bit, then range-checked) ----
@@ -186,6 +190,7 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   // ---- rope tiles: cached rows that keep their K, per chunk with delta != 0 ----
   std::vector<RopeTile> rope;
   for (int32_t b = 0; b < n_req; ++b) {
+    if (paged) break;  // the shared pool is never rotated in place
     const int32_t c0 = req_chunk_ptr[b], c1 = req_chunk_ptr[b + 1];
     for (int32_t c = c0; c < c1; ++c) {
       const int64_t delta = (int64_t)chunk_off[c + b] - pos_base;
@@ -204,6 +209,45 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
     }
   }
 
+  // ---- paged pool: per-chunk segment records and per-request key blocks ----
+  std::vector<int32_t> segs;     // [n_chunks][8]
+  std::vector<int32_t> kblocks;  // [n_kblocks][4]
+  std::vector<int64_t> kb_fresh(n_req + 1, 0), kb_pool(n_req + 1, 0);  // per request starts
+  if (paged) {
+    segs.assign((size_t)n_chunks * 8, 0);
+    for (int32_t b = 0; b < n_req; ++b) {
+      const int32_t c0 = req_chunk_ptr[b], c1 = req_chunk_ptr[b + 1];
+      for (int32_t c = c0; c < c1; ++c) {
+        const int64_t delta = (int64_t)chunk_off[c + b] - pos_base;
+        if (delta > (int64_t(1) << 24) || delta < -(int64_t(1) << 24)) return PIC_EUNSUPPORTED;
+        int32_t *sg = &segs[(size_t)c * 8];
+        sg[0] = chunk_off[c + b];
+        sg[1] = chunk_lens[c];
+        sg[2] = c > c0 ? std::min(k, chunk_lens[c]) : 0;
+        sg[3] = chunk_ids[c];
+        sg[4] = (int32_t)delta;
+        sg[5] = b;
+      }
+      // fresh rows of the request (seams then queries), 64 per block
+      kb_fresh[b] = (int64_t)kblocks.size() / 4;
+      const int32_t r_b = req_row_ptr[b + 1] - req_row_ptr[b];
+      for (int32_t r0 = 0; r0 < r_b; r0 += kKeyAlign) {
+        kblocks.insert(kblocks.end(), {-1, r0, rows[req_row_ptr[b] + r0], 0});
+      }
+      // pool rows chunk by chunk; blocks holding only seam rows are skipped
+      kb_pool[b] = (int64_t)kblocks.size() / 4;
+      for (int32_t c = c0; c < c1; ++c) {
+        const int32_t seam = segs[(size_t)c * 8 + 2];
+        for (int32_t t0 = 0; t0 < chunk_lens[c]; t0 += kKeyAlign) {
+          if (t0 + kKeyAlign <= seam) continue;
+          kblocks.insert(kblocks.end(), {c, t0, chunk_off[c + b] + t0, 0});
+        }
+      }
+      if ((int64_t)kblocks.size() / 4 > kMaxI32) return PIC_EINVAL;
+    }
+    kb_fresh[n_req] = kb_pool[n_req] = (int64_t)kblocks.size() / 4;
+  }
+
   // ---- attention tiles ----
   const int32_t tile_rows = PIC_ATTN_TILE_M / group;
   std::vector<AttnTile> tiles;
@@ -216,6 +260,8 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
       t.tok_base = req_tok_ptr[b];
       t.p_first = rows[r0];
       t.p_last = rows[r0 + t.n_rows - 1];
+      t.pad0 = req_row_ptr[b];                       // first fresh row of the request
+      t.pad1 = req_row_ptr[b + 1] - req_row_ptr[b];  // fresh rows of the request
       tiles.push_back(t);
     }
   }
@@ -235,7 +281,51 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   std::vector<AttnItem> items;
   std::vector<MergeEntry> merges;
   int64_t n_partials = 0;
-  for (int32_t ti = 0; ti < (int32_t)tiles.size(); ++ti) {
+  if (paged) {
+    // Item ranges follow a per-request grid of seg_len keys over the pool blocks; the
+    // first range also carries the fresh blocks (second block range of the item).
+    const int64_t per_range = std::max<int64_t>(1, seg_len / kKeyAlign);
+    for (int32_t ti = 0; ti < (int32_t)tiles.size(); ++ti) {
+      const AttnTile &t = tiles[ti];
+      const int32_t b = t.req;
+      auto needed = [&](int64_t lo, int64_t hi) {  // blocks of [lo, hi) starting <= p_last
+        int64_t n = 0;
+        while (lo + n < hi && kblocks[(size_t)(lo + n) * 4 + 2] <= t.p_last) ++n;
+        return n;
+      };
+      const int64_t n_fresh = needed(kb_fresh[b], kb_pool[b]);
+      const int64_t n_pool = needed(kb_pool[b], kb_fresh[b + 1]);
+      const int64_t n_ranges = std::max<int64_t>(1, (n_pool + per_range - 1) / per_range);
+      for (int32_t g = 0; g < h_kv; ++g) {
+        const int64_t slot_base = n_partials;
+        for (int64_t r = 0; r < n_ranges; ++r) {
+          AttnItem it{};
+          it.tile = ti;
+          it.kv_head = g;
+          const int64_t p0 = kb_pool[b] + r * per_range;
+          const int64_t p1 = kb_pool[b] + std::min(n_pool, (r + 1) * per_range);
+          if (r == 0) {
+            it.key_begin = (int32_t)kb_fresh[b];
+            it.key_end = (int32_t)(kb_fresh[b] + n_fresh);
+            it.pad0 = (int32_t)p0;
+            it.pad1 = (int32_t)std::max(p0, p1);
+          } else {
+            it.key_begin = (int32_t)p0;
+            it.key_end = (int32_t)p1;
+            it.pad0 = it.pad1 = (int32_t)p1;
+          }
+          it.slot = n_ranges > 1 ? (int32_t)(slot_base + r) : -1;
+          items.push_back(it);
+        }
+        if (n_ranges > 1) {
+          merges.push_back(MergeEntry{ti, g, (int32_t)slot_base, (int32_t)n_ranges});
+          n_partials += n_ranges;
+        }
+      }
+      if (n_partials > kMaxI32 / 2) return PIC_EINVAL;
+    }
+  }
+  for (int32_t ti = 0; !paged && ti < (int32_t)tiles.size(); ++ti) {
     const int64_t keys = (int64_t)tiles[ti].p_last + 1;
     const int64_t n_split = (keys + seg_len - 1) / seg_len;
     for (int32_t g = 0; g < h_kv; ++g) {
@@ -275,6 +365,8 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   const int64_t o_tiles = place((int64_t)tiles.size() * 8);
   const int64_t o_items = place((int64_t)items.size() * 8);
   const int64_t o_merge = place((int64_t)merges.size() * 4);
+  const int64_t o_segs = place((int64_t)segs.size());
+  const int64_t o_kblocks = place((int64_t)kblocks.size());
   if (words > kMaxI32) return PIC_EINVAL;
   *plan_words = words;
   if (plan == nullptr) return PIC_OK;
@@ -309,6 +401,10 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   h[PIC_H_O_ATTN_TILES] = (int32_t)o_tiles;
   h[PIC_H_O_ATTN_ITEMS] = (int32_t)o_items;
   h[PIC_H_O_MERGE] = (int32_t)o_merge;
+  h[PIC_H_PAGED] = paged ? 1 : 0;
+  h[PIC_H_O_SEGS] = (int32_t)o_segs;
+  h[PIC_H_N_KBLOCKS] = (int32_t)(kblocks.size() / 4);
+  h[PIC_H_O_KBLOCKS] = (int32_t)o_kblocks;
   if (n_req > 0) std::memcpy(h + o_rcp, req_chunk_ptr, sizeof(int32_t) * (n_req + 1));
   else h[o_rcp] = 0;
   if (!chunk_off.empty()) std::memcpy(h + o_coff, chunk_off.data(), sizeof(int32_t) * chunk_off.size());
@@ -322,6 +418,8 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   if (!tiles.empty()) std::memcpy(h + o_tiles, tiles.data(), sizeof(AttnTile) * tiles.size());
   if (!items.empty()) std::memcpy(h + o_items, items.data(), sizeof(AttnItem) * items.size());
   if (!merges.empty()) std::memcpy(h + o_merge, merges.data(), sizeof(MergeEntry) * merges.size());
+  if (!segs.empty()) std::memcpy(h + o_segs, segs.data(), sizeof(int32_t) * segs.size());
+  if (!kblocks.empty()) std::memcpy(h + o_kblocks, kblocks.data(), sizeof(int32_t) * kblocks.size());
   return PIC_OK;
 }
 

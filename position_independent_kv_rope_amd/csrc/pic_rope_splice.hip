@@ -25,34 +25,6 @@ namespace {
 
 constexpr int kRopeThreads = 256;
 constexpr int kRopeUnroll = 4;
-constexpr int kMaxPairs = 128;  // head_dim <= 256
-
-struct ThetaTable {
-  float hi[kMaxPairs];
-  float lo[kMaxPairs];
-};
-
-// 2*pi = kTwoPi1 + kTwoPi2 + kTwoPi3 to ~1e-22; kTwoPi1 has its low bits such that
-// n * kTwoPi1 subtracted from an fp32 angle by one FMA is exact for |n| < 2^24.
-constexpr float kTwoPi1 = 6.2831854820251465f;
-constexpr float kTwoPi2 = -1.7484555314695172e-07f;
-constexpr float kTwoPi3 = -6.8604980400235275e-15f;
-constexpr float kInvTwoPi = 0.15915493667125702f;
-
-__device__ __forceinline__ float2 delta_cos_sin(int delta, float th_hi, float th_lo) {
-  const float d = (float)delta;           // exact: |delta| <= 2^24 is enforced by the planner
-  const float p = d * th_hi;
-  const float e = fmaf(d, th_hi, -p);     // exact rounding error of d * th_hi
-  const float tail = fmaf(d, th_lo, e);   // small remainder of the angle
-  const float n = rintf(p * kInvTwoPi);
-  float r = fmaf(-n, kTwoPi1, p);         // exact
-  r = fmaf(-n, kTwoPi2, r);
-  r = r + fmaf(-n, kTwoPi3, tail);
-  float s, c;
-  sincosf(r, &s, &c);
-  return make_float2(c, s);
-}
-
 // 8 consecutive elements <-> 8 floats.
 __device__ __forceinline__ void load8(const __bf16 *p, float (&x)[8]) {
   const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
@@ -204,12 +176,7 @@ extern "C" int pic_rope_delta(const int32_t *plan_host, const int32_t *plan_dev,
   if (h[PIC_H_N_ROPE_TILES] == 0) return PIC_OK;
   if (plan_dev == nullptr || k == nullptr) return PIC_EINVAL;
 
-  ThetaTable theta{};
-  for (int i = 0; i < head_dim / 2; ++i) {
-    const double th = std::pow(rope_base, -2.0 * i / (double)head_dim);
-    theta.hi[i] = (float)th;
-    theta.lo[i] = (float)(th - (double)theta.hi[i]);
-  }
+  const ThetaTable theta = make_theta(head_dim, rope_base);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == PIC_BF16) return launch_rope<__bf16>(h, plan_dev, k, head_dim, rope_layout, theta, s);
   return launch_rope<float>(h, plan_dev, k, head_dim, rope_layout, theta, s);

@@ -55,13 +55,13 @@ def _build_raw(rcp, lens, ql, k, h_q=4, h_kv=4, pos_base=0, cap=None):
     words = ctypes.c_int64(0)
     ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p) if a.size else None
     n_req = len(ql)
-    st0 = L.pic_build_index(n_req, ptr(rcp), ptr(lens), ptr(ql), k, pos_base, h_q, h_kv, 0,
-                            None, 0, ctypes.byref(words))
+    st0 = L.pic_build_index(n_req, ptr(rcp), ptr(lens), ptr(ql), None, k, pos_base, h_q, h_kv,
+                            0, None, 0, ctypes.byref(words))
     if st0 != 0 or cap is None:
         return st0, words.value
     buf = np.full(max(cap, 1), 0x5A5A5A5A, dtype=np.int32)
-    st1 = L.pic_build_index(n_req, ptr(rcp), ptr(lens), ptr(ql), k, pos_base, h_q, h_kv, 0,
-                            ptr(buf), cap, ctypes.byref(words))
+    st1 = L.pic_build_index(n_req, ptr(rcp), ptr(lens), ptr(ql), None, k, pos_base, h_q, h_kv,
+                            0, ptr(buf), cap, ctypes.byref(words))
     return st1, buf
 
 
@@ -235,3 +235,67 @@ def test_plan_epic_sweep_sizes():
        st.sampled_from([(32, 8), (32, 4), (4, 4), (8, 1), (16, 16)]), st.integers(-5, 5))
 def test_plan_property(reqs, qs, k, heads, pos_base):
     check_plan(reqs, qs[:len(reqs)], k, heads[0], heads[1], pos_base=pos_base, n_cu=8)
+
+
+# ---------------------------------------------------------------------------
+# Paged plans (shared chunk pool)
+# ---------------------------------------------------------------------------
+
+
+def check_paged_plan(reqs, ids, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0):
+    plan = P.pic_build_index(reqs, q_lens, k, h_q, h_kv, pos_base=pos_base, n_cu=n_cu,
+                             chunk_ids_per_req=ids)
+    assert plan.paged and plan[P.H_N_ROPE_TILES] == 0
+    flat_rows = [r for lens, q in zip(reqs, q_lens) for r in O.recompute_positions(lens, q, k)]
+    assert plan.rows.tolist() == flat_rows
+    segs = plan.segments.tolist()
+    kb = plan.kblocks.tolist()
+    c = 0
+    req_row_ptr = plan.req_row_ptr.tolist()
+    for b, (lens, q) in enumerate(zip(reqs, q_lens)):
+        offs = O.chunk_offsets(lens)
+        for j, L in enumerate(lens):
+            off, ln, seam, cid, delta, req = segs[c][:6]
+            assert (off, ln, req, cid) == (offs[j], L, b, ids[b][j])
+            assert seam == (0 if j == 0 else min(k, L)) and delta == offs[j] - pos_base
+            c += 1
+    # every key a request can see is covered exactly once: fresh rows by fresh blocks,
+    # pool rows t >= n_seam by pool blocks (blocks may also hold masked keys)
+    for b, (lens, q) in enumerate(zip(reqs, q_lens)):
+        n_fresh = req_row_ptr[b + 1] - req_row_ptr[b]
+        fresh_cov, pool_cov = [], []
+        c0 = sum(len(r) for r in reqs[:b])
+        for chunk, t0, first_pos, _ in kb:
+            if chunk == -1:
+                continue
+            if segs[chunk][5] == b:
+                off, ln, seam = segs[chunk][:3]
+                assert first_pos == off + t0
+                pool_cov += [off + t for t in range(t0, min(t0 + 64, ln)) if t >= seam]
+        rows_b = flat_rows[req_row_ptr[b]:req_row_ptr[b + 1]]
+        want_pool = [p for p in range(sum(lens)) if p not in set(rows_b)]
+        assert sorted(pool_cov) == want_pool
+    # items: per (tile, head) the block ranges cover the needed fresh and pool blocks
+    tiles = plan.attn_tiles.tolist()
+    for tile, g, b1, e1, slot, b2, e2, _ in plan.attn_items.tolist():
+        assert 0 <= b1 <= e1 and 0 <= b2 <= e2
+        for i in list(range(b1, e1)) + list(range(b2, e2)):
+            assert kb[i][2] <= tiles[tile][5]  # no block starts after the tile's last row
+    return plan
+
+
+def test_paged_plan_small():
+    check_paged_plan([[37, 64, 5, 130], [70, 70]], [[3, 0, 7, 2], [2, 5]], [9, 4], 8, 32, 4)
+    check_paged_plan([[4, 5, 5]], [[0, 1, 2]], [3], 2, 4, 4, pos_base=3)
+
+
+def test_paged_plan_shared_pool_workload():
+    from position_independent_kv_rope_amd import workloads as W
+    wl = W.shared_pool()
+    check_paged_plan([r.chunk_lens for r in wl.requests], [r.chunk_ids for r in wl.requests],
+                     [r.q_len for r in wl.requests], wl.k, wl.h_q, wl.h_kv, n_cu=256)
+
+
+def test_paged_plan_rejects_negative_ids():
+    with pytest.raises(P.PicError):
+        P.pic_build_index([[4, 5]], [1], 2, 4, 4, chunk_ids_per_req=[[0, -1]])

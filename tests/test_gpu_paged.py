@@ -1,0 +1,155 @@
+"""GPU parity of the paged shared-chunk path (pic_selective_attn_paged) against the
+oracle: chunks gathered from the pool, rotated by R(delta_c), spliced with the fresh
+rows, then selective attention -- bf16 I/O, max-abs <= 2e-2.  The pool is read-only:
+it is checked to be bit-identical after the call."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import position_independent_kv_rope_amd as P
+from position_independent_kv_rope_amd import workloads as W
+from oracle import pic_oracle as O
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    P.lib()
+
+
+def say(*a):
+    print("[gpu-paged]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t):
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def run_paged(wl, layout="adjacent", pos_base=0, nan_slack=False, n_cu=0, sample_rows=None):
+    reqs = [r.chunk_lens for r in wl.requests]
+    ids = [r.chunk_ids for r in wl.requests]
+    qs = [r.q_len for r in wl.requests]
+    plan = P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, pos_base=pos_base, n_cu=n_cu,
+                             chunk_ids_per_req=ids)
+    plan.to_device()
+    cbp, blocks = W.pool_block_table(wl)
+    pk, pv = W.pool_tensors(wl)
+    # the block table the kernel walks: enough blocks per chunk, ids inside the pool
+    bs = wl.block_size
+    assert len(cbp) == len(wl.pool_lens) + 1
+    assert all(cbp[i + 1] - cbp[i] >= -(-L // bs) for i, L in enumerate(wl.pool_lens))
+    assert blocks.min(initial=0) >= 0 and blocks.max(initial=0) < pk.shape[0]
+    assert all(0 <= c < len(wl.pool_lens) for r in wl.requests for c in r.chunk_ids)
+    if nan_slack:  # slots past a chunk's length hold NaN: they must not leak into outputs
+        bs = wl.block_size
+        for i, L in enumerate(wl.pool_lens):
+            if L % bs:
+                last = blocks[cbp[i + 1] - 1]
+                pk[last, L % bs:] = float("nan")
+                pv[last, L % bs:] = float("nan")
+    q, kf, vf = W.fresh_tensors(wl, plan.n_rows)
+    dev = "cuda"
+    pkd, pvd = pk.to(dev), pv.to(dev)
+    out = torch.full((plan.n_rows, wl.h_q, wl.head_dim), float("nan"), dtype=q.dtype, device=dev)
+    ws = P.attn_workspace(plan, wl.head_dim)
+    say(wl.name, "k=%d" % wl.k, layout, "pos_base=%d" % pos_base, "items=%d merges=%d" %
+        (plan[P.H_N_ATTN_ITEMS], plan[P.H_N_MERGE]))
+    lay = P.PIC_ROPE_HALF if layout == "half" else P.PIC_ROPE_ADJACENT
+    P.pic_selective_attn_paged(plan, q.to(dev), pkd, pvd, torch.from_numpy(cbp).to(dev),
+                               torch.from_numpy(blocks).to(dev), kf.to(dev), vf.to(dev), out,
+                               wl.rope_base, layout=lay, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(pkd.cpu()), torch.nan_to_num(pk))  # pool untouched
+    assert torch.equal(torch.nan_to_num(pvd.cpu()), torch.nan_to_num(pv))
+    got_all = out.cpu()
+    pk64, pv64 = f64(pk), f64(pv)
+    worst = 0.0
+    bs = wl.block_size
+    for b, r in enumerate(wl.requests):
+        row0, row1 = int(plan.req_row_ptr[b]), int(plan.req_row_ptr[b + 1])
+        rows = O.recompute_positions(r.chunk_lens, r.q_len, wl.k)
+        assert plan.rows[row0:row1].tolist() == rows
+        if row1 == row0:
+            continue
+        ck = [O.gather_paged_chunk(pk64, blocks[cbp[i]:cbp[i + 1]], wl.pool_lens[i]) for i in r.chunk_ids]
+        cv = [O.gather_paged_chunk(pv64, blocks[cbp[i]:cbp[i + 1]], wl.pool_lens[i]) for i in r.chunk_ids]
+        offs = O.chunk_offsets(r.chunk_lens)
+        if ck:
+            k_ctx, v_ctx = O.rope_delta(ck, wl.rope_base, layout, pos_base), O.concat_chunks(cv)
+        else:  # a request with only query tokens
+            k_ctx = v_ctx = np.zeros((0, wl.h_kv, wl.head_dim))
+        kx, vx = O.splice(k_ctx, v_ctx, f64(kf[row0:row1]), f64(vf[row0:row1]), rows,
+                          offs[-1] + r.q_len)
+        qb = f64(q[row0:row1])
+        if sample_rows is None:
+            want = O.selective_attn(qb, kx, vx, rows)
+            got = f64(got_all[row0:row1])
+        else:
+            rng = np.random.default_rng(77 + b)
+            n = row1 - row0
+            picks = sorted(set(rng.integers(0, n, size=min(sample_rows, n)).tolist()) | {0, n - 1})
+            heads = rng.integers(0, wl.h_q, size=len(picks))
+            want = O.attn_rows_direct([qb[i, h] for i, h in zip(picks, heads)], kx, vx,
+                                      [rows[i] for i in picks], heads // (wl.h_q // wl.h_kv))
+            got = np.stack([f64(got_all[row0 + i, h]) for i, h in zip(picks, heads)])
+        assert np.isfinite(got).all()
+        err = float(np.max(np.abs(got - want)))
+        worst = max(worst, err)
+        if sample_rows is not None:
+            say("request", b, "max-abs error", err)
+        assert err <= TOL, ("paged attention", b, err)
+    say(wl.name, "max-abs error", worst)
+    return worst
+
+
+def small_pool(k, h_q=32, h_kv=4, d=128, seed=31, lens=None, n_req=3):
+    rng = np.random.default_rng(seed)
+    lens = lens or [17, 33, 5, 64, 100, 48, 16, 1, 130, 77, 64, 15]
+    reqs = []
+    for b in range(n_req):
+        m = int(rng.integers(2, len(lens)))
+        ids = [int(x) for x in rng.permutation(len(lens))[:m]]
+        reqs.append(W.Request([lens[i] for i in ids], int(rng.integers(1, 40)), chunk_ids=ids))
+    return W.Workload("small_pool", "bf16", h_q, h_kv, d, 500000.0, k, reqs, pool_lens=lens,
+                      block_size=16, pool_block_perm_seed=seed + 1, seed=seed)
+
+
+@pytest.mark.parametrize("k", [8, 3])
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_paged_small(k, layout):
+    run_paged(small_pool(k), layout)
+
+
+def test_paged_nan_slack_and_pos_base():
+    run_paged(small_pool(8, seed=41), nan_slack=True)
+    run_paged(small_pool(0, h_q=16, h_kv=4, seed=43), pos_base=4)
+
+
+def test_paged_edge_requests():
+    # a lone chunk without query tokens, a request without chunks, a chunk used twice in
+    # one request, chunks shorter than the seam window and exactly one pool block long
+    lens = [16, 3, 200, 64, 1]
+    reqs = [W.Request([200], 0, chunk_ids=[2]),
+            W.Request([], 5, chunk_ids=[]),
+            W.Request([16, 3, 16, 64, 1, 200], 7, chunk_ids=[0, 1, 0, 3, 4, 2])]
+    wl = W.Workload("paged_edges", "bf16", 8, 2, 128, 10000.0, 8, reqs, pool_lens=lens,
+                    block_size=16, pool_block_perm_seed=3, seed=53)
+    run_paged(wl)
+
+
+def test_paged_gqa4_d64():
+    run_paged(small_pool(4, h_q=32, h_kv=8, d=64, seed=47))
+
+
+def test_paged_shared_pool_full_size_sampled():
+    # the shared-pool workload (256 pooled chunks, 8 requests x ~116k tokens, w = 8) in
+    # the launch configuration bench.py times (n_cu = 256), sampled rows
+    run_paged(W.shared_pool(), n_cu=256, sample_rows=24)
