@@ -7,6 +7,12 @@ are resident in HBM before the timed region.  Prints ONE JSON line.
 
 Default workload: 4 independent requests of ~50k tokens each (chunks of 512-2048
 tokens, 256 query tokens), GQA 32/8, head_dim 128, bf16, k = 16.
+
+--workload shared_pool: 256 chunks stored once in a paged pool of 16-token blocks,
+8 requests each splicing 96-128 of them (~116k tokens) + 128 query tokens, seam
+window w = 8, GQA 32/4.  The pool is never rotated or written: one step is the
+planner, the plan upload and pic_selective_attn_paged (rotation on load, fresh rows
+read in place).
 """
 
 import argparse
@@ -31,8 +37,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="epic_sweep",
-                    choices=["rag_single", "long_context", "epic_sweep"])
-    ap.add_argument("--k", type=int, default=16)
+                    choices=["rag_single", "long_context", "epic_sweep", "shared_pool"])
+    ap.add_argument("--k", type=int, default=None,
+                    help="recompute count (default 16; the seam window 8 for shared_pool)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="recomputed rows of request 0 the oracle times (0 = all)")
@@ -56,6 +63,9 @@ def copy_calibration():
 
 def make_workload(name, k):
     from position_independent_kv_rope_amd import workloads as W
+    if name == "shared_pool":
+        return W.shared_pool(w=8 if k is None else k)
+    k = 16 if k is None else k
     if name == "rag_single":
         wl = W.rag_single()
         wl.k = k
@@ -121,6 +131,133 @@ def cpu_baseline(wl, k_in, v_in, q, kf, vf, plan, sample_rows):
             "host_cpus": os.cpu_count()}
 
 
+def cpu_baseline_paged(wl, pk, pv, cbp, blocks, q, kf, vf, plan, sample_rows):
+    """Time the CPU oracle (as it stands) on request 0 of the paged batch: gather of the
+    request's chunks from the pool, rotation, splice and selective attention."""
+    import torch
+    from threadpoolctl import threadpool_info
+    from oracle import pic_oracle as O
+    r = wl.requests[0]
+    row0, row1 = int(plan.req_row_ptr[0]), int(plan.req_row_ptr[1])
+    f64 = lambda t: t.to(torch.float64).numpy()
+    # the request's pool blocks only (the rest of the pool is not part of its work)
+    t0 = time.perf_counter()
+    ck, cv = [], []
+    for i in r.chunk_ids:
+        ids = blocks[cbp[i]:cbp[i + 1]]
+        sub = torch.from_numpy(ids.astype(np.int64))
+        ck.append(O.gather_paged_chunk(f64(pk[sub]), np.arange(len(ids)), wl.pool_lens[i]))
+        cv.append(O.gather_paged_chunk(f64(pv[sub]), np.arange(len(ids)), wl.pool_lens[i]))
+    rows = O.recompute_positions(r.chunk_lens, r.q_len, wl.k)
+    offs = O.chunk_offsets(r.chunk_lens)
+    k_ctx = O.rope_delta(ck, wl.rope_base)
+    v_ctx = O.concat_chunks(cv)
+    kx, vx = O.splice(k_ctx, v_ctx, f64(kf[row0:row1]), f64(vf[row0:row1]), rows,
+                      offs[-1] + r.q_len)
+    n_att = len(rows) if sample_rows <= 0 else min(sample_rows, len(rows))
+    sel = slice(len(rows) - n_att, len(rows))
+    O.selective_attn(f64(q[row0:row1])[sel], kx, vx, rows[sel])
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    n_tokens = offs[-1] + r.q_len
+    return {"value": n_tokens / dt if n_att == len(rows) else None, "unit": "tokens/s",
+            "cores": int(threads), "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "request 0 of the batch (%d tokens in %d pooled chunks, %d of %d "
+                      "recomputed rows), fp64 NumPy oracle: pool gather, index, rotation, "
+                      "splice and selective attention"
+                      % (n_tokens, len(r.chunk_ids), n_att, len(rows)),
+            "host_cpus": os.cpu_count()}
+
+
+def bench_paged(args, wl):
+    import torch
+    import position_independent_kv_rope_amd as P
+    from position_independent_kv_rope_amd import workloads as W
+    reqs = [r.chunk_lens for r in wl.requests]
+    ids = [r.chunk_ids for r in wl.requests]
+    qs = [r.q_len for r in wl.requests]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, n_cu=n_cu, chunk_ids_per_req=ids)
+    cbp, blocks = W.pool_block_table(wl)
+    pk_h, pv_h = W.pool_tensors(wl)
+    q_h, kf_h, vf_h = W.fresh_tensors(wl, plan.n_rows)
+    dev = "cuda"
+    pk, pv = pk_h.to(dev), pv_h.to(dev)
+    cbp_d, blocks_d = torch.from_numpy(cbp).to(dev), torch.from_numpy(blocks).to(dev)
+    q, kf, vf = q_h.to(dev), kf_h.to(dev), vf_h.to(dev)
+    out = torch.empty_like(q)
+    ws = P.attn_workspace(plan, wl.head_dim)
+    plan_dev = torch.empty(plan.words.size, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    s = wl.torch_dtype.itemsize
+    D, hq, hkv = wl.head_dim, wl.h_q, wl.h_kv
+    rows = plan.rows.astype(np.int64)
+    attn_flops = 4.0 * D * hq * float(np.sum(rows + 1))
+    # every request reads its chunks' K/V once, plus Q and O of the recomputed rows
+    attn_bytes = 2.0 * s * hkv * D * plan.n_tokens + 2.0 * s * hq * D * plan.n_rows
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+
+    def step(i=None):
+        p = P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, n_cu=n_cu, chunk_ids_per_req=ids)
+        plan_dev.copy_(torch.from_numpy(p.words))
+        p.dev = plan_dev
+        e = ev[i] if i is not None else None
+        if e: e[0].record()
+        P.pic_selective_attn_paged(p, q, pk, pv, cbp_d, blocks_d, kf, vf, out, wl.rope_base,
+                                   workspace=ws)
+        if e: e[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / args.steps
+    t_attn = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    tokens = plan.n_tokens
+    attn_tflops = attn_flops / (t_attn * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": "shared_pool", "requests": len(wl.requests), "tokens": tokens,
+                   "pool_chunks": len(wl.pool_lens), "pool_blocks": int(blocks.size),
+                   "block_size": wl.block_size, "recomputed_rows": plan.n_rows,
+                   "seam_window": wl.k, "h_q": hq, "h_kv": hkv, "head_dim": D,
+                   "rope_base": wl.rope_base, "parallelism": "none (1 GPU)"},
+        "attn_tflops": round(attn_tflops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
+                     "traffic": load_traffic("attn_paged", "shared_pool_k%d" % wl.k),
+                     "kernel": "pic_selective_attn_paged call (paged_angles_kernel + "
+                               "attn_bf16_paged_kernel + merge_kernel)",
+                     "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes},
+        "kernels": {
+            "selective_attn_paged": {"ms": round(t_attn, 4), "flops": attn_flops,
+                                     "TFLOP_s": round(attn_tflops, 2),
+                                     "items": plan[P.H_N_ATTN_ITEMS], "merges": plan[P.H_N_MERGE]},
+            "host_plan_and_upload_ms": round(ms_step - t_attn, 4),
+        },
+    }
+    rec["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_paged(
+        wl, pk_h, pv_h, cbp, blocks, q_h, kf_h, vf_h, plan, args.cpu_sample_rows)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -138,6 +275,8 @@ def main():
         sys.exit(1)
     P.lib()
     wl = make_workload(args.workload, args.k)
+    if wl.pool_lens is not None:
+        return bench_paged(args, wl)
     reqs = [r.chunk_lens for r in wl.requests]
     qs = [r.q_len for r in wl.requests]
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count

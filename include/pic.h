@@ -198,7 +198,9 @@ size_t pic_attn_workspace_bytes(const int32_t *plan_host, int32_t head_dim);
  * accumulation and an fp32 online softmax; f32 runs fp32 MFMA.  head_dim in {64, 128}
  * for bf16, {16, 32, 64, 128} for f32.  workspace: device, >= pic_attn_workspace_bytes
  * (may be NULL when that is 0); contents on entry are ignored.  A paged plan (built with
- * chunk_ids) is rejected with PIC_EINVAL: it needs pic_selective_attn_paged.
+ * chunk_ids) is rejected with PIC_EINVAL: it needs pic_selective_attn_paged.  A request
+ * whose K (or V) rows exceed 2 GiB (N_b * h_kv * head_dim * dtype size) is
+ * PIC_EUNSUPPORTED (32-bit buffer offsets).
  */
 int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_dev, const void *q,
                        const void *k, const void *v, void *out, int32_t dtype,

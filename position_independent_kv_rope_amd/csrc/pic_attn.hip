@@ -1132,6 +1132,10 @@ extern "C" int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_
   if (!h.valid() || h[PIC_H_PAGED]) return PIC_EINVAL;
   if (dtype != PIC_BF16 && dtype != PIC_F32) return PIC_EINVAL;
   if (!(scale > 0.f) || !std::isfinite(scale) || head_dim <= 0) return PIC_EINVAL;
+  // K/V of one request are addressed with 32-bit byte offsets
+  if ((int64_t)h[PIC_H_MAX_TOKENS] * h[PIC_H_H_KV] * head_dim * (int64_t)dtype_size(dtype) >
+      0x7fff0000LL)
+    return PIC_EUNSUPPORTED;
   if (h[PIC_H_N_ATTN_ITEMS] == 0) return PIC_OK;
   if (!plan_dev || !q || !k || !v || !out) return PIC_EINVAL;
   const size_t need = pic_attn_workspace_bytes(plan_host, head_dim);

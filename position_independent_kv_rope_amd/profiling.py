@@ -25,7 +25,8 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SHORT = [("attn_bf16_kernel", "attn_bf16"), ("attn_f32_kernel", "attn_f32"),
+SHORT = [("attn_bf16_paged_kernel", "attn_bf16_paged"), ("paged_angles_kernel", "paged_angles"),
+         ("attn_bf16_kernel", "attn_bf16"), ("attn_f32_kernel", "attn_f32"),
          ("merge_kernel", "merge"), ("rope_delta_kernel", "rope_delta"),
          ("splice_kernel", "splice"), ("copyBuffer", "copy (calibration)")]
 
