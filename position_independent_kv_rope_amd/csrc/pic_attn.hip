@@ -205,7 +205,9 @@ __device__ __forceinline__ void attn_bf16_body(
 
   // Mask, online softmax and O^T += V^T P^T for the block starting at key kb0; S^T of
   // the next block (K buffer Knext) is computed into s_nxt meanwhile, its 16 MFMAs
-  // interleaved with the 32 exponentials (after the last block the result is unused).  The running max m_run is only moved when a
+  // interleaved with the 32 exponentials and each K operand read two MFMAs ahead
+  // (after the last block the result is unused); the PV MFMAs read their transposed V
+  // operands two ahead as well.  The running max m_run is only moved when a
   // column's block max exceeds it by more than kLazy (log2 units), so rescaling the
   // accumulators is rare; probabilities then stay below 2^kLazy, far inside fp32/bf16
   // range, and the final normalisation is unchanged (acc and l share the reference).
@@ -244,12 +246,19 @@ __device__ __forceinline__ void attn_bf16_body(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s_nxt[t][j] = 0.f;
+    constexpr int kPre = 2;  // K operand reads in flight ahead of their MFMA
+    bf16x8 kop[2 * kKS];
+    auto kload = [&](int q) {
+      kop[q] = *reinterpret_cast<const bf16x8 *>(Knext + koff[q >> 1] + (q & 1) * 32 * kRowB);
+    };
+#pragma unroll
+    for (int q = 0; q < kPre; ++q) kload(q);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       if (q < 2 * kKS) {  // S^T MFMAs of the next block, one per pair; tiles alternate
+        if (q + kPre < 2 * kKS) kload(q + kPre);
         const int t = q & 1, s = q >> 1;
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Knext + koff[s] + t * 32 * kRowB);
-        s_nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], s_nxt[t], 0, 0, 0);
+        s_nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[q], qop[s], s_nxt[t], 0, 0, 0);
       }
       const int t = q >> 3, j = 2 * (q & 7);
       bf16x2v pr;
@@ -262,25 +271,37 @@ __device__ __forceinline__ void attn_bf16_body(
     }
     // keep the schedule interleaved: per pair, its K read, one MFMA, the VALU work
 #pragma unroll
+    for (int q = 0; q < kPre; ++q) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
     for (int q = 0; q < 2 * kKS; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      if (q + kPre < 2 * kKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
     }
     l_lane += ps0 + ps1;
     __builtin_amdgcn_s_setprio(1);
+    constexpr int kPreV = 2;  // V operands in flight ahead of their MFMA
+    bf16x8 vop[4 * kDB];
+    auto vload = [&](int o) {
+      const char *vr = Vb + voff[o % kDB] + (o / kDB) * 16 * kRowB;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vr);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 4 * kRowB));
+      __builtin_memcpy(&vop[o], &lo, 8);
+      __builtin_memcpy(reinterpret_cast<char *>(&vop[o]) + 8, &hi, 8);
+    };
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int o = 0; o < kPreV; ++o) vload(o);
 #pragma unroll
-      for (int d = 0; d < kDB; ++d) {
-        const char *vr = Vb + voff[d] + c * 16 * kRowB;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vr);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 4 * kRowB));
-        bf16x8 a;
-        __builtin_memcpy(&a, &lo, 8);
-        __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &hi, 8);
-        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[d], 0, 0, 0);
-      }
+    for (int o = 0; o < 4 * kDB; ++o) {
+      if (o + kPreV < 4 * kDB) vload(o + kPreV);
+      acc[o % kDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[o], pb[o / kDB], acc[o % kDB], 0, 0, 0);
+    }
+#pragma unroll
+    for (int o = 0; o < kPreV; ++o) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int o = 0; o < 4 * kDB; ++o) {
+      if (o + kPreV < 4 * kDB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -637,12 +658,19 @@ __device__ __forceinline__ void attn_bf16_paged_body(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s_nxt[t][j] = 0.f;
+    constexpr int kPre = 2;  // K operand reads in flight ahead of their MFMA
+    bf16x8 kop[2 * kKS];
+    auto kload = [&](int q) {
+      kop[q] = *reinterpret_cast<const bf16x8 *>(Knext + koff[q >> 1] + (q & 1) * 32 * kRowB);
+    };
+#pragma unroll
+    for (int q = 0; q < kPre; ++q) kload(q);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       if (q < 2 * kKS) {
+        if (q + kPre < 2 * kKS) kload(q + kPre);
         const int t = q & 1, s = q >> 1;
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Knext + koff[s] + t * 32 * kRowB);
-        s_nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], s_nxt[t], 0, 0, 0);
+        s_nxt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[q], qop[s], s_nxt[t], 0, 0, 0);
       }
       const int t = q >> 3, j = 2 * (q & 7);
       bf16x2v pr;
@@ -654,8 +682,10 @@ __device__ __forceinline__ void attn_bf16_paged_body(
       else ps0 = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps0, false);
     }
 #pragma unroll
+    for (int q = 0; q < kPre; ++q) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
     for (int q = 0; q < 2 * kKS; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (q + kPre < 2 * kKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
