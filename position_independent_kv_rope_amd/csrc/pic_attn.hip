@@ -205,7 +205,7 @@ __device__ __forceinline__ void attn_bf16_body(
 
   // Mask, online softmax and O^T += V^T P^T for the block starting at key kb0; S^T of
   // the next block (K buffer Knext) is computed into s_nxt meanwhile, its 16 MFMAs
-  // interleaved with the 32 exponentials and each K operand read two MFMAs ahead
+  // interleaved with the 32 exponentials and each K operand read eight MFMAs ahead
   // (after the last block the result is unused); the PV MFMAs read their transposed V
   // operands two ahead as well.  The running max m_run is only moved when a
   // column's block max exceeds it by more than kLazy (log2 units), so rescaling the
@@ -246,7 +246,7 @@ __device__ __forceinline__ void attn_bf16_body(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) s_nxt[t][j] = 0.f;
-    constexpr int kPre = 2;  // K operand reads in flight ahead of their MFMA
+    constexpr int kPre = 8;  // K operand reads in flight ahead of their MFMA
     bf16x8 kop[2 * kKS];
     auto kload = [&](int q) {
       kop[q] = *reinterpret_cast<const bf16x8 *>(Knext + koff[q >> 1] + (q & 1) * 32 * kRowB);
@@ -276,7 +276,7 @@ __device__ __forceinline__ void attn_bf16_body(
     for (int q = 0; q < 2 * kKS; ++q) {
       if (q + kPre < 2 * kKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
     }
     l_lane += ps0 + ps1;
     __builtin_amdgcn_s_setprio(1);
