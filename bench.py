@@ -42,6 +42,10 @@ def parse():
                     choices=["rag_single", "long_context", "epic_sweep", "shared_pool"])
     ap.add_argument("--k", type=int, default=None,
                     help="recompute count (default 16; the seam window 8 for shared_pool)")
+    ap.add_argument("--rope-scheme", default="delta", choices=["delta", "nope"],
+                    help="delta: cached K carries RoPE at local positions and is rotated by "
+                         "delta (pic_rope_delta); nope: cached K is position-free and gets "
+                         "RoPE at the target positions (pic_rope_apply)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="recomputed rows of request 0 the oracle times (0 = all)")
@@ -130,7 +134,7 @@ class PlanUploader:
         return plan
 
 
-def cpu_baseline(wl, k_in, v_in, q, kf, vf, plan, sample_rows):
+def cpu_baseline(wl, k_in, v_in, q, kf, vf, plan, sample_rows, scheme="delta"):
     """Time the CPU oracle (as it stands) on request 0 of the same inputs."""
     import torch
     from threadpoolctl import threadpool_info
@@ -146,7 +150,7 @@ def cpu_baseline(wl, k_in, v_in, q, kf, vf, plan, sample_rows):
     cv = [vin[offs[c]:offs[c + 1]] for c in range(len(r.chunk_lens))]
     t0 = time.perf_counter()
     rows = O.recompute_positions(r.chunk_lens, r.q_len, wl.k)
-    k_ctx = O.rope_delta(ck, wl.rope_base)
+    k_ctx = O.rope_apply(ck, wl.rope_base) if scheme == "nope" else O.rope_delta(ck, wl.rope_base)
     v_ctx = O.concat_chunks(cv)
     kx, vx = O.splice(k_ctx, v_ctx, f64(kf[row0:row1]), f64(vf[row0:row1]), rows,
                       offs[-1] + r.q_len)
@@ -333,7 +337,10 @@ def main():
     D, hq, hkv = wl.head_dim, wl.h_q, wl.h_kv
     rows = plan.rows.astype(np.int64)
     attn_flops = 4.0 * D * hq * float(np.sum(rows + 1))
-    rope_rows = int(plan.rope_tiles[:, 1].sum()) if plan[P.H_N_ROPE_TILES] else 0
+    tiles = plan.rope_tiles if plan[P.H_N_ROPE_TILES] else np.zeros((0, 4), dtype=np.int64)
+    # rows the rotation touches: tiles with delta != 0 (by delta), every kept row (nope)
+    rotated = tiles if args.rope_scheme == "nope" else tiles[tiles[:, 2] != 0]
+    rope_rows = int(rotated[:, 1].sum())
     rope_bytes = 2.0 * s * hkv * D * rope_rows
     splice_bytes = 4.0 * s * hkv * D * plan.n_rows
     attn_bytes = 2.0 * s * hkv * D * plan.n_tokens + 2.0 * s * hq * D * plan.n_rows
@@ -348,7 +355,10 @@ def main():
         uploader.upload(p)
         e = ev[i] if i is not None else None
         if e: e[0].record()
-        P.pic_rope_delta(p, k, wl.rope_base)
+        if args.rope_scheme == "nope":
+            P.pic_rope_apply(p, k, wl.rope_base)
+        else:
+            P.pic_rope_delta(p, k, wl.rope_base)
         if e: e[1].record()
         P.pic_splice(p, k, v, kf, vf)
         if e: e[2].record()
@@ -388,7 +398,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "requests": len(wl.requests), "tokens": tokens,
                    "recomputed_rows": plan.n_rows, "k": wl.k, "h_q": hq, "h_kv": hkv,
-                   "head_dim": D, "rope_base": wl.rope_base,
+                   "head_dim": D, "rope_base": wl.rope_base, "rope_scheme": args.rope_scheme,
                    "parallelism": "none (1 GPU)"},
         "attn_tflops": round(attn_tflops, 2),
         "splice_pass_tokens_per_s": round(tokens / ((t_rope + t_splice) * 1e-3), 1),
@@ -398,7 +408,8 @@ def main():
                      "kernel": "pic_selective_attn call (attn_bf16_kernel + merge_kernel)",
                      "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes},
         "kernels": {
-            "rope_delta": {"ms": round(t_rope, 4), "bytes": rope_bytes,
+            ("rope_apply" if args.rope_scheme == "nope" else "rope_delta"): {
+                "ms": round(t_rope, 4), "bytes": rope_bytes,
                            "GB_s": round(rope_bytes / (t_rope * 1e-3) / 1e9, 1),
                            "hbm_frac": round(rope_bytes / (t_rope * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
             "splice": {"ms": round(t_splice, 4), "bytes": splice_bytes,
@@ -413,7 +424,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl, k_in, v_in, q_h, kf_h, vf_h, plan,
-                                           args.cpu_sample_rows)
+                                           args.cpu_sample_rows, args.rope_scheme)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

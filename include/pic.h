@@ -104,7 +104,9 @@ enum {
   PIC_H_O_REQ_ROW_PTR,/* [n_req+1] first recomputed row of each request; last = n_rows */
   PIC_H_O_ROWS,       /* [n_rows] request-local global position p_r of each recomputed row */
   PIC_H_O_ROW_TOK,    /* [n_rows] K/V buffer row of each recomputed row (req_tok_ptr[b] + p_r) */
-  PIC_H_O_ROPE_TILES, /* [n_rope_tiles][4]: first K row, row count, delta, chunk index */
+  PIC_H_O_ROPE_TILES, /* [n_rope_tiles][4]: first K row, row count, delta, global position
+                         of the first row; every cached row that keeps its K, <= 32 rows
+                         of one chunk per tile (tiles with delta 0 included) */
   PIC_H_O_ATTN_TILES, /* [n_attn_tiles][8]: req, first row, row count, req_tok_ptr[req],
                          p_first, p_last, req_row_ptr[req], recomputed rows of req */
   PIC_H_O_ATTN_ITEMS, /* [n_attn_items][8]: tile, kv head, key_begin, key_end,
@@ -156,18 +158,32 @@ int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr, const int32_t *
 /*
  * pic_rope_delta -- rotary correction of cached K in place.          [RoPE-C] 3.3
  *
- * For every rope tile of the plan (every chunk with delta_c != 0, cached rows that
- * are not recomputed), each pair of each head of each row is rotated by the angle
+ * For every rope tile of the plan with delta_c != 0 (cached rows that are not
+ * recomputed), each pair of each head of each row is rotated by the angle
  * delta_c * theta_i: one direct rotation, fp32 arithmetic with a double-float
  * angle (theta_i from fp64 on the host, exact product, Cody-Waite reduction),
- * result rounded to the storage type (RNE).  Rows that the splice overwrites are
- * skipped; V is never touched.
+ * result rounded to the storage type (RNE).  Rows that the splice overwrites and
+ * chunks with delta 0 are skipped; V is never touched.
  *
  * plan_host / plan_dev: the same plan on the host and on the device.  k: device
  * buffer [n_tokens, h_kv, head_dim] of dtype.  head_dim even, head_dim % 8 == 0 for
  * PIC_ROPE_ADJACENT and head_dim % 16 == 0 for PIC_ROPE_HALF, 8 <= head_dim <= 256.
  */
 int pic_rope_delta(const int32_t *plan_host, const int32_t *plan_dev, void *k, int32_t dtype,
+                   int32_t head_dim, int32_t rope_layout, double rope_base, void *stream);
+
+/*
+ * pic_rope_apply -- RoPE at the target positions for a position-free cache.
+ *                                                                   [RoPE-C] 3.2
+ * Scheme B: the cache holds K before RoPE ("nope"); on a hit every cached row that is
+ * not recomputed gets RoPE at its global position p = off_c + t (t = row within its
+ * chunk; pos_base plays no role): each pair is rotated by p * theta_i, with the same
+ * double-float fp32 angle, pair layouts, sizes and rounding as pic_rope_delta.  Rows
+ * that the splice overwrites are skipped; V is never touched.  Arguments and errors
+ * as pic_rope_delta, plus PIC_EUNSUPPORTED when a kept row sits at position >= 2^24; k
+ * holds the nope rows on entry and the rotated rows on return.
+ */
+int pic_rope_apply(const int32_t *plan_host, const int32_t *plan_dev, void *k, int32_t dtype,
                    int32_t head_dim, int32_t rope_layout, double rope_base, void *stream);
 
 /*

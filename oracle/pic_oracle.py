@@ -14,7 +14,8 @@ LegoLink / seam-window recompute, written from these pages:
   Step 3 splice and attention), the method/complexity table and the Step 5 k sweep.
 * [RoPE-C] 10100.com article on why RoPE breaks prefix caching: section 2.2 (RoPE
   rotates each adjacent dimension pair by an angle proportional to the position),
-  section 3.3 (scheme C, rotary correction by a delta rotation) and footnote 3
+  section 3.2 (scheme B: cache K before RoPE, apply RoPE at the target positions on a
+  hit), section 3.3 (scheme C, rotary correction by a delta rotation) and footnote 3
   (HF Llama ``inv_freq``).
 * [HYPIC] joto.ai article on HYPIC: section 2.2 (seam window of w tokens at the
   head of every internal segment, default w = 8).
@@ -185,6 +186,17 @@ def rope_delta(cached_k_chunks, base, layout="adjacent", pos_base=0):
     if not parts:
         raise ValueError("at least one chunk is required")
     return np.concatenate(parts, axis=0)
+
+
+def rope_apply(nope_k_chunks, base, layout="adjacent"):
+    """Scheme B ([RoPE-C] 3.2): concatenate the position-free ("nope") cached K of every
+    chunk and apply RoPE at the global positions off_c + t.  Returns [ctx, Hkv, D] fp64.
+    """
+    lens = [int(np.asarray(a).shape[0]) for a in nope_k_chunks]
+    if not lens:
+        raise ValueError("at least one chunk is required")
+    x = np.concatenate([np.asarray(a, dtype=np.float64) for a in nope_k_chunks], axis=0)
+    return rope_rotate(x, np.arange(x.shape[0]), base, layout)
 
 
 def concat_chunks(chunks):

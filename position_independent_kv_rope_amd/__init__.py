@@ -27,7 +27,8 @@ PIC_ATTN_TILE_M = 128
  H_O_ROW_TOK, H_O_ROPE_TILES, H_O_ATTN_TILES, H_O_ATTN_ITEMS, H_O_MERGE, H_PAGED, H_O_SEGS,
  H_N_KBLOCKS, H_O_KBLOCKS) = range(31)
 
-EXPORTED = ("pic_build_index", "pic_rope_delta", "pic_splice", "pic_attn_workspace_bytes",
+EXPORTED = ("pic_build_index", "pic_rope_delta", "pic_rope_apply", "pic_splice",
+            "pic_attn_workspace_bytes",
             "pic_selective_attn", "pic_selective_attn_paged", "pic_strerror")
 
 
@@ -58,6 +59,8 @@ def lib():
     L.pic_build_index.restype = ctypes.c_int
     L.pic_rope_delta.argtypes = [p, p, p, i32, i32, i32, f64, p]
     L.pic_rope_delta.restype = ctypes.c_int
+    L.pic_rope_apply.argtypes = [p, p, p, i32, i32, i32, f64, p]
+    L.pic_rope_apply.restype = ctypes.c_int
     L.pic_splice.argtypes = [p, p, p, p, p, p, i32, i32, p]
     L.pic_splice.restype = ctypes.c_int
     L.pic_attn_workspace_bytes.argtypes = [p, i32]
@@ -234,6 +237,16 @@ def pic_rope_delta(plan, k, rope_base, layout=PIC_ROPE_ADJACENT, stream=None):
     st = lib().pic_rope_delta(plan.host_ptr(), plan.dev_ptr(), _dev(k, "k"), _dtype_code(k),
                               int(k.shape[2]), int(layout), float(rope_base), _stream(stream))
     _check("pic_rope_delta", st)
+
+
+def pic_rope_apply(plan, k, rope_base, layout=PIC_ROPE_ADJACENT, stream=None):
+    """In-place RoPE at the global positions of the kept cached rows of a position-free
+    ("nope") cache k ([n_tokens, h_kv, D]) on the current stream."""
+    if k.shape[0] != plan.n_tokens or k.shape[1] != plan[H_H_KV]:
+        raise ValueError("k shape %s does not match the plan" % (tuple(k.shape),))
+    st = lib().pic_rope_apply(plan.host_ptr(), plan.dev_ptr(), _dev(k, "k"), _dtype_code(k),
+                              int(k.shape[2]), int(layout), float(rope_base), _stream(stream))
+    _check("pic_rope_apply", st)
 
 
 def pic_splice(plan, k, v, k_fresh, v_fresh, stream=None):

@@ -31,7 +31,8 @@ struct MergeEntry {
   int32_t tile, kv_head, slot_base, n_slots;
 };
 struct RopeTile {
-  int32_t tok_begin, n_rows, delta, chunk;
+  int32_t tok_begin, n_rows, delta;
+  int32_t pos0;  // global position (within the request) of the first row
 };
 
 static_assert(sizeof(AttnTile) == 32, "plan record size");

@@ -187,14 +187,14 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
         row_tok[i] = req_tok_ptr[b] + rows[i];
   }
 
-  // ---- rope tiles: cached rows that keep their K, per chunk with delta != 0 ----
+  // ---- rope tiles: every cached row that keeps its K (delta 0 included: rotation by
+  // delta skips those tiles, RoPE at the target position needs them) ----
   std::vector<RopeTile> rope;
   for (int32_t b = 0; b < n_req; ++b) {
     if (paged) break;  // the shared pool is never rotated in place
     const int32_t c0 = req_chunk_ptr[b], c1 = req_chunk_ptr[b + 1];
     for (int32_t c = c0; c < c1; ++c) {
       const int64_t delta = (int64_t)chunk_off[c + b] - pos_base;
-      if (delta == 0) continue;
       // the device forms delta in fp32 exactly, which holds for |delta| <= 2^24
       if (delta > (int64_t(1) << 24) || delta < -(int64_t(1) << 24)) return PIC_EUNSUPPORTED;
       const int32_t skip = (c > c0) ? std::min(k, chunk_lens[c]) : 0;
@@ -203,7 +203,7 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
         rt.tok_begin = req_tok_ptr[b] + chunk_off[c + b] + t;
         rt.n_rows = std::min<int32_t>(PIC_ROPE_TILE_ROWS, chunk_lens[c] - t);
         rt.delta = (int32_t)delta;
-        rt.chunk = c;
+        rt.pos0 = chunk_off[c + b] + t;
         rope.push_back(rt);
       }
     }

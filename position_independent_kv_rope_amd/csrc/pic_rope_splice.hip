@@ -1,4 +1,9 @@
-// Rotary correction of cached K (pic_rope_delta) and the row splice (pic_splice).
+// Rotary correction of cached K (pic_rope_delta), RoPE of a position-free cache at the
+// target positions (pic_rope_apply) and the row splice (pic_splice).
+//
+// Scheme B of the same article (section 3.2) caches K before RoPE and applies RoPE at
+// the target positions on a hit; pic_rope_apply is that path, with one angle per
+// (row, pair) instead of one per pair.
 //
 // Rotary correction follows the 10100.com article on RoPE and prefix caching, section
 // 3.3 (scheme C): a cached K row carrying RoPE at position p is moved to p + delta by
@@ -57,18 +62,30 @@ __device__ __forceinline__ void store8(float *p, const float (&x)[8]) {
   *reinterpret_cast<f32x4 *>(p + 4) = b;
 }
 
-// One workgroup per rope tile (<= PIC_ROPE_TILE_ROWS rows of one chunk, one delta).
+// One workgroup per rope tile (<= PIC_ROPE_TILE_ROWS rows of one chunk).
+// kAbs == false (rotation by delta): one angle delta * theta_i per pair for the whole
+//   tile; tiles with delta 0 return at once.
+// kAbs == true (RoPE at the target position): angle (pos0 + r) * theta_i for row r.
+// The angles go to LDS (dynamic: n_pairs or n_rows * n_pairs float2) once per tile.
 // kHalf == false: pairs (2i, 2i+1); a unit is 8 consecutive elements = 4 pairs.
 // kHalf == true:  pairs (i, i+D/2); a unit is elements [8j, 8j+8) and [D/2+8j, D/2+8j+8).
-template <typename T, bool kHalf>
-__global__ __launch_bounds__(kRopeThreads) void rope_delta_kernel(
+template <typename T, bool kHalf, bool kAbs>
+__global__ __launch_bounds__(kRopeThreads) void rope_kernel(
     T *__restrict__ k, const RopeTile *__restrict__ tiles, int h_kv, int head_dim,
     ThetaTable theta) {
-  __shared__ float2 cs[kMaxPairs];
+  extern __shared__ float2 cs[];
   const RopeTile t = tiles[blockIdx.x];
+  if (!kAbs && t.delta == 0) return;
   const int n_pairs = head_dim >> 1;
-  for (int i = threadIdx.x; i < n_pairs; i += kRopeThreads)
-    cs[i] = delta_cos_sin(t.delta, theta.hi[i], theta.lo[i]);
+  if (kAbs) {
+    for (int e = threadIdx.x; e < t.n_rows * n_pairs; e += kRopeThreads) {
+      const int r = e / n_pairs, i = e - r * n_pairs;
+      cs[e] = delta_cos_sin(t.pos0 + r, theta.hi[i], theta.lo[i]);
+    }
+  } else {
+    for (int i = threadIdx.x; i < n_pairs; i += kRopeThreads)
+      cs[i] = delta_cos_sin(t.delta, theta.hi[i], theta.lo[i]);
+  }
   __syncthreads();
 
   const int units_per_head = kHalf ? (head_dim >> 4) : (head_dim >> 3);
@@ -80,7 +97,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_delta_kernel(
   for (int u0 = threadIdx.x; u0 < total; u0 += kRopeThreads * kRopeUnroll) {
     float a[kRopeUnroll][8], b[kRopeUnroll][8];
     T *pa[kRopeUnroll];
-    int jj[kRopeUnroll];
+    int cso[kRopeUnroll];  // this unit's first angle in cs
     bool live[kRopeUnroll];
 #pragma unroll
     for (int q = 0; q < kRopeUnroll; ++q) {
@@ -91,7 +108,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_delta_kernel(
       const int rem = uu - row * units_per_row;
       const int head = rem / units_per_head;
       const int j = rem - head * units_per_head;
-      jj[q] = j;
+      cso[q] = (kAbs ? row * n_pairs : 0) + (kHalf ? 8 * j : 4 * j);
       pa[q] = base + row * row_elems + head * head_dim + 8 * j;
       if (live[q]) {
         load8(pa[q], a[q]);
@@ -104,7 +121,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_delta_kernel(
       if (kHalf) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float2 c = cs[8 * jj[q] + i];
+          const float2 c = cs[cso[q] + i];
           const float x0 = a[q][i], x1 = b[q][i];
           a[q][i] = x0 * c.x - x1 * c.y;
           b[q][i] = x0 * c.y + x1 * c.x;
@@ -114,7 +131,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_delta_kernel(
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float2 c = cs[4 * jj[q] + i];
+          const float2 c = cs[cso[q] + i];
           const float x0 = a[q][2 * i], x1 = a[q][2 * i + 1];
           a[q][2 * i] = x0 * c.x - x1 * c.y;
           a[q][2 * i + 1] = x0 * c.y + x1 * c.x;
@@ -143,28 +160,26 @@ __global__ __launch_bounds__(256) void splice_kernel(u32x4 *__restrict__ k, u32x
   }
 }
 
-template <typename T>
+template <typename T, bool kAbs>
 int launch_rope(const PlanHeader &h, const int32_t *plan_dev, void *k, int head_dim, int layout,
                 const ThetaTable &theta, hipStream_t s) {
   const RopeTile *tiles = reinterpret_cast<const RopeTile *>(plan_dev + h[PIC_H_O_ROPE_TILES]);
   const dim3 grid(h[PIC_H_N_ROPE_TILES]);
+  const size_t lds = (kAbs ? PIC_ROPE_TILE_ROWS : 1) * (size_t)(head_dim / 2) * sizeof(float2);
   if (layout == PIC_ROPE_HALF)
-    hipLaunchKernelGGL((rope_delta_kernel<T, true>), grid, dim3(kRopeThreads), 0, s,
+    hipLaunchKernelGGL((rope_kernel<T, true, kAbs>), grid, dim3(kRopeThreads), lds, s,
                        static_cast<T *>(k), tiles, h[PIC_H_H_KV], head_dim, theta);
   else
-    hipLaunchKernelGGL((rope_delta_kernel<T, false>), grid, dim3(kRopeThreads), 0, s,
+    hipLaunchKernelGGL((rope_kernel<T, false, kAbs>), grid, dim3(kRopeThreads), lds, s,
                        static_cast<T *>(k), tiles, h[PIC_H_H_KV], head_dim, theta);
   PIC_LAUNCH_CHECK();
   return PIC_OK;
 }
 
-}  // namespace
-}  // namespace pic
-
-extern "C" int pic_rope_delta(const int32_t *plan_host, const int32_t *plan_dev, void *k,
-                              int32_t dtype, int32_t head_dim, int32_t rope_layout,
-                              double rope_base, void *stream) {
-  using namespace pic;
+// Shared argument checks and dispatch of pic_rope_delta / pic_rope_apply.
+template <bool kAbs>
+int rope_entry(const int32_t *plan_host, const int32_t *plan_dev, void *k, int32_t dtype,
+               int32_t head_dim, int32_t rope_layout, double rope_base, void *stream) {
   const PlanHeader h{plan_host};
   if (!h.valid()) return PIC_EINVAL;
   if (dtype != PIC_BF16 && dtype != PIC_F32) return PIC_EINVAL;
@@ -175,11 +190,34 @@ extern "C" int pic_rope_delta(const int32_t *plan_host, const int32_t *plan_dev,
   if (head_dim % unit != 0 || head_dim > 2 * kMaxPairs) return PIC_EUNSUPPORTED;
   if (h[PIC_H_N_ROPE_TILES] == 0) return PIC_OK;
   if (plan_dev == nullptr || k == nullptr) return PIC_EINVAL;
+  if (kAbs) {  // positions are formed in fp32 exactly, which holds below 2^24
+    const RopeTile *tl = reinterpret_cast<const RopeTile *>(plan_host + h[PIC_H_O_ROPE_TILES]);
+    for (int32_t i = 0; i < h[PIC_H_N_ROPE_TILES]; ++i)
+      if ((int64_t)tl[i].pos0 + tl[i].n_rows > (int64_t(1) << 24)) return PIC_EUNSUPPORTED;
+  }
 
   const ThetaTable theta = make_theta(head_dim, rope_base);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == PIC_BF16) return launch_rope<__bf16>(h, plan_dev, k, head_dim, rope_layout, theta, s);
-  return launch_rope<float>(h, plan_dev, k, head_dim, rope_layout, theta, s);
+  if (dtype == PIC_BF16)
+    return launch_rope<__bf16, kAbs>(h, plan_dev, k, head_dim, rope_layout, theta, s);
+  return launch_rope<float, kAbs>(h, plan_dev, k, head_dim, rope_layout, theta, s);
+}
+
+}  // namespace
+}  // namespace pic
+
+extern "C" int pic_rope_delta(const int32_t *plan_host, const int32_t *plan_dev, void *k,
+                              int32_t dtype, int32_t head_dim, int32_t rope_layout,
+                              double rope_base, void *stream) {
+  return pic::rope_entry<false>(plan_host, plan_dev, k, dtype, head_dim, rope_layout, rope_base,
+                                stream);
+}
+
+extern "C" int pic_rope_apply(const int32_t *plan_host, const int32_t *plan_dev, void *k,
+                              int32_t dtype, int32_t head_dim, int32_t rope_layout,
+                              double rope_base, void *stream) {
+  return pic::rope_entry<true>(plan_host, plan_dev, k, dtype, head_dim, rope_layout, rope_base,
+                               stream);
 }
 
 extern "C" int pic_splice(const int32_t *plan_host, const int32_t *plan_dev, void *k, void *v,

@@ -136,7 +136,8 @@ def check_plan(reqs, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0):
     assert plan.row_tok.tolist() == [exp_tok[b] + r for b, rr in enumerate(exp_rows) for r in rr]
     assert plan.n_tokens == exp_tok[-1] and plan.n_rows == len(flat_rows)
 
-    # rope tiles: exactly the cached rows that keep their K, with delta = off_c - pos_base
+    # rope tiles: exactly the cached rows that keep their K, each with delta = off_c -
+    # pos_base and its global position (rows of one tile are consecutive in one chunk)
     want = {}
     for b, (lens, q) in enumerate(zip(reqs, q_lens)):
         offs = O.chunk_offsets(lens)
@@ -144,14 +145,14 @@ def check_plan(reqs, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0):
         for c, L_c in enumerate(lens):
             delta = offs[c] - pos_base
             for t in range(L_c):
-                if delta != 0 and offs[c] + t not in rec:
-                    want[exp_tok[b] + offs[c] + t] = delta
+                if offs[c] + t not in rec:
+                    want[exp_tok[b] + offs[c] + t] = (delta, offs[c] + t)
     got = {}
-    for tok0, n, delta, _ in plan.rope_tiles.tolist():
+    for tok0, n, delta, pos0 in plan.rope_tiles.tolist():
         assert 1 <= n <= 32
-        for t in range(tok0, tok0 + n):
+        for i, t in enumerate(range(tok0, tok0 + n)):
             assert t not in got
-            got[t] = delta
+            got[t] = (delta, pos0 + i)
     assert got == want
 
     # attention tiles: every (row, head) once; items cover [0, p_last] of each tile

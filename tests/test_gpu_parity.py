@@ -41,7 +41,9 @@ def f64(t):
 class Run:
     """One pass of the path on the GPU, keeping every intermediate on the host."""
 
-    def __init__(self, wl, layout="adjacent", n_cu=0, pos_base=0):
+    def __init__(self, wl, layout="adjacent", n_cu=0, pos_base=0, scheme="delta"):
+        # scheme "delta": cached K carries RoPE at local positions (rotation by delta);
+        # scheme "nope": cached K is position-free and gets RoPE at the target positions
         self.wl = wl
         reqs = [r.chunk_lens for r in wl.requests]
         qs = [r.q_len for r in wl.requests]
@@ -56,8 +58,12 @@ class Run:
         q, kf, vf = self.q.to(dev), self.kf.to(dev), self.vf.to(dev)
         out = torch.full_like(q, float("nan"))
         ws = P.attn_workspace(self.plan, wl.head_dim)
-        say(wl.name, "k=%d" % wl.k, layout, "rope_delta")
-        P.pic_rope_delta(self.plan, k, wl.rope_base, LAYOUTS[layout])
+        say(wl.name, "k=%d" % wl.k, layout, "rope_" + scheme)
+        if scheme == "nope":
+            P.pic_rope_apply(self.plan, k, wl.rope_base, LAYOUTS[layout])
+        else:
+            P.pic_rope_delta(self.plan, k, wl.rope_base, LAYOUTS[layout])
+        self.scheme = scheme
         torch.cuda.synchronize()
         self.k_rot = k.cpu()
         say(wl.name, "splice")
@@ -88,7 +94,10 @@ class Run:
         chunks_k = [kin[offs[c]:offs[c + 1]] for c in range(len(r.chunk_lens))]
         chunks_v = [vin[offs[c]:offs[c + 1]] for c in range(len(r.chunk_lens))]
         rows = O.recompute_positions(r.chunk_lens, r.q_len, self.wl.k)
-        if chunks_k:
+        if chunks_k and self.scheme == "nope":
+            k_ctx = O.rope_apply(chunks_k, self.wl.rope_base, self.layout)
+            v_ctx = O.concat_chunks(chunks_v)
+        elif chunks_k:
             k_ctx = O.rope_delta(chunks_k, self.wl.rope_base, self.layout, self.pos_base)
             v_ctx = O.concat_chunks(chunks_v)
         else:
@@ -126,7 +135,7 @@ def check_run(run, sample_rows=None):
         # and, with pos_base = 0, all of chunk 0 (delta_0 = 0)
         rec_t = torch.tensor(rows, dtype=torch.long) + tok0
         assert torch.equal(run.k_rot[rec_t], run.k_in[rec_t])
-        if run.pos_base == 0 and r.chunk_lens:
+        if run.pos_base == 0 and r.chunk_lens and run.scheme == "delta":
             L0 = r.chunk_lens[0]
             assert torch.equal(run.k_rot[tok0:tok0 + L0], run.k_in[tok0:tok0 + L0])
         # splice: fresh rows bit-exact, V elsewhere unchanged, K elsewhere = rotated
@@ -255,3 +264,27 @@ def test_attention_is_deterministic():
     P.pic_selective_attn(run.plan, d["q"], d["k"], d["v"], again, workspace=d["ws"])
     torch.cuda.synchronize()
     assert torch.equal(again.cpu(), run.out)
+
+
+# ---------------------------------------------------------------------------
+# Scheme B: position-free cache, RoPE applied at the target positions
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_scheme_b_worked_example_fp32(layout):
+    check_run(Run(W.worked_example(), layout, scheme="nope"))
+
+
+def test_scheme_b_rag_single_bf16():
+    check_run(Run(W.rag_single(), scheme="nope"))
+
+
+def test_scheme_b_long_context_bf16_half():
+    check_run(Run(W.long_context(k=2), "half", scheme="nope"), sample_rows=32)
+
+
+def test_scheme_b_epic_sweep_full_size_sampled():
+    # every kept row of the 4 x ~50k batch rotated at its global position (chunk 0
+    # included), sampled attention rows, launched as bench.py launches it (n_cu = 256)
+    check_run(Run(W.epic_sweep(k=16), n_cu=256, scheme="nope"), sample_rows=24)

@@ -6,6 +6,7 @@ fails at least one of them; the "planted" tests at the end plant such mistakes
 into the oracle and check that a pin catches each one.  CPU only.
 """
 
+import cmath
 import json
 import math
 import os
@@ -182,6 +183,44 @@ def test_rope_delta_restores_global_rotation(pos_base):
     got = O.rope_delta(cached, 1e4, pos_base=pos_base)
     want = O.rope_rotate(k0, np.arange(offs[-1]), 1e4)
     assert np.max(np.abs(got - want)) < 1e-12
+
+
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_scheme_b_equals_scheme_c(layout):
+    # [RoPE-C] 3.2 and 3.3 reach the same K at the target positions: RoPE applied to the
+    # position-free rows at global positions (scheme B) equals the delta rotation of
+    # rows cached with RoPE at local positions (scheme C).
+    rng = np.random.default_rng(8)
+    lens = [6, 0, 9, 4, 1]
+    offs = O.chunk_offsets(lens)
+    nope = [rng.standard_normal((L, 2, 16)) for L in lens]
+    cached = [O.rope_rotate(x, np.arange(x.shape[0]), 1e4, layout) for x in nope]
+    got = O.rope_apply(nope, 1e4, layout)
+    want = O.rope_delta(cached, 1e4, layout)
+    assert got.shape == (offs[-1], 2, 16)
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+def test_scheme_b_two_dims_is_complex_rotation_by_global_position():
+    # D = 2: one pair with theta_0 = 1, so row t of the concatenation turns by t radians.
+    lens = [3, 2, 4]
+    rng = np.random.default_rng(9)
+    nope = [rng.standard_normal((L, 1, 2)) for L in lens]
+    got = O.rope_apply(nope, 10000.0)
+    t = 0
+    for x in nope:
+        for row in x:
+            z = complex(row[0, 0], row[0, 1]) * cmath.exp(1j * t)
+            assert abs(got[t, 0, 0] - z.real) < 1e-12 and abs(got[t, 0, 1] - z.imag) < 1e-12
+            t += 1
+
+
+def test_planted_scheme_b_local_positions_fails():
+    # restarting positions at every chunk (forgetting the offsets) must break the pin
+    rng = np.random.default_rng(10)
+    nope = [rng.standard_normal((L, 1, 8)) for L in (5, 5)]
+    wrong = np.concatenate([O.rope_rotate(x, np.arange(5), 1e4) for x in nope])
+    assert np.max(np.abs(wrong - O.rope_apply(nope, 1e4))) > 0.1
 
 
 # ---------------------------------------------------------------------------
