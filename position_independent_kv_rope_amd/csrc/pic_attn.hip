@@ -51,6 +51,16 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ bool wave_any(bool p) { return __any((int)p); }
 
+// max / sum of a value over the lane pair (l, l ^ 32), in the VALU (v_permlane32_swap)
+__device__ __forceinline__ float pair_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 // ================================ bf16 kernel ==================================
 
 constexpr int kBfWaves = 4;
@@ -228,7 +238,7 @@ __device__ __forceinline__ void attn_bf16_body(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[t][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    mx = pair_max(mx) * scale_log2;
     const bool upd = mx > m_run + kLazy;  // false while everything seen is masked
     if (wave_any(upd)) {
       const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
@@ -336,7 +346,7 @@ __device__ __forceinline__ void attn_bf16_body(
   }
 
   // ---- epilogue ----
-  const float l_row = l_lane + __shfl_xor(l_lane, 32);
+  const float l_row = pair_sum(l_lane);
   if (!valid) return;
   if (it.slot < 0) {
     const float inv = 1.f / l_row;
@@ -641,7 +651,7 @@ __device__ __forceinline__ void attn_bf16_paged_body(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[t][j]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    mx = pair_max(mx) * scale_log2;
     const bool upd = mx > m_run + kLazy;
     if (wave_any(upd)) {
       const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;
@@ -752,7 +762,7 @@ __device__ __forceinline__ void attn_bf16_paged_body(
   }
 
   // ---- epilogue (as in the contiguous kernel) ----
-  const float l_row = l_lane + __shfl_xor(l_lane, 32);
+  const float l_row = pair_sum(l_lane);
   if (!valid) return;
   if (it.slot < 0) {
     const float inv = 1.f / l_row;
