@@ -76,9 +76,10 @@ enum { PIC_ROPE_ADJACENT = 0, PIC_ROPE_HALF = 1 };
  * PIC_PLAN_HEADER_WORDS words, then sections at the word offsets the header gives.
  * ---------------------------------------------------------------------------- */
 #define PIC_PLAN_MAGIC 0x31434950 /* "PIC1" */
-#define PIC_PLAN_HEADER_WORDS 32
+#define PIC_PLAN_HEADER_WORDS 40
 #define PIC_ATTN_TILE_M 128 /* query vectors (row, head) per attention tile */
 #define PIC_ROPE_TILE_ROWS 32
+#define PIC_DECODE_COLS 64 /* query columns (use, head) of one decode item */
 
 enum {
   PIC_H_MAGIC = 0,
@@ -121,7 +122,15 @@ enum {
                          request's fresh rows), first local key (t0, or fresh row offset),
                          position of the first key, 0; per request the fresh blocks
                          come first, then the pool blocks in position order */
-  PIC_H_RESERVED4
+  PIC_H_N_DEC_ITEMS,  /* paged: decode work items (0 when h_q/h_kv > PIC_DECODE_COLS) */
+  PIC_H_O_DEC_ITEMS,  /* paged: [n_dec_items][8] source (pool chunk id >= 0, or -1-b for
+                         the fresh rows of request b), first key, end key, first use,
+                         use count, 0, 0, 0; items of one pool chunk are adjacent */
+  PIC_H_N_DEC_USES,
+  PIC_H_O_DEC_USES,   /* paged: [n_dec_uses] per use, the global chunk index c reading the
+                         item's pool chunk (or -1-b for fresh rows); at most
+                         PIC_DECODE_COLS / (h_q/h_kv) uses per item */
+  PIC_H_RESERVED5
 };
 
 /*
@@ -139,7 +148,8 @@ enum {
  *
  * chunk_ids: NULL for spliced contiguous K/V buffers.  Otherwise the chunks are stored
  * once in a shared paged pool and chunk_ids[c] (>= 0) names the pool chunk of request
- * chunk c (chunk_lens[c] must be its length): the plan then has no rope tiles (the pool
+ * chunk c (chunk_lens[c] must be its length, the same wherever the id appears, else
+ * PIC_EINVAL): the plan then has no rope tiles (the pool
  * is read-only; pic_selective_attn_paged rotates on load), and attention items walk
  * per-request key blocks (fresh rows first, then pool rows chunk by chunk).
  *
@@ -251,6 +261,32 @@ int pic_selective_attn_paged(const int32_t *plan_host, const int32_t *plan_dev, 
                              void *out, int32_t dtype, int32_t head_dim, int32_t rope_layout,
                              double rope_base, float scale, void *workspace,
                              size_t workspace_bytes, void *stream);
+
+/*
+ * pic_decode_attn_paged -- one decode step over the spliced KV of a shared pool.
+ *                        [EPIC] decode after the link; [HYPIC] 2.2; [RoPE-C] 3.3
+ * For every request b of a paged plan, its next token (position N_b, right after its
+ * q_b query tokens) attends causally over all of the request's keys: its pool chunks
+ * (as pic_selective_attn_paged sees them: rotated by delta_c, seam rows replaced by
+ * the fresh rows), its recomputed rows (k_fresh/v_fresh, the link's fresh buffer) and
+ * itself:  out[b, h] = sum_j softmax_j(q_new[b, h] . K_b[j, g] * scale) V_b[j, g].
+ * Work is chunk-major: each pool chunk is read once per call for all request chunks
+ * that use it (the plan's decode items).  q_new/out: device [n_req][h_q][head_dim];
+ * k_new/v_new: device [n_req][h_kv][head_dim], RoPE'd at N_b; pool and fresh arguments
+ * as pic_selective_attn_paged.  Later decode steps append the generated rows to the
+ * fresh buffer through a plan with longer queries.  bf16 only, head_dim in {64, 128},
+ * h_q/h_kv <= PIC_DECODE_COLS.  workspace >= pic_decode_workspace_bytes (partials +
+ * angle table).  Errors as pic_selective_attn_paged.
+ */
+size_t pic_decode_workspace_bytes(const int32_t *plan_host, int32_t head_dim);
+int pic_decode_attn_paged(const int32_t *plan_host, const int32_t *plan_dev, const void *q_new,
+                          const void *k_new, const void *v_new, const void *pool_k,
+                          const void *pool_v, int64_t pool_blocks, int32_t block_size,
+                          const int32_t *chunk_block_ptr, int32_t n_pool_chunks,
+                          const int32_t *block_ids, const void *k_fresh, const void *v_fresh,
+                          void *out, int32_t dtype, int32_t head_dim, int32_t rope_layout,
+                          double rope_base, float scale, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /* Short static description of a status code. */
 const char *pic_strerror(int status);

@@ -350,6 +350,19 @@ def attn_rows_direct(q_rows, kx, vx, positions, heads, scale=None):
 # ---------------------------------------------------------------------------
 
 
+def decode_attn(q_new, kx, vx, k_new, v_new, scale=None):
+    """One decode step after the link: the next token, at position N right after the N
+    spliced keys, attends over keys 0..N including itself ([KV-scratch] incremental
+    decode with the offset mask for a single new row, P = N).  q_new: [Hq, D];
+    k_new/v_new: [Hkv, D] (RoPE'd at N).  Returns [Hq, D] fp64."""
+    kx = np.asarray(kx, dtype=np.float64)
+    vx = np.asarray(vx, dtype=np.float64)
+    n = kx.shape[0]
+    kx2 = np.concatenate([kx, np.asarray(k_new, dtype=np.float64)[None]], axis=0)
+    vx2 = np.concatenate([vx, np.asarray(v_new, dtype=np.float64)[None]], axis=0)
+    return selective_attn(np.asarray(q_new, dtype=np.float64)[None], kx2, vx2, [n], scale)[0]
+
+
 def link_request(cached_k_chunks, cached_v_chunks, q_len, k, k_fresh, v_fresh, q_fresh,
                  base, layout="adjacent", pos_base=0, scale=None):
     """Run the whole link for one request and one layer.

@@ -25,11 +25,13 @@ PIC_ATTN_TILE_M = 128
  H_TILE_ROWS, H_N_ROPE_TILES, H_N_ATTN_TILES, H_N_ATTN_ITEMS, H_N_MERGE, H_N_PARTIALS,
  H_MAX_TOKENS, H_O_REQ_CHUNK_PTR, H_O_CHUNK_OFF, H_O_REQ_TOK_PTR, H_O_REQ_ROW_PTR, H_O_ROWS,
  H_O_ROW_TOK, H_O_ROPE_TILES, H_O_ATTN_TILES, H_O_ATTN_ITEMS, H_O_MERGE, H_PAGED, H_O_SEGS,
- H_N_KBLOCKS, H_O_KBLOCKS) = range(31)
+ H_N_KBLOCKS, H_O_KBLOCKS, H_N_DEC_ITEMS, H_O_DEC_ITEMS, H_N_DEC_USES, H_O_DEC_USES) = range(35)
+PIC_DECODE_COLS = 64
 
 EXPORTED = ("pic_build_index", "pic_rope_delta", "pic_rope_apply", "pic_splice",
             "pic_attn_workspace_bytes",
-            "pic_selective_attn", "pic_selective_attn_paged", "pic_strerror")
+            "pic_selective_attn", "pic_selective_attn_paged", "pic_decode_workspace_bytes",
+            "pic_decode_attn_paged", "pic_strerror")
 
 
 class PicError(RuntimeError):
@@ -70,6 +72,11 @@ def lib():
     L.pic_selective_attn_paged.argtypes = [p, p, p, p, p, i64, i32, p, i32, p, p, p, p, i32, i32,
                                            i32, f64, f32, p, sz, p]
     L.pic_selective_attn_paged.restype = ctypes.c_int
+    L.pic_decode_workspace_bytes.argtypes = [p, i32]
+    L.pic_decode_workspace_bytes.restype = sz
+    L.pic_decode_attn_paged.argtypes = [p, p, p, p, p, p, p, i64, i32, p, i32, p, p, p, p, i32,
+                                        i32, i32, f64, f32, p, sz, p]
+    L.pic_decode_attn_paged.restype = ctypes.c_int
     L.pic_strerror.argtypes = [ctypes.c_int]
     L.pic_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -162,6 +169,14 @@ class Plan:
     @property
     def kblocks(self):
         return self._sec(H_O_KBLOCKS, self[H_N_KBLOCKS], 4)
+
+    @property
+    def dec_items(self):
+        return self._sec(H_O_DEC_ITEMS, self[H_N_DEC_ITEMS], 8)
+
+    @property
+    def dec_uses(self):
+        return self._sec(H_O_DEC_USES, self[H_N_DEC_USES], 1).reshape(-1)
 
     def to_device(self, device="cuda"):
         """Upload the plan (one int32 tensor) and keep it with the host copy."""
@@ -328,3 +343,49 @@ def pic_selective_attn_paged(plan, q, pool_k, pool_v, chunk_block_ptr, block_ids
         _dev(k_fresh, "k_fresh"), _dev(v_fresh, "v_fresh"), _dev(out, "out"), _dtype_code(q), d,
         int(layout), float(rope_base), float(scale), ws, ws_bytes, _stream(stream))
     _check("pic_selective_attn_paged", st)
+
+
+def decode_workspace(plan, head_dim, device="cuda"):
+    """Workspace tensor for pic_decode_attn_paged."""
+    import torch
+    n = int(lib().pic_decode_workspace_bytes(plan.host_ptr(), int(head_dim)))
+    return torch.empty(max(1, (n + 3) // 4), dtype=torch.float32, device=device)
+
+
+def pic_decode_attn_paged(plan, q_new, k_new, v_new, pool_k, pool_v, chunk_block_ptr, block_ids,
+                          k_fresh, v_fresh, out, rope_base, layout=PIC_ROPE_ADJACENT, scale=None,
+                          workspace=None, stream=None):
+    """One decode step of every request of a paged plan: the next token (position N_b)
+    attends over the request's pool chunks, recomputed rows and itself."""
+    import torch
+    d = int(q_new.shape[2])
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if not plan.paged:
+        raise ValueError("plan was not built with chunk ids (paged pool)")
+    n_req = plan[H_N_REQ]
+    if q_new.shape != (n_req, plan[H_H_Q], d) or out.shape != q_new.shape:
+        raise ValueError("q_new/out must be [n_req, h_q, D]")
+    if k_new.shape != (n_req, plan[H_H_KV], d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [n_req, h_kv, D]")
+    if pool_k.dim() != 4 or pool_v.shape != pool_k.shape or pool_k.shape[2] != plan[H_H_KV]:
+        raise ValueError("pool must be [blocks, block_size, h_kv, D]")
+    if k_fresh.shape != (plan.n_rows, plan[H_H_KV], d) or v_fresh.shape != k_fresh.shape:
+        raise ValueError("fresh K/V must be [n_rows, h_kv, D]")
+    for t, name in ((chunk_block_ptr, "chunk_block_ptr"), (block_ids, "block_ids")):
+        if t.dtype != torch.int32 or t.dim() != 1:
+            raise ValueError(name + " must be a 1-D int32 tensor")
+    for t in (k_new, v_new, pool_k, pool_v, k_fresh, v_fresh, out):
+        if t.dtype != q_new.dtype:
+            raise ValueError("all tensors must share one dtype")
+    if workspace is None:
+        workspace = decode_workspace(plan, d, q_new.device)
+    st = lib().pic_decode_attn_paged(
+        plan.host_ptr(), plan.dev_ptr(), _dev(q_new, "q_new"), _dev(k_new, "k_new"),
+        _dev(v_new, "v_new"), _dev(pool_k, "pool_k"), _dev(pool_v, "pool_v"),
+        int(pool_k.shape[0]), int(pool_k.shape[1]), _dev(chunk_block_ptr, "chunk_block_ptr"),
+        int(chunk_block_ptr.numel()) - 1, _dev(block_ids, "block_ids"), _dev(k_fresh, "k_fresh"),
+        _dev(v_fresh, "v_fresh"), _dev(out, "out"), _dtype_code(q_new), d, int(layout),
+        float(rope_base), float(scale), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("pic_decode_attn_paged", st)

@@ -810,6 +810,344 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_paged_kernel(
                                  ws_ml, h_q, h_kv, tile_rows, scale_log2, pool_bytes);
 }
 
+// ======================== decode over the shared pool =========================
+//
+// One decode step: the next token of every request (at position N_b, right after its
+// query tokens) attends over all of the request's keys -- its pool chunks (rotated by
+// delta_c), its recomputed rows (seams and queries, from the fresh buffer) and itself.
+// Decode is bound by HBM, so the work is chunk-major: an item streams one pool chunk
+// once and scores it against the queries of every request chunk that reads it, each
+// query rotated by -delta of its own use (<q, R(delta) k> = <R(-delta) q, k>), so a
+// chunk shared by several requests leaves HBM once per step.  Each (use, kv head)
+// writes a partial (m, l, O) for its G query heads; the merge folds in the partial of
+// the request's fresh rows and the new token itself.
+
+constexpr int kDecWaves = PIC_DECODE_COLS / 32;  // one 32-column MFMA block per wave
+constexpr int kDecThreads = 64 * kDecWaves;
+
+template <int D, bool kHalf>
+__device__ __forceinline__ void dec_attn_body(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ pool_k,
+    const __bf16 *__restrict__ pool_v, const int32_t *__restrict__ chunk_block_ptr,
+    const int32_t *__restrict__ block_ids, const __bf16 *__restrict__ k_fresh,
+    const __bf16 *__restrict__ v_fresh, const DecItem *__restrict__ items,
+    const int32_t *__restrict__ uses, const int32_t *__restrict__ segs,
+    const int32_t *__restrict__ req_row_ptr, const float2 *__restrict__ angles,
+    float *__restrict__ ws_o, float *__restrict__ ws_ml, int h_q, int h_kv, int n_chunks,
+    float scale_log2, int pool_bytes) {
+  constexpr int kRowB = D * 2;
+  constexpr int kCPR = D / 8;
+  constexpr int kTileB = kKB * kRowB;
+  constexpr int kRPI = 1024 / kRowB;
+  constexpr int kRounds = kKB / (kRPI * kDecWaves);
+  constexpr int kKS = D / 16;
+  constexpr int kDB = D / 32;
+  constexpr int kPairs = D / 2;
+  static_assert(kRounds * kRPI * kDecWaves == kKB, "direct loads must tile the block");
+  static_assert(kRPI <= kPoolBlockRows, "one direct load must stay inside a pool block");
+  __shared__ __attribute__((aligned(1024))) char lds[4 * kTileB];  // K0 K1 V0 V1
+
+  const DecItem it = items[blockIdx.x];
+  const int g = blockIdx.y;
+  const int group = h_q / h_kv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31;
+  const int grp = lane >> 5;
+  const int q16 = lane >> 4;
+  const int i16 = lane & 15;
+  const bool pool = it.src >= 0;
+
+  // ---- this lane's query column: (use u, head hh) ----
+  const int col = 32 * wave + n;
+  const int u = col / group, hh = col - u * group;
+  const bool valid = u < it.n_uses;
+  const int use = valid ? uses[it.use_begin + u] : 0;
+  const int req = !valid ? 0 : (pool ? segs[8 * use + 5] : -1 - use);
+  const int seam = (valid && pool) ? segs[8 * use + 2] : 0;
+  const int slot = pool ? use : n_chunks + req;
+
+  bf16x8 qop[kKS];
+  {
+    const __bf16 *qp = q + ((int64_t)req * h_q + g * group + hh) * D + 8 * grp;
+    bf16x8 qo[kKS];
+#pragma unroll
+    for (int s = 0; s < kKS; ++s)
+      qo[s] = valid ? *reinterpret_cast<const bf16x8 *>(qp + 16 * s) : bf16x8{};
+    if (pool && valid) {  // into the chunk's local frame: rotate by -delta of this use
+      const float2 *cs = angles + (int64_t)use * kPairs;
+      if constexpr (!kHalf) {
+#pragma unroll
+        for (int s = 0; s < kKS; ++s)
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            const float2 c = cs[8 * s + 4 * grp + j / 2];
+            const float a = (float)qo[s][j], b = (float)qo[s][j + 1];
+            qop[s][j] = (__bf16)(a * c.x + b * c.y);
+            qop[s][j + 1] = (__bf16)(b * c.x - a * c.y);
+          }
+      } else {
+#pragma unroll
+        for (int s = 0; s < kKS / 2; ++s)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float2 c = cs[16 * s + 8 * grp + j];
+            const float a = (float)qo[s][j], b = (float)qo[s + kKS / 2][j];
+            qop[s][j] = (__bf16)(a * c.x + b * c.y);
+            qop[s + kKS / 2][j] = (__bf16)(b * c.x - a * c.y);
+          }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < kKS; ++s) qop[s] = qo[s];
+    }
+  }
+
+  f32x16 acc[kDB];
+#pragma unroll
+  for (int d = 0; d < kDB; ++d)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[d][j] = 0.f;
+  float m_run = kNegInf, l_lane = 0.f;
+
+  // ---- staging: pool rows through the block table, or the request's fresh rows ----
+  const int n_keys = it.t_end - it.t_begin;
+  const int n_blocks = (n_keys + kKB - 1) / kKB;
+  const int tok_bytes = h_kv * D * 2;
+  const int blk_bytes = kPoolBlockRows * tok_bytes;
+  const int32_t *bl = pool ? block_ids + chunk_block_ptr[it.src] : nullptr;
+  const int fresh_b = pool ? 0 : -1 - it.src;
+  const int64_t fresh_off = pool ? 0 : ((int64_t)req_row_ptr[fresh_b] * h_kv + g) * D;
+  int voff_k[kRounds], voff_v[kRounds], row_r[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int R = kRPI * (kDecWaves * r + wave) + lane / kCPR;
+    const int pch = lane % kCPR;
+    row_r[r] = R;
+    const int inblk = pool ? (R % kPoolBlockRows) * tok_bytes + g * kRowB : R * tok_bytes;
+    voff_k[r] = inblk + 16 * (pch ^ swz_k<kCPR>(R));
+    voff_v[r] = inblk + 16 * (pch ^ swz_v<kCPR>(R));
+  }
+  // block j of K (is_v false) or V into LDS buffer buf; rows past the item's keys read
+  // as zero (the buffer range), slack rows of a chunk's last pool block included
+  auto issue = [&](int j, bool is_v, int buf) {
+    const int t0 = it.t_begin + j * kKB;
+    if (pool) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(is_v ? pool_v : pool_k), 0, pool_bytes, 0x00020000);
+#pragma unroll
+      for (int r = 0; r < kRounds; ++r) {
+        const int t = t0 + kRPI * (kDecWaves * r + wave);  // first row of this load
+        const int soff = t < it.t_end ? bl[t / kPoolBlockRows] * blk_bytes : pool_bytes;
+        const int voff = t0 + row_r[r] < it.t_end ? (is_v ? voff_v[r] : voff_k[r]) : pool_bytes;
+        const int dst = buf * kTileB + (kDecWaves * r + wave) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16, voff, soff, 0, 0);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)((is_v ? v_fresh : k_fresh) + fresh_off), 0, it.t_end * tok_bytes, 0x00020000);
+      const int soff = t0 * tok_bytes;
+#pragma unroll
+      for (int r = 0; r < kRounds; ++r) {
+        const int dst = buf * kTileB + (kDecWaves * r + wave) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16,
+                                                 is_v ? voff_v[r] : voff_k[r], soff, 0, 0);
+      }
+    }
+  };
+
+  int koff[kKS];
+  {
+    const int r0 = perm_key(0, n);
+    const int f = swz_k<kCPR>(r0);
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) koff[s] = r0 * kRowB + 16 * ((2 * s + grp) ^ f);
+  }
+  int voff[kDB];
+  {
+    const int rr = 8 * (q16 >> 1) + (i16 >> 2);
+    const int f = swz_v<kCPR>(rr) >> 2;
+#pragma unroll
+    for (int d = 0; d < kDB; ++d)
+      voff[d] = rr * kRowB + 16 * (4 * (d ^ f) + 2 * (q16 & 1) + ((i16 & 3) >> 1)) +
+                8 * (i16 & 1);
+  }
+
+  issue(0, false, 0);
+  issue(0, true, 2);
+  for (int j = 0; j < n_blocks; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < n_blocks) {
+      issue(j + 1, false, buf ^ 1);
+      issue(j + 1, true, 2 + (buf ^ 1));
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kRounds) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    asm volatile("s_barrier" ::: "memory");
+    const char *Kb = lds + buf * kTileB;
+    const char *Vb = lds + (2 + buf) * kTileB;
+    f32x16 sc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) sc[t][jj] = 0.f;
+#pragma unroll
+      for (int s = 0; s < kKS; ++s) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Kb + koff[s] + t * 32 * kRowB);
+        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], sc[t], 0, 0, 0);
+      }
+    }
+    const int t0 = it.t_begin + j * kKB;
+    if (t0 < seam || t0 + kKB > it.t_end || !valid) {  // seam rows, rows past the keys
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const int tk = t0 + perm_key(t, 8 * (jj >> 2) + 4 * grp + (jj & 3));
+          if (tk < seam || tk >= it.t_end || !valid) sc[t][jj] = kNegInf;
+        }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, sc[t][jj]);
+    mx = pair_max(mx) * scale_log2;
+    if (mx > m_run) {  // exact running max (decode is bound by HBM, not by this VALU)
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
+      m_run = mx;
+      l_lane *= alpha;
+#pragma unroll
+      for (int d = 0; d < kDB; ++d) acc[d] *= alpha;
+    }
+    const float base = m_run == kNegInf ? 0.f : m_run;
+    bf16x8 pb[4];
+    const bf16x2v ones = {(__bf16)1.f, (__bf16)1.f};
+    float ps = 0.f;
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) {
+      const int t = qq >> 3, jj = 2 * (qq & 7);
+      bf16x2v pr;
+      pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][jj], scale_log2, -base));
+      pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][jj + 1], scale_log2, -base));
+      pb[2 * t + (jj >> 3)][jj & 7] = pr[0];
+      pb[2 * t + (jj >> 3)][(jj & 7) + 1] = pr[1];
+      ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
+    }
+    l_lane += ps;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int d = 0; d < kDB; ++d) {
+        const char *vr = Vb + voff[d] + c * 16 * kRowB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vr);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 4 * kRowB));
+        bf16x8 a;
+        __builtin_memcpy(&a, &lo, 8);
+        __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &hi, 8);
+        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[d], 0, 0, 0);
+      }
+    asm volatile("s_barrier" ::: "memory");  // buffer buf is refilled next
+  }
+
+  // ---- partial (m, l, O) of this (use, kv head, head) ----
+  const float l_row = pair_sum(l_lane);
+  if (!valid) return;
+  const int64_t at = ((int64_t)slot * h_kv + g) * group + hh;
+  float *wo = ws_o + at * D + 4 * grp;
+#pragma unroll
+  for (int d = 0; d < kDB; ++d)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      f32x4 o;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) o[b] = acc[d][4 * a + b];
+      *reinterpret_cast<f32x4 *>(wo + 32 * d + 8 * a) = o;
+    }
+  if (grp == 0) {
+    ws_ml[at * 2 + 0] = m_run;
+    ws_ml[at * 2 + 1] = l_row;
+  }
+}
+
+template <int D, bool kHalf>
+__global__ __launch_bounds__(kDecThreads) void dec_attn_kernel(
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ pool_k,
+    const __bf16 *__restrict__ pool_v, const int32_t *__restrict__ chunk_block_ptr,
+    const int32_t *__restrict__ block_ids, const __bf16 *__restrict__ k_fresh,
+    const __bf16 *__restrict__ v_fresh, const DecItem *__restrict__ items,
+    const int32_t *__restrict__ uses, const int32_t *__restrict__ segs,
+    const int32_t *__restrict__ req_row_ptr, const float2 *__restrict__ angles,
+    float *__restrict__ ws_o, float *__restrict__ ws_ml, int h_q, int h_kv, int n_chunks,
+    float scale_log2, int pool_bytes) {
+  dec_attn_body<D, kHalf>(q, pool_k, pool_v, chunk_block_ptr, block_ids, k_fresh, v_fresh,
+                          items, uses, segs, req_row_ptr, angles, ws_o, ws_ml, h_q, h_kv,
+                          n_chunks, scale_log2, pool_bytes);
+}
+
+// Per (request, query head, 4 dims): online log-sum-exp over the request's pool-chunk
+// partials, its fresh-row partial and the new token (score q . k_new, weight v_new).
+template <int D>
+__global__ __launch_bounds__(256) void dec_merge_kernel(
+    __bf16 *__restrict__ out, const __bf16 *__restrict__ q, const __bf16 *__restrict__ k_new,
+    const __bf16 *__restrict__ v_new, const int32_t *__restrict__ req_chunk_ptr,
+    const int32_t *__restrict__ req_row_ptr, const int32_t *__restrict__ segs,
+    const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int n_req, int h_q,
+    int h_kv, int n_chunks, float scale_log2) {
+  constexpr int kC = D / 4;
+  const int group = h_q / h_kv;
+  const int64_t total = (int64_t)n_req * h_q * kC;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * 256) {
+    const int b = (int)(idx / (h_q * kC));
+    const int rem = (int)(idx - (int64_t)b * h_q * kC);
+    const int h = rem / kC, c4 = rem - h * kC;
+    const int g = h / group, hh = h - g * group;
+    // the new token: one key at its own position
+    const __bf16 *qp = q + ((int64_t)b * h_q + h) * D;
+    const __bf16 *kp = k_new + ((int64_t)b * h_kv + g) * D;
+    float dot = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < D; d += 8) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(qp + d);
+      const bf16x8 k = *reinterpret_cast<const bf16x8 *>(kp + d);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = fmaf((float)a[e], (float)k[e], dot);
+    }
+    float mmax = dot * scale_log2, den = 1.f;
+    f32x4 num;
+    {
+      const bf16x4 v = *reinterpret_cast<const bf16x4 *>(v_new + ((int64_t)b * h_kv + g) * D + 4 * c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] = (float)v[e];
+    }
+    auto fold = [&](int64_t slot) {
+      const int64_t at = (slot * h_kv + g) * group + hh;
+      const float ms = ws_ml[at * 2], ls = ws_ml[at * 2 + 1];
+      if (ms == kNegInf) return;
+      const f32x4 os = *reinterpret_cast<const f32x4 *>(ws_o + at * D + 4 * c4);
+      if (ms > mmax) {
+        const float r = __builtin_amdgcn_exp2f(mmax - ms);
+        den *= r;
+        num *= r;
+        mmax = ms;
+      }
+      const float w = __builtin_amdgcn_exp2f(ms - mmax);
+      den += w * ls;
+      num += w * os;
+    };
+    for (int c = req_chunk_ptr[b]; c < req_chunk_ptr[b + 1]; ++c)
+      if (segs[8 * c + 1] > 0) fold(c);
+    if (req_row_ptr[b + 1] > req_row_ptr[b]) fold(n_chunks + b);
+    const float inv = 1.f / den;
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (__bf16)(num[e] * inv);
+    *reinterpret_cast<bf16x4 *>(out + ((int64_t)b * h_q + h) * D + 4 * c4) = o;
+  }
+}
+
 // ================================ fp32 kernel ==================================
 
 constexpr int kF32Waves = 8;
@@ -1108,8 +1446,111 @@ int launch_paged(const PlanHeader &h, const int32_t *plan_dev, const void *q, co
   return PIC_OK;
 }
 
+// Decode workspace: partial O [n_chunks + n_req][h_kv][G][D], partial (m, l) [..][2],
+// then the angle table [n_chunks][D/2] float2 (16-byte aligned).
+size_t dec_partial_floats(const PlanHeader &h, int head_dim) {
+  return (size_t)(h[PIC_H_N_CHUNKS] + h[PIC_H_N_REQ]) * h[PIC_H_H_Q] * ((size_t)head_dim + 2);
+}
+
+template <int D, bool kHalf>
+int launch_decode(const PlanHeader &h, const int32_t *plan_dev, const void *q, const void *k_new,
+                  const void *v_new, const void *pool_k, const void *pool_v, const int32_t *cbp,
+                  const int32_t *bids, const void *kf, const void *vf, void *out, double rope_base,
+                  float scale, void *workspace, int pool_bytes, hipStream_t s) {
+  const int32_t *segs = plan_dev + h[PIC_H_O_SEGS];
+  const DecItem *items = reinterpret_cast<const DecItem *>(plan_dev + h[PIC_H_O_DEC_ITEMS]);
+  const int32_t *uses = plan_dev + h[PIC_H_O_DEC_USES];
+  const int32_t *rcp = plan_dev + h[PIC_H_O_REQ_CHUNK_PTR];
+  const int32_t *rrp = plan_dev + h[PIC_H_O_REQ_ROW_PTR];
+  float *ws_o = static_cast<float *>(workspace);
+  float *ws_ml = ws_o + (size_t)(h[PIC_H_N_CHUNKS] + h[PIC_H_N_REQ]) * h[PIC_H_H_Q] * D;
+  const size_t ang_off = (dec_partial_floats(h, D) * sizeof(float) + 15) / 16 * 16;
+  float2 *angles = reinterpret_cast<float2 *>(static_cast<char *>(workspace) + ang_off);
+  const int n_chunks = h[PIC_H_N_CHUNKS];
+  if (n_chunks > 0) {
+    const int64_t total = (int64_t)n_chunks * (D / 2);
+    const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65535);
+    hipLaunchKernelGGL(paged_angles_kernel, dim3(blocks), dim3(256), 0, s, angles, segs,
+                       n_chunks, D / 2, make_theta(D, rope_base));
+    PIC_LAUNCH_CHECK();
+  }
+  const float scale_log2 = scale * kLog2e;
+  if (h[PIC_H_N_DEC_ITEMS] > 0) {
+    hipLaunchKernelGGL((dec_attn_kernel<D, kHalf>),
+                       dim3(h[PIC_H_N_DEC_ITEMS], h[PIC_H_H_KV]), dim3(kDecThreads), 0, s,
+                       static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(pool_k),
+                       static_cast<const __bf16 *>(pool_v), cbp, bids,
+                       static_cast<const __bf16 *>(kf), static_cast<const __bf16 *>(vf), items,
+                       uses, segs, rrp, angles, ws_o, ws_ml, h[PIC_H_H_Q], h[PIC_H_H_KV],
+                       n_chunks, scale_log2, pool_bytes);
+    PIC_LAUNCH_CHECK();
+  }
+  const int64_t threads = (int64_t)h[PIC_H_N_REQ] * h[PIC_H_H_Q] * (D / 4);
+  const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((threads + 255) / 256, 1 << 20));
+  hipLaunchKernelGGL((dec_merge_kernel<D>), dim3(blocks), dim3(256), 0, s,
+                     static_cast<__bf16 *>(out), static_cast<const __bf16 *>(q),
+                     static_cast<const __bf16 *>(k_new), static_cast<const __bf16 *>(v_new), rcp,
+                     rrp, segs, ws_o, ws_ml, h[PIC_H_N_REQ], h[PIC_H_H_Q], h[PIC_H_H_KV],
+                     n_chunks, scale_log2);
+  PIC_LAUNCH_CHECK();
+  return PIC_OK;
+}
+
 }  // namespace
 }  // namespace pic
+
+extern "C" size_t pic_decode_workspace_bytes(const int32_t *plan_host, int32_t head_dim) {
+  using namespace pic;
+  const PlanHeader h{plan_host};
+  if (!h.valid() || !h[PIC_H_PAGED] || head_dim <= 0) return 0;
+  return (dec_partial_floats(h, head_dim) * sizeof(float) + 15) / 16 * 16 +
+         (size_t)h[PIC_H_N_CHUNKS] * (head_dim / 2) * sizeof(float2);
+}
+
+extern "C" int pic_decode_attn_paged(
+    const int32_t *plan_host, const int32_t *plan_dev, const void *q_new, const void *k_new,
+    const void *v_new, const void *pool_k, const void *pool_v, int64_t pool_blocks,
+    int32_t block_size, const int32_t *chunk_block_ptr, int32_t n_pool_chunks,
+    const int32_t *block_ids, const void *k_fresh, const void *v_fresh, void *out, int32_t dtype,
+    int32_t head_dim, int32_t rope_layout, double rope_base, float scale, void *workspace,
+    size_t workspace_bytes, void *stream) {
+  using namespace pic;
+  const PlanHeader h{plan_host};
+  if (!h.valid() || !h[PIC_H_PAGED]) return PIC_EINVAL;
+  if (dtype != PIC_BF16 && dtype != PIC_F32) return PIC_EINVAL;
+  if (rope_layout != PIC_ROPE_ADJACENT && rope_layout != PIC_ROPE_HALF) return PIC_EINVAL;
+  if (!(scale > 0.f) || !std::isfinite(scale) || head_dim <= 0 || pool_blocks < 0) return PIC_EINVAL;
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return PIC_EINVAL;
+  if (dtype != PIC_BF16 || block_size != kPoolBlockRows) return PIC_EUNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PIC_EUNSUPPORTED;
+  if (h[PIC_H_H_Q] / h[PIC_H_H_KV] > PIC_DECODE_COLS) return PIC_EUNSUPPORTED;
+  const int64_t tok_bytes = (int64_t)h[PIC_H_H_KV] * head_dim * 2;
+  const int64_t pool_bytes = pool_blocks * kPoolBlockRows * tok_bytes;
+  if (pool_bytes > 0x7fff0000LL || (int64_t)h[PIC_H_N_ROWS] * tok_bytes > 0x7fff0000LL)
+    return PIC_EUNSUPPORTED;
+  const int32_t *segs_h = plan_host + h[PIC_H_O_SEGS];
+  for (int32_t c = 0; c < h[PIC_H_N_CHUNKS]; ++c)
+    if (segs_h[8 * c + 3] >= n_pool_chunks) return PIC_EINVAL;
+  if (h[PIC_H_N_REQ] == 0) return PIC_OK;
+  if (!plan_dev || !q_new || !k_new || !v_new || !out || !workspace) return PIC_EINVAL;
+  if (h[PIC_H_N_CHUNKS] > 0 && (!pool_k || !pool_v || !chunk_block_ptr || !block_ids))
+    return PIC_EINVAL;
+  if (h[PIC_H_N_ROWS] > 0 && (!k_fresh || !v_fresh)) return PIC_EINVAL;
+  if (workspace_bytes < pic_decode_workspace_bytes(plan_host, head_dim)) return PIC_ENOSPC;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool half = rope_layout == PIC_ROPE_HALF;
+#define PIC_DEC(D_, H_)                                                                     \
+  return launch_decode<D_, H_>(h, plan_dev, q_new, k_new, v_new, pool_k, pool_v,            \
+                               chunk_block_ptr, block_ids, k_fresh, v_fresh, out, rope_base, \
+                               scale, workspace, (int)pool_bytes, s)
+  if (head_dim == 128) {
+    if (half) PIC_DEC(128, true);
+    PIC_DEC(128, false);
+  }
+  if (half) PIC_DEC(64, true);
+  PIC_DEC(64, false);
+#undef PIC_DEC
+}
 
 extern "C" size_t pic_attn_workspace_bytes(const int32_t *plan_host, int32_t head_dim) {
   using namespace pic;

@@ -30,6 +30,10 @@ struct AttnItem {
 struct MergeEntry {
   int32_t tile, kv_head, slot_base, n_slots;
 };
+struct DecItem {
+  int32_t src;  // pool chunk id (>= 0) or -1 - b for the fresh rows of request b
+  int32_t t_begin, t_end, use_begin, n_uses, pad0, pad1, pad2;
+};
 struct RopeTile {
   int32_t tok_begin, n_rows, delta;
   int32_t pos0;  // global position (within the request) of the first row
@@ -39,6 +43,7 @@ static_assert(sizeof(AttnTile) == 32, "plan record size");
 static_assert(sizeof(AttnItem) == 32, "plan record size");
 static_assert(sizeof(MergeEntry) == 16, "plan record size");
 static_assert(sizeof(RopeTile) == 16, "plan record size");
+static_assert(sizeof(DecItem) == 32, "plan record size");
 
 inline size_t dtype_size(int32_t dt) { return dt == PIC_BF16 ? 2 : (dt == PIC_F32 ? 4 : 0); }
 

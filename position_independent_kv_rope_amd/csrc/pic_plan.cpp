@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <cstring>
 #include <numeric>
+#include <unordered_map>
 #include <vector>
 
 #include "pic_internal.h"
@@ -141,6 +142,13 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
     if (chunk_lens[c] < 0 || (chunk_ids != nullptr && chunk_ids[c] < 0)) return PIC_EINVAL;
   const bool paged = chunk_ids != nullptr;
   if (n_cu <= 0) n_cu = 256;
+  if (paged) {  // a pool chunk has one length wherever it is used
+    std::unordered_map<int32_t, int32_t> len_of;
+    for (int32_t c = 0; c < n_chunks; ++c) {
+      const auto ins = len_of.emplace(chunk_ids[c], chunk_lens[c]);
+      if (!ins.second && ins.first->second != chunk_lens[c]) return PIC_EINVAL;
+    }
+  }
 
   // ---- offsets, token and row pointers (64-bit, then range-checked) ----
   std::vector<int32_t> chunk_off(n_chunks + n_req);
@@ -348,6 +356,49 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   }
   items = xcd_order(std::move(items), tiles, kXcd);
 
+  // ---- decode items (paged plans): every pool chunk once, for all its uses ----
+  // A decode step streams each pool chunk from HBM once and serves every request
+  // chunk that reads it (up to PIC_DECODE_COLS / G uses per item); each request's fresh
+  // rows (seams and queries) form one more item.
+  std::vector<DecItem> dec_items;
+  std::vector<int32_t> dec_uses;
+  if (paged && group <= PIC_DECODE_COLS) {
+    const int32_t per_item = PIC_DECODE_COLS / group;
+    std::vector<std::pair<int32_t, int32_t>> by_id;  // (pool chunk id, global chunk index)
+    for (int32_t c = 0; c < n_chunks; ++c)
+      if (chunk_lens[c] > 0) by_id.push_back({chunk_ids[c], c});
+    std::stable_sort(by_id.begin(), by_id.end(),
+                     [](const std::pair<int32_t, int32_t> &a,
+                        const std::pair<int32_t, int32_t> &b) { return a.first < b.first; });
+    for (size_t i = 0; i < by_id.size();) {
+      size_t j = i;
+      while (j < by_id.size() && by_id[j].first == by_id[i].first) ++j;
+      for (size_t u = i; u < j; u += per_item) {
+        DecItem d{};
+        d.src = by_id[i].first;
+        d.t_begin = 0;
+        d.t_end = chunk_lens[by_id[i].second];
+        d.use_begin = (int32_t)dec_uses.size();
+        d.n_uses = (int32_t)std::min<size_t>(per_item, j - u);
+        for (size_t v = u; v < u + (size_t)d.n_uses; ++v) dec_uses.push_back(by_id[v].second);
+        dec_items.push_back(d);
+      }
+      i = j;
+    }
+    for (int32_t b = 0; b < n_req; ++b) {
+      const int32_t r_b = req_row_ptr[b + 1] - req_row_ptr[b];
+      if (r_b == 0) continue;
+      DecItem d{};
+      d.src = -1 - b;
+      d.t_begin = 0;
+      d.t_end = r_b;
+      d.use_begin = (int32_t)dec_uses.size();
+      d.n_uses = 1;
+      dec_uses.push_back(-1 - b);
+      dec_items.push_back(d);
+    }
+  }
+
   // ---- layout of the plan ----
   int64_t words = PIC_PLAN_HEADER_WORDS;
   auto place = [&words](int64_t n) {
@@ -367,6 +418,8 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   const int64_t o_merge = place((int64_t)merges.size() * 4);
   const int64_t o_segs = place((int64_t)segs.size());
   const int64_t o_kblocks = place((int64_t)kblocks.size());
+  const int64_t o_dec_items = place((int64_t)dec_items.size() * 8);
+  const int64_t o_dec_uses = place((int64_t)dec_uses.size());
   if (words > kMaxI32) return PIC_EINVAL;
   *plan_words = words;
   if (plan == nullptr) return PIC_OK;
@@ -405,6 +458,10 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   h[PIC_H_O_SEGS] = (int32_t)o_segs;
   h[PIC_H_N_KBLOCKS] = (int32_t)(kblocks.size() / 4);
   h[PIC_H_O_KBLOCKS] = (int32_t)o_kblocks;
+  h[PIC_H_N_DEC_ITEMS] = (int32_t)dec_items.size();
+  h[PIC_H_O_DEC_ITEMS] = (int32_t)o_dec_items;
+  h[PIC_H_N_DEC_USES] = (int32_t)dec_uses.size();
+  h[PIC_H_O_DEC_USES] = (int32_t)o_dec_uses;
   if (n_req > 0) std::memcpy(h + o_rcp, req_chunk_ptr, sizeof(int32_t) * (n_req + 1));
   else h[o_rcp] = 0;
   if (!chunk_off.empty()) std::memcpy(h + o_coff, chunk_off.data(), sizeof(int32_t) * chunk_off.size());
@@ -420,6 +477,10 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   if (!merges.empty()) std::memcpy(h + o_merge, merges.data(), sizeof(MergeEntry) * merges.size());
   if (!segs.empty()) std::memcpy(h + o_segs, segs.data(), sizeof(int32_t) * segs.size());
   if (!kblocks.empty()) std::memcpy(h + o_kblocks, kblocks.data(), sizeof(int32_t) * kblocks.size());
+  if (!dec_items.empty())
+    std::memcpy(h + o_dec_items, dec_items.data(), sizeof(DecItem) * dec_items.size());
+  if (!dec_uses.empty())
+    std::memcpy(h + o_dec_uses, dec_uses.data(), sizeof(int32_t) * dec_uses.size());
   return PIC_OK;
 }
 

@@ -166,6 +166,15 @@ def pool_tensors(wl):
             draw(shape, wl.seed * 7 + 2, wl.torch_dtype, wl.value_scale))
 
 
+def decode_tensors(wl):
+    """The next token of every request (decode step): Q [n_req, Hq, D], K/V
+    [n_req, Hkv, D]."""
+    n = len(wl.requests)
+    return (draw((n, wl.h_q, wl.head_dim), wl.seed * 7 + 6, wl.torch_dtype, wl.value_scale),
+            draw((n, wl.h_kv, wl.head_dim), wl.seed * 7 + 7, wl.torch_dtype, wl.value_scale),
+            draw((n, wl.h_kv, wl.head_dim), wl.seed * 7 + 8, wl.torch_dtype, wl.value_scale))
+
+
 CONFIGS = {
     "worked_example": worked_example,
     "rag_single": rag_single,

@@ -282,11 +282,35 @@ def check_paged_plan(reqs, ids, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0):
         assert 0 <= b1 <= e1 and 0 <= b2 <= e2
         for i in list(range(b1, e1)) + list(range(b2, e2)):
             assert kb[i][2] <= tiles[tile][5]  # no block starts after the tile's last row
+    # decode items: every request chunk with keys is one use of exactly one item of
+    # its pool chunk (whole chunk, at most PIC_DECODE_COLS / G uses), plus one item per
+    # request with fresh rows
+    group = h_q // h_kv
+    items, uses = plan.dec_items.tolist(), plan.dec_uses.tolist()
+    assert plan[P.H_N_DEC_USES] == len(uses)
+    flat_lens = [x for lens in reqs for x in lens]
+    flat_ids = [x for c in ids for x in c]
+    seen, fresh = [], []
+    for src, t0, t1, u0, nu, _, _, _ in items:
+        assert 1 <= nu <= P.PIC_DECODE_COLS // group and t0 == 0
+        us = uses[u0:u0 + nu]
+        if src >= 0:
+            for c in us:
+                assert flat_ids[c] == src and flat_lens[c] == t1 > 0
+            seen += us
+        else:
+            b = -1 - src
+            assert us == [src] and t1 == int(plan.req_row_ptr[b + 1] - plan.req_row_ptr[b]) > 0
+            fresh.append(b)
+    assert sorted(seen) == [c for c, L in enumerate(flat_lens) if L > 0]
+    assert fresh == [b for b in range(len(reqs)) if plan.req_row_ptr[b + 1] > plan.req_row_ptr[b]]
     return plan
 
 
 def test_paged_plan_small():
-    check_paged_plan([[37, 64, 5, 130], [70, 70]], [[3, 0, 7, 2], [2, 5]], [9, 4], 8, 32, 4)
+    check_paged_plan([[37, 64, 5, 130], [130, 70]], [[3, 0, 7, 2], [2, 5]], [9, 4], 8, 32, 4)
+    # one pool chunk read twice by one request, and by two requests
+    check_paged_plan([[16, 3, 16, 64], [64, 16]], [[0, 1, 0, 3], [3, 0]], [7, 0], 8, 8, 2)
     check_paged_plan([[4, 5, 5]], [[0, 1, 2]], [3], 2, 4, 4, pos_base=3)
 
 
@@ -300,3 +324,9 @@ def test_paged_plan_shared_pool_workload():
 def test_paged_plan_rejects_negative_ids():
     with pytest.raises(P.PicError):
         P.pic_build_index([[4, 5]], [1], 2, 4, 4, chunk_ids_per_req=[[0, -1]])
+
+
+def test_paged_plan_rejects_inconsistent_chunk_lengths():
+    # a pool chunk has one length wherever it is used
+    with pytest.raises(P.PicError):
+        P.pic_build_index([[4, 5], [6]], [1, 1], 2, 4, 4, chunk_ids_per_req=[[0, 1], [1]])

@@ -153,3 +153,84 @@ def test_paged_shared_pool_full_size_sampled():
     # the shared-pool workload (256 pooled chunks, 8 requests x ~116k tokens, w = 8) in
     # the launch configuration bench.py times (n_cu = 256), sampled rows
     run_paged(W.shared_pool(), n_cu=256, sample_rows=24)
+
+
+# ---------------------------------------------------------------------------
+# Decode step over the shared pool (pic_decode_attn_paged)
+# ---------------------------------------------------------------------------
+
+
+def run_decode(wl, layout="adjacent", nan_slack=False, n_cu=0, requests=None):
+    reqs = [r.chunk_lens for r in wl.requests]
+    ids = [r.chunk_ids for r in wl.requests]
+    qs = [r.q_len for r in wl.requests]
+    plan = P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, n_cu=n_cu, chunk_ids_per_req=ids)
+    plan.to_device()
+    cbp, blocks = W.pool_block_table(wl)
+    pk, pv = W.pool_tensors(wl)
+    bs = wl.block_size
+    assert len(cbp) == len(wl.pool_lens) + 1
+    assert all(cbp[i + 1] - cbp[i] >= -(-L // bs) for i, L in enumerate(wl.pool_lens))
+    assert blocks.min(initial=0) >= 0 and blocks.max(initial=0) < pk.shape[0]
+    if nan_slack:
+        for i, L in enumerate(wl.pool_lens):
+            if L % bs:
+                last = blocks[cbp[i + 1] - 1]
+                pk[last, L % bs:] = float("nan")
+                pv[last, L % bs:] = float("nan")
+    _, kf, vf = W.fresh_tensors(wl, plan.n_rows)
+    qn, kn, vn = W.decode_tensors(wl)
+    dev = "cuda"
+    out = torch.full(qn.shape, float("nan"), dtype=qn.dtype, device=dev)
+    say(wl.name, "decode", layout, "items=%d uses=%d" % (plan[P.H_N_DEC_ITEMS],
+                                                        plan[P.H_N_DEC_USES]))
+    lay = P.PIC_ROPE_HALF if layout == "half" else P.PIC_ROPE_ADJACENT
+    P.pic_decode_attn_paged(plan, qn.to(dev), kn.to(dev), vn.to(dev), pk.to(dev), pv.to(dev),
+                            torch.from_numpy(cbp).to(dev), torch.from_numpy(blocks).to(dev),
+                            kf.to(dev), vf.to(dev), out, wl.rope_base, layout=lay)
+    torch.cuda.synchronize()
+    got_all = f64(out.cpu())
+    assert np.isfinite(got_all).all()
+    pk64, pv64 = f64(pk), f64(pv)
+    worst = 0.0
+    for b, r in enumerate(wl.requests):
+        if requests is not None and b not in requests:
+            continue
+        row0, row1 = int(plan.req_row_ptr[b]), int(plan.req_row_ptr[b + 1])
+        rows = O.recompute_positions(r.chunk_lens, r.q_len, wl.k)
+        ck = [O.gather_paged_chunk(pk64, blocks[cbp[i]:cbp[i + 1]], wl.pool_lens[i]) for i in r.chunk_ids]
+        cv = [O.gather_paged_chunk(pv64, blocks[cbp[i]:cbp[i + 1]], wl.pool_lens[i]) for i in r.chunk_ids]
+        if ck:
+            k_ctx, v_ctx = O.rope_delta(ck, wl.rope_base, layout), O.concat_chunks(cv)
+        else:
+            k_ctx = v_ctx = np.zeros((0, wl.h_kv, wl.head_dim))
+        n_total = sum(r.chunk_lens) + r.q_len
+        kx, vx = O.splice(k_ctx, v_ctx, f64(kf[row0:row1]), f64(vf[row0:row1]), rows, n_total)
+        want = O.decode_attn(f64(qn[b]), kx, vx, f64(kn[b]), f64(vn[b]))
+        err = float(np.max(np.abs(got_all[b] - want)))
+        worst = max(worst, err)
+        assert err <= TOL, ("decode", b, err)
+    say(wl.name, "decode max-abs error", worst)
+    return worst
+
+
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_decode_small(layout):
+    run_decode(small_pool(8), layout)
+
+
+def test_decode_edges_nan_slack_and_gqa4_d64():
+    run_decode(small_pool(8, seed=41), nan_slack=True)
+    run_decode(small_pool(4, h_q=32, h_kv=8, d=64, seed=47))
+    lens = [16, 3, 200, 64, 1]
+    reqs = [W.Request([200], 0, chunk_ids=[2]),           # no recomputed rows at all
+            W.Request([], 5, chunk_ids=[]),               # only query rows
+            W.Request([16, 3, 16, 64, 1, 200], 7, chunk_ids=[0, 1, 0, 3, 4, 2])]
+    run_decode(W.Workload("decode_edges", "bf16", 8, 2, 128, 10000.0, 8, reqs, pool_lens=lens,
+                          block_size=16, pool_block_perm_seed=3, seed=53))
+
+
+def test_decode_shared_pool_full_size():
+    # the shared-pool batch (8 requests x ~116k tokens from 256 pooled chunks, w = 8):
+    # every request's output against the oracle
+    run_decode(W.shared_pool(), n_cu=256)

@@ -492,3 +492,37 @@ def test_attn_rows_direct_matches_selective_attn():
                              [h // (hq // hkv) for _, h in picks])
     want = np.stack([full[i, h] for i, h in picks])
     assert np.max(np.abs(got - want)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Decode after the link
+# ---------------------------------------------------------------------------
+
+
+def test_decode_attn_is_last_row_of_full_causal_attention():
+    # the decode output equals the last row of plain causal attention over the spliced
+    # sequence extended by the new token (brute force, N x N mask)
+    rng = np.random.default_rng(11)
+    n, hq, hkv, d = 13, 4, 2, 8
+    k_all = rng.standard_normal((n + 1, hkv, d))
+    v_all = rng.standard_normal((n + 1, hkv, d))
+    q_all = rng.standard_normal((n + 1, hq, d))
+    want = O.full_causal_attn(q_all, k_all, v_all)[n]
+    got = O.decode_attn(q_all[n], k_all[:n], v_all[:n], k_all[n], v_all[n])
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+def test_decode_attn_single_key_and_planted_self_exclusion():
+    rng = np.random.default_rng(12)
+    d = 8
+    k_new, v_new = rng.standard_normal((1, d)), rng.standard_normal((1, d))
+    # no earlier keys: the output is the new token's own value
+    got = O.decode_attn(rng.standard_normal((2, d)), np.zeros((0, 1, d)), np.zeros((0, 1, d)),
+                        k_new[0][None], v_new[0][None])
+    assert np.allclose(got, np.broadcast_to(v_new, (2, d)), atol=1e-12)
+    # leaving the new token out of its own keys must change the result
+    kx, vx = rng.standard_normal((6, 1, d)), rng.standard_normal((6, 1, d))
+    q = rng.standard_normal((1, d))
+    with_self = O.decode_attn(q, kx, vx, k_new, v_new)
+    without = O.selective_attn(q[None], kx, vx, [5])[0]
+    assert np.max(np.abs(with_self - without)) > 1e-3
