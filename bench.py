@@ -46,6 +46,9 @@ def parse():
                     help="delta: cached K carries RoPE at local positions and is rotated by "
                          "delta (pic_rope_delta); nope: cached K is position-free and gets "
                          "RoPE at the target positions (pic_rope_apply)")
+    ap.add_argument("--decode", action="store_true",
+                    help="shared_pool only: time one decode step of every request "
+                         "(pic_decode_attn_paged) instead of the link")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="recomputed rows of request 0 the oracle times (0 = all)")
@@ -300,6 +303,118 @@ def bench_paged(args, wl):
     print(json.dumps(rec), flush=True)
 
 
+def bench_decode(args, wl):
+    """One decode step of every request of the shared-pool batch: its next token attends
+    over the request's pool chunks (rotated on load), recomputed rows and itself."""
+    import torch
+    import position_independent_kv_rope_amd as P
+    from position_independent_kv_rope_amd import workloads as W
+    from oracle import pic_oracle as O
+    reqs = [r.chunk_lens for r in wl.requests]
+    ids = [r.chunk_ids for r in wl.requests]
+    qs = [r.q_len for r in wl.requests]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, n_cu=n_cu, chunk_ids_per_req=ids)
+    plan.to_device()
+    cbp, blocks = W.pool_block_table(wl)
+    pk_h, pv_h = W.pool_tensors(wl)
+    _, kf_h, vf_h = W.fresh_tensors(wl, plan.n_rows)
+    qn_h, kn_h, vn_h = W.decode_tensors(wl)
+    dev = "cuda"
+    pk, pv = pk_h.to(dev), pv_h.to(dev)
+    cbp_d, blocks_d = torch.from_numpy(cbp).to(dev), torch.from_numpy(blocks).to(dev)
+    kf, vf = kf_h.to(dev), vf_h.to(dev)
+    qn, kn, vn = qn_h.to(dev), kn_h.to(dev), vn_h.to(dev)
+    out = torch.empty_like(qn)
+    ws = P.decode_workspace(plan, wl.head_dim)
+    torch.cuda.synchronize()
+
+    s = wl.torch_dtype.itemsize
+    D, hq, hkv = wl.head_dim, wl.h_q, wl.h_kv
+    row_bytes = s * hkv * D  # one token's K (or V) for all KV heads
+    used = sorted({i for r in wl.requests for i in r.chunk_ids})
+    pool_used_tokens = sum(wl.pool_lens[i] for i in used)
+    # chunk-major minimum: every used pool chunk once, the fresh rows, the new tokens, Q/O
+    dec_bytes = (2.0 * row_bytes * (pool_used_tokens + plan.n_rows + len(wl.requests))
+                 + 2.0 * s * hq * D * len(wl.requests))
+    per_request_bytes = 2.0 * row_bytes * (plan.n_tokens + len(wl.requests))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+
+    def step(i=None):
+        e = ev[i] if i is not None else None
+        if e: e[0].record()
+        P.pic_decode_attn_paged(plan, qn, kn, vn, pk, pv, cbp_d, blocks_d, kf, vf, out,
+                                wl.rope_base, workspace=ws)
+        if e: e[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    t_dec = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    gbs = dec_bytes / (t_dec * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(plan.n_tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": "shared_pool_decode", "requests": len(wl.requests),
+                   "context_tokens": plan.n_tokens, "pool_chunks": len(wl.pool_lens),
+                   "pool_chunks_used": len(used), "seam_window": wl.k, "h_q": hq, "h_kv": hkv,
+                   "head_dim": D, "parallelism": "none (1 GPU)"},
+        "decode_steps_per_s": round(1e3 / ms_step, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic("decode", "shared_pool_k%d" % wl.k),
+                     "kernel": "pic_decode_attn_paged call (paged_angles_kernel + "
+                               "dec_attn_kernel + dec_merge_kernel)",
+                     "algorithmic_bytes": dec_bytes,
+                     "per_request_streaming_bytes": per_request_bytes},
+        "kernels": {"decode_attn": {"ms": round(t_dec, 4), "GB_s": round(gbs, 1),
+                                    "items": plan[P.H_N_DEC_ITEMS], "uses": plan[P.H_N_DEC_USES]}},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle's decode of request 0: pool gather, rotation, splice, attention
+        t1 = time.perf_counter()
+        r = wl.requests[0]
+        row0, row1 = int(plan.req_row_ptr[0]), int(plan.req_row_ptr[1])
+        f64 = lambda t: t.to(torch.float64).numpy()
+        ck, cv = [], []
+        for i in r.chunk_ids:
+            sub = torch.from_numpy(blocks[cbp[i]:cbp[i + 1]].astype(np.int64))
+            ck.append(O.gather_paged_chunk(f64(pk_h[sub]), np.arange(len(sub)), wl.pool_lens[i]))
+            cv.append(O.gather_paged_chunk(f64(pv_h[sub]), np.arange(len(sub)), wl.pool_lens[i]))
+        rows = O.recompute_positions(r.chunk_lens, r.q_len, wl.k)
+        kx, vx = O.splice(O.rope_delta(ck, wl.rope_base), O.concat_chunks(cv),
+                          f64(kf_h[row0:row1]), f64(vf_h[row0:row1]), rows,
+                          sum(r.chunk_lens) + r.q_len)
+        O.decode_attn(f64(qn_h[0]), kx, vx, f64(kn_h[0]), f64(vn_h[0]))
+        dt = time.perf_counter() - t1
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        n0 = sum(r.chunk_lens) + r.q_len
+        rec["cpu_baseline"] = {"value": round(n0 / dt, 1), "unit": "tokens/s", "cores": int(threads),
+                               "kind": "oracle", "seconds": round(dt, 3),
+                               "sample": "decode step of request 0 (%d context tokens): pool "
+                                         "gather, rotation, splice, attention of the new token"
+                                         % n0, "host_cpus": os.cpu_count()}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -318,7 +433,10 @@ def main():
     P.lib()
     wl = make_workload(args.workload, args.k)
     if wl.pool_lens is not None:
-        return bench_paged(args, wl)
+        return bench_decode(args, wl) if args.decode else bench_paged(args, wl)
+    if args.decode:
+        print("--decode needs --workload shared_pool", file=sys.stderr)
+        sys.exit(2)
     reqs = [r.chunk_lens for r in wl.requests]
     qs = [r.q_len for r in wl.requests]
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count

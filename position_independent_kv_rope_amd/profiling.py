@@ -26,6 +26,7 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SHORT = [("attn_bf16_paged_kernel", "attn_bf16_paged"), ("paged_angles_kernel", "paged_angles"),
+         ("dec_attn_kernel", "dec_attn"), ("dec_merge_kernel", "dec_merge"),
          ("attn_bf16_kernel", "attn_bf16"), ("attn_f32_kernel", "attn_f32"),
          ("merge_kernel", "merge"), ("rope_delta_kernel", "rope_delta"),
          ("splice_kernel", "splice"), ("copyBuffer", "copy (calibration)")]
