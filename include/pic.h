@@ -79,7 +79,8 @@ enum { PIC_ROPE_ADJACENT = 0, PIC_ROPE_HALF = 1 };
 #define PIC_PLAN_HEADER_WORDS 40
 #define PIC_ATTN_TILE_M 128 /* query vectors (row, head) per attention tile */
 #define PIC_ROPE_TILE_ROWS 32
-#define PIC_DECODE_COLS 64 /* query columns (use, head) of one decode item */
+#define PIC_DECODE_COLS 64   /* query columns (use, head) of one decode item */
+#define PIC_DECODE_RANGE 256 /* keys of one decode item (a multiple of 64) */
 
 enum {
   PIC_H_MAGIC = 0,
@@ -124,13 +125,21 @@ enum {
                          come first, then the pool blocks in position order */
   PIC_H_N_DEC_ITEMS,  /* paged: decode work items (0 when h_q/h_kv > PIC_DECODE_COLS) */
   PIC_H_O_DEC_ITEMS,  /* paged: [n_dec_items][8] source (pool chunk id >= 0, or -1-b for
-                         the fresh rows of request b), first key, end key, first use,
-                         use count, 0, 0, 0; items of one pool chunk are adjacent */
+                         the fresh rows of request b), first key, end key (a range of
+                         <= PIC_DECODE_RANGE keys of the chunk or of the fresh rows), first
+                         use, use count, range index r, 0, 0; items of one pool chunk
+                         are adjacent */
   PIC_H_N_DEC_USES,
   PIC_H_O_DEC_USES,   /* paged: [n_dec_uses] per use, the global chunk index c reading the
                          item's pool chunk (or -1-b for fresh rows); at most
                          PIC_DECODE_COLS / (h_q/h_kv) uses per item */
-  PIC_H_RESERVED5
+  PIC_H_N_DEC_SLOTS,  /* paged: decode partial slots (one per key range of each request
+                         chunk and of each request's fresh rows) */
+  PIC_H_O_DEC_SLOT_BASE, /* paged: [n_chunks + n_req] first slot of each request chunk,
+                         then of each request's fresh rows (range r adds r) */
+  PIC_H_O_DEC_REQ_SLOTS, /* paged: [n_req + 1] slots of request b are
+                         [ptr[b], ptr[b+1]), every one written by exactly one item */
+  PIC_H_RESERVED6
 };
 
 /*

@@ -832,9 +832,9 @@ __device__ __forceinline__ void dec_attn_body(
     const int32_t *__restrict__ block_ids, const __bf16 *__restrict__ k_fresh,
     const __bf16 *__restrict__ v_fresh, const DecItem *__restrict__ items,
     const int32_t *__restrict__ uses, const int32_t *__restrict__ segs,
-    const int32_t *__restrict__ req_row_ptr, const float2 *__restrict__ angles,
-    float *__restrict__ ws_o, float *__restrict__ ws_ml, int h_q, int h_kv, int n_chunks,
-    float scale_log2, int pool_bytes) {
+    const int32_t *__restrict__ req_row_ptr, const int32_t *__restrict__ slot_base,
+    const float2 *__restrict__ angles, float *__restrict__ ws_o, float *__restrict__ ws_ml,
+    int h_q, int h_kv, int n_chunks, float scale_log2, int pool_bytes) {
   constexpr int kRowB = D * 2;
   constexpr int kCPR = D / 8;
   constexpr int kTileB = kKB * kRowB;
@@ -865,7 +865,7 @@ __device__ __forceinline__ void dec_attn_body(
   const int use = valid ? uses[it.use_begin + u] : 0;
   const int req = !valid ? 0 : (pool ? segs[8 * use + 5] : -1 - use);
   const int seam = (valid && pool) ? segs[8 * use + 2] : 0;
-  const int slot = pool ? use : n_chunks + req;
+  const int slot = valid ? slot_base[pool ? use : n_chunks + req] + it.range : 0;
 
   bf16x8 qop[kKS];
   {
@@ -1078,74 +1078,78 @@ __global__ __launch_bounds__(kDecThreads) void dec_attn_kernel(
     const int32_t *__restrict__ block_ids, const __bf16 *__restrict__ k_fresh,
     const __bf16 *__restrict__ v_fresh, const DecItem *__restrict__ items,
     const int32_t *__restrict__ uses, const int32_t *__restrict__ segs,
-    const int32_t *__restrict__ req_row_ptr, const float2 *__restrict__ angles,
-    float *__restrict__ ws_o, float *__restrict__ ws_ml, int h_q, int h_kv, int n_chunks,
-    float scale_log2, int pool_bytes) {
+    const int32_t *__restrict__ req_row_ptr, const int32_t *__restrict__ slot_base,
+    const float2 *__restrict__ angles, float *__restrict__ ws_o, float *__restrict__ ws_ml,
+    int h_q, int h_kv, int n_chunks, float scale_log2, int pool_bytes) {
   dec_attn_body<D, kHalf>(q, pool_k, pool_v, chunk_block_ptr, block_ids, k_fresh, v_fresh,
-                          items, uses, segs, req_row_ptr, angles, ws_o, ws_ml, h_q, h_kv,
-                          n_chunks, scale_log2, pool_bytes);
+                          items, uses, segs, req_row_ptr, slot_base, angles, ws_o, ws_ml, h_q,
+                          h_kv, n_chunks, scale_log2, pool_bytes);
 }
 
-// Per (request, query head, 4 dims): online log-sum-exp over the request's pool-chunk
-// partials, its fresh-row partial and the new token (score q . k_new, weight v_new).
+// One workgroup per (request, query head): 8 groups of D/4 lanes fold disjoint subsets
+// of the request's partial slots (online log-sum-exp, 4 dims per lane), group 0 also
+// the new token (score q . k_new, weight v_new); the 8 results are combined in LDS.
+constexpr int kDecMergeGroups = 8;
+
 template <int D>
-__global__ __launch_bounds__(256) void dec_merge_kernel(
+__global__ __launch_bounds__(kDecMergeGroups * (D / 4)) void dec_merge_kernel(
     __bf16 *__restrict__ out, const __bf16 *__restrict__ q, const __bf16 *__restrict__ k_new,
-    const __bf16 *__restrict__ v_new, const int32_t *__restrict__ req_chunk_ptr,
-    const int32_t *__restrict__ req_row_ptr, const int32_t *__restrict__ segs,
-    const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int n_req, int h_q,
-    int h_kv, int n_chunks, float scale_log2) {
+    const __bf16 *__restrict__ v_new, const int32_t *__restrict__ req_slots,
+    const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int h_q, int h_kv,
+    float scale_log2) {
   constexpr int kC = D / 4;
+  __shared__ float part_m[kDecMergeGroups][kC], part_l[kDecMergeGroups][kC];
+  __shared__ f32x4 part_o[kDecMergeGroups][kC];
+  const int b = blockIdx.x / h_q, h = blockIdx.x - b * h_q;
   const int group = h_q / h_kv;
-  const int64_t total = (int64_t)n_req * h_q * kC;
-  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * 256) {
-    const int b = (int)(idx / (h_q * kC));
-    const int rem = (int)(idx - (int64_t)b * h_q * kC);
-    const int h = rem / kC, c4 = rem - h * kC;
-    const int g = h / group, hh = h - g * group;
-    // the new token: one key at its own position
+  const int g = h / group, hh = h - g * group;
+  const int gi = threadIdx.x / kC, c4 = threadIdx.x - gi * kC;
+  float mmax = kNegInf, den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  if (gi == 0) {  // the new token: one key at its own position
     const __bf16 *qp = q + ((int64_t)b * h_q + h) * D;
     const __bf16 *kp = k_new + ((int64_t)b * h_kv + g) * D;
     float dot = 0.f;
-#pragma unroll 8
+#pragma unroll 4
     for (int d = 0; d < D; d += 8) {
       const bf16x8 a = *reinterpret_cast<const bf16x8 *>(qp + d);
       const bf16x8 k = *reinterpret_cast<const bf16x8 *>(kp + d);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot = fmaf((float)a[e], (float)k[e], dot);
     }
-    float mmax = dot * scale_log2, den = 1.f;
-    f32x4 num;
-    {
-      const bf16x4 v = *reinterpret_cast<const bf16x4 *>(v_new + ((int64_t)b * h_kv + g) * D + 4 * c4);
+    mmax = dot * scale_log2;
+    den = 1.f;
+    const bf16x4 v = *reinterpret_cast<const bf16x4 *>(v_new + ((int64_t)b * h_kv + g) * D + 4 * c4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) num[e] = (float)v[e];
-    }
-    auto fold = [&](int64_t slot) {
-      const int64_t at = (slot * h_kv + g) * group + hh;
-      const float ms = ws_ml[at * 2], ls = ws_ml[at * 2 + 1];
-      if (ms == kNegInf) return;
-      const f32x4 os = *reinterpret_cast<const f32x4 *>(ws_o + at * D + 4 * c4);
-      if (ms > mmax) {
-        const float r = __builtin_amdgcn_exp2f(mmax - ms);
-        den *= r;
-        num *= r;
-        mmax = ms;
-      }
-      const float w = __builtin_amdgcn_exp2f(ms - mmax);
-      den += w * ls;
-      num += w * os;
-    };
-    for (int c = req_chunk_ptr[b]; c < req_chunk_ptr[b + 1]; ++c)
-      if (segs[8 * c + 1] > 0) fold(c);
-    if (req_row_ptr[b + 1] > req_row_ptr[b]) fold(n_chunks + b);
-    const float inv = 1.f / den;
-    bf16x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = (__bf16)(num[e] * inv);
-    *reinterpret_cast<bf16x4 *>(out + ((int64_t)b * h_q + h) * D + 4 * c4) = o;
+    for (int e = 0; e < 4; ++e) num[e] = (float)v[e];
   }
+  auto fold = [&](float ms, float ls, const f32x4 &os) {
+    if (ms == kNegInf) return;
+    if (ms > mmax) {
+      const float r = __builtin_amdgcn_exp2f(mmax - ms);  // 0 when mmax is -inf
+      den *= r;
+      num *= r;
+      mmax = ms;
+    }
+    const float w = __builtin_amdgcn_exp2f(ms - mmax);
+    den += w * ls;
+    num += w * os;
+  };
+  for (int sl = req_slots[b] + gi; sl < req_slots[b + 1]; sl += kDecMergeGroups) {
+    const int64_t at = ((int64_t)sl * h_kv + g) * group + hh;
+    fold(ws_ml[at * 2], ws_ml[at * 2 + 1], *reinterpret_cast<const f32x4 *>(ws_o + at * D + 4 * c4));
+  }
+  part_m[gi][c4] = mmax;
+  part_l[gi][c4] = den;
+  part_o[gi][c4] = num;
+  __syncthreads();
+  if (gi != 0) return;
+  for (int o = 1; o < kDecMergeGroups; ++o) fold(part_m[o][c4], part_l[o][c4], part_o[o][c4]);
+  const float inv = 1.f / den;
+  bf16x4 res;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) res[e] = (__bf16)(num[e] * inv);
+  *reinterpret_cast<bf16x4 *>(out + ((int64_t)b * h_q + h) * D + 4 * c4) = res;
 }
 
 // ================================ fp32 kernel ==================================
@@ -1446,10 +1450,10 @@ int launch_paged(const PlanHeader &h, const int32_t *plan_dev, const void *q, co
   return PIC_OK;
 }
 
-// Decode workspace: partial O [n_chunks + n_req][h_kv][G][D], partial (m, l) [..][2],
+// Decode workspace: partial O [n_dec_slots][h_kv][G][D], partial (m, l) [..][2],
 // then the angle table [n_chunks][D/2] float2 (16-byte aligned).
 size_t dec_partial_floats(const PlanHeader &h, int head_dim) {
-  return (size_t)(h[PIC_H_N_CHUNKS] + h[PIC_H_N_REQ]) * h[PIC_H_H_Q] * ((size_t)head_dim + 2);
+  return (size_t)h[PIC_H_N_DEC_SLOTS] * h[PIC_H_H_Q] * ((size_t)head_dim + 2);
 }
 
 template <int D, bool kHalf>
@@ -1460,10 +1464,11 @@ int launch_decode(const PlanHeader &h, const int32_t *plan_dev, const void *q, c
   const int32_t *segs = plan_dev + h[PIC_H_O_SEGS];
   const DecItem *items = reinterpret_cast<const DecItem *>(plan_dev + h[PIC_H_O_DEC_ITEMS]);
   const int32_t *uses = plan_dev + h[PIC_H_O_DEC_USES];
-  const int32_t *rcp = plan_dev + h[PIC_H_O_REQ_CHUNK_PTR];
   const int32_t *rrp = plan_dev + h[PIC_H_O_REQ_ROW_PTR];
+  const int32_t *slot_base = plan_dev + h[PIC_H_O_DEC_SLOT_BASE];
+  const int32_t *req_slots = plan_dev + h[PIC_H_O_DEC_REQ_SLOTS];
   float *ws_o = static_cast<float *>(workspace);
-  float *ws_ml = ws_o + (size_t)(h[PIC_H_N_CHUNKS] + h[PIC_H_N_REQ]) * h[PIC_H_H_Q] * D;
+  float *ws_ml = ws_o + (size_t)h[PIC_H_N_DEC_SLOTS] * h[PIC_H_H_Q] * D;
   const size_t ang_off = (dec_partial_floats(h, D) * sizeof(float) + 15) / 16 * 16;
   float2 *angles = reinterpret_cast<float2 *>(static_cast<char *>(workspace) + ang_off);
   const int n_chunks = h[PIC_H_N_CHUNKS];
@@ -1481,17 +1486,15 @@ int launch_decode(const PlanHeader &h, const int32_t *plan_dev, const void *q, c
                        static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(pool_k),
                        static_cast<const __bf16 *>(pool_v), cbp, bids,
                        static_cast<const __bf16 *>(kf), static_cast<const __bf16 *>(vf), items,
-                       uses, segs, rrp, angles, ws_o, ws_ml, h[PIC_H_H_Q], h[PIC_H_H_KV],
-                       n_chunks, scale_log2, pool_bytes);
+                       uses, segs, rrp, slot_base, angles, ws_o, ws_ml, h[PIC_H_H_Q],
+                       h[PIC_H_H_KV], n_chunks, scale_log2, pool_bytes);
     PIC_LAUNCH_CHECK();
   }
-  const int64_t threads = (int64_t)h[PIC_H_N_REQ] * h[PIC_H_H_Q] * (D / 4);
-  const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((threads + 255) / 256, 1 << 20));
-  hipLaunchKernelGGL((dec_merge_kernel<D>), dim3(blocks), dim3(256), 0, s,
-                     static_cast<__bf16 *>(out), static_cast<const __bf16 *>(q),
-                     static_cast<const __bf16 *>(k_new), static_cast<const __bf16 *>(v_new), rcp,
-                     rrp, segs, ws_o, ws_ml, h[PIC_H_N_REQ], h[PIC_H_H_Q], h[PIC_H_H_KV],
-                     n_chunks, scale_log2);
+  hipLaunchKernelGGL((dec_merge_kernel<D>), dim3(h[PIC_H_N_REQ] * h[PIC_H_H_Q]),
+                     dim3(kDecMergeGroups * (D / 4)), 0, s, static_cast<__bf16 *>(out),
+                     static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k_new),
+                     static_cast<const __bf16 *>(v_new), req_slots, ws_o, ws_ml, h[PIC_H_H_Q],
+                     h[PIC_H_H_KV], scale_log2);
   PIC_LAUNCH_CHECK();
   return PIC_OK;
 }

@@ -32,7 +32,9 @@ struct MergeEntry {
 };
 struct DecItem {
   int32_t src;  // pool chunk id (>= 0) or -1 - b for the fresh rows of request b
-  int32_t t_begin, t_end, use_begin, n_uses, pad0, pad1, pad2;
+  int32_t t_begin, t_end, use_begin, n_uses;
+  int32_t range;  // key range index within the chunk (or the fresh rows)
+  int32_t pad0, pad1;
 };
 struct RopeTile {
   int32_t tok_begin, n_rows, delta;

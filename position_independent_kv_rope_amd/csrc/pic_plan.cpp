@@ -359,10 +359,27 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   // ---- decode items (paged plans): every pool chunk once, for all its uses ----
   // A decode step streams each pool chunk from HBM once and serves every request
   // chunk that reads it (up to PIC_DECODE_COLS / G uses per item); each request's fresh
-  // rows (seams and queries) form one more item.
+  // rows (seams and queries) are further items.  Items cover <= PIC_DECODE_RANGE keys;
+  // every (request chunk, range) and (request fresh rows, range) owns one partial slot,
+  // and the slots of a request are contiguous.
   std::vector<DecItem> dec_items;
-  std::vector<int32_t> dec_uses;
+  std::vector<int32_t> dec_uses, dec_slot_base, dec_req_slots;
   if (paged && group <= PIC_DECODE_COLS) {
+    auto n_ranges = [](int32_t len) { return (len + PIC_DECODE_RANGE - 1) / PIC_DECODE_RANGE; };
+    dec_slot_base.assign((size_t)n_chunks + n_req, 0);
+    dec_req_slots.assign((size_t)n_req + 1, 0);
+    int64_t slots = 0;
+    for (int32_t b = 0; b < n_req; ++b) {
+      dec_req_slots[b] = (int32_t)slots;
+      for (int32_t c = req_chunk_ptr[b]; c < req_chunk_ptr[b + 1]; ++c) {
+        dec_slot_base[c] = (int32_t)slots;
+        slots += n_ranges(chunk_lens[c]);
+      }
+      dec_slot_base[n_chunks + b] = (int32_t)slots;
+      slots += n_ranges(req_row_ptr[b + 1] - req_row_ptr[b]);
+      if (slots > kMaxI32 / 2) return PIC_EINVAL;
+    }
+    dec_req_slots[n_req] = (int32_t)slots;
     const int32_t per_item = PIC_DECODE_COLS / group;
     std::vector<std::pair<int32_t, int32_t>> by_id;  // (pool chunk id, global chunk index)
     for (int32_t c = 0; c < n_chunks; ++c)
@@ -373,29 +390,39 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
     for (size_t i = 0; i < by_id.size();) {
       size_t j = i;
       while (j < by_id.size() && by_id[j].first == by_id[i].first) ++j;
+      const int32_t len = chunk_lens[by_id[i].second];
       for (size_t u = i; u < j; u += per_item) {
-        DecItem d{};
-        d.src = by_id[i].first;
-        d.t_begin = 0;
-        d.t_end = chunk_lens[by_id[i].second];
-        d.use_begin = (int32_t)dec_uses.size();
-        d.n_uses = (int32_t)std::min<size_t>(per_item, j - u);
-        for (size_t v = u; v < u + (size_t)d.n_uses; ++v) dec_uses.push_back(by_id[v].second);
-        dec_items.push_back(d);
+        const int32_t use_begin = (int32_t)dec_uses.size();
+        const int32_t nu = (int32_t)std::min<size_t>(per_item, j - u);
+        for (size_t v = u; v < u + (size_t)nu; ++v) dec_uses.push_back(by_id[v].second);
+        for (int32_t r = 0; r < n_ranges(len); ++r) {
+          DecItem d{};
+          d.src = by_id[i].first;
+          d.t_begin = r * PIC_DECODE_RANGE;
+          d.t_end = std::min(len, (r + 1) * PIC_DECODE_RANGE);
+          d.use_begin = use_begin;
+          d.n_uses = nu;
+          d.range = r;
+          dec_items.push_back(d);
+        }
       }
       i = j;
     }
     for (int32_t b = 0; b < n_req; ++b) {
       const int32_t r_b = req_row_ptr[b + 1] - req_row_ptr[b];
       if (r_b == 0) continue;
-      DecItem d{};
-      d.src = -1 - b;
-      d.t_begin = 0;
-      d.t_end = r_b;
-      d.use_begin = (int32_t)dec_uses.size();
-      d.n_uses = 1;
+      const int32_t use_begin = (int32_t)dec_uses.size();
       dec_uses.push_back(-1 - b);
-      dec_items.push_back(d);
+      for (int32_t r = 0; r < n_ranges(r_b); ++r) {
+        DecItem d{};
+        d.src = -1 - b;
+        d.t_begin = r * PIC_DECODE_RANGE;
+        d.t_end = std::min(r_b, (r + 1) * PIC_DECODE_RANGE);
+        d.use_begin = use_begin;
+        d.n_uses = 1;
+        d.range = r;
+        dec_items.push_back(d);
+      }
     }
   }
 
@@ -420,6 +447,8 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   const int64_t o_kblocks = place((int64_t)kblocks.size());
   const int64_t o_dec_items = place((int64_t)dec_items.size() * 8);
   const int64_t o_dec_uses = place((int64_t)dec_uses.size());
+  const int64_t o_dec_slot_base = place((int64_t)dec_slot_base.size());
+  const int64_t o_dec_req_slots = place((int64_t)dec_req_slots.size());
   if (words > kMaxI32) return PIC_EINVAL;
   *plan_words = words;
   if (plan == nullptr) return PIC_OK;
@@ -462,6 +491,9 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   h[PIC_H_O_DEC_ITEMS] = (int32_t)o_dec_items;
   h[PIC_H_N_DEC_USES] = (int32_t)dec_uses.size();
   h[PIC_H_O_DEC_USES] = (int32_t)o_dec_uses;
+  h[PIC_H_N_DEC_SLOTS] = dec_req_slots.empty() ? 0 : dec_req_slots.back();
+  h[PIC_H_O_DEC_SLOT_BASE] = (int32_t)o_dec_slot_base;
+  h[PIC_H_O_DEC_REQ_SLOTS] = (int32_t)o_dec_req_slots;
   if (n_req > 0) std::memcpy(h + o_rcp, req_chunk_ptr, sizeof(int32_t) * (n_req + 1));
   else h[o_rcp] = 0;
   if (!chunk_off.empty()) std::memcpy(h + o_coff, chunk_off.data(), sizeof(int32_t) * chunk_off.size());
@@ -481,6 +513,10 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
     std::memcpy(h + o_dec_items, dec_items.data(), sizeof(DecItem) * dec_items.size());
   if (!dec_uses.empty())
     std::memcpy(h + o_dec_uses, dec_uses.data(), sizeof(int32_t) * dec_uses.size());
+  if (!dec_slot_base.empty())
+    std::memcpy(h + o_dec_slot_base, dec_slot_base.data(), sizeof(int32_t) * dec_slot_base.size());
+  if (!dec_req_slots.empty())
+    std::memcpy(h + o_dec_req_slots, dec_req_slots.data(), sizeof(int32_t) * dec_req_slots.size());
   return PIC_OK;
 }
 

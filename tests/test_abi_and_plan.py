@@ -282,28 +282,42 @@ def check_paged_plan(reqs, ids, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0):
         assert 0 <= b1 <= e1 and 0 <= b2 <= e2
         for i in list(range(b1, e1)) + list(range(b2, e2)):
             assert kb[i][2] <= tiles[tile][5]  # no block starts after the tile's last row
-    # decode items: every request chunk with keys is one use of exactly one item of
-    # its pool chunk (whole chunk, at most PIC_DECODE_COLS / G uses), plus one item per
-    # request with fresh rows
+    # decode items: every (request chunk, PIC_DECODE_RANGE-key range) with keys is one use
+    # of exactly one item of its pool chunk (at most PIC_DECODE_COLS / G uses), every
+    # range of a request's fresh rows is one item of its own; each writes the partial
+    # slot slot_base[chunk or n_chunks + request] + range, and a request's slots form
+    # the contiguous run [req_slots[b], req_slots[b + 1])
     group = h_q // h_kv
+    R = P.PIC_DECODE_RANGE
     items, uses = plan.dec_items.tolist(), plan.dec_uses.tolist()
-    assert plan[P.H_N_DEC_USES] == len(uses)
+    base, rs = plan.dec_slot_base.tolist(), plan.dec_req_slots.tolist()
+    n_chunks = plan[P.H_N_CHUNKS]
+    assert plan[P.H_N_DEC_USES] == len(uses) and len(base) == n_chunks + len(reqs)
     flat_lens = [x for lens in reqs for x in lens]
     flat_ids = [x for c in ids for x in c]
-    seen, fresh = [], []
-    for src, t0, t1, u0, nu, _, _, _ in items:
-        assert 1 <= nu <= P.PIC_DECODE_COLS // group and t0 == 0
+    n_fresh = [int(plan.req_row_ptr[b + 1] - plan.req_row_ptr[b]) for b in range(len(reqs))]
+    seen, fresh, slots = [], [], []
+    for src, t0, t1, u0, nu, r, _, _ in items:
+        assert 1 <= nu <= P.PIC_DECODE_COLS // group and t0 == r * R < t1
         us = uses[u0:u0 + nu]
         if src >= 0:
             for c in us:
-                assert flat_ids[c] == src and flat_lens[c] == t1 > 0
-            seen += us
+                assert flat_ids[c] == src and t1 == min(flat_lens[c], t0 + R)
+                b = segs[c][5]
+                slots.append(base[c] + r)
+                assert rs[b] <= base[c] + r < rs[b + 1]
+            seen += [(c, r) for c in us]
         else:
             b = -1 - src
-            assert us == [src] and t1 == int(plan.req_row_ptr[b + 1] - plan.req_row_ptr[b]) > 0
-            fresh.append(b)
-    assert sorted(seen) == [c for c, L in enumerate(flat_lens) if L > 0]
-    assert fresh == [b for b in range(len(reqs)) if plan.req_row_ptr[b + 1] > plan.req_row_ptr[b]]
+            assert us == [src] and t1 == min(n_fresh[b], t0 + R)
+            fresh.append((b, r))
+            slots.append(base[n_chunks + b] + r)
+            assert rs[b] <= base[n_chunks + b] + r < rs[b + 1]
+    ranges = lambda L: range((L + R - 1) // R)
+    assert sorted(seen) == [(c, r) for c, L in enumerate(flat_lens) for r in ranges(L)]
+    assert sorted(fresh) == [(b, r) for b, L in enumerate(n_fresh) for r in ranges(L)]
+    assert sorted(slots) == list(range(plan[P.H_N_DEC_SLOTS])) and rs[0] == 0
+    assert rs[-1] == plan[P.H_N_DEC_SLOTS] and rs == sorted(rs)
     return plan
 
 
@@ -312,6 +326,8 @@ def test_paged_plan_small():
     # one pool chunk read twice by one request, and by two requests
     check_paged_plan([[16, 3, 16, 64], [64, 16]], [[0, 1, 0, 3], [3, 0]], [7, 0], 8, 8, 2)
     check_paged_plan([[4, 5, 5]], [[0, 1, 2]], [3], 2, 4, 4, pos_base=3)
+    # chunks and fresh rows longer than one decode range, a chunk of exactly one range
+    check_paged_plan([[300, 600, 256], [600, 10]], [[0, 1, 2], [1, 3]], [300, 0], 8, 16, 2)
 
 
 def test_paged_plan_shared_pool_workload():
