@@ -76,11 +76,12 @@ enum { PIC_ROPE_ADJACENT = 0, PIC_ROPE_HALF = 1 };
  * PIC_PLAN_HEADER_WORDS words, then sections at the word offsets the header gives.
  * ---------------------------------------------------------------------------- */
 #define PIC_PLAN_MAGIC 0x31434950 /* "PIC1" */
-#define PIC_PLAN_HEADER_WORDS 40
+#define PIC_PLAN_HEADER_WORDS 48
 #define PIC_ATTN_TILE_M 128 /* query vectors (row, head) per attention tile */
 #define PIC_ROPE_TILE_ROWS 32
 #define PIC_DECODE_COLS 64   /* query columns (use, head) of one decode item */
 #define PIC_DECODE_RANGE 256 /* keys of one decode item (a multiple of 64) */
+#define PIC_DECODE_WG_PER_CU 4 /* decode workgroups resident per compute unit */
 
 enum {
   PIC_H_MAGIC = 0,
@@ -139,7 +140,13 @@ enum {
                          then of each request's fresh rows (range r adds r) */
   PIC_H_O_DEC_REQ_SLOTS, /* paged: [n_req + 1] slots of request b are
                          [ptr[b], ptr[b+1]), every one written by exactly one item */
-  PIC_H_RESERVED6
+  PIC_H_N_DEC_WG,     /* paged: decode workgroups (<= n_cu * PIC_DECODE_WG_PER_CU) */
+  PIC_H_O_DEC_WG_PTR, /* paged: [n_dec_wg + 1] units of workgroup w are
+                         units[ptr[w] .. ptr[w+1]) */
+  PIC_H_O_DEC_UNITS,  /* paged: [n_dec_items * h_kv] unit = item * h_kv + kv head; every
+                         (item, kv head) once, spread over the workgroups by key blocks
+                         (longest first, each to the least loaded workgroup) */
+  PIC_H_RESERVED7
 };
 
 /*
@@ -280,12 +287,14 @@ int pic_selective_attn_paged(const int32_t *plan_host, const int32_t *plan_dev, 
  * the fresh rows), its recomputed rows (k_fresh/v_fresh, the link's fresh buffer) and
  * itself:  out[b, h] = sum_j softmax_j(q_new[b, h] . K_b[j, g] * scale) V_b[j, g].
  * Work is chunk-major: each pool chunk is read once per call for all request chunks
- * that use it (the plan's decode items).  q_new/out: device [n_req][h_q][head_dim];
+ * that use it (the plan's decode items), on a resident grid that walks the plan's
+ * decode units.  q_new/out: device [n_req][h_q][head_dim];
  * k_new/v_new: device [n_req][h_kv][head_dim], RoPE'd at N_b; pool and fresh arguments
- * as pic_selective_attn_paged.  Later decode steps append the generated rows to the
- * fresh buffer through a plan with longer queries.  bf16 only, head_dim in {64, 128},
- * h_q/h_kv <= PIC_DECODE_COLS.  workspace >= pic_decode_workspace_bytes (partials +
- * angle table).  Errors as pic_selective_attn_paged.
+ * as pic_selective_attn_paged, without its size limit (64-bit offsets).  Later decode
+ * steps append the generated rows to the fresh buffer through a plan with longer
+ * queries.  bf16 only, head_dim in {64, 128}, h_q/h_kv <= PIC_DECODE_COLS.
+ * workspace >= pic_decode_workspace_bytes (partials + angle table).  Errors as
+ * pic_selective_attn_paged, without the size cases.
  */
 size_t pic_decode_workspace_bytes(const int32_t *plan_host, int32_t head_dim);
 int pic_decode_attn_paged(const int32_t *plan_host, const int32_t *plan_dev, const void *q_new,

@@ -26,9 +26,11 @@ PIC_ATTN_TILE_M = 128
  H_MAX_TOKENS, H_O_REQ_CHUNK_PTR, H_O_CHUNK_OFF, H_O_REQ_TOK_PTR, H_O_REQ_ROW_PTR, H_O_ROWS,
  H_O_ROW_TOK, H_O_ROPE_TILES, H_O_ATTN_TILES, H_O_ATTN_ITEMS, H_O_MERGE, H_PAGED, H_O_SEGS,
  H_N_KBLOCKS, H_O_KBLOCKS, H_N_DEC_ITEMS, H_O_DEC_ITEMS, H_N_DEC_USES, H_O_DEC_USES,
- H_N_DEC_SLOTS, H_O_DEC_SLOT_BASE, H_O_DEC_REQ_SLOTS) = range(38)
+ H_N_DEC_SLOTS, H_O_DEC_SLOT_BASE, H_O_DEC_REQ_SLOTS, H_N_DEC_WG, H_O_DEC_WG_PTR,
+ H_O_DEC_UNITS) = range(41)
 PIC_DECODE_COLS = 64
 PIC_DECODE_RANGE = 256
+PIC_DECODE_WG_PER_CU = 4
 
 EXPORTED = ("pic_build_index", "pic_rope_delta", "pic_rope_apply", "pic_splice",
             "pic_attn_workspace_bytes",
@@ -191,6 +193,16 @@ class Plan:
     @property
     def dec_req_slots(self):
         return self._sec(H_O_DEC_REQ_SLOTS, self[H_N_REQ] + 1 if self._has_decode() else 0, 1)
+
+    @property
+    def dec_wg_ptr(self):
+        n = self[H_N_DEC_WG] + 1 if self._has_decode() and self[H_N_DEC_WG] > 0 else 0
+        return self._sec(H_O_DEC_WG_PTR, n, 1)
+
+    @property
+    def dec_units(self):
+        n = self[H_N_DEC_ITEMS] * self[H_H_KV] if self._has_decode() else 0
+        return self._sec(H_O_DEC_UNITS, n, 1)
 
     def to_device(self, device="cuda"):
         """Upload the plan (one int32 tensor) and keep it with the host copy."""

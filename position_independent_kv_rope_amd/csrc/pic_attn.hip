@@ -824,7 +824,24 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_paged_kernel(
 
 constexpr int kDecWaves = PIC_DECODE_COLS / 32;  // one 32-column MFMA block per wave
 constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kDecKB = 32;  // keys per staged block: K + V double-buffered in 32 KiB (D = 128)
 
+// Where the keys of one decode unit (item, kv head) live.  Pool units read the chunk
+// through its block table, fresh units the request's recomputed rows; either way the
+// base address excludes the kv head, which sits in the per-lane offsets.
+struct DecSrc {
+  const char *k, *v;      // pool tensors, or the request's first fresh row
+  const int32_t *blocks;  // pool block ids of the chunk (pool units)
+  int t_begin, t_end;     // keys of the unit, relative to the chunk or to the fresh rows
+  int n_blocks;           // kDecKB-key blocks
+  int item, g;
+  bool pool;
+};
+
+// The grid is resident (at most PIC_DECODE_WG_PER_CU workgroups per CU, each with the
+// unit list the planner balanced): a workgroup streams the key blocks of all its units
+// back to back, staging the next block -- possibly the first of its next unit -- while
+// the current one is scored, so the HBM stream does not drain between units.
 template <int D, bool kHalf>
 __device__ __forceinline__ void dec_attn_body(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ pool_k,
@@ -833,22 +850,24 @@ __device__ __forceinline__ void dec_attn_body(
     const __bf16 *__restrict__ v_fresh, const DecItem *__restrict__ items,
     const int32_t *__restrict__ uses, const int32_t *__restrict__ segs,
     const int32_t *__restrict__ req_row_ptr, const int32_t *__restrict__ slot_base,
+    const int32_t *__restrict__ wg_ptr, const int32_t *__restrict__ units,
     const float2 *__restrict__ angles, float *__restrict__ ws_o, float *__restrict__ ws_ml,
-    int h_q, int h_kv, int n_chunks, float scale_log2, int pool_bytes) {
+    int h_q, int h_kv, int n_chunks, float scale_log2, int64_t pool_blocks) {
   constexpr int kRowB = D * 2;
   constexpr int kCPR = D / 8;
-  constexpr int kTileB = kKB * kRowB;
-  constexpr int kRPI = 1024 / kRowB;
-  constexpr int kRounds = kKB / (kRPI * kDecWaves);
+  constexpr int kTileB = kDecKB * kRowB;
+  constexpr int kRPI = 1024 / kRowB;  // rows per direct load (one wave, 16 B a lane)
+  constexpr int kRounds = kDecKB / (kRPI * kDecWaves);
   constexpr int kKS = D / 16;
   constexpr int kDB = D / 32;
   constexpr int kPairs = D / 2;
-  static_assert(kRounds * kRPI * kDecWaves == kKB, "direct loads must tile the block");
-  static_assert(kRPI <= kPoolBlockRows, "one direct load must stay inside a pool block");
+  constexpr int kT = kDecKB / 32;  // 32-key S^T tiles per block
+  static_assert(kDecKB == 32 || kDecKB == 64, "one or two 32-key tiles per block");
+  static_assert(kRounds * kRPI * kDecWaves == kDecKB, "direct loads must tile the block");
+  static_assert(kPoolBlockRows % kRPI == 0, "one direct load stays inside a pool block");
   __shared__ __attribute__((aligned(1024))) char lds[4 * kTileB];  // K0 K1 V0 V1
 
-  const DecItem it = items[blockIdx.x];
-  const int g = blockIdx.y;
+  const int u_begin = wg_ptr[blockIdx.x], u_end = wg_ptr[blockIdx.x + 1];
   const int group = h_q / h_kv;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -856,103 +875,72 @@ __device__ __forceinline__ void dec_attn_body(
   const int grp = lane >> 5;
   const int q16 = lane >> 4;
   const int i16 = lane & 15;
-  const bool pool = it.src >= 0;
+  const int tok_bytes = h_kv * kRowB;
+  const int64_t blk_bytes = (int64_t)kPoolBlockRows * tok_bytes;
 
-  // ---- this lane's query column: (use u, head hh) ----
-  const int col = 32 * wave + n;
-  const int u = col / group, hh = col - u * group;
-  const bool valid = u < it.n_uses;
-  const int use = valid ? uses[it.use_begin + u] : 0;
-  const int req = !valid ? 0 : (pool ? segs[8 * use + 5] : -1 - use);
-  const int seam = (valid && pool) ? segs[8 * use + 2] : 0;
-  const int slot = valid ? slot_base[pool ? use : n_chunks + req] + it.range : 0;
-
-  bf16x8 qop[kKS];
-  {
-    const __bf16 *qp = q + ((int64_t)req * h_q + g * group + hh) * D + 8 * grp;
-    bf16x8 qo[kKS];
-#pragma unroll
-    for (int s = 0; s < kKS; ++s)
-      qo[s] = valid ? *reinterpret_cast<const bf16x8 *>(qp + 16 * s) : bf16x8{};
-    if (pool && valid) {  // into the chunk's local frame: rotate by -delta of this use
-      const float2 *cs = angles + (int64_t)use * kPairs;
-      if constexpr (!kHalf) {
-#pragma unroll
-        for (int s = 0; s < kKS; ++s)
-#pragma unroll
-          for (int j = 0; j < 8; j += 2) {
-            const float2 c = cs[8 * s + 4 * grp + j / 2];
-            const float a = (float)qo[s][j], b = (float)qo[s][j + 1];
-            qop[s][j] = (__bf16)(a * c.x + b * c.y);
-            qop[s][j + 1] = (__bf16)(b * c.x - a * c.y);
-          }
-      } else {
-#pragma unroll
-        for (int s = 0; s < kKS / 2; ++s)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float2 c = cs[16 * s + 8 * grp + j];
-            const float a = (float)qo[s][j], b = (float)qo[s + kKS / 2][j];
-            qop[s][j] = (__bf16)(a * c.x + b * c.y);
-            qop[s + kKS / 2][j] = (__bf16)(b * c.x - a * c.y);
-          }
-      }
+  auto load_src = [&](int ui) {
+    DecSrc sr;
+    const int code = units[ui];
+    sr.item = code / h_kv;
+    sr.g = code - sr.item * h_kv;
+    const DecItem it = items[sr.item];
+    sr.pool = it.src >= 0;
+    sr.t_begin = it.t_begin;
+    sr.t_end = it.t_end;
+    sr.n_blocks = (it.t_end - it.t_begin + kDecKB - 1) / kDecKB;
+    if (sr.pool) {
+      sr.k = reinterpret_cast<const char *>(pool_k);
+      sr.v = reinterpret_cast<const char *>(pool_v);
+      sr.blocks = block_ids + chunk_block_ptr[it.src];
     } else {
-#pragma unroll
-      for (int s = 0; s < kKS; ++s) qop[s] = qo[s];
+      const int64_t row0 = (int64_t)req_row_ptr[-1 - it.src] * tok_bytes;
+      sr.k = reinterpret_cast<const char *>(k_fresh) + row0;
+      sr.v = reinterpret_cast<const char *>(v_fresh) + row0;
+      sr.blocks = nullptr;
     }
-  }
+    return sr;
+  };
 
-  f32x16 acc[kDB];
+  // per-lane offsets of the next block's loads inside a kRPI-row group: row, kv head,
+  // swizzled 16-byte chunk
+  int nk[kRounds], nv[kRounds];
+  auto set_head = [&](int g) {
 #pragma unroll
-  for (int d = 0; d < kDB; ++d)
+    for (int r = 0; r < kRounds; ++r) {
+      const int R = kRPI * (kDecWaves * r + wave) + lane / kCPR;  // row in the block
+      const int pch = lane % kCPR;
+      nk[r] = (lane / kCPR) * tok_bytes + g * kRowB + 16 * (pch ^ swz_k<kCPR>(R));
+      nv[r] = (lane / kCPR) * tok_bytes + g * kRowB + 16 * (pch ^ swz_v<kCPR>(R));
+    }
+  };
+  // Stage block j of sr (K and V) into LDS buffer buf.  Each direct load gets a
+  // resource that starts at its first row and ends after the rows that are keys of the
+  // unit, so the range check alone zeroes rows past t_end (slack rows of a chunk's last
+  // pool block included); the scalar offset stays 0.
+  auto issue = [&](const DecSrc &sr, int j, int buf, const int (&ok)[kRounds],
+                   const int (&ov)[kRounds]) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[d][j] = 0.f;
-  float m_run = kNegInf, l_lane = 0.f;
-
-  // ---- staging: pool rows through the block table, or the request's fresh rows ----
-  const int n_keys = it.t_end - it.t_begin;
-  const int n_blocks = (n_keys + kKB - 1) / kKB;
-  const int tok_bytes = h_kv * D * 2;
-  const int blk_bytes = kPoolBlockRows * tok_bytes;
-  const int32_t *bl = pool ? block_ids + chunk_block_ptr[it.src] : nullptr;
-  const int fresh_b = pool ? 0 : -1 - it.src;
-  const int64_t fresh_off = pool ? 0 : ((int64_t)req_row_ptr[fresh_b] * h_kv + g) * D;
-  int voff_k[kRounds], voff_v[kRounds], row_r[kRounds];
-#pragma unroll
-  for (int r = 0; r < kRounds; ++r) {
-    const int R = kRPI * (kDecWaves * r + wave) + lane / kCPR;
-    const int pch = lane % kCPR;
-    row_r[r] = R;
-    const int inblk = pool ? (R % kPoolBlockRows) * tok_bytes + g * kRowB : R * tok_bytes;
-    voff_k[r] = inblk + 16 * (pch ^ swz_k<kCPR>(R));
-    voff_v[r] = inblk + 16 * (pch ^ swz_v<kCPR>(R));
-  }
-  // block j of K (is_v false) or V into LDS buffer buf; rows past the item's keys read
-  // as zero (the buffer range), slack rows of a chunk's last pool block included
-  auto issue = [&](int j, bool is_v, int buf) {
-    const int t0 = it.t_begin + j * kKB;
-    if (pool) {
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)(is_v ? pool_v : pool_k), 0, pool_bytes, 0x00020000);
-#pragma unroll
-      for (int r = 0; r < kRounds; ++r) {
-        const int t = t0 + kRPI * (kDecWaves * r + wave);  // first row of this load
-        const int soff = t < it.t_end ? bl[t / kPoolBlockRows] * blk_bytes : pool_bytes;
-        const int voff = t0 + row_r[r] < it.t_end ? (is_v ? voff_v[r] : voff_k[r]) : pool_bytes;
-        const int dst = buf * kTileB + (kDecWaves * r + wave) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16, voff, soff, 0, 0);
+    for (int r = 0; r < kRounds; ++r) {
+      const int t = sr.t_begin + j * kDecKB + kRPI * (kDecWaves * r + wave);  // first row
+      int rows = min(max(sr.t_end - t, 0), kRPI);
+      int64_t off = 0;
+      if (sr.pool) {  // a block id outside the pool reads zeros
+        const int bid = rows > 0 ? sr.blocks[t / kPoolBlockRows] : -1;
+        if (bid < 0 || bid >= pool_blocks)
+          rows = 0;
+        else
+          off = bid * blk_bytes + (int64_t)(t % kPoolBlockRows) * tok_bytes;
+      } else {
+        off = (int64_t)t * tok_bytes;
       }
-    } else {
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)((is_v ? v_fresh : k_fresh) + fresh_off), 0, it.t_end * tok_bytes, 0x00020000);
-      const int soff = t0 * tok_bytes;
-#pragma unroll
-      for (int r = 0; r < kRounds; ++r) {
-        const int dst = buf * kTileB + (kDecWaves * r + wave) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16,
-                                                 is_v ? voff_v[r] : voff_k[r], soff, 0, 0);
-      }
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void *)(sr.k + off), 0, rows * tok_bytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void *)(sr.v + off), 0, rows * tok_bytes, 0x00020000);
+      const int dst = buf * kTileB + (kDecWaves * r + wave) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(lds + dst), 16, ok[r], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(lds + 2 * kTileB + dst), 16,
+                                               ov[r], 0, 0, 0);
     }
   };
 
@@ -973,131 +961,215 @@ __device__ __forceinline__ void dec_attn_body(
                 8 * (i16 & 1);
   }
 
-  issue(0, false, 0);
-  issue(0, true, 2);
-  for (int j = 0; j < n_blocks; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_blocks) {
-      issue(j + 1, false, buf ^ 1);
-      issue(j + 1, true, 2 + (buf ^ 1));
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kRounds) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    asm volatile("s_barrier" ::: "memory");
-    const char *Kb = lds + buf * kTileB;
-    const char *Vb = lds + (2 + buf) * kTileB;
-    f32x16 sc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) sc[t][jj] = 0.f;
-#pragma unroll
-      for (int s = 0; s < kKS; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Kb + koff[s] + t * 32 * kRowB);
-        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], sc[t], 0, 0, 0);
+  if (u_begin >= u_end) return;
+  DecSrc cur = load_src(u_begin);
+  DecSrc nxt = cur;  // unit of the next block to stage
+  int n_ui = u_begin, n_j = 0;
+  set_head(cur.g);
+  issue(nxt, 0, 0, nk, nv);
+  int blk = 0;  // blocks consumed so far (selects the LDS buffer)
+  auto advance = [&]() {  // step (n_ui, n_j) to the next block to stage
+    if (++n_j == nxt.n_blocks) {
+      n_j = 0;
+      if (++n_ui < u_end) {
+        nxt = load_src(n_ui);
+        set_head(nxt.g);
       }
     }
-    const int t0 = it.t_begin + j * kKB;
-    if (t0 < seam || t0 + kKB > it.t_end || !valid) {  // seam rows, rows past the keys
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const int tk = t0 + perm_key(t, 8 * (jj >> 2) + 4 * grp + (jj & 3));
-          if (tk < seam || tk >= it.t_end || !valid) sc[t][jj] = kNegInf;
-        }
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, sc[t][jj]);
-    mx = pair_max(mx) * scale_log2;
-    if (mx > m_run) {  // exact running max (decode is bound by HBM, not by this VALU)
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
-      m_run = mx;
-      l_lane *= alpha;
-#pragma unroll
-      for (int d = 0; d < kDB; ++d) acc[d] *= alpha;
-    }
-    const float base = m_run == kNegInf ? 0.f : m_run;
-    bf16x8 pb[4];
-    const bf16x2v ones = {(__bf16)1.f, (__bf16)1.f};
-    float ps = 0.f;
-#pragma unroll
-    for (int qq = 0; qq < 16; ++qq) {
-      const int t = qq >> 3, jj = 2 * (qq & 7);
-      bf16x2v pr;
-      pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][jj], scale_log2, -base));
-      pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][jj + 1], scale_log2, -base));
-      pb[2 * t + (jj >> 3)][jj & 7] = pr[0];
-      pb[2 * t + (jj >> 3)][(jj & 7) + 1] = pr[1];
-      ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
-    }
-    l_lane += ps;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int d = 0; d < kDB; ++d) {
-        const char *vr = Vb + voff[d] + c * 16 * kRowB;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vr);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 4 * kRowB));
-        bf16x8 a;
-        __builtin_memcpy(&a, &lo, 8);
-        __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &hi, 8);
-        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[d], 0, 0, 0);
-      }
-    asm volatile("s_barrier" ::: "memory");  // buffer buf is refilled next
-  }
+  };
+  advance();
 
-  // ---- partial (m, l, O) of this (use, kv head, head) ----
-  const float l_row = pair_sum(l_lane);
-  if (!valid) return;
-  const int64_t at = ((int64_t)slot * h_kv + g) * group + hh;
-  float *wo = ws_o + at * D + 4 * grp;
+  for (int ui = u_begin; ui < u_end; ++ui) {
+    if (ui > u_begin) cur = load_src(ui);
+    const DecItem it = items[cur.item];
+    const int g = cur.g;
+    const bool pool = cur.pool;
+    // ---- this lane's query column: (use u, head hh) ----
+    const int col = 32 * wave + n;
+    const int u = col / group, hh = col - u * group;
+    const bool valid = u < it.n_uses;
+    const bool active = 32 * wave < it.n_uses * group;  // wave-uniform
+    const int use = valid ? uses[it.use_begin + u] : 0;
+    const int req = !valid ? 0 : (pool ? segs[8 * use + 5] : -1 - use);
+    const int seam = (valid && pool) ? segs[8 * use + 2] : 0;
+    const int slot = valid ? slot_base[pool ? use : n_chunks + req] + it.range : 0;
+
+    bf16x8 qop[kKS];
+    {
+      const __bf16 *qp = q + ((int64_t)req * h_q + g * group + hh) * D + 8 * grp;
+      bf16x8 qo[kKS];
 #pragma unroll
-  for (int d = 0; d < kDB; ++d)
+      for (int s = 0; s < kKS; ++s)
+        qo[s] = valid ? *reinterpret_cast<const bf16x8 *>(qp + 16 * s) : bf16x8{};
+      if (pool && valid) {  // into the chunk's local frame: rotate by -delta of this use
+        const float2 *cs = angles + (int64_t)use * kPairs;
+        if constexpr (!kHalf) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      f32x4 o;
+          for (int s = 0; s < kKS; ++s)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) o[b] = acc[d][4 * a + b];
-      *reinterpret_cast<f32x4 *>(wo + 32 * d + 8 * a) = o;
+            for (int j = 0; j < 8; j += 2) {
+              const float2 c = cs[8 * s + 4 * grp + j / 2];
+              const float a = (float)qo[s][j], b = (float)qo[s][j + 1];
+              qop[s][j] = (__bf16)(a * c.x + b * c.y);
+              qop[s][j + 1] = (__bf16)(b * c.x - a * c.y);
+            }
+        } else {
+#pragma unroll
+          for (int s = 0; s < kKS / 2; ++s)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float2 c = cs[16 * s + 8 * grp + j];
+              const float a = (float)qo[s][j], b = (float)qo[s + kKS / 2][j];
+              qop[s][j] = (__bf16)(a * c.x + b * c.y);
+              qop[s + kKS / 2][j] = (__bf16)(b * c.x - a * c.y);
+            }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < kKS; ++s) qop[s] = qo[s];
+      }
     }
-  if (grp == 0) {
-    ws_ml[at * 2 + 0] = m_run;
-    ws_ml[at * 2 + 1] = l_row;
+
+    f32x16 acc[kDB];
+#pragma unroll
+    for (int d = 0; d < kDB; ++d)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[d][j] = 0.f;
+    float m_run = kNegInf, l_lane = 0.f;
+
+    for (int j = 0; j < cur.n_blocks; ++j, ++blk) {
+      const int buf = blk & 1;
+      if (n_ui < u_end) {  // stage the next block while this one is scored
+        issue(nxt, n_j, buf ^ 1, nk, nv);
+        advance();
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kRounds) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      asm volatile("s_barrier" ::: "memory");
+      if (active) {  // a wave whose 32 columns are all past the item's uses only stages
+        const char *Kb = lds + buf * kTileB;
+        const char *Vb = lds + (2 + buf) * kTileB;
+        f32x16 sc[kT];
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) sc[t][jj] = 0.f;
+#pragma unroll
+          for (int s = 0; s < kKS; ++s) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Kb + koff[s] + t * 32 * kRowB);
+            sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[s], sc[t], 0, 0, 0);
+          }
+        }
+        const int t0 = cur.t_begin + j * kDecKB;
+        if (t0 < seam || t0 + kDecKB > cur.t_end || !valid) {  // seam rows, rows past the keys
+#pragma unroll
+          for (int t = 0; t < kT; ++t)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+              const int tk = t0 + perm_key(t, 8 * (jj >> 2) + 4 * grp + (jj & 3));
+              if (tk < seam || tk >= cur.t_end || !valid) sc[t][jj] = kNegInf;
+            }
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int t = 0; t < kT; ++t)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, sc[t][jj]);
+        mx = pair_max(mx) * scale_log2;
+        if (mx > m_run) {  // exact running max (decode is bound by HBM, not by this VALU)
+          const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
+          m_run = mx;
+          l_lane *= alpha;
+#pragma unroll
+          for (int d = 0; d < kDB; ++d) acc[d] *= alpha;
+        }
+        const float base = m_run == kNegInf ? 0.f : m_run;
+        bf16x8 pb[2 * kT];
+        const bf16x2v ones = {(__bf16)1.f, (__bf16)1.f};
+        float ps = 0.f;
+#pragma unroll
+        for (int qq = 0; qq < 8 * kT; ++qq) {
+          const int t = qq >> 3, jj = 2 * (qq & 7);
+          bf16x2v pr;
+          pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][jj], scale_log2, -base));
+          pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[t][jj + 1], scale_log2, -base));
+          pb[2 * t + (jj >> 3)][jj & 7] = pr[0];
+          pb[2 * t + (jj >> 3)][(jj & 7) + 1] = pr[1];
+          ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
+        }
+        l_lane += ps;
+#pragma unroll
+        for (int c = 0; c < 2 * kT; ++c)
+#pragma unroll
+          for (int d = 0; d < kDB; ++d) {
+            const char *vr = Vb + voff[d] + c * 16 * kRowB;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vr);
+            const s16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 4 * kRowB));
+            bf16x8 a;
+            __builtin_memcpy(&a, &lo, 8);
+            __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &hi, 8);
+            acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[d], 0, 0, 0);
+          }
+      }
+      asm volatile("s_barrier" ::: "memory");  // buffer buf is refilled next
+    }
+
+    // ---- partial (m, l, O) of this (use, kv head, head) ----
+    if (active) {
+      const float l_row = pair_sum(l_lane);
+      if (valid) {
+        const int64_t at = ((int64_t)slot * h_kv + g) * group + hh;
+        float *wo = ws_o + at * D + 4 * grp;
+#pragma unroll
+        for (int d = 0; d < kDB; ++d)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            f32x4 o;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) o[b] = acc[d][4 * a + b];
+            *reinterpret_cast<f32x4 *>(wo + 32 * d + 8 * a) = o;
+          }
+        if (grp == 0) {
+          ws_ml[at * 2 + 0] = m_run;
+          ws_ml[at * 2 + 1] = l_row;
+        }
+      }
+    }
   }
 }
 
 template <int D, bool kHalf>
-__global__ __launch_bounds__(kDecThreads) void dec_attn_kernel(
+__global__ __launch_bounds__(kDecThreads, 2) void dec_attn_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ pool_k,
     const __bf16 *__restrict__ pool_v, const int32_t *__restrict__ chunk_block_ptr,
     const int32_t *__restrict__ block_ids, const __bf16 *__restrict__ k_fresh,
     const __bf16 *__restrict__ v_fresh, const DecItem *__restrict__ items,
     const int32_t *__restrict__ uses, const int32_t *__restrict__ segs,
     const int32_t *__restrict__ req_row_ptr, const int32_t *__restrict__ slot_base,
+    const int32_t *__restrict__ wg_ptr, const int32_t *__restrict__ units,
     const float2 *__restrict__ angles, float *__restrict__ ws_o, float *__restrict__ ws_ml,
-    int h_q, int h_kv, int n_chunks, float scale_log2, int pool_bytes) {
+    int h_q, int h_kv, int n_chunks, float scale_log2, int64_t pool_blocks) {
   dec_attn_body<D, kHalf>(q, pool_k, pool_v, chunk_block_ptr, block_ids, k_fresh, v_fresh,
-                          items, uses, segs, req_row_ptr, slot_base, angles, ws_o, ws_ml, h_q,
-                          h_kv, n_chunks, scale_log2, pool_bytes);
+                          items, uses, segs, req_row_ptr, slot_base, wg_ptr, units, angles,
+                          ws_o, ws_ml, h_q, h_kv, n_chunks, scale_log2, pool_blocks);
 }
 
-// One workgroup per (request, query head): 8 groups of D/4 lanes fold disjoint subsets
-// of the request's partial slots (online log-sum-exp, 4 dims per lane), group 0 also
-// the new token (score q . k_new, weight v_new); the 8 results are combined in LDS.
-constexpr int kDecMergeGroups = 8;
+// One workgroup per (request, query head): groups of D/4 lanes fold disjoint subsets
+// of the request's partial slots (online log-sum-exp, 4 dims per lane, two slots'
+// loads in flight per group), group 0 also the new token (score q . k_new, weight
+// v_new); the group results are combined in LDS.
+constexpr int kDecMergeThreads = 1024;
 
 template <int D>
-__global__ __launch_bounds__(kDecMergeGroups * (D / 4)) void dec_merge_kernel(
+__global__ __launch_bounds__(kDecMergeThreads) void dec_merge_kernel(
     __bf16 *__restrict__ out, const __bf16 *__restrict__ q, const __bf16 *__restrict__ k_new,
     const __bf16 *__restrict__ v_new, const int32_t *__restrict__ req_slots,
     const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int h_q, int h_kv,
     float scale_log2) {
   constexpr int kC = D / 4;
+  constexpr int kDecMergeGroups = kDecMergeThreads / kC;
   __shared__ float part_m[kDecMergeGroups][kC], part_l[kDecMergeGroups][kC];
   __shared__ f32x4 part_o[kDecMergeGroups][kC];
   const int b = blockIdx.x / h_q, h = blockIdx.x - b * h_q;
@@ -1135,9 +1207,17 @@ __global__ __launch_bounds__(kDecMergeGroups * (D / 4)) void dec_merge_kernel(
     den += w * ls;
     num += w * os;
   };
-  for (int sl = req_slots[b] + gi; sl < req_slots[b + 1]; sl += kDecMergeGroups) {
-    const int64_t at = ((int64_t)sl * h_kv + g) * group + hh;
-    fold(ws_ml[at * 2], ws_ml[at * 2 + 1], *reinterpret_cast<const f32x4 *>(ws_o + at * D + 4 * c4));
+  const int s_end = req_slots[b + 1];
+  for (int sl = req_slots[b] + gi; sl < s_end; sl += 2 * kDecMergeGroups) {
+    const int sl2 = sl + kDecMergeGroups < s_end ? sl + kDecMergeGroups : sl;
+    const int64_t a1 = ((int64_t)sl * h_kv + g) * group + hh;
+    const int64_t a2 = ((int64_t)sl2 * h_kv + g) * group + hh;
+    const float2 ml1 = *reinterpret_cast<const float2 *>(ws_ml + a1 * 2);
+    const float2 ml2 = *reinterpret_cast<const float2 *>(ws_ml + a2 * 2);
+    const f32x4 o1 = *reinterpret_cast<const f32x4 *>(ws_o + a1 * D + 4 * c4);
+    const f32x4 o2 = *reinterpret_cast<const f32x4 *>(ws_o + a2 * D + 4 * c4);
+    fold(ml1.x, ml1.y, o1);
+    if (sl2 != sl) fold(ml2.x, ml2.y, o2);
   }
   part_m[gi][c4] = mmax;
   part_l[gi][c4] = den;
@@ -1460,7 +1540,7 @@ template <int D, bool kHalf>
 int launch_decode(const PlanHeader &h, const int32_t *plan_dev, const void *q, const void *k_new,
                   const void *v_new, const void *pool_k, const void *pool_v, const int32_t *cbp,
                   const int32_t *bids, const void *kf, const void *vf, void *out, double rope_base,
-                  float scale, void *workspace, int pool_bytes, hipStream_t s) {
+                  float scale, void *workspace, int64_t pool_blocks, hipStream_t s) {
   const int32_t *segs = plan_dev + h[PIC_H_O_SEGS];
   const DecItem *items = reinterpret_cast<const DecItem *>(plan_dev + h[PIC_H_O_DEC_ITEMS]);
   const int32_t *uses = plan_dev + h[PIC_H_O_DEC_USES];
@@ -1480,18 +1560,18 @@ int launch_decode(const PlanHeader &h, const int32_t *plan_dev, const void *q, c
     PIC_LAUNCH_CHECK();
   }
   const float scale_log2 = scale * kLog2e;
-  if (h[PIC_H_N_DEC_ITEMS] > 0) {
-    hipLaunchKernelGGL((dec_attn_kernel<D, kHalf>),
-                       dim3(h[PIC_H_N_DEC_ITEMS], h[PIC_H_H_KV]), dim3(kDecThreads), 0, s,
-                       static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(pool_k),
+  if (h[PIC_H_N_DEC_WG] > 0) {
+    hipLaunchKernelGGL((dec_attn_kernel<D, kHalf>), dim3(h[PIC_H_N_DEC_WG]), dim3(kDecThreads),
+                       0, s, static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(pool_k),
                        static_cast<const __bf16 *>(pool_v), cbp, bids,
                        static_cast<const __bf16 *>(kf), static_cast<const __bf16 *>(vf), items,
-                       uses, segs, rrp, slot_base, angles, ws_o, ws_ml, h[PIC_H_H_Q],
-                       h[PIC_H_H_KV], n_chunks, scale_log2, pool_bytes);
+                       uses, segs, rrp, slot_base, plan_dev + h[PIC_H_O_DEC_WG_PTR],
+                       plan_dev + h[PIC_H_O_DEC_UNITS], angles, ws_o, ws_ml, h[PIC_H_H_Q],
+                       h[PIC_H_H_KV], n_chunks, scale_log2, pool_blocks);
     PIC_LAUNCH_CHECK();
   }
   hipLaunchKernelGGL((dec_merge_kernel<D>), dim3(h[PIC_H_N_REQ] * h[PIC_H_H_Q]),
-                     dim3(kDecMergeGroups * (D / 4)), 0, s, static_cast<__bf16 *>(out),
+                     dim3(kDecMergeThreads), 0, s, static_cast<__bf16 *>(out),
                      static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k_new),
                      static_cast<const __bf16 *>(v_new), req_slots, ws_o, ws_ml, h[PIC_H_H_Q],
                      h[PIC_H_H_KV], scale_log2);
@@ -1527,10 +1607,6 @@ extern "C" int pic_decode_attn_paged(
   if (dtype != PIC_BF16 || block_size != kPoolBlockRows) return PIC_EUNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PIC_EUNSUPPORTED;
   if (h[PIC_H_H_Q] / h[PIC_H_H_KV] > PIC_DECODE_COLS) return PIC_EUNSUPPORTED;
-  const int64_t tok_bytes = (int64_t)h[PIC_H_H_KV] * head_dim * 2;
-  const int64_t pool_bytes = pool_blocks * kPoolBlockRows * tok_bytes;
-  if (pool_bytes > 0x7fff0000LL || (int64_t)h[PIC_H_N_ROWS] * tok_bytes > 0x7fff0000LL)
-    return PIC_EUNSUPPORTED;
   const int32_t *segs_h = plan_host + h[PIC_H_O_SEGS];
   for (int32_t c = 0; c < h[PIC_H_N_CHUNKS]; ++c)
     if (segs_h[8 * c + 3] >= n_pool_chunks) return PIC_EINVAL;
@@ -1545,7 +1621,7 @@ extern "C" int pic_decode_attn_paged(
 #define PIC_DEC(D_, H_)                                                                     \
   return launch_decode<D_, H_>(h, plan_dev, q_new, k_new, v_new, pool_k, pool_v,            \
                                chunk_block_ptr, block_ids, k_fresh, v_fresh, out, rope_base, \
-                               scale, workspace, (int)pool_bytes, s)
+                               scale, workspace, pool_blocks, s)
   if (head_dim == 128) {
     if (half) PIC_DEC(128, true);
     PIC_DEC(128, false);

@@ -46,6 +46,7 @@ static_assert(sizeof(AttnItem) == 32, "plan record size");
 static_assert(sizeof(MergeEntry) == 16, "plan record size");
 static_assert(sizeof(RopeTile) == 16, "plan record size");
 static_assert(sizeof(DecItem) == 32, "plan record size");
+static_assert(PIC_H_RESERVED7 < PIC_PLAN_HEADER_WORDS, "header fields fit the header");
 
 inline size_t dtype_size(int32_t dt) { return dt == PIC_BF16 ? 2 : (dt == PIC_F32 ? 4 : 0); }
 

@@ -17,6 +17,7 @@
 #include <cstring>
 #include <numeric>
 #include <unordered_map>
+#include <queue>
 #include <vector>
 
 #include "pic_internal.h"
@@ -363,7 +364,7 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   // every (request chunk, range) and (request fresh rows, range) owns one partial slot,
   // and the slots of a request are contiguous.
   std::vector<DecItem> dec_items;
-  std::vector<int32_t> dec_uses, dec_slot_base, dec_req_slots;
+  std::vector<int32_t> dec_uses, dec_slot_base, dec_req_slots, dec_wg_ptr, dec_units;
   if (paged && group <= PIC_DECODE_COLS) {
     auto n_ranges = [](int32_t len) { return (len + PIC_DECODE_RANGE - 1) / PIC_DECODE_RANGE; };
     dec_slot_base.assign((size_t)n_chunks + n_req, 0);
@@ -424,6 +425,37 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
         dec_items.push_back(d);
       }
     }
+    // Units (item, kv head) onto a resident grid: longest first, each to the workgroup
+    // with the fewest key blocks so far (ties: lowest index), so that the workgroups
+    // stream about equal bytes and drain together.
+    const int64_t n_units = (int64_t)dec_items.size() * h_kv;
+    if (n_units > kMaxI32 / 2) return PIC_EINVAL;
+    const int32_t n_wg = (int32_t)std::min<int64_t>(n_units, (int64_t)n_cu * PIC_DECODE_WG_PER_CU);
+    std::vector<std::pair<int32_t, int32_t>> cost;  // (key blocks + 1, unit)
+    cost.reserve((size_t)n_units);
+    for (size_t i = 0; i < dec_items.size(); ++i) {
+      const int32_t nb = (dec_items[i].t_end - dec_items[i].t_begin + 31) / 32 + 1;
+      for (int32_t g = 0; g < h_kv; ++g) cost.push_back({nb, (int32_t)(i * h_kv + g)});
+    }
+    std::stable_sort(cost.begin(), cost.end(),
+                     [](const std::pair<int32_t, int32_t> &a,
+                        const std::pair<int32_t, int32_t> &b) { return a.first > b.first; });
+    using Load = std::pair<int64_t, int32_t>;  // (blocks assigned, workgroup)
+    std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+    for (int32_t w = 0; w < n_wg; ++w) heap.push({0, w});
+    std::vector<std::vector<int32_t>> per_wg((size_t)n_wg);
+    for (const auto &cu : cost) {
+      Load l = heap.top();
+      heap.pop();
+      per_wg[l.second].push_back(cu.second);
+      heap.push({l.first + cu.first, l.second});
+    }
+    dec_wg_ptr.assign((size_t)n_wg + 1, 0);
+    dec_units.reserve((size_t)n_units);
+    for (int32_t w = 0; w < n_wg; ++w) {
+      dec_units.insert(dec_units.end(), per_wg[w].begin(), per_wg[w].end());
+      dec_wg_ptr[w + 1] = (int32_t)dec_units.size();
+    }
   }
 
   // ---- layout of the plan ----
@@ -449,6 +481,8 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   const int64_t o_dec_uses = place((int64_t)dec_uses.size());
   const int64_t o_dec_slot_base = place((int64_t)dec_slot_base.size());
   const int64_t o_dec_req_slots = place((int64_t)dec_req_slots.size());
+  const int64_t o_dec_wg_ptr = place((int64_t)dec_wg_ptr.size());
+  const int64_t o_dec_units = place((int64_t)dec_units.size());
   if (words > kMaxI32) return PIC_EINVAL;
   *plan_words = words;
   if (plan == nullptr) return PIC_OK;
@@ -494,6 +528,9 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   h[PIC_H_N_DEC_SLOTS] = dec_req_slots.empty() ? 0 : dec_req_slots.back();
   h[PIC_H_O_DEC_SLOT_BASE] = (int32_t)o_dec_slot_base;
   h[PIC_H_O_DEC_REQ_SLOTS] = (int32_t)o_dec_req_slots;
+  h[PIC_H_N_DEC_WG] = dec_wg_ptr.empty() ? 0 : (int32_t)dec_wg_ptr.size() - 1;
+  h[PIC_H_O_DEC_WG_PTR] = (int32_t)o_dec_wg_ptr;
+  h[PIC_H_O_DEC_UNITS] = (int32_t)o_dec_units;
   if (n_req > 0) std::memcpy(h + o_rcp, req_chunk_ptr, sizeof(int32_t) * (n_req + 1));
   else h[o_rcp] = 0;
   if (!chunk_off.empty()) std::memcpy(h + o_coff, chunk_off.data(), sizeof(int32_t) * chunk_off.size());
@@ -517,6 +554,10 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
     std::memcpy(h + o_dec_slot_base, dec_slot_base.data(), sizeof(int32_t) * dec_slot_base.size());
   if (!dec_req_slots.empty())
     std::memcpy(h + o_dec_req_slots, dec_req_slots.data(), sizeof(int32_t) * dec_req_slots.size());
+  if (!dec_wg_ptr.empty())
+    std::memcpy(h + o_dec_wg_ptr, dec_wg_ptr.data(), sizeof(int32_t) * dec_wg_ptr.size());
+  if (!dec_units.empty())
+    std::memcpy(h + o_dec_units, dec_units.data(), sizeof(int32_t) * dec_units.size());
   return PIC_OK;
 }
 

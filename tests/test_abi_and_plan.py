@@ -318,6 +318,20 @@ def check_paged_plan(reqs, ids, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0):
     assert sorted(fresh) == [(b, r) for b, L in enumerate(n_fresh) for r in ranges(L)]
     assert sorted(slots) == list(range(plan[P.H_N_DEC_SLOTS])) and rs[0] == 0
     assert rs[-1] == plan[P.H_N_DEC_SLOTS] and rs == sorted(rs)
+    # decode schedule: every (item, kv head) unit on exactly one workgroup of a grid of
+    # min(units, n_cu * PIC_DECODE_WG_PER_CU), no workgroup idle, and the key-block loads
+    # balanced to within one unit (greedy longest-first)
+    n_units = len(items) * h_kv
+    wp, un = plan.dec_wg_ptr.tolist(), plan.dec_units.tolist()
+    n_wg = plan[P.H_N_DEC_WG]
+    assert n_wg == min(n_units, (n_cu if n_cu > 0 else 256) * P.PIC_DECODE_WG_PER_CU)
+    assert sorted(un) == list(range(n_units))
+    if n_units:
+        assert wp[0] == 0 and wp[-1] == n_units and len(wp) == n_wg + 1
+        assert all(wp[w] < wp[w + 1] for w in range(n_wg))
+        cost = [(items[u // h_kv][2] - items[u // h_kv][1] + 31) // 32 + 1 for u in range(n_units)]
+        loads = [sum(cost[u] for u in un[wp[w]:wp[w + 1]]) for w in range(n_wg)]
+        assert max(loads) - min(loads) <= max(cost)
     return plan
 
 
