@@ -383,7 +383,10 @@ def bench_decode(args, wl):
                      "algorithmic_bytes": dec_bytes,
                      "per_request_streaming_bytes": per_request_bytes},
         "kernels": {"decode_attn": {"ms": round(t_dec, 4), "GB_s": round(gbs, 1),
-                                    "items": plan[P.H_N_DEC_ITEMS], "uses": plan[P.H_N_DEC_USES]}},
+                                    "items": plan[P.H_N_DEC_ITEMS], "uses": plan[P.H_N_DEC_USES],
+                                    "pieces": plan[P.H_N_DEC_PIECES],
+                                    "workgroups": plan[P.H_N_DEC_WG],
+                                    "records": plan[P.H_N_DEC_RECS]}},
     }
     if not args.no_cpu_baseline:
         # the oracle's decode of request 0: pool gather, rotation, splice, attention

@@ -80,7 +80,7 @@ enum { PIC_ROPE_ADJACENT = 0, PIC_ROPE_HALF = 1 };
 #define PIC_ATTN_TILE_M 128 /* query vectors (row, head) per attention tile */
 #define PIC_ROPE_TILE_ROWS 32
 #define PIC_DECODE_COLS 64   /* query columns (use, head) of one decode item */
-#define PIC_DECODE_RANGE 256 /* keys of one decode item (a multiple of 64) */
+#define PIC_DECODE_BLOCK 32    /* keys per decode block (the unit the grid is split in) */
 #define PIC_DECODE_WG_PER_CU 4 /* decode workgroups resident per compute unit */
 
 enum {
@@ -124,28 +124,28 @@ enum {
                          request's fresh rows), first local key (t0, or fresh row offset),
                          position of the first key, 0; per request the fresh blocks
                          come first, then the pool blocks in position order */
-  PIC_H_N_DEC_ITEMS,  /* paged: decode work items (0 when h_q/h_kv > PIC_DECODE_COLS) */
-  PIC_H_O_DEC_ITEMS,  /* paged: [n_dec_items][8] source (pool chunk id >= 0, or -1-b for
-                         the fresh rows of request b), first key, end key (a range of
-                         <= PIC_DECODE_RANGE keys of the chunk or of the fresh rows), first
-                         use, use count, range index r, 0, 0; items of one pool chunk
-                         are adjacent */
+  PIC_H_N_DEC_ITEMS,  /* paged: decode items (0 when h_q/h_kv > PIC_DECODE_COLS) */
+  PIC_H_O_DEC_ITEMS,  /* paged: [n_dec_items][4] source (pool chunk id >= 0, or -1-b for
+                         the fresh rows of request b), key count, first use, use count;
+                         items of one pool chunk are adjacent */
   PIC_H_N_DEC_USES,
   PIC_H_O_DEC_USES,   /* paged: [n_dec_uses] per use, the global chunk index c reading the
                          item's pool chunk (or -1-b for fresh rows); at most
                          PIC_DECODE_COLS / (h_q/h_kv) uses per item */
-  PIC_H_N_DEC_SLOTS,  /* paged: decode partial slots (one per key range of each request
-                         chunk and of each request's fresh rows) */
-  PIC_H_O_DEC_SLOT_BASE, /* paged: [n_chunks + n_req] first slot of each request chunk,
-                         then of each request's fresh rows (range r adds r) */
-  PIC_H_O_DEC_REQ_SLOTS, /* paged: [n_req + 1] slots of request b are
-                         [ptr[b], ptr[b+1]), every one written by exactly one item */
-  PIC_H_N_DEC_WG,     /* paged: decode workgroups (<= n_cu * PIC_DECODE_WG_PER_CU) */
-  PIC_H_O_DEC_WG_PTR, /* paged: [n_dec_wg + 1] units of workgroup w are
-                         units[ptr[w] .. ptr[w+1]) */
-  PIC_H_O_DEC_UNITS,  /* paged: [n_dec_items * h_kv] unit = item * h_kv + kv head; every
-                         (item, kv head) once, spread over the workgroups by key blocks
-                         (longest first, each to the least loaded workgroup) */
+  PIC_H_N_DEC_RECS,   /* paged: decode partial records, each (m, l, O) of the G query
+                         heads of one (piece, use) */
+  PIC_H_O_DEC_REC_PTR,/* paged: [n_req * h_kv + 1] records of request b and kv head g are
+                         [ptr[b*h_kv+g], ptr[b*h_kv+g+1]) */
+  PIC_H_N_DEC_PIECES, /* paged: decode pieces */
+  PIC_H_O_DEC_PIECES, /* paged: [n_dec_pieces][8] item, kv head, first key, end key, offset
+                         of its records in piece_recs, 0, 0, 0.  The (item, kv head) units,
+                         in item order, are cut into PIC_DECODE_BLOCK-key blocks and the
+                         block sequence into n_dec_wg equal runs; a piece is one unit's part
+                         of one run */
+  PIC_H_O_DEC_PIECE_RECS, /* paged: per piece, the record of each of its item's uses */
+  PIC_H_N_DEC_WG,     /* paged: decode workgroups, min(blocks, n_cu * PIC_DECODE_WG_PER_CU) */
+  PIC_H_O_DEC_WG_PTR, /* paged: [n_dec_wg + 1] pieces of workgroup w are
+                         pieces[ptr[w] .. ptr[w+1]) */
   PIC_H_RESERVED7
 };
 

@@ -26,10 +26,10 @@ PIC_ATTN_TILE_M = 128
  H_MAX_TOKENS, H_O_REQ_CHUNK_PTR, H_O_CHUNK_OFF, H_O_REQ_TOK_PTR, H_O_REQ_ROW_PTR, H_O_ROWS,
  H_O_ROW_TOK, H_O_ROPE_TILES, H_O_ATTN_TILES, H_O_ATTN_ITEMS, H_O_MERGE, H_PAGED, H_O_SEGS,
  H_N_KBLOCKS, H_O_KBLOCKS, H_N_DEC_ITEMS, H_O_DEC_ITEMS, H_N_DEC_USES, H_O_DEC_USES,
- H_N_DEC_SLOTS, H_O_DEC_SLOT_BASE, H_O_DEC_REQ_SLOTS, H_N_DEC_WG, H_O_DEC_WG_PTR,
- H_O_DEC_UNITS) = range(41)
+ H_N_DEC_RECS, H_O_DEC_REC_PTR, H_N_DEC_PIECES, H_O_DEC_PIECES, H_O_DEC_PIECE_RECS,
+ H_N_DEC_WG, H_O_DEC_WG_PTR) = range(42)
 PIC_DECODE_COLS = 64
-PIC_DECODE_RANGE = 256
+PIC_DECODE_BLOCK = 32
 PIC_DECODE_WG_PER_CU = 4
 
 EXPORTED = ("pic_build_index", "pic_rope_delta", "pic_rope_apply", "pic_splice",
@@ -176,7 +176,8 @@ class Plan:
 
     @property
     def dec_items(self):
-        return self._sec(H_O_DEC_ITEMS, self[H_N_DEC_ITEMS], 8)
+        """[n][4]: source (pool chunk id, or -1-b), key count, first use, use count."""
+        return self._sec(H_O_DEC_ITEMS, self[H_N_DEC_ITEMS], 4)
 
     @property
     def dec_uses(self):
@@ -186,23 +187,25 @@ class Plan:
         return self.paged and self[H_H_Q] // self[H_H_KV] <= PIC_DECODE_COLS
 
     @property
-    def dec_slot_base(self):
-        n = self[H_N_CHUNKS] + self[H_N_REQ] if self._has_decode() else 0
-        return self._sec(H_O_DEC_SLOT_BASE, n, 1)
+    def dec_rec_ptr(self):
+        n = self[H_N_REQ] * self[H_H_KV] + 1 if self._has_decode() else 0
+        return self._sec(H_O_DEC_REC_PTR, n, 1)
 
     @property
-    def dec_req_slots(self):
-        return self._sec(H_O_DEC_REQ_SLOTS, self[H_N_REQ] + 1 if self._has_decode() else 0, 1)
+    def dec_pieces(self):
+        """[n][8]: item, kv head, first key, end key, record offset, 0, 0, 0."""
+        return self._sec(H_O_DEC_PIECES, self[H_N_DEC_PIECES], 8)
+
+    @property
+    def dec_piece_recs(self):
+        items = self.dec_items
+        n = int(sum(items[p[0], 3] for p in self.dec_pieces)) if len(items) else 0
+        return self._sec(H_O_DEC_PIECE_RECS, n, 1)
 
     @property
     def dec_wg_ptr(self):
         n = self[H_N_DEC_WG] + 1 if self._has_decode() and self[H_N_DEC_WG] > 0 else 0
         return self._sec(H_O_DEC_WG_PTR, n, 1)
-
-    @property
-    def dec_units(self):
-        n = self[H_N_DEC_ITEMS] * self[H_H_KV] if self._has_decode() else 0
-        return self._sec(H_O_DEC_UNITS, n, 1)
 
     def to_device(self, device="cuda"):
         """Upload the plan (one int32 tensor) and keep it with the host copy."""

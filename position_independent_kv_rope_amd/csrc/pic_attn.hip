@@ -824,24 +824,26 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_paged_kernel(
 
 constexpr int kDecWaves = PIC_DECODE_COLS / 32;  // one 32-column MFMA block per wave
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kDecKB = 32;  // keys per staged block: K + V double-buffered in 32 KiB (D = 128)
+constexpr int kDecKB = PIC_DECODE_BLOCK;  // K + V double-buffered in 32 KiB (D = 128)
 
-// Where the keys of one decode unit (item, kv head) live.  Pool units read the chunk
-// through its block table, fresh units the request's recomputed rows; either way the
-// base address excludes the kv head, which sits in the per-lane offsets.
+// Where the keys of one decode piece (part of an (item, kv head) unit) live.  Pool
+// pieces read the chunk through its block table, fresh pieces the request's recomputed
+// rows; either way the base address excludes the kv head, which sits in the per-lane
+// offsets.
 struct DecSrc {
   const char *k, *v;      // pool tensors, or the request's first fresh row
-  const int32_t *blocks;  // pool block ids of the chunk (pool units)
-  int t_begin, t_end;     // keys of the unit, relative to the chunk or to the fresh rows
+  const int32_t *blocks;  // pool block ids of the chunk (pool pieces)
+  int t_begin, t_end;     // keys of the piece, relative to the chunk or to the fresh rows
   int n_blocks;           // kDecKB-key blocks
-  int item, g;
+  int item, g, rec_off;
   bool pool;
 };
 
-// The grid is resident (at most PIC_DECODE_WG_PER_CU workgroups per CU, each with the
-// unit list the planner balanced): a workgroup streams the key blocks of all its units
-// back to back, staging the next block -- possibly the first of its next unit -- while
-// the current one is scored, so the HBM stream does not drain between units.
+// The grid is resident (at most PIC_DECODE_WG_PER_CU workgroups per CU, each with an
+// equal run of key blocks cut into pieces by the planner): a workgroup streams the
+// blocks of all its pieces back to back, staging the next block -- possibly the first
+// of its next piece -- while the current one is scored, so the HBM stream does not
+// drain between pieces.
 template <int D, bool kHalf>
 __device__ __forceinline__ void dec_attn_body(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ pool_k,
@@ -849,10 +851,10 @@ __device__ __forceinline__ void dec_attn_body(
     const int32_t *__restrict__ block_ids, const __bf16 *__restrict__ k_fresh,
     const __bf16 *__restrict__ v_fresh, const DecItem *__restrict__ items,
     const int32_t *__restrict__ uses, const int32_t *__restrict__ segs,
-    const int32_t *__restrict__ req_row_ptr, const int32_t *__restrict__ slot_base,
-    const int32_t *__restrict__ wg_ptr, const int32_t *__restrict__ units,
+    const int32_t *__restrict__ req_row_ptr, const DecPiece *__restrict__ pieces,
+    const int32_t *__restrict__ piece_recs, const int32_t *__restrict__ wg_ptr,
     const float2 *__restrict__ angles, float *__restrict__ ws_o, float *__restrict__ ws_ml,
-    int h_q, int h_kv, int n_chunks, float scale_log2, int64_t pool_blocks) {
+    int h_q, int h_kv, float scale_log2, int64_t pool_blocks) {
   constexpr int kRowB = D * 2;
   constexpr int kCPR = D / 8;
   constexpr int kTileB = kDecKB * kRowB;
@@ -878,16 +880,17 @@ __device__ __forceinline__ void dec_attn_body(
   const int tok_bytes = h_kv * kRowB;
   const int64_t blk_bytes = (int64_t)kPoolBlockRows * tok_bytes;
 
-  auto load_src = [&](int ui) {
+  auto load_src = [&](int pi) {
     DecSrc sr;
-    const int code = units[ui];
-    sr.item = code / h_kv;
-    sr.g = code - sr.item * h_kv;
-    const DecItem it = items[sr.item];
+    const DecPiece pc = pieces[pi];
+    sr.item = pc.item;
+    sr.g = pc.g;
+    sr.rec_off = pc.rec_off;
+    const DecItem it = items[pc.item];
     sr.pool = it.src >= 0;
-    sr.t_begin = it.t_begin;
-    sr.t_end = it.t_end;
-    sr.n_blocks = (it.t_end - it.t_begin + kDecKB - 1) / kDecKB;
+    sr.t_begin = pc.t_begin;
+    sr.t_end = pc.t_end;
+    sr.n_blocks = (pc.t_end - pc.t_begin + kDecKB - 1) / kDecKB;
     if (sr.pool) {
       sr.k = reinterpret_cast<const char *>(pool_k);
       sr.v = reinterpret_cast<const char *>(pool_v);
@@ -992,7 +995,7 @@ __device__ __forceinline__ void dec_attn_body(
     const int use = valid ? uses[it.use_begin + u] : 0;
     const int req = !valid ? 0 : (pool ? segs[8 * use + 5] : -1 - use);
     const int seam = (valid && pool) ? segs[8 * use + 2] : 0;
-    const int slot = valid ? slot_base[pool ? use : n_chunks + req] + it.range : 0;
+    const int rec = valid ? piece_recs[cur.rec_off + u] : 0;
 
     bf16x8 qop[kKS];
     {
@@ -1120,7 +1123,7 @@ __device__ __forceinline__ void dec_attn_body(
     if (active) {
       const float l_row = pair_sum(l_lane);
       if (valid) {
-        const int64_t at = ((int64_t)slot * h_kv + g) * group + hh;
+        const int64_t at = (int64_t)rec * group + hh;
         float *wo = ws_o + at * D + 4 * grp;
 #pragma unroll
         for (int d = 0; d < kDB; ++d)
@@ -1147,25 +1150,25 @@ __global__ __launch_bounds__(kDecThreads, 2) void dec_attn_kernel(
     const int32_t *__restrict__ block_ids, const __bf16 *__restrict__ k_fresh,
     const __bf16 *__restrict__ v_fresh, const DecItem *__restrict__ items,
     const int32_t *__restrict__ uses, const int32_t *__restrict__ segs,
-    const int32_t *__restrict__ req_row_ptr, const int32_t *__restrict__ slot_base,
-    const int32_t *__restrict__ wg_ptr, const int32_t *__restrict__ units,
+    const int32_t *__restrict__ req_row_ptr, const DecPiece *__restrict__ pieces,
+    const int32_t *__restrict__ piece_recs, const int32_t *__restrict__ wg_ptr,
     const float2 *__restrict__ angles, float *__restrict__ ws_o, float *__restrict__ ws_ml,
-    int h_q, int h_kv, int n_chunks, float scale_log2, int64_t pool_blocks) {
+    int h_q, int h_kv, float scale_log2, int64_t pool_blocks) {
   dec_attn_body<D, kHalf>(q, pool_k, pool_v, chunk_block_ptr, block_ids, k_fresh, v_fresh,
-                          items, uses, segs, req_row_ptr, slot_base, wg_ptr, units, angles,
-                          ws_o, ws_ml, h_q, h_kv, n_chunks, scale_log2, pool_blocks);
+                          items, uses, segs, req_row_ptr, pieces, piece_recs, wg_ptr, angles,
+                          ws_o, ws_ml, h_q, h_kv, scale_log2, pool_blocks);
 }
 
 // One workgroup per (request, query head): groups of D/4 lanes fold disjoint subsets
-// of the request's partial slots (online log-sum-exp, 4 dims per lane, two slots'
-// loads in flight per group), group 0 also the new token (score q . k_new, weight
-// v_new); the group results are combined in LDS.
+// of the records of (request, kv head) (online log-sum-exp, 4 dims per lane, two
+// records' loads in flight per group), group 0 also the new token (score q . k_new,
+// weight v_new); the group results are combined in LDS.
 constexpr int kDecMergeThreads = 1024;
 
 template <int D>
 __global__ __launch_bounds__(kDecMergeThreads) void dec_merge_kernel(
     __bf16 *__restrict__ out, const __bf16 *__restrict__ q, const __bf16 *__restrict__ k_new,
-    const __bf16 *__restrict__ v_new, const int32_t *__restrict__ req_slots,
+    const __bf16 *__restrict__ v_new, const int32_t *__restrict__ rec_ptr,
     const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int h_q, int h_kv,
     float scale_log2) {
   constexpr int kC = D / 4;
@@ -1207,11 +1210,11 @@ __global__ __launch_bounds__(kDecMergeThreads) void dec_merge_kernel(
     den += w * ls;
     num += w * os;
   };
-  const int s_end = req_slots[b + 1];
-  for (int sl = req_slots[b] + gi; sl < s_end; sl += 2 * kDecMergeGroups) {
+  const int s_end = rec_ptr[b * h_kv + g + 1];
+  for (int sl = rec_ptr[b * h_kv + g] + gi; sl < s_end; sl += 2 * kDecMergeGroups) {
     const int sl2 = sl + kDecMergeGroups < s_end ? sl + kDecMergeGroups : sl;
-    const int64_t a1 = ((int64_t)sl * h_kv + g) * group + hh;
-    const int64_t a2 = ((int64_t)sl2 * h_kv + g) * group + hh;
+    const int64_t a1 = (int64_t)sl * group + hh;
+    const int64_t a2 = (int64_t)sl2 * group + hh;
     const float2 ml1 = *reinterpret_cast<const float2 *>(ws_ml + a1 * 2);
     const float2 ml2 = *reinterpret_cast<const float2 *>(ws_ml + a2 * 2);
     const f32x4 o1 = *reinterpret_cast<const f32x4 *>(ws_o + a1 * D + 4 * c4);
@@ -1530,10 +1533,10 @@ int launch_paged(const PlanHeader &h, const int32_t *plan_dev, const void *q, co
   return PIC_OK;
 }
 
-// Decode workspace: partial O [n_dec_slots][h_kv][G][D], partial (m, l) [..][2],
+// Decode workspace: partial O [n_dec_recs][G][D], partial (m, l) [..][2],
 // then the angle table [n_chunks][D/2] float2 (16-byte aligned).
 size_t dec_partial_floats(const PlanHeader &h, int head_dim) {
-  return (size_t)h[PIC_H_N_DEC_SLOTS] * h[PIC_H_H_Q] * ((size_t)head_dim + 2);
+  return (size_t)h[PIC_H_N_DEC_RECS] * (h[PIC_H_H_Q] / h[PIC_H_H_KV]) * ((size_t)head_dim + 2);
 }
 
 template <int D, bool kHalf>
@@ -1545,10 +1548,10 @@ int launch_decode(const PlanHeader &h, const int32_t *plan_dev, const void *q, c
   const DecItem *items = reinterpret_cast<const DecItem *>(plan_dev + h[PIC_H_O_DEC_ITEMS]);
   const int32_t *uses = plan_dev + h[PIC_H_O_DEC_USES];
   const int32_t *rrp = plan_dev + h[PIC_H_O_REQ_ROW_PTR];
-  const int32_t *slot_base = plan_dev + h[PIC_H_O_DEC_SLOT_BASE];
-  const int32_t *req_slots = plan_dev + h[PIC_H_O_DEC_REQ_SLOTS];
+  const DecPiece *pieces = reinterpret_cast<const DecPiece *>(plan_dev + h[PIC_H_O_DEC_PIECES]);
+  const int32_t *rec_ptr = plan_dev + h[PIC_H_O_DEC_REC_PTR];
   float *ws_o = static_cast<float *>(workspace);
-  float *ws_ml = ws_o + (size_t)h[PIC_H_N_DEC_SLOTS] * h[PIC_H_H_Q] * D;
+  float *ws_ml = ws_o + (size_t)h[PIC_H_N_DEC_RECS] * (h[PIC_H_H_Q] / h[PIC_H_H_KV]) * D;
   const size_t ang_off = (dec_partial_floats(h, D) * sizeof(float) + 15) / 16 * 16;
   float2 *angles = reinterpret_cast<float2 *>(static_cast<char *>(workspace) + ang_off);
   const int n_chunks = h[PIC_H_N_CHUNKS];
@@ -1565,15 +1568,15 @@ int launch_decode(const PlanHeader &h, const int32_t *plan_dev, const void *q, c
                        0, s, static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(pool_k),
                        static_cast<const __bf16 *>(pool_v), cbp, bids,
                        static_cast<const __bf16 *>(kf), static_cast<const __bf16 *>(vf), items,
-                       uses, segs, rrp, slot_base, plan_dev + h[PIC_H_O_DEC_WG_PTR],
-                       plan_dev + h[PIC_H_O_DEC_UNITS], angles, ws_o, ws_ml, h[PIC_H_H_Q],
-                       h[PIC_H_H_KV], n_chunks, scale_log2, pool_blocks);
+                       uses, segs, rrp, pieces, plan_dev + h[PIC_H_O_DEC_PIECE_RECS],
+                       plan_dev + h[PIC_H_O_DEC_WG_PTR], angles, ws_o, ws_ml, h[PIC_H_H_Q],
+                       h[PIC_H_H_KV], scale_log2, pool_blocks);
     PIC_LAUNCH_CHECK();
   }
   hipLaunchKernelGGL((dec_merge_kernel<D>), dim3(h[PIC_H_N_REQ] * h[PIC_H_H_Q]),
                      dim3(kDecMergeThreads), 0, s, static_cast<__bf16 *>(out),
                      static_cast<const __bf16 *>(q), static_cast<const __bf16 *>(k_new),
-                     static_cast<const __bf16 *>(v_new), req_slots, ws_o, ws_ml, h[PIC_H_H_Q],
+                     static_cast<const __bf16 *>(v_new), rec_ptr, ws_o, ws_ml, h[PIC_H_H_Q],
                      h[PIC_H_H_KV], scale_log2);
   PIC_LAUNCH_CHECK();
   return PIC_OK;

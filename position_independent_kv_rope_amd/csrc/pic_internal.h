@@ -32,9 +32,13 @@ struct MergeEntry {
 };
 struct DecItem {
   int32_t src;  // pool chunk id (>= 0) or -1 - b for the fresh rows of request b
-  int32_t t_begin, t_end, use_begin, n_uses;
-  int32_t range;  // key range index within the chunk (or the fresh rows)
-  int32_t pad0, pad1;
+  int32_t n_keys, use_begin, n_uses;
+};
+struct DecPiece {
+  int32_t item, g;        // decode item and kv head
+  int32_t t_begin, t_end; // keys of the item this piece scores
+  int32_t rec_off;        // its records: piece_recs[rec_off .. rec_off + n_uses)
+  int32_t pad0, pad1, pad2;
 };
 struct RopeTile {
   int32_t tok_begin, n_rows, delta;
@@ -45,7 +49,8 @@ static_assert(sizeof(AttnTile) == 32, "plan record size");
 static_assert(sizeof(AttnItem) == 32, "plan record size");
 static_assert(sizeof(MergeEntry) == 16, "plan record size");
 static_assert(sizeof(RopeTile) == 16, "plan record size");
-static_assert(sizeof(DecItem) == 32, "plan record size");
+static_assert(sizeof(DecItem) == 16, "plan record size");
+static_assert(sizeof(DecPiece) == 32, "plan record size");
 static_assert(PIC_H_RESERVED7 < PIC_PLAN_HEADER_WORDS, "header fields fit the header");
 
 inline size_t dtype_size(int32_t dt) { return dt == PIC_BF16 ? 2 : (dt == PIC_F32 ? 4 : 0); }

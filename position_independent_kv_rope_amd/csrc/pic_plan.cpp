@@ -17,7 +17,6 @@
 #include <cstring>
 #include <numeric>
 #include <unordered_map>
-#include <queue>
 #include <vector>
 
 #include "pic_internal.h"
@@ -360,27 +359,16 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   // ---- decode items (paged plans): every pool chunk once, for all its uses ----
   // A decode step streams each pool chunk from HBM once and serves every request
   // chunk that reads it (up to PIC_DECODE_COLS / G uses per item); each request's fresh
-  // rows (seams and queries) are further items.  Items cover <= PIC_DECODE_RANGE keys;
-  // every (request chunk, range) and (request fresh rows, range) owns one partial slot,
-  // and the slots of a request are contiguous.
+  // rows (seams and queries) are further items.  Each (item, kv head) unit is a run of
+  // PIC_DECODE_BLOCK-key blocks; the concatenated runs are cut into n_dec_wg equal
+  // parts, one per resident workgroup, so every workgroup streams the same bytes.  The
+  // part of a unit inside one workgroup's run is a piece; it leaves one record
+  // (m, l, O of the G heads) per use, and the records of each (request, kv head) are
+  // numbered contiguously for the merge.
   std::vector<DecItem> dec_items;
-  std::vector<int32_t> dec_uses, dec_slot_base, dec_req_slots, dec_wg_ptr, dec_units;
+  std::vector<DecPiece> dec_pieces;
+  std::vector<int32_t> dec_uses, dec_rec_ptr, dec_piece_recs, dec_wg_ptr;
   if (paged && group <= PIC_DECODE_COLS) {
-    auto n_ranges = [](int32_t len) { return (len + PIC_DECODE_RANGE - 1) / PIC_DECODE_RANGE; };
-    dec_slot_base.assign((size_t)n_chunks + n_req, 0);
-    dec_req_slots.assign((size_t)n_req + 1, 0);
-    int64_t slots = 0;
-    for (int32_t b = 0; b < n_req; ++b) {
-      dec_req_slots[b] = (int32_t)slots;
-      for (int32_t c = req_chunk_ptr[b]; c < req_chunk_ptr[b + 1]; ++c) {
-        dec_slot_base[c] = (int32_t)slots;
-        slots += n_ranges(chunk_lens[c]);
-      }
-      dec_slot_base[n_chunks + b] = (int32_t)slots;
-      slots += n_ranges(req_row_ptr[b + 1] - req_row_ptr[b]);
-      if (slots > kMaxI32 / 2) return PIC_EINVAL;
-    }
-    dec_req_slots[n_req] = (int32_t)slots;
     const int32_t per_item = PIC_DECODE_COLS / group;
     std::vector<std::pair<int32_t, int32_t>> by_id;  // (pool chunk id, global chunk index)
     for (int32_t c = 0; c < n_chunks; ++c)
@@ -391,71 +379,70 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
     for (size_t i = 0; i < by_id.size();) {
       size_t j = i;
       while (j < by_id.size() && by_id[j].first == by_id[i].first) ++j;
-      const int32_t len = chunk_lens[by_id[i].second];
       for (size_t u = i; u < j; u += per_item) {
-        const int32_t use_begin = (int32_t)dec_uses.size();
-        const int32_t nu = (int32_t)std::min<size_t>(per_item, j - u);
-        for (size_t v = u; v < u + (size_t)nu; ++v) dec_uses.push_back(by_id[v].second);
-        for (int32_t r = 0; r < n_ranges(len); ++r) {
-          DecItem d{};
-          d.src = by_id[i].first;
-          d.t_begin = r * PIC_DECODE_RANGE;
-          d.t_end = std::min(len, (r + 1) * PIC_DECODE_RANGE);
-          d.use_begin = use_begin;
-          d.n_uses = nu;
-          d.range = r;
-          dec_items.push_back(d);
-        }
+        DecItem d{};
+        d.src = by_id[i].first;
+        d.n_keys = chunk_lens[by_id[i].second];
+        d.use_begin = (int32_t)dec_uses.size();
+        d.n_uses = (int32_t)std::min<size_t>(per_item, j - u);
+        for (size_t v = u; v < u + (size_t)d.n_uses; ++v) dec_uses.push_back(by_id[v].second);
+        dec_items.push_back(d);
       }
       i = j;
     }
     for (int32_t b = 0; b < n_req; ++b) {
       const int32_t r_b = req_row_ptr[b + 1] - req_row_ptr[b];
       if (r_b == 0) continue;
-      const int32_t use_begin = (int32_t)dec_uses.size();
+      dec_items.push_back(DecItem{-1 - b, r_b, (int32_t)dec_uses.size(), 1});
       dec_uses.push_back(-1 - b);
-      for (int32_t r = 0; r < n_ranges(r_b); ++r) {
-        DecItem d{};
-        d.src = -1 - b;
-        d.t_begin = r * PIC_DECODE_RANGE;
-        d.t_end = std::min(r_b, (r + 1) * PIC_DECODE_RANGE);
-        d.use_begin = use_begin;
-        d.n_uses = 1;
-        d.range = r;
-        dec_items.push_back(d);
+    }
+    constexpr int32_t kB = PIC_DECODE_BLOCK;
+    int64_t total = 0;  // blocks over all units
+    for (const DecItem &d : dec_items) total += (int64_t)(d.n_keys + kB - 1) / kB * h_kv;
+    if (total > kMaxI32 / 2) return PIC_EINVAL;
+    const int64_t n_wg = std::min<int64_t>(total, (int64_t)n_cu * PIC_DECODE_WG_PER_CU);
+    auto run_begin = [&](int64_t w) { return w * total / n_wg; };  // first block of run w
+    // the request of each use (a pool use names its request chunk)
+    std::vector<int32_t> chunk_req((size_t)n_chunks);
+    for (int32_t b = 0; b < n_req; ++b)
+      for (int32_t c = req_chunk_ptr[b]; c < req_chunk_ptr[b + 1]; ++c) chunk_req[c] = b;
+    auto use_req = [&](int32_t use) { return use >= 0 ? chunk_req[use] : -1 - use; };
+    std::vector<int64_t> n_recs((size_t)n_req * h_kv, 0);
+    int64_t pos = 0, w = 0;
+    dec_wg_ptr.push_back(0);
+    for (size_t it = 0; it < dec_items.size(); ++it) {
+      const DecItem &d = dec_items[it];
+      const int64_t nb = (d.n_keys + kB - 1) / kB;
+      for (int32_t g = 0; g < h_kv; ++g) {
+        for (int64_t blk = 0; blk < nb;) {
+          while (pos >= run_begin(w + 1)) {  // close run w
+            dec_wg_ptr.push_back((int32_t)dec_pieces.size());
+            ++w;
+          }
+          const int64_t take = std::min<int64_t>(nb - blk, run_begin(w + 1) - pos);
+          DecPiece pc{};
+          pc.item = (int32_t)it;
+          pc.g = g;
+          pc.t_begin = (int32_t)(blk * kB);
+          pc.t_end = (int32_t)std::min<int64_t>(d.n_keys, (blk + take) * kB);
+          pc.rec_off = (int32_t)dec_piece_recs.size();
+          for (int32_t u = 0; u < d.n_uses; ++u) {  // record ids assigned below
+            const int32_t b = use_req(dec_uses[d.use_begin + u]);
+            dec_piece_recs.push_back(b * h_kv + g);
+            ++n_recs[(size_t)b * h_kv + g];
+          }
+          dec_pieces.push_back(pc);
+          blk += take;
+          pos += take;
+        }
       }
     }
-    // Units (item, kv head) onto a resident grid: longest first, each to the workgroup
-    // with the fewest key blocks so far (ties: lowest index), so that the workgroups
-    // stream about equal bytes and drain together.
-    const int64_t n_units = (int64_t)dec_items.size() * h_kv;
-    if (n_units > kMaxI32 / 2) return PIC_EINVAL;
-    const int32_t n_wg = (int32_t)std::min<int64_t>(n_units, (int64_t)n_cu * PIC_DECODE_WG_PER_CU);
-    std::vector<std::pair<int32_t, int32_t>> cost;  // (key blocks + 1, unit)
-    cost.reserve((size_t)n_units);
-    for (size_t i = 0; i < dec_items.size(); ++i) {
-      const int32_t nb = (dec_items[i].t_end - dec_items[i].t_begin + 31) / 32 + 1;
-      for (int32_t g = 0; g < h_kv; ++g) cost.push_back({nb, (int32_t)(i * h_kv + g)});
-    }
-    std::stable_sort(cost.begin(), cost.end(),
-                     [](const std::pair<int32_t, int32_t> &a,
-                        const std::pair<int32_t, int32_t> &b) { return a.first > b.first; });
-    using Load = std::pair<int64_t, int32_t>;  // (blocks assigned, workgroup)
-    std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
-    for (int32_t w = 0; w < n_wg; ++w) heap.push({0, w});
-    std::vector<std::vector<int32_t>> per_wg((size_t)n_wg);
-    for (const auto &cu : cost) {
-      Load l = heap.top();
-      heap.pop();
-      per_wg[l.second].push_back(cu.second);
-      heap.push({l.first + cu.first, l.second});
-    }
-    dec_wg_ptr.assign((size_t)n_wg + 1, 0);
-    dec_units.reserve((size_t)n_units);
-    for (int32_t w = 0; w < n_wg; ++w) {
-      dec_units.insert(dec_units.end(), per_wg[w].begin(), per_wg[w].end());
-      dec_wg_ptr[w + 1] = (int32_t)dec_units.size();
-    }
+    while ((int64_t)dec_wg_ptr.size() < n_wg + 1) dec_wg_ptr.push_back((int32_t)dec_pieces.size());
+    dec_rec_ptr.assign((size_t)n_req * h_kv + 1, 0);
+    for (size_t x = 0; x < n_recs.size(); ++x) dec_rec_ptr[x + 1] = dec_rec_ptr[x] + (int32_t)n_recs[x];
+    if (dec_rec_ptr.back() > kMaxI32 / 2) return PIC_EINVAL;
+    std::vector<int32_t> next(dec_rec_ptr.begin(), dec_rec_ptr.end() - 1);
+    for (int32_t &r : dec_piece_recs) r = next[r]++;  // (request, kv head) -> record id
   }
 
   // ---- layout of the plan ----
@@ -477,12 +464,12 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   const int64_t o_merge = place((int64_t)merges.size() * 4);
   const int64_t o_segs = place((int64_t)segs.size());
   const int64_t o_kblocks = place((int64_t)kblocks.size());
-  const int64_t o_dec_items = place((int64_t)dec_items.size() * 8);
+  const int64_t o_dec_items = place((int64_t)dec_items.size() * 4);
   const int64_t o_dec_uses = place((int64_t)dec_uses.size());
-  const int64_t o_dec_slot_base = place((int64_t)dec_slot_base.size());
-  const int64_t o_dec_req_slots = place((int64_t)dec_req_slots.size());
+  const int64_t o_dec_rec_ptr = place((int64_t)dec_rec_ptr.size());
+  const int64_t o_dec_pieces = place((int64_t)dec_pieces.size() * 8);
+  const int64_t o_dec_piece_recs = place((int64_t)dec_piece_recs.size());
   const int64_t o_dec_wg_ptr = place((int64_t)dec_wg_ptr.size());
-  const int64_t o_dec_units = place((int64_t)dec_units.size());
   if (words > kMaxI32) return PIC_EINVAL;
   *plan_words = words;
   if (plan == nullptr) return PIC_OK;
@@ -525,12 +512,13 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   h[PIC_H_O_DEC_ITEMS] = (int32_t)o_dec_items;
   h[PIC_H_N_DEC_USES] = (int32_t)dec_uses.size();
   h[PIC_H_O_DEC_USES] = (int32_t)o_dec_uses;
-  h[PIC_H_N_DEC_SLOTS] = dec_req_slots.empty() ? 0 : dec_req_slots.back();
-  h[PIC_H_O_DEC_SLOT_BASE] = (int32_t)o_dec_slot_base;
-  h[PIC_H_O_DEC_REQ_SLOTS] = (int32_t)o_dec_req_slots;
+  h[PIC_H_N_DEC_RECS] = dec_rec_ptr.empty() ? 0 : dec_rec_ptr.back();
+  h[PIC_H_O_DEC_REC_PTR] = (int32_t)o_dec_rec_ptr;
+  h[PIC_H_N_DEC_PIECES] = (int32_t)dec_pieces.size();
+  h[PIC_H_O_DEC_PIECES] = (int32_t)o_dec_pieces;
+  h[PIC_H_O_DEC_PIECE_RECS] = (int32_t)o_dec_piece_recs;
   h[PIC_H_N_DEC_WG] = dec_wg_ptr.empty() ? 0 : (int32_t)dec_wg_ptr.size() - 1;
   h[PIC_H_O_DEC_WG_PTR] = (int32_t)o_dec_wg_ptr;
-  h[PIC_H_O_DEC_UNITS] = (int32_t)o_dec_units;
   if (n_req > 0) std::memcpy(h + o_rcp, req_chunk_ptr, sizeof(int32_t) * (n_req + 1));
   else h[o_rcp] = 0;
   if (!chunk_off.empty()) std::memcpy(h + o_coff, chunk_off.data(), sizeof(int32_t) * chunk_off.size());
@@ -550,14 +538,14 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
     std::memcpy(h + o_dec_items, dec_items.data(), sizeof(DecItem) * dec_items.size());
   if (!dec_uses.empty())
     std::memcpy(h + o_dec_uses, dec_uses.data(), sizeof(int32_t) * dec_uses.size());
-  if (!dec_slot_base.empty())
-    std::memcpy(h + o_dec_slot_base, dec_slot_base.data(), sizeof(int32_t) * dec_slot_base.size());
-  if (!dec_req_slots.empty())
-    std::memcpy(h + o_dec_req_slots, dec_req_slots.data(), sizeof(int32_t) * dec_req_slots.size());
+  if (!dec_rec_ptr.empty())
+    std::memcpy(h + o_dec_rec_ptr, dec_rec_ptr.data(), sizeof(int32_t) * dec_rec_ptr.size());
+  if (!dec_pieces.empty())
+    std::memcpy(h + o_dec_pieces, dec_pieces.data(), sizeof(DecPiece) * dec_pieces.size());
+  if (!dec_piece_recs.empty())
+    std::memcpy(h + o_dec_piece_recs, dec_piece_recs.data(), sizeof(int32_t) * dec_piece_recs.size());
   if (!dec_wg_ptr.empty())
     std::memcpy(h + o_dec_wg_ptr, dec_wg_ptr.data(), sizeof(int32_t) * dec_wg_ptr.size());
-  if (!dec_units.empty())
-    std::memcpy(h + o_dec_units, dec_units.data(), sizeof(int32_t) * dec_units.size());
   return PIC_OK;
 }
 

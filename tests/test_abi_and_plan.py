@@ -282,56 +282,69 @@ def check_paged_plan(reqs, ids, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0):
         assert 0 <= b1 <= e1 and 0 <= b2 <= e2
         for i in list(range(b1, e1)) + list(range(b2, e2)):
             assert kb[i][2] <= tiles[tile][5]  # no block starts after the tile's last row
-    # decode items: every (request chunk, PIC_DECODE_RANGE-key range) with keys is one use
-    # of exactly one item of its pool chunk (at most PIC_DECODE_COLS / G uses), every
-    # range of a request's fresh rows is one item of its own; each writes the partial
-    # slot slot_base[chunk or n_chunks + request] + range, and a request's slots form
-    # the contiguous run [req_slots[b], req_slots[b + 1])
+    # decode items: every request chunk with keys is one use of exactly one item of its
+    # pool chunk (at most PIC_DECODE_COLS / G uses, all of the chunk's keys), and every
+    # request with fresh rows has one item of its own
     group = h_q // h_kv
-    R = P.PIC_DECODE_RANGE
+    B = P.PIC_DECODE_BLOCK
     items, uses = plan.dec_items.tolist(), plan.dec_uses.tolist()
-    base, rs = plan.dec_slot_base.tolist(), plan.dec_req_slots.tolist()
     n_chunks = plan[P.H_N_CHUNKS]
-    assert plan[P.H_N_DEC_USES] == len(uses) and len(base) == n_chunks + len(reqs)
+    assert plan[P.H_N_DEC_USES] == len(uses)
     flat_lens = [x for lens in reqs for x in lens]
     flat_ids = [x for c in ids for x in c]
     n_fresh = [int(plan.req_row_ptr[b + 1] - plan.req_row_ptr[b]) for b in range(len(reqs))]
-    seen, fresh, slots = [], [], []
-    for src, t0, t1, u0, nu, r, _, _ in items:
-        assert 1 <= nu <= P.PIC_DECODE_COLS // group and t0 == r * R < t1
+    use_req = [segs[c][5] if c >= 0 else -1 - c for c in uses]
+    seen, fresh = [], []
+    for src, n_keys, u0, nu in items:
+        assert 1 <= nu <= P.PIC_DECODE_COLS // group
         us = uses[u0:u0 + nu]
         if src >= 0:
-            for c in us:
-                assert flat_ids[c] == src and t1 == min(flat_lens[c], t0 + R)
-                b = segs[c][5]
-                slots.append(base[c] + r)
-                assert rs[b] <= base[c] + r < rs[b + 1]
-            seen += [(c, r) for c in us]
+            assert all(flat_ids[c] == src and flat_lens[c] == n_keys > 0 for c in us)
+            seen += us
         else:
-            b = -1 - src
-            assert us == [src] and t1 == min(n_fresh[b], t0 + R)
-            fresh.append((b, r))
-            slots.append(base[n_chunks + b] + r)
-            assert rs[b] <= base[n_chunks + b] + r < rs[b + 1]
-    ranges = lambda L: range((L + R - 1) // R)
-    assert sorted(seen) == [(c, r) for c, L in enumerate(flat_lens) for r in ranges(L)]
-    assert sorted(fresh) == [(b, r) for b, L in enumerate(n_fresh) for r in ranges(L)]
-    assert sorted(slots) == list(range(plan[P.H_N_DEC_SLOTS])) and rs[0] == 0
-    assert rs[-1] == plan[P.H_N_DEC_SLOTS] and rs == sorted(rs)
-    # decode schedule: every (item, kv head) unit on exactly one workgroup of a grid of
-    # min(units, n_cu * PIC_DECODE_WG_PER_CU), no workgroup idle, and the key-block loads
-    # balanced to within one unit (greedy longest-first)
-    n_units = len(items) * h_kv
-    wp, un = plan.dec_wg_ptr.tolist(), plan.dec_units.tolist()
+            assert us == [src] and n_keys == n_fresh[-1 - src] > 0
+            fresh.append(-1 - src)
+    assert sorted(seen) == [c for c, L in enumerate(flat_lens) if L > 0]
+    assert fresh == [b for b in range(len(reqs)) if n_fresh[b] > 0]
+    # pieces: the (item, kv head) units, in order, cut into B-key blocks; the block
+    # sequence split into n_wg equal runs (min(blocks, n_cu * PIC_DECODE_WG_PER_CU) of
+    # them); a piece is a unit's part of one run, and it writes one record per use
+    pieces, wp = plan.dec_pieces.tolist(), plan.dec_wg_ptr.tolist()
+    precs, rp = plan.dec_piece_recs.tolist(), plan.dec_rec_ptr.tolist()
+    units = [(i, g, n_keys) for i, (_, n_keys, _, _) in enumerate(items) for g in range(h_kv)]
+    total = sum((n + B - 1) // B for _, _, n in units)
     n_wg = plan[P.H_N_DEC_WG]
-    assert n_wg == min(n_units, (n_cu if n_cu > 0 else 256) * P.PIC_DECODE_WG_PER_CU)
-    assert sorted(un) == list(range(n_units))
-    if n_units:
-        assert wp[0] == 0 and wp[-1] == n_units and len(wp) == n_wg + 1
-        assert all(wp[w] < wp[w + 1] for w in range(n_wg))
-        cost = [(items[u // h_kv][2] - items[u // h_kv][1] + 31) // 32 + 1 for u in range(n_units)]
-        loads = [sum(cost[u] for u in un[wp[w]:wp[w + 1]]) for w in range(n_wg)]
-        assert max(loads) - min(loads) <= max(cost)
+    assert n_wg == min(total, (n_cu if n_cu > 0 else 256) * P.PIC_DECODE_WG_PER_CU)
+    if total == 0:
+        assert pieces == [] and rp[-1] == 0
+        return plan
+    assert wp[0] == 0 and wp[-1] == len(pieces) and len(wp) == n_wg + 1
+    cover = {}  # (item, g) -> blocks in piece order
+    for w in range(n_wg):
+        assert wp[w] < wp[w + 1]  # no idle workgroup
+        run = 0
+        for it, g, t0, t1, off, _, _, _ in pieces[wp[w]:wp[w + 1]]:
+            n_keys = items[it][1]
+            assert t0 % B == 0 and t0 < t1 and (t1 % B == 0 or t1 == n_keys) and t1 <= n_keys
+            cover.setdefault((it, g), []).append((t0, t1))
+            run += (t1 - t0 + B - 1) // B
+        assert run in (total // n_wg, (total + n_wg - 1) // n_wg)
+    for it, g, n_keys in units:  # each unit's pieces tile its keys in order
+        spans = cover.pop((it, g))
+        assert spans[0][0] == 0 and spans[-1][1] == n_keys
+        assert all(a[1] == b[0] for a, b in zip(spans, spans[1:]))
+    assert not cover
+    # records: ids of (request b, kv head g) are the contiguous run [rp[b*h_kv+g], ..+1)
+    assert rp[0] == 0 and rp == sorted(rp) and rp[-1] == plan[P.H_N_DEC_RECS]
+    got = []
+    for it, g, t0, t1, off, _, _, _ in pieces:
+        _, _, u0, nu = items[it]
+        for u in range(nu):
+            b = use_req[u0 + u]
+            r = precs[off + u]
+            assert rp[b * h_kv + g] <= r < rp[b * h_kv + g + 1]
+            got.append(r)
+    assert sorted(got) == list(range(rp[-1]))
     return plan
 
 
@@ -340,8 +353,10 @@ def test_paged_plan_small():
     # one pool chunk read twice by one request, and by two requests
     check_paged_plan([[16, 3, 16, 64], [64, 16]], [[0, 1, 0, 3], [3, 0]], [7, 0], 8, 8, 2)
     check_paged_plan([[4, 5, 5]], [[0, 1, 2]], [3], 2, 4, 4, pos_base=3)
-    # chunks and fresh rows longer than one decode range, a chunk of exactly one range
-    check_paged_plan([[300, 600, 256], [600, 10]], [[0, 1, 2], [1, 3]], [300, 0], 8, 16, 2)
+    # long chunks and fresh rows over a grid of few workgroups (runs cut inside units),
+    # a chunk of exactly a whole number of blocks
+    check_paged_plan([[300, 600, 256], [600, 10]], [[0, 1, 2], [1, 3]], [300, 0], 8, 16, 2,
+                     n_cu=3)
 
 
 def test_paged_plan_shared_pool_workload():

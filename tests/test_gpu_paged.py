@@ -182,8 +182,8 @@ def run_decode(wl, layout="adjacent", nan_slack=False, n_cu=0, requests=None):
     qn, kn, vn = W.decode_tensors(wl)
     dev = "cuda"
     out = torch.full(qn.shape, float("nan"), dtype=qn.dtype, device=dev)
-    say(wl.name, "decode", layout, "items=%d uses=%d" % (plan[P.H_N_DEC_ITEMS],
-                                                        plan[P.H_N_DEC_USES]))
+    say(wl.name, "decode", layout, "items=%d uses=%d pieces=%d workgroups=%d" % (
+        plan[P.H_N_DEC_ITEMS], plan[P.H_N_DEC_USES], plan[P.H_N_DEC_PIECES], plan[P.H_N_DEC_WG]))
     lay = P.PIC_ROPE_HALF if layout == "half" else P.PIC_ROPE_ADJACENT
     P.pic_decode_attn_paged(plan, qn.to(dev), kn.to(dev), vn.to(dev), pk.to(dev), pv.to(dev),
                             torch.from_numpy(cbp).to(dev), torch.from_numpy(blocks).to(dev),
@@ -228,6 +228,13 @@ def test_decode_edges_nan_slack_and_gqa4_d64():
             W.Request([16, 3, 16, 64, 1, 200], 7, chunk_ids=[0, 1, 0, 3, 4, 2])]
     run_decode(W.Workload("decode_edges", "bf16", 8, 2, 128, 10000.0, 8, reqs, pool_lens=lens,
                           block_size=16, pool_block_perm_seed=3, seed=53))
+
+
+def test_decode_few_workgroups():
+    # grids of 4 and 12 workgroups: each streams many pieces back to back and the equal
+    # runs cut units in the middle, so one (use, kv head) leaves several records
+    run_decode(small_pool(8, seed=59), n_cu=1)
+    run_decode(small_pool(8, seed=61), layout="half", n_cu=3)
 
 
 def test_decode_shared_pool_full_size():
