@@ -290,7 +290,7 @@ int pic_selective_attn_paged(const int32_t *plan_host, const int32_t *plan_dev, 
  * that use it (the plan's decode items), on a resident grid that walks the plan's
  * decode units.  q_new/out: device [n_req][h_q][head_dim];
  * k_new/v_new: device [n_req][h_kv][head_dim], RoPE'd at N_b; pool and fresh arguments
- * as pic_selective_attn_paged, without its size limit (64-bit offsets).  Later decode
+ * as pic_selective_attn_paged, without its fresh-row size limit.  Later decode
  * steps append the generated rows to the fresh buffer through a plan with longer
  * queries.  bf16 only, head_dim in {64, 128}, h_q/h_kv <= PIC_DECODE_COLS.
  * workspace >= pic_decode_workspace_bytes (partials + angle table).  Errors as

@@ -155,7 +155,8 @@ __device__ __forceinline__ void attn_bf16_body(
   const int tok_bytes = h_kv * D * 2;
 
   // ---- direct global->LDS staging: buffer resources clamp rows >= key_end to zero ----
-  // (the resources are rebuilt where used: a lambda may not capture the resource type)
+  // (the resources are rebuilt where used: a lambda may not capture the resource type;
+  // the block's row offset rides in the per-lane offset, which the range check sees)
   const int64_t head_off = ((int64_t)tile.tok_base * h_kv + g) * D;
   const __bf16 *kh = kbuf + head_off;
   const __bf16 *vh = vbuf + head_off;
@@ -173,11 +174,12 @@ __device__ __forceinline__ void attn_bf16_body(
   auto issue = [&](const __bf16 *base, const int (&voffs)[kRounds], int kb0, int buf) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, n_records, 0x00020000);
-    const int soff = kb0 * tok_bytes;
+    const int first = kb0 * tok_bytes;
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
       const int dst = buf * kTileB + (kBfWaves * r + wave) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16, voffs[r], soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16, voffs[r] + first,
+                                               0, 0, 0);
     }
   };
 
@@ -427,7 +429,7 @@ __device__ __forceinline__ void attn_bf16_paged_body(
     const AttnItem *__restrict__ items, const int32_t *__restrict__ segs,
     const int4 *__restrict__ kblocks, const float2 *__restrict__ angles,
     float *__restrict__ ws_o, float *__restrict__ ws_ml, int h_q, int h_kv, int tile_rows,
-    float scale_log2, int pool_bytes) {
+    float scale_log2, int pool_bytes, int pool_blocks) {
   constexpr int kRowB = D * 2;
   constexpr int kCPR = D / 8;
   constexpr int kTileB = kKB * kRowB;
@@ -540,31 +542,37 @@ __device__ __forceinline__ void attn_bf16_paged_body(
   }
 
   // Stage one K (is_v = false) or V block into LDS buffer `buf` (direct loads).
+  // Fresh rows: the block's row offset rides in the per-lane offset, which the range
+  // check sees, so rows past the fresh rows read zeros.  Pool blocks: a block past the
+  // chunk's end or an id outside the pool gets a resource of zero records (zeros); any
+  // other block lies wholly inside the pool, so its offset may ride in the scalar offset.
   auto issue = [&](int4 dsc, bool is_v, int buf) {
     if (dsc.x < 0) {
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           (void *)(is_v ? vfh : kfh), 0, n_fresh * tok_bytes, 0x00020000);
-      const int soff = dsc.y * tok_bytes;
+      const int first = dsc.y * tok_bytes;
 #pragma unroll
       for (int r = 0; r < kRounds; ++r) {
         const int dst = buf * kTileB + (kBfWaves * r + wave) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16,
-                                                 is_v ? voff_fv[r] : voff_f[r], soff, 0, 0);
+                                                 (is_v ? voff_fv[r] : voff_f[r]) + first, 0, 0, 0);
       }
     } else {
       const int32_t *sg = segs + 8 * dsc.x;
       const int len = sg[1], cid = sg[3];
       const int nb = (len + kPoolBlockRows - 1) / kPoolBlockRows;
       const int32_t *bl = block_ids + chunk_block_ptr[cid];
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)(is_v ? pool_v : pool_k), 0, pool_bytes, 0x00020000);
 #pragma unroll
       for (int r = 0; r < kRounds; ++r) {
         const int pb = (dsc.y + kRPI * (kBfWaves * r + wave)) / kPoolBlockRows;
-        const int soff = pb < nb ? bl[pb] * blk_bytes : pool_bytes;  // past the chunk: zeros
+        const int bid = pb < nb ? bl[pb] : -1;
+        const bool ok = (unsigned)bid < (unsigned)pool_blocks;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(is_v ? pool_v : pool_k), 0, ok ? pool_bytes : 0, 0x00020000);
         const int dst = buf * kTileB + (kBfWaves * r + wave) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16,
-                                                 is_v ? voff_pv[r] : voff_p[r], soff, 0, 0);
+                                                 is_v ? voff_pv[r] : voff_p[r],
+                                                 ok ? bid * blk_bytes : 0, 0, 0);
       }
     }
   };
@@ -804,10 +812,11 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_paged_kernel(
     const AttnItem *__restrict__ items, const int32_t *__restrict__ segs,
     const int4 *__restrict__ kblocks, const float2 *__restrict__ angles,
     float *__restrict__ ws_o, float *__restrict__ ws_ml, int h_q, int h_kv, int tile_rows,
-    float scale_log2, int pool_bytes) {
+    float scale_log2, int pool_bytes, int pool_blocks) {
   attn_bf16_paged_body<D, kHalf>(q, pool_k, pool_v, chunk_block_ptr, block_ids, k_fresh,
                                  v_fresh, out, rows, tiles, items, segs, kblocks, angles, ws_o,
-                                 ws_ml, h_q, h_kv, tile_rows, scale_log2, pool_bytes);
+                                 ws_ml, h_q, h_kv, tile_rows, scale_log2, pool_bytes,
+                                 pool_blocks);
 }
 
 // ======================== decode over the shared pool =========================
@@ -824,7 +833,8 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_paged_kernel(
 
 constexpr int kDecWaves = PIC_DECODE_COLS / 32;  // one 32-column MFMA block per wave
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kDecKB = PIC_DECODE_BLOCK;  // K + V double-buffered in 32 KiB (D = 128)
+constexpr int kDecKB = PIC_DECODE_BLOCK;
+constexpr int kDecStages = 2;  // K + V buffers per workgroup: 32 KiB of LDS at D = 128
 
 // Where the keys of one decode piece (part of an (item, kv head) unit) live.  Pool
 // pieces read the chunk through its block table, fresh pieces the request's recomputed
@@ -867,7 +877,8 @@ __device__ __forceinline__ void dec_attn_body(
   static_assert(kDecKB == 32 || kDecKB == 64, "one or two 32-key tiles per block");
   static_assert(kRounds * kRPI * kDecWaves == kDecKB, "direct loads must tile the block");
   static_assert(kPoolBlockRows % kRPI == 0, "one direct load stays inside a pool block");
-  __shared__ __attribute__((aligned(1024))) char lds[4 * kTileB];  // K0 K1 V0 V1
+  static_assert(kDecStages >= 2 && kDecStages <= 4, "vmcnt waits cover up to 3 blocks ahead");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kDecStages * kTileB];  // K..., V...
 
   const int u_begin = wg_ptr[blockIdx.x], u_end = wg_ptr[blockIdx.x + 1];
   const int group = h_q / h_kv;
@@ -942,8 +953,8 @@ __device__ __forceinline__ void dec_attn_body(
           __builtin_amdgcn_make_buffer_rsrc((void *)(sr.v + off), 0, rows * tok_bytes, 0x00020000);
       const int dst = buf * kTileB + (kDecWaves * r + wave) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(lds + dst), 16, ok[r], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(lds + 2 * kTileB + dst), 16,
-                                               ov[r], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(lds + kDecStages * kTileB + dst),
+                                               16, ov[r], 0, 0, 0);
     }
   };
 
@@ -969,8 +980,6 @@ __device__ __forceinline__ void dec_attn_body(
   DecSrc nxt = cur;  // unit of the next block to stage
   int n_ui = u_begin, n_j = 0;
   set_head(cur.g);
-  issue(nxt, 0, 0, nk, nv);
-  int blk = 0;  // blocks consumed so far (selects the LDS buffer)
   auto advance = [&]() {  // step (n_ui, n_j) to the next block to stage
     if (++n_j == nxt.n_blocks) {
       n_j = 0;
@@ -980,7 +989,18 @@ __device__ __forceinline__ void dec_attn_body(
       }
     }
   };
-  advance();
+  // Blocks are numbered in streaming order; block x lives in buffer x % kDecStages.
+  // `ahead` counts the staged blocks not yet consumed (the current one included).
+  int ahead = 0, stage_buf = 0;
+#pragma unroll
+  for (int i = 0; i < kDecStages - 1; ++i)
+    if (n_ui < u_end) {
+      issue(nxt, n_j, stage_buf, nk, nv);
+      advance();
+      ++ahead;
+      stage_buf = stage_buf + 1 == kDecStages ? 0 : stage_buf + 1;
+    }
+  int buf = 0;
 
   for (int ui = u_begin; ui < u_end; ++ui) {
     if (ui > u_begin) cur = load_src(ui);
@@ -1040,19 +1060,26 @@ __device__ __forceinline__ void dec_attn_body(
       for (int j = 0; j < 16; ++j) acc[d][j] = 0.f;
     float m_run = kNegInf, l_lane = 0.f;
 
-    for (int j = 0; j < cur.n_blocks; ++j, ++blk) {
-      const int buf = blk & 1;
-      if (n_ui < u_end) {  // stage the next block while this one is scored
-        issue(nxt, n_j, buf ^ 1, nk, nv);
+    for (int j = 0; j < cur.n_blocks; ++j) {
+      if (n_ui < u_end) {  // stage one more block while this one is scored
+        issue(nxt, n_j, stage_buf, nk, nv);
         advance();
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kRounds) : "memory");
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        ++ahead;
+        stage_buf = stage_buf + 1 == kDecStages ? 0 : stage_buf + 1;
       }
+      const int later = ahead - 1;  // blocks staged after this one (their loads may pend)
+      if (kDecStages > 3 && later >= 3)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * kRounds) : "memory");
+      else if (kDecStages > 2 && later == 2)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kRounds) : "memory");
+      else if (later == 1)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kRounds) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       asm volatile("s_barrier" ::: "memory");
       if (active) {  // a wave whose 32 columns are all past the item's uses only stages
         const char *Kb = lds + buf * kTileB;
-        const char *Vb = lds + (2 + buf) * kTileB;
+        const char *Vb = lds + (kDecStages + buf) * kTileB;
         f32x16 sc[kT];
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
@@ -1116,7 +1143,9 @@ __device__ __forceinline__ void dec_attn_body(
             acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[d], 0, 0, 0);
           }
       }
-      asm volatile("s_barrier" ::: "memory");  // buffer buf is refilled next
+      asm volatile("s_barrier" ::: "memory");  // buffer buf may be refilled next
+      --ahead;
+      buf = buf + 1 == kDecStages ? 0 : buf + 1;
     }
 
     // ---- partial (m, l, O) of this (use, kv head, head) ----
@@ -1495,7 +1524,7 @@ template <int D, bool kHalf>
 int launch_paged(const PlanHeader &h, const int32_t *plan_dev, const void *q, const void *pool_k,
                  const void *pool_v, const int32_t *cbp, const int32_t *bids, const void *kf,
                  const void *vf, void *out, double rope_base, float scale, void *workspace,
-                 int pool_bytes, hipStream_t s) {
+                 int64_t pool_blocks, hipStream_t s) {
   const int32_t *rows = plan_dev + h[PIC_H_O_ROWS];
   const AttnTile *tiles = reinterpret_cast<const AttnTile *>(plan_dev + h[PIC_H_O_ATTN_TILES]);
   const AttnItem *items = reinterpret_cast<const AttnItem *>(plan_dev + h[PIC_H_O_ATTN_ITEMS]);
@@ -1520,7 +1549,7 @@ int launch_paged(const PlanHeader &h, const int32_t *plan_dev, const void *q, co
                      cbp, bids, static_cast<const __bf16 *>(kf), static_cast<const __bf16 *>(vf),
                      static_cast<__bf16 *>(out), rows, tiles, items, segs, kblocks, angles, ws_o,
                      ws_ml, h[PIC_H_H_Q], h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], scale * kLog2e,
-                     pool_bytes);
+                     (int)(pool_blocks * kPoolBlockRows * h[PIC_H_H_KV] * D * 2), (int)pool_blocks);
   PIC_LAUNCH_CHECK();
   if (h[PIC_H_N_MERGE] > 0) {
     const int64_t threads = (int64_t)h[PIC_H_N_MERGE] * kM * (D / 4);
@@ -1657,10 +1686,11 @@ extern "C" int pic_selective_attn_paged(
   if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return PIC_EINVAL;
   if (dtype != PIC_BF16 || block_size != kPoolBlockRows) return PIC_EUNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PIC_EUNSUPPORTED;
+  // 32-bit buffer offsets (past-the-end loads sit at pool_bytes + one block)
   const int64_t tok_bytes = (int64_t)h[PIC_H_H_KV] * head_dim * 2;
   const int64_t pool_bytes = pool_blocks * kPoolBlockRows * tok_bytes;
-  // 32-bit buffer offsets (plus one pool block of slack past the end)
-  if (pool_bytes > 0x7fff0000LL || (int64_t)h[PIC_H_N_ROWS] * tok_bytes > 0x7fff0000LL)
+  if (pool_bytes > 0x7fff0000LL - kPoolBlockRows * tok_bytes ||
+      (int64_t)h[PIC_H_N_ROWS] * tok_bytes > 0x7fff0000LL)
     return PIC_EUNSUPPORTED;
   const int32_t *segs_h = plan_host + h[PIC_H_O_SEGS];
   for (int32_t c = 0; c < h[PIC_H_N_CHUNKS]; ++c)
@@ -1676,7 +1706,7 @@ extern "C" int pic_selective_attn_paged(
 #define PIC_PAGED(D_, H_)                                                                    \
   return launch_paged<D_, H_>(h, plan_dev, q, pool_k, pool_v, chunk_block_ptr, block_ids,     \
                               k_fresh, v_fresh, out, rope_base, scale, workspace,             \
-                              (int)pool_bytes, s)
+                              pool_blocks, s)
   if (head_dim == 128) {
     if (half) PIC_PAGED(128, true);
     PIC_PAGED(128, false);
