@@ -8,12 +8,13 @@
     python -m position_independent_kv_rope_amd.profiling traffic \
         --fetch <bench FETCH_SIZE csv> --write <bench WRITE_SIZE csv> \
         --copy-fetch <copy FETCH_SIZE csv> --copy-write <copy WRITE_SIZE csv> \
-        --kernel attn_bf16_kernel --out profiles/traffic_attn_<workload>.json \
+        --kernel attn_bf16_kernel,merge_kernel --out profiles/traffic_attn_<workload>.json \
         --sources position_independent_kv_rope_amd/csrc/pic_attn.hip
 
-``traffic`` scales the per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of a kernel by
-what the same counters read for a plain device copy of known size, and records the
-sha256 of the kernel sources so a stale measurement is not reused after a change.
+``traffic`` scales the per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the kernels of one
+call (summed) by what the same counters read for a plain device copy of known size, and
+records the sha256 of the kernel sources so a stale measurement is not reused after a
+change.
 """
 
 import argparse
@@ -22,6 +23,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -33,6 +35,9 @@ SHORT = [("attn_bf16_paged_kernel", "attn_bf16_paged"), ("paged_angles_kernel", 
 
 
 def short_name(name):
+    m = re.search(r"rope_kernelI\w+?Lb[01]ELb([01])E", name)  # rope_kernel<T, half, absolute>
+    if m:
+        return "rope_apply" if m.group(1) == "1" else "rope_delta"
     for key, s in SHORT:
         if key in name:
             return s
@@ -77,10 +82,10 @@ def traffic(args):
     cw = counters([args.copy_write])["copy (calibration)"]["WRITE_SIZE"]
     copy_kib = args.copy_bytes / 1024.0
     f_scale, w_scale = copy_kib / cf, copy_kib / cw
-    k = short_name(args.kernel)
-    fb = fetch[k]["FETCH_SIZE"] * f_scale * 1024.0
-    wb = write[k]["WRITE_SIZE"] * w_scale * 1024.0
-    rec = {"kernel": k, "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+    ks = [short_name(k) for k in args.kernel.split(",")]  # the kernels of one call, summed
+    fb = sum(fetch[k]["FETCH_SIZE"] for k in ks) * f_scale * 1024.0
+    wb = sum(write[k]["WRITE_SIZE"] for k in ks) * w_scale * 1024.0
+    rec = {"kernel": " + ".join(ks), "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
            "bytes_per_launch": fb + wb, "fetch_scale": f_scale, "write_scale": w_scale,
            "copy_bytes": args.copy_bytes, "sources": args.sources,
            "source_hash": src_hash(args.sources), "command": args.command}
