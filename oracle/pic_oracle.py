@@ -46,6 +46,10 @@ Readings of places where the pages are silent, garbled or disagree:
 9. Every recomputed row produces an output (seam outputs feed the next layer in the
    per-layer loop); the query rows are the last q of them.
 10. Zero-length chunks are legal and contribute nothing; q = 0 is legal.
+11. The layer of the multi-layer link is compute_qkv (projection, RoPE at the global
+    positions) -> splice -> attention -> x + O W_o^T; the pages do not show the rest of
+    a transformer block, and per-row maps after the attention would not change which
+    rows are recomputed or how they are spliced.
 """
 
 import math
@@ -379,6 +383,109 @@ def link_request(cached_k_chunks, cached_v_chunks, q_len, k, k_fresh, v_fresh, q
     kx, vx = splice(k_ctx, v_ctx, k_fresh, v_fresh, rows, n_total)
     out = selective_attn(q_fresh, kx, vx, rows, scale)
     return {"rows": rows, "offsets": offs, "kx": kx, "vx": vx, "out": out}
+
+
+# ---------------------------------------------------------------------------
+# The layer loop of the link ([EPIC] Step 3 runs over the model's layers): per layer
+# the recomputed rows' Q/K/V come from their hidden states with RoPE at the global
+# positions (compute_qkv), are spliced and attend, and the attention output carries
+# the rows' hidden states to the next layer.  The pages show only compute_qkv, the
+# splice and the attention of a layer; the layer here is the plainest block that
+# closes the loop: x <- x + O W_o^T (output projection plus residual), with the
+# projections in the nn.Linear layout (weight rows are output features).
+# ---------------------------------------------------------------------------
+
+
+def qkv_rope(x, w_qkv, positions, h_q, h_kv, base, layout="adjacent"):
+    """compute_qkv of [EPIC] Step 3: y = x W^T, split into Q (h_q heads), K and V (h_kv
+    heads each), Q and K rotated at ``positions`` (the global positions), V not.
+
+    x: [T, d_model]; w_qkv: [(h_q + 2 h_kv) * D, d_model].  Returns fp64
+    q [T, h_q, D], k [T, h_kv, D], v [T, h_kv, D].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_qkv, dtype=np.float64)
+    n_out = w.shape[0]
+    assert n_out % (h_q + 2 * h_kv) == 0
+    head_dim = n_out // (h_q + 2 * h_kv)
+    y = x @ w.T
+    t_count = x.shape[0]
+    q = y[:, :h_q * head_dim].reshape(t_count, h_q, head_dim)
+    k = y[:, h_q * head_dim:(h_q + h_kv) * head_dim].reshape(t_count, h_kv, head_dim)
+    v = y[:, (h_q + h_kv) * head_dim:].reshape(t_count, h_kv, head_dim)
+    return rope_rotate(q, positions, base, layout), rope_rotate(k, positions, base, layout), v
+
+
+def out_proj_residual(o, w_o, x):
+    """Next hidden state of the rows: x + O W_o^T, O [T, h_q, D] read as [T, h_q * D];
+    w_o: [d_model, h_q * D].  Returns [T, d_model] fp64."""
+    o = np.asarray(o, dtype=np.float64)
+    o2 = o.reshape(o.shape[0], -1)
+    return np.asarray(x, dtype=np.float64) + o2 @ np.asarray(w_o, dtype=np.float64).T
+
+
+def link_layers(x_rows, layers, q_len, k, h_q, h_kv, base, layout="adjacent", pos_base=0,
+                scale=None):
+    """The whole link of one request over several layers.
+
+    x_rows: [R, d_model] hidden states of the recomputed rows (ascending positions)
+    entering layer 0.  layers: one dict per layer with ``w_qkv``, ``w_o`` and the
+    request's cached chunks ``k_chunks`` (K with RoPE at local positions pos_base..)
+    and ``v_chunks``.  Per layer: compute_qkv at the global positions, rotate the
+    cached K by delta_c, splice, selective attention, output projection + residual.
+    Returns dict(rows, x) with the rows' hidden states after the last layer.
+    """
+    lens = [int(np.asarray(a).shape[0]) for a in layers[0]["k_chunks"]]
+    rows = recompute_positions(lens, q_len, k)
+    n_total = sum(lens) + int(q_len)
+    x = np.asarray(x_rows, dtype=np.float64)
+    for layer in layers:
+        q, kf, vf = qkv_rope(x, layer["w_qkv"], rows, h_q, h_kv, base, layout)
+        if lens:
+            k_ctx = rope_delta(layer["k_chunks"], base, layout, pos_base)
+            v_ctx = concat_chunks(layer["v_chunks"])
+        else:
+            k_ctx = np.zeros((0,) + kf.shape[1:])
+            v_ctx = np.zeros((0,) + vf.shape[1:])
+        kx, vx = splice(k_ctx, v_ctx, kf, vf, rows, n_total)
+        o = selective_attn(q, kx, vx, rows, scale)
+        x = out_proj_residual(o, layer["w_o"], x)
+    return {"rows": rows, "x": x}
+
+
+def prefill_layers(x_seq, weights, positions, h_q, h_kv, base, layout="adjacent", scale=None):
+    """Dense causal prefill of a token sequence through the same layers, written apart
+    from the link: every row is computed, with one explicit N x N causal mask.
+
+    x_seq: [N, d_model] layer-0 hidden states; weights: list of (w_qkv, w_o);
+    positions: [N] RoPE positions of the rows.  Run on one chunk at its local
+    positions it is [EPIC] compile_chunk (returns the per-layer cached K, V); run on
+    the whole spliced sequence at 0..N-1 it is full recompute.  Returns
+    dict(x=[N, d_model], k=[per layer [N, h_kv, D]], v=[...]).
+    """
+    x = np.asarray(x_seq, dtype=np.float64)
+    n = x.shape[0]
+    ks, vs = [], []
+    for w_qkv, w_o in weights:
+        w_qkv = np.asarray(w_qkv, dtype=np.float64)
+        head_dim = w_qkv.shape[0] // (h_q + 2 * h_kv)
+        y = x @ w_qkv.T
+        q = rope_rotate(y[:, :h_q * head_dim].reshape(n, h_q, head_dim), positions, base, layout)
+        kk = rope_rotate(y[:, h_q * head_dim:(h_q + h_kv) * head_dim].reshape(n, h_kv, head_dim),
+                         positions, base, layout)
+        vv = y[:, (h_q + h_kv) * head_dim:].reshape(n, h_kv, head_dim)
+        ks.append(kk)
+        vs.append(vv)
+        sc = (1.0 / math.sqrt(head_dim)) if scale is None else scale
+        causal = np.tril(np.ones((n, n), dtype=bool))
+        o = np.zeros((n, h_q, head_dim))
+        for h in range(h_q):
+            g = h // (h_q // h_kv)
+            s = np.where(causal, (q[:, h, :] @ kk[:, g, :].T) * sc, -np.inf)
+            s = np.exp(s - s.max(axis=1, keepdims=True))
+            o[:, h, :] = (s / s.sum(axis=1, keepdims=True)) @ vv[:, g, :]
+        x = x + o.reshape(n, h_q * head_dim) @ np.asarray(w_o, dtype=np.float64).T
+    return {"x": x, "k": ks, "v": vs}
 
 
 # ---------------------------------------------------------------------------

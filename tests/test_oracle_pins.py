@@ -526,3 +526,130 @@ def test_decode_attn_single_key_and_planted_self_exclusion():
     with_self = O.decode_attn(q, kx, vx, k_new, v_new)
     without = O.selective_attn(q[None], kx, vx, [5])[0]
     assert np.max(np.abs(with_self - without)) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# The multi-layer link: compute_qkv at global positions, splice, attention, residual
+# ---------------------------------------------------------------------------
+
+
+def _tiny_model(seed, n_layers, d_model=16, h_q=4, h_kv=2, d=4):
+    rng = np.random.default_rng(seed)
+    n_out = (h_q + 2 * h_kv) * d
+    return [(rng.standard_normal((n_out, d_model)) / math.sqrt(d_model),
+             rng.standard_normal((d_model, h_q * d)) / math.sqrt(h_q * d))
+            for _ in range(n_layers)]
+
+
+def _compiled_link(weights, x_chunks, x_query, k, base, layout, pos_base, h_q=4, h_kv=2,
+                   link=None):
+    """Compile every chunk alone at local positions pos_base.. ([EPIC] compile_chunk), then
+    link the request: returns (link rows, link x, full-prefill x of the whole sequence)."""
+    lens = [len(c) for c in x_chunks]
+    per_layer = [{"w_qkv": w, "w_o": wo, "k_chunks": [], "v_chunks": []} for w, wo in weights]
+    for xc in x_chunks:
+        comp = O.prefill_layers(xc, weights, pos_base + np.arange(len(xc)), h_q, h_kv, base, layout)
+        for layer, kc, vc in zip(per_layer, comp["k"], comp["v"]):
+            layer["k_chunks"].append(kc)
+            layer["v_chunks"].append(vc)
+    x_all = np.concatenate(list(x_chunks) + [x_query], axis=0)
+    rows = O.recompute_positions(lens, len(x_query), k)
+    res = (link or O.link_layers)(x_all[rows], per_layer, len(x_query), k, h_q, h_kv, base,
+                                  layout, pos_base)
+    full = O.prefill_layers(x_all, weights, np.arange(len(x_all)), h_q, h_kv, base, layout)
+    return res["rows"], res["x"], full["x"]
+
+
+@pytest.mark.parametrize("layout,pos_base", [("adjacent", 0), ("half", 0), ("adjacent", 4)])
+def test_link_layers_full_recompute_equals_prefill(layout, pos_base):
+    # chunks compiled alone, then linked with k >= every chunk length: every row but
+    # chunk 0's is recomputed, so after all layers the rows' hidden states equal a plain
+    # causal prefill of the whole sequence ([EPIC] full recompute; fp64 1e-10)
+    rng = np.random.default_rng(31)
+    weights = _tiny_model(32, 3)
+    x_chunks = [rng.standard_normal((n, 16)) for n in (4, 5, 5)]
+    x_query = rng.standard_normal((3, 16))
+    rows, got, full = _compiled_link(weights, x_chunks, x_query, 5, 1e4, layout, pos_base)
+    assert rows == list(range(4, 17))
+    assert np.max(np.abs(got - full[rows])) < 1e-10
+    # with chunk 0 alone and pos_base 0, even k = 0 is exact (no seam to repair)
+    rows0, got0, full0 = _compiled_link(weights, x_chunks[:1], x_query, 0, 1e4, layout, 0)
+    assert np.max(np.abs(got0 - full0[rows0])) < 1e-10
+
+
+def test_link_layers_seam_recompute_differs_from_full_recompute():
+    # k < L: cached rows keep their chunk-local context, so the link is an approximation
+    # of full recompute, and a visible one with random weights (the pins above are not
+    # vacuous)
+    rng = np.random.default_rng(33)
+    weights = _tiny_model(34, 2)
+    x_chunks = [rng.standard_normal((n, 16)) for n in (4, 5, 5)]
+    x_query = rng.standard_normal((3, 16))
+    rows, got, full = _compiled_link(weights, x_chunks, x_query, 2, 1e4, "adjacent", 0)
+    assert rows == [4, 5, 9, 10, 14, 15, 16]
+    assert np.max(np.abs(got - full[rows])) > 1e-3
+
+
+def test_link_layers_one_layer_is_link_request_plus_projection():
+    # one layer: the attention part is exactly the single-layer link of the rows' fresh
+    # Q/K/V, and the layer adds O W_o^T to the hidden states
+    rng = np.random.default_rng(35)
+    (w, wo), = _tiny_model(36, 1)
+    lens, q_len, k = [4, 5, 5], 3, 2
+    kc = [rng.standard_normal((n, 2, 4)) for n in lens]
+    vc = [rng.standard_normal((n, 2, 4)) for n in lens]
+    rows = O.recompute_positions(lens, q_len, k)
+    x = rng.standard_normal((len(rows), 16))
+    q, kf, vf = O.qkv_rope(x, w, rows, 4, 2, 1e4)
+    one = O.link_request(kc, vc, q_len, k, kf, vf, q, 1e4)
+    got = O.link_layers(x, [{"w_qkv": w, "w_o": wo, "k_chunks": kc, "v_chunks": vc}], q_len, k,
+                        4, 2, 1e4)["x"]
+    assert np.max(np.abs(got - (x + one["out"].reshape(len(rows), -1) @ wo.T))) < 1e-12
+
+
+def test_qkv_rope_split_and_rotation():
+    # the projection's output features are Q heads, then K heads, then V heads; with an
+    # identity-like weight each part is the matching slice of x, Q and K rotated at the
+    # given positions and V untouched
+    rng = np.random.default_rng(37)
+    h_q, h_kv, d = 2, 1, 4
+    x = rng.standard_normal((5, (h_q + 2 * h_kv) * d))
+    w = np.eye(x.shape[1])
+    pos = [0, 3, 7, 100, -2]
+    q, k, v = O.qkv_rope(x, w, pos, h_q, h_kv, 1e4)
+    assert np.allclose(q[0], x[0, :8].reshape(2, 4), atol=1e-15)  # position 0: identity
+    assert np.allclose(v, x[:, 12:].reshape(5, 1, 4), atol=1e-15)
+    # D = 4, pair i = (2i, 2i+1) rotated by p * theta_i: complex multiplication
+    theta = [1.0, 1e4 ** -0.5]
+    for t, p in enumerate(pos):
+        for i in range(2):
+            z = complex(x[t, 8 + 2 * i], x[t, 9 + 2 * i]) * cmath.exp(1j * p * theta[i])
+            assert abs(complex(k[t, 0, 2 * i], k[t, 0, 2 * i + 1]) - z) < 1e-12
+
+
+@pytest.mark.parametrize("mistake", ["local_positions", "no_residual", "layer_order"])
+def test_planted_link_layer_mistakes_fail(mistake):
+    rng = np.random.default_rng(39)
+    weights = _tiny_model(40, 3)
+    x_chunks = [rng.standard_normal((n, 16)) for n in (4, 5, 5)]
+    x_query = rng.standard_normal((3, 16))
+
+    def wrong(x_rows, layers, q_len, k, h_q, h_kv, base, layout, pos_base, scale=None):
+        lens = [len(c) for c in layers[0]["k_chunks"]]
+        rows = O.recompute_positions(lens, q_len, k)
+        offs = O.chunk_offsets(lens)
+        local = [r - max(o for o in offs[:-1] if o <= r) if r < offs[-1] else r for r in rows]
+        x = np.asarray(x_rows, dtype=np.float64)
+        seq = layers[::-1] if mistake == "layer_order" else layers
+        for layer in seq:
+            pos = local if mistake == "local_positions" else rows
+            q, kf, vf = O.qkv_rope(x, layer["w_qkv"], pos, h_q, h_kv, base, layout)
+            kx, vx = O.splice(O.rope_delta(layer["k_chunks"], base, layout, pos_base),
+                              O.concat_chunks(layer["v_chunks"]), kf, vf, rows, offs[-1] + q_len)
+            o = O.selective_attn(q, kx, vx, rows)
+            x = (o.reshape(len(rows), -1) @ layer["w_o"].T if mistake == "no_residual"
+                 else O.out_proj_residual(o, layer["w_o"], x))
+        return {"rows": rows, "x": x}
+
+    rows, got, full = _compiled_link(weights, x_chunks, x_query, 5, 1e4, "adjacent", 0, link=wrong)
+    assert np.max(np.abs(got - full[rows])) > 1e-3
