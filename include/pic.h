@@ -306,6 +306,60 @@ int pic_decode_attn_paged(const int32_t *plan_host, const int32_t *plan_dev, con
                           double rope_base, float scale, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/*
+ * pic_qkv_rope -- compute_qkv of the recomputed rows.                [EPIC] Step 2-3
+ * The rows' Q, K and V from their hidden states, with RoPE at their global positions:
+ * y = x W^T for x [n_rows][d_model] (bf16, plan row order) and w_qkv
+ * [(h_q + 2 h_kv) * head_dim][d_model] (bf16, one row per output feature: Q heads,
+ * then K heads, then V heads); q [n_rows][h_q][head_dim], k_fresh/v_fresh
+ * [n_rows][h_kv][head_dim] receive bf16 results, Q and K rotated at p_r (the plan's
+ * rows) with theta_i = rope_base^(-2i/head_dim) in rope_layout, V not rotated.  fp32
+ * accumulation; RoPE applied before the one bf16 rounding.  workspace >=
+ * pic_qkv_workspace_bytes (per-row cos/sin table).  bf16 only, head_dim in {64, 128},
+ * d_model % 64 == 0, h_q*head_dim and h_kv*head_dim multiples of 128, positions < 2^24;
+ * else PIC_EUNSUPPORTED.  Errors: PIC_EINVAL (null pointers, bad layout/base),
+ * PIC_ENOSPC (workspace), PIC_EDEVICE.  Device pointers; caller-owned buffers.
+ */
+size_t pic_qkv_workspace_bytes(const int32_t *plan_host, int32_t head_dim);
+int pic_qkv_rope(const int32_t *plan_host, const int32_t *plan_dev, const void *x,
+                 const void *w_qkv, void *q, void *k_fresh, void *v_fresh, int32_t dtype,
+                 int32_t d_model, int32_t head_dim, int32_t rope_layout, double rope_base,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pic_out_proj -- next hidden state of the recomputed rows.          [EPIC] Step 3
+ * x <- x + O W_o^T in place: o [n_rows][h_q][head_dim] (the attention output, read as
+ * [n_rows][h_q*head_dim]), w_o [d_model][h_q*head_dim] (bf16, one row per output
+ * feature), x [n_rows][d_model] bf16; fp32 accumulation and residual add, one bf16
+ * rounding.  The pages show only compute_qkv, the splice and the attention of a
+ * layer; this output projection plus residual is the plainest block that carries
+ * the rows to the next layer.  bf16 only; d_model % 128 == 0, h_q*head_dim % 64 == 0;
+ * else PIC_EUNSUPPORTED.  Errors as pic_qkv_rope.
+ */
+int pic_out_proj(const int32_t *plan_host, const void *o, const void *w_o, void *x,
+                 int32_t dtype, int32_t d_model, int32_t head_dim, void *stream);
+
+/*
+ * pic_link -- the whole link over n_layers layers (contiguous K/V).  [EPIC] Step 1-3
+ * For l = 0 .. n_layers-1 on one stream: pic_rope_delta(k_cache[l]);
+ * pic_qkv_rope(x, w_qkv[l]) -> q, k_fresh, v_fresh; pic_splice(k_cache[l], v_cache[l]);
+ * pic_selective_attn(q, k_cache[l], v_cache[l]) -> o; pic_out_proj(o, w_o[l], x).
+ * w_qkv, w_o, k_cache, v_cache: host arrays of n_layers device pointers (each layer's
+ * weights, and its spliced K/V buffers [n_tokens][h_kv][head_dim] holding the cached
+ * chunks at their local positions, which are rotated and spliced in place).  x: the
+ * rows' hidden states entering layer 0, [n_rows][d_model], updated in place to the
+ * last layer's output.  q/k_fresh/v_fresh/o: caller scratch of the per-layer shapes.
+ * workspace >= pic_link_workspace_bytes.  Every argument check of the per-layer calls
+ * runs before the first launch; errors as those calls.  bf16 only.
+ */
+size_t pic_link_workspace_bytes(const int32_t *plan_host, int32_t head_dim);
+int pic_link(const int32_t *plan_host, const int32_t *plan_dev, int32_t n_layers, void *x,
+             const void *const *w_qkv, const void *const *w_o, void *const *k_cache,
+             void *const *v_cache, void *q, void *k_fresh, void *v_fresh, void *o,
+             int32_t dtype, int32_t d_model, int32_t head_dim, int32_t rope_layout,
+             double rope_base, float scale, void *workspace, size_t workspace_bytes,
+             void *stream);
+
 /* Short static description of a status code. */
 const char *pic_strerror(int status);
 

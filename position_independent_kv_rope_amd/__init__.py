@@ -35,7 +35,8 @@ PIC_DECODE_WG_PER_CU = 4
 EXPORTED = ("pic_build_index", "pic_rope_delta", "pic_rope_apply", "pic_splice",
             "pic_attn_workspace_bytes",
             "pic_selective_attn", "pic_selective_attn_paged", "pic_decode_workspace_bytes",
-            "pic_decode_attn_paged", "pic_strerror")
+            "pic_decode_attn_paged", "pic_qkv_workspace_bytes", "pic_qkv_rope",
+            "pic_out_proj", "pic_link_workspace_bytes", "pic_link", "pic_strerror")
 
 
 class PicError(RuntimeError):
@@ -81,6 +82,17 @@ def lib():
     L.pic_decode_attn_paged.argtypes = [p, p, p, p, p, p, p, i64, i32, p, i32, p, p, p, p, i32,
                                         i32, i32, f64, f32, p, sz, p]
     L.pic_decode_attn_paged.restype = ctypes.c_int
+    L.pic_qkv_workspace_bytes.argtypes = [p, i32]
+    L.pic_qkv_workspace_bytes.restype = sz
+    L.pic_qkv_rope.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, f64, p, sz, p]
+    L.pic_qkv_rope.restype = ctypes.c_int
+    L.pic_out_proj.argtypes = [p, p, p, p, i32, i32, i32, p]
+    L.pic_out_proj.restype = ctypes.c_int
+    L.pic_link_workspace_bytes.argtypes = [p, i32]
+    L.pic_link_workspace_bytes.restype = sz
+    L.pic_link.argtypes = [p, p, i32, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, f64, f32,
+                           p, sz, p]
+    L.pic_link.restype = ctypes.c_int
     L.pic_strerror.argtypes = [ctypes.c_int]
     L.pic_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -418,3 +430,91 @@ def pic_decode_attn_paged(plan, q_new, k_new, v_new, pool_k, pool_v, chunk_block
         float(rope_base), float(scale), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check("pic_decode_attn_paged", st)
+
+
+def _bytes_workspace(n, device):
+    import torch
+    return torch.empty(max(1, (int(n) + 3) // 4), dtype=torch.float32, device=device)
+
+
+def pic_qkv_rope(plan, x, w_qkv, q, k_fresh, v_fresh, rope_base, layout=PIC_ROPE_ADJACENT,
+                 workspace=None, stream=None):
+    """compute_qkv of the recomputed rows: q/k_fresh/v_fresh from x [n_rows, d_model] and
+    w_qkv [(h_q + 2 h_kv) * D, d_model], Q and K rotated at the rows' global positions."""
+    d = int(q.shape[2])
+    d_model = int(x.shape[1])
+    hq, hkv = plan[H_H_Q], plan[H_H_KV]
+    if x.shape[0] != plan.n_rows or q.shape != (plan.n_rows, hq, d):
+        raise ValueError("x/q shapes do not match the plan")
+    if k_fresh.shape != (plan.n_rows, hkv, d) or v_fresh.shape != k_fresh.shape:
+        raise ValueError("k_fresh/v_fresh must be [n_rows, h_kv, D]")
+    if w_qkv.shape != ((hq + 2 * hkv) * d, d_model):
+        raise ValueError("w_qkv must be [(h_q + 2 h_kv) * D, d_model]")
+    for t in (w_qkv, q, k_fresh, v_fresh):
+        if t.dtype != x.dtype:
+            raise ValueError("all tensors must share one dtype")
+    if workspace is None:
+        workspace = _bytes_workspace(lib().pic_qkv_workspace_bytes(plan.host_ptr(), d), x.device)
+    st = lib().pic_qkv_rope(plan.host_ptr(), plan.dev_ptr(), _dev(x, "x"), _dev(w_qkv, "w_qkv"),
+                            _dev(q, "q"), _dev(k_fresh, "k_fresh"), _dev(v_fresh, "v_fresh"),
+                            _dtype_code(x), d_model, d, int(layout), float(rope_base),
+                            _dev(workspace, "workspace"),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("pic_qkv_rope", st)
+
+
+def pic_out_proj(plan, o, w_o, x, stream=None):
+    """x += o W_o^T in place (o [n_rows, h_q, D], w_o [d_model, h_q * D])."""
+    d = int(o.shape[2])
+    d_model = int(x.shape[1])
+    if o.shape != (plan.n_rows, plan[H_H_Q], d) or x.shape[0] != plan.n_rows:
+        raise ValueError("o/x shapes do not match the plan")
+    if w_o.shape != (d_model, plan[H_H_Q] * d):
+        raise ValueError("w_o must be [d_model, h_q * D]")
+    if w_o.dtype != x.dtype or o.dtype != x.dtype:
+        raise ValueError("all tensors must share one dtype")
+    st = lib().pic_out_proj(plan.host_ptr(), _dev(o, "o"), _dev(w_o, "w_o"), _dev(x, "x"),
+                            _dtype_code(x), d_model, d, _stream(stream))
+    _check("pic_out_proj", st)
+
+
+def link_workspace(plan, head_dim, device="cuda"):
+    """Workspace tensor for pic_link."""
+    return _bytes_workspace(lib().pic_link_workspace_bytes(plan.host_ptr(), int(head_dim)), device)
+
+
+def pic_link(plan, x, w_qkv, w_o, k_cache, v_cache, q, k_fresh, v_fresh, o, rope_base,
+             layout=PIC_ROPE_ADJACENT, scale=None, workspace=None, stream=None):
+    """The whole link over len(w_qkv) layers: per layer rope-delta, compute_qkv, splice,
+    selective attention and output projection; x (the rows' hidden states) in place."""
+    n_layers = len(w_qkv)
+    if not (len(w_o) == len(k_cache) == len(v_cache) == n_layers):
+        raise ValueError("one w_qkv, w_o, k_cache and v_cache per layer")
+    d = int(q.shape[2])
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    d_model = int(x.shape[1])
+    hq, hkv = plan[H_H_Q], plan[H_H_KV]
+    if x.shape[0] != plan.n_rows or q.shape != (plan.n_rows, hq, d) or o.shape != q.shape:
+        raise ValueError("x/q/o shapes do not match the plan")
+    if k_fresh.shape != (plan.n_rows, hkv, d) or v_fresh.shape != k_fresh.shape:
+        raise ValueError("k_fresh/v_fresh must be [n_rows, h_kv, D]")
+    for l in range(n_layers):
+        if w_qkv[l].shape != ((hq + 2 * hkv) * d, d_model) or w_o[l].shape != (d_model, hq * d):
+            raise ValueError("layer %d weight shapes" % l)
+        if k_cache[l].shape != (plan.n_tokens, hkv, d) or v_cache[l].shape != k_cache[l].shape:
+            raise ValueError("layer %d K/V must be [n_tokens, h_kv, D]" % l)
+    for t in list(w_qkv) + list(w_o) + list(k_cache) + list(v_cache) + [q, k_fresh, v_fresh, o]:
+        if t.dtype != x.dtype:
+            raise ValueError("all tensors must share one dtype")
+    arr = lambda ts, name: (ctypes.c_void_p * max(1, n_layers))(*[_dev(t, name).value for t in ts])
+    if workspace is None:
+        workspace = link_workspace(plan, d, x.device)
+    st = lib().pic_link(plan.host_ptr(), plan.dev_ptr(), n_layers, _dev(x, "x"),
+                        arr(w_qkv, "w_qkv"), arr(w_o, "w_o"), arr(k_cache, "k_cache"),
+                        arr(v_cache, "v_cache"), _dev(q, "q"), _dev(k_fresh, "k_fresh"),
+                        _dev(v_fresh, "v_fresh"), _dev(o, "o"), _dtype_code(x), d_model, d,
+                        int(layout), float(rope_base), float(scale),
+                        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                        _stream(stream))
+    _check("pic_link", st)

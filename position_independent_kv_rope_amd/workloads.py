@@ -175,6 +175,28 @@ def decode_tensors(wl):
             draw((n, wl.h_kv, wl.head_dim), wl.seed * 7 + 8, wl.torch_dtype, wl.value_scale))
 
 
+def link_tensors(wl, n_layers, d_model, n_rows):
+    """A random model for the multi-layer link (no trained weights exist here).
+
+    Returns (x0, w_qkv, w_o, k_cache, v_cache): x0 [n_rows, d_model] layer-0 hidden
+    states of the recomputed rows (N(0, 1)); per layer w_qkv [(Hq + 2 Hkv) D, d_model]
+    and w_o [d_model, Hq D] (nn.Linear layout, N(0, 1/fan_in) so activations stay
+    O(1)), and the cached K/V buffers [n_tokens, Hkv, D] as context_tensors lays
+    them out.  ``n_rows`` is supplied by the caller."""
+    hq, hkv, d = wl.h_q, wl.h_kv, wl.head_dim
+    base = wl.seed * 7 + 100
+    x0 = draw((n_rows, d_model), base, wl.torch_dtype)
+    w_qkv, w_o, kc, vc = [], [], [], []
+    shape = (wl.n_tokens, hkv, d)
+    for l in range(n_layers):
+        s = base + 10 * (l + 1)
+        w_qkv.append(draw(((hq + 2 * hkv) * d, d_model), s, wl.torch_dtype, 1.0 / np.sqrt(d_model)))
+        w_o.append(draw((d_model, hq * d), s + 1, wl.torch_dtype, 1.0 / np.sqrt(hq * d)))
+        kc.append(draw(shape, s + 2, wl.torch_dtype, wl.value_scale))
+        vc.append(draw(shape, s + 3, wl.torch_dtype, wl.value_scale))
+    return x0, w_qkv, w_o, kc, vc
+
+
 CONFIGS = {
     "worked_example": worked_example,
     "rag_single": rag_single,

@@ -111,6 +111,53 @@ def test_device_entry_points_reject_bad_arguments_without_launching():
     assert L.pic_attn_workspace_bytes(bp, 128) == 0
 
 
+def test_link_entry_points_reject_bad_arguments_without_launching():
+    L = P.lib()
+    plan = P.pic_build_index([[40, 50]], [7], 2, 8, 2)  # G = 4, h_kv * 128 = 256
+    hp = plan.host_ptr()
+    bogus = np.zeros(64, dtype=np.int32)
+    bp = bogus.ctypes.data_as(ctypes.c_void_p)
+    f = ctypes.c_void_p(0x1000)
+    ws = P.lib().pic_qkv_workspace_bytes(hp, 128)
+    assert ws >= plan.n_rows * 64 * 8 and L.pic_qkv_workspace_bytes(bp, 128) == 0
+    qkv = lambda *a: L.pic_qkv_rope(*a)
+    ok = (hp, f, f, f, f, f, f, P.PIC_BF16, 256, 128, 0, 1e4, f, ws, None)
+    def with_(i, v):
+        a = list(ok)
+        a[i] = v
+        return qkv(*a)
+    assert with_(0, bp) == P.PIC_EINVAL                 # not a plan
+    assert with_(7, 9) == P.PIC_EINVAL                  # dtype
+    assert with_(7, P.PIC_F32) == P.PIC_EUNSUPPORTED    # the GEMMs are bf16
+    assert with_(9, 96) == P.PIC_EUNSUPPORTED           # head_dim
+    assert with_(8, 200) == P.PIC_EUNSUPPORTED          # d_model % 64
+    assert with_(10, 3) == P.PIC_EINVAL                 # layout
+    assert with_(11, 0.0) == P.PIC_EINVAL               # base
+    assert with_(2, None) == P.PIC_EINVAL               # x
+    assert with_(12, None) == P.PIC_EINVAL              # workspace
+    assert with_(13, ws - 1) == P.PIC_ENOSPC
+    small = P.pic_build_index([[40, 50]], [7], 2, 1, 1)  # h_q * 64 = 64: not whole tiles
+    assert L.pic_qkv_rope(small.host_ptr(), f, f, f, f, f, f, P.PIC_BF16, 256, 64, 0, 1e4, f,
+                          ws, None) == P.PIC_EUNSUPPORTED
+    assert L.pic_out_proj(hp, f, f, f, P.PIC_BF16, 192, 128, None) == P.PIC_EUNSUPPORTED
+    assert L.pic_out_proj(hp, None, f, f, P.PIC_BF16, 256, 128, None) == P.PIC_EINVAL
+    assert L.pic_out_proj(bp, f, f, f, P.PIC_BF16, 256, 128, None) == P.PIC_EINVAL
+    # pic_link: a bad layer pointer or short workspace is refused before any launch
+    arr = (ctypes.c_void_p * 2)(0x1000, 0x1000)
+    bad = (ctypes.c_void_p * 2)(0x1000, None)
+    lws = L.pic_link_workspace_bytes(hp, 128)
+    assert lws >= ws
+    link = lambda wq, wsz, dt=P.PIC_BF16, sc=0.088: L.pic_link(
+        hp, f, 2, f, wq, arr, arr, arr, f, f, f, f, dt, 256, 128, 0, 1e4, sc, f, wsz, None)
+    assert link(bad, lws) == P.PIC_EINVAL
+    assert link(arr, lws - 1) == P.PIC_ENOSPC
+    assert link(arr, lws, dt=P.PIC_F32) == P.PIC_EUNSUPPORTED
+    assert link(arr, lws, sc=0.0) == P.PIC_EINVAL
+    paged = P.pic_build_index([[40, 50]], [7], 2, 8, 2, chunk_ids_per_req=[[0, 1]])
+    assert L.pic_link(paged.host_ptr(), f, 2, f, arr, arr, arr, arr, f, f, f, f, P.PIC_BF16, 256,
+                      128, 0, 1e4, 0.088, f, lws, None) == P.PIC_EINVAL
+
+
 # ---------------------------------------------------------------------------
 # Planner vs oracle
 # ---------------------------------------------------------------------------
