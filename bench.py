@@ -49,6 +49,12 @@ def parse():
     ap.add_argument("--decode", action="store_true",
                     help="shared_pool only: time one decode step of every request "
                          "(pic_decode_attn_paged) instead of the link")
+    ap.add_argument("--link-layers", type=int, default=0,
+                    help="contiguous workloads: time the whole multi-layer link (pic_link: "
+                         "per layer rope-delta, compute_qkv, splice, attention, output "
+                         "projection) of a random model with this many layers")
+    ap.add_argument("--d-model", type=int, default=0,
+                    help="model width for --link-layers (default h_q * head_dim)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="recomputed rows of request 0 the oracle times (0 = all)")
@@ -418,6 +424,163 @@ def bench_decode(args, wl):
     print(json.dumps(rec), flush=True)
 
 
+def bench_link(args, wl):
+    """The whole link of a random model with args.link_layers layers: per step the host
+    planner, the plan upload and one pic_link call (per layer: rope-delta of that layer's
+    cached K, compute_qkv of the recomputed rows at their global positions, splice,
+    selective attention, output projection + residual)."""
+    import torch
+    import position_independent_kv_rope_amd as P
+    from position_independent_kv_rope_amd import workloads as W
+    from oracle import pic_oracle as O
+    n_layers = args.link_layers
+    D, hq, hkv = wl.head_dim, wl.h_q, wl.h_kv
+    d_model = args.d_model or hq * D
+    reqs = [r.chunk_lens for r in wl.requests]
+    qs = [r.q_len for r in wl.requests]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = P.pic_build_index(reqs, qs, wl.k, hq, hkv, n_cu=n_cu)
+    x0_h, wq_h, wo_h, kc_h, vc_h = W.link_tensors(wl, n_layers, d_model, plan.n_rows)
+    dev = "cuda"
+    x = x0_h.to(dev)
+    wq = [t.to(dev) for t in wq_h]
+    wo = [t.to(dev) for t in wo_h]
+    kc = [t.to(dev) for t in kc_h]
+    vc = [t.to(dev) for t in vc_h]
+    q = torch.empty((plan.n_rows, hq, D), dtype=wl.torch_dtype, device=dev)
+    kf = torch.empty((plan.n_rows, hkv, D), dtype=wl.torch_dtype, device=dev)
+    vf, o = torch.empty_like(kf), torch.empty_like(q)
+    ws = P.link_workspace(plan, D, dev)
+    qkv_ws = P._bytes_workspace(P.lib().pic_qkv_workspace_bytes(plan.host_ptr(), D), dev)
+    attn_ws = P.attn_workspace(plan, D, dev)
+    uploader = PlanUploader(plan.words.size, dev)
+    torch.cuda.synchronize()
+
+    rows = plan.rows.astype(np.int64)
+    attn_flops = 4.0 * D * hq * float(np.sum(rows + 1))
+    qkv_flops = 2.0 * plan.n_rows * d_model * (hq + 2 * hkv) * D
+    out_flops = 2.0 * plan.n_rows * hq * D * d_model
+    link_flops = n_layers * (attn_flops + qkv_flops + out_flops)
+    s = wl.torch_dtype.itemsize
+    attn_bytes = 2.0 * s * hkv * D * plan.n_tokens + 2.0 * s * hq * D * plan.n_rows
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    plan_s = []
+
+    def step(i=None):
+        t0 = time.perf_counter()
+        p = P.pic_build_index(reqs, qs, wl.k, hq, hkv, n_cu=n_cu)
+        plan_s.append(time.perf_counter() - t0)
+        uploader.upload(p)
+        e = ev[i] if i is not None else None
+        if e: e[0].record()
+        P.pic_link(p, x, wq, wo, kc, vc, q, kf, vf, o, wl.rope_base, workspace=ws)
+        if e: e[1].record()
+
+    # the caches, weights and hidden states stay resident; repeated steps rotate the
+    # caches again and grow the residual stream, which changes no launch or byte count
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    t_link = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+    # per-kernel breakdown: the same entry points pic_link calls, one event between each
+    names = ("rope_delta", "qkv_rope", "splice", "selective_attn", "out_proj")
+    reps = 3
+    plan.to_device()
+    bev = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_layers)]
+           for _ in range(reps)]
+    for rr in range(reps):
+        for l in range(n_layers):
+            e = bev[rr][l]
+            e[0].record()
+            P.pic_rope_delta(plan, kc[l], wl.rope_base)
+            e[1].record()
+            P.pic_qkv_rope(plan, x, wq[l], q, kf, vf, wl.rope_base, workspace=qkv_ws)
+            e[2].record()
+            P.pic_splice(plan, kc[l], vc[l], kf, vf)
+            e[3].record()
+            P.pic_selective_attn(plan, q, kc[l], vc[l], o, workspace=attn_ws)
+            e[4].record()
+            P.pic_out_proj(plan, o, wo[l], x)
+            e[5].record()
+    torch.cuda.synchronize()
+    t = {n: float(np.mean([bev[rr][l][j].elapsed_time(bev[rr][l][j + 1])
+                           for rr in range(reps) for l in range(n_layers)]))
+         for j, n in enumerate(names)}
+    attn_tflops = attn_flops / (t["selective_attn"] * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    rec = {
+        "metric": METRIC,
+        "value": round(plan.n_tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload + "_link", "requests": len(wl.requests),
+                   "tokens": plan.n_tokens, "recomputed_rows": plan.n_rows, "k": wl.k,
+                   "layers": n_layers, "d_model": d_model, "h_q": hq, "h_kv": hkv,
+                   "head_dim": D, "rope_base": wl.rope_base, "parallelism": "none (1 GPU)"},
+        "link_ms": round(t_link, 4),
+        "link_tflops": round(link_flops / (t_link * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
+                     "traffic": load_traffic("attn", args.workload + "_k%d" % wl.k),
+                     "kernel": "pic_selective_attn call (attn_bf16_kernel + merge_kernel), "
+                               "per layer",
+                     "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes},
+        "kernels": {
+            "rope_delta": {"ms": round(t["rope_delta"], 4)},
+            "qkv_rope": {"ms": round(t["qkv_rope"], 4), "flops": qkv_flops,
+                         "TFLOP_s": round(qkv_flops / (t["qkv_rope"] * 1e-3) / 1e12, 2)},
+            "splice": {"ms": round(t["splice"], 4)},
+            "selective_attn": {"ms": round(t["selective_attn"], 4), "flops": attn_flops,
+                               "TFLOP_s": round(attn_tflops, 2)},
+            "out_proj": {"ms": round(t["out_proj"], 4), "flops": out_flops,
+                         "TFLOP_s": round(out_flops / (t["out_proj"] * 1e-3) / 1e12, 2)},
+            "per_layer_ms": round(sum(t.values()), 4),
+            "host_plan_ms": round(1e3 * float(np.mean(plan_s)), 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        # the oracle's link of request 0 through the first (up to) two layers, scaled to
+        # all layers: compute_qkv, rotation, splice, attention, output projection
+        r = wl.requests[0]
+        f64 = lambda t: t.to(torch.float64).numpy()
+        offs = O.chunk_offsets(r.chunk_lens)
+        n_run = min(2, n_layers)
+        r0, r1 = int(plan.req_row_ptr[0]), int(plan.req_row_ptr[1])
+        t1 = time.perf_counter()
+        layers = [{"w_qkv": f64(wq_h[l]), "w_o": f64(wo_h[l]),
+                   "k_chunks": [f64(kc_h[l][offs[c]:offs[c + 1]]) for c in range(len(r.chunk_lens))],
+                   "v_chunks": [f64(vc_h[l][offs[c]:offs[c + 1]]) for c in range(len(r.chunk_lens))]}
+                  for l in range(n_run)]
+        O.link_layers(f64(x0_h[r0:r1]), layers, r.q_len, wl.k, hq, hkv, wl.rope_base)
+        dt = (time.perf_counter() - t1) * n_layers / n_run
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        n0 = sum(r.chunk_lens) + r.q_len
+        rec["cpu_baseline"] = {"value": round(n0 / dt, 1), "unit": "tokens/s", "cores": int(threads),
+                               "kind": "oracle", "seconds": round(dt, 3),
+                               "sample": "request 0 (%d tokens) through %d of the %d layers, "
+                                         "scaled to all: compute_qkv, rotation, splice, "
+                                         "attention, output projection" % (n0, n_run, n_layers),
+                               "host_cpus": os.cpu_count()}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -440,6 +603,8 @@ def main():
     if args.decode:
         print("--decode needs --workload shared_pool", file=sys.stderr)
         sys.exit(2)
+    if args.link_layers > 0:
+        return bench_link(args, wl)
     reqs = [r.chunk_lens for r in wl.requests]
     qs = [r.q_len for r in wl.requests]
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count

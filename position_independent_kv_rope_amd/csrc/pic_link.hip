@@ -53,10 +53,9 @@ struct QkvOut {
 };
 
 template <int kEpi, int D, bool kHalf>
-__global__ __launch_bounds__(kGThreads, 2) void gemm_nt_kernel(const __bf16 *__restrict__ A,
-                                                               const __bf16 *__restrict__ W,
-                                                               int M, int K, QkvOut qo,
-                                                               __bf16 *__restrict__ x) {
+__device__ __forceinline__ void gemm_nt_body(const __bf16 *__restrict__ A,
+                                             const __bf16 *__restrict__ W, int M, int K,
+                                             QkvOut qo, __bf16 *__restrict__ x) {
   __shared__ __attribute__((aligned(1024))) char lds[kGLdsBytes];
   const int m0 = blockIdx.x * kGT, n0 = blockIdx.y * kGT;
   const int lane = threadIdx.x & 63;
@@ -236,6 +235,21 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_nt_kernel(const __bf16 *__r
   }
 }
 
+template <int D, bool kHalf>
+__global__ __launch_bounds__(kGThreads, 2) void qkv_rope_gemm_kernel(const __bf16 *__restrict__ x,
+                                                                     const __bf16 *__restrict__ w,
+                                                                     int M, int K, QkvOut qo) {
+  gemm_nt_body<kEpiQkvRope, D, kHalf>(x, w, M, K, qo, nullptr);
+}
+
+template <int D>
+__global__ __launch_bounds__(kGThreads, 2) void out_proj_gemm_kernel(const __bf16 *__restrict__ o,
+                                                                     const __bf16 *__restrict__ w,
+                                                                     int M, int K,
+                                                                     __bf16 *__restrict__ x) {
+  gemm_nt_body<kEpiResidual, D, false>(o, w, M, K, QkvOut{}, x);
+}
+
 // cos/sin of p_r * theta_i for every recomputed row r and pair i
 __global__ __launch_bounds__(256) void row_angles_kernel(float2 *__restrict__ cs,
                                                          const int32_t *__restrict__ rows,
@@ -281,9 +295,9 @@ int launch_qkv(const PlanHeader &h, const int32_t *plan_dev, const void *x, cons
   const int n_out = (h[PIC_H_H_Q] + 2 * h[PIC_H_H_KV]) * D;
   QkvOut qo{static_cast<__bf16 *>(q), static_cast<__bf16 *>(kf), static_cast<__bf16 *>(vf), cs,
             h[PIC_H_H_Q], h[PIC_H_H_KV]};
-  hipLaunchKernelGGL((gemm_nt_kernel<kEpiQkvRope, D, kHalf>), dim3((M + kGT - 1) / kGT, n_out / kGT),
+  hipLaunchKernelGGL((qkv_rope_gemm_kernel<D, kHalf>), dim3((M + kGT - 1) / kGT, n_out / kGT),
                      dim3(kGThreads), 0, s, static_cast<const __bf16 *>(x),
-                     static_cast<const __bf16 *>(w), M, d_model, qo, (__bf16 *)nullptr);
+                     static_cast<const __bf16 *>(w), M, d_model, qo);
   PIC_LAUNCH_CHECK();
   return PIC_OK;
 }
@@ -338,17 +352,14 @@ extern "C" int pic_out_proj(const int32_t *plan_host, const void *o, const void 
   if (M == 0) return PIC_OK;
   if (!o || !w_o || !x) return PIC_EINVAL;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  QkvOut none{};
   if (head_dim == 128)
-    hipLaunchKernelGGL((gemm_nt_kernel<kEpiResidual, 128, false>),
-                       dim3((M + kGT - 1) / kGT, d_model / kGT), dim3(kGThreads), 0, s,
-                       static_cast<const __bf16 *>(o), static_cast<const __bf16 *>(w_o), M, k_in,
-                       none, static_cast<__bf16 *>(x));
+    hipLaunchKernelGGL((out_proj_gemm_kernel<128>), dim3((M + kGT - 1) / kGT, d_model / kGT),
+                       dim3(kGThreads), 0, s, static_cast<const __bf16 *>(o),
+                       static_cast<const __bf16 *>(w_o), M, k_in, static_cast<__bf16 *>(x));
   else
-    hipLaunchKernelGGL((gemm_nt_kernel<kEpiResidual, 64, false>),
-                       dim3((M + kGT - 1) / kGT, d_model / kGT), dim3(kGThreads), 0, s,
-                       static_cast<const __bf16 *>(o), static_cast<const __bf16 *>(w_o), M, k_in,
-                       none, static_cast<__bf16 *>(x));
+    hipLaunchKernelGGL((out_proj_gemm_kernel<64>), dim3((M + kGT - 1) / kGT, d_model / kGT),
+                       dim3(kGThreads), 0, s, static_cast<const __bf16 *>(o),
+                       static_cast<const __bf16 *>(w_o), M, k_in, static_cast<__bf16 *>(x));
   PIC_LAUNCH_CHECK();
   return PIC_OK;
 }

@@ -27,7 +27,9 @@ import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SHORT = [("attn_bf16_paged_kernel", "attn_bf16_paged"), ("paged_angles_kernel", "paged_angles"),
+SHORT = [("qkv_rope_gemm_kernel", "qkv_rope_gemm"), ("out_proj_gemm_kernel", "out_proj_gemm"),
+         ("row_angles_kernel", "row_angles"),
+         ("attn_bf16_paged_kernel", "attn_bf16_paged"), ("paged_angles_kernel", "paged_angles"),
          ("dec_attn_kernel", "dec_attn"), ("dec_merge_kernel", "dec_merge"),
          ("attn_bf16_kernel", "attn_bf16"), ("attn_f32_kernel", "attn_f32"),
          ("merge_kernel", "merge"), ("rope_delta_kernel", "rope_delta"),
