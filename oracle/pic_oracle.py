@@ -17,8 +17,10 @@ LegoLink / seam-window recompute, written from these pages:
   section 3.2 (scheme B: cache K before RoPE, apply RoPE at the target positions on a
   hit), section 3.3 (scheme C, rotary correction by a delta rotation) and footnote 3
   (HF Llama ``inv_freq``).
-* [HYPIC] joto.ai article on HYPIC: section 2.2 (seam window of w tokens at the
-  head of every internal segment, default w = 8).
+* [HYPIC] joto.ai article on HYPIC: section 2.1 (linear layers: cached segment
+  transition T_C and zero-init state S(C|0), composed as T(C2) S(C1) + S(C2)) and
+  section 2.2 (seam window of w tokens at the head of every internal segment,
+  default w = 8).
 * [KV-scratch] "KV cache 从零实现：两层 Decoder、位置偏移与正确性验证": section on the
   offset causal mask (allowed[i, j] = [j <= P + i]) and the equivalence-testing
   method (fp64 re-runs, error injection).
@@ -486,6 +488,48 @@ def prefill_layers(x_seq, weights, positions, h_q, h_kv, base, layout="adjacent"
             o[:, h, :] = (s / s.sum(axis=1, keepdims=True)) @ vv[:, g, :]
         x = x + o.reshape(n, h_q * head_dim) @ np.asarray(w_o, dtype=np.float64).T
     return {"x": x, "k": ks, "v": vs}
+
+
+# ---------------------------------------------------------------------------
+# Linear-attention layers of a hybrid model ([HYPIC] 2.1): a layer keeps one state
+# matrix per head, S_t = A_t S_{t-1} + W_t (A_t the token's transition, W_t its write,
+# e.g. beta_t k_t v_t^T).  A segment C is cached as its cumulative transition
+# T_C = A_L ... A_1 and its zero-init final state S(C|0); after any prefix the state
+# is S(prefix . C) = T_C S(prefix) + S(C|0).
+# ---------------------------------------------------------------------------
+
+
+def linear_recurrence(a_list, w_list, s0):
+    """Token-level recurrence S_t = A_t S_{t-1} + W_t from S_0 = s0; returns S_N (fp64).
+    a_list: [N][dk, dk]; w_list: [N][dk, dv]."""
+    s = np.array(s0, dtype=np.float64)
+    for a, w in zip(a_list, w_list):
+        s = np.asarray(a, dtype=np.float64) @ s + np.asarray(w, dtype=np.float64)
+    return s
+
+
+def segment_summary(a_list, w_list, dv):
+    """(T_C, S(C|0)) of one segment: T_C = A_L ... A_1 (the latest transition on the
+    left) and the recurrence run from a zero state."""
+    dk = np.asarray(a_list[0]).shape[0] if len(a_list) else None
+    if dk is None:
+        raise ValueError("a segment needs at least one token")
+    t = np.eye(dk)
+    for a in a_list:
+        t = np.asarray(a, dtype=np.float64) @ t
+    return t, linear_recurrence(a_list, w_list, np.zeros((dk, dv)))
+
+
+def compose_states(t_list, s_list, s0=None):
+    """States after each segment of a request: S_j = T_j S_{j-1} + S_j(0), S_{-1} = s0
+    (zero when None).  t_list: [m][dk, dk]; s_list: [m][dk, dv].  Returns [m, dk, dv]."""
+    out = []
+    s = None if s0 is None else np.asarray(s0, dtype=np.float64)
+    for t, s_seg in zip(t_list, s_list):
+        s_seg = np.asarray(s_seg, dtype=np.float64)
+        s = s_seg.copy() if s is None else np.asarray(t, dtype=np.float64) @ s + s_seg
+        out.append(s)
+    return np.stack(out) if out else np.zeros((0,) + np.asarray(s_list).shape[1:])
 
 
 # ---------------------------------------------------------------------------

@@ -653,3 +653,75 @@ def test_planted_link_layer_mistakes_fail(mistake):
 
     rows, got, full = _compiled_link(weights, x_chunks, x_query, 5, 1e4, "adjacent", 0, link=wrong)
     assert np.max(np.abs(got - full[rows])) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# HYPIC linear-layer state composition
+# ---------------------------------------------------------------------------
+
+
+def _delta_rule_tokens(rng, n, dk, dv):
+    """Per-token transitions and writes of a gated delta rule (one of the linear
+    attention families the composition covers): A_t = alpha_t (I - beta_t k k^T),
+    W_t = beta_t k v^T with unit k."""
+    a_list, w_list = [], []
+    for _ in range(n):
+        k = rng.standard_normal(dk)
+        k /= np.linalg.norm(k)
+        v = rng.standard_normal(dv)
+        alpha, beta = rng.uniform(0.9, 1.0), rng.uniform(0.1, 0.9)
+        a_list.append(alpha * (np.eye(dk) - beta * np.outer(k, k)))
+        w_list.append(beta * np.outer(k, v))
+    return a_list, w_list
+
+
+def test_state_composition_equals_token_recurrence():
+    # cached (T_C, S(C|0)) of independent segments, composed in prompt order, give the
+    # state of the token-level recurrence over the whole prompt, after every segment
+    rng = np.random.default_rng(41)
+    dk, dv = 6, 5
+    lens = [7, 1, 12, 4]
+    segs = [_delta_rule_tokens(rng, n, dk, dv) for n in lens]
+    summaries = [O.segment_summary(a, w, dv) for a, w in segs]
+    got = O.compose_states([t for t, _ in summaries], [s for _, s in summaries])
+    s = np.zeros((dk, dv))
+    for j, (a, w) in enumerate(segs):
+        s = O.linear_recurrence(a, w, s)
+        assert np.max(np.abs(got[j] - s)) < 1e-12
+    # a non-zero initial state enters through every T
+    s0 = rng.standard_normal((dk, dv))
+    got0 = O.compose_states([t for t, _ in summaries], [x for _, x in summaries], s0)
+    a_all = [a for a, _ in segs for a in a]
+    w_all = [w for _, w in segs for w in w]
+    assert np.max(np.abs(got0[-1] - O.linear_recurrence(a_all, w_all, s0))) < 1e-12
+
+
+def test_state_composition_special_cases_and_associativity():
+    rng = np.random.default_rng(43)
+    dk, dv = 4, 3
+    t = [rng.standard_normal((dk, dk)) for _ in range(3)]
+    s = [rng.standard_normal((dk, dv)) for _ in range(3)]
+    # identity transitions: the states are running sums; one segment is its own state
+    got = O.compose_states([np.eye(dk)] * 3, s)
+    assert np.allclose(got, np.cumsum(np.stack(s), axis=0), atol=1e-14)
+    assert np.array_equal(O.compose_states(t[:1], s[:1])[0], s[0])
+    # composing (T, S) pairs is associative: merging the last two segments first
+    # ((T3 T2, T3 S2 + S3)) gives the same final state
+    merged = (t[2] @ t[1], t[2] @ s[1] + s[2])
+    two = O.compose_states([t[0], merged[0]], [s[0], merged[1]])
+    assert np.max(np.abs(two[-1] - O.compose_states(t, s)[-1])) < 1e-12
+
+
+def test_planted_state_composition_mistakes_fail():
+    # naive addition of zero-init states (T dropped) and a swapped segment order both
+    # miss the true state by far more than any tolerance
+    rng = np.random.default_rng(45)
+    dk, dv = 6, 5
+    segs = [_delta_rule_tokens(rng, n, dk, dv) for n in (30, 30)]
+    summaries = [O.segment_summary(a, w, dv) for a, w in segs]
+    want = O.linear_recurrence([a for a, _ in segs for a in a], [w for _, w in segs for w in w],
+                               np.zeros((dk, dv)))
+    naive = summaries[0][1] + summaries[1][1]
+    assert np.max(np.abs(naive - want)) > 1e-2
+    swapped = O.compose_states([summaries[1][0], summaries[0][0]], [summaries[1][1], summaries[0][1]])
+    assert np.max(np.abs(swapped[-1] - want)) > 1e-2
