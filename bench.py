@@ -55,6 +55,11 @@ def parse():
                          "projection) of a random model with this many layers")
     ap.add_argument("--d-model", type=int, default=0,
                     help="model width for --link-layers (default h_q * head_dim)")
+    ap.add_argument("--state-compose", action="store_true",
+                    help="shared_pool only: time the linear-layer state composition over "
+                         "every request's chunks (pic_state_compose), --heads heads")
+    ap.add_argument("--heads", type=int, default=32,
+                    help="linear-attention heads for --state-compose")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="recomputed rows of request 0 the oracle times (0 = all)")
@@ -98,14 +103,14 @@ def src_hash(paths):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, workload):
+def load_traffic(kernel, workload, sources=None):
     """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
     path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != src_hash(rec.get("sources", ATTN_SOURCES)):
+    if rec.get("source_hash") != src_hash(rec.get("sources", sources or ATTN_SOURCES)):
         return None
     return rec.get("bytes_per_launch")
 
@@ -581,6 +586,95 @@ def bench_link(args, wl):
     print(json.dumps(rec), flush=True)
 
 
+def bench_state(args, wl):
+    """HYPIC linear-layer state composition over the shared-pool batch: every request's
+    chunks composed in prompt order from cached (T_C, S(C|0)) per head, writing the state
+    after every chunk and the final states (fp32)."""
+    import torch
+    import position_independent_kv_rope_amd as P
+    from position_independent_kv_rope_amd import workloads as W
+    from oracle import pic_oracle as O
+    H, d = args.heads, 128
+    reqs = [r.chunk_lens for r in wl.requests]
+    ids = [r.chunk_ids for r in wl.requests]
+    qs = [r.q_len for r in wl.requests]
+    plan = P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, chunk_ids_per_req=ids)
+    plan.to_device()
+    t_h, s_h = W.state_pool_tensors(wl, H, d)
+    dev = "cuda"
+    t_pool, s_pool = t_h.to(dev), s_h.to(dev)
+    n_req, n_chunks = len(reqs), plan[P.H_N_CHUNKS]
+    final = torch.empty((n_req, H, d, d), dtype=torch.float32, device=dev)
+    prefix = torch.empty((n_chunks, H, d, d), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    steps = n_chunks * H  # (chunk, head) products
+    flops = steps * 2.0 * d * d * d
+    used = sorted({i for r in wl.requests for i in r.chunk_ids})
+    mat = 4.0 * d * d
+    # every used chunk's T and S(C|0) once, the state after every chunk and the finals
+    alg_bytes = len(used) * H * 2 * mat + steps * mat + n_req * H * mat
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+
+    def step(i=None):
+        e = ev[i] if i is not None else None
+        if e: e[0].record()
+        P.pic_state_compose(plan, t_pool, s_pool, final, prefix_out=prefix)
+        if e: e[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    t_call = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    tflops = flops / (t_call * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS["f32"]
+    rec = {
+        "metric": METRIC,
+        "value": round(plan.n_tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "shared_pool_state_compose", "requests": n_req,
+                   "context_tokens": plan.n_tokens, "chunks": n_chunks, "pool_chunks": len(wl.pool_lens),
+                   "heads": H, "d_k": d, "d_v": d, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": load_traffic("state", "shared_pool_h%d" % H,
+                                             ["position_independent_kv_rope_amd/csrc/pic_state.hip"]),
+                     "kernel": "pic_state_compose call (state_compose_kernel)",
+                     "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes,
+                     "hbm_GB_s_at_algorithmic_bytes": round(alg_bytes / (t_call * 1e-3) / 1e9, 1)},
+        "kernels": {"state_compose": {"ms": round(t_call, 4), "TFLOP_s": round(tflops, 2),
+                                      "products": steps}},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle's composition of request 0, every head
+        t1 = time.perf_counter()
+        r = wl.requests[0]
+        tp = [t_h[i].double().numpy() for i in r.chunk_ids]
+        sp = [s_h[i].double().numpy() for i in r.chunk_ids]
+        for h in range(H):
+            O.compose_states([t[h] for t in tp], [s[h] for s in sp])
+        dt = time.perf_counter() - t1
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        n0 = sum(r.chunk_lens) + r.q_len
+        rec["cpu_baseline"] = {"value": round(n0 / dt, 1), "unit": "tokens/s", "cores": int(threads),
+                               "kind": "oracle", "seconds": round(dt, 3),
+                               "sample": "request 0 (%d chunks, %d tokens), all %d heads: fp64 "
+                                         "composition of the cached (T, S) pairs"
+                                         % (len(r.chunk_ids), n0, H),
+                               "host_cpus": os.cpu_count()}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -599,6 +693,8 @@ def main():
     P.lib()
     wl = make_workload(args.workload, args.k)
     if wl.pool_lens is not None:
+        if args.state_compose:
+            return bench_state(args, wl)
         return bench_decode(args, wl) if args.decode else bench_paged(args, wl)
     if args.decode:
         print("--decode needs --workload shared_pool", file=sys.stderr)

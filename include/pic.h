@@ -360,6 +360,27 @@ int pic_link(const int32_t *plan_host, const int32_t *plan_dev, int32_t n_layers
              double rope_base, float scale, void *workspace, size_t workspace_bytes,
              void *stream);
 
+/*
+ * pic_state_compose -- linear-layer states over the chunks of every request.
+ *                                                                  [HYPIC] 2.1
+ * A linear-attention head keeps one state S [d_k][d_v]; a cached chunk is its
+ * cumulative transition T_C [d_k][d_k] (the product of its tokens' transitions, the
+ * latest on the left) and its state from a zero start S(C|0).  For every request b of
+ * a paged plan and head h, over the request's chunks c in prompt order (pool chunk
+ * id_c from the plan): S_c = T_{id_c} S_{c-1} + S_{id_c}(0), with S_{-1} = s_init[b][h]
+ * (zero when s_init is NULL).  t_pool [n_pool_chunks][n_heads][d_k][d_k] and s_pool
+ * [n_pool_chunks][n_heads][d_k][d_v] (device, fp32, row-major); prefix_out
+ * [n_chunks][n_heads][d_k][d_v] receives S_c after every chunk of every request (in
+ * plan chunk order; NULL skips it); final_out [n_req][n_heads][d_k][d_v] the state
+ * after each request's last chunk (s_init, or zero, for a request without chunks).
+ * fp32 only, d_k = d_v = 128; else PIC_EUNSUPPORTED.  Errors: PIC_EINVAL (not a paged
+ * plan, a chunk id >= n_pool_chunks, null pointers, sizes <= 0), PIC_EDEVICE.
+ */
+int pic_state_compose(const int32_t *plan_host, const int32_t *plan_dev, int32_t n_heads,
+                      int32_t d_k, int32_t d_v, const void *t_pool, const void *s_pool,
+                      int32_t n_pool_chunks, const void *s_init, void *prefix_out,
+                      void *final_out, int32_t dtype, void *stream);
+
 /* Short static description of a status code. */
 const char *pic_strerror(int status);
 

@@ -36,7 +36,8 @@ EXPORTED = ("pic_build_index", "pic_rope_delta", "pic_rope_apply", "pic_splice",
             "pic_attn_workspace_bytes",
             "pic_selective_attn", "pic_selective_attn_paged", "pic_decode_workspace_bytes",
             "pic_decode_attn_paged", "pic_qkv_workspace_bytes", "pic_qkv_rope",
-            "pic_out_proj", "pic_link_workspace_bytes", "pic_link", "pic_strerror")
+            "pic_out_proj", "pic_link_workspace_bytes", "pic_link", "pic_state_compose",
+            "pic_strerror")
 
 
 class PicError(RuntimeError):
@@ -93,6 +94,8 @@ def lib():
     L.pic_link.argtypes = [p, p, i32, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, f64, f32,
                            p, sz, p]
     L.pic_link.restype = ctypes.c_int
+    L.pic_state_compose.argtypes = [p, p, i32, i32, i32, p, p, i32, p, p, p, i32, p]
+    L.pic_state_compose.restype = ctypes.c_int
     L.pic_strerror.argtypes = [ctypes.c_int]
     L.pic_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -518,3 +521,31 @@ def pic_link(plan, x, w_qkv, w_o, k_cache, v_cache, q, k_fresh, v_fresh, o, rope
                         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                         _stream(stream))
     _check("pic_link", st)
+
+
+def pic_state_compose(plan, t_pool, s_pool, final_out, prefix_out=None, s_init=None,
+                      stream=None):
+    """Linear-layer states over each request's chunks: S_c = T S_{c-1} + S(C|0).
+    t_pool [n_pool, H, dk, dk], s_pool [n_pool, H, dk, dv], final_out [n_req, H, dk, dv],
+    prefix_out [n_chunks, H, dk, dv] or None, s_init [n_req, H, dk, dv] or None."""
+    if not plan.paged:
+        raise ValueError("plan was not built with chunk ids (paged pool)")
+    n_pool, n_heads, d_k, d_v = (int(x) for x in s_pool.shape)
+    if t_pool.shape != (n_pool, n_heads, d_k, d_k):
+        raise ValueError("t_pool must be [n_pool, H, dk, dk]")
+    if final_out.shape != (plan[H_N_REQ], n_heads, d_k, d_v):
+        raise ValueError("final_out must be [n_req, H, dk, dv]")
+    if prefix_out is not None and prefix_out.shape != (plan[H_N_CHUNKS], n_heads, d_k, d_v):
+        raise ValueError("prefix_out must be [n_chunks, H, dk, dv]")
+    if s_init is not None and s_init.shape != final_out.shape:
+        raise ValueError("s_init must be [n_req, H, dk, dv]")
+    for t in (t_pool, final_out) + tuple(x for x in (prefix_out, s_init) if x is not None):
+        if t.dtype != s_pool.dtype:
+            raise ValueError("all tensors must share one dtype")
+    opt = lambda t, n: None if t is None else _dev(t, n)
+    st = lib().pic_state_compose(plan.host_ptr(), plan.dev_ptr(), n_heads, d_k, d_v,
+                                 _dev(t_pool, "t_pool"), _dev(s_pool, "s_pool"), n_pool,
+                                 opt(s_init, "s_init"), opt(prefix_out, "prefix_out"),
+                                 _dev(final_out, "final_out"), _dtype_code(s_pool),
+                                 _stream(stream))
+    _check("pic_state_compose", st)

@@ -197,6 +197,19 @@ def link_tensors(wl, n_layers, d_model, n_rows):
     return x0, w_qkv, w_o, kc, vc
 
 
+def state_pool_tensors(wl, n_heads, d=128, decay=0.9, noise=0.1, s_scale=0.1):
+    """Cached linear-layer summaries of every pool chunk (no trained model exists here):
+    T [n_pool, H, d, d] = decay * (I + noise * G / sqrt(d)) with G ~ N(0, 1), a
+    contraction like a product of decaying token transitions, and S(C|0) [n_pool, H, d, d]
+    ~ N(0, s_scale^2), so composed states stay O(1).  fp32 CPU tensors."""
+    import torch
+    n_pool = len(wl.pool_lens)
+    g = draw((n_pool, n_heads, d, d), wl.seed * 7 + 200, torch.float32, noise / np.sqrt(d))
+    t = decay * (g + torch.eye(d, dtype=torch.float32))
+    sz = draw((n_pool, n_heads, d, d), wl.seed * 7 + 201, torch.float32, s_scale)
+    return t, sz
+
+
 CONFIGS = {
     "worked_example": worked_example,
     "rag_single": rag_single,

@@ -111,6 +111,24 @@ def test_device_entry_points_reject_bad_arguments_without_launching():
     assert L.pic_attn_workspace_bytes(bp, 128) == 0
 
 
+def test_state_compose_rejects_bad_arguments_without_launching():
+    L = P.lib()
+    f = ctypes.c_void_p(0x1000)
+    plan = P.pic_build_index([[40, 50]], [7], 2, 8, 2, chunk_ids_per_req=[[0, 3]])
+    hp = plan.host_ptr()
+    call = lambda hp=hp, heads=4, dk=128, dv=128, n_pool=4, fin=f, dt=P.PIC_F32, t=f: \
+        L.pic_state_compose(hp, f, heads, dk, dv, t, f, n_pool, None, None, fin, dt, None)
+    contiguous = P.pic_build_index([[40, 50]], [7], 2, 8, 2)
+    assert call(hp=contiguous.host_ptr()) == P.PIC_EINVAL   # needs chunk ids
+    assert call(heads=0) == P.PIC_EINVAL
+    assert call(n_pool=3) == P.PIC_EINVAL                   # chunk id 3 >= n_pool
+    assert call(fin=None) == P.PIC_EINVAL
+    assert call(t=None) == P.PIC_EINVAL
+    assert call(dt=9) == P.PIC_EINVAL
+    assert call(dt=P.PIC_BF16) == P.PIC_EUNSUPPORTED        # the scan is fp32
+    assert call(dk=64, dv=64) == P.PIC_EUNSUPPORTED
+
+
 def test_link_entry_points_reject_bad_arguments_without_launching():
     L = P.lib()
     plan = P.pic_build_index([[40, 50]], [7], 2, 8, 2)  # G = 4, h_kv * 128 = 256
