@@ -12,8 +12,9 @@
 // operand every wave reads), the chunk's T [128 x 128] is staged to LDS through
 // registers, and each wave computes a 32 x 64 block of S_j with v_mfma_f32_16x16x4_f32
 // (fp32 operands and accumulation: the scan compounds rounding, so no bf16 here).  The
-// row strides of the two LDS tiles (132 and 144 floats) make the MFMA operand reads
-// conflict-free: A reads 16 rows x 4 k of T, B reads 4 k x 16 columns of S.  While a
+// row strides of the two LDS tiles (132 and 144 floats, S also with a 16-column block
+// swizzle) make the MFMA operand reads and the state writes conflict-free: A reads 16
+// rows x 4 k of T, B reads 4 k x 16 columns of S.  While a
 // chunk is multiplied, the next chunk's T and S(C|0) are already being loaded into
 // registers.
 #include <algorithm>
@@ -29,6 +30,11 @@ constexpr int kSThreads = 512;            // 8 waves: 4 row blocks x 2 column bl
 constexpr int kTStride = kSD + 4;         // floats per T row in LDS
 constexpr int kSStride = kSD + 16;        // floats per S row in LDS
 constexpr int kTFloats = kSD * kSD / kSThreads;  // floats of T (and of S(C|0)) per thread
+
+// S element (r, c) in LDS: row stride kSStride, and the 16-column block index XORed with
+// (r / 4) mod 4.  B reads (rows k .. k+3, 16 columns) stay on 64 distinct banks, and so
+// do the accumulator writes, whose lanes cover rows 4 apart.
+__device__ __forceinline__ int sidx(int r, int c) { return r * kSStride + (c ^ (((r >> 2) & 3) << 4)); }
 
 __global__ __launch_bounds__(kSThreads, 1) void state_compose_kernel(
     const int32_t *__restrict__ segs, const int32_t *__restrict__ req_chunk_ptr, int n_heads,
@@ -63,10 +69,15 @@ __global__ __launch_bounds__(kSThreads, 1) void state_compose_kernel(
                      __uint_as_float(v[3])};
     }
   };
-  auto store_lds = [&](float *dst, int stride, const f32x4 (&reg)[kTFloats / 4]) {
+  auto store_t = [&](const f32x4 (&reg)[kTFloats / 4]) {
 #pragma unroll
     for (int r = 0; r < kTFloats / 4; ++r)
-      *reinterpret_cast<f32x4 *>(dst + (lrow + 16 * r) * stride + lcol) = reg[r];
+      *reinterpret_cast<f32x4 *>(t_lds + (lrow + 16 * r) * kTStride + lcol) = reg[r];
+  };
+  auto store_s = [&](const f32x4 (&reg)[kTFloats / 4]) {  // 4 columns stay together
+#pragma unroll
+    for (int r = 0; r < kTFloats / 4; ++r)
+      *reinterpret_cast<f32x4 *>(s_lds + sidx(lrow + 16 * r, lcol)) = reg[r];
   };
   // S(C|0) straight into the accumulator layout: tile (i, jt) of this wave covers rows
   // 32 wr + 16 i + 4 quad + e, column 64 wc + 16 jt + col
@@ -104,7 +115,7 @@ __global__ __launch_bounds__(kSThreads, 1) void state_compose_kernel(
 #pragma unroll
       for (int r = 0; r < kTFloats / 4; ++r) reg[r] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    store_lds(s_lds, kSStride, reg);
+    store_s(reg);
   }
   f32x4 acc[2][4];
   if (c0 == c1) {  // no chunks: the state stays the initial one
@@ -115,7 +126,7 @@ __global__ __launch_bounds__(kSThreads, 1) void state_compose_kernel(
       for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc[i][jt][e] = s_lds[(32 * wr + 16 * i + 4 * quad + e) * kSStride + 64 * wc + 16 * jt + col];
+          acc[i][jt][e] = s_lds[sidx(32 * wr + 16 * i + 4 * quad + e, 64 * wc + 16 * jt + col)];
     store_acc(final_out + ((int64_t)b * n_heads + h) * mat, acc);
     return;
   }
@@ -123,7 +134,7 @@ __global__ __launch_bounds__(kSThreads, 1) void state_compose_kernel(
   f32x4 snext[2][4];
   load_mat(chunk_mat(t_pool, c0), treg);
   load_acc(chunk_mat(s_pool, c0), snext);
-  store_lds(t_lds, kTStride, treg);
+  store_t(treg);
   __syncthreads();
 
   for (int c = c0; c < c1; ++c) {
@@ -135,17 +146,21 @@ __global__ __launch_bounds__(kSThreads, 1) void state_compose_kernel(
       load_mat(chunk_mat(t_pool, c + 1), treg);
       load_acc(chunk_mat(s_pool, c + 1), snext);
     }
-    // acc += T[32 wr .. +31][:] S[:][64 wc .. +63], 4 k per MFMA
+    // acc += T[32 wr .. +31][:] S[:][64 wc .. +63], 4 k per MFMA; rows k + quad of S
+    // have (k / 4) mod 4 = kk as their column swizzle
     const float *ta = t_lds + (32 * wr + col) * kTStride + quad;
     const float *sb = s_lds + quad * kSStride + 64 * wc + col;
-#pragma unroll 2
-    for (int k = 0; k < kSD; k += 4) {
-      const float a0 = ta[k], a1 = ta[16 * kTStride + k];
+    for (int k0 = 0; k0 < kSD; k0 += 16) {
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const float bv = sb[k * kSStride + 16 * jt];
-        acc[0][jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bv, acc[0][jt], 0, 0, 0);
-        acc[1][jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bv, acc[1][jt], 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk) {
+        const int k = k0 + 4 * kk;
+        const float a0 = ta[k], a1 = ta[16 * kTStride + k];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const float bv = sb[k * kSStride + 16 * (jt ^ kk)];
+          acc[0][jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bv, acc[0][jt], 0, 0, 0);
+          acc[1][jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bv, acc[1][jt], 0, 0, 0);
+        }
       }
     }
     // every wave is done reading T_c and S_{c-1} (LDS only: the loads and stores in
@@ -157,10 +172,9 @@ __global__ __launch_bounds__(kSThreads, 1) void state_compose_kernel(
       for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          s_lds[(32 * wr + 16 * i + 4 * quad + e) * kSStride + 64 * wc + 16 * jt + col] =
-              acc[i][jt][e];
+          s_lds[sidx(32 * wr + 16 * i + 4 * quad + e, 64 * wc + 16 * jt + col)] = acc[i][jt][e];
     if (prefix_out) store_acc(prefix_out + ((int64_t)c * n_heads + h) * mat, acc);
-    if (c + 1 < c1) store_lds(t_lds, kTStride, treg);
+    if (c + 1 < c1) store_t(treg);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // S_c and T_{c+1} in LDS
   }
   store_acc(final_out + ((int64_t)b * n_heads + h) * mat, acc);
