@@ -52,12 +52,38 @@ struct QkvOut {
   int h_q, h_kv;
 };
 
+// Output tile of a workgroup.  Consecutive workgroups go round-robin to the 8 XCDs
+// (each with its own L2), so workgroup b works on position (b % 8) * per + b / 8 of
+// the tile sequence: every XCD takes one contiguous stretch.  The sequence walks groups
+// of kGroupM row tiles column by column, so the ~64 tiles an XCD runs at once form an
+// 8 x 8 block that shares its A and W tiles in that XCD's L2 as they stream through K.
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+
+__device__ __forceinline__ bool gemm_tile(int mt, int nt, int &tm, int &tn) {
+  const int total = mt * nt;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int u = (int)(blockIdx.x % kXcds) * per + (int)(blockIdx.x / kXcds);
+  if (u >= total) return false;
+  const int g = u / (kGroupM * nt);
+  const int gm = min(kGroupM, mt - g * kGroupM);
+  const int w = u - g * kGroupM * nt;
+  tm = g * kGroupM + w % gm;
+  tn = w / gm;
+  return true;
+}
+
+inline unsigned gemm_grid(int mt, int nt) {
+  return (unsigned)(((int64_t)mt * nt + kXcds - 1) / kXcds * kXcds);
+}
+
 template <int kEpi, int D, bool kHalf>
 __device__ __forceinline__ void gemm_nt_body(const __bf16 *__restrict__ A,
-                                             const __bf16 *__restrict__ W, int M, int K,
-                                             QkvOut qo, __bf16 *__restrict__ x) {
+                                             const __bf16 *__restrict__ W, int M, int K, int N,
+                                             int tm, int tn, QkvOut qo,
+                                             __bf16 *__restrict__ x) {
   __shared__ __attribute__((aligned(1024))) char lds[kGLdsBytes];
-  const int m0 = blockIdx.x * kGT, n0 = blockIdx.y * kGT;
+  const int m0 = tm * kGT, n0 = tn * kGT;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;
@@ -160,7 +186,7 @@ __device__ __forceinline__ void gemm_nt_body(const __bf16 *__restrict__ A,
   const float *crow = ct + ml * kGCStride;
   if constexpr (kEpi == kEpiResidual) {
     // x[m][n0 + f] += C[m][f] for this thread's 64 features
-    __bf16 *xr = x + (int64_t)m * gridDim.y * kGT + n0 + 64 * part;
+    __bf16 *xr = x + (int64_t)m * N + n0 + 64 * part;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       bf16x8 v = *reinterpret_cast<const bf16x8 *>(xr + 8 * c);
@@ -238,16 +264,20 @@ __device__ __forceinline__ void gemm_nt_body(const __bf16 *__restrict__ A,
 template <int D, bool kHalf>
 __global__ __launch_bounds__(kGThreads, 2) void qkv_rope_gemm_kernel(const __bf16 *__restrict__ x,
                                                                      const __bf16 *__restrict__ w,
-                                                                     int M, int K, QkvOut qo) {
-  gemm_nt_body<kEpiQkvRope, D, kHalf>(x, w, M, K, qo, nullptr);
+                                                                     int M, int K, int N, QkvOut qo) {
+  int tm, tn;
+  if (!gemm_tile((M + kGT - 1) / kGT, N / kGT, tm, tn)) return;
+  gemm_nt_body<kEpiQkvRope, D, kHalf>(x, w, M, K, N, tm, tn, qo, nullptr);
 }
 
 template <int D>
 __global__ __launch_bounds__(kGThreads, 2) void out_proj_gemm_kernel(const __bf16 *__restrict__ o,
                                                                      const __bf16 *__restrict__ w,
-                                                                     int M, int K,
+                                                                     int M, int K, int N,
                                                                      __bf16 *__restrict__ x) {
-  gemm_nt_body<kEpiResidual, D, false>(o, w, M, K, QkvOut{}, x);
+  int tm, tn;
+  if (!gemm_tile((M + kGT - 1) / kGT, N / kGT, tm, tn)) return;
+  gemm_nt_body<kEpiResidual, D, false>(o, w, M, K, N, tm, tn, QkvOut{}, x);
 }
 
 // cos/sin of p_r * theta_i for every recomputed row r and pair i
@@ -295,9 +325,9 @@ int launch_qkv(const PlanHeader &h, const int32_t *plan_dev, const void *x, cons
   const int n_out = (h[PIC_H_H_Q] + 2 * h[PIC_H_H_KV]) * D;
   QkvOut qo{static_cast<__bf16 *>(q), static_cast<__bf16 *>(kf), static_cast<__bf16 *>(vf), cs,
             h[PIC_H_H_Q], h[PIC_H_H_KV]};
-  hipLaunchKernelGGL((qkv_rope_gemm_kernel<D, kHalf>), dim3((M + kGT - 1) / kGT, n_out / kGT),
+  hipLaunchKernelGGL((qkv_rope_gemm_kernel<D, kHalf>), dim3(gemm_grid((M + kGT - 1) / kGT, n_out / kGT)),
                      dim3(kGThreads), 0, s, static_cast<const __bf16 *>(x),
-                     static_cast<const __bf16 *>(w), M, d_model, qo);
+                     static_cast<const __bf16 *>(w), M, d_model, n_out, qo);
   PIC_LAUNCH_CHECK();
   return PIC_OK;
 }
@@ -353,13 +383,13 @@ extern "C" int pic_out_proj(const int32_t *plan_host, const void *o, const void 
   if (!o || !w_o || !x) return PIC_EINVAL;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (head_dim == 128)
-    hipLaunchKernelGGL((out_proj_gemm_kernel<128>), dim3((M + kGT - 1) / kGT, d_model / kGT),
+    hipLaunchKernelGGL((out_proj_gemm_kernel<128>), dim3(gemm_grid((M + kGT - 1) / kGT, d_model / kGT)),
                        dim3(kGThreads), 0, s, static_cast<const __bf16 *>(o),
-                       static_cast<const __bf16 *>(w_o), M, k_in, static_cast<__bf16 *>(x));
+                       static_cast<const __bf16 *>(w_o), M, k_in, d_model, static_cast<__bf16 *>(x));
   else
-    hipLaunchKernelGGL((out_proj_gemm_kernel<64>), dim3((M + kGT - 1) / kGT, d_model / kGT),
+    hipLaunchKernelGGL((out_proj_gemm_kernel<64>), dim3(gemm_grid((M + kGT - 1) / kGT, d_model / kGT)),
                        dim3(kGThreads), 0, s, static_cast<const __bf16 *>(o),
-                       static_cast<const __bf16 *>(w_o), M, k_in, static_cast<__bf16 *>(x));
+                       static_cast<const __bf16 *>(w_o), M, k_in, d_model, static_cast<__bf16 *>(x));
   PIC_LAUNCH_CHECK();
   return PIC_OK;
 }
