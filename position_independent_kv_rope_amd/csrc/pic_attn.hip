@@ -863,7 +863,7 @@ __device__ __forceinline__ void dec_attn_body(
     const int32_t *__restrict__ uses, const int32_t *__restrict__ segs,
     const int32_t *__restrict__ req_row_ptr, const DecPiece *__restrict__ pieces,
     const int32_t *__restrict__ piece_recs, const int32_t *__restrict__ wg_ptr,
-    const float2 *__restrict__ angles, float *__restrict__ ws_o, float *__restrict__ ws_ml,
+    const float2 *__restrict__ angles, __bf16 *__restrict__ ws_o, float *__restrict__ ws_ml,
     int h_q, int h_kv, float scale_log2, int64_t pool_blocks) {
   constexpr int kRowB = D * 2;
   constexpr int kCPR = D / 8;
@@ -1153,15 +1153,15 @@ __device__ __forceinline__ void dec_attn_body(
       const float l_row = pair_sum(l_lane);
       if (valid) {
         const int64_t at = (int64_t)rec * group + hh;
-        float *wo = ws_o + at * D + 4 * grp;
+        __bf16 *wo = ws_o + at * D + 4 * grp;
 #pragma unroll
         for (int d = 0; d < kDB; ++d)
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
-            f32x4 o;
+            bf16x4 o;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) o[b] = acc[d][4 * a + b];
-            *reinterpret_cast<f32x4 *>(wo + 32 * d + 8 * a) = o;
+            for (int b = 0; b < 4; ++b) o[b] = (__bf16)acc[d][4 * a + b];
+            *reinterpret_cast<bf16x4 *>(wo + 32 * d + 8 * a) = o;
           }
         if (grp == 0) {
           ws_ml[at * 2 + 0] = m_run;
@@ -1181,7 +1181,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void dec_attn_kernel(
     const int32_t *__restrict__ uses, const int32_t *__restrict__ segs,
     const int32_t *__restrict__ req_row_ptr, const DecPiece *__restrict__ pieces,
     const int32_t *__restrict__ piece_recs, const int32_t *__restrict__ wg_ptr,
-    const float2 *__restrict__ angles, float *__restrict__ ws_o, float *__restrict__ ws_ml,
+    const float2 *__restrict__ angles, __bf16 *__restrict__ ws_o, float *__restrict__ ws_ml,
     int h_q, int h_kv, float scale_log2, int64_t pool_blocks) {
   dec_attn_body<D, kHalf>(q, pool_k, pool_v, chunk_block_ptr, block_ids, k_fresh, v_fresh,
                           items, uses, segs, req_row_ptr, pieces, piece_recs, wg_ptr, angles,
@@ -1198,7 +1198,7 @@ template <int D>
 __global__ __launch_bounds__(kDecMergeThreads) void dec_merge_kernel(
     __bf16 *__restrict__ out, const __bf16 *__restrict__ q, const __bf16 *__restrict__ k_new,
     const __bf16 *__restrict__ v_new, const int32_t *__restrict__ rec_ptr,
-    const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int h_q, int h_kv,
+    const __bf16 *__restrict__ ws_o, const float *__restrict__ ws_ml, int h_q, int h_kv,
     float scale_log2) {
   constexpr int kC = D / 4;
   constexpr int kDecMergeGroups = kDecMergeThreads / kC;
@@ -1246,8 +1246,10 @@ __global__ __launch_bounds__(kDecMergeThreads) void dec_merge_kernel(
     const int64_t a2 = (int64_t)sl2 * group + hh;
     const float2 ml1 = *reinterpret_cast<const float2 *>(ws_ml + a1 * 2);
     const float2 ml2 = *reinterpret_cast<const float2 *>(ws_ml + a2 * 2);
-    const f32x4 o1 = *reinterpret_cast<const f32x4 *>(ws_o + a1 * D + 4 * c4);
-    const f32x4 o2 = *reinterpret_cast<const f32x4 *>(ws_o + a2 * D + 4 * c4);
+    const bf16x4 b1 = *reinterpret_cast<const bf16x4 *>(ws_o + a1 * D + 4 * c4);
+    const bf16x4 b2 = *reinterpret_cast<const bf16x4 *>(ws_o + a2 * D + 4 * c4);
+    const f32x4 o1 = {(float)b1[0], (float)b1[1], (float)b1[2], (float)b1[3]};
+    const f32x4 o2 = {(float)b2[0], (float)b2[1], (float)b2[2], (float)b2[3]};
     fold(ml1.x, ml1.y, o1);
     if (sl2 != sl) fold(ml2.x, ml2.y, o2);
   }
@@ -1562,10 +1564,16 @@ int launch_paged(const PlanHeader &h, const int32_t *plan_dev, const void *q, co
   return PIC_OK;
 }
 
-// Decode workspace: partial O [n_dec_recs][G][D], partial (m, l) [..][2],
-// then the angle table [n_chunks][D/2] float2 (16-byte aligned).
-size_t dec_partial_floats(const PlanHeader &h, int head_dim) {
-  return (size_t)h[PIC_H_N_DEC_RECS] * (h[PIC_H_H_Q] / h[PIC_H_H_KV]) * ((size_t)head_dim + 2);
+// Decode workspace: record O [n_dec_recs][G][D] in bf16 (the records are HBM traffic
+// of an HBM-bound step; each is one rounding of an unnormalised sum the merge weights
+// and renormalises), record (m, l) [..][2] fp32, then the angle table [n_chunks][D/2]
+// float2; sections 16-byte aligned.
+size_t dec_o_bytes(const PlanHeader &h, int head_dim) {
+  return ((size_t)h[PIC_H_N_DEC_RECS] * (h[PIC_H_H_Q] / h[PIC_H_H_KV]) * head_dim * 2 + 15) / 16 * 16;
+}
+size_t dec_record_bytes(const PlanHeader &h, int head_dim) {
+  return dec_o_bytes(h, head_dim) +
+         ((size_t)h[PIC_H_N_DEC_RECS] * (h[PIC_H_H_Q] / h[PIC_H_H_KV]) * 2 * sizeof(float) + 15) / 16 * 16;
 }
 
 template <int D, bool kHalf>
@@ -1579,10 +1587,10 @@ int launch_decode(const PlanHeader &h, const int32_t *plan_dev, const void *q, c
   const int32_t *rrp = plan_dev + h[PIC_H_O_REQ_ROW_PTR];
   const DecPiece *pieces = reinterpret_cast<const DecPiece *>(plan_dev + h[PIC_H_O_DEC_PIECES]);
   const int32_t *rec_ptr = plan_dev + h[PIC_H_O_DEC_REC_PTR];
-  float *ws_o = static_cast<float *>(workspace);
-  float *ws_ml = ws_o + (size_t)h[PIC_H_N_DEC_RECS] * (h[PIC_H_H_Q] / h[PIC_H_H_KV]) * D;
-  const size_t ang_off = (dec_partial_floats(h, D) * sizeof(float) + 15) / 16 * 16;
-  float2 *angles = reinterpret_cast<float2 *>(static_cast<char *>(workspace) + ang_off);
+  __bf16 *ws_o = static_cast<__bf16 *>(workspace);
+  float *ws_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + dec_o_bytes(h, D));
+  float2 *angles =
+      reinterpret_cast<float2 *>(static_cast<char *>(workspace) + dec_record_bytes(h, D));
   const int n_chunks = h[PIC_H_N_CHUNKS];
   if (n_chunks > 0) {
     const int64_t total = (int64_t)n_chunks * (D / 2);
@@ -1618,8 +1626,7 @@ extern "C" size_t pic_decode_workspace_bytes(const int32_t *plan_host, int32_t h
   using namespace pic;
   const PlanHeader h{plan_host};
   if (!h.valid() || !h[PIC_H_PAGED] || head_dim <= 0) return 0;
-  return (dec_partial_floats(h, head_dim) * sizeof(float) + 15) / 16 * 16 +
-         (size_t)h[PIC_H_N_CHUNKS] * (head_dim / 2) * sizeof(float2);
+  return dec_record_bytes(h, head_dim) + (size_t)h[PIC_H_N_CHUNKS] * (head_dim / 2) * sizeof(float2);
 }
 
 extern "C" int pic_decode_attn_paged(
