@@ -299,7 +299,7 @@ def bench_paged(args, wl):
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                      "traffic": load_traffic("attn_paged", "shared_pool_k%d" % wl.k),
                      "kernel": "pic_selective_attn_paged call (paged_angles_kernel + "
-                               "attn_bf16_paged_kernel + merge_kernel)",
+                               "paged_blocks_kernel + attn_bf16_paged_kernel + merge_kernel)",
                      "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes},
         "kernels": {
             "selective_attn_paged": {"ms": round(t_attn, 4), "flops": attn_flops,

@@ -260,15 +260,18 @@ int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_dev, const 
  * block_ids device int32.  The plan must come from pic_build_index with chunk_ids, all
  * of them < n_pool_chunks (checked on the host).  Not checkable on the host and left to
  * the caller: each listed chunk has at least ceil(L_c / 16) blocks, and block ids are
- * < pool_blocks (a larger id reads zeros: the pool loads are range-checked).  k_fresh/v_fresh [n_rows][h_kv][head_dim] hold the recomputed rows (RoPE'd
- * at their global positions) and are read in place; q/out as in pic_selective_attn.
- * Cached keys of chunk c are scored in their local frame against the query rotated by
- * -delta_c (same theta and pair layout as pic_rope_delta).  bf16 only, head_dim in
- * {64, 128}, pool and fresh K/V each < 2 GiB.  Pool slots past a chunk's length may
- * hold anything (NaN included).  workspace >= pic_attn_workspace_bytes(plan_host,
- * head_dim) (partials + angle table).  Errors: PIC_EINVAL (not a paged plan, null
- * pointers, a chunk id >= n_pool_chunks, bad scale/base/layout), PIC_EUNSUPPORTED
- * (dtype, head_dim, block_size != 16, sizes), PIC_ENOSPC (workspace), PIC_EDEVICE.
+ * < pool_blocks (a larger id reads zeros: the pool loads are range-checked).
+ * k_fresh/v_fresh [n_rows][h_kv][head_dim] hold the recomputed rows (RoPE'd at their
+ * global positions) and are read in place; q/out as in pic_selective_attn.  Cached keys
+ * of chunk c are scored in their local frame against the query rotated by -delta_c
+ * (same theta and pair layout as pic_rope_delta).  bf16 only, head_dim in {64, 128},
+ * pool and fresh K/V each < 2 GiB.  Pool slots past a chunk's length may hold anything
+ * (NaN included).  workspace >= pic_attn_workspace_bytes(plan_host, head_dim):
+ * partials, the angle table and one 32-byte record per key block (a small kernel fills
+ * them from the block table before the attention kernel runs).  Errors: PIC_EINVAL (not
+ * a paged plan, null pointers, a chunk id >= n_pool_chunks, bad scale/base/layout),
+ * PIC_EUNSUPPORTED (dtype, head_dim, block_size != 16, sizes), PIC_ENOSPC (workspace),
+ * PIC_EDEVICE.
  */
 int pic_selective_attn_paged(const int32_t *plan_host, const int32_t *plan_dev, const void *q,
                              const void *pool_k, const void *pool_v, int64_t pool_blocks,

@@ -419,17 +419,60 @@ __global__ __launch_bounds__(256) void paged_angles_kernel(float2 *__restrict__ 
   }
 }
 
+// Everything the attention kernel needs to stage and mask one 64-key block, resolved
+// once per launch so that the kernel reads a single 32-byte record per block (one
+// scalar load) instead of walking segment -> chunk -> block table with dependent loads.
+struct KeyBlockRec {
+  int32_t frame;     // global chunk index c (its angle row), or -1: the request's fresh rows
+  int32_t row;       // fresh: first fresh row of the block; pool: first local key t0
+  int32_t base_pos;  // pool: global position of local key t0
+  int32_t vis;       // pool: visible local keys [s0, nv) of the block as s0 | nv << 8
+  int32_t off[4];    // pool: byte offset of each 16-row pool block, -1: reads zeros
+};
+static_assert(sizeof(KeyBlockRec) == 32, "one s_load_dwordx8 per record");
+static_assert(kKB == 4 * kPoolBlockRows, "a key block spans four pool blocks");
+
+__global__ __launch_bounds__(256) void paged_blocks_kernel(
+    KeyBlockRec *__restrict__ recs, const int4 *__restrict__ kblocks,
+    const int32_t *__restrict__ segs, const int32_t *__restrict__ chunk_block_ptr,
+    const int32_t *__restrict__ block_ids, int n_kblocks, int pool_blocks, int blk_bytes) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_kblocks) return;
+  const int4 d = kblocks[i];
+  KeyBlockRec r;
+  r.frame = d.x;
+  r.row = d.y;
+  if (d.x < 0) {
+    r.base_pos = 0;
+    r.vis = kKB << 8;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) r.off[b] = -1;
+  } else {
+    const int32_t *sg = segs + 8 * d.x;
+    const int off = sg[0], len = sg[1], seam = sg[2], cid = sg[3];
+    const int nb = (len + kPoolBlockRows - 1) / kPoolBlockRows;
+    const int32_t *bl = block_ids + chunk_block_ptr[cid];
+    r.base_pos = off + d.y;
+    r.vis = max(0, min(kKB, seam - d.y)) | (min(kKB, len - d.y) << 8);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int pb = d.y / kPoolBlockRows + b;
+      const int bid = pb < nb ? bl[pb] : -1;
+      r.off[b] = (unsigned)bid < (unsigned)pool_blocks ? bid * blk_bytes : -1;
+    }
+  }
+  recs[i] = r;
+}
+
 template <int D, bool kHalf>
 __device__ __forceinline__ void attn_bf16_paged_body(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ pool_k,
-    const __bf16 *__restrict__ pool_v, const int32_t *__restrict__ chunk_block_ptr,
-    const int32_t *__restrict__ block_ids, const __bf16 *__restrict__ k_fresh,
+    const __bf16 *__restrict__ pool_v, const __bf16 *__restrict__ k_fresh,
     const __bf16 *__restrict__ v_fresh, __bf16 *__restrict__ out,
     const int32_t *__restrict__ rows, const AttnTile *__restrict__ tiles,
-    const AttnItem *__restrict__ items, const int32_t *__restrict__ segs,
-    const int4 *__restrict__ kblocks, const float2 *__restrict__ angles,
-    float *__restrict__ ws_o, float *__restrict__ ws_ml, int h_q, int h_kv, int tile_rows,
-    float scale_log2, int pool_bytes, int pool_blocks) {
+    const AttnItem *__restrict__ items, const KeyBlockRec *__restrict__ recs,
+    const float2 *__restrict__ angles, float *__restrict__ ws_o, float *__restrict__ ws_ml,
+    int h_q, int h_kv, int tile_rows, float scale_log2, int pool_bytes) {
   constexpr int kRowB = D * 2;
   constexpr int kCPR = D / 8;
   constexpr int kTileB = kKB * kRowB;
@@ -518,80 +561,72 @@ __device__ __forceinline__ void attn_bf16_paged_body(
   // ---- key blocks: item ranges [key_begin, key_end) then [pad0, pad1) ----
   const int n1 = it.key_end - it.key_begin;
   const int n_blocks = n1 + (it.pad1 - it.pad0);
-  auto desc = [&](int ib) { return kblocks[ib < n1 ? it.key_begin + ib : it.pad0 + ib - n1]; };
+  auto desc = [&](int ib) { return recs[ib < n1 ? it.key_begin + ib : it.pad0 + ib - n1]; };
 
   const int tok_bytes = h_kv * D * 2;
-  const int blk_bytes = kPoolBlockRows * tok_bytes;
   const __bf16 *kfh = k_fresh + ((int64_t)fresh_base * h_kv + g) * D;
   const __bf16 *vfh = v_fresh + ((int64_t)fresh_base * h_kv + g) * D;
-  int voff_f[kRounds], voff_p[kRounds];
+  // per-lane byte offsets of the row and chunk each lane stages, relative to the block's
+  // first row (K and V swizzles); everything uniform goes into the resource's base
+  int voff_k[kRounds], voff_v[kRounds];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int R = kRPI * (kBfWaves * r + wave) + lane / kCPR;
     const int pch = lane % kCPR;
-    voff_f[r] = R * tok_bytes + 16 * (pch ^ swz_k<kCPR>(R));
-    voff_p[r] = (R % kPoolBlockRows) * tok_bytes + g * kRowB + 16 * (pch ^ swz_k<kCPR>(R));
-  }
-  int voff_fv[kRounds], voff_pv[kRounds];
-#pragma unroll
-  for (int r = 0; r < kRounds; ++r) {
-    const int R = kRPI * (kBfWaves * r + wave) + lane / kCPR;
-    const int pch = lane % kCPR;
-    voff_fv[r] = R * tok_bytes + 16 * (pch ^ swz_v<kCPR>(R));
-    voff_pv[r] = (R % kPoolBlockRows) * tok_bytes + g * kRowB + 16 * (pch ^ swz_v<kCPR>(R));
+    voff_k[r] = R * tok_bytes + 16 * (pch ^ swz_k<kCPR>(R));
+    voff_v[r] = R * tok_bytes + 16 * (pch ^ swz_v<kCPR>(R));
   }
 
-  // Stage one K (is_v = false) or V block into LDS buffer `buf` (direct loads).
-  // Fresh rows: the block's row offset rides in the per-lane offset, which the range
-  // check sees, so rows past the fresh rows read zeros.  Pool blocks: a block past the
-  // chunk's end or an id outside the pool gets a resource of zero records (zeros); any
-  // other block lies wholly inside the pool, so its offset may ride in the scalar offset.
-  auto issue = [&](int4 dsc, bool is_v, int buf) {
-    if (dsc.x < 0) {
+  // Stage one K (is_v = false) or V block into LDS buffer `buf` (direct loads).  The
+  // resource's base is the block's first row, so the per-lane offsets are the same for
+  // every block.  Fresh rows: the range (rows left in the fresh buffer) clamps rows past
+  // them to zero.  Pool rows: the load of rows r0 .. r0 + kRPI - 1 (one 16-row pool block)
+  // gets that pool block's row 0 minus r0 rows as its base, so the same per-lane offsets
+  // land in it; a pool block past the chunk's end or outside the pool (offset -1) gets a
+  // resource of zero records (zeros), any other lies wholly inside the pool.
+  auto issue = [&](const KeyBlockRec &dsc, bool is_v, int buf) {
+    const int *vo = is_v ? voff_v : voff_k;
+    if (dsc.frame < 0) {
+      const char *base =
+          reinterpret_cast<const char *>(is_v ? vfh : kfh) + (int64_t)dsc.row * tok_bytes;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void *)(is_v ? vfh : kfh), 0, n_fresh * tok_bytes, 0x00020000);
-      const int first = dsc.y * tok_bytes;
+          (void *)base, 0, (n_fresh - dsc.row) * tok_bytes, 0x00020000);
 #pragma unroll
       for (int r = 0; r < kRounds; ++r) {
         const int dst = buf * kTileB + (kBfWaves * r + wave) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16,
-                                                 (is_v ? voff_fv[r] : voff_f[r]) + first, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16, vo[r], 0, 0, 0);
       }
     } else {
-      const int32_t *sg = segs + 8 * dsc.x;
-      const int len = sg[1], cid = sg[3];
-      const int nb = (len + kPoolBlockRows - 1) / kPoolBlockRows;
-      const int32_t *bl = block_ids + chunk_block_ptr[cid];
+      const char *pool = reinterpret_cast<const char *>(is_v ? pool_v : pool_k) + g * kRowB;
 #pragma unroll
       for (int r = 0; r < kRounds; ++r) {
-        const int pb = (dsc.y + kRPI * (kBfWaves * r + wave)) / kPoolBlockRows;
-        const int bid = pb < nb ? bl[pb] : -1;
-        const bool ok = (unsigned)bid < (unsigned)pool_blocks;
+        const int r0 = kRPI * (kBfWaves * r + wave) / kPoolBlockRows * kPoolBlockRows;
+        const int pl = r0 / kPoolBlockRows;  // uniform, 0..3
+        const int o = pl == 0 ? dsc.off[0] : pl == 1 ? dsc.off[1] : pl == 2 ? dsc.off[2] : dsc.off[3];
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(is_v ? pool_v : pool_k), 0, ok ? pool_bytes : 0, 0x00020000);
+            (void *)(pool + (int64_t)o - (int64_t)r0 * tok_bytes), 0, o >= 0 ? 0x7fffffff : 0,
+            0x00020000);
         const int dst = buf * kTileB + (kBfWaves * r + wave) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16,
-                                                 is_v ? voff_pv[r] : voff_p[r],
-                                                 ok ? bid * blk_bytes : 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16, vo[r], 0, 0, 0);
       }
     }
   };
   // After a V block landed: zero V rows past the chunk's end (pool blocks) and record
   // key positions (fresh blocks).
-  auto finish_v = [&](int4 dsc, int buf) {
-    if (dsc.x < 0) {
+  auto finish_v = [&](const KeyBlockRec &dsc, int buf) {
+    if (dsc.frame < 0) {
       if (wave == 0) {
-        const int r = dsc.y + lane;
+        const int r = dsc.row + lane;
         kpos[buf & 1][lane] = r < n_fresh ? rows[fresh_base + r] : 0x7fffffff;
       }
       return;
     }
-    const int len = segs[8 * dsc.x + 1];
-    if (dsc.y + kKB <= len) return;
+    const int nv = dsc.vis >> 8;
+    if (nv >= kKB) return;
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
       const int R = kRPI * (kBfWaves * r + wave) + lane / kCPR;
-      if (dsc.y + R >= len) {
+      if (R >= nv) {
         const int dst = (2 + buf) * kTileB + (kBfWaves * r + wave) * 1024 + 16 * lane;
         *reinterpret_cast<u32x4 *>(lds + dst) = u32x4{0u, 0u, 0u, 0u};
       }
@@ -628,11 +663,11 @@ __device__ __forceinline__ void attn_bf16_paged_body(
     }
   };
 
-  auto softmax_pv = [&](f32x16 (&sc)[2], int4 dsc, int buf, const char *Knext,
+  auto softmax_pv = [&](f32x16 (&sc)[2], const KeyBlockRec &dsc, int buf, const char *Knext,
                         f32x16 (&s_nxt)[2]) {
     constexpr float kLazy = 8.f;
     const char *Vb = lds + (2 + buf) * kTileB;
-    if (dsc.x < 0) {  // fresh keys: positions from LDS
+    if (dsc.frame < 0) {  // fresh keys: positions from LDS
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -641,16 +676,15 @@ __device__ __forceinline__ void attn_bf16_paged_body(
           if (kp > pos) sc[t][j] = kNegInf;
         }
     } else {
-      const int32_t *sg = segs + 8 * dsc.x;
-      const int off = sg[0], len = sg[1], seam = sg[2];
-      if (dsc.y < seam || dsc.y + kKB > len || off + dsc.y + kKB - 1 > pos_min) {
-        const int lim = min(len, pos - off + 1);  // keys t < lim are visible
+      const int s0 = dsc.vis & 255, nv = dsc.vis >> 8;
+      if (s0 > 0 || nv < kKB || dsc.base_pos + kKB - 1 > pos_min) {
+        const int lim = min(nv, pos - dsc.base_pos + 1);  // block keys [s0, lim) are visible
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const int tk = dsc.y + perm_key(t, 8 * (j >> 2) + 4 * grp + (j & 3));
-            if (tk < seam || tk >= lim) sc[t][j] = kNegInf;
+            const int tk = perm_key(t, 8 * (j >> 2) + 4 * grp + (j & 3));
+            if (tk < s0 || tk >= lim) sc[t][j] = kNegInf;
           }
       }
     }
@@ -709,45 +743,55 @@ __device__ __forceinline__ void attn_bf16_paged_body(
     }
     l_lane += ps0 + ps1;
     __builtin_amdgcn_s_setprio(1);
+    constexpr int kPreV = 2;  // V operands in flight ahead of their MFMA
+    bf16x8 vop[4 * kDB];
+    auto vload = [&](int o) {
+      const char *vr = Vb + voff[o % kDB] + (o / kDB) * 16 * kRowB;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vr);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 4 * kRowB));
+      __builtin_memcpy(&vop[o], &lo, 8);
+      __builtin_memcpy(reinterpret_cast<char *>(&vop[o]) + 8, &hi, 8);
+    };
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int o = 0; o < kPreV; ++o) vload(o);
 #pragma unroll
-      for (int d = 0; d < kDB; ++d) {
-        const char *vr = Vb + voff[d] + c * 16 * kRowB;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vr);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 4 * kRowB));
-        bf16x8 a;
-        __builtin_memcpy(&a, &lo, 8);
-        __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &hi, 8);
-        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], acc[d], 0, 0, 0);
-      }
+    for (int o = 0; o < 4 * kDB; ++o) {
+      if (o + kPreV < 4 * kDB) vload(o + kPreV);
+      acc[o % kDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[o], pb[o / kDB], acc[o % kDB], 0, 0, 0);
+    }
+#pragma unroll
+    for (int o = 0; o < kPreV; ++o) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int o = 0; o < 4 * kDB; ++o) {
+      if (o + kPreV < 4 * kDB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
     __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- prologue: K(0), V(0), K(1) ----
-  int4 d0 = desc(0);
+  KeyBlockRec d0 = desc(0);
   issue(d0, false, 0);
   issue(d0, true, 2);
-  int4 d1 = n_blocks > 1 ? desc(1) : d0;
+  KeyBlockRec d1 = n_blocks > 1 ? desc(1) : d0;
   if (n_blocks > 1) issue(d1, false, 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   finish_v(d0, 0);
   __syncthreads();
   f32x16 sa[2], sb[2];
-  set_frame(d0.x < 0 ? -1 : d0.x);
+  set_frame(d0.frame);
   qk(lds, sa);
   __syncthreads();
 
   // Block ib: S^T(ib) is in registers; stage K(ib+2) and V(ib+1), compute S^T(ib+1) in
   // block ib+1's frame, then the softmax and PV of block ib.
-  auto step = [&](int ib, auto bufc, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], int4 dc,
-                  int4 dn) {
+  auto step = [&](int ib, auto bufc, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
+                  const KeyBlockRec &dc, const KeyBlockRec &dn, const KeyBlockRec &dnn) {
     constexpr int kB = decltype(bufc)::value;
-    if (ib + 2 < n_blocks) issue(desc(ib + 2), false, kB);
+    if (ib + 2 < n_blocks) issue(dnn, false, kB);
     if (ib + 1 < n_blocks) {
       issue(dn, true, 2 + (kB ^ 1));
-      set_frame(dn.x < 0 ? -1 : dn.x);
+      set_frame(dn.frame);
     }
     softmax_pv(s_cur, dc, kB, lds + (kB ^ 1) * kTileB, s_nxt);
     if (ib + 1 < n_blocks) {
@@ -757,15 +801,18 @@ __device__ __forceinline__ void attn_bf16_paged_body(
     }
   };
 
-  int4 dc = d0, dn = d1;
+  // the records of blocks ib, ib+1 and ib+2 are in registers at step ib
+  KeyBlockRec dc = d0, dn = d1, dnn = n_blocks > 2 ? desc(2) : d1;
   for (int ib = 0; ib < n_blocks; ib += 2) {
-    step(ib, std::integral_constant<int, 0>{}, sa, sb, dc, dn);
+    step(ib, std::integral_constant<int, 0>{}, sa, sb, dc, dn, dnn);
     dc = dn;
-    dn = ib + 2 < n_blocks ? desc(ib + 2) : dc;
+    dn = dnn;
+    dnn = ib + 3 < n_blocks ? desc(ib + 3) : dn;
     if (ib + 1 < n_blocks) {
-      step(ib + 1, std::integral_constant<int, 1>{}, sb, sa, dc, dn);
+      step(ib + 1, std::integral_constant<int, 1>{}, sb, sa, dc, dn, dnn);
       dc = dn;
-      dn = ib + 3 < n_blocks ? desc(ib + 3) : dc;
+      dn = dnn;
+      dnn = ib + 4 < n_blocks ? desc(ib + 4) : dn;
     }
   }
 
@@ -805,18 +852,15 @@ __device__ __forceinline__ void attn_bf16_paged_body(
 template <int D, bool kHalf>
 __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_paged_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ pool_k,
-    const __bf16 *__restrict__ pool_v, const int32_t *__restrict__ chunk_block_ptr,
-    const int32_t *__restrict__ block_ids, const __bf16 *__restrict__ k_fresh,
+    const __bf16 *__restrict__ pool_v, const __bf16 *__restrict__ k_fresh,
     const __bf16 *__restrict__ v_fresh, __bf16 *__restrict__ out,
     const int32_t *__restrict__ rows, const AttnTile *__restrict__ tiles,
-    const AttnItem *__restrict__ items, const int32_t *__restrict__ segs,
-    const int4 *__restrict__ kblocks, const float2 *__restrict__ angles,
-    float *__restrict__ ws_o, float *__restrict__ ws_ml, int h_q, int h_kv, int tile_rows,
-    float scale_log2, int pool_bytes, int pool_blocks) {
-  attn_bf16_paged_body<D, kHalf>(q, pool_k, pool_v, chunk_block_ptr, block_ids, k_fresh,
-                                 v_fresh, out, rows, tiles, items, segs, kblocks, angles, ws_o,
-                                 ws_ml, h_q, h_kv, tile_rows, scale_log2, pool_bytes,
-                                 pool_blocks);
+    const AttnItem *__restrict__ items, const KeyBlockRec *__restrict__ recs,
+    const float2 *__restrict__ angles, float *__restrict__ ws_o, float *__restrict__ ws_ml,
+    int h_q, int h_kv, int tile_rows, float scale_log2, int pool_bytes) {
+  attn_bf16_paged_body<D, kHalf>(q, pool_k, pool_v, k_fresh, v_fresh, out, rows, tiles, items,
+                                 recs, angles, ws_o, ws_ml, h_q, h_kv, tile_rows, scale_log2,
+                                 pool_bytes);
 }
 
 // ======================== decode over the shared pool =========================
@@ -1514,12 +1558,17 @@ namespace pic {
 namespace {
 
 // Workspace layout: partial O [slots][kM][D], partial (m, l) [slots][kM][2], then for
-// paged plans the angle table [n_chunks][D/2] float2 (16-byte aligned).
+// paged plans the angle table [n_chunks][D/2] float2 and the key-block records
+// [n_kblocks] (sections 16-byte aligned).
 size_t partial_bytes(const PlanHeader &h, int head_dim) {
   return (size_t)h[PIC_H_N_PARTIALS] * kM * ((size_t)head_dim + 2) * sizeof(float);
 }
 size_t angle_offset(const PlanHeader &h, int head_dim) {
   return (partial_bytes(h, head_dim) + 15) / 16 * 16;
+}
+size_t keyblock_offset(const PlanHeader &h, int head_dim) {
+  return angle_offset(h, head_dim) +
+         ((size_t)h[PIC_H_N_CHUNKS] * (head_dim / 2) * sizeof(float2) + 15) / 16 * 16;
 }
 
 template <int D, bool kHalf>
@@ -1537,6 +1586,7 @@ int launch_paged(const PlanHeader &h, const int32_t *plan_dev, const void *q, co
   float *ws_o = reinterpret_cast<float *>(ws);
   float *ws_ml = ws_o + (int64_t)h[PIC_H_N_PARTIALS] * kM * D;
   float2 *angles = reinterpret_cast<float2 *>(ws + angle_offset(h, D));
+  KeyBlockRec *recs = reinterpret_cast<KeyBlockRec *>(ws + keyblock_offset(h, D));
   const int n_chunks = h[PIC_H_N_CHUNKS];
   if (n_chunks > 0) {
     const int64_t total = (int64_t)n_chunks * (D / 2);
@@ -1545,13 +1595,21 @@ int launch_paged(const PlanHeader &h, const int32_t *plan_dev, const void *q, co
                        n_chunks, D / 2, make_theta(D, rope_base));
     PIC_LAUNCH_CHECK();
   }
+  const int tok_bytes = h[PIC_H_H_KV] * D * 2;
+  const int n_kblocks = h[PIC_H_N_KBLOCKS];
+  if (n_kblocks > 0) {
+    hipLaunchKernelGGL(paged_blocks_kernel, dim3((n_kblocks + 255) / 256), dim3(256), 0, s,
+                       recs, kblocks, segs, cbp, bids, n_kblocks, (int)pool_blocks,
+                       kPoolBlockRows * tok_bytes);
+    PIC_LAUNCH_CHECK();
+  }
   hipLaunchKernelGGL((attn_bf16_paged_kernel<D, kHalf>), dim3(h[PIC_H_N_ATTN_ITEMS]),
                      dim3(kBfThreads), 0, s, static_cast<const __bf16 *>(q),
                      static_cast<const __bf16 *>(pool_k), static_cast<const __bf16 *>(pool_v),
-                     cbp, bids, static_cast<const __bf16 *>(kf), static_cast<const __bf16 *>(vf),
-                     static_cast<__bf16 *>(out), rows, tiles, items, segs, kblocks, angles, ws_o,
-                     ws_ml, h[PIC_H_H_Q], h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], scale * kLog2e,
-                     (int)(pool_blocks * kPoolBlockRows * h[PIC_H_H_KV] * D * 2), (int)pool_blocks);
+                     static_cast<const __bf16 *>(kf), static_cast<const __bf16 *>(vf),
+                     static_cast<__bf16 *>(out), rows, tiles, items, recs, angles, ws_o, ws_ml,
+                     h[PIC_H_H_Q], h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], scale * kLog2e,
+                     (int)(pool_blocks * kPoolBlockRows * tok_bytes));
   PIC_LAUNCH_CHECK();
   if (h[PIC_H_N_MERGE] > 0) {
     const int64_t threads = (int64_t)h[PIC_H_N_MERGE] * kM * (D / 4);
@@ -1675,7 +1733,7 @@ extern "C" size_t pic_attn_workspace_bytes(const int32_t *plan_host, int32_t hea
   const PlanHeader h{plan_host};
   if (!h.valid() || head_dim <= 0) return 0;
   if (!h[PIC_H_PAGED]) return partial_bytes(h, head_dim);
-  return angle_offset(h, head_dim) + (size_t)h[PIC_H_N_CHUNKS] * (head_dim / 2) * sizeof(float2);
+  return keyblock_offset(h, head_dim) + (size_t)h[PIC_H_N_KBLOCKS] * sizeof(KeyBlockRec);
 }
 
 extern "C" int pic_selective_attn_paged(

@@ -31,6 +31,7 @@ SHORT = [("qkv_rope_gemm_kernel", "qkv_rope_gemm"), ("out_proj_gemm_kernel", "ou
          ("state_compose_kernel", "state_compose"),
          ("row_angles_kernel", "row_angles"),
          ("attn_bf16_paged_kernel", "attn_bf16_paged"), ("paged_angles_kernel", "paged_angles"),
+         ("paged_blocks_kernel", "paged_blocks"),
          ("dec_attn_kernel", "dec_attn"), ("dec_merge_kernel", "dec_merge"),
          ("attn_bf16_kernel", "attn_bf16"), ("attn_f32_kernel", "attn_f32"),
          ("merge_kernel", "merge"), ("rope_delta_kernel", "rope_delta"),

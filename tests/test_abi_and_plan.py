@@ -111,6 +111,26 @@ def test_device_entry_points_reject_bad_arguments_without_launching():
     assert L.pic_attn_workspace_bytes(bp, 128) == 0
 
 
+def test_paged_workspace_covers_partials_angles_and_key_block_records():
+    # the paged call keeps split-KV partials, a cos/sin table per chunk and one 32-byte
+    # record per key block in the caller's workspace; one byte short is refused
+    L = P.lib()
+    f = ctypes.c_void_p(0x1000)
+    plan = P.pic_build_index([[3000, 7000, 2600], [9000]], [40, 9], 8, 8, 2,
+                             chunk_ids_per_req=[[0, 1, 2], [3]], n_cu=2)
+    d = 128
+    ws = P.pic_attn_workspace_bytes(plan, d)
+    partials = plan[P.H_N_PARTIALS] * P.PIC_ATTN_TILE_M * (d + 2) * 4
+    angles = plan[P.H_N_CHUNKS] * (d // 2) * 8
+    assert plan[P.H_N_PARTIALS] > 0 and plan[P.H_N_KBLOCKS] > 0
+    assert ws >= partials + angles + 32 * plan[P.H_N_KBLOCKS]
+    assert ws <= partials + angles + 32 * plan[P.H_N_KBLOCKS] + 32
+    call = lambda wsb: L.pic_selective_attn_paged(
+        plan.host_ptr(), f, f, f, f, 64, 16, f, 4, f, f, f, f, P.PIC_BF16, d,
+        P.PIC_ROPE_ADJACENT, 1e4, 0.088, f, wsb, None)
+    assert call(ws - 1) == P.PIC_ENOSPC
+
+
 def test_state_compose_rejects_bad_arguments_without_launching():
     L = P.lib()
     f = ctypes.c_void_p(0x1000)
