@@ -174,12 +174,13 @@ __device__ __forceinline__ void attn_bf16_body(
   auto issue = [&](const __bf16 *base, const int (&voffs)[kRounds], int kb0, int buf) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, n_records, 0x00020000);
-    const int first = kb0 * tok_bytes;
+    // unsigned: rows past the request's end may lie past 2^31 bytes (read as zeros)
+    const unsigned first = (unsigned)kb0 * (unsigned)tok_bytes;
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
       const int dst = buf * kTileB + (kBfWaves * r + wave) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16, voffs[r] + first,
-                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lds + dst), 16,
+                                               (int)((unsigned)voffs[r] + first), 0, 0, 0);
     }
   };
 

@@ -14,7 +14,9 @@ round-to-nearest-even.
 
 Recipe (all draws use ``torch.Generator`` on the CPU, Mersenne Twister, seeded):
   * chunk lengths: ``numpy.random.default_rng(seed)`` integers, inclusive bounds;
-  * tensors: ``torch.randn(float32) * scale`` then ``.to(dtype)`` (RNE for bf16).
+  * tensors: ``torch.randn(float32) * scale`` then ``.to(dtype)`` (RNE for bf16);
+  * the size-limit request's 2 GiB K/V buffers: the same on the GPU with torch's
+    seeded device generator (``device_context_tensors``).
 """
 
 from dataclasses import dataclass, field
@@ -107,6 +109,16 @@ def shared_pool(n_pool=256, n_req=8, m_lo=96, m_hi=128, q_len=128, w=8, seed=5):
                     seed=seed)
 
 
+def single_huge(n_tokens, q_len=64, chunk=65536, k=2, seed=6):
+    """One request of exactly ``n_tokens`` tokens (``q_len`` query tokens, the context
+    in chunks of ``chunk`` tokens, the last one shorter), GQA 32/8, D = 128, bf16: the
+    size-limit case.  Its K/V come from ``device_context_tensors``."""
+    ctx = n_tokens - q_len
+    lens = [chunk] * (ctx // chunk) + ([ctx % chunk] if ctx % chunk else [])
+    return Workload("single_huge", "bf16", 32, 8, 128, 500000.0, k, [Request(lens, q_len)],
+                    seed=seed)
+
+
 def pool_block_table(wl):
     """Physical block ids of every pool chunk, in a shuffled physical order.
 
@@ -145,6 +157,23 @@ def context_tensors(wl):
     k_buf = draw(shape, wl.seed * 7 + 1, wl.torch_dtype, wl.value_scale)
     v_buf = draw(shape, wl.seed * 7 + 2, wl.torch_dtype, wl.value_scale)
     return k_buf, v_buf
+
+
+def device_context_tensors(wl, device):
+    """Like ``context_tensors`` but drawn on ``device`` with torch's seeded device
+    generator (Philox), for buffers whose host draw would take minutes; slices are
+    copied to the host for the oracle."""
+    shape = (wl.n_tokens, wl.h_kv, wl.head_dim)
+    out = []
+    for j in (1, 2):
+        g = torch.Generator(device=device)
+        g.manual_seed(int(wl.seed * 7 + j))
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if wl.value_scale != 1.0:
+            x.mul_(float(wl.value_scale))
+        out.append(x.to(wl.torch_dtype))
+        del x
+    return out[0], out[1]
 
 
 def fresh_tensors(wl, n_rows):

@@ -111,6 +111,21 @@ def test_device_entry_points_reject_bad_arguments_without_launching():
     assert L.pic_attn_workspace_bytes(bp, 128) == 0
 
 
+def test_request_size_limit_is_checked_before_launch():
+    # K/V of one request are addressed with 32-bit byte offsets: 0x7fff0000 bytes of K
+    # (N * h_kv * D * 2) are taken, one token more is refused without a launch
+    L = P.lib()
+    f = ctypes.c_void_p(0x1000)
+    n_max = 0x7FFF0000 // (8 * 128 * 2)
+    for n, want in ((n_max + 1, P.PIC_EUNSUPPORTED), (n_max, P.PIC_EINVAL)):
+        plan = P.pic_build_index([[n - 64]], [64], 2, 32, 8)
+        assert plan.n_tokens == n
+        # a null output pointer is the only other fault, so the size check comes first
+        st = L.pic_selective_attn(plan.host_ptr(), f, f, f, f, None, P.PIC_BF16, 128, 0.088,
+                                  f, 1 << 40, None)
+        assert st == want
+
+
 def test_paged_workspace_covers_partials_angles_and_key_block_records():
     # the paged call keeps split-KV partials, a cos/sin table per chunk and one 32-byte
     # record per key block in the caller's workspace; one byte short is refused

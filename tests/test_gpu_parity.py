@@ -288,3 +288,82 @@ def test_scheme_b_epic_sweep_full_size_sampled():
     # every kept row of the 4 x ~50k batch rotated at its global position (chunk 0
     # included), sampled attention rows, launched as bench.py launches it (n_cu = 256)
     check_run(Run(W.epic_sweep(k=16), n_cu=256, scheme="nope"), sample_rows=24)
+
+
+# K/V of one request are addressed with 32-bit byte offsets: pic_selective_attn takes
+# requests up to 0x7fff0000 bytes of K (N * h_kv * D * 2), and refuses larger ones
+MAX_REQUEST_BYTES = 0x7FFF0000
+
+
+def test_max_request_size_sampled():
+    # the largest request the contiguous path takes: 1,048,544 tokens of 8 KV heads of
+    # 128 (2 GiB of K and of V), 16 chunks, k = 2, in the launch configuration bench.py
+    # times.  Rotated rows at the top of the buffer, every spliced row, and sampled
+    # attention rows (the last query row among them) against the oracle.
+    n_max = MAX_REQUEST_BYTES // (8 * 128 * 2)
+    wl = W.single_huge(n_max)
+    r = wl.requests[0]
+    plan = P.pic_build_index([r.chunk_lens], [r.q_len], wl.k, wl.h_q, wl.h_kv, n_cu=256)
+    plan.to_device()
+    assert plan.n_tokens == n_max
+    dev = "cuda"
+    say("max request: drawing K/V on the device", plan.n_tokens, "tokens")
+    k, v = W.device_context_tensors(wl, dev)
+    q_h, kf_h, vf_h = W.fresh_tensors(wl, plan.n_rows)
+    groups = [0, wl.h_kv - 1]  # KV heads checked against the oracle
+    k_in = {g: k[:, g, :].cpu() for g in groups}
+    v_in = {g: v[:, g, :].cpu() for g in groups}
+    q, kf, vf = q_h.to(dev), kf_h.to(dev), vf_h.to(dev)
+    out = torch.full_like(q, float("nan"))
+    say("max request: rope_delta, splice, selective_attn (items=%d merges=%d)"
+        % (plan[P.H_N_ATTN_ITEMS], plan[P.H_N_MERGE]))
+    P.pic_rope_delta(plan, k, wl.rope_base)
+    torch.cuda.synchronize()
+    rows = O.recompute_positions(r.chunk_lens, r.q_len, wl.k)
+    assert plan.rows.tolist() == rows
+    offs = O.chunk_offsets(r.chunk_lens)
+    ctx = offs[-1]
+    # rotated K: the last 64 kept rows of the buffer and 64 random kept rows, all heads
+    rec = set(rows)
+    kept_tail = [j for j in range(ctx - 1, -1, -1) if j not in rec][:64]
+    rng = np.random.default_rng(77)
+    picks = sorted(set(kept_tail) | {int(j) for j in rng.integers(0, ctx, 64) if int(j) not in rec})
+    pick_t = torch.tensor(picks, dtype=torch.long, device=dev)
+    got_rot = f64(k.index_select(0, pick_t))
+    say("max request: oracle rotation of", len(picks), "sampled rows")
+    chunk_of = np.searchsorted(np.asarray(offs[1:]), np.asarray(picks), side="right")
+    k_pre = {g: f64(k_in[g][picks]) for g in groups}
+    for g in groups:
+        want = O.rope_rotate(k_pre[g][:, None, :], np.asarray(offs)[chunk_of], wl.rope_base)[:, 0]
+        err = float(np.max(np.abs(got_rot[:, g] - want)))
+        say("rope_delta head", g, "max-abs error", err)
+        assert err <= TOL["bf16"]
+    P.pic_splice(plan, k, v, kf, vf)
+    ws = P.attn_workspace(plan, wl.head_dim)
+    P.pic_selective_attn(plan, q, k, v, out, workspace=ws)
+    torch.cuda.synchronize()
+    rows_t = torch.tensor(rows, dtype=torch.long, device=dev)
+    assert torch.equal(k.index_select(0, rows_t).cpu(), kf_h)
+    assert torch.equal(v.index_select(0, rows_t).cpu(), vf_h)
+    out_h = out.cpu()
+    assert torch.isfinite(out_h.float()).all()
+    # attention: sampled (row, head) pairs in the checked KV heads, against the oracle
+    # chained from the same inputs (rotation per chunk, splice of the fresh rows)
+    n = len(rows)
+    G = wl.h_q // wl.h_kv
+    sample = sorted({0, n - 1, n - 2, n - 64, 1, 15, 29} | set(rng.integers(0, n, 5).tolist()))
+    for g in groups:
+        say("max request: oracle K/V of KV head", g)
+        kin = f64(k_in[g])[:, None, :]
+        vin = f64(v_in[g])[:, None, :]
+        k_ctx = O.rope_delta([kin[offs[c]:offs[c + 1]] for c in range(len(r.chunk_lens))],
+                             wl.rope_base)
+        kx, vx = O.splice(k_ctx, vin[:ctx], f64(kf_h[:, g:g + 1]), f64(vf_h[:, g:g + 1]), rows,
+                          plan.n_tokens)
+        heads = [g * G + (i % G) for i in sample]
+        want = O.attn_rows_direct([f64(q_h[i, h]) for i, h in zip(sample, heads)], kx, vx,
+                                  [rows[i] for i in sample], [0] * len(sample))
+        got = np.stack([f64(out_h[i, h]) for i, h in zip(sample, heads)])
+        err = float(np.max(np.abs(got - want)))
+        say("selective_attn head group", g, "max-abs error", err)
+        assert err <= TOL["bf16"]
