@@ -159,21 +159,24 @@ def context_tensors(wl):
     return k_buf, v_buf
 
 
+def device_draw(shape, seed, dtype, device, scale=1.0):
+    """N(0, 1) * scale rounded to ``dtype``, drawn on ``device`` with torch's seeded
+    device generator (Philox): for buffers whose host draw would take minutes (slices
+    are copied to the host for the oracle)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(tuple(int(s) for s in shape), generator=g, device=device,
+                    dtype=torch.float32)
+    if scale != 1.0:
+        x.mul_(float(scale))
+    return x.to(dtype)
+
+
 def device_context_tensors(wl, device):
-    """Like ``context_tensors`` but drawn on ``device`` with torch's seeded device
-    generator (Philox), for buffers whose host draw would take minutes; slices are
-    copied to the host for the oracle."""
+    """``context_tensors`` drawn on ``device`` (``device_draw``)."""
     shape = (wl.n_tokens, wl.h_kv, wl.head_dim)
-    out = []
-    for j in (1, 2):
-        g = torch.Generator(device=device)
-        g.manual_seed(int(wl.seed * 7 + j))
-        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
-        if wl.value_scale != 1.0:
-            x.mul_(float(wl.value_scale))
-        out.append(x.to(wl.torch_dtype))
-        del x
-    return out[0], out[1]
+    return tuple(device_draw(shape, wl.seed * 7 + j, wl.torch_dtype, device, wl.value_scale)
+                 for j in (1, 2))
 
 
 def fresh_tensors(wl, n_rows):

@@ -126,6 +126,22 @@ def test_request_size_limit_is_checked_before_launch():
         assert st == want
 
 
+def test_pool_size_limit_is_checked_before_launch():
+    # pool K/V are addressed with 32-bit byte offsets: a pool of up to 0x7fff0000 bytes
+    # less one block is taken, one block more is refused without a launch
+    L = P.lib()
+    f = ctypes.c_void_p(0x1000)
+    plan = P.pic_build_index([[40, 50]], [7], 2, 32, 4, chunk_ids_per_req=[[0, 1]])
+    blk = 16 * 4 * 128 * 2
+    n_max = (0x7FFF0000 - blk) // blk
+    for nb, want in ((n_max + 1, P.PIC_EUNSUPPORTED), (n_max, P.PIC_EINVAL)):
+        # a null output pointer is the only other fault, so the size check comes first
+        st = L.pic_selective_attn_paged(plan.host_ptr(), f, f, f, f, nb, 16, f, 2, f, f, f,
+                                        None, P.PIC_BF16, 128, P.PIC_ROPE_ADJACENT, 1e4, 0.088,
+                                        f, 1 << 40, None)
+        assert st == want
+
+
 def test_paged_workspace_covers_partials_angles_and_key_block_records():
     # the paged call keeps split-KV partials, a cos/sin table per chunk and one 32-byte
     # record per key block in the caller's workspace; one byte short is refused

@@ -241,3 +241,70 @@ def test_decode_shared_pool_full_size():
     # the shared-pool batch (8 requests x ~116k tokens from 256 pooled chunks, w = 8):
     # every request's output against the oracle
     run_decode(W.shared_pool(), n_cu=256)
+
+
+# pool K (and V) of pic_selective_attn_paged are addressed with 32-bit byte offsets:
+# pool_blocks * 16 * h_kv * D * 2 <= 0x7fff0000 - 16 * h_kv * D * 2
+POOL_LIMIT_BYTES = 0x7FFF0000
+
+
+def test_largest_pool_prefill_and_decode():
+    # a 2 GiB pool (131,066 blocks of 16 tokens, 4 KV heads of 128): one chunk in the
+    # pool's last blocks in descending order, one on random blocks, one just below the
+    # first; two requests splice them (one chunk shared).  Prefill of every row and the
+    # decode step of both requests against the oracle.
+    tok_bytes = 4 * 128 * 2
+    n_blocks = (POOL_LIMIT_BYTES - 16 * tok_bytes) // (16 * tok_bytes)
+    lens = [4100, 3000, 2500]
+    need = [-(-L // 16) for L in lens]
+    rng = np.random.default_rng(83)
+    b0 = np.arange(n_blocks - 1, n_blocks - 1 - need[0], -1)
+    b2 = np.arange(n_blocks - need[0] - need[2], n_blocks - need[0])
+    rest = np.setdiff1d(np.arange(n_blocks), np.concatenate([b0, b2]))
+    b1 = rng.choice(rest, need[1], replace=False)
+    blocks = np.concatenate([b0, b1, b2]).astype(np.int32)
+    cbp = np.concatenate([[0], np.cumsum(need)]).astype(np.int32)
+    reqs = [W.Request([lens[0], lens[1], lens[2]], 64, chunk_ids=[0, 1, 2]),
+            W.Request([lens[2], lens[0]], 32, chunk_ids=[2, 0])]
+    wl = W.Workload("largest_pool", "bf16", 32, 4, 128, 500000.0, 8, reqs, pool_lens=lens,
+                    block_size=16, seed=71)
+    plan = P.pic_build_index([r.chunk_lens for r in reqs], [r.q_len for r in reqs], wl.k,
+                             wl.h_q, wl.h_kv, n_cu=256, chunk_ids_per_req=[r.chunk_ids for r in reqs])
+    plan.to_device()
+    dev = "cuda"
+    say("largest pool: drawing", n_blocks, "blocks on the device")
+    shape = (n_blocks, 16, wl.h_kv, wl.head_dim)
+    pk = W.device_draw(shape, 711, torch.bfloat16, dev)
+    pv = W.device_draw(shape, 712, torch.bfloat16, dev)
+    assert pk.numel() * 2 <= POOL_LIMIT_BYTES - 16 * tok_bytes
+    used = torch.from_numpy(blocks.astype(np.int64)).to(dev)
+    mini_k, mini_v = f64(pk.index_select(0, used)), f64(pv.index_select(0, used))
+    mini_ids = np.arange(len(blocks))  # chunk i's blocks, in order, in the host copy
+    q, kf, vf = W.fresh_tensors(wl, plan.n_rows)
+    qn, kn, vn = W.decode_tensors(wl)
+    out = torch.full((plan.n_rows, wl.h_q, wl.head_dim), float("nan"), dtype=q.dtype, device=dev)
+    cbp_d, blocks_d = torch.from_numpy(cbp).to(dev), torch.from_numpy(blocks).to(dev)
+    say("largest pool: prefill items=%d, decode pieces=%d" % (plan[P.H_N_ATTN_ITEMS],
+                                                              plan[P.H_N_DEC_PIECES]))
+    P.pic_selective_attn_paged(plan, q.to(dev), pk, pv, cbp_d, blocks_d, kf.to(dev), vf.to(dev),
+                               out, wl.rope_base, workspace=P.attn_workspace(plan, wl.head_dim))
+    dec = torch.full(qn.shape, float("nan"), dtype=qn.dtype, device=dev)
+    P.pic_decode_attn_paged(plan, qn.to(dev), kn.to(dev), vn.to(dev), pk, pv, cbp_d, blocks_d,
+                            kf.to(dev), vf.to(dev), dec, wl.rope_base)
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(pk.index_select(0, used)), mini_k)  # pool untouched
+    got_all, dec_all = f64(out.cpu()), f64(dec.cpu())
+    assert np.isfinite(got_all).all() and np.isfinite(dec_all).all()
+    for b, r in enumerate(reqs):
+        row0, row1 = int(plan.req_row_ptr[b]), int(plan.req_row_ptr[b + 1])
+        rows = O.recompute_positions(r.chunk_lens, r.q_len, wl.k)
+        assert plan.rows[row0:row1].tolist() == rows
+        ck = [O.gather_paged_chunk(mini_k, mini_ids[cbp[i]:cbp[i + 1]], lens[i]) for i in r.chunk_ids]
+        cv = [O.gather_paged_chunk(mini_v, mini_ids[cbp[i]:cbp[i + 1]], lens[i]) for i in r.chunk_ids]
+        k_ctx, v_ctx = O.rope_delta(ck, wl.rope_base), O.concat_chunks(cv)
+        kx, vx = O.splice(k_ctx, v_ctx, f64(kf[row0:row1]), f64(vf[row0:row1]), rows,
+                          sum(r.chunk_lens) + r.q_len)
+        err = float(np.max(np.abs(got_all[row0:row1] - O.selective_attn(f64(q[row0:row1]), kx, vx, rows))))
+        derr = float(np.max(np.abs(dec_all[b] - O.decode_attn(f64(qn[b]), kx, vx, f64(kn[b]), f64(vn[b])))))
+        say("largest pool request", b, "prefill max-abs error", err, "decode", derr)
+        assert err <= TOL and derr <= TOL
