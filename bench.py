@@ -95,6 +95,13 @@ def make_workload(name, k):
     return W.epic_sweep(k=k)
 
 
+def pct(times_ms):
+    """p50 / p95 of per-step event times (ms)."""
+    t = np.asarray(times_ms, dtype=np.float64)
+    return {"p50_ms": round(float(np.percentile(t, 50)), 4),
+            "p95_ms": round(float(np.percentile(t, 95)), 4)}
+
+
 def src_hash(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -272,7 +279,8 @@ def bench_paged(args, wl):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / args.steps
-    t_attn = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    l_attn = [e[0].elapsed_time(e[1]) for e in ev]
+    t_attn = float(np.mean(l_attn))
     tokens = plan.n_tokens
     attn_tflops = attn_flops / (t_attn * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[wl.dtype]
@@ -302,7 +310,7 @@ def bench_paged(args, wl):
                                "paged_blocks_kernel + attn_bf16_paged_kernel + merge_kernel)",
                      "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes},
         "kernels": {
-            "selective_attn_paged": {"ms": round(t_attn, 4), "flops": attn_flops,
+            "selective_attn_paged": {"ms": round(t_attn, 4), **pct(l_attn), "flops": attn_flops,
                                      "TFLOP_s": round(attn_tflops, 2),
                                      "items": plan[P.H_N_ATTN_ITEMS], "merges": plan[P.H_N_MERGE]},
             "host_plan_ms": round(1e3 * float(np.mean(plan_s)), 4),
@@ -366,7 +374,8 @@ def bench_decode(args, wl):
         step(i)
     torch.cuda.synchronize()
     ms_step = 1e3 * (time.perf_counter() - t0) / args.steps
-    t_dec = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    l_dec = [e[0].elapsed_time(e[1]) for e in ev]
+    t_dec = float(np.mean(l_dec))
     gbs = dec_bytes / (t_dec * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
@@ -393,7 +402,7 @@ def bench_decode(args, wl):
                                "dec_attn_kernel + dec_merge_kernel)",
                      "algorithmic_bytes": dec_bytes,
                      "per_request_streaming_bytes": per_request_bytes},
-        "kernels": {"decode_attn": {"ms": round(t_dec, 4), "GB_s": round(gbs, 1),
+        "kernels": {"decode_attn": {"ms": round(t_dec, 4), **pct(l_dec), "GB_s": round(gbs, 1),
                                     "items": plan[P.H_N_DEC_ITEMS], "uses": plan[P.H_N_DEC_USES],
                                     "pieces": plan[P.H_N_DEC_PIECES],
                                     "workgroups": plan[P.H_N_DEC_WG],
@@ -491,7 +500,8 @@ def bench_link(args, wl):
         step(i)
     torch.cuda.synchronize()
     ms_step = 1e3 * (time.perf_counter() - t0) / args.steps
-    t_link = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    l_link = [e[0].elapsed_time(e[1]) for e in ev]
+    t_link = float(np.mean(l_link))
 
     # per-kernel breakdown: the same entry points pic_link calls, one event between each
     names = ("rope_delta", "qkv_rope", "splice", "selective_attn", "out_proj")
@@ -537,6 +547,7 @@ def bench_link(args, wl):
                    "layers": n_layers, "d_model": d_model, "h_q": hq, "h_kv": hkv,
                    "head_dim": D, "rope_base": wl.rope_base, "parallelism": "none (1 GPU)"},
         "link_ms": round(t_link, 4),
+        "link_p50_ms": pct(l_link)["p50_ms"], "link_p95_ms": pct(l_link)["p95_ms"],
         "link_tflops": round(link_flops / (t_link * 1e-3) / 1e12, 2),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
@@ -629,7 +640,8 @@ def bench_state(args, wl):
         step(i)
     torch.cuda.synchronize()
     ms_step = 1e3 * (time.perf_counter() - t0) / args.steps
-    t_call = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    l_call = [e[0].elapsed_time(e[1]) for e in ev]
+    t_call = float(np.mean(l_call))
     tflops = flops / (t_call * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS["f32"]
     rec = {
@@ -649,7 +661,8 @@ def bench_state(args, wl):
                      "kernel": "pic_state_compose call (state_compose_kernel)",
                      "algorithmic_flops": flops, "algorithmic_bytes": alg_bytes,
                      "hbm_GB_s_at_algorithmic_bytes": round(alg_bytes / (t_call * 1e-3) / 1e9, 1)},
-        "kernels": {"state_compose": {"ms": round(t_call, 4), "TFLOP_s": round(tflops, 2),
+        "kernels": {"state_compose": {"ms": round(t_call, 4), **pct(l_call),
+                                      "TFLOP_s": round(tflops, 2),
                                       "products": steps}},
     }
     if not args.no_cpu_baseline:
@@ -757,9 +770,10 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / args.steps
 
-    t_rope = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    t_splice = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    l_rope = [e[0].elapsed_time(e[1]) for e in ev]
+    l_splice = [e[1].elapsed_time(e[2]) for e in ev]
+    l_attn = [e[2].elapsed_time(e[3]) for e in ev]
+    t_rope, t_splice, t_attn = (float(np.mean(x)) for x in (l_rope, l_splice, l_attn))
     tokens = plan.n_tokens
     value = tokens / (ms_step * 1e-3)
     attn_tflops = attn_flops / (t_attn * 1e-3) / 1e12
@@ -791,13 +805,13 @@ def main():
                      "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes},
         "kernels": {
             ("rope_apply" if args.rope_scheme == "nope" else "rope_delta"): {
-                "ms": round(t_rope, 4), "bytes": rope_bytes,
+                "ms": round(t_rope, 4), **pct(l_rope), "bytes": rope_bytes,
                            "GB_s": round(rope_bytes / (t_rope * 1e-3) / 1e9, 1),
                            "hbm_frac": round(rope_bytes / (t_rope * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-            "splice": {"ms": round(t_splice, 4), "bytes": splice_bytes,
+            "splice": {"ms": round(t_splice, 4), **pct(l_splice), "bytes": splice_bytes,
                        "GB_s": round(splice_bytes / (t_splice * 1e-3) / 1e9, 1),
                        "hbm_frac": round(splice_bytes / (t_splice * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-            "selective_attn": {"ms": round(t_attn, 4), "flops": attn_flops,
+            "selective_attn": {"ms": round(t_attn, 4), **pct(l_attn), "flops": attn_flops,
                                "TFLOP_s": round(attn_tflops, 2),
                                "items": plan[P.H_N_ATTN_ITEMS], "merges": plan[P.H_N_MERGE]},
             "host_plan_ms": round(1e3 * float(np.mean(plan_s)), 4),
