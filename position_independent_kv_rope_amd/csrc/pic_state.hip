@@ -11,12 +11,13 @@
 // One workgroup per (request, head), 8 waves.  S_{j-1} lives in LDS (it is the B
 // operand every wave reads), the chunk's T [128 x 128] is staged to LDS through
 // registers, and each wave computes a 32 x 64 block of S_j with v_mfma_f32_16x16x4_f32
-// (fp32 operands and accumulation: the scan compounds rounding, so no bf16 here).  The
-// row strides of the two LDS tiles (132 and 144 floats, S also with a 16-column block
-// swizzle) make the MFMA operand reads and the state writes conflict-free: A reads 16
-// rows x 4 k of T, B reads 4 k x 16 columns of S.  While a
-// chunk is multiplied, the next chunk's T and S(C|0) are already being loaded into
-// registers.
+// (fp32 operands and accumulation: the scan compounds rounding, so no bf16 here).  T rows
+// have a stride of 132 floats, so the A reads (16 rows x 4 k) are conflict-free.  S is
+// kept with its four 16-column blocks of each 64-column half interleaved, so a lane's B
+// operands for the four column tiles of one k are one 16-byte read, and its four
+// accumulator values of one row one 16-byte write (16 lanes cover 256 contiguous
+// bytes).  While a chunk is multiplied, the next chunk's T and S(C|0) are already being
+// loaded into registers.
 #include <algorithm>
 
 #include "pic_device.h"
@@ -28,13 +29,13 @@ namespace {
 constexpr int kSD = 128;                  // d_k = d_v
 constexpr int kSThreads = 512;            // 8 waves: 4 row blocks x 2 column blocks
 constexpr int kTStride = kSD + 4;         // floats per T row in LDS
-constexpr int kSStride = kSD + 16;        // floats per S row in LDS
 constexpr int kTFloats = kSD * kSD / kSThreads;  // floats of T (and of S(C|0)) per thread
 
-// S element (r, c) in LDS: row stride kSStride, and the 16-column block index XORed with
-// (r / 4) mod 4.  B reads (rows k .. k+3, 16 columns) stay on 64 distinct banks, and so
-// do the accumulator writes, whose lanes cover rows 4 apart.
-__device__ __forceinline__ int sidx(int r, int c) { return r * kSStride + (c ^ (((r >> 2) & 3) << 4)); }
+// S element (r, c) in LDS: column c = 64 h + 16 j + i (half h, block j, column i) sits at
+// r * 128 + 4 (16 h + i) + j, so the four blocks' column i are adjacent.
+__device__ __forceinline__ int sidx(int r, int c) {
+  return r * kSD + 4 * (16 * (c >> 6) + (c & 15)) + ((c >> 4) & 3);
+}
 
 __global__ __launch_bounds__(kSThreads, 1) void state_compose_kernel(
     const int32_t *__restrict__ segs, const int32_t *__restrict__ req_chunk_ptr, int n_heads,
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(kSThreads, 1) void state_compose_kernel(
     const float *__restrict__ s_init, float *__restrict__ prefix_out,
     float *__restrict__ final_out) {
   __shared__ __attribute__((aligned(16))) float t_lds[kSD * kTStride];
-  __shared__ __attribute__((aligned(16))) float s_lds[kSD * kSStride];
+  __shared__ __attribute__((aligned(16))) float s_lds[kSD * kSD];
   const int b = blockIdx.x / n_heads, h = blockIdx.x - b * n_heads;
   const int c0 = req_chunk_ptr[b], c1 = req_chunk_ptr[b + 1];
   const int lane = threadIdx.x & 63;
@@ -74,10 +75,11 @@ __global__ __launch_bounds__(kSThreads, 1) void state_compose_kernel(
     for (int r = 0; r < kTFloats / 4; ++r)
       *reinterpret_cast<f32x4 *>(t_lds + (lrow + 16 * r) * kTStride + lcol) = reg[r];
   };
-  auto store_s = [&](const f32x4 (&reg)[kTFloats / 4]) {  // 4 columns stay together
+  auto store_s = [&](const f32x4 (&reg)[kTFloats / 4]) {  // once per request
 #pragma unroll
     for (int r = 0; r < kTFloats / 4; ++r)
-      *reinterpret_cast<f32x4 *>(s_lds + sidx(lrow + 16 * r, lcol)) = reg[r];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_lds[sidx(lrow + 16 * r, lcol + j)] = reg[r][j];
   };
   // S(C|0) straight into the accumulator layout: tile (i, jt) of this wave covers rows
   // 32 wr + 16 i + 4 quad + e, column 64 wc + 16 jt + col
@@ -146,20 +148,20 @@ __global__ __launch_bounds__(kSThreads, 1) void state_compose_kernel(
       load_mat(chunk_mat(t_pool, c + 1), treg);
       load_acc(chunk_mat(s_pool, c + 1), snext);
     }
-    // acc += T[32 wr .. +31][:] S[:][64 wc .. +63], 4 k per MFMA; rows k + quad of S
-    // have (k / 4) mod 4 = kk as their column swizzle
+    // acc += T[32 wr .. +31][:] S[:][64 wc .. +63], 4 k per MFMA; one 16-byte read
+    // gives row k + quad, column col of the four column tiles
     const float *ta = t_lds + (32 * wr + col) * kTStride + quad;
-    const float *sb = s_lds + quad * kSStride + 64 * wc + col;
+    const float *sb = s_lds + quad * kSD + 4 * (16 * wc + col);
     for (int k0 = 0; k0 < kSD; k0 += 16) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int k = k0 + 4 * kk;
         const float a0 = ta[k], a1 = ta[16 * kTStride + k];
+        const f32x4 bq = *reinterpret_cast<const f32x4 *>(sb + k * kSD);
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-          const float bv = sb[k * kSStride + 16 * (jt ^ kk)];
-          acc[0][jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bv, acc[0][jt], 0, 0, 0);
-          acc[1][jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bv, acc[1][jt], 0, 0, 0);
+          acc[0][jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bq[jt], acc[0][jt], 0, 0, 0);
+          acc[1][jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bq[jt], acc[1][jt], 0, 0, 0);
         }
       }
     }
@@ -169,10 +171,9 @@ __global__ __launch_bounds__(kSThreads, 1) void state_compose_kernel(
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s_lds[sidx(32 * wr + 16 * i + 4 * quad + e, 64 * wc + 16 * jt + col)] = acc[i][jt][e];
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<f32x4 *>(s_lds + sidx(32 * wr + 16 * i + 4 * quad + e, 64 * wc + col)) =
+            f32x4{acc[i][0][e], acc[i][1][e], acc[i][2][e], acc[i][3][e]};
     if (prefix_out) store_acc(prefix_out + ((int64_t)c * n_heads + h) * mat, acc);
     if (c + 1 < c1) store_t(treg);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // S_c and T_{c+1} in LDS
