@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--decode", action="store_true",
                     help="shared_pool only: time one decode step of every request "
                          "(pic_decode_attn_paged) instead of the link")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --decode: capture the step's launches in a HIP graph once "
+                         "(the plan is fixed) and replay it every step")
     ap.add_argument("--link-layers", type=int, default=0,
                     help="contiguous workloads: time the whole multi-layer link (pic_link: "
                          "per layer rope-delta, compute_qkv, splice, attention, output "
@@ -359,11 +362,30 @@ def bench_decode(args, wl):
     per_request_bytes = 2.0 * row_bytes * (plan.n_tokens + len(wl.requests))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
 
+    def call():
+        P.pic_decode_attn_paged(plan, qn, kn, vn, pk, pv, cbp_d, blocks_d, kf, vf, out,
+                                wl.rope_base, workspace=ws)
+
+    graph = None
+    if args.graph:  # the step's launches captured once (fixed plan), replayed per step
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        torch.cuda.synchronize()
+
     def step(i=None):
         e = ev[i] if i is not None else None
         if e: e[0].record()
-        P.pic_decode_attn_paged(plan, qn, kn, vn, pk, pv, cbp_d, blocks_d, kf, vf, out,
-                                wl.rope_base, workspace=ws)
+        if graph is not None:
+            graph.replay()
+        else:
+            call()
         if e: e[1].record()
 
     for _ in range(args.warmup):
@@ -393,7 +415,8 @@ def bench_decode(args, wl):
         "config": {"workload": "shared_pool_decode", "requests": len(wl.requests),
                    "context_tokens": plan.n_tokens, "pool_chunks": len(wl.pool_lens),
                    "pool_chunks_used": len(used), "seam_window": wl.k, "h_q": hq, "h_kv": hkv,
-                   "head_dim": D, "parallelism": "none (1 GPU)"},
+                   "head_dim": D, "parallelism": "none (1 GPU)",
+                   "launch": "hip graph replay" if graph is not None else "eager"},
         "decode_steps_per_s": round(1e3 / ms_step, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
