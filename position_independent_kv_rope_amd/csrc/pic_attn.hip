@@ -400,10 +400,11 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_bf16_kernel(
 // (rotations are orthogonal), once per chunk per wave.  The recomputed rows (seams and
 // queries) are read straight from the fresh buffers in the global frame, as their own
 // key blocks; the online softmax does not depend on key order.  Every staged block
-// therefore comes from one buffer, so direct buffer->LDS loads still apply: pool blocks
-// take one scalar block-table lookup per 16 rows, rows past a chunk's last block read
-// as zero, and V rows past a chunk's end are zeroed in LDS so that masked keys
-// contribute exactly nothing.
+// therefore comes from one buffer, so direct buffer->LDS loads still apply: a 64-key
+// block's four 16-row pool blocks come from a per-block record that a small kernel
+// resolves from the block table before the attention kernel runs, rows past a chunk's
+// last block read as zero, and V rows past a chunk's end are zeroed in LDS so that
+// masked keys contribute exactly nothing.
 
 constexpr int kPoolBlockRows = 16;
 
