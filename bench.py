@@ -18,7 +18,6 @@ read in place).
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -105,14 +104,6 @@ def pct(times_ms):
             "p95_ms": round(float(np.percentile(t, 95)), 4)}
 
 
-def src_hash(paths):
-    h = hashlib.sha256()
-    for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(kernel, workload, sources=None):
     """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
     path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
@@ -120,6 +111,7 @@ def load_traffic(kernel, workload, sources=None):
         return None
     with open(path) as f:
         rec = json.load(f)
+    from position_independent_kv_rope_amd.profiling import src_hash
     if rec.get("source_hash") != src_hash(rec.get("sources", sources or ATTN_SOURCES)):
         return None
     return rec.get("bytes_per_launch")

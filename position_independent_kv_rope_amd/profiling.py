@@ -13,8 +13,8 @@
 
 ``traffic`` scales the per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the kernels of one
 call (summed) by what the same counters read for a plain device copy of known size, and
-records the sha256 of the kernel sources so a stale measurement is not reused after a
-change.
+records the sha256 of the kernel sources' code (comments and white space removed) so a
+stale measurement is not reused after a code change.
 """
 
 import argparse
@@ -72,10 +72,16 @@ def counters(paths):
 
 
 def src_hash(paths):
+    """sha256 of the sources' code with comments and white space removed, so that a
+    counter run stays valid across comment-only edits and goes stale with any code
+    change."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(re.sub(r"\s+", "", text).encode())
     return h.hexdigest()[:16]
 
 
