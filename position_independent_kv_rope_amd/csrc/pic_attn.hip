@@ -364,15 +364,15 @@ __device__ __forceinline__ void attn_bf16_body(
         *reinterpret_cast<bf16x4 *>(op + 32 * d + 8 * a) = o;
       }
   } else {
-    float *wo = ws_o + ((int64_t)it.slot * kM + m) * D + 4 * grp;
+    __bf16 *wo = reinterpret_cast<__bf16 *>(ws_o) + ((int64_t)it.slot * kM + m) * D + 4 * grp;
 #pragma unroll
     for (int d = 0; d < kDB; ++d)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        f32x4 o;
+        bf16x4 o;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) o[b] = acc[d][4 * a + b];
-        *reinterpret_cast<f32x4 *>(wo + 32 * d + 8 * a) = o;
+        for (int b = 0; b < 4; ++b) o[b] = (__bf16)acc[d][4 * a + b];
+        *reinterpret_cast<bf16x4 *>(wo + 32 * d + 8 * a) = o;
       }
     if (grp == 0) {
       ws_ml[((int64_t)it.slot * kM + m) * 2 + 0] = m_run;
@@ -834,15 +834,15 @@ __device__ __forceinline__ void attn_bf16_paged_body(
         *reinterpret_cast<bf16x4 *>(op + 32 * d + 8 * a) = o;
       }
   } else {
-    float *wo = ws_o + ((int64_t)it.slot * kM + m) * D + 4 * grp;
+    __bf16 *wo = reinterpret_cast<__bf16 *>(ws_o) + ((int64_t)it.slot * kM + m) * D + 4 * grp;
 #pragma unroll
     for (int d = 0; d < kDB; ++d)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        f32x4 o;
+        bf16x4 o;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) o[b] = acc[d][4 * a + b];
-        *reinterpret_cast<f32x4 *>(wo + 32 * d + 8 * a) = o;
+        for (int b = 0; b < 4; ++b) o[b] = (__bf16)acc[d][4 * a + b];
+        *reinterpret_cast<bf16x4 *>(wo + 32 * d + 8 * a) = o;
       }
     if (grp == 0) {
       ws_ml[((int64_t)it.slot * kM + m) * 2 + 0] = m_run;
@@ -1468,7 +1468,9 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(
 
 // Combine the split partials of each (tile, kv head) with their log-sum-exp weights:
 // one thread per (merge entry, query vector, 4 output dims), a single pass over the
-// slots with an online maximum.
+// slots with an online maximum.  The bf16 kernels store partial O in bf16 (one rounding
+// of an unnormalised sum, which the merge weights by exp(m) and divides by the summed
+// l), the fp32 kernel in fp32; both sit at the start of the same fp32-sized region.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(
     T *__restrict__ out, const AttnTile *__restrict__ tiles, const MergeEntry *__restrict__ merges,
@@ -1494,7 +1496,15 @@ __global__ __launch_bounds__(256) void merge_kernel(
       const int64_t at = (int64_t)(me.slot_base + s) * kM + m;
       const float ms = ws_ml[at * 2];
       const float ls = ws_ml[at * 2 + 1];
-      const f32x4 os = *reinterpret_cast<const f32x4 *>(ws_o + at * D + 4 * c);
+      f32x4 os;
+      if constexpr (std::is_same<T, __bf16>::value) {
+        const bf16x4 ob =
+            *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const __bf16 *>(ws_o) + at * D + 4 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) os[i] = (float)ob[i];
+      } else {
+        os = *reinterpret_cast<const f32x4 *>(ws_o + at * D + 4 * c);
+      }
       if (ms == kNegInf) continue;
       if (ms > mmax) {
         const float r = __builtin_amdgcn_exp2f(mmax - ms);  // 0 when mmax is -inf
