@@ -1467,8 +1467,8 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(
 // ================================ merge ========================================
 
 // Combine the split partials of each (tile, kv head) with their log-sum-exp weights:
-// one thread per (merge entry, query vector, 4 output dims), a single pass over the
-// slots with an online maximum.  The bf16 kernels store partial O in bf16 (one rounding
+// one thread per (merge entry, query vector, 8 output dims: 16-byte partial loads), a
+// single pass over the slots with an online maximum.  The bf16 kernels store partial O in bf16 (one rounding
 // of an unnormalised sum, which the merge weights by exp(m) and divides by the summed
 // l), the fp32 kernel in fp32; both sit at the start of the same fp32-sized region.
 template <typename T, int D>
@@ -1476,7 +1476,9 @@ __global__ __launch_bounds__(256) void merge_kernel(
     T *__restrict__ out, const AttnTile *__restrict__ tiles, const MergeEntry *__restrict__ merges,
     const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int h_q, int h_kv,
     int tile_rows, int n_merge) {
-  constexpr int kC = D / 4;
+  constexpr int kV = 8;  // output dims per thread
+  constexpr int kC = D / kV;
+  typedef __attribute__((__vector_size__(kV * sizeof(float)))) float f32x8;
   const int group = h_q / h_kv;
   const int64_t total = (int64_t)n_merge * kM * kC;
   for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total;
@@ -1490,21 +1492,21 @@ __global__ __launch_bounds__(256) void merge_kernel(
     if (row_local >= tile.n_rows) continue;
     const int head = me.kv_head * group + m / tile_rows;
     float mmax = kNegInf, den = 0.f;
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    f32x8 num = {};
 #pragma unroll 4
     for (int s = 0; s < me.n_slots; ++s) {
       const int64_t at = (int64_t)(me.slot_base + s) * kM + m;
-      const float ms = ws_ml[at * 2];
-      const float ls = ws_ml[at * 2 + 1];
-      f32x4 os;
+      const float2 ml = *reinterpret_cast<const float2 *>(ws_ml + at * 2);
+      f32x8 os;
       if constexpr (std::is_same<T, __bf16>::value) {
-        const bf16x4 ob =
-            *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const __bf16 *>(ws_o) + at * D + 4 * c);
+        const bf16x8 ob =
+            *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const __bf16 *>(ws_o) + at * D + kV * c);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) os[i] = (float)ob[i];
+        for (int i = 0; i < kV; ++i) os[i] = (float)ob[i];
       } else {
-        os = *reinterpret_cast<const f32x4 *>(ws_o + at * D + 4 * c);
+        os = *reinterpret_cast<const f32x8 *>(ws_o + at * D + kV * c);
       }
+      const float ms = ml.x, ls = ml.y;
       if (ms == kNegInf) continue;
       if (ms > mmax) {
         const float r = __builtin_amdgcn_exp2f(mmax - ms);  // 0 when mmax is -inf
@@ -1517,14 +1519,14 @@ __global__ __launch_bounds__(256) void merge_kernel(
       num += w * os;
     }
     const float inv = 1.f / den;
-    T *op = out + ((int64_t)(tile.row_begin + row_local) * h_q + head) * D + 4 * c;
+    T *op = out + ((int64_t)(tile.row_begin + row_local) * h_q + head) * D + kV * c;
     if constexpr (std::is_same<T, __bf16>::value) {
-      bf16x4 o;
+      bf16x8 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = (__bf16)(num[i] * inv);
-      *reinterpret_cast<bf16x4 *>(op) = o;
+      for (int i = 0; i < kV; ++i) o[i] = (__bf16)(num[i] * inv);
+      *reinterpret_cast<bf16x8 *>(op) = o;
     } else {
-      *reinterpret_cast<f32x4 *>(op) = num * inv;
+      *reinterpret_cast<f32x8 *>(op) = num * inv;
     }
   }
 }
@@ -1553,7 +1555,7 @@ int launch_attn(const PlanHeader &h, const int32_t *plan_dev, const void *q, con
   }
   PIC_LAUNCH_CHECK();
   if (h[PIC_H_N_MERGE] > 0) {
-    const int64_t threads = (int64_t)h[PIC_H_N_MERGE] * kM * (D / 4);
+    const int64_t threads = (int64_t)h[PIC_H_N_MERGE] * kM * (D / 8);
     const unsigned blocks = (unsigned)std::min<int64_t>((threads + 255) / 256, 1 << 20);
     hipLaunchKernelGGL((merge_kernel<T, D>), dim3(blocks), dim3(256), 0, s,
                        static_cast<T *>(out), tiles, merges, ws_o, ws_ml, h[PIC_H_H_Q],
@@ -1624,7 +1626,7 @@ int launch_paged(const PlanHeader &h, const int32_t *plan_dev, const void *q, co
                      (int)(pool_blocks * kPoolBlockRows * tok_bytes));
   PIC_LAUNCH_CHECK();
   if (h[PIC_H_N_MERGE] > 0) {
-    const int64_t threads = (int64_t)h[PIC_H_N_MERGE] * kM * (D / 4);
+    const int64_t threads = (int64_t)h[PIC_H_N_MERGE] * kM * (D / 8);
     const unsigned blocks = (unsigned)std::min<int64_t>((threads + 255) / 256, 1 << 20);
     hipLaunchKernelGGL((merge_kernel<__bf16, D>), dim3(blocks), dim3(256), 0, s,
                        static_cast<__bf16 *>(out), tiles, merges, ws_o, ws_ml, h[PIC_H_H_Q],
