@@ -1,19 +1,26 @@
 /*
  * pic.h -- C ABI of the position-independent KV splicing library (libpic.so, gfx950).
  *
- * The library runs the link phase of LegoLink / seam-window selective recompute for
- * one attention layer on one GPU:
+ * The library runs the link phase of LegoLink / seam-window selective recompute on
+ * one GPU.  The path of one attention layer:
  *
  *   1. pic_build_index     host planner: chunk offsets, the recompute index (the first
  *                          min(k, L_c) tokens of every chunk except chunk 0, then every
- *                          query token) and the launch schedule of the three kernels.
+ *                          query token) and the launch schedule of the kernels.
  *   2. pic_rope_delta      in place, rotates the cached K of every chunk from its local
  *                          RoPE positions to its global offset with one direct rotation
- *                          R(delta_c) per row.
+ *                          R(delta_c) per row (pic_rope_apply: RoPE at the global
+ *                          positions for a position-free cache).
  *   3. pic_splice          copies the fresh K/V of the recomputed rows into the spliced
  *                          buffers at their global positions.
  *   4. pic_selective_attn  causal attention of the recomputed rows (global positions)
  *                          over every spliced key j <= p_r, GQA, flash-style on MFMA.
+ *
+ * Around it: pic_selective_attn_paged (steps 2-4 over chunks stored once in a shared
+ * paged pool, rotation folded into the query), pic_decode_attn_paged (the next token of
+ * every request over the same pool), pic_qkv_rope / pic_out_proj / pic_link (the
+ * recomputed rows' projections and the multi-layer link) and pic_state_compose (the
+ * state of a linear-attention layer composed over cached chunk summaries).
  *
  * Sources (page title and section):
  *   [EPIC]  "EPIC: Efficient Position-Independent Caching for Serving Large Language
@@ -22,7 +29,8 @@
  *           neighbouring dimensions by position-proportional angles), 3.3 (scheme C,
  *           rotary correction by the delta rotation, one direct kernel rather than two
  *           stacked rotations), footnote 3 (inv_freq = base^(-2i/D)).
- *   [HYPIC] joto.ai article on HYPIC: 2.2 seam window (k = w = 8 per internal segment).
+ *   [HYPIC] joto.ai article on HYPIC: 2.1 composition of linear-layer states, 2.2 seam
+ *           window (k = w = 8 per internal segment).
  *   [KV-scratch] "KV cache 从零实现：两层 Decoder、位置偏移与正确性验证": offset mask
  *           allowed[i, j] = [j <= P + i].
  *
@@ -224,8 +232,8 @@ int pic_splice(const int32_t *plan_host, const int32_t *plan_dev, void *k, void 
                void *stream);
 
 /* Bytes of workspace pic_selective_attn (split-KV partials; 0 if the plan has no split
- * tile) or pic_selective_attn_paged (partials + per-chunk angle table) needs.  Returns 0
- * on a bad plan as well; the attention call checks again. */
+ * tile) or pic_selective_attn_paged (partials, per-chunk angle table, per-key-block
+ * records) needs.  Returns 0 on a bad plan as well; the attention call checks again. */
 size_t pic_attn_workspace_bytes(const int32_t *plan_host, int32_t head_dim);
 
 /*
@@ -241,8 +249,8 @@ size_t pic_attn_workspace_bytes(const int32_t *plan_host, int32_t head_dim);
  * for bf16, {16, 32, 64, 128} for f32.  workspace: device, >= pic_attn_workspace_bytes
  * (may be NULL when that is 0); contents on entry are ignored.  A paged plan (built with
  * chunk_ids) is rejected with PIC_EINVAL: it needs pic_selective_attn_paged.  A request
- * whose K (or V) rows exceed 2 GiB (N_b * h_kv * head_dim * dtype size) is
- * PIC_EUNSUPPORTED (32-bit buffer offsets).
+ * whose K (or V) rows take more than 0x7fff0000 bytes (N_b * h_kv * head_dim * dtype
+ * size) is PIC_EUNSUPPORTED (32-bit buffer offsets).
  */
 int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_dev, const void *q,
                        const void *k, const void *v, void *out, int32_t dtype,
@@ -264,8 +272,9 @@ int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_dev, const 
  * k_fresh/v_fresh [n_rows][h_kv][head_dim] hold the recomputed rows (RoPE'd at their
  * global positions) and are read in place; q/out as in pic_selective_attn.  Cached keys
  * of chunk c are scored in their local frame against the query rotated by -delta_c
- * (same theta and pair layout as pic_rope_delta).  bf16 only, head_dim in {64, 128},
- * pool and fresh K/V each < 2 GiB.  Pool slots past a chunk's length may hold anything
+ * (same theta and pair layout as pic_rope_delta).  bf16 only, head_dim in {64, 128};
+ * 32-bit buffer offsets: the pool at most 0x7fff0000 bytes less one 16-row block, the
+ * fresh K (and V) at most 0x7fff0000 bytes.  Pool slots past a chunk's length may hold anything
  * (NaN included).  workspace >= pic_attn_workspace_bytes(plan_host, head_dim):
  * partials, the angle table and one 32-byte record per key block (a small kernel fills
  * them from the block table before the attention kernel runs).  Errors: PIC_EINVAL (not
