@@ -34,6 +34,31 @@ def _declared_symbols():
     return sorted(set(re.findall(r"\b(pic_[a-z_]+)\s*\(", text)))
 
 
+def test_plain_c_caller_plans_the_worked_example(tmp_path):
+    # the header compiles as C11 with warnings as errors, and a C program linked against
+    # libpic.so plans the pages' worked example through the ABI alone (host only)
+    import json
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    lib_dir = os.path.dirname(P.LIB_PATH)
+    exe = str(tmp_path / "abi_worked_example")
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.join(root, "include"),
+                    os.path.join(here, "c", "abi_worked_example.c"), "-o", exe,
+                    "-L", lib_dir, "-lpic", "-Wl,-rpath," + lib_dir], check=True)
+    out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split("\n")
+    gold = json.load(open(os.path.join(here, "golden", "worked_example.json")))
+    assert out[0].split()[1:] == [str(p) for p in gold["recompute_positions"]]
+    assert out[1].split()[1:] == [str(o) for o in gold["offsets"]]
+    assert out[2] == "tokens %d" % gold["n_total"]
+    assert out[3].startswith("bad plan: ") and len(out[3]) > len("bad plan: ")
+
+
 def test_library_exports_every_declared_symbol():
     syms = _declared_symbols()
     assert set(syms) == set(P.EXPORTED), syms
