@@ -308,3 +308,34 @@ def test_largest_pool_prefill_and_decode():
         derr = float(np.max(np.abs(dec_all[b] - O.decode_attn(f64(qn[b]), kx, vx, f64(kn[b]), f64(vn[b])))))
         say("largest pool request", b, "prefill max-abs error", err, "decode", derr)
         assert err <= TOL and derr <= TOL
+
+
+def _random_pool(i):
+    """Seeded random pool and requests: chunk lengths from 1 row to several pool blocks,
+    chunks shared between requests and repeated within one, chunk-free requests."""
+    rng = np.random.default_rng(7000 + i)
+    h_kv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    lens = [int(x) for x in rng.integers(1, 900, size=int(rng.integers(1, 10)))]
+    reqs = []
+    for _ in range(int(rng.integers(1, 5))):
+        m = int(rng.integers(0, 7))
+        ids = [int(x) for x in rng.integers(0, len(lens), size=m)]
+        reqs.append(W.Request([lens[c] for c in ids], int(rng.integers(0 if m else 1, 50)), chunk_ids=ids))
+    return W.Workload("random_pool%d" % i, "bf16", g * h_kv, h_kv, d, float(rng.choice([1e4, 5e5])),
+                      int(rng.integers(0, 12)), reqs, pool_lens=lens, block_size=16,
+                      pool_block_perm_seed=80 + i, seed=90 + i)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_pools(i):
+    # paged prefill (every row) and the decode step (every request) on seeded random
+    # pools, both pair layouts, NaN in the slack slots of every other case
+    wl = _random_pool(i)
+    layout = "half" if i % 2 else "adjacent"
+    say("random pool", i, "h_q=%d h_kv=%d D=%d k=%d" % (wl.h_q, wl.h_kv, wl.head_dim, wl.k),
+        layout, [(len(r.chunk_ids), r.q_len) for r in wl.requests])
+    run_paged(wl, layout, nan_slack=bool(i % 2), n_cu=(256 if i % 3 == 0 else 2))
+    if wl.h_q // wl.h_kv <= P.PIC_DECODE_COLS:
+        run_decode(wl, layout, nan_slack=bool(i % 2), n_cu=(1 if i % 3 == 1 else 256))

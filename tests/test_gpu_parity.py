@@ -367,3 +367,38 @@ def test_max_request_size_sampled():
         err = float(np.max(np.abs(got - want)))
         say("selective_attn head group", g, "max-abs error", err)
         assert err <= TOL["bf16"]
+
+
+def _random_case(i):
+    """Seeded random configuration: heads, GQA group, head_dim, dtype, layout, pos_base,
+    k and ragged requests (empty chunks, chunk-free and query-free requests)."""
+    rng = np.random.default_rng(4000 + i)
+    dtype = "bf16" if i % 3 else "f32"
+    d = int(rng.choice([64, 128] if dtype == "bf16" else [16, 32, 64, 128]))
+    h_kv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    reqs = []
+    for _ in range(int(rng.integers(1, 4))):
+        n = int(rng.integers(0, 6))
+        lens = [int(x) for x in rng.integers(0, 2500 if i % 2 else 500, size=n)]
+        if n and rng.random() < 0.3:
+            lens[int(rng.integers(0, n))] = 0
+        reqs.append((lens, int(rng.integers(0, 60))))
+    if sum(sum(l) + q for l, q in reqs) == 0:
+        reqs[0] = ([37], 5)
+    k = int(rng.integers(0, 20))
+    base = float(rng.choice([1e4, 5e5, 1e6]))
+    layout = "half" if rng.random() < 0.5 else "adjacent"
+    pos_base = int(rng.integers(0, 8)) if rng.random() < 0.3 else 0
+    wl = _custom("random%d" % i, dtype, g * h_kv, h_kv, d, base, k, reqs, seed=500 + i)
+    return wl, layout, pos_base
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_configurations(i):
+    # every stage of the contiguous path on a seeded random configuration, against the
+    # oracle (full compare), with the plan split for a few-CU launch as often as not
+    wl, layout, pos_base = _random_case(i)
+    say("random case", i, wl.dtype, "h_q=%d h_kv=%d D=%d k=%d" % (wl.h_q, wl.h_kv, wl.head_dim, wl.k),
+        layout, "pos_base=%d" % pos_base, [(sum(r.chunk_lens), len(r.chunk_lens), r.q_len) for r in wl.requests])
+    check_run(Run(wl, layout, n_cu=(2 if i % 2 else 0), pos_base=pos_base))
