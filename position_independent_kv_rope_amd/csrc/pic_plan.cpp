@@ -28,6 +28,7 @@ constexpr int32_t kKeyAlign = 64;       // attention key block
 constexpr int32_t kMinSplitKeys = 2048;  // smallest key range worth a partial result
 constexpr int kXcd = 8;                  // MI355X dies with a private L2 each
 constexpr int64_t kSegKeys = 8192;       // longest split-KV segment
+constexpr int64_t kTailKeys = 4096;      // longest item in a die's last round
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -37,9 +38,14 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // share its L2: streams are assigned to dies greedily by total cost (largest first,
 // to the least loaded die), each die runs its items segment by segment, and position
 // i of the launch takes the next item of die i % n_xcd.  When a die runs out, the
-// remaining items fill its positions, longest first.
+// remaining items fill its positions, longest first.  With tail_keys > 0, the items a
+// die starts during its last round (its final slots_per_die * round_keys keys of work)
+// are cut into pieces of at most tail_keys keys, kept in place on that die, so the
+// launch does not end waiting for a few long items.
 std::vector<pic::AttnItem> xcd_order(std::vector<pic::AttnItem> items,
-                                     const std::vector<pic::AttnTile> &tiles, int n_xcd) {
+                                     const std::vector<pic::AttnTile> &tiles, int n_xcd,
+                                     int64_t tail_keys = 0, int64_t slots_per_die = 0,
+                                     int64_t round_keys = 0) {
   using pic::AttnItem;
   auto len = [](const AttnItem &a) {  // second range used by paged plans
     return (int64_t)a.key_end - a.key_begin + ((int64_t)a.pad1 - a.pad0);
@@ -98,12 +104,49 @@ std::vector<pic::AttnItem> xcd_order(std::vector<pic::AttnItem> items,
     });
     std::vector<AttnItem> sorted;
     for (size_t i : idx) sorted.push_back(v[i]);
+    if (tail_keys > 0) {
+      int64_t total = 0;
+      for (const AttnItem &a : sorted) total += len(a);
+      const int64_t tail_from = total - slots_per_die * round_keys;
+      std::vector<AttnItem> cut;
+      int64_t done = 0;
+      size_t first_cut = sorted.size();
+      for (const AttnItem &a : sorted) {
+        const int64_t n = len(a);
+        if (done >= tail_from && n > tail_keys) {
+          first_cut = std::min(first_cut, cut.size());
+          const int64_t pieces = (n + tail_keys - 1) / tail_keys;
+          const int64_t step = round_up((n + pieces - 1) / pieces, kKeyAlign);
+          for (int64_t b = a.key_begin; b < a.key_end; b += step) {
+            AttnItem p = a;
+            p.key_begin = (int32_t)b;
+            p.key_end = (int32_t)std::min<int64_t>(a.key_end, b + step);
+            cut.push_back(p);
+          }
+        } else {
+          cut.push_back(a);
+        }
+        done += n;
+      }
+      // the pieces run segment by segment again, each stream's pieces side by side
+      auto stream = [&](const AttnItem &x) {
+        return (int64_t)tiles[x.tile].req * 65536 + x.kv_head;
+      };
+      std::stable_sort(cut.begin() + (std::ptrdiff_t)first_cut, cut.end(),
+                       [&](const AttnItem &x, const AttnItem &y) {
+                         if (x.key_begin != y.key_begin) return x.key_begin < y.key_begin;
+                         return stream(x) < stream(y);
+                       });
+      sorted.swap(cut);
+    }
     per_die[d].swap(sorted);
   }
+  size_t n_out = 0;  // the items after the tail cut
+  for (int d = 0; d < n_xcd; ++d) n_out += per_die[d].size();
   std::vector<AttnItem> out;
-  out.reserve(items.size());
+  out.reserve(n_out);
   std::vector<size_t> next(n_xcd, 0);
-  for (size_t pos = 0; out.size() < items.size(); ++pos) {
+  for (size_t pos = 0; out.size() < n_out; ++pos) {
     int d = (int)(pos % n_xcd);
     if (next[d] >= per_die[d].size()) {
       // this die is done: take the longest remaining item of any die
@@ -354,7 +397,34 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
     }
     if (n_partials > kMaxI32 / 2) return PIC_EINVAL;
   }
-  items = xcd_order(std::move(items), tiles, kXcd);
+  if (paged) {
+    items = xcd_order(std::move(items), tiles, kXcd);
+  } else {
+    // contiguous plans: shorter pieces in each die's last round, then the split-KV
+    // slots and merge entries follow the final item list (per (tile, kv head): its
+    // items in key order, contiguous slots when there is more than one)
+    items = xcd_order(std::move(items), tiles, kXcd, kTailKeys,
+                      std::max<int64_t>(1, slots / kXcd), seg_len);
+    std::vector<std::vector<int32_t>> of(tiles.size() * (size_t)h_kv);
+    for (int32_t i = 0; i < (int32_t)items.size(); ++i)
+      of[(size_t)items[i].tile * h_kv + items[i].kv_head].push_back(i);
+    merges.clear();
+    n_partials = 0;
+    for (size_t u = 0; u < of.size(); ++u) {
+      auto &v = of[u];
+      std::sort(v.begin(), v.end(),
+                [&](int32_t a, int32_t b) { return items[a].key_begin < items[b].key_begin; });
+      if (v.size() == 1) {
+        items[v[0]].slot = -1;
+      } else if (v.size() > 1) {
+        for (size_t r = 0; r < v.size(); ++r) items[v[r]].slot = (int32_t)(n_partials + r);
+        merges.push_back(MergeEntry{(int32_t)(u / h_kv), (int32_t)(u % h_kv),
+                                    (int32_t)n_partials, (int32_t)v.size()});
+        n_partials += (int64_t)v.size();
+      }
+    }
+    if (n_partials > kMaxI32 / 2) return PIC_EINVAL;
+  }
 
   // ---- decode items (paged plans): every pool chunk once, for all its uses ----
   // A decode step streams each pool chunk from HBM once and serves every request
