@@ -39,13 +39,15 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // to the least loaded die), each die runs its items segment by segment, and position
 // i of the launch takes the next item of die i % n_xcd.  When a die runs out, the
 // remaining items fill its positions, longest first.  With tail_keys > 0, the items a
-// die starts during its last round (its final slots_per_die * round_keys keys of work)
-// are cut into pieces of at most tail_keys keys, kept in place on that die, so the
-// launch does not end waiting for a few long items.
+// die starts during its last round (its final slots_per_die * round_keys of work) have
+// their first key range cut into pieces of at most tail_keys (multiples of align; a
+// second range, the fresh blocks of a paged item, stays with the first piece), kept on
+// that die, so the launch does not end waiting for a few long items.  Lengths are in
+// keys for contiguous plans and in key blocks for paged ones.
 std::vector<pic::AttnItem> xcd_order(std::vector<pic::AttnItem> items,
                                      const std::vector<pic::AttnTile> &tiles, int n_xcd,
                                      int64_t tail_keys = 0, int64_t slots_per_die = 0,
-                                     int64_t round_keys = 0) {
+                                     int64_t round_keys = 0, int64_t align = 1) {
   using pic::AttnItem;
   auto len = [](const AttnItem &a) {  // second range used by paged plans
     return (int64_t)a.key_end - a.key_begin + ((int64_t)a.pad1 - a.pad0);
@@ -112,15 +114,16 @@ std::vector<pic::AttnItem> xcd_order(std::vector<pic::AttnItem> items,
       int64_t done = 0;
       size_t first_cut = sorted.size();
       for (const AttnItem &a : sorted) {
-        const int64_t n = len(a);
-        if (done >= tail_from && n > tail_keys) {
+        const int64_t n = len(a), n1 = (int64_t)a.key_end - a.key_begin;
+        if (done >= tail_from && n1 > tail_keys) {
           first_cut = std::min(first_cut, cut.size());
-          const int64_t pieces = (n + tail_keys - 1) / tail_keys;
-          const int64_t step = round_up((n + pieces - 1) / pieces, kKeyAlign);
+          const int64_t pieces = (n1 + tail_keys - 1) / tail_keys;
+          const int64_t step = round_up((n1 + pieces - 1) / pieces, align);
           for (int64_t b = a.key_begin; b < a.key_end; b += step) {
             AttnItem p = a;
             p.key_begin = (int32_t)b;
             p.key_end = (int32_t)std::min<int64_t>(a.key_end, b + step);
+            if (b != a.key_begin) p.pad0 = p.pad1;  // the second range stays with piece 0
             cut.push_back(p);
           }
         } else {
@@ -397,14 +400,13 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
     }
     if (n_partials > kMaxI32 / 2) return PIC_EINVAL;
   }
-  if (paged) {
-    items = xcd_order(std::move(items), tiles, kXcd);
-  } else {
-    // contiguous plans: shorter pieces in each die's last round, then the split-KV
-    // slots and merge entries follow the final item list (per (tile, kv head): its
-    // items in key order, contiguous slots when there is more than one)
-    items = xcd_order(std::move(items), tiles, kXcd, kTailKeys,
-                      std::max<int64_t>(1, slots / kXcd), seg_len);
+  {
+    // shorter pieces in each die's last round (keys, or key blocks for paged plans),
+    // then the split-KV slots and merge entries follow the final item list (per (tile,
+    // kv head): its items in key order, contiguous slots when there is more than one)
+    const int64_t unit = paged ? kKeyAlign : 1;
+    items = xcd_order(std::move(items), tiles, kXcd, kTailKeys / unit,
+                      std::max<int64_t>(1, slots / kXcd), seg_len / unit, paged ? 1 : kKeyAlign);
     std::vector<std::vector<int32_t>> of(tiles.size() * (size_t)h_kv);
     for (int32_t i = 0; i < (int32_t)items.size(); ++i)
       of[(size_t)items[i].tile * h_kv + items[i].kv_head].push_back(i);
