@@ -351,7 +351,6 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
       const int64_t n_pool = needed(kb_pool[b], kb_fresh[b + 1]);
       const int64_t n_ranges = std::max<int64_t>(1, (n_pool + per_range - 1) / per_range);
       for (int32_t g = 0; g < h_kv; ++g) {
-        const int64_t slot_base = n_partials;
         for (int64_t r = 0; r < n_ranges; ++r) {
           AttnItem it{};
           it.tile = ti;
@@ -368,38 +367,26 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
             it.key_end = (int32_t)p1;
             it.pad0 = it.pad1 = (int32_t)p1;
           }
-          it.slot = n_ranges > 1 ? (int32_t)(slot_base + r) : -1;
           items.push_back(it);
         }
-        if (n_ranges > 1) {
-          merges.push_back(MergeEntry{ti, g, (int32_t)slot_base, (int32_t)n_ranges});
-          n_partials += n_ranges;
-        }
       }
-      if (n_partials > kMaxI32 / 2) return PIC_EINVAL;
     }
   }
   for (int32_t ti = 0; !paged && ti < (int32_t)tiles.size(); ++ti) {
     const int64_t keys = (int64_t)tiles[ti].p_last + 1;
     const int64_t n_split = (keys + seg_len - 1) / seg_len;
     for (int32_t g = 0; g < h_kv; ++g) {
-      const int64_t slot_base = n_partials;
       for (int64_t s = 0; s < n_split; ++s) {
         AttnItem it{};
         it.tile = ti;
         it.kv_head = g;
         it.key_begin = (int32_t)(s * seg_len);
         it.key_end = (int32_t)std::min<int64_t>(keys, (s + 1) * seg_len);
-        it.slot = n_split > 1 ? (int32_t)(slot_base + s) : -1;
         items.push_back(it);
       }
-      if (n_split > 1) {
-        merges.push_back(MergeEntry{ti, g, (int32_t)slot_base, (int32_t)n_split});
-        n_partials += n_split;
-      }
     }
-    if (n_partials > kMaxI32 / 2) return PIC_EINVAL;
   }
+  // (split-KV slots and merge entries are assigned once the dispatch order is final)
   {
     // shorter pieces in each die's last round (keys, or key blocks for paged plans),
     // then the split-KV slots and merge entries follow the final item list (per (tile,
