@@ -516,3 +516,14 @@ def test_paged_plan_rejects_inconsistent_chunk_lengths():
     # a pool chunk has one length wherever it is used
     with pytest.raises(P.PicError):
         P.pic_build_index([[4, 5], [6]], [1, 1], 2, 4, 4, chunk_ids_per_req=[[0, 1], [1]])
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the bench measures one GPU; asked for more it says so and exits non-zero, before
+    # touching a device
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
