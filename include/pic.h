@@ -270,12 +270,13 @@ int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_dev, const 
  * the caller: each listed chunk has at least ceil(L_c / 16) blocks, and block ids are
  * < pool_blocks (a larger id reads zeros: the pool loads are range-checked).
  * k_fresh/v_fresh [n_rows][h_kv][head_dim] hold the recomputed rows (RoPE'd at their
- * global positions) and are read in place; q/out as in pic_selective_attn.  Cached keys
- * of chunk c are scored in their local frame against the query rotated by -delta_c
- * (same theta and pair layout as pic_rope_delta).  bf16 only, head_dim in {64, 128};
- * 32-bit buffer offsets: the pool at most 0x7fff0000 bytes less one 16-row block, the
- * fresh K (and V) at most 0x7fff0000 bytes.  Pool slots past a chunk's length may hold anything
- * (NaN included).  workspace >= pic_attn_workspace_bytes(plan_host, head_dim):
+ * global positions) and are read in place; q/out as in pic_selective_attn.  bf16: cached
+ * keys of chunk c are scored in their local frame against the query rotated by -delta_c
+ * (bf16 MFMA, head_dim in {64, 128}); fp32: each staged pool key is rotated by delta_c
+ * into the global frame (fp32 MFMA, head_dim in {16, 32, 64, 128}); same theta and pair
+ * layout as pic_rope_delta.  32-bit buffer offsets: the pool at most 0x7fff0000 bytes
+ * less one 16-row block, the fresh K (and V) at most 0x7fff0000 bytes.  Pool slots past
+ * a chunk's length may hold anything (NaN included).  workspace >= pic_attn_workspace_bytes(plan_host, head_dim):
  * partials, the angle table and one 32-byte record per key block (a small kernel fills
  * them from the block table before the attention kernel runs).  Errors: PIC_EINVAL (not
  * a paged plan, null pointers, a chunk id >= n_pool_chunks, bad scale/base/layout),

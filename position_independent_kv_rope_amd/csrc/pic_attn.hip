@@ -1464,6 +1464,218 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(
   }
 }
 
+// ============================ fp32 kernel, paged pool ===========================
+//
+// The fp32 path over the shared pool: the same tiles, items and key-block records as the
+// bf16 paged kernel, the same tiling and math as the fp32 kernel above.  Here the
+// rotation goes on the keys: each staged pool row is rotated by R(delta_c) into the
+// global frame while it is written to LDS (fp32, from the per-chunk angle table), so the
+// query stays as it is; fresh rows are already global.  Rows past a chunk's end and
+// pool blocks outside the pool are staged as zeros without a load (slack slots may hold
+// anything), and masked.
+
+template <int D, bool kHalf>
+__global__ __launch_bounds__(kF32Threads) void attn_f32_paged_kernel(
+    const float *__restrict__ q, const float *__restrict__ pool_k,
+    const float *__restrict__ pool_v, const float *__restrict__ k_fresh,
+    const float *__restrict__ v_fresh, float *__restrict__ out,
+    const int32_t *__restrict__ rows, const AttnTile *__restrict__ tiles,
+    const AttnItem *__restrict__ items, const KeyBlockRec *__restrict__ recs,
+    const float2 *__restrict__ angles, float *__restrict__ ws_o, float *__restrict__ ws_ml,
+    int h_q, int h_kv, int tile_rows, float scale_log2) {
+  constexpr int kKs = D + 4;
+  constexpr int kVs = kKB + 4;
+  constexpr int kUPR = D / 4;
+  constexpr int kDB = D / 16;
+  constexpr int kQOps = D / 4;
+  constexpr int kPairs = D / 2;
+  static_assert(kKB == 4 * kPoolBlockRows, "a key block is four pool blocks");
+  __shared__ __attribute__((aligned(16))) float ks[kKB * kKs];
+  __shared__ __attribute__((aligned(16))) float vt[D * kVs];
+  __shared__ int kpos[kKB];
+
+  const AttnItem it = items[blockIdx.x];
+  const AttnTile tile = tiles[it.tile];
+  const int g = it.kv_head;
+  const int group = h_q / h_kv;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int fresh_base = tile.pad0, n_fresh = tile.pad1;
+
+  const int m = 16 * wave + col;
+  const int row_local = m % tile_rows;
+  const int head = g * group + m / tile_rows;
+  const bool valid = row_local < tile.n_rows;
+  const int row = tile.row_begin + (valid ? row_local : 0);
+  const int pos = valid ? rows[row] : -1;
+
+  float qop[kQOps];
+  {
+    const float *qp = q + ((int64_t)row * h_q + head) * D;
+#pragma unroll
+    for (int s = 0; s < kQOps; ++s) qop[s] = valid ? qp[4 * s + grp] : 0.f;
+  }
+  f32x4 acc[kDB];
+#pragma unroll
+  for (int d = 0; d < kDB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_lane = 0.f;
+
+  const int64_t tok = (int64_t)h_kv * D;  // floats per token row
+  const int n1 = it.key_end - it.key_begin;
+  const int n_blocks = n1 + (it.pad1 - it.pad0);
+  // address of key `key` of block dsc (K or V), or null: the row stages as zeros
+  auto row_ptr = [&](const KeyBlockRec &dsc, int key, bool is_v) -> const float * {
+    if (dsc.frame < 0) {
+      const int r = dsc.row + key;
+      if (r >= n_fresh) return nullptr;
+      return (is_v ? v_fresh : k_fresh) + ((int64_t)(fresh_base + r) * h_kv + g) * D;
+    }
+    if (key >= (dsc.vis >> 8)) return nullptr;  // past the chunk's end
+    const int pl = key / kPoolBlockRows;
+    const int o = pl == 0 ? dsc.off[0] : pl == 1 ? dsc.off[1] : pl == 2 ? dsc.off[2] : dsc.off[3];
+    if (o < 0) return nullptr;
+    return reinterpret_cast<const float *>(reinterpret_cast<const char *>(is_v ? pool_v : pool_k) + o) +
+           (int64_t)(key % kPoolBlockRows) * tok + (int64_t)g * D;
+  };
+
+  for (int ib = 0; ib < n_blocks; ++ib) {
+    const KeyBlockRec dsc = recs[ib < n1 ? it.key_begin + ib : it.pad0 + ib - n1];
+    const bool pool = dsc.frame >= 0;
+    const float2 *cs = angles + (int64_t)(pool ? dsc.frame : 0) * kPairs;
+    __syncthreads();
+    if (threadIdx.x < kKB) {
+      const int r = dsc.row + threadIdx.x;
+      kpos[threadIdx.x] = (!pool && r < n_fresh) ? rows[fresh_base + r] : 0x7fffffff;
+    }
+    // K, rotated into the global frame for pool rows
+    if constexpr (!kHalf) {  // pairs (2i, 2i+1): unit c holds pairs 2c and 2c + 1
+      for (int u = threadIdx.x; u < kKB * kUPR; u += kF32Threads) {
+        const int key = u / kUPR, c = u - key * kUPR;
+        const float *src = row_ptr(dsc, key, false);
+        f32x4 x = src ? *reinterpret_cast<const f32x4 *>(src + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        if (pool) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float2 a = cs[2 * c + h];
+            const float x0 = x[2 * h], x1 = x[2 * h + 1];
+            x[2 * h] = x0 * a.x - x1 * a.y;
+            x[2 * h + 1] = x0 * a.y + x1 * a.x;
+          }
+        }
+        *reinterpret_cast<f32x4 *>(&ks[key * kKs + 4 * c]) = x;
+      }
+    } else {  // pairs (i, i + D/2): units c and c + D/8 hold pairs 4c .. 4c + 3
+      for (int u = threadIdx.x; u < kKB * (kUPR / 2); u += kF32Threads) {
+        const int key = u / (kUPR / 2), c = u - key * (kUPR / 2);
+        const float *src = row_ptr(dsc, key, false);
+        f32x4 x = src ? *reinterpret_cast<const f32x4 *>(src + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 y = src ? *reinterpret_cast<const f32x4 *>(src + D / 2 + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        if (pool) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float2 a = cs[4 * c + e];
+            const float x0 = x[e], y0 = y[e];
+            x[e] = x0 * a.x - y0 * a.y;
+            y[e] = x0 * a.y + y0 * a.x;
+          }
+        }
+        *reinterpret_cast<f32x4 *>(&ks[key * kKs + 4 * c]) = x;
+        *reinterpret_cast<f32x4 *>(&ks[key * kKs + D / 2 + 4 * c]) = y;
+      }
+    }
+    // V transposed: 4 keys x 4 dims per work item
+    for (int u = threadIdx.x; u < (kKB / 4) * kUPR; u += kF32Threads) {
+      const int quad = u / kUPR, c = u - quad * kUPR;
+      f32x4 e[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float *src = row_ptr(dsc, 4 * quad + r, true);
+        e[r] = src ? *reinterpret_cast<const f32x4 *>(src + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4 *>(&vt[(4 * c + j) * kVs + 4 * quad]) =
+            f32x4{e[0][j], e[1][j], e[2][j], e[3][j]};
+    }
+    __syncthreads();
+
+    f32x4 sc[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const float *kr = ks + (16 * sb + col) * kKs + grp;
+#pragma unroll
+      for (int s = 0; s < kQOps; ++s)
+        sc[sb] = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[4 * s], qop[s], sc[sb], 0, 0, 0);
+    }
+    {
+      const int s0 = dsc.vis & 255, nv = dsc.vis >> 8;
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * sb + 4 * grp + i;
+          const bool ok = pool ? (key >= s0 && key < nv && dsc.base_pos + key <= pos)
+                               : kpos[key] <= pos;
+          if (!ok) sc[sb][i] = kNegInf;
+        }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[sb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const bool none = m_new == kNegInf;
+    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float base = none ? 0.f : m_new;
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[sb][i], scale_log2, -base));
+        sc[sb][i] = p;
+        psum += p;
+      }
+    l_lane = l_lane * alpha + psum;
+#pragma unroll
+    for (int d = 0; d < kDB; ++d) acc[d] *= alpha;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int d = 0; d < kDB; ++d) {
+          const float a = vt[(16 * d + col) * kVs + 16 * sb + 4 * grp + i];
+          acc[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sc[sb][i], acc[d], 0, 0, 0);
+        }
+  }
+
+  float l_row = l_lane + __shfl_xor(l_lane, 16);
+  l_row += __shfl_xor(l_row, 32);
+  if (!valid) return;
+  if (it.slot < 0) {
+    const float inv = 1.f / l_row;
+    float *op = out + ((int64_t)row * h_q + head) * D;
+#pragma unroll
+    for (int d = 0; d < kDB; ++d) *reinterpret_cast<f32x4 *>(op + 16 * d + 4 * grp) = acc[d] * inv;
+  } else {
+    float *wo = ws_o + ((int64_t)it.slot * kM + m) * D;
+#pragma unroll
+    for (int d = 0; d < kDB; ++d) *reinterpret_cast<f32x4 *>(wo + 16 * d + 4 * grp) = acc[d];
+    if (grp == 0) {
+      ws_ml[((int64_t)it.slot * kM + m) * 2 + 0] = m_run;
+      ws_ml[((int64_t)it.slot * kM + m) * 2 + 1] = l_row;
+    }
+  }
+}
+
 // ================================ merge ========================================
 
 // Combine the split partials of each (tile, kv head) with their log-sum-exp weights:
@@ -1636,6 +1848,59 @@ int launch_paged(const PlanHeader &h, const int32_t *plan_dev, const void *q, co
   return PIC_OK;
 }
 
+// fp32 over the pool: the same angle table, key-block records (with fp32 row bytes) and
+// merge as the bf16 path, and attn_f32_paged_kernel.
+template <int D, bool kHalf>
+int launch_paged_f32(const PlanHeader &h, const int32_t *plan_dev, const void *q,
+                     const void *pool_k, const void *pool_v, const int32_t *cbp,
+                     const int32_t *bids, const void *kf, const void *vf, void *out,
+                     double rope_base, float scale, void *workspace, int64_t pool_blocks,
+                     hipStream_t s) {
+  const int32_t *rows = plan_dev + h[PIC_H_O_ROWS];
+  const AttnTile *tiles = reinterpret_cast<const AttnTile *>(plan_dev + h[PIC_H_O_ATTN_TILES]);
+  const AttnItem *items = reinterpret_cast<const AttnItem *>(plan_dev + h[PIC_H_O_ATTN_ITEMS]);
+  const MergeEntry *merges = reinterpret_cast<const MergeEntry *>(plan_dev + h[PIC_H_O_MERGE]);
+  const int32_t *segs = plan_dev + h[PIC_H_O_SEGS];
+  const int4 *kblocks = reinterpret_cast<const int4 *>(plan_dev + h[PIC_H_O_KBLOCKS]);
+  char *ws = static_cast<char *>(workspace);
+  float *ws_o = reinterpret_cast<float *>(ws);
+  float *ws_ml = ws_o + (int64_t)h[PIC_H_N_PARTIALS] * kM * D;
+  float2 *angles = reinterpret_cast<float2 *>(ws + angle_offset(h, D));
+  KeyBlockRec *recs = reinterpret_cast<KeyBlockRec *>(ws + keyblock_offset(h, D));
+  const int n_chunks = h[PIC_H_N_CHUNKS];
+  if (n_chunks > 0) {
+    const int64_t total = (int64_t)n_chunks * (D / 2);
+    const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65535);
+    hipLaunchKernelGGL(paged_angles_kernel, dim3(blocks), dim3(256), 0, s, angles, segs,
+                       n_chunks, D / 2, make_theta(D, rope_base));
+    PIC_LAUNCH_CHECK();
+  }
+  const int tok_bytes = h[PIC_H_H_KV] * D * 4;
+  const int n_kblocks = h[PIC_H_N_KBLOCKS];
+  if (n_kblocks > 0) {
+    hipLaunchKernelGGL(paged_blocks_kernel, dim3((n_kblocks + 255) / 256), dim3(256), 0, s,
+                       recs, kblocks, segs, cbp, bids, n_kblocks, (int)pool_blocks,
+                       kPoolBlockRows * tok_bytes);
+    PIC_LAUNCH_CHECK();
+  }
+  hipLaunchKernelGGL((attn_f32_paged_kernel<D, kHalf>), dim3(h[PIC_H_N_ATTN_ITEMS]),
+                     dim3(kF32Threads), 0, s, static_cast<const float *>(q),
+                     static_cast<const float *>(pool_k), static_cast<const float *>(pool_v),
+                     static_cast<const float *>(kf), static_cast<const float *>(vf),
+                     static_cast<float *>(out), rows, tiles, items, recs, angles, ws_o, ws_ml,
+                     h[PIC_H_H_Q], h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], scale * kLog2e);
+  PIC_LAUNCH_CHECK();
+  if (h[PIC_H_N_MERGE] > 0) {
+    const int64_t threads = (int64_t)h[PIC_H_N_MERGE] * kM * (D / 8);
+    const unsigned blocks = (unsigned)std::min<int64_t>((threads + 255) / 256, 1 << 20);
+    hipLaunchKernelGGL((merge_kernel<float, D>), dim3(blocks), dim3(256), 0, s,
+                       static_cast<float *>(out), tiles, merges, ws_o, ws_ml, h[PIC_H_H_Q],
+                       h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], h[PIC_H_N_MERGE]);
+    PIC_LAUNCH_CHECK();
+  }
+  return PIC_OK;
+}
+
 // Decode workspace: record O [n_dec_recs][G][D] in bf16 (the records are HBM traffic
 // of an HBM-bound step; each is one rounding of an unnormalised sum the merge weights
 // and renormalises), record (m, l) [..][2] fp32, then the angle table [n_chunks][D/2]
@@ -1763,10 +2028,12 @@ extern "C" int pic_selective_attn_paged(
   if (rope_layout != PIC_ROPE_ADJACENT && rope_layout != PIC_ROPE_HALF) return PIC_EINVAL;
   if (!(scale > 0.f) || !std::isfinite(scale) || head_dim <= 0 || pool_blocks < 0) return PIC_EINVAL;
   if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return PIC_EINVAL;
-  if (dtype != PIC_BF16 || block_size != kPoolBlockRows) return PIC_EUNSUPPORTED;
-  if (head_dim != 64 && head_dim != 128) return PIC_EUNSUPPORTED;
+  if (block_size != kPoolBlockRows) return PIC_EUNSUPPORTED;
+  if (dtype == PIC_BF16 && head_dim != 64 && head_dim != 128) return PIC_EUNSUPPORTED;
+  if (dtype == PIC_F32 && head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return PIC_EUNSUPPORTED;
   // 32-bit buffer offsets (past-the-end loads sit at pool_bytes + one block)
-  const int64_t tok_bytes = (int64_t)h[PIC_H_H_KV] * head_dim * 2;
+  const int64_t tok_bytes = (int64_t)h[PIC_H_H_KV] * head_dim * (int64_t)dtype_size(dtype);
   const int64_t pool_bytes = pool_blocks * kPoolBlockRows * tok_bytes;
   if (pool_bytes > 0x7fff0000LL - kPoolBlockRows * tok_bytes ||
       (int64_t)h[PIC_H_N_ROWS] * tok_bytes > 0x7fff0000LL)
@@ -1782,6 +2049,22 @@ extern "C" int pic_selective_attn_paged(
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PIC_ENOSPC;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool half = rope_layout == PIC_ROPE_HALF;
+  if (dtype == PIC_F32) {
+#define PIC_PAGED32(D_)                                                                       \
+  return half ? launch_paged_f32<D_, true>(h, plan_dev, q, pool_k, pool_v, chunk_block_ptr,     \
+                                           block_ids, k_fresh, v_fresh, out, rope_base, scale,  \
+                                           workspace, pool_blocks, s)                           \
+              : launch_paged_f32<D_, false>(h, plan_dev, q, pool_k, pool_v, chunk_block_ptr,    \
+                                            block_ids, k_fresh, v_fresh, out, rope_base, scale, \
+                                            workspace, pool_blocks, s)
+    switch (head_dim) {
+      case 16: PIC_PAGED32(16);
+      case 32: PIC_PAGED32(32);
+      case 64: PIC_PAGED32(64);
+      default: PIC_PAGED32(128);
+    }
+#undef PIC_PAGED32
+  }
 #define PIC_PAGED(D_, H_)                                                                    \
   return launch_paged<D_, H_>(h, plan_dev, q, pool_k, pool_v, chunk_block_ptr, block_ids,     \
                               k_fresh, v_fresh, out, rope_base, scale, workspace,             \
