@@ -523,26 +523,24 @@ def bench_link(args, wl):
     t_link = float(np.mean(l_link))
 
     # per-kernel breakdown: the same entry points pic_link calls, one event between each
-    names = ("rope_delta", "qkv_rope", "splice", "selective_attn", "out_proj")
+    names = ("qkv_rope", "rope_splice", "selective_attn", "out_proj")
     reps = 3
     plan.to_device()
-    bev = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_layers)]
+    bev = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_layers)]
            for _ in range(reps)]
     for rr in range(reps):
         x.copy_(x0)
         for l in range(n_layers):
             e = bev[rr][l]
             e[0].record()
-            P.pic_rope_delta(plan, kc[l], wl.rope_base)
-            e[1].record()
             P.pic_qkv_rope(plan, x, wq[l], q, kf, vf, wl.rope_base, workspace=qkv_ws)
+            e[1].record()
+            P.pic_rope_splice(plan, kc[l], vc[l], kf, vf, wl.rope_base)
             e[2].record()
-            P.pic_splice(plan, kc[l], vc[l], kf, vf)
-            e[3].record()
             P.pic_selective_attn(plan, q, kc[l], vc[l], o, workspace=attn_ws)
-            e[4].record()
+            e[3].record()
             P.pic_out_proj(plan, o, wo[l], x)
-            e[5].record()
+            e[4].record()
     torch.cuda.synchronize()
     t = {n: float(np.mean([bev[rr][l][j].elapsed_time(bev[rr][l][j + 1])
                            for rr in range(reps) for l in range(n_layers)]))
@@ -576,10 +574,9 @@ def bench_link(args, wl):
                                "per layer",
                      "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes},
         "kernels": {
-            "rope_delta": {"ms": round(t["rope_delta"], 4)},
             "qkv_rope": {"ms": round(t["qkv_rope"], 4), "flops": qkv_flops,
                          "TFLOP_s": round(qkv_flops / (t["qkv_rope"] * 1e-3) / 1e12, 2)},
-            "splice": {"ms": round(t["splice"], 4)},
+            "rope_splice": {"ms": round(t["rope_splice"], 4)},
             "selective_attn": {"ms": round(t["selective_attn"], 4), "flops": attn_flops,
                                "TFLOP_s": round(attn_tflops, 2)},
             "out_proj": {"ms": round(t["out_proj"], 4), "flops": out_flops,
@@ -760,8 +757,9 @@ def main():
     splice_bytes = 4.0 * s * hkv * D * plan.n_rows
     attn_bytes = 2.0 * s * hkv * D * plan.n_tokens + 2.0 * s * hq * D * plan.n_rows
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     plan_s = []
+    mode = P.PIC_ROPE_AT_POSITION if args.rope_scheme == "nope" else P.PIC_ROPE_BY_DELTA
 
     def step(i=None):
         t0 = time.perf_counter()
@@ -770,15 +768,10 @@ def main():
         uploader.upload(p)
         e = ev[i] if i is not None else None
         if e: e[0].record()
-        if args.rope_scheme == "nope":
-            P.pic_rope_apply(p, k, wl.rope_base)
-        else:
-            P.pic_rope_delta(p, k, wl.rope_base)
+        P.pic_rope_splice(p, k, v, kf, vf, wl.rope_base, mode=mode)
         if e: e[1].record()
-        P.pic_splice(p, k, v, kf, vf)
-        if e: e[2].record()
         P.pic_selective_attn(p, q, k, v, out, workspace=ws)
-        if e: e[3].record()
+        if e: e[2].record()
 
     for _ in range(args.warmup):
         step()
@@ -790,10 +783,30 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / args.steps
 
-    l_rope = [e[0].elapsed_time(e[1]) for e in ev]
-    l_splice = [e[1].elapsed_time(e[2]) for e in ev]
-    l_attn = [e[2].elapsed_time(e[3]) for e in ev]
-    t_rope, t_splice, t_attn = (float(np.mean(x)) for x in (l_rope, l_splice, l_attn))
+    l_rs = [e[0].elapsed_time(e[1]) for e in ev]
+    l_attn = [e[1].elapsed_time(e[2]) for e in ev]
+    t_rs, t_attn = float(np.mean(l_rs)), float(np.mean(l_attn))
+
+    # breakdown after the timed steps: the two calls pic_rope_splice stands for, timed
+    # separately on the same buffers (each pass rotates K again: the bytes are the same),
+    # each pair followed by the attention call as in a step
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    dplan = uploader.upload(P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, n_cu=n_cu))
+    for e in sev:
+        e[0].record()
+        if args.rope_scheme == "nope":
+            P.pic_rope_apply(dplan, k, wl.rope_base)
+        else:
+            P.pic_rope_delta(dplan, k, wl.rope_base)
+        e[1].record()
+        P.pic_splice(dplan, k, v, kf, vf)
+        e[2].record()
+        P.pic_selective_attn(dplan, q, k, v, out, workspace=ws)
+    torch.cuda.synchronize()
+    l_rope = [e[0].elapsed_time(e[1]) for e in sev]
+    l_splice = [e[1].elapsed_time(e[2]) for e in sev]
+    t_rope, t_splice = float(np.mean(l_rope)), float(np.mean(l_splice))
+    rs_bytes = rope_bytes + splice_bytes
     tokens = plan.n_tokens
     value = tokens / (ms_step * 1e-3)
     attn_tflops = attn_flops / (t_attn * 1e-3) / 1e12
@@ -817,25 +830,32 @@ def main():
                    "head_dim": D, "rope_base": wl.rope_base, "rope_scheme": args.rope_scheme,
                    "parallelism": "none (1 GPU)"},
         "attn_tflops": round(attn_tflops, 2),
-        "splice_pass_tokens_per_s": round(tokens / ((t_rope + t_splice) * 1e-3), 1),
+        "splice_pass_tokens_per_s": round(tokens / (t_rs * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
                      "traffic": traffic,
                      "kernel": "pic_selective_attn call (attn_bf16_kernel + merge_kernel)",
                      "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes},
         "kernels": {
+            "rope_splice": {"ms": round(t_rs, 4), **pct(l_rs), "bytes": rs_bytes,
+                            "GB_s": round(rs_bytes / (t_rs * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(rs_bytes / (t_rs * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "call": "pic_rope_splice (%s + splice, one launch)"
+                                    % ("rope_apply" if args.rope_scheme == "nope" else "rope_delta")},
             ("rope_apply" if args.rope_scheme == "nope" else "rope_delta"): {
                 "ms": round(t_rope, 4), **pct(l_rope), "bytes": rope_bytes,
                            "GB_s": round(rope_bytes / (t_rope * 1e-3) / 1e9, 1),
-                           "hbm_frac": round(rope_bytes / (t_rope * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                           "hbm_frac": round(rope_bytes / (t_rope * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "call": "separate call, timed after the steps"},
             "splice": {"ms": round(t_splice, 4), **pct(l_splice), "bytes": splice_bytes,
                        "GB_s": round(splice_bytes / (t_splice * 1e-3) / 1e9, 1),
-                       "hbm_frac": round(splice_bytes / (t_splice * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                       "hbm_frac": round(splice_bytes / (t_splice * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "call": "separate call, timed after the steps"},
             "selective_attn": {"ms": round(t_attn, 4), **pct(l_attn), "flops": attn_flops,
                                "TFLOP_s": round(attn_tflops, 2),
                                "items": plan[P.H_N_ATTN_ITEMS], "merges": plan[P.H_N_MERGE]},
             "host_plan_ms": round(1e3 * float(np.mean(plan_s)), 4),
-            "gpu_idle_ms": round(ms_step - t_rope - t_splice - t_attn, 4),
+            "gpu_idle_ms": round(ms_step - t_rs - t_attn, 4),
         },
     }
     if not args.no_cpu_baseline:

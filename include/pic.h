@@ -12,7 +12,8 @@
  *                          R(delta_c) per row (pic_rope_apply: RoPE at the global
  *                          positions for a position-free cache).
  *   3. pic_splice          copies the fresh K/V of the recomputed rows into the spliced
- *                          buffers at their global positions.
+ *                          buffers at their global positions (pic_rope_splice: steps 2
+ *                          and 3 as one launch).
  *   4. pic_selective_attn  causal attention of the recomputed rows (global positions)
  *                          over every spliced key j <= p_r, GQA, flash-style on MFMA.
  *
@@ -78,6 +79,10 @@ enum { PIC_F32 = 0, PIC_BF16 = 1 };
 
 /* RoPE pair layouts. */
 enum { PIC_ROPE_ADJACENT = 0, PIC_ROPE_HALF = 1 };
+
+/* What pic_rope_splice does to the kept cached rows: the pic_rope_delta rotation or
+ * the pic_rope_apply RoPE at the target positions. */
+enum { PIC_ROPE_BY_DELTA = 0, PIC_ROPE_AT_POSITION = 1 };
 
 /* ------------------------------------------------------------------------------
  * Plan: one int32 array written by pic_build_index.  A header of
@@ -230,6 +235,20 @@ int pic_rope_apply(const int32_t *plan_host, const int32_t *plan_dev, void *k, i
 int pic_splice(const int32_t *plan_host, const int32_t *plan_dev, void *k, void *v,
                const void *k_fresh, const void *v_fresh, int32_t dtype, int32_t head_dim,
                void *stream);
+
+/*
+ * pic_rope_splice -- pic_rope_delta (rope_mode PIC_ROPE_BY_DELTA) or pic_rope_apply
+ * (PIC_ROPE_AT_POSITION), then pic_splice, as one kernel launch.
+ *                                                      [RoPE-C] 3.2-3.3, [EPIC] Step 3
+ * The result is bit-identical to the two calls in that order: the rotation skips every
+ * recomputed row, so the rows it rewrites and the rows the splice writes are disjoint
+ * and one launch needs no ordering between them.  Arguments, sizes and errors as the
+ * two calls (every check of both runs before the launch); PIC_EINVAL for another
+ * rope_mode.  Plans beyond 2^22 workgroups of work run as the two launches.
+ */
+int pic_rope_splice(const int32_t *plan_host, const int32_t *plan_dev, void *k, void *v,
+                    const void *k_fresh, const void *v_fresh, int32_t dtype, int32_t head_dim,
+                    int32_t rope_layout, double rope_base, int32_t rope_mode, void *stream);
 
 /* Bytes of workspace pic_selective_attn (split-KV partials; 0 if the plan has no split
  * tile) or pic_selective_attn_paged (partials, per-chunk angle table, per-key-block

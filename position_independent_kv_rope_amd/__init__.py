@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libpic.so")
 PIC_OK, PIC_EINVAL, PIC_ENOSPC, PIC_EUNSUPPORTED, PIC_EDEVICE = 0, -1, -2, -3, -4
 PIC_F32, PIC_BF16 = 0, 1
 PIC_ROPE_ADJACENT, PIC_ROPE_HALF = 0, 1
+PIC_ROPE_BY_DELTA, PIC_ROPE_AT_POSITION = 0, 1
 PIC_PLAN_MAGIC = 0x31434950
 PIC_ATTN_TILE_M = 128
 
@@ -33,6 +34,7 @@ PIC_DECODE_BLOCK = 32
 PIC_DECODE_WG_PER_CU = 4
 
 EXPORTED = ("pic_build_index", "pic_rope_delta", "pic_rope_apply", "pic_splice",
+            "pic_rope_splice",
             "pic_attn_workspace_bytes",
             "pic_selective_attn", "pic_selective_attn_paged", "pic_decode_workspace_bytes",
             "pic_decode_attn_paged", "pic_qkv_workspace_bytes", "pic_qkv_rope",
@@ -71,6 +73,8 @@ def lib():
     L.pic_rope_apply.restype = ctypes.c_int
     L.pic_splice.argtypes = [p, p, p, p, p, p, i32, i32, p]
     L.pic_splice.restype = ctypes.c_int
+    L.pic_rope_splice.argtypes = [p, p, p, p, p, p, i32, i32, i32, f64, i32, p]
+    L.pic_rope_splice.restype = ctypes.c_int
     L.pic_attn_workspace_bytes.argtypes = [p, i32]
     L.pic_attn_workspace_bytes.restype = sz
     L.pic_selective_attn.argtypes = [p, p, p, p, p, p, i32, i32, f32, p, sz, p]
@@ -318,6 +322,23 @@ def pic_splice(plan, k, v, k_fresh, v_fresh, stream=None):
                           _dev(k_fresh, "k_fresh"), _dev(v_fresh, "v_fresh"), _dtype_code(k),
                           int(k.shape[2]), _stream(stream))
     _check("pic_splice", st)
+
+
+def pic_rope_splice(plan, k, v, k_fresh, v_fresh, rope_base, layout=PIC_ROPE_ADJACENT,
+                    mode=PIC_ROPE_BY_DELTA, stream=None):
+    """pic_rope_delta (mode PIC_ROPE_BY_DELTA) or pic_rope_apply (PIC_ROPE_AT_POSITION),
+    then pic_splice, as one launch on the current stream."""
+    for t, n in ((k, plan.n_tokens), (v, plan.n_tokens), (k_fresh, plan.n_rows),
+                 (v_fresh, plan.n_rows)):
+        if t.shape[0] != n or t.dtype != k.dtype or tuple(t.shape[1:]) != tuple(k.shape[1:]):
+            raise ValueError("buffer shapes/dtypes do not match the plan")
+    if k.shape[1] != plan[H_H_KV]:
+        raise ValueError("k shape %s does not match the plan" % (tuple(k.shape),))
+    st = lib().pic_rope_splice(plan.host_ptr(), plan.dev_ptr(), _dev(k, "k"), _dev(v, "v"),
+                               _dev(k_fresh, "k_fresh"), _dev(v_fresh, "v_fresh"),
+                               _dtype_code(k), int(k.shape[2]), int(layout), float(rope_base),
+                               int(mode), _stream(stream))
+    _check("pic_rope_splice", st)
 
 
 def pic_attn_workspace_bytes(plan, head_dim):

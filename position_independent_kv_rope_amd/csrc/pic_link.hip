@@ -433,15 +433,12 @@ extern "C" int pic_link(const int32_t *plan_host, const int32_t *plan_dev, int32
   const size_t attn_ws = (pic_attn_workspace_bytes(plan_host, head_dim) + 255) / 256 * 256;
   char *ws = static_cast<char *>(workspace);
   for (int l = 0; l < n_layers && st == PIC_OK; ++l) {
-    st = pic_rope_delta(plan_host, plan_dev, k_cache[l], dtype, head_dim, rope_layout, rope_base,
-                        stream);
-    if (st == PIC_OK)
-      st = pic_qkv_rope(plan_host, plan_dev, x, w_qkv[l], q, k_fresh, v_fresh, dtype, d_model,
-                        head_dim, rope_layout, rope_base, ws + attn_ws, workspace_bytes - attn_ws,
-                        stream);
-    if (st == PIC_OK)
-      st = pic_splice(plan_host, plan_dev, k_cache[l], v_cache[l], k_fresh, v_fresh, dtype,
-                      head_dim, stream);
+    st = pic_qkv_rope(plan_host, plan_dev, x, w_qkv[l], q, k_fresh, v_fresh, dtype, d_model,
+                      head_dim, rope_layout, rope_base, ws + attn_ws, workspace_bytes - attn_ws,
+                      stream);
+    if (st == PIC_OK)  // the layer's rotation and splice as one launch
+      st = pic_rope_splice(plan_host, plan_dev, k_cache[l], v_cache[l], k_fresh, v_fresh, dtype,
+                           head_dim, rope_layout, rope_base, PIC_ROPE_BY_DELTA, stream);
     if (st == PIC_OK)
       st = pic_selective_attn(plan_host, plan_dev, q, k_cache[l], v_cache[l], o, dtype, head_dim,
                               scale, attn_ws ? ws : nullptr, attn_ws, stream);

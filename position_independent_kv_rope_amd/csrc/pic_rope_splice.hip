@@ -62,20 +62,16 @@ __device__ __forceinline__ void store8(float *p, const float (&x)[8]) {
   *reinterpret_cast<f32x4 *>(p + 4) = b;
 }
 
-// One workgroup per rope tile (<= PIC_ROPE_TILE_ROWS rows of one chunk).
+// One rope tile (<= PIC_ROPE_TILE_ROWS rows of one chunk), run by one workgroup.
 // kAbs == false (rotation by delta): one angle delta * theta_i per pair for the whole
-//   tile; tiles with delta 0 return at once.
+//   tile (callers skip tiles with delta 0).
 // kAbs == true (RoPE at the target position): angle (pos0 + r) * theta_i for row r.
-// The angles go to LDS (dynamic: n_pairs or n_rows * n_pairs float2) once per tile.
+// The angles go to LDS (cs: n_pairs or n_rows * n_pairs float2) once per tile.
 // kHalf == false: pairs (2i, 2i+1); a unit is 8 consecutive elements = 4 pairs.
 // kHalf == true:  pairs (i, i+D/2); a unit is elements [8j, 8j+8) and [D/2+8j, D/2+8j+8).
 template <typename T, bool kHalf, bool kAbs>
-__global__ __launch_bounds__(kRopeThreads) void rope_kernel(
-    T *__restrict__ k, const RopeTile *__restrict__ tiles, int h_kv, int head_dim,
-    ThetaTable theta) {
-  extern __shared__ float2 cs[];
-  const RopeTile t = tiles[blockIdx.x];
-  if (!kAbs && t.delta == 0) return;
+__device__ __forceinline__ void rope_tile(T *__restrict__ k, const RopeTile &t, int h_kv,
+                                          int head_dim, const ThetaTable &theta, float2 *cs) {
   const int n_pairs = head_dim >> 1;
   if (kAbs) {
     for (int e = threadIdx.x; e < t.n_rows * n_pairs; e += kRopeThreads) {
@@ -142,22 +138,77 @@ __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
   }
 }
 
-// Row scatter of the fresh K/V: 16-byte units, both buffers in one pass.
-__global__ __launch_bounds__(256) void splice_kernel(u32x4 *__restrict__ k, u32x4 *__restrict__ v,
-                                                     const u32x4 *__restrict__ kf,
-                                                     const u32x4 *__restrict__ vf,
-                                                     const int32_t *__restrict__ row_tok,
-                                                     int64_t total, int units_per_row) {
-  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total;
-       u += (int64_t)gridDim.x * 256) {
-    const int64_t r = u / units_per_row;
-    const int64_t c = u - r * units_per_row;
-    const int64_t dst = (int64_t)row_tok[r] * units_per_row + c;
-    const u32x4 a = kf[u];
-    const u32x4 b = vf[u];
-    k[dst] = a;
-    v[dst] = b;
+template <typename T, bool kHalf, bool kAbs>
+__global__ __launch_bounds__(kRopeThreads) void rope_kernel(
+    T *__restrict__ k, const RopeTile *__restrict__ tiles, int h_kv, int head_dim,
+    ThetaTable theta) {
+  extern __shared__ float2 cs[];
+  const RopeTile t = tiles[blockIdx.x];
+  if (!kAbs && t.delta == 0) return;
+  rope_tile<T, kHalf, kAbs>(k, t, h_kv, head_dim, theta, cs);
+}
+
+// Row scatter of the fresh K/V in 16-byte units, both buffers in one pass: one
+// workgroup copies the kSpliceUnroll * 256 consecutive units starting at u0 (unit u is
+// chunk u % units_per_row of fresh row u / units_per_row), all loads before the stores.
+constexpr int kSpliceThreads = 256;
+constexpr int kSpliceUnroll = 4;
+constexpr int64_t kSpliceBlockUnits = kSpliceThreads * kSpliceUnroll;
+__device__ __forceinline__ void splice_block(u32x4 *__restrict__ k, u32x4 *__restrict__ v,
+                                             const u32x4 *__restrict__ kf,
+                                             const u32x4 *__restrict__ vf,
+                                             const int32_t *__restrict__ row_tok, int64_t u0,
+                                             int64_t total, int units_per_row) {
+  u32x4 a[kSpliceUnroll], b[kSpliceUnroll];
+  int64_t dst[kSpliceUnroll];
+#pragma unroll
+  for (int q = 0; q < kSpliceUnroll; ++q) {
+    const int64_t u = u0 + q * kSpliceThreads + threadIdx.x;
+    dst[q] = -1;
+    if (u < total) {
+      const int64_t r = u / units_per_row;
+      dst[q] = (int64_t)row_tok[r] * units_per_row + (u - r * units_per_row);
+      a[q] = kf[u];
+      b[q] = vf[u];
+    }
   }
+#pragma unroll
+  for (int q = 0; q < kSpliceUnroll; ++q)
+    if (dst[q] >= 0) {
+      k[dst[q]] = a[q];
+      v[dst[q]] = b[q];
+    }
+}
+
+__global__ __launch_bounds__(kSpliceThreads) void splice_kernel(
+    u32x4 *__restrict__ k, u32x4 *__restrict__ v, const u32x4 *__restrict__ kf,
+    const u32x4 *__restrict__ vf, const int32_t *__restrict__ row_tok, int64_t total,
+    int units_per_row) {
+  for (int64_t u0 = (int64_t)blockIdx.x * kSpliceBlockUnits; u0 < total;
+       u0 += (int64_t)gridDim.x * kSpliceBlockUnits)
+    splice_block(k, v, kf, vf, row_tok, u0, total, units_per_row);
+}
+
+// Rotation and splice in one launch.  The rotation never touches a recomputed row
+// (rope tiles start after each chunk's recomputed head, and query rows belong to no
+// chunk), so the two parts write disjoint rows and need no ordering: workgroups
+// [0, n_splice) copy fresh rows, the rest take one rope tile each.
+template <typename T, bool kHalf, bool kAbs>
+__global__ __launch_bounds__(kRopeThreads) void rope_splice_kernel(
+    T *__restrict__ k, T *__restrict__ v, const u32x4 *__restrict__ kf,
+    const u32x4 *__restrict__ vf, const int32_t *__restrict__ row_tok, int64_t total,
+    int units_per_row, int n_splice, const RopeTile *__restrict__ tiles, int h_kv,
+    int head_dim, ThetaTable theta) {
+  static_assert(kRopeThreads == kSpliceThreads, "one workgroup size for both parts");
+  extern __shared__ float2 cs[];
+  if ((int)blockIdx.x < n_splice) {
+    splice_block(reinterpret_cast<u32x4 *>(k), reinterpret_cast<u32x4 *>(v), kf, vf, row_tok,
+                 (int64_t)blockIdx.x * kSpliceBlockUnits, total, units_per_row);
+    return;
+  }
+  const RopeTile t = tiles[blockIdx.x - n_splice];
+  if (!kAbs && t.delta == 0) return;
+  rope_tile<T, kHalf, kAbs>(k, t, h_kv, head_dim, theta, cs);
 }
 
 template <typename T, bool kAbs>
@@ -176,11 +227,11 @@ int launch_rope(const PlanHeader &h, const int32_t *plan_dev, void *k, int head_
   return PIC_OK;
 }
 
-// Shared argument checks and dispatch of pic_rope_delta / pic_rope_apply.
+// Argument checks shared by pic_rope_delta / pic_rope_apply / pic_rope_splice; PIC_OK
+// means the rotation may be launched (or has nothing to do when the plan has no tile).
 template <bool kAbs>
-int rope_entry(const int32_t *plan_host, const int32_t *plan_dev, void *k, int32_t dtype,
-               int32_t head_dim, int32_t rope_layout, double rope_base, void *stream) {
-  const PlanHeader h{plan_host};
+int rope_check(const PlanHeader &h, const int32_t *plan_dev, const void *k, int32_t dtype,
+               int32_t head_dim, int32_t rope_layout, double rope_base) {
   if (!h.valid()) return PIC_EINVAL;
   if (dtype != PIC_BF16 && dtype != PIC_F32) return PIC_EINVAL;
   if (rope_layout != PIC_ROPE_ADJACENT && rope_layout != PIC_ROPE_HALF) return PIC_EINVAL;
@@ -191,16 +242,95 @@ int rope_entry(const int32_t *plan_host, const int32_t *plan_dev, void *k, int32
   if (h[PIC_H_N_ROPE_TILES] == 0) return PIC_OK;
   if (plan_dev == nullptr || k == nullptr) return PIC_EINVAL;
   if (kAbs) {  // positions are formed in fp32 exactly, which holds below 2^24
+    const int32_t *plan_host = h.w;
     const RopeTile *tl = reinterpret_cast<const RopeTile *>(plan_host + h[PIC_H_O_ROPE_TILES]);
     for (int32_t i = 0; i < h[PIC_H_N_ROPE_TILES]; ++i)
       if ((int64_t)tl[i].pos0 + tl[i].n_rows > (int64_t(1) << 24)) return PIC_EUNSUPPORTED;
   }
+  return PIC_OK;
+}
 
+template <bool kAbs>
+int rope_entry(const int32_t *plan_host, const int32_t *plan_dev, void *k, int32_t dtype,
+               int32_t head_dim, int32_t rope_layout, double rope_base, void *stream) {
+  const PlanHeader h{plan_host};
+  const int st = rope_check<kAbs>(h, plan_dev, k, dtype, head_dim, rope_layout, rope_base);
+  if (st != PIC_OK || h[PIC_H_N_ROPE_TILES] == 0) return st;
   const ThetaTable theta = make_theta(head_dim, rope_base);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == PIC_BF16)
     return launch_rope<__bf16, kAbs>(h, plan_dev, k, head_dim, rope_layout, theta, s);
   return launch_rope<float, kAbs>(h, plan_dev, k, head_dim, rope_layout, theta, s);
+}
+
+// Argument checks of pic_splice; *total / *units_per_row describe the copy.
+int splice_check(const PlanHeader &h, const int32_t *plan_dev, const void *k, const void *v,
+                 const void *k_fresh, const void *v_fresh, int32_t dtype, int32_t head_dim,
+                 int64_t *total, int *units_per_row) {
+  *total = 0;
+  if (!h.valid()) return PIC_EINVAL;
+  const size_t es = dtype_size(dtype);
+  if (es == 0 || head_dim <= 0) return PIC_EINVAL;
+  if (head_dim % 8 != 0) return PIC_EUNSUPPORTED;
+  const int64_t n_rows = h[PIC_H_N_ROWS];
+  if (n_rows == 0) return PIC_OK;
+  if (!plan_dev || !k || !v || !k_fresh || !v_fresh) return PIC_EINVAL;
+  const int64_t row_bytes = (int64_t)h[PIC_H_H_KV] * head_dim * (int64_t)es;
+  *units_per_row = (int)(row_bytes / 16);
+  *total = n_rows * *units_per_row;
+  return PIC_OK;
+}
+
+int launch_splice(const PlanHeader &h, const int32_t *plan_dev, void *k, void *v,
+                  const void *k_fresh, const void *v_fresh, int64_t total, int units_per_row,
+                  hipStream_t s) {
+  const int64_t blocks =
+      std::min<int64_t>((total + kSpliceBlockUnits - 1) / kSpliceBlockUnits, 8192);
+  hipLaunchKernelGGL(splice_kernel, dim3((unsigned)blocks), dim3(kSpliceThreads), 0, s,
+                     static_cast<u32x4 *>(k), static_cast<u32x4 *>(v),
+                     static_cast<const u32x4 *>(k_fresh), static_cast<const u32x4 *>(v_fresh),
+                     plan_dev + h[PIC_H_O_ROW_TOK], total, units_per_row);
+  PIC_LAUNCH_CHECK();
+  return PIC_OK;
+}
+
+// Grid limit of the single launch (rope tiles + splice workgroups); larger plans run
+// the two parts as two launches on the same stream.
+constexpr int64_t kMaxFusedBlocks = int64_t(1) << 22;
+
+template <typename T, bool kAbs>
+int launch_rope_splice(const PlanHeader &h, const int32_t *plan_dev, void *k, void *v,
+                       const void *k_fresh, const void *v_fresh, int64_t total,
+                       int units_per_row, int head_dim, int layout, const ThetaTable &theta,
+                       hipStream_t s) {
+  const int n_tiles = h[PIC_H_N_ROPE_TILES];
+  const int64_t n_splice = (total + kSpliceBlockUnits - 1) / kSpliceBlockUnits;
+  if (n_splice + n_tiles > kMaxFusedBlocks) {
+    if (n_tiles > 0) {
+      const int st = launch_rope<T, kAbs>(h, plan_dev, k, head_dim, layout, theta, s);
+      if (st != PIC_OK) return st;
+    }
+    return total > 0 ? launch_splice(h, plan_dev, k, v, k_fresh, v_fresh, total, units_per_row, s)
+                     : PIC_OK;
+  }
+  const RopeTile *tiles = reinterpret_cast<const RopeTile *>(plan_dev + h[PIC_H_O_ROPE_TILES]);
+  const dim3 grid((unsigned)(n_splice + n_tiles));
+  const size_t lds = (kAbs ? PIC_ROPE_TILE_ROWS : 1) * (size_t)(head_dim / 2) * sizeof(float2);
+  const int32_t *row_tok = plan_dev + h[PIC_H_O_ROW_TOK];
+  if (layout == PIC_ROPE_HALF)
+    hipLaunchKernelGGL((rope_splice_kernel<T, true, kAbs>), grid, dim3(kRopeThreads), lds, s,
+                       static_cast<T *>(k), static_cast<T *>(v),
+                       static_cast<const u32x4 *>(k_fresh), static_cast<const u32x4 *>(v_fresh),
+                       row_tok, total, units_per_row, (int)n_splice, tiles, h[PIC_H_H_KV],
+                       head_dim, theta);
+  else
+    hipLaunchKernelGGL((rope_splice_kernel<T, false, kAbs>), grid, dim3(kRopeThreads), lds, s,
+                       static_cast<T *>(k), static_cast<T *>(v),
+                       static_cast<const u32x4 *>(k_fresh), static_cast<const u32x4 *>(v_fresh),
+                       row_tok, total, units_per_row, (int)n_splice, tiles, h[PIC_H_H_KV],
+                       head_dim, theta);
+  PIC_LAUNCH_CHECK();
+  return PIC_OK;
 }
 
 }  // namespace
@@ -225,22 +355,42 @@ extern "C" int pic_splice(const int32_t *plan_host, const int32_t *plan_dev, voi
                           int32_t head_dim, void *stream) {
   using namespace pic;
   const PlanHeader h{plan_host};
-  if (!h.valid()) return PIC_EINVAL;
-  const size_t es = dtype_size(dtype);
-  if (es == 0 || head_dim <= 0) return PIC_EINVAL;
-  if (head_dim % 8 != 0) return PIC_EUNSUPPORTED;
-  const int64_t n_rows = h[PIC_H_N_ROWS];
-  if (n_rows == 0) return PIC_OK;
-  if (!plan_dev || !k || !v || !k_fresh || !v_fresh) return PIC_EINVAL;
-  const int64_t row_bytes = (int64_t)h[PIC_H_H_KV] * head_dim * (int64_t)es;
-  const int units_per_row = (int)(row_bytes / 16);
-  const int64_t total = n_rows * units_per_row;
-  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
-  hipLaunchKernelGGL(splice_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<u32x4 *>(k),
-                     static_cast<u32x4 *>(v), static_cast<const u32x4 *>(k_fresh),
-                     static_cast<const u32x4 *>(v_fresh), plan_dev + h[PIC_H_O_ROW_TOK], total,
-                     units_per_row);
-  PIC_LAUNCH_CHECK();
-  return PIC_OK;
+  int64_t total;
+  int units_per_row;
+  const int st = splice_check(h, plan_dev, k, v, k_fresh, v_fresh, dtype, head_dim, &total,
+                              &units_per_row);
+  if (st != PIC_OK || total == 0) return st;
+  return launch_splice(h, plan_dev, k, v, k_fresh, v_fresh, total, units_per_row,
+                       static_cast<hipStream_t>(stream));
+}
+
+extern "C" int pic_rope_splice(const int32_t *plan_host, const int32_t *plan_dev, void *k,
+                               void *v, const void *k_fresh, const void *v_fresh, int32_t dtype,
+                               int32_t head_dim, int32_t rope_layout, double rope_base,
+                               int32_t rope_mode, void *stream) {
+  using namespace pic;
+  const PlanHeader h{plan_host};
+  if (rope_mode != PIC_ROPE_BY_DELTA && rope_mode != PIC_ROPE_AT_POSITION) return PIC_EINVAL;
+  const bool abs = rope_mode == PIC_ROPE_AT_POSITION;
+  int st = abs ? rope_check<true>(h, plan_dev, k, dtype, head_dim, rope_layout, rope_base)
+               : rope_check<false>(h, plan_dev, k, dtype, head_dim, rope_layout, rope_base);
+  if (st != PIC_OK) return st;
+  int64_t total;
+  int units_per_row = 0;
+  st = splice_check(h, plan_dev, k, v, k_fresh, v_fresh, dtype, head_dim, &total,
+                    &units_per_row);
+  if (st != PIC_OK) return st;
+  if (total == 0 && h[PIC_H_N_ROPE_TILES] == 0) return PIC_OK;
+  const ThetaTable theta = make_theta(head_dim, rope_base);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == PIC_BF16)
+    return abs ? launch_rope_splice<__bf16, true>(h, plan_dev, k, v, k_fresh, v_fresh, total,
+                                                  units_per_row, head_dim, rope_layout, theta, s)
+               : launch_rope_splice<__bf16, false>(h, plan_dev, k, v, k_fresh, v_fresh, total,
+                                                   units_per_row, head_dim, rope_layout, theta,
+                                                   s);
+  return abs ? launch_rope_splice<float, true>(h, plan_dev, k, v, k_fresh, v_fresh, total,
+                                               units_per_row, head_dim, rope_layout, theta, s)
+             : launch_rope_splice<float, false>(h, plan_dev, k, v, k_fresh, v_fresh, total,
+                                                units_per_row, head_dim, rope_layout, theta, s);
 }

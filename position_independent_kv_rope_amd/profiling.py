@@ -27,7 +27,8 @@ import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SHORT = [("qkv_rope_gemm_kernel", "qkv_rope_gemm"), ("out_proj_gemm_kernel", "out_proj_gemm"),
+SHORT = [("rope_splice_kernel", "rope_splice"),
+         ("qkv_rope_gemm_kernel", "qkv_rope_gemm"), ("out_proj_gemm_kernel", "out_proj_gemm"),
          ("state_compose_kernel", "state_compose"),
          ("row_angles_kernel", "row_angles"),
          ("attn_bf16_paged_kernel", "attn_bf16_paged"), ("paged_angles_kernel", "paged_angles"),

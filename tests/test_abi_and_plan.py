@@ -123,6 +123,17 @@ def test_device_entry_points_reject_bad_arguments_without_launching():
     assert L.pic_splice(bp, fake, fake, fake, fake, fake, P.PIC_F32, 16, None) == P.PIC_EINVAL
     assert L.pic_splice(hp, fake, fake, None, fake, fake, P.PIC_F32, 16, None) == P.PIC_EINVAL
     assert L.pic_splice(hp, fake, fake, fake, fake, fake, P.PIC_F32, 12, None) == P.PIC_EUNSUPPORTED
+    rs = L.pic_rope_splice
+    f4 = (fake, fake, fake, fake)
+    assert rs(bp, fake, *f4, P.PIC_F32, 16, 0, 1e4, 0, None) == P.PIC_EINVAL  # bad plan
+    assert rs(hp, fake, *f4, P.PIC_F32, 16, 0, 1e4, 2, None) == P.PIC_EINVAL  # rope_mode
+    assert rs(hp, fake, *f4, P.PIC_F32, 16, 2, 1e4, 0, None) == P.PIC_EINVAL  # layout
+    assert rs(hp, fake, *f4, P.PIC_F32, 16, 0, 0.0, 1, None) == P.PIC_EINVAL  # base
+    assert rs(hp, fake, *f4, 7, 16, 0, 1e4, 0, None) == P.PIC_EINVAL  # dtype
+    assert rs(hp, fake, None, fake, fake, fake, P.PIC_F32, 16, 0, 1e4, 0, None) == P.PIC_EINVAL
+    assert rs(hp, fake, fake, None, fake, fake, P.PIC_F32, 16, 0, 1e4, 0, None) == P.PIC_EINVAL
+    assert rs(hp, fake, fake, fake, fake, None, P.PIC_F32, 16, 0, 1e4, 1, None) == P.PIC_EINVAL
+    assert rs(hp, fake, *f4, P.PIC_F32, 12, 0, 1e4, 0, None) == P.PIC_EUNSUPPORTED
     args = (fake, fake, fake, fake)
     assert L.pic_selective_attn(hp, fake, *args, P.PIC_F32, 16, 0.0, None, 0, None) == P.PIC_EINVAL
     assert L.pic_selective_attn(hp, fake, *args, P.PIC_F32, 24, 0.25, None, 0, None) == P.PIC_EUNSUPPORTED

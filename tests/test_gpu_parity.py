@@ -41,7 +41,7 @@ def f64(t):
 class Run:
     """One pass of the path on the GPU, keeping every intermediate on the host."""
 
-    def __init__(self, wl, layout="adjacent", n_cu=0, pos_base=0, scheme="delta"):
+    def __init__(self, wl, layout="adjacent", n_cu=0, pos_base=0, scheme="delta", fused=False):
         # scheme "delta": cached K carries RoPE at local positions (rotation by delta);
         # scheme "nope": cached K is position-free and gets RoPE at the target positions
         self.wl = wl
@@ -58,18 +58,30 @@ class Run:
         q, kf, vf = self.q.to(dev), self.kf.to(dev), self.vf.to(dev)
         out = torch.full_like(q, float("nan"))
         ws = P.attn_workspace(self.plan, wl.head_dim)
-        say(wl.name, "k=%d" % wl.k, layout, "rope_" + scheme)
-        if scheme == "nope":
-            P.pic_rope_apply(self.plan, k, wl.rope_base, LAYOUTS[layout])
-        else:
-            P.pic_rope_delta(self.plan, k, wl.rope_base, LAYOUTS[layout])
         self.scheme = scheme
-        torch.cuda.synchronize()
-        self.k_rot = k.cpu()
-        say(wl.name, "splice")
-        P.pic_splice(self.plan, k, v, kf, vf)
-        torch.cuda.synchronize()
-        self.k_spl, self.v_spl = k.cpu(), v.cpu()
+        if fused:
+            # rotation and splice as one launch; the rotated-only K is the result with
+            # the recomputed rows put back to their inputs (the rotation skips them)
+            say(wl.name, "k=%d" % wl.k, layout, "rope_splice (one launch)", "rope_" + scheme)
+            mode = P.PIC_ROPE_AT_POSITION if scheme == "nope" else P.PIC_ROPE_BY_DELTA
+            P.pic_rope_splice(self.plan, k, v, kf, vf, wl.rope_base, LAYOUTS[layout], mode)
+            torch.cuda.synchronize()
+            self.k_spl, self.v_spl = k.cpu(), v.cpu()
+            self.k_rot = self.k_spl.clone()
+            rt = torch.as_tensor(np.asarray(self.plan.row_tok, dtype=np.int64))
+            self.k_rot[rt] = self.k_in[rt]
+        else:
+            say(wl.name, "k=%d" % wl.k, layout, "rope_" + scheme)
+            if scheme == "nope":
+                P.pic_rope_apply(self.plan, k, wl.rope_base, LAYOUTS[layout])
+            else:
+                P.pic_rope_delta(self.plan, k, wl.rope_base, LAYOUTS[layout])
+            torch.cuda.synchronize()
+            self.k_rot = k.cpu()
+            say(wl.name, "splice")
+            P.pic_splice(self.plan, k, v, kf, vf)
+            torch.cuda.synchronize()
+            self.k_spl, self.v_spl = k.cpu(), v.cpu()
         say(wl.name, "selective_attn items=%d merges=%d" % (self.plan[P.H_N_ATTN_ITEMS],
                                                           self.plan[P.H_N_MERGE]))
         P.pic_selective_attn(self.plan, q, k, v, out, workspace=ws)
@@ -402,3 +414,44 @@ def test_random_configurations(i):
     say("random case", i, wl.dtype, "h_q=%d h_kv=%d D=%d k=%d" % (wl.h_q, wl.h_kv, wl.head_dim, wl.k),
         layout, "pos_base=%d" % pos_base, [(sum(r.chunk_lens), len(r.chunk_lens), r.q_len) for r in wl.requests])
     check_run(Run(wl, layout, n_cu=(2 if i % 2 else 0), pos_base=pos_base))
+
+
+ONE_LAUNCH_CASES = [
+    # (workload, layout, scheme, pos_base, n_cu)
+    ("worked_example", "adjacent", "delta", 0, 0),
+    ("worked_example", "half", "nope", 0, 0),
+    ("ragged_bf16", "adjacent", "delta", 0, 2),
+    ("f32_d64", "half", "delta", 4, 0),
+    ("gqa8_bf16", "adjacent", "nope", 0, 0),
+    ("only_query_rows", "adjacent", "delta", 0, 0),
+    ("long_context_k16", "adjacent", "delta", 0, 256),
+]
+
+
+def _one_launch_workload(name):
+    if name == "worked_example":
+        return W.worked_example()
+    if name == "long_context_k16":
+        return W.long_context(k=16)
+    case = [c for c in EDGE_CASES if c[0] == name][0]
+    return _custom(*case)
+
+
+@pytest.mark.parametrize("case", ONE_LAUNCH_CASES, ids=["-".join(map(str, c)) for c in ONE_LAUNCH_CASES])
+def test_rope_splice_one_launch(case):
+    # pic_rope_splice: the oracle checks of every stage, and its spliced K/V bit-equal to
+    # the two calls it replaces on the same inputs
+    name, layout, scheme, pos_base, n_cu = case
+    wl = _one_launch_workload(name)
+    fused = Run(wl, layout, n_cu=n_cu, pos_base=pos_base, scheme=scheme, fused=True)
+    check_run(fused)
+    apart = Run(wl, layout, n_cu=n_cu, pos_base=pos_base, scheme=scheme)
+    assert torch.equal(fused.k_spl, apart.k_spl)
+    assert torch.equal(fused.v_spl, apart.v_spl)
+    assert torch.equal(fused.out, apart.out)
+
+
+def test_rope_splice_epic_sweep_full_size_sampled():
+    # the call bench.py times, at its size and launch configuration
+    run = Run(W.epic_sweep(k=16), n_cu=256, fused=True)
+    check_run(run, sample_rows=48)
