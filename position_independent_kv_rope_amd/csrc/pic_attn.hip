@@ -1285,19 +1285,29 @@ __global__ __launch_bounds__(kDecMergeThreads) void dec_merge_kernel(
     den += w * ls;
     num += w * os;
   };
+  // kU records per thread per pass, every load issued before the first fold (a request's
+  // records number in the hundreds, so most groups finish in one pass)
+  constexpr int kU = 8;
   const int s_end = rec_ptr[b * h_kv + g + 1];
-  for (int sl = rec_ptr[b * h_kv + g] + gi; sl < s_end; sl += 2 * kDecMergeGroups) {
-    const int sl2 = sl + kDecMergeGroups < s_end ? sl + kDecMergeGroups : sl;
-    const int64_t a1 = (int64_t)sl * group + hh;
-    const int64_t a2 = (int64_t)sl2 * group + hh;
-    const float2 ml1 = *reinterpret_cast<const float2 *>(ws_ml + a1 * 2);
-    const float2 ml2 = *reinterpret_cast<const float2 *>(ws_ml + a2 * 2);
-    const bf16x4 b1 = *reinterpret_cast<const bf16x4 *>(ws_o + a1 * D + 4 * c4);
-    const bf16x4 b2 = *reinterpret_cast<const bf16x4 *>(ws_o + a2 * D + 4 * c4);
-    const f32x4 o1 = {(float)b1[0], (float)b1[1], (float)b1[2], (float)b1[3]};
-    const f32x4 o2 = {(float)b2[0], (float)b2[1], (float)b2[2], (float)b2[3]};
-    fold(ml1.x, ml1.y, o1);
-    if (sl2 != sl) fold(ml2.x, ml2.y, o2);
+  for (int s0 = rec_ptr[b * h_kv + g] + gi; s0 < s_end; s0 += kU * kDecMergeGroups) {
+    float2 ml[kU];
+    bf16x4 ob[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int sl = s0 + u * kDecMergeGroups;
+      ml[u] = make_float2(kNegInf, 0.f);
+      if (sl < s_end) {
+        const int64_t a = (int64_t)sl * group + hh;
+        ml[u] = *reinterpret_cast<const float2 *>(ws_ml + a * 2);
+        ob[u] = *reinterpret_cast<const bf16x4 *>(ws_o + a * D + 4 * c4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (ml[u].x == kNegInf) continue;
+      const f32x4 o = {(float)ob[u][0], (float)ob[u][1], (float)ob[u][2], (float)ob[u][3]};
+      fold(ml[u].x, ml[u].y, o);
+    }
   }
   part_m[gi][c4] = mmax;
   part_l[gi][c4] = den;
