@@ -61,8 +61,10 @@ def replay_and_compare(fn, outputs, reps=3):
         say("replay", rep, "matches the eager result")
 
 
-def test_graph_contiguous_step():
+@pytest.mark.parametrize("one_launch", [False, True], ids=["two_calls", "rope_splice"])
+def test_graph_contiguous_step(one_launch):
     # restore K from a pristine copy, rotate, splice, attend: the whole one-batch path
+    # (rotation and splice as two calls, or as the one pic_rope_splice launch)
     # 4 x 4096 + 64 tokens: keys split into segments, so the merge kernel is captured too
     wl = W.Workload("graph_ctx", "bf16", 32, 8, 128, 500000.0, 16, [W.Request([4096] * 4, 64)],
                     seed=93)
@@ -80,8 +82,11 @@ def test_graph_contiguous_step():
     def fn():
         k.copy_(k0)
         v.copy_(v0)
-        P.pic_rope_delta(plan, k, wl.rope_base)
-        P.pic_splice(plan, k, v, kf, vf)
+        if one_launch:
+            P.pic_rope_splice(plan, k, v, kf, vf, wl.rope_base)
+        else:
+            P.pic_rope_delta(plan, k, wl.rope_base)
+            P.pic_splice(plan, k, v, kf, vf)
         P.pic_selective_attn(plan, q, k, v, out, workspace=ws)
 
     replay_and_compare(fn, [out, k])
