@@ -455,3 +455,14 @@ def test_rope_splice_epic_sweep_full_size_sampled():
     # the call bench.py times, at its size and launch configuration
     run = Run(W.epic_sweep(k=16), n_cu=256, fused=True)
     check_run(run, sample_rows=48)
+
+
+@pytest.mark.parametrize("i", [16, 17, 18, 19, 20, 21])
+def test_random_configurations_one_launch(i):
+    # seeded random configurations through pic_rope_splice (rotation by delta or RoPE at
+    # the target positions, then the splice, in one launch), every stage against the oracle
+    wl, layout, pos_base = _random_case(i)
+    scheme = "nope" if (i % 2 and pos_base == 0) else "delta"
+    say("random case (one launch)", i, wl.dtype, "h_q=%d h_kv=%d D=%d k=%d" % (wl.h_q, wl.h_kv, wl.head_dim, wl.k),
+        layout, scheme, "pos_base=%d" % pos_base)
+    check_run(Run(wl, layout, n_cu=(2 if i % 3 else 0), pos_base=pos_base, scheme=scheme, fused=True))
