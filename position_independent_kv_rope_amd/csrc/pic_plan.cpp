@@ -25,7 +25,7 @@ namespace {
 
 constexpr int64_t kMaxI32 = 0x7fffffff;
 constexpr int32_t kKeyAlign = 64;       // attention key block
-constexpr int32_t kMinSplitKeys = 2048;  // smallest key range worth a partial result
+constexpr int32_t kMinSplitKeys = 1024;  // smallest key range worth a partial result
 constexpr int kXcd = 8;                  // MI355X dies with a private L2 each
 constexpr int64_t kSegKeys = 8192;       // longest split-KV segment
 constexpr int64_t kTailKeys = 4096;      // longest item in a die's last round
@@ -324,13 +324,27 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   // Keys are split on a global grid of seg_len keys.  All tiles of one (request, kv
   // head) stream that reach a grid segment read the same K/V rows there; dispatched
   // together on one XCD they stream those rows in lockstep, so the XCD's L2 serves
-  // the re-reads.  seg_len is also capped so that small batches still fill the GPU
-  // (items no longer than half a fair share per workgroup slot).
+  // the re-reads.  seg_len is also capped so that small batches still fill the GPU:
+  // items no longer than a half or a third of a fair share per workgroup slot,
+  // whichever packs the item count (every tile's keys start at 0) closer to whole
+  // rounds of the slots.
   int64_t total_cost = 0;
   for (const AttnTile &t : tiles) total_cost += (int64_t)(t.p_last + 1) * h_kv;
   const int64_t slots = (int64_t)n_cu * 2;
-  int64_t seg_len = std::max<int64_t>(kMinSplitKeys, total_cost / std::max<int64_t>(1, slots * 2));
-  seg_len = round_up(std::min<int64_t>(seg_len, kSegKeys), kKeyAlign);
+  auto seg_for = [&](int64_t per_slot) {
+    const int64_t sl = std::max<int64_t>(kMinSplitKeys, total_cost / std::max<int64_t>(1, slots * per_slot));
+    return round_up(std::min<int64_t>(sl, kSegKeys), kKeyAlign);
+  };
+  auto round_fill = [&](int64_t sl) {
+    int64_t n = 0;
+    for (const AttnTile &t : tiles) n += (int64_t)h_kv * ((t.p_last + sl) / sl);
+    return (double)n / (double)(std::max<int64_t>(1, (n + slots - 1) / slots) * slots);
+  };
+  int64_t seg_len = seg_for(2);
+  {
+    const int64_t s3 = seg_for(3);
+    if (s3 != seg_len && round_fill(s3) > round_fill(seg_len)) seg_len = s3;
+  }
 
   std::vector<AttnItem> items;
   std::vector<MergeEntry> merges;
