@@ -538,3 +538,21 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_split_length_fills_whole_rounds_of_slots():
+    # small batches: the split segment is a half or a third of a fair share per workgroup
+    # slot (>= 1024 keys), whichever packs the item count closer to whole rounds of the
+    # 2 x n_cu slots; large batches keep the 8192-key segments
+    from position_independent_kv_rope_amd import workloads as W
+
+    def items(wl):
+        p = P.pic_build_index([r.chunk_lens for r in wl.requests], [r.q_len for r in wl.requests],
+                              wl.k, wl.h_q, wl.h_kv, n_cu=256)
+        return p[P.H_N_ATTN_ITEMS], p[P.H_N_MERGE]
+
+    n2, m2 = items(W.long_context(k=2))      # 6 tiles x 8 kv heads over 32,896 keys
+    n16, m16 = items(W.long_context(k=16))   # 20 tiles x 8 kv heads
+    assert (n2, m2) == (1016, 48)      # half share: 1,016 items = 1.98 rounds of 512
+    assert (n16, m16) == (1600, 152)   # third share: 3.1 rounds (half share: 2.16)
+    assert items(W.epic_sweep(k=16))[0] == 4600  # 8192-key segments, tail cut
