@@ -8,7 +8,12 @@ while the GPU executes step i (pinned, double-buffered, asynchronous plan upload
 Prints ONE JSON line.
 
 Default workload: 4 independent requests of ~50k tokens each (chunks of 512-2048
-tokens, 256 query tokens), GQA 32/8, head_dim 128, bf16, k = 16.
+tokens, 256 query tokens), GQA 32/8, head_dim 128, bf16, k = 16.  The default run also
+measures the other configurations of the same path and adds them to the one line as
+"sub_records", each with its own roofline and a bounded cpu_baseline: the same batch
+shape at k = 2, 4, 8; one 32,896-token request (32 chunks of 1024 + 128 query tokens)
+at k = 2 and 16; and the shared-pool batch below.  Every contiguous record also times
+the rotation + splice launch right after a 512 MB write that evicts the Infinity Cache.
 
 --workload shared_pool: 256 chunks stored once in a paged pool of 16-token blocks,
 8 requests each splicing 96-128 of them (~116k tokens) + 128 query tokens, seam
@@ -63,8 +68,12 @@ def parse():
     ap.add_argument("--heads", type=int, default=32,
                     help="linear-attention heads for --state-compose")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub-records", action="store_true",
+                    help="default workload only: skip the sub-records of the other "
+                         "configurations (k sweep, 32k-token request, shared pool)")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
-                    help="recomputed rows of request 0 the oracle times (0 = all)")
+                    help="recomputed rows per request whose attention the oracle times "
+                         "(0 = all; the time is scaled to all rows by causal-pair count)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (5 launches) to calibrate "
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE against known bytes")
@@ -150,51 +159,76 @@ class PlanUploader:
         return plan
 
 
-def cpu_baseline(wl, k_in, v_in, q, kf, vf, plan, sample_rows, scheme="delta"):
-    """Time the CPU oracle (as it stands) on request 0 of the same inputs."""
-    import torch
+def _threads():
     from threadpoolctl import threadpool_info
+    return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+
+
+def _sample_rows(rows, n_att):
+    """The last n_att rows (the longest ones) when sampling, else all of them."""
+    return slice(len(rows) - n_att, len(rows)) if 0 < n_att < len(rows) else slice(0, len(rows))
+
+
+def cpu_baseline(wl, k_in, v_in, q, kf, vf, plan, requests, sample_rows, scheme="delta"):
+    """Time the CPU oracle (as it stands) on the given requests of the same inputs:
+    index, rotation (or Scheme B), splice and selective attention.  With sample_rows > 0
+    only the last sample_rows recomputed rows of each request attend, and the attention
+    time is scaled to all rows by causal-pair count (flops)."""
+    import torch
     from oracle import pic_oracle as O
-    r = wl.requests[0]
-    tok0 = int(plan.req_tok_ptr[0])
-    row0, row1 = int(plan.req_row_ptr[0]), int(plan.req_row_ptr[1])
-    offs = O.chunk_offsets(r.chunk_lens)
     f64 = lambda t: t.to(torch.float64).numpy()
-    kin = f64(k_in[tok0:tok0 + offs[-1]])
-    vin = f64(v_in[tok0:tok0 + offs[-1]])
-    ck = [kin[offs[c]:offs[c + 1]] for c in range(len(r.chunk_lens))]
-    cv = [vin[offs[c]:offs[c + 1]] for c in range(len(r.chunk_lens))]
-    t0 = time.perf_counter()
-    rows = O.recompute_positions(r.chunk_lens, r.q_len, wl.k)
-    k_ctx = O.rope_apply(ck, wl.rope_base) if scheme == "nope" else O.rope_delta(ck, wl.rope_base)
-    v_ctx = O.concat_chunks(cv)
-    kx, vx = O.splice(k_ctx, v_ctx, f64(kf[row0:row1]), f64(vf[row0:row1]), rows,
-                      offs[-1] + r.q_len)
-    n_att = len(rows) if sample_rows <= 0 else min(sample_rows, len(rows))
-    # the last n_att rows (the longest ones) when sampling
-    sel = slice(len(rows) - n_att, len(rows))
-    O.selective_attn(f64(q[row0:row1])[sel], kx, vx, rows[sel])
-    dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    n_tokens = offs[-1] + r.q_len
-    frac_rows = n_att / max(1, len(rows))
-    return {"value": n_tokens / dt if frac_rows == 1.0 else None, "unit": "tokens/s",
-            "cores": int(threads), "kind": "oracle", "seconds": round(dt, 3),
-            "sample": "request 0 of the batch (%d tokens, %d of %d recomputed rows), fp64 "
-                      "NumPy oracle: index, rotation, splice and selective attention"
-                      % (n_tokens, n_att, len(rows)),
+    t_meas = t_full = 0.0
+    n_tokens = n_rows = n_att_rows = 0
+    for b in requests:
+        r = wl.requests[b]
+        tok0 = int(plan.req_tok_ptr[b])
+        row0, row1 = int(plan.req_row_ptr[b]), int(plan.req_row_ptr[b + 1])
+        offs = O.chunk_offsets(r.chunk_lens)
+        kin = f64(k_in[tok0:tok0 + offs[-1]])
+        vin = f64(v_in[tok0:tok0 + offs[-1]])
+        ck = [kin[offs[c]:offs[c + 1]] for c in range(len(r.chunk_lens))]
+        cv = [vin[offs[c]:offs[c + 1]] for c in range(len(r.chunk_lens))]
+        qb, kfb, vfb = f64(q[row0:row1]), f64(kf[row0:row1]), f64(vf[row0:row1])
+        t0 = time.perf_counter()
+        rows = O.recompute_positions(r.chunk_lens, r.q_len, wl.k)
+        k_ctx = O.rope_apply(ck, wl.rope_base) if scheme == "nope" else O.rope_delta(ck, wl.rope_base)
+        v_ctx = O.concat_chunks(cv)
+        kx, vx = O.splice(k_ctx, v_ctx, kfb, vfb, rows, offs[-1] + r.q_len)
+        t1 = time.perf_counter()
+        sel = _sample_rows(rows, sample_rows)
+        O.selective_attn(qb[sel], kx, vx, rows[sel])
+        t2 = time.perf_counter()
+        pairs = float(sum(p + 1 for p in rows))
+        pairs_s = float(sum(p + 1 for p in rows[sel]))
+        t_meas += t2 - t0
+        t_full += (t1 - t0) + (t2 - t1) * (pairs / pairs_s if pairs_s else 1.0)
+        n_tokens += offs[-1] + r.q_len
+        n_rows += len(rows)
+        n_att_rows += len(rows[sel])
+    scaled = n_att_rows < n_rows
+    return {"value": round(n_tokens / t_full, 1), "unit": "tokens/s", "cores": _threads(),
+            "kind": "oracle", "seconds": round(t_meas, 3),
+            "seconds_all_rows": round(t_full, 3),
+            "sample": "%d of %d requests of the batch (%d tokens, %d recomputed rows%s), fp64 "
+                      "NumPy oracle: index, %s, splice and selective attention"
+                      % (len(requests), len(wl.requests), n_tokens, n_rows,
+                         "; the last %d rows of each request attend and the attention time is "
+                         "scaled to all %d rows by causal-pair count" % (sample_rows, n_rows)
+                         if scaled else "", "RoPE at the target positions" if scheme == "nope"
+                         else "rotation"),
             "host_cpus": os.cpu_count()}
 
 
 def cpu_baseline_paged(wl, pk, pv, cbp, blocks, q, kf, vf, plan, sample_rows):
     """Time the CPU oracle (as it stands) on request 0 of the paged batch: gather of the
-    request's chunks from the pool, rotation, splice and selective attention."""
+    request's chunks from the pool, rotation, splice and selective attention (the last
+    sample_rows rows, the attention time scaled to all rows by causal-pair count)."""
     import torch
-    from threadpoolctl import threadpool_info
     from oracle import pic_oracle as O
     r = wl.requests[0]
     row0, row1 = int(plan.req_row_ptr[0]), int(plan.req_row_ptr[1])
     f64 = lambda t: t.to(torch.float64).numpy()
+    qb, kfb, vfb = f64(q[row0:row1]), f64(kf[row0:row1]), f64(vf[row0:row1])
     # the request's pool blocks only (the rest of the pool is not part of its work)
     t0 = time.perf_counter()
     ck, cv = [], []
@@ -207,24 +241,35 @@ def cpu_baseline_paged(wl, pk, pv, cbp, blocks, q, kf, vf, plan, sample_rows):
     offs = O.chunk_offsets(r.chunk_lens)
     k_ctx = O.rope_delta(ck, wl.rope_base)
     v_ctx = O.concat_chunks(cv)
-    kx, vx = O.splice(k_ctx, v_ctx, f64(kf[row0:row1]), f64(vf[row0:row1]), rows,
-                      offs[-1] + r.q_len)
-    n_att = len(rows) if sample_rows <= 0 else min(sample_rows, len(rows))
-    sel = slice(len(rows) - n_att, len(rows))
-    O.selective_attn(f64(q[row0:row1])[sel], kx, vx, rows[sel])
-    dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    kx, vx = O.splice(k_ctx, v_ctx, kfb, vfb, rows, offs[-1] + r.q_len)
+    t1 = time.perf_counter()
+    sel = _sample_rows(rows, sample_rows)
+    O.selective_attn(qb[sel], kx, vx, rows[sel])
+    t2 = time.perf_counter()
+    pairs, pairs_s = float(sum(p + 1 for p in rows)), float(sum(p + 1 for p in rows[sel]))
+    t_full = (t1 - t0) + (t2 - t1) * (pairs / pairs_s if pairs_s else 1.0)
     n_tokens = offs[-1] + r.q_len
-    return {"value": n_tokens / dt if n_att == len(rows) else None, "unit": "tokens/s",
-            "cores": int(threads), "kind": "oracle", "seconds": round(dt, 3),
-            "sample": "request 0 of the batch (%d tokens in %d pooled chunks, %d of %d "
-                      "recomputed rows), fp64 NumPy oracle: pool gather, index, rotation, "
-                      "splice and selective attention"
-                      % (n_tokens, len(r.chunk_ids), n_att, len(rows)),
+    n_att = len(rows[sel])
+    return {"value": round(n_tokens / t_full, 1), "unit": "tokens/s", "cores": _threads(),
+            "kind": "oracle", "seconds": round(t2 - t0, 3),
+            "seconds_all_rows": round(t_full, 3),
+            "sample": "request 0 of the batch (%d tokens in %d pooled chunks, %d recomputed "
+                      "rows%s), fp64 NumPy oracle: pool gather, index, rotation, splice and "
+                      "selective attention"
+                      % (n_tokens, len(r.chunk_ids), len(rows),
+                         "; the last %d rows attend and the attention time is scaled to all "
+                         "rows by causal-pair count" % n_att if n_att < len(rows) else ""),
             "host_cpus": os.cpu_count()}
 
 
 def bench_paged(args, wl):
+    print(json.dumps(run_paged(wl, steps, warmup,
+                               None if args.no_cpu_baseline else args.cpu_sample_rows)), flush=True)
+
+
+def run_paged(wl, steps, warmup, cpu_sample_rows):
+    """One step = planner (with chunk ids) + plan upload + pic_selective_attn_paged over
+    the shared-pool batch; returns the record (cpu_sample_rows None: no cpu_baseline)."""
     import torch
     import position_independent_kv_rope_amd as P
     from position_independent_kv_rope_amd import workloads as W
@@ -251,7 +296,7 @@ def bench_paged(args, wl):
     attn_flops = 4.0 * D * hq * float(np.sum(rows + 1))
     # every request reads its chunks' K/V once, plus Q and O of the recomputed rows
     attn_bytes = 2.0 * s * hkv * D * plan.n_tokens + 2.0 * s * hq * D * plan.n_rows
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     plan_s = []
 
     def step(i=None):
@@ -265,15 +310,15 @@ def bench_paged(args, wl):
                                    workspace=ws)
         if e: e[1].record()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = 1e3 * wall / args.steps
+    ms_step = 1e3 * wall / steps
     l_attn = [e[0].elapsed_time(e[1]) for e in ev]
     t_attn = float(np.mean(l_attn))
     tokens = plan.n_tokens
@@ -284,8 +329,8 @@ def bench_paged(args, wl):
         "value": round(tokens / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -312,9 +357,11 @@ def bench_paged(args, wl):
             "gpu_idle_ms": round(ms_step - t_attn, 4),
         },
     }
-    rec["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_paged(
-        wl, pk_h, pv_h, cbp, blocks, q_h, kf_h, vf_h, plan, args.cpu_sample_rows)
-    print(json.dumps(rec), flush=True)
+    del pk, pv, q, kf, vf, out, ws
+    torch.cuda.empty_cache()
+    rec["cpu_baseline"] = None if cpu_sample_rows is None else cpu_baseline_paged(
+        wl, pk_h, pv_h, cbp, blocks, q_h, kf_h, vf_h, plan, cpu_sample_rows)
+    return rec
 
 
 def bench_decode(args, wl):
@@ -705,32 +752,21 @@ def bench_state(args, wl):
     print(json.dumps(rec), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+SUB_RECORDS = [("epic_sweep", 2), ("epic_sweep", 4), ("epic_sweep", 8),
+               ("long_context", 2), ("long_context", 16), ("shared_pool", 8)]
+MALL_EVICT_BYTES = 512 << 20  # twice the 256 MB Infinity Cache
+
+
+def run_contiguous(wl, workload, steps, warmup, rope_scheme="delta", cpu_requests=None,
+                   cpu_sample_rows=0, evict_passes=10):
+    """One step = host planner + plan upload + pic_rope_splice + pic_selective_attn over one
+    batch of a contiguous workload.  Returns the record (cpu_requests None: no
+    cpu_baseline).  After the timed steps: the two calls the fused launch stands for,
+    timed separately, and evict_passes rotation + splice launches each timed right after
+    a 512 MB write that evicts the Infinity Cache (MALL)."""
     import torch
     import position_independent_kv_rope_amd as P
     from position_independent_kv_rope_amd import workloads as W
-
-    if args.copy_calibration:
-        return copy_calibration()
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    P.lib()
-    wl = make_workload(args.workload, args.k)
-    if wl.pool_lens is not None:
-        if args.state_compose:
-            return bench_state(args, wl)
-        return bench_decode(args, wl) if args.decode else bench_paged(args, wl)
-    if args.decode:
-        print("--decode needs --workload shared_pool", file=sys.stderr)
-        sys.exit(2)
-    if args.link_layers > 0:
-        return bench_link(args, wl)
     reqs = [r.chunk_lens for r in wl.requests]
     qs = [r.q_len for r in wl.requests]
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
@@ -751,15 +787,15 @@ def main():
     attn_flops = 4.0 * D * hq * float(np.sum(rows + 1))
     tiles = plan.rope_tiles if plan[P.H_N_ROPE_TILES] else np.zeros((0, 4), dtype=np.int64)
     # rows the rotation touches: tiles with delta != 0 (by delta), every kept row (nope)
-    rotated = tiles if args.rope_scheme == "nope" else tiles[tiles[:, 2] != 0]
+    rotated = tiles if rope_scheme == "nope" else tiles[tiles[:, 2] != 0]
     rope_rows = int(rotated[:, 1].sum())
     rope_bytes = 2.0 * s * hkv * D * rope_rows
     splice_bytes = 4.0 * s * hkv * D * plan.n_rows
     attn_bytes = 2.0 * s * hkv * D * plan.n_tokens + 2.0 * s * hq * D * plan.n_rows
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     plan_s = []
-    mode = P.PIC_ROPE_AT_POSITION if args.rope_scheme == "nope" else P.PIC_ROPE_BY_DELTA
+    mode = P.PIC_ROPE_AT_POSITION if rope_scheme == "nope" else P.PIC_ROPE_BY_DELTA
 
     def step(i=None):
         t0 = time.perf_counter()
@@ -773,15 +809,15 @@ def main():
         P.pic_selective_attn(p, q, k, v, out, workspace=ws)
         if e: e[2].record()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = 1e3 * wall / args.steps
+    ms_step = 1e3 * wall / steps
 
     l_rs = [e[0].elapsed_time(e[1]) for e in ev]
     l_attn = [e[1].elapsed_time(e[2]) for e in ev]
@@ -790,11 +826,11 @@ def main():
     # breakdown after the timed steps: the two calls pic_rope_splice stands for, timed
     # separately on the same buffers (each pass rotates K again: the bytes are the same),
     # each pair followed by the attention call as in a step
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     dplan = uploader.upload(P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, n_cu=n_cu))
     for e in sev:
         e[0].record()
-        if args.rope_scheme == "nope":
+        if rope_scheme == "nope":
             P.pic_rope_apply(dplan, k, wl.rope_base)
         else:
             P.pic_rope_delta(dplan, k, wl.rope_base)
@@ -807,27 +843,46 @@ def main():
     l_splice = [e[1].elapsed_time(e[2]) for e in sev]
     t_rope, t_splice = float(np.mean(l_rope)), float(np.mean(l_splice))
     rs_bytes = rope_bytes + splice_bytes
+    # the fused rotation + splice from HBM: a 512 MB write evicts the Infinity Cache
+    # before each timed launch (K and V of the smaller batches would otherwise be served
+    # from it)
+    l_ev = []
+    if evict_passes > 0:
+        scratch = torch.empty(MALL_EVICT_BYTES // 4, dtype=torch.int32, device=dev)
+        xev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(evict_passes)]
+        for i, e in enumerate(xev):
+            scratch.fill_(i)
+            e[0].record()
+            P.pic_rope_splice(dplan, k, v, kf, vf, wl.rope_base, mode=mode)
+            e[1].record()
+        torch.cuda.synchronize()
+        l_ev = [e[0].elapsed_time(e[1]) for e in xev]
+        del scratch
     tokens = plan.n_tokens
     value = tokens / (ms_step * 1e-3)
     attn_tflops = attn_flops / (t_attn * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[wl.dtype]
-    traffic = load_traffic("attn", args.workload + "_k%d" % wl.k)
+    traffic = load_traffic("attn", workload + "_k%d" % wl.k)
+    gbs = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e9, 1)
+    frac = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    fused = "pic_rope_splice (%s + splice, one launch)" % (
+        "rope_apply" if rope_scheme == "nope" else "rope_delta")
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": args.workload, "requests": len(wl.requests), "tokens": tokens,
+        "config": {"workload": workload, "requests": len(wl.requests), "tokens": tokens,
                    "recomputed_rows": plan.n_rows, "k": wl.k, "h_q": hq, "h_kv": hkv,
-                   "head_dim": D, "rope_base": wl.rope_base, "rope_scheme": args.rope_scheme,
+                   "head_dim": D, "rope_base": wl.rope_base, "rope_scheme": rope_scheme,
                    "parallelism": "none (1 GPU)"},
         "attn_tflops": round(attn_tflops, 2),
         "splice_pass_tokens_per_s": round(tokens / (t_rs * 1e-3), 1),
@@ -838,18 +893,14 @@ def main():
                      "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes},
         "kernels": {
             "rope_splice": {"ms": round(t_rs, 4), **pct(l_rs), "bytes": rs_bytes,
-                            "GB_s": round(rs_bytes / (t_rs * 1e-3) / 1e9, 1),
-                            "hbm_frac": round(rs_bytes / (t_rs * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                            "call": "pic_rope_splice (%s + splice, one launch)"
-                                    % ("rope_apply" if args.rope_scheme == "nope" else "rope_delta")},
-            ("rope_apply" if args.rope_scheme == "nope" else "rope_delta"): {
+                            "GB_s": gbs(rs_bytes, t_rs), "hbm_frac": frac(rs_bytes, t_rs),
+                            "call": fused + ", inside the steps"},
+            ("rope_apply" if rope_scheme == "nope" else "rope_delta"): {
                 "ms": round(t_rope, 4), **pct(l_rope), "bytes": rope_bytes,
-                           "GB_s": round(rope_bytes / (t_rope * 1e-3) / 1e9, 1),
-                           "hbm_frac": round(rope_bytes / (t_rope * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                           "call": "separate call, timed after the steps"},
+                "GB_s": gbs(rope_bytes, t_rope), "hbm_frac": frac(rope_bytes, t_rope),
+                "call": "separate call, timed after the steps"},
             "splice": {"ms": round(t_splice, 4), **pct(l_splice), "bytes": splice_bytes,
-                       "GB_s": round(splice_bytes / (t_splice * 1e-3) / 1e9, 1),
-                       "hbm_frac": round(splice_bytes / (t_splice * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "GB_s": gbs(splice_bytes, t_splice), "hbm_frac": frac(splice_bytes, t_splice),
                        "call": "separate call, timed after the steps"},
             "selective_attn": {"ms": round(t_attn, 4), **pct(l_attn), "flops": attn_flops,
                                "TFLOP_s": round(attn_tflops, 2),
@@ -858,11 +909,74 @@ def main():
             "gpu_idle_ms": round(ms_step - t_rs - t_attn, 4),
         },
     }
+    if l_ev:
+        t_ev = float(np.mean(l_ev))
+        rec["kernels"]["rope_splice_mall_evicted"] = {
+            "ms": round(t_ev, 4), **pct(l_ev), "bytes": rs_bytes, "GB_s": gbs(rs_bytes, t_ev),
+            "hbm_frac": frac(rs_bytes, t_ev),
+            "call": fused + ", each launch right after a 512 MB write (Infinity Cache evicted)"}
+    del k, v, q, kf, vf, out, ws
+    torch.cuda.empty_cache()
+    rec["cpu_baseline"] = None if cpu_requests is None else cpu_baseline(
+        wl, k_in, v_in, q_h, kf_h, vf_h, plan, cpu_requests, cpu_sample_rows, rope_scheme)
+    return rec
+
+
+def sub_record(rec):
+    """The per-configuration fields of a record (what a sub-record keeps)."""
+    keep = ("value", "unit", "ms_per_step", "steps", "warmup", "config", "attn_tflops",
+            "splice_pass_tokens_per_s", "roofline", "kernels", "cpu_baseline")
+    return {k: rec[k] for k in keep if k in rec}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import position_independent_kv_rope_amd as P
+
+    if args.copy_calibration:
+        return copy_calibration()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    P.lib()
+    wl = make_workload(args.workload, args.k)
+    if wl.pool_lens is not None:
+        if args.state_compose:
+            return bench_state(args, wl)
+        return bench_decode(args, wl) if args.decode else bench_paged(args, wl)
+    if args.decode:
+        print("--decode needs --workload shared_pool", file=sys.stderr)
+        sys.exit(2)
+    if args.link_layers > 0:
+        return bench_link(args, wl)
+    cpu = None
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, k_in, v_in, q_h, kf_h, vf_h, plan,
-                                           args.cpu_sample_rows, args.rope_scheme)
-    else:
-        rec["cpu_baseline"] = None
+        cpu = list(range(len(wl.requests)))
+    rec = run_contiguous(wl, args.workload, args.steps, args.warmup, args.rope_scheme, cpu,
+                         args.cpu_sample_rows)
+    headline = (args.workload == "epic_sweep" and args.k is None and args.rope_scheme == "delta"
+                and not args.no_sub_records)
+    if headline:
+        # the other configurations of the same path, each with its own roofline and a
+        # bounded cpu_baseline sample, as sub-records of the one line
+        sub_steps, sub_warm = max(3, min(args.steps, 10)), max(1, min(args.warmup, 3))
+        subs = {}
+        for name, k in SUB_RECORDS:
+            w = make_workload(name, k)
+            print("[bench] sub-record %s k=%d" % (name, k), file=sys.stderr, flush=True)
+            if w.pool_lens is not None:
+                r = run_paged(w, sub_steps, sub_warm, None if args.no_cpu_baseline else 96)
+            else:
+                r = run_contiguous(w, name, sub_steps, sub_warm, "delta",
+                                   None if args.no_cpu_baseline else [0],
+                                   0 if name == "long_context" else 128)
+            subs["%s_k%d" % (name, k)] = sub_record(r)
+        rec["sub_records"] = subs
     print(json.dumps(rec), flush=True)
 
 

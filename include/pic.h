@@ -263,7 +263,8 @@ size_t pic_attn_workspace_bytes(const int32_t *plan_host, int32_t head_dim);
  *   O[r, h] = sum_{j <= p} softmax_j(Q[r, h] . K[tok_b + j, g] * scale) V[tok_b + j, g]
  * over the spliced K/V of request b only.  q: device [n_rows, h_q, head_dim] (already
  * rotated at p); k, v: spliced device buffers; out: device [n_rows, h_q, head_dim]
- * of dtype.  scale > 0 (normally 1/sqrt(head_dim)).  bf16 runs bf16 MFMA with fp32
+ * of dtype.  scale: the softmax scale; a value <= 0 selects 1/sqrt(head_dim) (NaN or
+ * infinity is PIC_EINVAL).  bf16 runs bf16 MFMA with fp32
  * accumulation and an fp32 online softmax; f32 runs fp32 MFMA.  head_dim in {64, 128}
  * for bf16, {16, 32, 64, 128} for f32.  workspace: device, >= pic_attn_workspace_bytes
  * (may be NULL when that is 0); contents on entry are ignored.  A paged plan (built with
@@ -285,9 +286,12 @@ int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_dev, const 
  * pool chunk i occupies the blocks block_ids[chunk_block_ptr[i] .. chunk_block_ptr[i+1]-1]
  * in order (the last one partially); chunk_block_ptr is device [n_pool_chunks + 1] and
  * block_ids device int32.  The plan must come from pic_build_index with chunk_ids, all
- * of them < n_pool_chunks (checked on the host).  Not checkable on the host and left to
- * the caller: each listed chunk has at least ceil(L_c / 16) blocks, and block ids are
- * < pool_blocks (a larger id reads zeros: the pool loads are range-checked).
+ * of them < n_pool_chunks (checked on the host).  chunk_block_ptr must be a CSR over
+ * block_ids (non-decreasing, its last entry at most the length of block_ids).  Not
+ * checkable on the host and left to the caller: each listed chunk has at least
+ * ceil(L_c / 16) blocks (blocks its table row does not list read as zeros, never the
+ * next row's ids), and block ids are < pool_blocks (a larger or negative id reads
+ * zeros: the pool loads are range-checked).
  * k_fresh/v_fresh [n_rows][h_kv][head_dim] hold the recomputed rows (RoPE'd at their
  * global positions) and are read in place; q/out as in pic_selective_attn.  bf16: cached
  * keys of chunk c are scored in their local frame against the query rotated by -delta_c
@@ -298,7 +302,8 @@ int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_dev, const 
  * a chunk's length may hold anything (NaN included).  workspace >= pic_attn_workspace_bytes(plan_host, head_dim):
  * partials, the angle table and one 32-byte record per key block (a small kernel fills
  * them from the block table before the attention kernel runs).  Errors: PIC_EINVAL (not
- * a paged plan, null pointers, a chunk id >= n_pool_chunks, bad scale/base/layout),
+ * a paged plan, null pointers, a chunk id >= n_pool_chunks, NaN/infinite scale (<= 0
+ * selects 1/sqrt(head_dim)), bad base/layout),
  * PIC_EUNSUPPORTED (dtype, head_dim, block_size != 16, sizes), PIC_ENOSPC (workspace),
  * PIC_EDEVICE.
  */
@@ -317,7 +322,8 @@ int pic_selective_attn_paged(const int32_t *plan_host, const int32_t *plan_dev, 
  * q_b query tokens) attends causally over all of the request's keys: its pool chunks
  * (as pic_selective_attn_paged sees them: rotated by delta_c, seam rows replaced by
  * the fresh rows), its recomputed rows (k_fresh/v_fresh, the link's fresh buffer) and
- * itself:  out[b, h] = sum_j softmax_j(q_new[b, h] . K_b[j, g] * scale) V_b[j, g].
+ * itself:  out[b, h] = sum_j softmax_j(q_new[b, h] . K_b[j, g] * scale) V_b[j, g]
+ * (scale <= 0 selects 1/sqrt(head_dim)).
  * Work is chunk-major: each pool chunk is read once per call for all request chunks
  * that use it (the plan's decode items), on a resident grid that walks the plan's
  * decode units.  q_new/out: device [n_req][h_q][head_dim];
@@ -381,7 +387,8 @@ int pic_out_proj(const int32_t *plan_host, const void *o, const void *w_o, void 
  * chunks at their local positions, which are rotated and spliced in place).  x: the
  * rows' hidden states entering layer 0, [n_rows][d_model], updated in place to the
  * last layer's output.  q/k_fresh/v_fresh/o: caller scratch of the per-layer shapes.
- * workspace >= pic_link_workspace_bytes.  Every argument check of the per-layer calls
+ * workspace >= pic_link_workspace_bytes; scale as pic_selective_attn (<= 0 selects
+ * 1/sqrt(head_dim)).  Every argument check of the per-layer calls
  * runs before the first launch; errors as those calls.  bf16 only.
  */
 size_t pic_link_workspace_bytes(const int32_t *plan_host, int32_t head_dim);

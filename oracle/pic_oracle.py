@@ -78,45 +78,25 @@ def chunk_offsets(chunk_lens):
 def recompute_positions(chunk_lens, q_len, k):
     """LegoLink-k recompute set, in ascending order.
 
-    [EPIC] link_legolink Step 1: skip chunk 0; for every later chunk append its
-    first min(k, L_c) global positions; then append every query position
-    ctx .. ctx + q - 1.  [HYPIC] 2.2 uses the same rule with k = w.
+    The rule ([EPIC] Step 1 and the worked 4+5+5+3 example; [HYPIC] 2.2 with k = w):
+    a position j of the spliced prompt is recomputed exactly when it is a query
+    position (j >= ctx), or when it lies in a chunk other than the first and is one of
+    that chunk's first k tokens (j - off_c < k).  Positions are visited one by one;
+    the chunk holding j is tracked as j advances (empty chunks hold no position).
     """
     offs = chunk_offsets(chunk_lens)
-    rows = []
-    for c, length in enumerate(chunk_lens):
-        if c == 0:
-            continue
-        for j in range(min(int(k), int(length))):
-            rows.append(offs[c] + j)
     ctx = offs[-1]
-    for j in range(int(q_len)):
-        rows.append(ctx + j)
-    return rows
-
-
-def recompute_set_by_membership(chunk_lens, q_len, k):
-    """Second, independent formulation of the recompute set (used as a pin).
-
-    Position j of the spliced prompt is recomputed iff it is a query position, or
-    it lies in a chunk other than the first and is among that chunk's first k tokens.
-    Scans positions one by one instead of chunks.
-    """
-    total_ctx = sum(int(x) for x in chunk_lens)
-    n_total = total_ctx + int(q_len)
+    k = int(k)
     out = []
-    for j in range(n_total):
-        if j >= total_ctx:
+    c = 0
+    for j in range(ctx + int(q_len)):
+        if j >= ctx:
             out.append(j)
             continue
-        # find the chunk holding j by walking from the start
-        start = 0
-        for c, length in enumerate(chunk_lens):
-            if start <= j < start + int(length):
-                if c >= 1 and j - start < int(k):
-                    out.append(j)
-                break
-            start += int(length)
+        while j >= offs[c + 1]:
+            c += 1
+        if c >= 1 and j - offs[c] < k:
+            out.append(j)
     return out
 
 

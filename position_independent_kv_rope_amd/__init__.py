@@ -287,6 +287,11 @@ def _dev(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _scale(scale):
+    """None -> 0.0, which the library reads as its default 1/sqrt(head_dim)."""
+    return 0.0 if scale is None else float(scale)
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -348,8 +353,6 @@ def pic_attn_workspace_bytes(plan, head_dim):
 def pic_selective_attn(plan, q, k, v, out, scale=None, workspace=None, stream=None):
     """out[r, h] = causal attention of q[r, h] over the spliced k/v of its request."""
     d = int(q.shape[2])
-    if scale is None:
-        scale = 1.0 / np.sqrt(d)
     if q.shape[0] != plan.n_rows or out.shape != q.shape or q.shape[1] != plan[H_H_Q]:
         raise ValueError("q/out shapes do not match the plan")
     if k.shape[0] != plan.n_tokens or v.shape != k.shape or k.shape[1] != plan[H_H_KV]:
@@ -362,7 +365,7 @@ def pic_selective_attn(plan, q, k, v, out, scale=None, workspace=None, stream=No
         ws, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     st = lib().pic_selective_attn(plan.host_ptr(), plan.dev_ptr(), _dev(q, "q"), _dev(k, "k"),
                                   _dev(v, "v"), _dev(out, "out"), _dtype_code(q), d,
-                                  float(scale), ws, ws_bytes, _stream(stream))
+                                  _scale(scale), ws, ws_bytes, _stream(stream))
     _check("pic_selective_attn", st)
 
 
@@ -381,8 +384,6 @@ def pic_selective_attn_paged(plan, q, pool_k, pool_v, chunk_block_ptr, block_ids
     """Selective attention over a shared paged pool [blocks, 16, h_kv, D] (read-only)."""
     import torch
     d = int(q.shape[2])
-    if scale is None:
-        scale = 1.0 / np.sqrt(d)
     if not plan.paged:
         raise ValueError("plan was not built with chunk ids (paged pool)")
     if q.shape[0] != plan.n_rows or out.shape != q.shape or q.shape[1] != plan[H_H_Q]:
@@ -406,7 +407,7 @@ def pic_selective_attn_paged(plan, q, pool_k, pool_v, chunk_block_ptr, block_ids
         _dev(chunk_block_ptr, "chunk_block_ptr"), int(chunk_block_ptr.numel()) - 1,
         _dev(block_ids, "block_ids"),
         _dev(k_fresh, "k_fresh"), _dev(v_fresh, "v_fresh"), _dev(out, "out"), _dtype_code(q), d,
-        int(layout), float(rope_base), float(scale), ws, ws_bytes, _stream(stream))
+        int(layout), float(rope_base), _scale(scale), ws, ws_bytes, _stream(stream))
     _check("pic_selective_attn_paged", st)
 
 
@@ -424,8 +425,6 @@ def pic_decode_attn_paged(plan, q_new, k_new, v_new, pool_k, pool_v, chunk_block
     attends over the request's pool chunks, recomputed rows and itself."""
     import torch
     d = int(q_new.shape[2])
-    if scale is None:
-        scale = 1.0 / np.sqrt(d)
     if not plan.paged:
         raise ValueError("plan was not built with chunk ids (paged pool)")
     n_req = plan[H_N_REQ]
@@ -451,7 +450,7 @@ def pic_decode_attn_paged(plan, q_new, k_new, v_new, pool_k, pool_v, chunk_block
         int(pool_k.shape[0]), int(pool_k.shape[1]), _dev(chunk_block_ptr, "chunk_block_ptr"),
         int(chunk_block_ptr.numel()) - 1, _dev(block_ids, "block_ids"), _dev(k_fresh, "k_fresh"),
         _dev(v_fresh, "v_fresh"), _dev(out, "out"), _dtype_code(q_new), d, int(layout),
-        float(rope_base), float(scale), _dev(workspace, "workspace"),
+        float(rope_base), _scale(scale), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check("pic_decode_attn_paged", st)
 
@@ -515,8 +514,6 @@ def pic_link(plan, x, w_qkv, w_o, k_cache, v_cache, q, k_fresh, v_fresh, o, rope
     if not (len(w_o) == len(k_cache) == len(v_cache) == n_layers):
         raise ValueError("one w_qkv, w_o, k_cache and v_cache per layer")
     d = int(q.shape[2])
-    if scale is None:
-        scale = 1.0 / np.sqrt(d)
     d_model = int(x.shape[1])
     hq, hkv = plan[H_H_Q], plan[H_H_KV]
     if x.shape[0] != plan.n_rows or q.shape != (plan.n_rows, hq, d) or o.shape != q.shape:
@@ -538,7 +535,7 @@ def pic_link(plan, x, w_qkv, w_o, k_cache, v_cache, q, k_fresh, v_fresh, o, rope
                         arr(w_qkv, "w_qkv"), arr(w_o, "w_o"), arr(k_cache, "k_cache"),
                         arr(v_cache, "v_cache"), _dev(q, "q"), _dev(k_fresh, "k_fresh"),
                         _dev(v_fresh, "v_fresh"), _dev(o, "o"), _dtype_code(x), d_model, d,
-                        int(layout), float(rope_base), float(scale),
+                        int(layout), float(rope_base), _scale(scale),
                         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                         _stream(stream))
     _check("pic_link", st)

@@ -452,8 +452,12 @@ __global__ __launch_bounds__(256) void paged_blocks_kernel(
   } else {
     const int32_t *sg = segs + 8 * d.x;
     const int off = sg[0], len = sg[1], seam = sg[2], cid = sg[3];
-    const int nb = (len + kPoolBlockRows - 1) / kPoolBlockRows;
-    const int32_t *bl = block_ids + chunk_block_ptr[cid];
+    // blocks the chunk needs, bounded by the blocks its table row lists: an undersized
+    // row reads zeros past its end instead of the next chunk's ids (or past the table)
+    const int tab0 = chunk_block_ptr[cid];
+    const int nb = min((len + kPoolBlockRows - 1) / kPoolBlockRows,
+                       max(0, chunk_block_ptr[cid + 1] - tab0));
+    const int32_t *bl = block_ids + tab0;
     r.base_pos = off + d.y;
     r.vis = max(0, min(kKB, seam - d.y)) | (min(kKB, len - d.y) << 8);
 #pragma unroll
@@ -889,6 +893,7 @@ constexpr int kDecStages = 2;  // K + V buffers per workgroup: 32 KiB of LDS at 
 struct DecSrc {
   const char *k, *v;      // pool tensors, or the request's first fresh row
   const int32_t *blocks;  // pool block ids of the chunk (pool pieces)
+  int n_tab;              // ids its block-table row lists (pool pieces)
   int t_begin, t_end;     // keys of the piece, relative to the chunk or to the fresh rows
   int n_blocks;           // kDecKB-key blocks
   int item, g, rec_off;
@@ -952,11 +957,13 @@ __device__ __forceinline__ void dec_attn_body(
       sr.k = reinterpret_cast<const char *>(pool_k);
       sr.v = reinterpret_cast<const char *>(pool_v);
       sr.blocks = block_ids + chunk_block_ptr[it.src];
+      sr.n_tab = max(0, chunk_block_ptr[it.src + 1] - chunk_block_ptr[it.src]);
     } else {
       const int64_t row0 = (int64_t)req_row_ptr[-1 - it.src] * tok_bytes;
       sr.k = reinterpret_cast<const char *>(k_fresh) + row0;
       sr.v = reinterpret_cast<const char *>(v_fresh) + row0;
       sr.blocks = nullptr;
+      sr.n_tab = 0;
     }
     return sr;
   };
@@ -985,7 +992,8 @@ __device__ __forceinline__ void dec_attn_body(
       int rows = min(max(sr.t_end - t, 0), kRPI);
       int64_t off = 0;
       if (sr.pool) {  // a block id outside the pool reads zeros
-        const int bid = rows > 0 ? sr.blocks[t / kPoolBlockRows] : -1;
+        // blocks past the chunk's table row read zeros (never the next row's ids)
+        const int bid = rows > 0 && t / kPoolBlockRows < sr.n_tab ? sr.blocks[t / kPoolBlockRows] : -1;
         if (bid < 0 || bid >= pool_blocks)
           rows = 0;
         else
@@ -1988,7 +1996,7 @@ extern "C" int pic_decode_attn_paged(
   if (!h.valid() || !h[PIC_H_PAGED]) return PIC_EINVAL;
   if (dtype != PIC_BF16 && dtype != PIC_F32) return PIC_EINVAL;
   if (rope_layout != PIC_ROPE_ADJACENT && rope_layout != PIC_ROPE_HALF) return PIC_EINVAL;
-  if (!(scale > 0.f) || !std::isfinite(scale) || head_dim <= 0 || pool_blocks < 0) return PIC_EINVAL;
+  if (!resolve_scale(scale, head_dim) || pool_blocks < 0) return PIC_EINVAL;
   if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return PIC_EINVAL;
   if (dtype != PIC_BF16 || block_size != kPoolBlockRows) return PIC_EUNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PIC_EUNSUPPORTED;
@@ -2036,7 +2044,7 @@ extern "C" int pic_selective_attn_paged(
   if (!h.valid() || !h[PIC_H_PAGED]) return PIC_EINVAL;
   if (dtype != PIC_BF16 && dtype != PIC_F32) return PIC_EINVAL;
   if (rope_layout != PIC_ROPE_ADJACENT && rope_layout != PIC_ROPE_HALF) return PIC_EINVAL;
-  if (!(scale > 0.f) || !std::isfinite(scale) || head_dim <= 0 || pool_blocks < 0) return PIC_EINVAL;
+  if (!resolve_scale(scale, head_dim) || pool_blocks < 0) return PIC_EINVAL;
   if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return PIC_EINVAL;
   if (block_size != kPoolBlockRows) return PIC_EUNSUPPORTED;
   if (dtype == PIC_BF16 && head_dim != 64 && head_dim != 128) return PIC_EUNSUPPORTED;
@@ -2096,7 +2104,7 @@ extern "C" int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_
   const PlanHeader h{plan_host};
   if (!h.valid() || h[PIC_H_PAGED]) return PIC_EINVAL;
   if (dtype != PIC_BF16 && dtype != PIC_F32) return PIC_EINVAL;
-  if (!(scale > 0.f) || !std::isfinite(scale) || head_dim <= 0) return PIC_EINVAL;
+  if (!resolve_scale(scale, head_dim)) return PIC_EINVAL;
   // K/V of one request are addressed with 32-bit byte offsets
   if ((int64_t)h[PIC_H_MAX_TOKENS] * h[PIC_H_H_KV] * head_dim * (int64_t)dtype_size(dtype) >
       0x7fff0000LL)

@@ -55,4 +55,13 @@ static_assert(PIC_H_RESERVED7 < PIC_PLAN_HEADER_WORDS, "header fields fit the he
 
 inline size_t dtype_size(int32_t dt) { return dt == PIC_BF16 ? 2 : (dt == PIC_F32 ? 4 : 0); }
 
+// Softmax scale of the attention calls: a value <= 0 selects the default 1/sqrt(head_dim)
+// (the scaled dot product of the EPIC Step 3 listing); NaN or infinity is an error.
+inline bool resolve_scale(float &scale, int32_t head_dim) {
+  if (scale != scale || scale == __builtin_inff() || scale == -__builtin_inff() || head_dim <= 0)
+    return false;
+  if (scale <= 0.f) scale = (float)(1.0 / __builtin_sqrt((double)head_dim));
+  return true;
+}
+
 }  // namespace pic

@@ -414,7 +414,7 @@ extern "C" int pic_link(const int32_t *plan_host, const int32_t *plan_dev, int32
   if (!h.valid() || h[PIC_H_PAGED] || n_layers < 0) return PIC_EINVAL;
   if (rope_layout != PIC_ROPE_ADJACENT && rope_layout != PIC_ROPE_HALF) return PIC_EINVAL;
   if (!(rope_base > 0.0) || !std::isfinite(rope_base)) return PIC_EINVAL;
-  if (!(scale > 0.f) || !std::isfinite(scale)) return PIC_EINVAL;
+  if (!resolve_scale(scale, head_dim)) return PIC_EINVAL;
   int st = check_gemm(h, dtype, d_model, head_dim);
   if (st != PIC_OK) return st;
   if (d_model % kGT || (h[PIC_H_H_Q] * head_dim) % kGT || (h[PIC_H_H_KV] * head_dim) % kGT ||

@@ -41,9 +41,10 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // remaining items fill its positions, longest first.  With tail_keys > 0, the items a
 // die starts during its last round (its final slots_per_die * round_keys of work) have
 // their first key range cut into pieces of at most tail_keys (multiples of align; a
-// second range, the fresh blocks of a paged item, stays with the first piece), kept on
-// that die, so the launch does not end waiting for a few long items.  Lengths are in
-// keys for contiguous plans and in key blocks for paged ones.
+// second range -- the fresh blocks a paged plan attaches to the first pool range of a
+// tile -- stays with the first piece), kept on that die, so the launch does not end
+// waiting for a few long items.  Lengths are in keys for contiguous plans and in key
+// blocks for paged ones.
 std::vector<pic::AttnItem> xcd_order(std::vector<pic::AttnItem> items,
                                      const std::vector<pic::AttnTile> &tiles, int n_xcd,
                                      int64_t tail_keys = 0, int64_t slots_per_die = 0,
@@ -222,7 +223,9 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   req_tok_ptr[n_req] = (int32_t)tok;
   req_row_ptr[n_req] = (int32_t)nrows;
 
-  // ---- recompute index: ascending positions per request ----
+  // ---- recompute index: ascending positions per request.  Position j is recomputed
+  // when it is a query position (j >= ctx) or lies in a chunk c >= 1 with
+  // j - off_c < k; per chunk those are the positions off_c .. off_c + min(k, L_c) - 1 ----
   std::vector<int32_t> rows(nrows), row_tok(nrows);
   {
     int64_t r = 0;
@@ -351,7 +354,7 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
   int64_t n_partials = 0;
   if (paged) {
     // Item ranges follow a per-request grid of seg_len keys over the pool blocks; the
-    // first range also carries the fresh blocks (second block range of the item).
+    // item of the first range also carries the fresh blocks (its second block range).
     const int64_t per_range = std::max<int64_t>(1, seg_len / kKeyAlign);
     for (int32_t ti = 0; ti < (int32_t)tiles.size(); ++ti) {
       const AttnTile &t = tiles[ti];
@@ -371,11 +374,14 @@ extern "C" int pic_build_index(int32_t n_req, const int32_t *req_chunk_ptr,
           it.kv_head = g;
           const int64_t p0 = kb_pool[b] + r * per_range;
           const int64_t p1 = kb_pool[b] + std::min(n_pool, (r + 1) * per_range);
+          // the pool range is the first range of every item (the one the last-round
+          // cut shortens); the request's fresh blocks ride as the second range of the
+          // first item
           if (r == 0) {
-            it.key_begin = (int32_t)kb_fresh[b];
-            it.key_end = (int32_t)(kb_fresh[b] + n_fresh);
-            it.pad0 = (int32_t)p0;
-            it.pad1 = (int32_t)std::max(p0, p1);
+            it.key_begin = (int32_t)p0;
+            it.key_end = (int32_t)std::max(p0, p1);
+            it.pad0 = (int32_t)kb_fresh[b];
+            it.pad1 = (int32_t)(kb_fresh[b] + n_fresh);
           } else {
             it.key_begin = (int32_t)p0;
             it.key_end = (int32_t)p1;

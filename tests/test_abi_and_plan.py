@@ -135,7 +135,10 @@ def test_device_entry_points_reject_bad_arguments_without_launching():
     assert rs(hp, fake, fake, fake, fake, None, P.PIC_F32, 16, 0, 1e4, 1, None) == P.PIC_EINVAL
     assert rs(hp, fake, *f4, P.PIC_F32, 12, 0, 1e4, 0, None) == P.PIC_EUNSUPPORTED
     args = (fake, fake, fake, fake)
-    assert L.pic_selective_attn(hp, fake, *args, P.PIC_F32, 16, 0.0, None, 0, None) == P.PIC_EINVAL
+    # scale: NaN or infinity is refused (a value <= 0 selects 1/sqrt(head_dim); the GPU
+    # tests pass None, i.e. 0, and compare with the oracle at 1/sqrt(D))
+    for bad in (float("nan"), float("inf"), float("-inf")):
+        assert L.pic_selective_attn(hp, fake, *args, P.PIC_F32, 16, bad, None, 0, None) == P.PIC_EINVAL
     assert L.pic_selective_attn(hp, fake, *args, P.PIC_F32, 24, 0.25, None, 0, None) == P.PIC_EUNSUPPORTED
     assert L.pic_selective_attn(hp, fake, *args, P.PIC_BF16, 16, 0.25, None, 0, None) == P.PIC_EUNSUPPORTED
     assert L.pic_selective_attn(hp, None, *args, P.PIC_F32, 16, 0.25, None, 0, None) == P.PIC_EINVAL
@@ -257,7 +260,7 @@ def test_link_entry_points_reject_bad_arguments_without_launching():
     assert link(bad, lws) == P.PIC_EINVAL
     assert link(arr, lws - 1) == P.PIC_ENOSPC
     assert link(arr, lws, dt=P.PIC_F32) == P.PIC_EUNSUPPORTED
-    assert link(arr, lws, sc=0.0) == P.PIC_EINVAL
+    assert link(arr, lws, sc=float("nan")) == P.PIC_EINVAL
     paged = P.pic_build_index([[40, 50]], [7], 2, 8, 2, chunk_ids_per_req=[[0, 1]])
     assert L.pic_link(paged.host_ptr(), f, 2, f, arr, arr, arr, arr, f, f, f, f, P.PIC_BF16, 256,
                       128, 0, 1e4, 0.088, f, lws, None) == P.PIC_EINVAL
@@ -498,6 +501,41 @@ def check_paged_plan(reqs, ids, q_lens, k, h_q, h_kv, pos_base=0, n_cu=0):
             got.append(r)
     assert sorted(got) == list(range(rp[-1]))
     return plan
+
+
+def check_paged_tail_cut(reqs, ids, q_lens, k, h_q, h_kv, n_cu=256, tail_blocks=64):
+    """Paged plans: every item's first range is pool blocks and its second range (only
+    on a tile's first item) the request's fresh blocks; the final round of each die --
+    its last 2 * n_cu / 8 items, workgroup i running on die i % 8 -- holds pieces of at
+    most tail_blocks pool blocks (4,096 keys): the last-round cut acts on the pool range,
+    and the fresh blocks stay with one piece."""
+    plan = P.pic_build_index(reqs, q_lens, k, h_q, h_kv, n_cu=n_cu, chunk_ids_per_req=ids)
+    items = plan.attn_items.tolist()
+    kb = plan.kblocks.tolist()
+    slots_per_die = 2 * n_cu // 8
+    for _, _, b1, e1, _, b2, e2, _ in items:
+        assert all(kb[i][0] >= 0 for i in range(b1, e1))   # first range: pool blocks
+        assert all(kb[i][0] == -1 for i in range(b2, e2))  # second range: fresh blocks
+    for d in range(8):
+        for _, _, b1, e1, _, _, _, _ in items[d::8][-slots_per_die:]:
+            assert e1 - b1 <= tail_blocks, (d, b1, e1)
+    return plan
+
+
+def test_paged_plan_tail_cut_acts_on_pool_blocks():
+    # the shared-pool shape: 8 requests x 96-128 chunks of 512-1536 tokens
+    rng = np.random.default_rng(11)
+    pool = [int(x) for x in rng.integers(512, 1537, size=256)]
+    ids = [[int(x) for x in rng.permutation(256)[:int(rng.integers(96, 129))]] for _ in range(8)]
+    check_paged_tail_cut([[pool[i] for i in r] for r in ids], ids, [128] * 8, 8, 32, 4)
+    # 64 requests of 8 x 1024 tokens: one 8,192-key range per tile, so every item is a
+    # tile's first item (pool range plus fresh blocks) and the cut must shorten those
+    ids = [[int(x) for x in rng.permutation(96)[:8]] for _ in range(64)]
+    plan = check_paged_tail_cut([[1024] * 8 for _ in ids], ids, [128] * 64, 8, 32, 4)
+    items = plan.attn_items.tolist()
+    with_fresh = [(t, g) for t, g, _, _, _, b2, e2, _ in items if e2 > b2]
+    assert sorted(with_fresh) == sorted(set((t, g) for t, g, *_ in items))  # one per tile+head
+    assert max(e1 - b1 for _, _, b1, e1, *_ in items) == 128  # uncut items before the tail
 
 
 def test_paged_plan_small():

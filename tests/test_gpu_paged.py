@@ -358,3 +358,11 @@ def test_paged_f32(layout, d):
                              chunk_ids_per_req=[r.chunk_ids for r in long.requests])
     assert plan[P.H_N_MERGE] > 0
     run_paged(long, layout, n_cu=256)
+
+
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_paged_f32_rotation_at_delta_near_two_to_the_20(layout):
+    # pool chunks cached at local positions from -(2^20 - 5): each staged key is rotated
+    # by off_c + 2^20 - 5 (about 1.05e6) on load; every row against the oracle at 1e-5
+    wl = small_pool(4, h_q=8, h_kv=2, d=128, seed=29, dtype="f32")
+    run_paged(wl, layout, pos_base=-(1 << 20) + 5, n_cu=256)

@@ -466,3 +466,73 @@ def test_random_configurations_one_launch(i):
     say("random case (one launch)", i, wl.dtype, "h_q=%d h_kv=%d D=%d k=%d" % (wl.h_q, wl.h_kv, wl.head_dim, wl.k),
         layout, scheme, "pos_base=%d" % pos_base)
     check_run(Run(wl, layout, n_cu=(2 if i % 3 else 0), pos_base=pos_base, scheme=scheme, fused=True))
+
+
+# ---------------------------------------------------------------------------
+# The fp32 angle at the offsets of long contexts (delta ~ 1e5 .. 5e5)
+# ---------------------------------------------------------------------------
+#
+# The rotation's angle is delta * theta_i.  A plain fp32 product errs by ~1e-3 rad at
+# delta ~ 1e5, far below what the bf16 bound of 2e-2 can see, so these cases check the
+# rotation where the error would show: fp32 I/O at 1e-5, and bf16 output within one
+# unit in the last place of the oracle's value rounded to bf16.  One KV head keeps the
+# half-million-token request small (256 MB of fp32 K).
+
+LONG_OFFSETS = [([100000, 700, 400000, 300], 16)]  # chunks at 0, 1e5, 100,700, 500,700
+
+
+@pytest.mark.parametrize("scheme", ["delta", "nope"])
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_fp32_rotation_at_long_offsets(layout, scheme):
+    wl = _custom("long_offsets_f32", "f32", 4, 1, 128, 5e5, 2, LONG_OFFSETS, seed=41)
+    worst = check_run(Run(wl, layout, n_cu=256, scheme=scheme), sample_rows=16)
+    say("fp32 long offsets", layout, scheme, "rope max-abs", worst["rope"])
+
+
+@pytest.mark.parametrize("scheme", ["delta", "nope"])
+def test_fp32_rotation_one_launch_at_long_offsets(scheme):
+    wl = _custom("long_offsets_f32", "f32", 4, 1, 128, 5e5, 2, LONG_OFFSETS, seed=43)
+    check_run(Run(wl, "adjacent", n_cu=256, scheme=scheme, fused=True), sample_rows=8)
+
+
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_fp32_rotation_at_delta_near_two_to_the_20(layout):
+    # cached rows at local positions from -(2^20 - 3): every chunk rotates by
+    # off_c + 2^20 - 3 (about 1.05e6)
+    wl = _custom("pos_base_2e20_f32", "f32", 8, 2, 128, 5e5, 3, [([300, 257, 410], 33)], seed=45)
+    check_run(Run(wl, layout, pos_base=-(1 << 20) + 3))
+
+
+def _bf16_ulp(y):
+    """Spacing of bf16 numbers at |y| (y already representable in bf16)."""
+    a = np.abs(y)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(np.maximum(e, -126.0) - 7.0), np.exp2(-133.0))
+
+
+@pytest.mark.parametrize("scheme", ["delta", "nope"])
+def test_bf16_rotation_within_one_ulp_at_long_offsets(scheme):
+    # The GPU rotates in fp32 and rounds once to bf16.  With an angle good to ~1e-6 rad
+    # its fp32 value lies within E = 4e-6 * |pair| of the exact one, so each rotated
+    # element is the oracle's value rounded to bf16 or one unit in the last place away,
+    # up to E where the result nearly cancels; and a flip to the neighbouring bf16 value
+    # happens only when the exact value lies within E of a rounding midpoint: for
+    # ~1e-4 of the elements.  A plain fp32 product delta * theta flips ~13% of them at
+    # these offsets, an angle error of 1e-3 rad ~30%.
+    wl = _custom("long_offsets_bf16", "bf16", 4, 1, 128, 5e5, 2, LONG_OFFSETS, seed=47)
+    run = Run(wl, "adjacent", n_cu=256, scheme=scheme)
+    r, tok0, _, _ = run.request_slices(0)
+    rows, k_ctx, _, _ = run.oracle_request(0)
+    ctx = sum(r.chunk_lens)
+    rec = set(rows)
+    keep = np.array([j for j in range(ctx) if j not in rec], dtype=np.int64)
+    exact = k_ctx[keep]
+    want = torch.from_numpy(exact).to(torch.bfloat16).to(torch.float64).numpy()
+    got = f64(run.k_rot[tok0:tok0 + ctx])[keep]
+    pair = np.sqrt(exact[..., 0::2] ** 2 + exact[..., 1::2] ** 2).repeat(2, axis=-1)
+    diff = np.abs(got - want)
+    flipped = float(np.mean(diff > 0))
+    say("bf16 long offsets", scheme, "max ulps", float(np.max(diff / _bf16_ulp(want))),
+        "elements off the rounded oracle value: %.4f%%" % (100.0 * flipped))
+    assert np.all(diff <= _bf16_ulp(want) + 4e-6 * pair)
+    assert flipped <= 1e-3

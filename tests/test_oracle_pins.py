@@ -38,7 +38,7 @@ def test_worked_example_index():
     assert len(rows) == g["n_recomputed"]
     assert O.chunk_offsets(g["chunk_lens"])[-1] == g["total_ctx_len"]
     assert g["total_ctx_len"] + g["q_len"] == g["n_total"]
-    assert O.recompute_set_by_membership(g["chunk_lens"], g["q_len"], g["k"]) == rows
+    assert _recompute_by_chunk_walk(g["chunk_lens"], g["q_len"], g["k"]) == rows
 
 
 def test_k_sweep_counts():
@@ -62,14 +62,26 @@ def test_method_table_count_formula():
         assert len(O.recompute_positions(lens, q, k)) == (n - 1) * k + q
 
 
-def test_membership_formulation_exhaustive():
+def _recompute_by_chunk_walk(chunk_lens, q_len, k):
+    """Second formulation of the recompute set, chunk by chunk (the oracle scans
+    positions): for each chunk after the first, its first min(k, L_c) positions, then
+    the query positions."""
+    out, off = [], 0
+    for c, length in enumerate(chunk_lens):
+        if c > 0:
+            out.extend(off + j for j in range(min(k, length)))
+        off += length
+    return out + list(range(off, off + q_len))
+
+
+def test_chunk_walk_formulation_exhaustive():
     import itertools
     for n in range(1, 4):
         for lens in itertools.product(range(0, 5), repeat=n):
             for q in range(0, 3):
                 for k in range(0, 6):
                     a = O.recompute_positions(list(lens), q, k)
-                    b = O.recompute_set_by_membership(list(lens), q, k)
+                    b = _recompute_by_chunk_walk(list(lens), q, k)
                     assert a == b, (lens, q, k)
                     assert a == sorted(set(a))
 
