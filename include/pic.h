@@ -278,6 +278,24 @@ int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_dev, const 
                        void *stream);
 
 /*
+ * pic_selective_attn_noalloc -- pic_selective_attn without a workspace argument.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same computation, arguments,
+ * result bits and errors as pic_selective_attn, with the split-KV partials kept in a
+ * scratch array of PIC_ATTN_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends.  The call allocates nothing.  A plan whose partials need
+ * more (pic_attn_workspace_bytes > PIC_ATTN_SCRATCH_BYTES) is refused with
+ * PIC_ENOSPC before anything runs; PIC_EDEVICE if the array's address cannot be
+ * obtained.  Calls on one GPU share the array: calls that may overlap on one GPU
+ * (several streams or threads) race and must be serialised by the caller.
+ */
+#define PIC_ATTN_SCRATCH_BYTES (128u << 20) /* 128 MiB per GPU */
+int pic_selective_attn_noalloc(const int32_t *plan_host, const int32_t *plan_dev, const void *q,
+                               const void *k, const void *v, void *out, int32_t dtype,
+                               int32_t head_dim, float scale, void *stream);
+
+/*
  * pic_selective_attn_paged -- selective attention over a shared paged chunk pool.
  *                                  [EPIC] Step 3; [RoPE-C] 3.3; [HYPIC] 2.2
  * Same result as pic_rope_delta + pic_splice + pic_selective_attn on the gathered

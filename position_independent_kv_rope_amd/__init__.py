@@ -36,7 +36,8 @@ PIC_DECODE_WG_PER_CU = 4
 EXPORTED = ("pic_build_index", "pic_rope_delta", "pic_rope_apply", "pic_splice",
             "pic_rope_splice",
             "pic_attn_workspace_bytes",
-            "pic_selective_attn", "pic_selective_attn_paged", "pic_decode_workspace_bytes",
+            "pic_selective_attn", "pic_selective_attn_noalloc", "pic_selective_attn_paged",
+            "pic_decode_workspace_bytes",
             "pic_decode_attn_paged", "pic_qkv_workspace_bytes", "pic_qkv_rope",
             "pic_out_proj", "pic_link_workspace_bytes", "pic_link", "pic_state_compose",
             "pic_strerror")
@@ -79,6 +80,8 @@ def lib():
     L.pic_attn_workspace_bytes.restype = sz
     L.pic_selective_attn.argtypes = [p, p, p, p, p, p, i32, i32, f32, p, sz, p]
     L.pic_selective_attn.restype = ctypes.c_int
+    L.pic_selective_attn_noalloc.argtypes = [p, p, p, p, p, p, i32, i32, f32, p]
+    L.pic_selective_attn_noalloc.restype = ctypes.c_int
     L.pic_selective_attn_paged.argtypes = [p, p, p, p, p, i64, i32, p, i32, p, p, p, p, i32, i32,
                                            i32, f64, f32, p, sz, p]
     L.pic_selective_attn_paged.restype = ctypes.c_int
@@ -367,6 +370,27 @@ def pic_selective_attn(plan, q, k, v, out, scale=None, workspace=None, stream=No
                                   _dev(v, "v"), _dev(out, "out"), _dtype_code(q), d,
                                   _scale(scale), ws, ws_bytes, _stream(stream))
     _check("pic_selective_attn", st)
+
+
+PIC_ATTN_SCRATCH_BYTES = 128 << 20
+
+
+def pic_selective_attn_noalloc(plan, q, k, v, out, scale=None, stream=None):
+    """pic_selective_attn with the split-KV partials in the library's per-GPU scratch
+    array (no workspace, no allocation); plans needing more than PIC_ATTN_SCRATCH_BYTES
+    raise PicError (PIC_ENOSPC)."""
+    d = int(q.shape[2])
+    if q.shape[0] != plan.n_rows or out.shape != q.shape or q.shape[1] != plan[H_H_Q]:
+        raise ValueError("q/out shapes do not match the plan")
+    if k.shape[0] != plan.n_tokens or v.shape != k.shape or k.shape[1] != plan[H_H_KV]:
+        raise ValueError("k/v shapes do not match the plan")
+    for t in (k, v, out):
+        if t.dtype != q.dtype:
+            raise ValueError("q, k, v and out must share one dtype")
+    st = lib().pic_selective_attn_noalloc(plan.host_ptr(), plan.dev_ptr(), _dev(q, "q"),
+                                          _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                                          _dtype_code(q), d, _scale(scale), _stream(stream))
+    _check("pic_selective_attn_noalloc", st)
 
 
 def attn_workspace(plan, head_dim, device="cuda"):

@@ -32,6 +32,7 @@
 // I/O keeps fp32 accuracy), V staged transposed.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "pic_device.h"
@@ -2128,4 +2129,71 @@ extern "C" int pic_selective_attn(const int32_t *plan_host, const int32_t *plan_
     case 128: return launch_attn<float, 128>(h, plan_dev, q, k, v, out, scale, workspace, s);
     default: return PIC_EUNSUPPORTED;
   }
+}
+
+// ===================== selective attention without allocation =====================
+//
+// For callers that cannot allocate (code under HIP graph capture, tight serving loops):
+// the split-KV partials live in a file-scope device array instead of a caller
+// workspace.  Each GPU holds its own copy for the life of the process; its address is
+// looked up once per device (hipGetSymbolAddress, with that device current) and only
+// that address is used from the host.  Every call on a GPU shares the array: calls
+// that overlap on one GPU race.  Nothing in it needs clearing: every partial slot a
+// merge reads is written by its item in the same call (rows past a tile's end are
+// skipped by both, and a slot whose keys were all masked carries m = -inf, which the
+// merge skips).
+
+static __device__ __align__(256) unsigned char scratch[PIC_ATTN_SCRATCH_BYTES];
+
+namespace pic {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of this GPU's scratch array (nullptr on failure).
+void *scratch_ptr(int device) {
+  static std::mutex mu;
+  static void *ptr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[device] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[device] = p;
+  }
+  return ptr[device];
+}
+
+}  // namespace
+}  // namespace pic
+
+extern "C" int pic_selective_attn_noalloc(const int32_t *plan_host, const int32_t *plan_dev,
+                                          const void *q, const void *k, const void *v, void *out,
+                                          int32_t dtype, int32_t head_dim, float scale,
+                                          void *stream) {
+  using namespace pic;
+  const PlanHeader h{plan_host};
+  if (!h.valid() || h[PIC_H_PAGED]) return PIC_EINVAL;
+  if (dtype != PIC_BF16 && dtype != PIC_F32) return PIC_EINVAL;
+  if (!resolve_scale(scale, head_dim)) return PIC_EINVAL;
+  // every check of pic_selective_attn, then the scratch bound, before any device call
+  if (dtype == PIC_BF16 ? (head_dim != 64 && head_dim != 128)
+                        : (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128))
+    return PIC_EUNSUPPORTED;
+  if ((int64_t)h[PIC_H_MAX_TOKENS] * h[PIC_H_H_KV] * head_dim * (int64_t)dtype_size(dtype) >
+      0x7fff0000LL)
+    return PIC_EUNSUPPORTED;
+  if (h[PIC_H_N_ATTN_ITEMS] == 0) return PIC_OK;
+  if (!plan_dev || !q || !k || !v || !out) return PIC_EINVAL;
+  const size_t need = pic_attn_workspace_bytes(plan_host, head_dim);
+  if (need > (size_t)PIC_ATTN_SCRATCH_BYTES) return PIC_ENOSPC;
+  void *ws = nullptr;
+  if (need > 0) {
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= kMaxDevices)
+      return PIC_EDEVICE;
+    ws = scratch_ptr(device);
+    if (ws == nullptr) return PIC_EDEVICE;
+  }
+  return pic_selective_attn(plan_host, plan_dev, q, k, v, out, dtype, head_dim, scale, ws, need,
+                            stream);
 }
