@@ -13,7 +13,8 @@ measures the other configurations of the same path and adds them to the one line
 "sub_records", each with its own roofline and a bounded cpu_baseline: the same batch
 shape at k = 2, 4, 8; one 32,896-token request (32 chunks of 1024 + 128 query tokens)
 at k = 2 and 16; and the shared-pool batch below.  Every contiguous record also times
-the rotation + splice launch right after a 512 MB write that evicts the Infinity Cache.
+the rotation + splice launch right after a 512 MB write and read-back that evict the
+Infinity Cache.
 
 --workload shared_pool: 256 chunks stored once in a paged pool of 16-token blocks,
 8 requests each splicing 96-128 of them (~116k tokens) + 128 query tokens, seam
@@ -843,15 +844,17 @@ def run_contiguous(wl, workload, steps, warmup, rope_scheme="delta", cpu_request
     l_splice = [e[1].elapsed_time(e[2]) for e in sev]
     t_rope, t_splice = float(np.mean(l_rope)), float(np.mean(l_splice))
     rs_bytes = rope_bytes + splice_bytes
-    # the fused rotation + splice from HBM: a 512 MB write evicts the Infinity Cache
-    # before each timed launch (K and V of the smaller batches would otherwise be served
-    # from it)
+    # the fused rotation + splice from HBM: before each timed launch a 512 MB buffer is
+    # written and then read back, which evicts the Infinity Cache (K and V of the smaller
+    # batches would otherwise be served from it) and leaves it holding clean lines, so
+    # the timed launch pays for no write-back of the eviction pass
     l_ev = []
     if evict_passes > 0:
         scratch = torch.empty(MALL_EVICT_BYTES // 4, dtype=torch.int32, device=dev)
         xev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(evict_passes)]
         for i, e in enumerate(xev):
             scratch.fill_(i)
+            scratch.sum()
             e[0].record()
             P.pic_rope_splice(dplan, k, v, kf, vf, wl.rope_base, mode=mode)
             e[1].record()
@@ -914,7 +917,8 @@ def run_contiguous(wl, workload, steps, warmup, rope_scheme="delta", cpu_request
         rec["kernels"]["rope_splice_mall_evicted"] = {
             "ms": round(t_ev, 4), **pct(l_ev), "bytes": rs_bytes, "GB_s": gbs(rs_bytes, t_ev),
             "hbm_frac": frac(rs_bytes, t_ev),
-            "call": fused + ", each launch right after a 512 MB write (Infinity Cache evicted)"}
+            "call": fused + ", each launch right after a 512 MB write and read-back (Infinity "
+                    "Cache evicted, no dirty lines left)"}
     del k, v, q, kf, vf, out, ws
     torch.cuda.empty_cache()
     rec["cpu_baseline"] = None if cpu_requests is None else cpu_baseline(

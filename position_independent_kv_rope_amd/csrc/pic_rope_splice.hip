@@ -21,6 +21,7 @@
 // reduction modulo 2*pi uses a three-part Cody-Waite constant whose first product is
 // exact, so the reduced angle is accurate to a few 1e-7 rad even at delta ~ 1e5.
 #include <cmath>
+#include <type_traits>
 
 #include "pic_device.h"
 #include "pic_internal.h"
@@ -62,90 +63,133 @@ __device__ __forceinline__ void store8(float *p, const float (&x)[8]) {
   *reinterpret_cast<f32x4 *>(p + 4) = b;
 }
 
+// 8 consecutive elements of T as loaded (16 bytes of bf16, 32 bytes of fp32).
+typedef __attribute__((__vector_size__(8 * sizeof(float)))) float f32x8;
+template <typename T>
+using Raw8 = typename std::conditional<sizeof(T) == 2, bf16x8, f32x8>::type;
+
 // One rope tile (<= PIC_ROPE_TILE_ROWS rows of one chunk), run by one workgroup.
 // kAbs == false (rotation by delta): one angle delta * theta_i per pair for the whole
 //   tile (callers skip tiles with delta 0).
 // kAbs == true (RoPE at the target position): angle (pos0 + r) * theta_i for row r.
-// The angles go to LDS (cs: n_pairs or n_rows * n_pairs float2) once per tile.
 // kHalf == false: pairs (2i, 2i+1); a unit is 8 consecutive elements = 4 pairs.
 // kHalf == true:  pairs (i, i+D/2); a unit is elements [8j, 8j+8) and [D/2+8j, D/2+8j+8).
+// Every thread first issues the loads of all its units of the round (up to 16 16-byte
+// loads: a whole bf16 tile of 32 rows x 1024 elements is one round), then the angles
+// are evaluated into LDS (cs: n_pairs or n_rows * n_pairs float2) while those loads
+// are in flight; the barrier waits on the LDS writes only.  So every workgroup keeps its
+// whole tile in flight at once, which matters when the launch is one wave of
+// workgroups (a 32k-token request is ~1,000 tiles).
 template <typename T, bool kHalf, bool kAbs>
 __device__ __forceinline__ void rope_tile(T *__restrict__ k, const RopeTile &t, int h_kv,
-                                          int head_dim, const ThetaTable &theta, float2 *cs) {
+                                          int head_dim, const ThetaTable &theta, float2 *cs,
+                                          int head0, int n_heads) {
+  constexpr int kLoadsPerUnit = (kHalf ? 2 : 1) * (int)sizeof(T) / 2;  // 16-byte loads
+  constexpr int kU = 16 / kLoadsPerUnit;                                 // units per round
   const int n_pairs = head_dim >> 1;
-  if (kAbs) {
-    for (int e = threadIdx.x; e < t.n_rows * n_pairs; e += kRopeThreads) {
-      const int r = e / n_pairs, i = e - r * n_pairs;
-      cs[e] = delta_cos_sin(t.pos0 + r, theta.hi[i], theta.lo[i]);
-    }
-  } else {
-    for (int i = threadIdx.x; i < n_pairs; i += kRopeThreads)
-      cs[i] = delta_cos_sin(t.delta, theta.hi[i], theta.lo[i]);
-  }
-  __syncthreads();
-
   const int units_per_head = kHalf ? (head_dim >> 4) : (head_dim >> 3);
-  const int units_per_row = units_per_head * h_kv;
+  const int units_per_row = units_per_head * n_heads;  // this workgroup's heads of a row
   const int total = t.n_rows * units_per_row;
   const int64_t row_elems = (int64_t)h_kv * head_dim;
-  T *base = k + (int64_t)t.tok_begin * row_elems;
+  T *base = k + (int64_t)t.tok_begin * row_elems + (int64_t)head0 * head_dim;
 
-  for (int u0 = threadIdx.x; u0 < total; u0 += kRopeThreads * kRopeUnroll) {
-    float a[kRopeUnroll][8], b[kRopeUnroll][8];
-    T *pa[kRopeUnroll];
-    int cso[kRopeUnroll];  // this unit's first angle in cs
-    bool live[kRopeUnroll];
+  // a unit's place in the tile: element offset from base and first angle in cs
+  auto place = [&](int u, int &off, int &cso) {
+    const int row = u / units_per_row;
+    const int rem = u - row * units_per_row;
+    const int head = rem / units_per_head;
+    const int j = rem - head * units_per_head;
+    cso = (kAbs ? row * n_pairs : 0) + (kHalf ? 8 * j : 4 * j);
+    off = row * (int)row_elems + head * head_dim + 8 * j;
+  };
+  // this thread's theta values, read before the tile's loads are issued (vector memory
+  // completes in order: a wait for them must not wait for the tile)
+  // (unconditional loads, clamped indices: no branch splits the loads into blocks, so
+  // the wait for theta below counts only the two theta loads)
+  // Rotation by delta: thread i < n_pairs evaluates pair i.  RoPE at the position: entry
+  // e = tid + 256 m is pair e % n_pairs, which is tid % n_pairs when n_pairs divides 256.
+  const bool pair_fixed = kRopeThreads % n_pairs == 0;
+  const int ti = kAbs && pair_fixed ? (int)threadIdx.x % n_pairs : min((int)threadIdx.x, n_pairs - 1);
+  float th_hi = theta.hi[ti], th_lo = theta.lo[ti];
+  asm volatile("" ::: "memory");  // theta loads issued before the tile's loads
+  // one round: this thread's kU units starting at u0 (the first round also evaluates the
+  // angles while its loads are in flight)
+  auto round_at = [&](int u0, bool first) {
+    Raw8<T> ra[kU], rb[kU];  // raw 8-element vectors: converted only when rotated
 #pragma unroll
-    for (int q = 0; q < kRopeUnroll; ++q) {
-      const int u = u0 + q * kRopeThreads;
-      live[q] = u < total;
-      const int uu = live[q] ? u : 0;
-      const int row = uu / units_per_row;
-      const int rem = uu - row * units_per_row;
-      const int head = rem / units_per_head;
-      const int j = rem - head * units_per_head;
-      cso[q] = (kAbs ? row * n_pairs : 0) + (kHalf ? 8 * j : 4 * j);
-      pa[q] = base + row * row_elems + head * head_dim + 8 * j;
-      if (live[q]) {
-        load8(pa[q], a[q]);
-        if (kHalf) load8(pa[q] + n_pairs, b[q]);
+    for (int q = 0; q < kU; ++q) {
+      const int u = min(u0 + q * kRopeThreads, total - 1);  // past the tile: reload its last unit
+      int off, cso;
+      place(u, off, cso);
+      ra[q] = *reinterpret_cast<const Raw8<T> *>(base + off);
+      if (kHalf) rb[q] = *reinterpret_cast<const Raw8<T> *>(base + off + n_pairs);
+    }
+    // every load is issued before the angle math (which waits for theta only)
+    asm volatile("" : "+v"(th_hi), "+v"(th_lo) : : "memory");
+    if (first) {
+      if (kAbs && pair_fixed) {
+        for (int e = threadIdx.x; e < t.n_rows * n_pairs; e += kRopeThreads)
+          cs[e] = delta_cos_sin(t.pos0 + e / n_pairs, th_hi, th_lo);
+      } else if (kAbs) {
+        for (int e = threadIdx.x; e < t.n_rows * n_pairs; e += kRopeThreads) {
+          const int r = e / n_pairs, i = e - r * n_pairs;
+          cs[e] = delta_cos_sin(t.pos0 + r, theta.hi[i], theta.lo[i]);
+        }
+      } else if ((int)threadIdx.x < n_pairs) {
+        cs[threadIdx.x] = delta_cos_sin(t.delta, th_hi, th_lo);
       }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this thread's LDS writes done
+      __builtin_amdgcn_s_barrier();         // (the tile's loads stay in flight)
     }
 #pragma unroll
-    for (int q = 0; q < kRopeUnroll; ++q) {
-      if (!live[q]) continue;
+    for (int q = 0; q < kU; ++q) {
+      const int u = u0 + q * kRopeThreads;
+      if (u >= total) continue;
+      int off, cso;
+      place(u, off, cso);
+      T *pa = base + off;
+      float a[8], b[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[j] = (float)ra[q][j];
       if (kHalf) {
 #pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = (float)rb[q][j];
+#pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float2 c = cs[cso[q] + i];
-          const float x0 = a[q][i], x1 = b[q][i];
-          a[q][i] = x0 * c.x - x1 * c.y;
-          b[q][i] = x0 * c.y + x1 * c.x;
+          const float2 c = cs[cso + i];
+          const float x0 = a[i], x1 = b[i];
+          a[i] = x0 * c.x - x1 * c.y;
+          b[i] = x0 * c.y + x1 * c.x;
         }
-        store8(pa[q], a[q]);
-        store8(pa[q] + n_pairs, b[q]);
+        store8(pa, a);
+        store8(pa + n_pairs, b);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float2 c = cs[cso[q] + i];
-          const float x0 = a[q][2 * i], x1 = a[q][2 * i + 1];
-          a[q][2 * i] = x0 * c.x - x1 * c.y;
-          a[q][2 * i + 1] = x0 * c.y + x1 * c.x;
+          const float2 c = cs[cso + i];
+          const float x0 = a[2 * i], x1 = a[2 * i + 1];
+          a[2 * i] = x0 * c.x - x1 * c.y;
+          a[2 * i + 1] = x0 * c.y + x1 * c.x;
         }
-        store8(pa[q], a[q]);
+        store8(pa, a);
       }
     }
-  }
+  };
+  round_at(threadIdx.x, true);  // a bf16 tile of <= 32 rows is this one round
+  for (int u0 = threadIdx.x + kRopeThreads * kU; u0 < total; u0 += kRopeThreads * kU)
+    round_at(u0, false);
 }
 
 template <typename T, bool kHalf, bool kAbs>
 __global__ __launch_bounds__(kRopeThreads) void rope_kernel(
-    T *__restrict__ k, const RopeTile *__restrict__ tiles, int h_kv, int head_dim,
+    T *__restrict__ k, const RopeTile *__restrict__ tiles, int h_kv, int head_dim, int split,
     ThetaTable theta) {
   extern __shared__ float2 cs[];
-  const RopeTile t = tiles[blockIdx.x];
+  const int tile = blockIdx.x / split, part = blockIdx.x - tile * split;
+  const RopeTile t = tiles[tile];
   if (!kAbs && t.delta == 0) return;
-  rope_tile<T, kHalf, kAbs>(k, t, h_kv, head_dim, theta, cs);
+  const int hp = h_kv / split;
+  rope_tile<T, kHalf, kAbs>(k, t, h_kv, head_dim, theta, cs, part * hp, hp);
 }
 
 // Row scatter of the fresh K/V in 16-byte units, both buffers in one pass: one
@@ -198,7 +242,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_splice_kernel(
     T *__restrict__ k, T *__restrict__ v, const u32x4 *__restrict__ kf,
     const u32x4 *__restrict__ vf, const int32_t *__restrict__ row_tok, int64_t total,
     int units_per_row, int n_splice, const RopeTile *__restrict__ tiles, int h_kv,
-    int head_dim, ThetaTable theta) {
+    int head_dim, int split, ThetaTable theta) {
   static_assert(kRopeThreads == kSpliceThreads, "one workgroup size for both parts");
   extern __shared__ float2 cs[];
   if ((int)blockIdx.x < n_splice) {
@@ -206,23 +250,45 @@ __global__ __launch_bounds__(kRopeThreads) void rope_splice_kernel(
                  (int64_t)blockIdx.x * kSpliceBlockUnits, total, units_per_row);
     return;
   }
-  const RopeTile t = tiles[blockIdx.x - n_splice];
+  const int idx = (int)blockIdx.x - n_splice;
+  const int tile = idx / split, part = idx - tile * split;
+  const RopeTile t = tiles[tile];
   if (!kAbs && t.delta == 0) return;
-  rope_tile<T, kHalf, kAbs>(k, t, h_kv, head_dim, theta, cs);
+  const int hp = h_kv / split;
+  rope_tile<T, kHalf, kAbs>(k, t, h_kv, head_dim, theta, cs, part * hp, hp);
+}
+
+// Workgroups per rope tile.  Large launches share a tile's KV heads out over `split`
+// workgroups (a power of two dividing h_kv) until the launch holds kRopeSplitBlocks of
+// them: more, shorter workgroups keep the HBM stream busier towards the end of the
+// launch (4 x 50k tokens, 6,135 tiles: 131 -> 125 us).  Launches of fewer than
+// kRopeSplitFrom tiles keep one workgroup per tile: there every extra workgroup costs
+// more in dispatch than it returns (32k tokens, 992 tiles: 28 us whole, 29/38/60 us in
+// halves/quarters/eighths).
+constexpr int64_t kRopeSplitFrom = 2048;
+constexpr int64_t kRopeSplitBlocks = 8192;
+int rope_split(int n_tiles, int h_kv) {
+  int split = 1;
+  if (n_tiles < kRopeSplitFrom) return split;
+  while (2 * split <= h_kv && h_kv % (2 * split) == 0 &&
+         (int64_t)n_tiles * split < kRopeSplitBlocks)
+    split *= 2;
+  return split;
 }
 
 template <typename T, bool kAbs>
 int launch_rope(const PlanHeader &h, const int32_t *plan_dev, void *k, int head_dim, int layout,
                 const ThetaTable &theta, hipStream_t s) {
   const RopeTile *tiles = reinterpret_cast<const RopeTile *>(plan_dev + h[PIC_H_O_ROPE_TILES]);
-  const dim3 grid(h[PIC_H_N_ROPE_TILES]);
+  const int split = rope_split(h[PIC_H_N_ROPE_TILES], h[PIC_H_H_KV]);
+  const dim3 grid(h[PIC_H_N_ROPE_TILES] * split);
   const size_t lds = (kAbs ? PIC_ROPE_TILE_ROWS : 1) * (size_t)(head_dim / 2) * sizeof(float2);
   if (layout == PIC_ROPE_HALF)
     hipLaunchKernelGGL((rope_kernel<T, true, kAbs>), grid, dim3(kRopeThreads), lds, s,
-                       static_cast<T *>(k), tiles, h[PIC_H_H_KV], head_dim, theta);
+                       static_cast<T *>(k), tiles, h[PIC_H_H_KV], head_dim, split, theta);
   else
     hipLaunchKernelGGL((rope_kernel<T, false, kAbs>), grid, dim3(kRopeThreads), lds, s,
-                       static_cast<T *>(k), tiles, h[PIC_H_H_KV], head_dim, theta);
+                       static_cast<T *>(k), tiles, h[PIC_H_H_KV], head_dim, split, theta);
   PIC_LAUNCH_CHECK();
   return PIC_OK;
 }
@@ -304,8 +370,9 @@ int launch_rope_splice(const PlanHeader &h, const int32_t *plan_dev, void *k, vo
                        int units_per_row, int head_dim, int layout, const ThetaTable &theta,
                        hipStream_t s) {
   const int n_tiles = h[PIC_H_N_ROPE_TILES];
+  const int split = rope_split(n_tiles, h[PIC_H_H_KV]);
   const int64_t n_splice = (total + kSpliceBlockUnits - 1) / kSpliceBlockUnits;
-  if (n_splice + n_tiles > kMaxFusedBlocks) {
+  if (n_splice + (int64_t)n_tiles * split > kMaxFusedBlocks) {
     if (n_tiles > 0) {
       const int st = launch_rope<T, kAbs>(h, plan_dev, k, head_dim, layout, theta, s);
       if (st != PIC_OK) return st;
@@ -314,7 +381,7 @@ int launch_rope_splice(const PlanHeader &h, const int32_t *plan_dev, void *k, vo
                      : PIC_OK;
   }
   const RopeTile *tiles = reinterpret_cast<const RopeTile *>(plan_dev + h[PIC_H_O_ROPE_TILES]);
-  const dim3 grid((unsigned)(n_splice + n_tiles));
+  const dim3 grid((unsigned)(n_splice + (int64_t)n_tiles * split));
   const size_t lds = (kAbs ? PIC_ROPE_TILE_ROWS : 1) * (size_t)(head_dim / 2) * sizeof(float2);
   const int32_t *row_tok = plan_dev + h[PIC_H_O_ROW_TOK];
   if (layout == PIC_ROPE_HALF)
@@ -322,13 +389,13 @@ int launch_rope_splice(const PlanHeader &h, const int32_t *plan_dev, void *k, vo
                        static_cast<T *>(k), static_cast<T *>(v),
                        static_cast<const u32x4 *>(k_fresh), static_cast<const u32x4 *>(v_fresh),
                        row_tok, total, units_per_row, (int)n_splice, tiles, h[PIC_H_H_KV],
-                       head_dim, theta);
+                       head_dim, split, theta);
   else
     hipLaunchKernelGGL((rope_splice_kernel<T, false, kAbs>), grid, dim3(kRopeThreads), lds, s,
                        static_cast<T *>(k), static_cast<T *>(v),
                        static_cast<const u32x4 *>(k_fresh), static_cast<const u32x4 *>(v_fresh),
                        row_tok, total, units_per_row, (int)n_splice, tiles, h[PIC_H_H_KV],
-                       head_dim, theta);
+                       head_dim, split, theta);
   PIC_LAUNCH_CHECK();
   return PIC_OK;
 }
