@@ -264,7 +264,7 @@ def cpu_baseline_paged(wl, pk, pv, cbp, blocks, q, kf, vf, plan, sample_rows):
 
 
 def bench_paged(args, wl):
-    print(json.dumps(run_paged(wl, steps, warmup,
+    print(json.dumps(run_paged(wl, args.steps, args.warmup,
                                None if args.no_cpu_baseline else args.cpu_sample_rows)), flush=True)
 
 

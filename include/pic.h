@@ -18,7 +18,8 @@
  *                          over every spliced key j <= p_r, GQA, flash-style on MFMA.
  *
  * Around it: pic_selective_attn_paged (steps 2-4 over chunks stored once in a shared
- * paged pool, rotation folded into the query), pic_decode_attn_paged (the next token of
+ * paged pool, rotation folded into the query), pic_rope_splice_pool (steps 2-3 from such a
+ * pool into contiguous buffers, for pic_selective_attn), pic_decode_attn_paged (the next token of
  * every request over the same pool), pic_qkv_rope / pic_out_proj / pic_link (the
  * recomputed rows' projections and the multi-layer link) and pic_state_compose (the
  * state of a linear-attention layer composed over cached chunk summaries).
@@ -249,6 +250,33 @@ int pic_splice(const int32_t *plan_host, const int32_t *plan_dev, void *k, void 
 int pic_rope_splice(const int32_t *plan_host, const int32_t *plan_dev, void *k, void *v,
                     const void *k_fresh, const void *v_fresh, int32_t dtype, int32_t head_dim,
                     int32_t rope_layout, double rope_base, int32_t rope_mode, void *stream);
+
+/*
+ * pic_rope_splice_pool -- rotation + splice from a shared paged pool into contiguous
+ * spliced K/V.                                 [RoPE-C] 3.3, [EPIC] Step 3, [HYPIC] 2.2
+ * The pool (chunks stored once, carrying RoPE at local positions pos_base..; layout and
+ * block table as pic_selective_attn_paged) is only read.  For a paged plan (built with
+ * chunk_ids), every row of the contiguous buffers k, v [n_tokens][h_kv][head_dim] is
+ * written: kept row t of request chunk c (t >= min(k, L_c), chunk 0 entirely) becomes
+ * R(delta_c) applied to the pool chunk's row t (delta_c = off_c - pos_base, same angle,
+ * pair layout and rounding as pic_rope_delta) and V the pool row copied; every
+ * recomputed row gets its fresh K/V (bit copies).  The result is what pic_rope_delta +
+ * pic_splice would leave on the gathered chunks, so pic_selective_attn with a plan
+ * built from the same chunk lengths, query lengths, k and pos_base without chunk_ids
+ * (whose token layout is the same) runs over it.  Rows whose pool block the chunk's
+ * block-table row does not list, or whose id is outside the pool, are written as zeros.
+ * One launch; no size limit on the pool (64-bit offsets).  head_dim even,
+ * head_dim % 8 == 0 (PIC_ROPE_ADJACENT) or % 16 == 0 (PIC_ROPE_HALF), <= 256; bf16 or
+ * f32.  Errors: PIC_EINVAL (not a paged plan, a chunk id >= n_pool_chunks, null
+ * pointers, bad layout/base), PIC_EUNSUPPORTED (block_size != 16, head_dim, plans
+ * beyond 2^22 workgroups), PIC_EDEVICE.
+ */
+int pic_rope_splice_pool(const int32_t *plan_host, const int32_t *plan_dev, const void *pool_k,
+                         const void *pool_v, int64_t pool_blocks, int32_t block_size,
+                         const int32_t *chunk_block_ptr, int32_t n_pool_chunks,
+                         const int32_t *block_ids, void *k, void *v, const void *k_fresh,
+                         const void *v_fresh, int32_t dtype, int32_t head_dim,
+                         int32_t rope_layout, double rope_base, void *stream);
 
 /* Bytes of workspace pic_selective_attn (split-KV partials; 0 if the plan has no split
  * tile) or pic_selective_attn_paged (partials, per-chunk angle table, per-key-block

@@ -34,7 +34,7 @@ PIC_DECODE_BLOCK = 32
 PIC_DECODE_WG_PER_CU = 4
 
 EXPORTED = ("pic_build_index", "pic_rope_delta", "pic_rope_apply", "pic_splice",
-            "pic_rope_splice",
+            "pic_rope_splice", "pic_rope_splice_pool",
             "pic_attn_workspace_bytes",
             "pic_selective_attn", "pic_selective_attn_noalloc", "pic_selective_attn_paged",
             "pic_decode_workspace_bytes",
@@ -76,6 +76,9 @@ def lib():
     L.pic_splice.restype = ctypes.c_int
     L.pic_rope_splice.argtypes = [p, p, p, p, p, p, i32, i32, i32, f64, i32, p]
     L.pic_rope_splice.restype = ctypes.c_int
+    L.pic_rope_splice_pool.argtypes = [p, p, p, p, i64, i32, p, i32, p, p, p, p, p, i32, i32, i32,
+                                       f64, p]
+    L.pic_rope_splice_pool.restype = ctypes.c_int
     L.pic_attn_workspace_bytes.argtypes = [p, i32]
     L.pic_attn_workspace_bytes.restype = sz
     L.pic_selective_attn.argtypes = [p, p, p, p, p, p, i32, i32, f32, p, sz, p]
@@ -347,6 +350,37 @@ def pic_rope_splice(plan, k, v, k_fresh, v_fresh, rope_base, layout=PIC_ROPE_ADJ
                                _dtype_code(k), int(k.shape[2]), int(layout), float(rope_base),
                                int(mode), _stream(stream))
     _check("pic_rope_splice", st)
+
+
+def pic_rope_splice_pool(plan, pool_k, pool_v, chunk_block_ptr, block_ids, k, v, k_fresh,
+                         v_fresh, rope_base, layout=PIC_ROPE_ADJACENT, stream=None):
+    """Rotation + splice of a paged plan's requests from the shared pool [blocks, 16, h_kv,
+    D] (read-only) into contiguous k/v [n_tokens, h_kv, D]; pic_selective_attn with the
+    matching contiguous plan then attends over them."""
+    import torch
+    if not plan.paged:
+        raise ValueError("plan was not built with chunk ids (paged pool)")
+    d = int(k.shape[2])
+    if k.shape != (plan.n_tokens, plan[H_H_KV], d) or v.shape != k.shape:
+        raise ValueError("k/v must be [n_tokens, h_kv, D]")
+    if pool_k.dim() != 4 or pool_v.shape != pool_k.shape or pool_k.shape[2] != plan[H_H_KV] \
+            or pool_k.shape[3] != d:
+        raise ValueError("pool must be [blocks, block_size, h_kv, D]")
+    if k_fresh.shape != (plan.n_rows, plan[H_H_KV], d) or v_fresh.shape != k_fresh.shape:
+        raise ValueError("fresh K/V must be [n_rows, h_kv, D]")
+    for t, name in ((chunk_block_ptr, "chunk_block_ptr"), (block_ids, "block_ids")):
+        if t.dtype != torch.int32 or t.dim() != 1:
+            raise ValueError(name + " must be a 1-D int32 tensor")
+    for t in (pool_k, pool_v, v, k_fresh, v_fresh):
+        if t.dtype != k.dtype:
+            raise ValueError("all tensors must share one dtype")
+    st = lib().pic_rope_splice_pool(
+        plan.host_ptr(), plan.dev_ptr(), _dev(pool_k, "pool_k"), _dev(pool_v, "pool_v"),
+        int(pool_k.shape[0]), int(pool_k.shape[1]), _dev(chunk_block_ptr, "chunk_block_ptr"),
+        int(chunk_block_ptr.numel()) - 1, _dev(block_ids, "block_ids"), _dev(k, "k"),
+        _dev(v, "v"), _dev(k_fresh, "k_fresh"), _dev(v_fresh, "v_fresh"), _dtype_code(k), d,
+        int(layout), float(rope_base), _stream(stream))
+    _check("pic_rope_splice_pool", st)
 
 
 def pic_attn_workspace_bytes(plan, head_dim):

@@ -364,6 +364,171 @@ int launch_splice(const PlanHeader &h, const int32_t *plan_dev, void *k, void *v
 // the two parts as two launches on the same stream.
 constexpr int64_t kMaxFusedBlocks = int64_t(1) << 22;
 
+// ---- rotation + splice from a shared paged pool into contiguous spliced buffers ----
+//
+// The shared-pool counterpart of the one-launch rotation + splice: the pool (chunks
+// stored once, RoPE at local positions, [blocks][16][h_kv][D]) is only read; each
+// request's spliced K/V are written to contiguous caller buffers [n_tokens][h_kv][D]:
+// kept row t of request chunk c becomes R(delta_c) K_pool[t] (V copied), and every
+// recomputed row its fresh K/V.  A paged plan's key-block records give the work: one
+// workgroup per 64-row pool block of a request chunk (rows past the chunk's seam), the
+// first workgroups copying the fresh rows.  Pool blocks that the chunk's block-table
+// row does not list, or ids outside the pool, give zero rows.
+constexpr int kPoolBlockRows = 16;
+constexpr int kKeyBlockRows = 64;
+
+template <typename T, bool kHalf>
+__device__ __forceinline__ void pool_block(T *__restrict__ k, T *__restrict__ v,
+                                           const T *__restrict__ pool_k,
+                                           const T *__restrict__ pool_v, int c, int t0,
+                                           const int32_t *__restrict__ segs,
+                                           const int32_t *__restrict__ chunk_block_ptr,
+                                           const int32_t *__restrict__ block_ids,
+                                           const int32_t *__restrict__ req_tok_ptr, int h_kv,
+                                           int head_dim, int64_t pool_blocks,
+                                           const ThetaTable &theta, float2 *cs, int *bid_s) {
+  constexpr int kLoadsPerUnit = (kHalf ? 2 : 1) * (int)sizeof(T) / 2;  // 16-byte loads
+  constexpr int kU = 8 / kLoadsPerUnit;  // units of K (and of V) per thread per round
+  const int32_t *sg = segs + 8 * c;
+  const int off = sg[0], len = sg[1], seam = sg[2], pid = sg[3], delta = sg[4], req = sg[5];
+  const int t_lo = max(t0, seam), t_hi = min(t0 + kKeyBlockRows, len);
+  const int n_pairs = head_dim >> 1;
+  if ((int)threadIdx.x < kKeyBlockRows / kPoolBlockRows) {
+    const int tab0 = chunk_block_ptr[pid];
+    const int ntab = max(0, chunk_block_ptr[pid + 1] - tab0);
+    const int pb = t0 / kPoolBlockRows + (int)threadIdx.x;
+    const int bid = pb < ntab ? block_ids[tab0 + pb] : -1;
+    bid_s[threadIdx.x] = bid >= 0 && bid < pool_blocks ? bid : -1;
+  }
+  for (int i = threadIdx.x; i < n_pairs; i += kRopeThreads)
+    cs[i] = delta_cos_sin(delta, theta.hi[i], theta.lo[i]);
+  __syncthreads();
+  if (t_lo >= t_hi) return;
+
+  const int units_per_head = kHalf ? (head_dim >> 4) : (head_dim >> 3);
+  const int units_per_row = units_per_head * h_kv;
+  const int total = (t_hi - t_lo) * units_per_row;
+  const int64_t row_elems = (int64_t)h_kv * head_dim;
+  const int64_t dst0 = (int64_t)req_tok_ptr[req] + off;  // K/V row of local key 0
+  // a unit's source (pool) and destination element offsets; src < 0: a zero row
+  auto place = [&](int u, int64_t &src, int64_t &dst, int &cso) {
+    const int i = u / units_per_row;
+    const int rem = u - i * units_per_row;
+    const int head = rem / units_per_head;
+    const int j = rem - head * units_per_head;
+    const int t = t_lo + i;
+    const int bid = bid_s[(t - t0) / kPoolBlockRows];
+    const int64_t in_row = (int64_t)head * head_dim + 8 * j;
+    src = bid < 0 ? -1 : ((int64_t)bid * kPoolBlockRows + t % kPoolBlockRows) * row_elems + in_row;
+    dst = (dst0 + t) * row_elems + in_row;
+    cso = kHalf ? 8 * j : 4 * j;
+  };
+  for (int u0 = threadIdx.x; u0 < total; u0 += kRopeThreads * kU) {
+    Raw8<T> ka[kU], kb[kU], va[kU], vb[kU];
+#pragma unroll
+    for (int q = 0; q < kU; ++q) {
+      const int u = min(u0 + q * kRopeThreads, total - 1);
+      int64_t src, dst;
+      int cso;
+      place(u, src, dst, cso);
+      const int64_t sa = src < 0 ? 0 : src;  // zero rows load row 0 and discard it
+      ka[q] = *reinterpret_cast<const Raw8<T> *>(pool_k + sa);
+      va[q] = *reinterpret_cast<const Raw8<T> *>(pool_v + sa);
+      if (kHalf) {
+        kb[q] = *reinterpret_cast<const Raw8<T> *>(pool_k + sa + n_pairs);
+        vb[q] = *reinterpret_cast<const Raw8<T> *>(pool_v + sa + n_pairs);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kU; ++q) {
+      const int u = u0 + q * kRopeThreads;
+      if (u >= total) continue;
+      int64_t src, dst;
+      int cso;
+      place(u, src, dst, cso);
+      float a[8], b[8], x[8], y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[e] = src < 0 ? 0.f : (float)ka[q][e];
+        x[e] = src < 0 ? 0.f : (float)va[q][e];
+        if (kHalf) {
+          b[e] = src < 0 ? 0.f : (float)kb[q][e];
+          y[e] = src < 0 ? 0.f : (float)vb[q][e];
+        }
+      }
+      if (kHalf) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float2 cz = cs[cso + i];
+          const float x0 = a[i], x1 = b[i];
+          a[i] = x0 * cz.x - x1 * cz.y;
+          b[i] = x0 * cz.y + x1 * cz.x;
+        }
+        store8(k + dst, a);
+        store8(k + dst + n_pairs, b);
+        store8(v + dst, x);
+        store8(v + dst + n_pairs, y);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float2 cz = cs[cso + i];
+          const float x0 = a[2 * i], x1 = a[2 * i + 1];
+          a[2 * i] = x0 * cz.x - x1 * cz.y;
+          a[2 * i + 1] = x0 * cz.y + x1 * cz.x;
+        }
+        store8(k + dst, a);
+        store8(v + dst, x);
+      }
+    }
+  }
+}
+
+template <typename T, bool kHalf>
+__global__ __launch_bounds__(kRopeThreads) void pool_rope_splice_kernel(
+    T *__restrict__ k, T *__restrict__ v, const T *__restrict__ pool_k,
+    const T *__restrict__ pool_v, const u32x4 *__restrict__ kf, const u32x4 *__restrict__ vf,
+    const int32_t *__restrict__ row_tok, int64_t total, int units_per_row, int n_splice,
+    const int4 *__restrict__ kblocks, const int32_t *__restrict__ segs,
+    const int32_t *__restrict__ chunk_block_ptr, const int32_t *__restrict__ block_ids,
+    const int32_t *__restrict__ req_tok_ptr, int h_kv, int head_dim, int64_t pool_blocks,
+    ThetaTable theta) {
+  static_assert(kRopeThreads == kSpliceThreads, "one workgroup size for both parts");
+  extern __shared__ float2 cs[];
+  __shared__ int bid_s[kKeyBlockRows / kPoolBlockRows];
+  if ((int)blockIdx.x < n_splice) {
+    splice_block(reinterpret_cast<u32x4 *>(k), reinterpret_cast<u32x4 *>(v), kf, vf, row_tok,
+                 (int64_t)blockIdx.x * kSpliceBlockUnits, total, units_per_row);
+    return;
+  }
+  const int4 kb = kblocks[blockIdx.x - n_splice];
+  if (kb.x < 0) return;  // a block of fresh rows: copied by the splice workgroups
+  pool_block<T, kHalf>(k, v, pool_k, pool_v, kb.x, kb.y, segs, chunk_block_ptr, block_ids,
+                       req_tok_ptr, h_kv, head_dim, pool_blocks, theta, cs, bid_s);
+}
+
+template <typename T, bool kHalf>
+int launch_pool_rope_splice(const PlanHeader &h, const int32_t *plan_dev, void *k, void *v,
+                            const void *pool_k, const void *pool_v, int64_t pool_blocks,
+                            const int32_t *cbp, const int32_t *bids, const void *k_fresh,
+                            const void *v_fresh, int64_t total, int units_per_row, int head_dim,
+                            const ThetaTable &theta, hipStream_t s) {
+  const int64_t n_splice = (total + kSpliceBlockUnits - 1) / kSpliceBlockUnits;
+  const int64_t n_kb = h[PIC_H_N_KBLOCKS];
+  if (n_splice + n_kb > kMaxFusedBlocks) return PIC_EUNSUPPORTED;
+  if (n_splice + n_kb == 0) return PIC_OK;
+  const size_t lds = (size_t)(head_dim / 2) * sizeof(float2);
+  hipLaunchKernelGGL((pool_rope_splice_kernel<T, kHalf>), dim3((unsigned)(n_splice + n_kb)),
+                     dim3(kRopeThreads), lds, s, static_cast<T *>(k), static_cast<T *>(v),
+                     static_cast<const T *>(pool_k), static_cast<const T *>(pool_v),
+                     static_cast<const u32x4 *>(k_fresh), static_cast<const u32x4 *>(v_fresh),
+                     plan_dev + h[PIC_H_O_ROW_TOK], total, units_per_row, (int)n_splice,
+                     reinterpret_cast<const int4 *>(plan_dev + h[PIC_H_O_KBLOCKS]),
+                     plan_dev + h[PIC_H_O_SEGS], cbp, bids, plan_dev + h[PIC_H_O_REQ_TOK_PTR],
+                     h[PIC_H_H_KV], head_dim, pool_blocks, theta);
+  PIC_LAUNCH_CHECK();
+  return PIC_OK;
+}
+
 template <typename T, bool kAbs>
 int launch_rope_splice(const PlanHeader &h, const int32_t *plan_dev, void *k, void *v,
                        const void *k_fresh, const void *v_fresh, int64_t total,
@@ -460,4 +625,49 @@ extern "C" int pic_rope_splice(const int32_t *plan_host, const int32_t *plan_dev
                                                units_per_row, head_dim, rope_layout, theta, s)
              : launch_rope_splice<float, false>(h, plan_dev, k, v, k_fresh, v_fresh, total,
                                                 units_per_row, head_dim, rope_layout, theta, s);
+}
+
+extern "C" int pic_rope_splice_pool(const int32_t *plan_host, const int32_t *plan_dev,
+                                    const void *pool_k, const void *pool_v, int64_t pool_blocks,
+                                    int32_t block_size, const int32_t *chunk_block_ptr,
+                                    int32_t n_pool_chunks, const int32_t *block_ids, void *k,
+                                    void *v, const void *k_fresh, const void *v_fresh,
+                                    int32_t dtype, int32_t head_dim, int32_t rope_layout,
+                                    double rope_base, void *stream) {
+  using namespace pic;
+  const PlanHeader h{plan_host};
+  if (!h.valid() || !h[PIC_H_PAGED]) return PIC_EINVAL;
+  if (dtype != PIC_BF16 && dtype != PIC_F32) return PIC_EINVAL;
+  if (rope_layout != PIC_ROPE_ADJACENT && rope_layout != PIC_ROPE_HALF) return PIC_EINVAL;
+  if (head_dim <= 0 || head_dim % 2 != 0 || !(rope_base > 0.0) || !std::isfinite(rope_base) ||
+      pool_blocks < 0)
+    return PIC_EINVAL;
+  const int unit = rope_layout == PIC_ROPE_HALF ? 16 : 8;
+  if (block_size != kPoolBlockRows || head_dim % unit != 0 || head_dim > 2 * kMaxPairs)
+    return PIC_EUNSUPPORTED;
+  const int32_t *segs_h = plan_host + h[PIC_H_O_SEGS];
+  for (int32_t c = 0; c < h[PIC_H_N_CHUNKS]; ++c)
+    if (segs_h[8 * c + 3] >= n_pool_chunks) return PIC_EINVAL;
+  if (h[PIC_H_N_TOKENS] == 0) return PIC_OK;
+  if (!plan_dev || !k || !v) return PIC_EINVAL;
+  if (h[PIC_H_N_CHUNKS] > 0 && (!pool_k || !pool_v || !chunk_block_ptr || !block_ids))
+    return PIC_EINVAL;
+  if (h[PIC_H_N_ROWS] > 0 && (!k_fresh || !v_fresh)) return PIC_EINVAL;
+  const int64_t row_bytes = (int64_t)h[PIC_H_H_KV] * head_dim * (int64_t)dtype_size(dtype);
+  const int units_per_row = (int)(row_bytes / 16);
+  const int64_t total = (int64_t)h[PIC_H_N_ROWS] * units_per_row;
+  const ThetaTable theta = make_theta(head_dim, rope_base);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool half = rope_layout == PIC_ROPE_HALF;
+#define PIC_POOL(T_, H_)                                                                   \
+  return launch_pool_rope_splice<T_, H_>(h, plan_dev, k, v, pool_k, pool_v, pool_blocks,   \
+                                         chunk_block_ptr, block_ids, k_fresh, v_fresh, total, \
+                                         units_per_row, head_dim, theta, s)
+  if (dtype == PIC_BF16) {
+    if (half) PIC_POOL(__bf16, true);
+    PIC_POOL(__bf16, false);
+  }
+  if (half) PIC_POOL(float, true);
+  PIC_POOL(float, false);
+#undef PIC_POOL
 }

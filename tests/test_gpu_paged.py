@@ -34,7 +34,29 @@ def f64(t):
     return t.detach().cpu().to(torch.float64).numpy()
 
 
-def run_paged(wl, layout="adjacent", pos_base=0, nan_slack=False, n_cu=0, sample_rows=None):
+def _drop_last_block(cbp, blocks, i):
+    """A CSR block table whose row i lists one block fewer; every other row still lists
+    its own blocks (the ids after row i move up by one place)."""
+    keep = np.ones(len(blocks), dtype=bool)
+    keep[cbp[i + 1] - 1] = False
+    cbp = cbp.copy()
+    cbp[i + 1:] -= 1
+    return cbp, blocks[keep]
+
+
+def _gather_or_zeros(pool64, cbp, blocks, i, L, h_kv, d):
+    """The oracle's gather of pool chunk i; rows whose block its table row does not list
+    read as zeros."""
+    listed = min(L, (cbp[i + 1] - cbp[i]) * pool64.shape[1])
+    g = O.gather_paged_chunk(pool64, blocks[cbp[i]:cbp[i + 1]], listed) if listed > 0 \
+        else np.zeros((0, h_kv, d))
+    if g.shape[0] < L:
+        g = np.concatenate([g, np.zeros((L - g.shape[0], h_kv, d))])
+    return g
+
+
+def run_paged(wl, layout="adjacent", pos_base=0, nan_slack=False, n_cu=0, sample_rows=None,
+              drop_last_block_of=None):
     reqs = [r.chunk_lens for r in wl.requests]
     ids = [r.chunk_ids for r in wl.requests]
     qs = [r.q_len for r in wl.requests]
@@ -56,6 +78,8 @@ def run_paged(wl, layout="adjacent", pos_base=0, nan_slack=False, n_cu=0, sample
                 last = blocks[cbp[i + 1] - 1]
                 pk[last, L % bs:] = float("nan")
                 pv[last, L % bs:] = float("nan")
+    if drop_last_block_of is not None:
+        cbp, blocks = _drop_last_block(cbp, blocks, drop_last_block_of)
     q, kf, vf = W.fresh_tensors(wl, plan.n_rows)
     dev = "cuda"
     pkd, pvd = pk.to(dev), pv.to(dev)
@@ -80,8 +104,10 @@ def run_paged(wl, layout="adjacent", pos_base=0, nan_slack=False, n_cu=0, sample
         assert plan.rows[row0:row1].tolist() == rows
         if row1 == row0:
             continue
-        ck = [O.gather_paged_chunk(pk64, blocks[cbp[i]:cbp[i + 1]], wl.pool_lens[i]) for i in r.chunk_ids]
-        cv = [O.gather_paged_chunk(pv64, blocks[cbp[i]:cbp[i + 1]], wl.pool_lens[i]) for i in r.chunk_ids]
+        ck = [_gather_or_zeros(pk64, cbp, blocks, i, wl.pool_lens[i], wl.h_kv, wl.head_dim)
+              for i in r.chunk_ids]
+        cv = [_gather_or_zeros(pv64, cbp, blocks, i, wl.pool_lens[i], wl.h_kv, wl.head_dim)
+              for i in r.chunk_ids]
         offs = O.chunk_offsets(r.chunk_lens)
         if ck:
             k_ctx, v_ctx = O.rope_delta(ck, wl.rope_base, layout, pos_base), O.concat_chunks(cv)
@@ -366,3 +392,136 @@ def test_paged_f32_rotation_at_delta_near_two_to_the_20(layout):
     # by off_c + 2^20 - 5 (about 1.05e6) on load; every row against the oracle at 1e-5
     wl = small_pool(4, h_q=8, h_kv=2, d=128, seed=29, dtype="f32")
     run_paged(wl, layout, pos_base=-(1 << 20) + 5, n_cu=256)
+
+
+# ---------------------------------------------------------------------------
+# Rotation + splice from the pool into contiguous buffers (pic_rope_splice_pool),
+# then the contiguous selective attention over them
+# ---------------------------------------------------------------------------
+
+
+def run_pool_gather(wl, layout="adjacent", pos_base=0, nan_slack=False, n_cu=0,
+                    sample_rows=None, drop_last_block_of=None):
+    """Gather + rotate + splice from the pool with a paged plan, attend with the contiguous
+    plan of the same requests; every row against the oracle.  drop_last_block_of: a pool
+    chunk whose block-table row is cut by one block (its last rows must read as zeros)."""
+    reqs = [r.chunk_lens for r in wl.requests]
+    ids = [r.chunk_ids for r in wl.requests]
+    qs = [r.q_len for r in wl.requests]
+    pplan = P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, pos_base=pos_base, n_cu=n_cu,
+                              chunk_ids_per_req=ids)
+    cplan = P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, pos_base=pos_base, n_cu=n_cu)
+    assert pplan.req_tok_ptr.tolist() == cplan.req_tok_ptr.tolist()
+    assert pplan.rows.tolist() == cplan.rows.tolist()
+    pplan.to_device()
+    cplan.to_device()
+    cbp, blocks = W.pool_block_table(wl)
+    pk, pv = W.pool_tensors(wl)
+    bs = wl.block_size
+    if nan_slack:
+        for i, L in enumerate(wl.pool_lens):
+            if L % bs:
+                last = blocks[cbp[i + 1] - 1]
+                pk[last, L % bs:] = float("nan")
+                pv[last, L % bs:] = float("nan")
+    cbp_used = cbp.copy()
+    if drop_last_block_of is not None:
+        cbp_used, blocks = _drop_last_block(cbp, blocks, drop_last_block_of)
+    q, kf, vf = W.fresh_tensors(wl, pplan.n_rows)
+    dev = "cuda"
+    k = torch.full((pplan.n_tokens, wl.h_kv, wl.head_dim), float("nan"), dtype=q.dtype, device=dev)
+    v = torch.full_like(k, float("nan"))
+    lay = P.PIC_ROPE_HALF if layout == "half" else P.PIC_ROPE_ADJACENT
+    say(wl.name, "pool gather k=%d" % wl.k, layout, "pos_base=%d" % pos_base,
+        "kblocks=%d" % pplan[P.H_N_KBLOCKS])
+    P.pic_rope_splice_pool(pplan, pk.to(dev), pv.to(dev), torch.from_numpy(cbp_used).to(dev),
+                           torch.from_numpy(blocks).to(dev), k, v, kf.to(dev), vf.to(dev),
+                           wl.rope_base, layout=lay)
+    out = torch.full((pplan.n_rows, wl.h_q, wl.head_dim), float("nan"), dtype=q.dtype, device=dev)
+    P.pic_selective_attn(cplan, q.to(dev), k, v, out, workspace=P.attn_workspace(cplan, wl.head_dim))
+    torch.cuda.synchronize()
+    kg, vg, got_all = k.cpu(), v.cpu(), out.cpu()
+    tol = TOL_F32 if wl.dtype == "f32" else TOL
+    pk64, pv64 = f64(pk), f64(pv)
+    worst = {"rope": 0.0, "attn": 0.0}
+    for b, r in enumerate(wl.requests):
+        tok0 = int(pplan.req_tok_ptr[b])
+        row0, row1 = int(pplan.req_row_ptr[b]), int(pplan.req_row_ptr[b + 1])
+        rows = O.recompute_positions(r.chunk_lens, r.q_len, wl.k)
+        offs = O.chunk_offsets(r.chunk_lens)
+        n_b = offs[-1] + r.q_len
+        ck, cv = [], []
+        for i in r.chunk_ids:  # blocks the table row does not list read as zeros
+            ck.append(_gather_or_zeros(pk64, cbp_used, blocks, i, wl.pool_lens[i], wl.h_kv,
+                                       wl.head_dim))
+            cv.append(_gather_or_zeros(pv64, cbp_used, blocks, i, wl.pool_lens[i], wl.h_kv,
+                                       wl.head_dim))
+        if ck:
+            k_ctx, v_ctx = O.rope_delta(ck, wl.rope_base, layout, pos_base), O.concat_chunks(cv)
+        else:
+            k_ctx = v_ctx = np.zeros((0, wl.h_kv, wl.head_dim))
+        kx, vx = O.splice(k_ctx, v_ctx, f64(kf[row0:row1]), f64(vf[row0:row1]), rows, n_b)
+        gk_b, gv_b = f64(kg[tok0:tok0 + n_b]), f64(vg[tok0:tok0 + n_b])
+        assert np.isfinite(gk_b).all() and np.isfinite(gv_b).all()  # every row written
+        rec = set(rows)
+        keep = [j for j in range(offs[-1]) if j not in rec]
+        if keep:
+            err = float(np.max(np.abs(gk_b[keep] - kx[keep])))
+            worst["rope"] = max(worst["rope"], err)
+            assert err <= tol, ("pool rotation", b, err)
+        assert np.array_equal(gv_b, vx)  # V and the fresh rows are bit copies
+        assert np.array_equal(gk_b[rows], kx[rows])
+        qb = f64(q[row0:row1])
+        if row1 == row0:
+            continue
+        if sample_rows is None:
+            want = O.selective_attn(qb, kx, vx, rows)
+            got = f64(got_all[row0:row1])
+        else:
+            rng = np.random.default_rng(91 + b)
+            n = row1 - row0
+            picks = sorted(set(rng.integers(0, n, size=min(sample_rows, n)).tolist()) | {0, n - 1})
+            heads = rng.integers(0, wl.h_q, size=len(picks))
+            want = O.attn_rows_direct([qb[i, h] for i, h in zip(picks, heads)], kx, vx,
+                                      [rows[i] for i in picks], heads // (wl.h_q // wl.h_kv))
+            got = np.stack([f64(got_all[row0 + i, h]) for i, h in zip(picks, heads)])
+        err = float(np.max(np.abs(got - want)))
+        worst["attn"] = max(worst["attn"], err)
+        assert err <= tol, ("attention over the gathered K/V", b, err)
+    say(wl.name, "pool gather max-abs errors", worst)
+    return worst
+
+
+@pytest.mark.parametrize("layout", ["adjacent", "half"])
+def test_pool_gather_small(layout):
+    run_pool_gather(small_pool(8), layout, nan_slack=True)
+    run_pool_gather(small_pool(3, h_q=16, h_kv=4, seed=43), layout, pos_base=4)
+
+
+def test_pool_gather_f32_and_edges():
+    run_pool_gather(small_pool(8, h_q=8, h_kv=2, d=64, seed=53, dtype="f32"), "adjacent",
+                    nan_slack=True, n_cu=2)
+    run_pool_gather(small_pool(2, h_q=4, h_kv=4, d=128, seed=57, dtype="f32"), "half",
+                    pos_base=-(1 << 20) + 5)
+    # a request without chunks (only query rows) and one without query rows
+    wl = small_pool(4, seed=59)
+    wl.requests.append(W.Request([], 9, chunk_ids=[]))
+    wl.requests.append(W.Request([wl.pool_lens[2], wl.pool_lens[8]], 0, chunk_ids=[2, 8]))
+    run_pool_gather(wl)
+
+
+def test_undersized_block_table_row_reads_zeros():
+    # pool chunk 8 (130 rows = 9 blocks) listed with 8 blocks: its last 2 rows read as
+    # zeros, never the next chunk's first block -- through the gather and through the
+    # paged attention kernel alike
+    wl = small_pool(8, seed=61)
+    wl.requests[0] = W.Request([wl.pool_lens[3], wl.pool_lens[8], wl.pool_lens[9]], 17,
+                               chunk_ids=[3, 8, 9])
+    run_pool_gather(wl, drop_last_block_of=8)
+    run_paged(wl, drop_last_block_of=8)
+
+
+def test_pool_gather_shared_pool_full_size_sampled():
+    # the shared-pool batch (8 x ~116k tokens): every gathered row against the oracle,
+    # sampled attention rows of the contiguous kernel over the result
+    run_pool_gather(W.shared_pool(), n_cu=256, sample_rows=24)
