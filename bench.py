@@ -20,7 +20,10 @@ Infinity Cache.
 8 requests each splicing 96-128 of them (~116k tokens) + 128 query tokens, seam
 window w = 8, GQA 32/4.  The pool is never rotated or written: one step is the
 planner, the plan upload and pic_selective_attn_paged (rotation on load, fresh rows
-read in place).
+read in place).  With --gather one step is instead the planner (a paged plan for the
+gather, a contiguous plan for the attention), both uploads, pic_rope_splice_pool (pool
+blocks -> contiguous rotated K/V with the fresh rows spliced in) and pic_selective_attn;
+the default run adds it as the "shared_pool_gathered_k8" sub-record.
 """
 
 import argparse
@@ -68,6 +71,9 @@ def parse():
                          "every request's chunks (pic_state_compose), --heads heads")
     ap.add_argument("--heads", type=int, default=32,
                     help="linear-attention heads for --state-compose")
+    ap.add_argument("--gather", action="store_true",
+                    help="shared_pool only: gather the pool chunks into contiguous K/V "
+                         "(pic_rope_splice_pool), then pic_selective_attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sub-records", action="store_true",
                     help="default workload only: skip the sub-records of the other "
@@ -264,8 +270,123 @@ def cpu_baseline_paged(wl, pk, pv, cbp, blocks, q, kf, vf, plan, sample_rows):
 
 
 def bench_paged(args, wl):
-    print(json.dumps(run_paged(wl, args.steps, args.warmup,
-                               None if args.no_cpu_baseline else args.cpu_sample_rows)), flush=True)
+    run = run_pool_gathered if args.gather else run_paged
+    print(json.dumps(run(wl, args.steps, args.warmup,
+                         None if args.no_cpu_baseline else args.cpu_sample_rows)), flush=True)
+
+
+def run_pool_gathered(wl, steps, warmup, cpu_sample_rows):
+    """One step = planner (a paged plan with chunk ids for the gather, a contiguous plan of
+    the same requests for the attention) + both uploads + pic_rope_splice_pool +
+    pic_selective_attn over the shared-pool batch; returns the record."""
+    import torch
+    import position_independent_kv_rope_amd as P
+    from position_independent_kv_rope_amd import workloads as W
+    reqs = [r.chunk_lens for r in wl.requests]
+    ids = [r.chunk_ids for r in wl.requests]
+    qs = [r.q_len for r in wl.requests]
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    plans = lambda: (P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, n_cu=n_cu,
+                                       chunk_ids_per_req=ids),
+                     P.pic_build_index(reqs, qs, wl.k, wl.h_q, wl.h_kv, n_cu=n_cu))
+    pplan, cplan = plans()
+    cbp, blocks = W.pool_block_table(wl)
+    pk_h, pv_h = W.pool_tensors(wl)
+    q_h, kf_h, vf_h = W.fresh_tensors(wl, cplan.n_rows)
+    dev = "cuda"
+    pk, pv = pk_h.to(dev), pv_h.to(dev)
+    cbp_d, blocks_d = torch.from_numpy(cbp).to(dev), torch.from_numpy(blocks).to(dev)
+    q, kf, vf = q_h.to(dev), kf_h.to(dev), vf_h.to(dev)
+    k = torch.empty((cplan.n_tokens, wl.h_kv, wl.head_dim), dtype=q.dtype, device=dev)
+    v = torch.empty_like(k)
+    out = torch.empty_like(q)
+    ws = P.attn_workspace(cplan, wl.head_dim)
+    up_p, up_c = PlanUploader(pplan.words.size, dev), PlanUploader(cplan.words.size, dev)
+    torch.cuda.synchronize()
+
+    s = wl.torch_dtype.itemsize
+    D, hq, hkv = wl.head_dim, wl.h_q, wl.h_kv
+    rows = cplan.rows.astype(np.int64)
+    attn_flops = 4.0 * D * hq * float(np.sum(rows + 1))
+    attn_bytes = 2.0 * s * hkv * D * cplan.n_tokens + 2.0 * s * hq * D * cplan.n_rows
+    # the gather reads every context row of K and V from the pool and the fresh rows, and
+    # writes every row of K and V once
+    n_ctx = int(sum(sum(r.chunk_lens) for r in wl.requests))
+    row_bytes = s * hkv * D
+    gather_bytes = 2.0 * row_bytes * (n_ctx + cplan.n_rows) + 2.0 * row_bytes * cplan.n_tokens
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    plan_s = []
+
+    def step(i=None):
+        t0 = time.perf_counter()
+        pp, cp = plans()
+        plan_s.append(time.perf_counter() - t0)
+        up_p.upload(pp)
+        up_c.upload(cp)
+        e = ev[i] if i is not None else None
+        if e: e[0].record()
+        P.pic_rope_splice_pool(pp, pk, pv, cbp_d, blocks_d, k, v, kf, vf, wl.rope_base)
+        if e: e[1].record()
+        P.pic_selective_attn(cp, q, k, v, out, workspace=ws)
+        if e: e[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / steps
+    l_g = [e[0].elapsed_time(e[1]) for e in ev]
+    l_attn = [e[1].elapsed_time(e[2]) for e in ev]
+    t_g, t_attn = float(np.mean(l_g)), float(np.mean(l_attn))
+    tokens = cplan.n_tokens
+    attn_tflops = attn_flops / (t_attn * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": "shared_pool (gathered)", "requests": len(wl.requests),
+                   "tokens": tokens, "pool_chunks": len(wl.pool_lens),
+                   "pool_blocks": int(blocks.size), "block_size": wl.block_size,
+                   "recomputed_rows": cplan.n_rows, "seam_window": wl.k, "h_q": hq,
+                   "h_kv": hkv, "head_dim": D, "rope_base": wl.rope_base,
+                   "parallelism": "none (1 GPU)"},
+        "attn_tflops": round(attn_tflops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4),
+                     "traffic": load_traffic("attn", "shared_pool_gathered_k%d" % wl.k),
+                     "kernel": "pic_selective_attn call (attn_bf16_kernel + merge_kernel)",
+                     "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes},
+        "kernels": {
+            "rope_splice_pool": {"ms": round(t_g, 4), **pct(l_g), "bytes": gather_bytes,
+                                 "GB_s": round(gather_bytes / (t_g * 1e-3) / 1e9, 1),
+                                 "hbm_frac": round(gather_bytes / (t_g * 1e-3) / 1e9
+                                                   / HBM_PEAK_GBS, 4)},
+            "selective_attn": {"ms": round(t_attn, 4), **pct(l_attn), "flops": attn_flops,
+                               "TFLOP_s": round(attn_tflops, 2),
+                               "items": cplan[P.H_N_ATTN_ITEMS], "merges": cplan[P.H_N_MERGE]},
+            "host_plan_ms": round(1e3 * float(np.mean(plan_s)), 4),
+            "gpu_idle_ms": round(ms_step - t_g - t_attn, 4),
+        },
+    }
+    del pk, pv, q, kf, vf, k, v, out, ws
+    torch.cuda.empty_cache()
+    rec["cpu_baseline"] = None if cpu_sample_rows is None else cpu_baseline_paged(
+        wl, pk_h, pv_h, cbp, blocks, q_h, kf_h, vf_h, cplan, cpu_sample_rows)
+    return rec
 
 
 def run_paged(wl, steps, warmup, cpu_sample_rows):
@@ -754,7 +875,8 @@ def bench_state(args, wl):
 
 
 SUB_RECORDS = [("epic_sweep", 2), ("epic_sweep", 4), ("epic_sweep", 8),
-               ("long_context", 2), ("long_context", 16), ("shared_pool", 8)]
+               ("long_context", 2), ("long_context", 16), ("shared_pool", 8),
+               ("shared_pool_gathered", 8)]
 MALL_EVICT_BYTES = 512 << 20  # twice the 256 MB Infinity Cache
 
 
@@ -971,10 +1093,12 @@ def main():
         sub_steps, sub_warm = max(3, min(args.steps, 10)), max(1, min(args.warmup, 3))
         subs = {}
         for name, k in SUB_RECORDS:
-            w = make_workload(name, k)
+            gathered = name == "shared_pool_gathered"
+            w = make_workload("shared_pool" if gathered else name, k)
             print("[bench] sub-record %s k=%d" % (name, k), file=sys.stderr, flush=True)
             if w.pool_lens is not None:
-                r = run_paged(w, sub_steps, sub_warm, None if args.no_cpu_baseline else 96)
+                r = (run_pool_gathered if gathered else run_paged)(
+                    w, sub_steps, sub_warm, None if args.no_cpu_baseline else 96)
             else:
                 r = run_contiguous(w, name, sub_steps, sub_warm, "delta",
                                    None if args.no_cpu_baseline else [0],
