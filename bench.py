@@ -99,6 +99,54 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
+def measured_peaks():
+    """Rates this GPU reaches with plain library calls, measured live (context for the
+    spec-peak fractions, never the denominator of `frac`): a 1 GiB device-to-device copy
+    (read + write bytes), a sum over 2 GiB (read bytes) and an 8192^3 bf16 GEMM of
+    random operands (vendor BLAS)."""
+    import torch
+    dev = "cuda"
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    del dst
+    big = torch.ones(n // 2, dtype=torch.float32, device=dev)
+    t_read = timed(lambda: big.sum(), 10)
+    del big, src
+    m = 8192
+    a = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+    t_gemm = timed(lambda: torch.matmul(a, b), 10)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GB_s": round(2 * n / t_copy / 1e9, 1),
+            "read_GB_s": round(2 * n / t_read / 1e9, 1),
+            "gemm_bf16_TFLOP_s": round(2.0 * m ** 3 / t_gemm / 1e12, 1),
+            "how": "torch copy_ of 1 GiB (read + write), torch sum over 2 GiB, torch.matmul "
+                   "8192^3 bf16 with random operands; 10 launches each, HIP events"}
+
+
+def with_measured(rec, peaks):
+    """Add the fraction of the measured GEMM rate next to the spec fraction."""
+    if peaks and rec.get("roofline", {}).get("unit") == "TFLOP/s" and rec.get("dtype") == "bf16":
+        rec["roofline"]["frac_of_measured_gemm"] = round(
+            rec["roofline"]["achieved"] / peaks["gemm_bf16_TFLOP_s"], 4)
+    return rec
+
+
 def make_workload(name, k):
     from position_independent_kv_rope_amd import workloads as W
     if name == "shared_pool":
@@ -1083,8 +1131,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = list(range(len(wl.requests)))
-    rec = run_contiguous(wl, args.workload, args.steps, args.warmup, args.rope_scheme, cpu,
-                         args.cpu_sample_rows)
+    peaks = measured_peaks()
+    rec = with_measured(run_contiguous(wl, args.workload, args.steps, args.warmup,
+                                       args.rope_scheme, cpu, args.cpu_sample_rows), peaks)
+    rec["measured_peaks"] = peaks
     headline = (args.workload == "epic_sweep" and args.k is None and args.rope_scheme == "delta"
                 and not args.no_sub_records)
     if headline:
@@ -1103,7 +1153,7 @@ def main():
                 r = run_contiguous(w, name, sub_steps, sub_warm, "delta",
                                    None if args.no_cpu_baseline else [0],
                                    0 if name == "long_context" else 128)
-            subs["%s_k%d" % (name, k)] = sub_record(r)
+            subs["%s_k%d" % (name, k)] = sub_record(with_measured(r, peaks))
         rec["sub_records"] = subs
     print(json.dumps(rec), flush=True)
 

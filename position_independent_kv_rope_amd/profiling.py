@@ -27,7 +27,7 @@ import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SHORT = [("rope_splice_kernel", "rope_splice"),
+SHORT = [("pool_rope_splice_kernel", "rope_splice_pool"), ("rope_splice_kernel", "rope_splice"),
          ("qkv_rope_gemm_kernel", "qkv_rope_gemm"), ("out_proj_gemm_kernel", "out_proj_gemm"),
          ("state_compose_kernel", "state_compose"),
          ("row_angles_kernel", "row_angles"),
@@ -64,12 +64,55 @@ def kernel_stats(path):
 
 
 def counters(paths):
-    """Mean per dispatch of every counter, per kernel."""
+    """Mean per dispatch of every counter, per kernel (a counter's rows of one dispatch --
+    one per hardware instance when rocprofv3 reports them apart -- are summed first).
+    Each counter run also gives the mean dispatch duration of its own dispatches, in ns,
+    under the key "duration_ns:<counter run file>"."""
     agg = collections.defaultdict(lambda: collections.defaultdict(list))
     for p in paths:
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        dur, kname = {}, {}
         for r in read_csv(p):
-            agg[short_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            d = r.get("Dispatch_Id", str(len(dur)))
+            per[d][r["Counter_Name"]] += float(r["Counter_Value"])
+            kname[d] = short_name(r["Kernel_Name"])
+            if "Start_Timestamp" in r and "End_Timestamp" in r:
+                dur[d] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+        for d, cs in per.items():
+            for c, v in cs.items():
+                agg[kname[d]][c].append(v)
+            if d in dur:
+                agg[kname[d]]["duration_ns:" + os.path.basename(os.path.dirname(p))].append(dur[d])
     return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
+
+
+# MI355X: 32 shader engines (8 XCDs x 4) each count SQ_BUSY_CYCLES, and 1024 SIMDs (256
+# CUs x 4) each count SQ_VALU_MFMA_BUSY_CYCLES, so per dispatch
+#   shader clock  = SQ_BUSY_CYCLES / 32 / duration
+#   MFMA busy     = SQ_VALU_MFMA_BUSY_CYCLES / 1024 / (SQ_BUSY_CYCLES / 32)
+N_SE, N_SIMD = 32, 1024
+
+
+def derived(c):
+    """Clock, MFMA-busy fraction, instruction mix and wait fractions from one kernel's
+    counters (None where a counter is missing)."""
+    out = {}
+    dur = [v for k, v in c.items() if k.startswith("duration_ns:") and "SQ" in k]
+    busy = c.get("SQ_BUSY_CYCLES")
+    if busy and dur:
+        out["shader_clock_GHz"] = busy / N_SE / dur[0]
+    if busy and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        out["mfma_busy"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / (busy / N_SE)
+    if c.get("SQ_INSTS_MFMA"):
+        out["valu_per_mfma"] = c.get("SQ_INSTS_VALU", 0.0) / c["SQ_INSTS_MFMA"]
+        if "SQ_INSTS_LDS" in c:
+            out["lds_per_mfma"] = c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"]
+    if c.get("SQ_WAVE_CYCLES"):
+        for k, name in (("SQ_WAIT_ANY", "wave_cycles_in_waitcnt"),
+                        ("SQ_WAIT_INST_ANY", "wave_cycles_waiting_to_issue")):
+            if k in c:
+                out[name] = c[k] / c["SQ_WAVE_CYCLES"]
+    return out
 
 
 def src_hash(paths):
@@ -140,9 +183,26 @@ def report(args):
             out.append("- counter traffic / algorithmic bytes: %.2f" % ((fb + wb) / args.algo_bytes))
     if "TCC_HIT" in c and "TCC_MISS" in c:
         out.append("- L2 hit rate: %.1f%%" % (100.0 * c["TCC_HIT"] / (c["TCC_HIT"] + c["TCC_MISS"])))
+    dv = derived(c)
+    if "shader_clock_GHz" in dv:
+        out.append("- shader clock during the SQ counter run: %.2f GHz (SQ_BUSY_CYCLES / 32 "
+                   "shader engines / dispatch duration)" % dv["shader_clock_GHz"])
+    if "mfma_busy" in dv:
+        out.append("- MFMA busy: %.1f%% of busy cycles (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs "
+                   "over SQ_BUSY_CYCLES / 32)" % (100 * dv["mfma_busy"]))
+    if "valu_per_mfma" in dv:
+        out.append("- VALU instructions per MFMA: %.2f%s" % (
+            dv["valu_per_mfma"], "; LDS instructions per MFMA: %.2f" % dv["lds_per_mfma"]
+            if "lds_per_mfma" in dv else ""))
+    if "wave_cycles_in_waitcnt" in dv:
+        out.append("- wave cycles in s_waitcnt: %.1f%%; waiting to issue: %.1f%% "
+                   "(SQ_WAIT_ANY, SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES)" % (
+                       100 * dv["wave_cycles_in_waitcnt"],
+                       100 * dv.get("wave_cycles_waiting_to_issue", 0.0)))
     if c:
         out += ["", "Raw counters (mean per dispatch): " +
-                ", ".join("%s=%.6g" % kv for kv in sorted(c.items()))]
+                ", ".join("%s=%.6g" % kv for kv in sorted(c.items())
+                          if not kv[0].startswith("duration_ns:"))]
     text = "\n".join(out) + "\n"
     if args.out:
         with open(args.out, "w") as f:
