@@ -62,6 +62,17 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+// The lane id, produced afresh at each call (an opaque instruction pair the compiler
+// cannot merge with another), so values derived from it on a rarely taken path are
+// recomputed there instead of being held across the main loop: in a kernel at the
+// register limit such values get spilled, and reloading a spill is a vector memory load
+// whose wait also waits for every direct load issued before it.
+__device__ __forceinline__ int fresh_lane() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
+
 // ================================ bf16 kernel ==================================
 
 constexpr int kBfWaves = 4;
@@ -619,12 +630,14 @@ __device__ __forceinline__ void attn_bf16_paged_body(
     }
   };
   // After a V block landed: zero V rows past the chunk's end (pool blocks) and record
-  // key positions (fresh blocks).
+  // key positions (fresh blocks).  Both are rare (a chunk's last block, the fresh
+  // blocks): the lane-derived values and the zero are made here (fresh_lane).
   auto finish_v = [&](const KeyBlockRec &dsc, int buf) {
     if (dsc.frame < 0) {
       if (wave == 0) {
-        const int r = dsc.row + lane;
-        kpos[buf & 1][lane] = r < n_fresh ? rows[fresh_base + r] : 0x7fffffff;
+        const int ln = fresh_lane();
+        const int r = dsc.row + ln;
+        kpos[buf & 1][ln] = r < n_fresh ? rows[fresh_base + r] : 0x7fffffff;
       }
       return;
     }
@@ -632,10 +645,13 @@ __device__ __forceinline__ void attn_bf16_paged_body(
     if (nv >= kKB) return;
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
-      const int R = kRPI * (kBfWaves * r + wave) + lane / kCPR;
+      const int ln = fresh_lane();
+      const int R = kRPI * (kBfWaves * r + wave) + ln / kCPR;
       if (R >= nv) {
-        const int dst = (2 + buf) * kTileB + (kBfWaves * r + wave) * 1024 + 16 * lane;
-        *reinterpret_cast<u32x4 *>(lds + dst) = u32x4{0u, 0u, 0u, 0u};
+        const int dst = (2 + buf) * kTileB + (kBfWaves * r + wave) * 1024 + 16 * ln;
+        unsigned z;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+        *reinterpret_cast<u32x4 *>(lds + dst) = u32x4{z, z, z, z};
       }
     }
   };
