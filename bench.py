@@ -38,7 +38,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "spliced context tokens/s + selective-attn TFLOP/s (1 GPU, % of roofline)"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
-ATTN_SOURCES = ["position_independent_kv_rope_amd/csrc/pic_attn.hip"]
+CSRC = "position_independent_kv_rope_amd/csrc/"
+ATTN_SOURCES = [CSRC + "pic_attn.hip", CSRC + "pic_attn_common.h"]
 
 
 def parse():

@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpic.so")
 
-SOURCES = ["pic_plan.cpp", "pic_rope_splice.hip", "pic_attn.hip", "pic_link.hip", "pic_state.hip"]
+SOURCES = ["pic_plan.cpp", "pic_rope_splice.hip", "pic_attn.hip", "pic_attn_paged.hip",
+           "pic_decode.hip", "pic_link.hip", "pic_state.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

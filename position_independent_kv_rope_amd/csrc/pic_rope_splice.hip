@@ -30,7 +30,6 @@ namespace pic {
 namespace {
 
 constexpr int kRopeThreads = 256;
-constexpr int kRopeUnroll = 4;
 // 8 consecutive elements <-> 8 floats.
 __device__ __forceinline__ void load8(const __bf16 *p, float (&x)[8]) {
   const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);

@@ -9,7 +9,8 @@
         --fetch <bench FETCH_SIZE csv> --write <bench WRITE_SIZE csv> \
         --copy-fetch <copy FETCH_SIZE csv> --copy-write <copy WRITE_SIZE csv> \
         --kernel attn_bf16_kernel,merge_kernel --out profiles/traffic_attn_<workload>.json \
-        --sources position_independent_kv_rope_amd/csrc/pic_attn.hip
+        --sources position_independent_kv_rope_amd/csrc/pic_attn.hip \
+                  position_independent_kv_rope_amd/csrc/pic_attn_common.h
 
 ``traffic`` scales the per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the kernels of one
 call (summed) by what the same counters read for a plain device copy of known size, and
@@ -221,7 +222,8 @@ def main(argv=None):
     for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--kernel", "--out"):
         t.add_argument(a, required=True)
     t.add_argument("--copy-bytes", type=float, default=float(1 << 30))
-    t.add_argument("--sources", nargs="+", default=["position_independent_kv_rope_amd/csrc/pic_attn.hip"])
+    t.add_argument("--sources", nargs="+", required=True,
+                   help="the kernel sources whose code the record stays valid for")
     t.add_argument("--command", default="")
     r = sub.add_parser("report")
     r.add_argument("--kernel", required=True)
