@@ -430,12 +430,14 @@ __device__ __forceinline__ void pool_block(T *__restrict__ k, T *__restrict__ v,
       int64_t src, dst;
       int cso;
       place(u, src, dst, cso);
-      const int64_t sa = src < 0 ? 0 : src;  // zero rows load row 0 and discard it
-      ka[q] = *reinterpret_cast<const Raw8<T> *>(pool_k + sa);
-      va[q] = *reinterpret_cast<const Raw8<T> *>(pool_v + sa);
-      if (kHalf) {
-        kb[q] = *reinterpret_cast<const Raw8<T> *>(pool_k + sa + n_pairs);
-        vb[q] = *reinterpret_cast<const Raw8<T> *>(pool_v + sa + n_pairs);
+      ka[q] = va[q] = kb[q] = vb[q] = Raw8<T>{};
+      if (src >= 0) {  // zero rows (unlisted or out-of-pool blocks) load nothing
+        ka[q] = *reinterpret_cast<const Raw8<T> *>(pool_k + src);
+        va[q] = *reinterpret_cast<const Raw8<T> *>(pool_v + src);
+        if (kHalf) {
+          kb[q] = *reinterpret_cast<const Raw8<T> *>(pool_k + src + n_pairs);
+          vb[q] = *reinterpret_cast<const Raw8<T> *>(pool_v + src + n_pairs);
+        }
       }
     }
 #pragma unroll

@@ -150,6 +150,27 @@ def test_device_entry_points_reject_bad_arguments_without_launching():
     assert L.pic_attn_workspace_bytes(bp, 128) == 0
 
 
+def test_pool_gather_rejects_bad_arguments_without_launching():
+    L = P.lib()
+    f = ctypes.c_void_p(0x1000)
+    paged = P.pic_build_index([[40, 50]], [7], 2, 8, 4, chunk_ids_per_req=[[0, 1]])
+    contig = P.pic_build_index([[40, 50]], [7], 2, 8, 4)
+    call = lambda plan, n_pool=2, bs=16, dtype=P.PIC_BF16, d=128, layout=P.PIC_ROPE_ADJACENT, \
+        base=1e4, k=f, pool_blocks=64: L.pic_rope_splice_pool(
+            plan.host_ptr(), f, f, f, pool_blocks, bs, f, n_pool, f, k, f, f, f, dtype, d,
+            layout, base, None)
+    assert call(contig) == P.PIC_EINVAL                 # needs a plan built with chunk ids
+    assert call(paged, n_pool=1) == P.PIC_EINVAL        # chunk id 1 outside the table
+    assert call(paged, dtype=7) == P.PIC_EINVAL
+    assert call(paged, layout=2) == P.PIC_EINVAL
+    assert call(paged, base=0.0) == P.PIC_EINVAL
+    assert call(paged, base=float("nan")) == P.PIC_EINVAL
+    assert call(paged, pool_blocks=-1) == P.PIC_EINVAL
+    assert call(paged, d=130) == P.PIC_EUNSUPPORTED     # not a multiple of 8
+    assert call(paged, bs=32) == P.PIC_EUNSUPPORTED     # 16-row pool blocks only
+    assert call(paged, k=None) == P.PIC_EINVAL
+
+
 def test_request_size_limit_is_checked_before_launch():
     # K/V of one request are addressed with 32-bit byte offsets: 0x7fff0000 bytes of K
     # (N * h_kv * D * 2) are taken, one token more is refused without a launch

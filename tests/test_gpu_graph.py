@@ -125,3 +125,26 @@ def test_graph_decode():
     say("decode pieces=%d records=%d" % (plan[P.H_N_DEC_PIECES], plan[P.H_N_DEC_RECS]))
     replay_and_compare(lambda: P.pic_decode_attn_paged(plan, qn, kn, vn, pk, pv, cbp, blocks, kf, vf,
                                                        out, wl.rope_base, workspace=ws), [out])
+
+
+def test_graph_pool_gather():
+    # the gather form of the pool path: pool blocks -> contiguous rotated K/V with the
+    # fresh rows spliced in (paged plan), then the contiguous attention (plan of the same
+    # requests without chunk ids)
+    wl, plan, pk, pv, cbp, blocks, q, kf, vf = _pool_case()
+    reqs = wl.requests
+    cplan = P.pic_build_index([r.chunk_lens for r in reqs], [r.q_len for r in reqs], wl.k,
+                              wl.h_q, wl.h_kv, n_cu=256)
+    cplan.to_device()
+    k = torch.empty((cplan.n_tokens, wl.h_kv, wl.head_dim), dtype=q.dtype, device="cuda")
+    v = torch.empty_like(k)
+    out = torch.empty_like(q)
+    ws = P.attn_workspace(cplan, wl.head_dim)
+    say("pool gather kblocks=%d, attention items=%d merges=%d"
+        % (plan[P.H_N_KBLOCKS], cplan[P.H_N_ATTN_ITEMS], cplan[P.H_N_MERGE]))
+
+    def fn():
+        P.pic_rope_splice_pool(plan, pk, pv, cbp, blocks, k, v, kf, vf, wl.rope_base)
+        P.pic_selective_attn(cplan, q, k, v, out, workspace=ws)
+
+    replay_and_compare(fn, [out, k, v])
