@@ -357,13 +357,15 @@ def _random_pool(i):
 
 @pytest.mark.parametrize("i", range(8))
 def test_random_pools(i):
-    # paged prefill (every row) and the decode step (every request) on seeded random
-    # pools, both pair layouts, NaN in the slack slots of every other case
+    # paged prefill (every row), the gather form (every gathered row and output) and the
+    # decode step (every request) on seeded random pools, both pair layouts, NaN in the
+    # slack slots of every other case
     wl = _random_pool(i)
     layout = "half" if i % 2 else "adjacent"
     say("random pool", i, "h_q=%d h_kv=%d D=%d k=%d" % (wl.h_q, wl.h_kv, wl.head_dim, wl.k),
         layout, [(len(r.chunk_ids), r.q_len) for r in wl.requests])
     run_paged(wl, layout, nan_slack=bool(i % 2), n_cu=(256 if i % 3 == 0 else 2))
+    run_pool_gather(wl, layout, nan_slack=bool(i % 2), n_cu=(2 if i % 3 == 0 else 256))
     if wl.h_q // wl.h_kv <= P.PIC_DECODE_COLS:
         run_decode(wl, layout, nan_slack=bool(i % 2), n_cu=(1 if i % 3 == 1 else 256))
 
