@@ -22,10 +22,12 @@
 // domain (scores scaled by scale * log2 e).
 //
 // bf16 kernel (the hot one): 4 waves x 32 queries, v_mfma_f32_32x32x16_bf16 for both
-// products, K/V blocks of 64 keys double-buffered in LDS and staged by direct
-// buffer->LDS loads (the buffer range clamps rows past the item's keys to zero), K
-// one block ahead of V so that S^T of block i+1 is computed while block i's softmax
-// runs (software pipelining inside each wave), V read transposed for
+// products, K/V blocks of 64 keys in LDS (three K buffers, two V buffers: 80 KB, two
+// workgroups per CU) staged by direct buffer->LDS loads (the buffer range clamps rows
+// past the item's keys to zero), K three blocks ahead and V one, so that S^T of block
+// i+1 is computed while block i's softmax runs (software pipelining inside each wave)
+// and the wait at the end of a block leaves the newest K loads in flight, V read
+// transposed for
 // the PV operand with ds_read_b64_tr_b16, row sums taken from the bf16 probabilities
 // with v_dot2_f32_bf16.
 // fp32 kernel: 8 waves x 16 queries, v_mfma_f32_16x16x4_f32 (fp32 operands, so fp32
@@ -51,8 +53,8 @@ __device__ __forceinline__ void attn_bf16_body(
   constexpr int kDB = D / 32;                  // 32-wide d blocks of O^T
   static_assert(kRounds * kRPI * kBfWaves == kKB, "direct loads must tile the block");
   static_assert(2 * kKS <= 16, "S^T MFMAs of a block must fit the 16 exponential pairs");
-  // [buffer 0: K, V][buffer 1: K, V]
-  __shared__ __attribute__((aligned(1024))) char lds[4 * kTileB];
+  // K buffers 0..2, V buffers 3..4
+  __shared__ __attribute__((aligned(1024))) char lds[5 * kTileB];
 
   const AttnItem it = items[blockIdx.x];
   const AttnTile tile = tiles[it.tile];
@@ -111,8 +113,7 @@ __device__ __forceinline__ void attn_bf16_body(
     voff_k[r] = R * tok_bytes + 16 * (p ^ swz_k<kCPR>(R));
     voff_v[r] = R * tok_bytes + 16 * (p ^ swz_v<kCPR>(R));
   }
-  // LDS: K blocks in buffers 0/1, V blocks in buffers 2/3.  K is staged one block
-  // ahead of V so that S^T of block i+1 can be computed while block i's softmax runs.
+  // LDS: K blocks in buffers 0..2, V blocks in buffers 3..4 (buf counts kTileB units).
   auto issue = [&](const __bf16 *base, const int (&voffs)[kRounds], int kb0, int buf) {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, n_records, 0x00020000);
@@ -140,8 +141,8 @@ __device__ __forceinline__ void attn_bf16_body(
     const int f = swz_v<kCPR>(rr) >> 2;
 #pragma unroll
     for (int d = 0; d < kDB; ++d)
-      voff[d] = rr * kRowB + 16 * (4 * (d ^ f) + 2 * (q16 & 1) + ((i16 & 3) >> 1)) +
-                8 * (i16 & 1);
+      voff[d] = 3 * kTileB + rr * kRowB + 16 * (4 * (d ^ f) + 2 * (q16 & 1) + ((i16 & 3) >> 1)) +
+                8 * (i16 & 1);  // V buffers start after the three K buffers
   }
 
   // S^T = K Q^T for the two 32-key tiles of the block in K buffer kb.
@@ -166,7 +167,7 @@ __device__ __forceinline__ void attn_bf16_body(
   // column's block max exceeds it by more than kLazy (log2 units), so rescaling the
   // accumulators is rare; probabilities then stay below 2^kLazy, far inside fp32/bf16
   // range, and the final normalisation is unchanged (acc and l share the reference).
-  auto softmax_pv = [&](f32x16 (&sc)[2], int kb0, const char *Vb, const char *Knext,
+  auto softmax_pv = [&](f32x16 (&sc)[2], int kb0, int Vb_off, const char *Knext,
                         f32x16 (&s_nxt)[2]) {
     constexpr float kLazy = 8.f;
     if (kb0 + kKB - 1 > min(pos_min, key_last)) {
@@ -238,7 +239,7 @@ __device__ __forceinline__ void attn_bf16_body(
     constexpr int kPreV = 2;  // V operands in flight ahead of their MFMA
     bf16x8 vop[4 * kDB];
     auto vload = [&](int o) {
-      const char *vr = Vb + voff[o % kDB] + (o / kDB) * 16 * kRowB;
+      const char *vr = lds + voff[o % kDB] + Vb_off + (o / kDB) * 16 * kRowB;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)vr);
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vr + 4 * kRowB));
       __builtin_memcpy(&vop[o], &lo, 8);
@@ -262,32 +263,50 @@ __device__ __forceinline__ void attn_bf16_body(
   };
 
   const int n_blocks = (key_end - key_begin + kKB - 1) / kKB;
+  // K blocks rotate through three buffers, V blocks through two: block ib's K lives in
+  // K buffer ib % 3, its V in V buffer ib % 2.  K is staged three blocks ahead, so the
+  // wait at the end of a block leaves the newest K loads in flight.
   issue(kh, voff_k, key_begin, 0);
-  issue(vh, voff_v, key_begin, 2);
+  issue(vh, voff_v, key_begin, 3);
   if (n_blocks > 1) issue(kh, voff_k, key_begin + kKB, 1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (n_blocks > 2) {
+    issue(kh, voff_k, key_begin + 2 * kKB, 2);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRounds) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __syncthreads();
   f32x16 sa[2], sb[2];
   qk(lds, sa);
   __syncthreads();  // K buffer 0 is refilled next
 
-  // Block ib: S^T(ib) is in registers; stage K(ib+2) and V(ib+1), compute S^T(ib+1),
-  // then the softmax and PV of block ib.  kB = ib & 1 selects the buffers.
-  auto step = [&](int ib, auto bufc, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
-    constexpr int kB = decltype(bufc)::value;
+  // Block ib: S^T(ib) is in registers; stage V(ib+1) and K(ib+3), compute S^T(ib+1),
+  // then the softmax and PV of block ib.  KC = ib % 3, VC = ib % 2.
+  auto step = [&](int ib, auto kc, auto vc, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+    constexpr int KC = decltype(kc)::value, VC = decltype(vc)::value;
     const int kb0 = key_begin + ib * kKB;
-    if (ib + 2 < n_blocks) issue(kh, voff_k, kb0 + 2 * kKB, kB);
-    if (ib + 1 < n_blocks) issue(vh, voff_v, kb0 + kKB, 2 + (kB ^ 1));
-    softmax_pv(s_cur, kb0, lds + (2 + kB) * kTileB, lds + (kB ^ 1) * kTileB, s_nxt);
+    if (ib + 1 < n_blocks) issue(vh, voff_v, kb0 + kKB, 3 + (VC ^ 1));
+    const bool k3 = ib + 3 < n_blocks;
+    if (k3) issue(kh, voff_k, kb0 + 3 * kKB, KC);
+    softmax_pv(s_cur, kb0, VC * kTileB, lds + ((KC + 1) % 3) * kTileB, s_nxt);
     if (ib + 1 < n_blocks) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (k3)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRounds) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
   };
-
-  for (int ib = 0; ib < n_blocks; ib += 2) {
-    step(ib, std::integral_constant<int, 0>{}, sa, sb);
-    if (ib + 1 < n_blocks) step(ib + 1, std::integral_constant<int, 1>{}, sb, sa);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  for (int ib = 0; ib < n_blocks; ib += 6) {
+    step(ib, I0{}, I0{}, sa, sb);
+    if (ib + 1 < n_blocks) step(ib + 1, I1{}, I1{}, sb, sa);
+    if (ib + 2 < n_blocks) step(ib + 2, I2{}, I0{}, sa, sb);
+    if (ib + 3 < n_blocks) step(ib + 3, I0{}, I1{}, sb, sa);
+    if (ib + 4 < n_blocks) step(ib + 4, I1{}, I0{}, sa, sb);
+    if (ib + 5 < n_blocks) step(ib + 5, I2{}, I1{}, sb, sa);
   }
 
   // ---- epilogue ----
