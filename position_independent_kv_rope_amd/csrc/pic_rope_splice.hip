@@ -266,9 +266,11 @@ __global__ __launch_bounds__(kRopeThreads) void rope_splice_kernel(
 // halves/quarters/eighths).
 constexpr int64_t kRopeSplitFrom = 2048;
 constexpr int64_t kRopeSplitBlocks = 8192;
-int rope_split(int n_tiles, int h_kv) {
+int rope_split(int n_tiles, int h_kv, bool absolute) {
   int split = 1;
-  if (n_tiles < kRopeSplitFrom) return split;
+  // RoPE at the target position builds a per-row angle table for the whole tile, which
+  // every workgroup of a split tile would build again: those tiles stay whole
+  if (absolute || n_tiles < kRopeSplitFrom) return split;
   while (2 * split <= h_kv && h_kv % (2 * split) == 0 &&
          (int64_t)n_tiles * split < kRopeSplitBlocks)
     split *= 2;
@@ -279,7 +281,7 @@ template <typename T, bool kAbs>
 int launch_rope(const PlanHeader &h, const int32_t *plan_dev, void *k, int head_dim, int layout,
                 const ThetaTable &theta, hipStream_t s) {
   const RopeTile *tiles = reinterpret_cast<const RopeTile *>(plan_dev + h[PIC_H_O_ROPE_TILES]);
-  const int split = rope_split(h[PIC_H_N_ROPE_TILES], h[PIC_H_H_KV]);
+  const int split = rope_split(h[PIC_H_N_ROPE_TILES], h[PIC_H_H_KV], kAbs);
   const dim3 grid(h[PIC_H_N_ROPE_TILES] * split);
   const size_t lds = (kAbs ? PIC_ROPE_TILE_ROWS : 1) * (size_t)(head_dim / 2) * sizeof(float2);
   if (layout == PIC_ROPE_HALF)
@@ -536,7 +538,7 @@ int launch_rope_splice(const PlanHeader &h, const int32_t *plan_dev, void *k, vo
                        int units_per_row, int head_dim, int layout, const ThetaTable &theta,
                        hipStream_t s) {
   const int n_tiles = h[PIC_H_N_ROPE_TILES];
-  const int split = rope_split(n_tiles, h[PIC_H_H_KV]);
+  const int split = rope_split(n_tiles, h[PIC_H_H_KV], kAbs);
   const int64_t n_splice = (total + kSpliceBlockUnits - 1) / kSpliceBlockUnits;
   if (n_splice + (int64_t)n_tiles * split > kMaxFusedBlocks) {
     if (n_tiles > 0) {
