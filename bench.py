@@ -184,50 +184,34 @@ def load_traffic(kernel, workload, sources=None):
 
 class PlanUploader:
     """Host planner output -> device plan, pipelined: the plan words go through one of two
-    pinned host buffers into one of two device buffers, copied on a side stream of
-    default priority, so the host plans step i+1 and its plan crosses PCIe while the GPU
-    still runs step i; the compute stream waits only for the copy of its own plan, and
-    the kernels of a step run back to back (the events around each call time GPU work
-    only).  A copy into a device buffer waits until the kernels of the step that read
-    it before (two uploads back) have finished; a pinned buffer is refilled only after
-    the copy that read it has completed."""
+    pinned host buffers and are copied asynchronously on the compute stream, so the host
+    plans step i+1 while the GPU still runs step i and the GPU runs the kernels of a step
+    back to back (the events around each call then time GPU work only).  A buffer is
+    reused only after the copy that read it has completed."""
 
     def __init__(self, n_words, device):
         import torch
         self.torch = torch
-        self.dev = [torch.empty(n_words, dtype=torch.int32, device=device) for _ in range(2)]
+        self.dev = torch.empty(n_words, dtype=torch.int32, device=device)
         self.host = [torch.empty(n_words, dtype=torch.int32, pin_memory=True) for _ in range(2)]
-        self.stream = torch.cuda.Stream(device=device)
-        self.copied = [None, None]  # copy into buffer b done (side stream)
-        self.mark = None            # compute work enqueued before the previous upload
+        self.done = [None, None]
         self.i = 0
 
     def upload(self, plan):
         torch = self.torch
         b = self.i % 2
         self.i += 1
+        if self.done[b] is not None:
+            self.done[b].synchronize()
         n = plan.words.size
-        if n > self.dev[b].numel():
+        if n > self.dev.numel():
             raise ValueError("plan grew beyond the preallocated device buffer")
-        compute = torch.cuda.current_stream()
-        # everything enqueued so far on the compute stream (the steps before this one);
-        # the next upload into the other buffer waits for the mark of this upload's
-        # predecessor, i.e. for the step that read that buffer
-        mark = torch.cuda.Event()
-        mark.record(compute)
-        reused_after, self.mark = self.mark, mark
-        if self.copied[b] is not None:
-            self.copied[b].synchronize()
         self.host[b].numpy()[:n] = plan.words
-        if reused_after is not None:
-            self.stream.wait_event(reused_after)
-        with torch.cuda.stream(self.stream):
-            self.dev[b][:n].copy_(self.host[b][:n], non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record(self.stream)
-        self.copied[b] = ev
-        compute.wait_event(ev)
-        plan.dev = self.dev[b]
+        self.dev[:n].copy_(self.host[b][:n], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.done[b] = ev
+        plan.dev = self.dev
         return plan
 
 
