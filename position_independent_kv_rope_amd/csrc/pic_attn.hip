@@ -525,15 +525,7 @@ int launch_attn(const PlanHeader &h, const int32_t *plan_dev, const void *q, con
                        ws_o, ws_ml, h[PIC_H_H_Q], h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], scale_log2);
   }
   PIC_LAUNCH_CHECK();
-  if (h[PIC_H_N_MERGE] > 0) {
-    const int64_t threads = (int64_t)h[PIC_H_N_MERGE] * kM * (D / 8);
-    const unsigned blocks = (unsigned)std::min<int64_t>((threads + 255) / 256, 1 << 20);
-    hipLaunchKernelGGL((merge_kernel<T, D>), dim3(blocks), dim3(256), 0, s,
-                       static_cast<T *>(out), tiles, merges, ws_o, ws_ml, h[PIC_H_H_Q],
-                       h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], h[PIC_H_N_MERGE]);
-    PIC_LAUNCH_CHECK();
-  }
-  return PIC_OK;
+  return launch_merge<T, D>(h, tiles, merges, out, ws_o, ws_ml, s);
 }
 
 }  // namespace

@@ -186,6 +186,119 @@ __global__ __launch_bounds__(256) void merge_kernel(
   }
 }
 
+// The same merge with four adjacent lanes per output, for plans whose merges average
+// many slots (tens on a 32k-token request, where one lane per output waits for one load
+// latency per few slots): lane j of the four folds slots j, j + 4, ... with all of its
+// loads issued before its first fold, then the four partial states are combined across
+// the lanes and lane 0 stores.  With a few slots per merge the one-lane kernel is as
+// fast and launches a quarter of the workgroups, so it stays the default.
+constexpr int kMergeWideFrom = 16;  // mean slots per merge from which the wide kernel runs
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel_x4(
+    T *__restrict__ out, const AttnTile *__restrict__ tiles, const MergeEntry *__restrict__ merges,
+    const float *__restrict__ ws_o, const float *__restrict__ ws_ml, int h_q, int h_kv,
+    int tile_rows, int n_merge) {
+  constexpr int kV = 8;
+  constexpr int kC = D / kV;
+  constexpr int kLanes = 4, kBatch = 4;
+  typedef __attribute__((__vector_size__(kV * sizeof(float)))) float f32x8;
+  const int group = h_q / h_kv;
+  // the four lanes of a group run the same iterations (total and the grid stride are
+  // multiples of four), so the exchange below sees all of them
+  const int64_t total = (int64_t)n_merge * kM * kC * kLanes;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < total;
+       u += (int64_t)gridDim.x * 256) {
+    const int j = (int)(u % kLanes);
+    const int64_t w = u / kLanes;
+    const int e = (int)(w / (kM * kC));
+    const int rem = (int)(w - (int64_t)e * (kM * kC));
+    const int m = rem / kC, c = rem - m * kC;
+    const MergeEntry me = merges[e];
+    const AttnTile tile = tiles[me.tile];
+    const int row_local = m % tile_rows;
+    if (row_local >= tile.n_rows) continue;  // the same for the four lanes
+    const int head = me.kv_head * group + m / tile_rows;
+    float mmax = kNegInf, den = 0.f;
+    f32x8 num = {};
+    auto fold = [&](float ms, float ls, const f32x8 &os) {
+      if (ms == kNegInf) return;
+      if (ms > mmax) {
+        const float r = __builtin_amdgcn_exp2f(mmax - ms);  // 0 when mmax is -inf
+        den *= r;
+        num *= r;
+        mmax = ms;
+      }
+      const float wt = __builtin_amdgcn_exp2f(ms - mmax);
+      den += wt * ls;
+      num += wt * os;
+    };
+    for (int s0 = j; s0 < me.n_slots; s0 += kLanes * kBatch) {
+      float2 ml[kBatch];
+      f32x8 os[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int sl = s0 + b * kLanes;
+        ml[b] = make_float2(kNegInf, 0.f);
+        os[b] = f32x8{};
+        if (sl < me.n_slots) {
+          const int64_t at = (int64_t)(me.slot_base + sl) * kM + m;
+          ml[b] = *reinterpret_cast<const float2 *>(ws_ml + at * 2);
+          if constexpr (std::is_same<T, __bf16>::value) {
+            const bf16x8 ob = *reinterpret_cast<const bf16x8 *>(
+                reinterpret_cast<const __bf16 *>(ws_o) + at * D + kV * c);
+#pragma unroll
+            for (int i = 0; i < kV; ++i) os[b][i] = (float)ob[i];
+          } else {
+            os[b] = *reinterpret_cast<const f32x8 *>(ws_o + at * D + kV * c);
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) fold(ml[b].x, ml[b].y, os[b]);
+    }
+#pragma unroll
+    for (int x = 1; x < kLanes; x <<= 1) {
+      const float om = __shfl_xor(mmax, x), ol = __shfl_xor(den, x);
+      f32x8 on;
+#pragma unroll
+      for (int i = 0; i < kV; ++i) on[i] = __shfl_xor(num[i], x);
+      fold(om, ol, on);
+    }
+    if (j != 0) continue;
+    const float inv = 1.f / den;
+    T *op = out + ((int64_t)(tile.row_begin + row_local) * h_q + head) * D + kV * c;
+    if constexpr (std::is_same<T, __bf16>::value) {
+      bf16x8 o;
+#pragma unroll
+      for (int i = 0; i < kV; ++i) o[i] = (__bf16)(num[i] * inv);
+      *reinterpret_cast<bf16x8 *>(op) = o;
+    } else {
+      *reinterpret_cast<f32x8 *>(op) = num * inv;
+    }
+  }
+}
+
+// Launch the merge of a plan's split partials (nothing when the plan has none).
+template <typename T, int D>
+int launch_merge(const PlanHeader &h, const AttnTile *tiles, const MergeEntry *merges, void *out,
+                 const float *ws_o, const float *ws_ml, hipStream_t s) {
+  if (h[PIC_H_N_MERGE] == 0) return PIC_OK;
+  const bool wide = h[PIC_H_N_PARTIALS] >= (int64_t)kMergeWideFrom * h[PIC_H_N_MERGE];
+  const int64_t threads = (int64_t)h[PIC_H_N_MERGE] * kM * (D / 8) * (wide ? 4 : 1);
+  const unsigned blocks = (unsigned)std::min<int64_t>((threads + 255) / 256, 1 << 20);
+  if (wide)
+    hipLaunchKernelGGL((merge_kernel_x4<T, D>), dim3(blocks), dim3(256), 0, s,
+                       static_cast<T *>(out), tiles, merges, ws_o, ws_ml, h[PIC_H_H_Q],
+                       h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], h[PIC_H_N_MERGE]);
+  else
+    hipLaunchKernelGGL((merge_kernel<T, D>), dim3(blocks), dim3(256), 0, s,
+                       static_cast<T *>(out), tiles, merges, ws_o, ws_ml, h[PIC_H_H_Q],
+                       h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], h[PIC_H_N_MERGE]);
+  PIC_LAUNCH_CHECK();
+  return PIC_OK;
+}
+
 // Workspace layout: partial O [slots][kM][D], partial (m, l) [slots][kM][2], then for
 // paged plans the angle table [n_chunks][D/2] float2 and the key-block records
 // [n_kblocks] (sections 16-byte aligned).

@@ -718,15 +718,7 @@ int launch_paged(const PlanHeader &h, const int32_t *plan_dev, const void *q, co
                      h[PIC_H_H_Q], h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], scale * kLog2e,
                      (int)(pool_blocks * kPoolBlockRows * tok_bytes));
   PIC_LAUNCH_CHECK();
-  if (h[PIC_H_N_MERGE] > 0) {
-    const int64_t threads = (int64_t)h[PIC_H_N_MERGE] * kM * (D / 8);
-    const unsigned blocks = (unsigned)std::min<int64_t>((threads + 255) / 256, 1 << 20);
-    hipLaunchKernelGGL((merge_kernel<__bf16, D>), dim3(blocks), dim3(256), 0, s,
-                       static_cast<__bf16 *>(out), tiles, merges, ws_o, ws_ml, h[PIC_H_H_Q],
-                       h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], h[PIC_H_N_MERGE]);
-    PIC_LAUNCH_CHECK();
-  }
-  return PIC_OK;
+  return launch_merge<__bf16, D>(h, tiles, merges, out, ws_o, ws_ml, s);
 }
 
 // fp32 over the pool: the same angle table, key-block records (with fp32 row bytes) and
@@ -771,15 +763,7 @@ int launch_paged_f32(const PlanHeader &h, const int32_t *plan_dev, const void *q
                      static_cast<float *>(out), rows, tiles, items, recs, angles, ws_o, ws_ml,
                      h[PIC_H_H_Q], h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], scale * kLog2e);
   PIC_LAUNCH_CHECK();
-  if (h[PIC_H_N_MERGE] > 0) {
-    const int64_t threads = (int64_t)h[PIC_H_N_MERGE] * kM * (D / 8);
-    const unsigned blocks = (unsigned)std::min<int64_t>((threads + 255) / 256, 1 << 20);
-    hipLaunchKernelGGL((merge_kernel<float, D>), dim3(blocks), dim3(256), 0, s,
-                       static_cast<float *>(out), tiles, merges, ws_o, ws_ml, h[PIC_H_H_Q],
-                       h[PIC_H_H_KV], h[PIC_H_TILE_ROWS], h[PIC_H_N_MERGE]);
-    PIC_LAUNCH_CHECK();
-  }
-  return PIC_OK;
+  return launch_merge<float, D>(h, tiles, merges, out, ws_o, ws_ml, s);
 }
 
 }  // namespace
