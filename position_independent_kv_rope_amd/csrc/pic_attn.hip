@@ -67,9 +67,25 @@ __device__ __forceinline__ void attn_bf16_body(
   const int q16 = lane >> 4;   // 16-lane group of the transposing read
   const int i16 = lane & 15;
 
-  const int m = 32 * wave + n;
-  const int row_local = m % tile_rows;
-  const int head = g * group + m / tile_rows;
+  // Query columns.  With G <= 32 query heads per KV head, wave w owns rows
+  // [w * 32/G, (w + 1) * 32/G) of the tile with all G heads (column n: row n / G, head
+  // n % G), so the rows of one wave are a quarter of the tile's span of positions: fewer
+  // key blocks straddle them (masking) and the blocks past its last row are skipped.
+  // (G is a power of two dividing 128; with G > 32 a wave takes 32 consecutive
+  // head-major columns.)  mcol is the column's index in the split partials, which the
+  // merge reads head-major: head * tile_rows + row.
+  int row_local, hl;
+  if (group <= 32) {
+    const int lg = __builtin_ctz(group);
+    row_local = (wave << (5 - lg)) + (n >> lg);
+    hl = n & (group - 1);
+  } else {
+    const int m = 32 * wave + n;
+    row_local = m % tile_rows;
+    hl = m / tile_rows;
+  }
+  const int mcol = hl * tile_rows + row_local;
+  const int head = g * group + hl;
   const bool valid = row_local < tile.n_rows;
   const int row = tile.row_begin + (valid ? row_local : 0);
   const int pos = valid ? rows[row] : -1;
@@ -82,8 +98,14 @@ __device__ __forceinline__ void attn_bf16_body(
       qop[s] = valid ? *reinterpret_cast<const bf16x8 *>(qp + 16 * s) : bf16x8{};
   }
   int pos_min = valid ? pos : 0x7fffffff;
+  int pos_max = pos;  // -1 for a padding column
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) pos_min = min(pos_min, __shfl_xor(pos_min, o));
+  for (int o = 1; o < 64; o <<= 1) {
+    pos_min = min(pos_min, __shfl_xor(pos_min, o));
+    pos_max = max(pos_max, __shfl_xor(pos_max, o));
+  }
+  pos_min = __builtin_amdgcn_readfirstlane(pos_min);
+  pos_max = __builtin_amdgcn_readfirstlane(pos_max);
 
   f32x16 acc[kDB];
 #pragma unroll
@@ -288,7 +310,9 @@ __device__ __forceinline__ void attn_bf16_body(
     if (ib + 1 < n_blocks) issue(vh, voff_v, kb0 + kKB, 3 + (VC ^ 1));
     const bool k3 = ib + 3 < n_blocks;
     if (k3) issue(kh, voff_k, kb0 + 3 * kKB, KC);
-    softmax_pv(s_cur, kb0, VC * kTileB, lds + ((KC + 1) % 3) * kTileB, s_nxt);
+    // a block past this wave's last row (and every later one) is masked for all its
+    // columns: the wave only stages its share of the loads
+    if (kb0 <= pos_max) softmax_pv(s_cur, kb0, VC * kTileB, lds + ((KC + 1) % 3) * kTileB, s_nxt);
     if (ib + 1 < n_blocks) {
       if (k3)
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRounds) : "memory");
@@ -325,7 +349,7 @@ __device__ __forceinline__ void attn_bf16_body(
         *reinterpret_cast<bf16x4 *>(op + 32 * d + 8 * a) = o;
       }
   } else {
-    __bf16 *wo = reinterpret_cast<__bf16 *>(ws_o) + ((int64_t)it.slot * kM + m) * D + 4 * grp;
+    __bf16 *wo = reinterpret_cast<__bf16 *>(ws_o) + ((int64_t)it.slot * kM + mcol) * D + 4 * grp;
 #pragma unroll
     for (int d = 0; d < kDB; ++d)
 #pragma unroll
@@ -336,8 +360,8 @@ __device__ __forceinline__ void attn_bf16_body(
         *reinterpret_cast<bf16x4 *>(wo + 32 * d + 8 * a) = o;
       }
     if (grp == 0) {
-      ws_ml[((int64_t)it.slot * kM + m) * 2 + 0] = m_run;
-      ws_ml[((int64_t)it.slot * kM + m) * 2 + 1] = l_row;
+      ws_ml[((int64_t)it.slot * kM + mcol) * 2 + 0] = m_run;
+      ws_ml[((int64_t)it.slot * kM + mcol) * 2 + 1] = l_row;
     }
   }
 }
