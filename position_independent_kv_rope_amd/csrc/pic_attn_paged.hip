@@ -90,17 +90,37 @@ __device__ __forceinline__ void attn_bf16_paged_body(
   const int q16 = lane >> 4;
   const int i16 = lane & 15;
 
-  const int m = 32 * wave + n;
-  const int row_local = m % tile_rows;
-  const int head = g * group + m / tile_rows;
+  // Query columns as in the contiguous kernel: with G <= 32, wave w owns a quarter of
+  // the tile's rows with all G heads; mcol is the head-major column index the merge reads.
+  int row_local, hl;
+  if (group <= 32) {
+    const int lg = __builtin_ctz(group);
+    row_local = (wave << (5 - lg)) + (n >> lg);
+    hl = n & (group - 1);
+  } else {
+    const int m = 32 * wave + n;
+    row_local = m % tile_rows;
+    hl = m / tile_rows;
+  }
+  const int mcol = hl * tile_rows + row_local;
+  const int head = g * group + hl;
   const bool valid = row_local < tile.n_rows;
   const int row = tile.row_begin + (valid ? row_local : 0);
   const int pos = valid ? rows[row] : -1;
   const int fresh_base = tile.pad0, n_fresh = tile.pad1;
 
+  // the wave's first position, and its last position and row (-1: no valid column)
   int pos_min = valid ? pos : 0x7fffffff;
+  int pos_max = pos, row_max = valid ? row : -1;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) pos_min = min(pos_min, __shfl_xor(pos_min, o));
+  for (int o = 1; o < 64; o <<= 1) {
+    pos_min = min(pos_min, __shfl_xor(pos_min, o));
+    pos_max = max(pos_max, __shfl_xor(pos_max, o));
+    row_max = max(row_max, __shfl_xor(row_max, o));
+  }
+  pos_min = __builtin_amdgcn_readfirstlane(pos_min);
+  pos_max = __builtin_amdgcn_readfirstlane(pos_max);
+  row_max = __builtin_amdgcn_readfirstlane(row_max);
 
   // ---- query operand in the frame of the block being scored ----
   bf16x8 qop[kKS];
@@ -382,15 +402,25 @@ __device__ __forceinline__ void attn_bf16_paged_body(
 
   // Block ib: S^T(ib) is in registers; stage K(ib+2) and V(ib+1), compute S^T(ib+1) in
   // block ib+1's frame, then the softmax and PV of block ib.
+  // A block no key of which any column of this wave sees: fresh rows after the wave's
+  // last row, or a pool block starting past its last position.  Step ib is skipped
+  // (the wave only stages its share of the loads) when block ib and block ib+1 are both
+  // unseen; a block that is unseen while the next one is not still runs, on stale
+  // scores, and its mask then covers every key (fresh keys after every row of the wave,
+  // pool keys past pos_min), so it contributes nothing.
+  auto unseen = [&](const KeyBlockRec &d) {
+    return d.frame < 0 ? fresh_base + d.row > row_max : d.base_pos > pos_max;
+  };
   auto step = [&](int ib, auto bufc, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2],
                   const KeyBlockRec &dc, const KeyBlockRec &dn, const KeyBlockRec &dnn) {
     constexpr int kB = decltype(bufc)::value;
+    const bool skip = unseen(dc) && (ib + 1 >= n_blocks || unseen(dn));
     if (ib + 2 < n_blocks) issue(dnn, false, kB);
     if (ib + 1 < n_blocks) {
       issue(dn, true, 2 + (kB ^ 1));
-      set_frame(dn.frame);
+      if (!skip) set_frame(dn.frame);
     }
-    softmax_pv(s_cur, dc, kB, lds + (kB ^ 1) * kTileB, s_nxt);
+    if (!skip) softmax_pv(s_cur, dc, kB, lds + (kB ^ 1) * kTileB, s_nxt);
     if (ib + 1 < n_blocks) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       finish_v(dn, kB ^ 1);
@@ -429,7 +459,7 @@ __device__ __forceinline__ void attn_bf16_paged_body(
         *reinterpret_cast<bf16x4 *>(op + 32 * d + 8 * a) = o;
       }
   } else {
-    __bf16 *wo = reinterpret_cast<__bf16 *>(ws_o) + ((int64_t)it.slot * kM + m) * D + 4 * grp;
+    __bf16 *wo = reinterpret_cast<__bf16 *>(ws_o) + ((int64_t)it.slot * kM + mcol) * D + 4 * grp;
 #pragma unroll
     for (int d = 0; d < kDB; ++d)
 #pragma unroll
@@ -440,8 +470,8 @@ __device__ __forceinline__ void attn_bf16_paged_body(
         *reinterpret_cast<bf16x4 *>(wo + 32 * d + 8 * a) = o;
       }
     if (grp == 0) {
-      ws_ml[((int64_t)it.slot * kM + m) * 2 + 0] = m_run;
-      ws_ml[((int64_t)it.slot * kM + m) * 2 + 1] = l_row;
+      ws_ml[((int64_t)it.slot * kM + mcol) * 2 + 0] = m_run;
+      ws_ml[((int64_t)it.slot * kM + mcol) * 2 + 1] = l_row;
     }
   }
 }
