@@ -117,20 +117,33 @@ __device__ __forceinline__ void dec_attn_body(
       nv[r] = (lane / kCPR) * tok_bytes + g * kRowB + 16 * (pch ^ swz_v<kCPR>(R));
     }
   };
+  // Pool block ids of block j of sr (pieces start on a block boundary, so pool block p
+  // of the block holds rows [t_begin + j * kDecKB + 16 p, ... + 16)); -1 for rows past the
+  // piece's keys or past the chunk's table row (never the next row's ids).  They are
+  // read one block ahead of the loads that use them, so the scalar-load round trip
+  // does not hold back the issue of a block.
+  constexpr int kPB = kDecKB / kPoolBlockRows;
+  auto fetch_ids = [&](const DecSrc &sr, int j, int (&id)[kPB]) {
+#pragma unroll
+    for (int p = 0; p < kPB; ++p) {
+      const int t = sr.t_begin + j * kDecKB + kPoolBlockRows * p;
+      id[p] = sr.pool && t < sr.t_end && t / kPoolBlockRows < sr.n_tab ? sr.blocks[t / kPoolBlockRows] : -1;
+    }
+  };
   // Stage block j of sr (K and V) into LDS buffer buf.  Each direct load gets a
   // resource that starts at its first row and ends after the rows that are keys of the
   // unit, so the range check alone zeroes rows past t_end (slack rows of a chunk's last
   // pool block included); the scalar offset stays 0.
   auto issue = [&](const DecSrc &sr, int j, int buf, const int (&ok)[kRounds],
-                   const int (&ov)[kRounds]) {
+                   const int (&ov)[kRounds], const int (&id)[kPB]) {
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
       const int t = sr.t_begin + j * kDecKB + kRPI * (kDecWaves * r + wave);  // first row
-      int rows = min(max(sr.t_end - t, 0), kRPI);
+      // (wave-uniform; kept in a scalar register so the resource is uniform too)
+      int rows = __builtin_amdgcn_readfirstlane(min(max(sr.t_end - t, 0), kRPI));
       int64_t off = 0;
       if (sr.pool) {  // a block id outside the pool reads zeros
-        // blocks past the chunk's table row read zeros (never the next row's ids)
-        const int bid = rows > 0 && t / kPoolBlockRows < sr.n_tab ? sr.blocks[t / kPoolBlockRows] : -1;
+        const int bid = rows > 0 ? id[(kRPI * (kDecWaves * r + wave)) / kPoolBlockRows] : -1;
         if (bid < 0 || bid >= pool_blocks)
           rows = 0;
         else
@@ -170,7 +183,9 @@ __device__ __forceinline__ void dec_attn_body(
   DecSrc cur = load_src(u_begin);
   DecSrc nxt = cur;  // unit of the next block to stage
   int n_ui = u_begin, n_j = 0;
+  int nid[kPB];  // its pool block ids
   set_head(cur.g);
+  fetch_ids(nxt, 0, nid);
   auto advance = [&]() {  // step (n_ui, n_j) to the next block to stage
     if (++n_j == nxt.n_blocks) {
       n_j = 0;
@@ -179,6 +194,7 @@ __device__ __forceinline__ void dec_attn_body(
         set_head(nxt.g);
       }
     }
+    if (n_ui < u_end) fetch_ids(nxt, n_j, nid);
   };
   // Blocks are numbered in streaming order; block x lives in buffer x % kDecStages.
   // `ahead` counts the staged blocks not yet consumed (the current one included).
@@ -186,7 +202,7 @@ __device__ __forceinline__ void dec_attn_body(
 #pragma unroll
   for (int i = 0; i < kDecStages - 1; ++i)
     if (n_ui < u_end) {
-      issue(nxt, n_j, stage_buf, nk, nv);
+      issue(nxt, n_j, stage_buf, nk, nv, nid);
       advance();
       ++ahead;
       stage_buf = stage_buf + 1 == kDecStages ? 0 : stage_buf + 1;
@@ -253,7 +269,7 @@ __device__ __forceinline__ void dec_attn_body(
 
     for (int j = 0; j < cur.n_blocks; ++j) {
       if (n_ui < u_end) {  // stage one more block while this one is scored
-        issue(nxt, n_j, stage_buf, nk, nv);
+        issue(nxt, n_j, stage_buf, nk, nv, nid);
         advance();
         ++ahead;
         stage_buf = stage_buf + 1 == kDecStages ? 0 : stage_buf + 1;
