@@ -176,6 +176,13 @@ def test_paged_gqa4_d64():
     run_paged(small_pool(4, h_q=32, h_kv=8, d=64, seed=47))
 
 
+@pytest.mark.parametrize("h_q", [32, 64])
+def test_paged_wide_groups(h_q):
+    # one KV head: G = 32 (a wave owns one row of the tile with all its heads) and G = 64
+    # (32 consecutive head-major columns per wave)
+    run_paged(small_pool(3, h_q=h_q, h_kv=1, d=64, seed=61 + h_q))
+
+
 def test_paged_shared_pool_full_size_sampled():
     # the shared-pool workload (256 pooled chunks, 8 requests x ~116k tokens, w = 8) in
     # the launch configuration bench.py times (n_cu = 256), sampled rows

@@ -222,6 +222,12 @@ EDGE_CASES = [
     ("f32_d64", "f32", 16, 4, 64, 5e5, 5, [([300, 129], 33)]),
     ("f32_d128", "f32", 32, 8, 128, 5e5, 16, [([200, 180], 20)]),
     ("only_query_rows", "f32", 4, 4, 16, 1e4, 2, [([], 6), ([0], 3)]),
+    # wide GQA groups: a wave owns 32/G rows with all G heads (G = 16, 32), or, past 32
+    # heads per KV head, 32 consecutive head-major columns of the tile (G = 64, 128)
+    ("gqa16_bf16", "bf16", 32, 2, 128, 5e5, 3, [([300, 257, 90], 21), ([130], 4)]),
+    ("gqa32_bf16_d64", "bf16", 32, 1, 64, 1e4, 5, [([200, 333], 17)]),
+    ("gqa64_bf16_d64", "bf16", 64, 1, 64, 1e4, 2, [([150, 180, 70], 9)]),
+    ("gqa128_bf16_d64", "bf16", 128, 1, 64, 1e4, 2, [([90, 140], 5)]),
 ]
 
 
