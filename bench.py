@@ -765,6 +765,24 @@ def bench_link(args, wl):
          for j, n in enumerate(names)}
     attn_tflops = attn_flops / (t["selective_attn"] * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[wl.dtype]
+
+    # the vendor library (torch -> hipBLASLt) on the same two GEMM shapes, plain (no RoPE
+    # epilogue, no residual): a same-shape reference for the projection kernels
+    import torch.nn.functional as F
+
+    def lib_ms(a, w):
+        for _ in range(2):
+            F.linear(a, w)
+        le = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(10)]
+        for e in le:
+            e[0].record()
+            F.linear(a, w)
+            e[1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in le]))
+
+    lib_qkv = lib_ms(x, wq[0])
+    lib_out = lib_ms(o.reshape(plan.n_rows, hq * D), wo[0])
     rec = {
         "metric": METRIC,
         "value": round(plan.n_tokens / (ms_step * 1e-3), 1),
@@ -793,12 +811,19 @@ def bench_link(args, wl):
                      "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_bytes},
         "kernels": {
             "qkv_rope": {"ms": round(t["qkv_rope"], 4), "flops": qkv_flops,
-                         "TFLOP_s": round(qkv_flops / (t["qkv_rope"] * 1e-3) / 1e12, 2)},
+                         "TFLOP_s": round(qkv_flops / (t["qkv_rope"] * 1e-3) / 1e12, 2),
+                         "library_same_shape_TFLOP_s": round(qkv_flops / (lib_qkv * 1e-3) / 1e12, 2),
+                         "frac_of_library": round(lib_qkv / t["qkv_rope"], 3)},
             "rope_splice": {"ms": round(t["rope_splice"], 4)},
             "selective_attn": {"ms": round(t["selective_attn"], 4), "flops": attn_flops,
                                "TFLOP_s": round(attn_tflops, 2)},
             "out_proj": {"ms": round(t["out_proj"], 4), "flops": out_flops,
-                         "TFLOP_s": round(out_flops / (t["out_proj"] * 1e-3) / 1e12, 2)},
+                         "TFLOP_s": round(out_flops / (t["out_proj"] * 1e-3) / 1e12, 2),
+                         "library_same_shape_TFLOP_s": round(out_flops / (lib_out * 1e-3) / 1e12, 2),
+                         "frac_of_library": round(lib_out / t["out_proj"], 3)},
+            "library_reference": "torch.nn.functional.linear (hipBLASLt) on the same [rows x "
+                                 "d_in] x [d_out x d_in]^T shapes, bf16, 10 launches, HIP "
+                                 "events; plain GEMM without the RoPE epilogue or residual",
             "per_layer_ms": round(sum(t.values()), 4),
             "host_plan_ms": round(1e3 * float(np.mean(plan_s)), 4),
         },
