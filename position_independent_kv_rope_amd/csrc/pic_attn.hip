@@ -21,15 +21,15 @@
 // consecutive keys its PV operand slots need.  The running max is kept in the exp2
 // domain (scores scaled by scale * log2 e).
 //
-// bf16 kernel (the hot one): 4 waves x 32 queries, v_mfma_f32_32x32x16_bf16 for both
-// products, K/V blocks of 64 keys in LDS (three K buffers, two V buffers: 80 KB, two
-// workgroups per CU) staged by direct buffer->LDS loads (the buffer range clamps rows
-// past the item's keys to zero), K three blocks ahead and V one, so that S^T of block
-// i+1 is computed while block i's softmax runs (software pipelining inside each wave)
-// and the wait at the end of a block leaves the newest K loads in flight, V read
-// transposed for
-// the PV operand with ds_read_b64_tr_b16, row sums taken from the bf16 probabilities
-// with v_dot2_f32_bf16.
+// bf16 kernel (the hot one): 4 waves x 32 queries (a wave owns a quarter of the tile's
+// rows with all their heads, and skips key blocks past its last row),
+// v_mfma_f32_32x32x16_bf16 for both products, K/V blocks of 64 keys in LDS (three K
+// buffers, two V buffers: 80 KB, two workgroups per CU) staged by direct buffer->LDS
+// loads (the buffer range clamps rows past the item's keys to zero), K three blocks
+// ahead and V one, so that S^T of block i+1 is computed while block i's softmax runs
+// (software pipelining inside each wave) and the wait at the end of a block leaves the
+// newest K loads in flight, V read transposed for the PV operand with
+// ds_read_b64_tr_b16, row sums taken from the bf16 probabilities with v_dot2_f32_bf16.
 // fp32 kernel: 8 waves x 16 queries, v_mfma_f32_16x16x4_f32 (fp32 operands, so fp32
 // I/O keeps fp32 accuracy), V staged transposed.
 #include "pic_attn_common.h"
