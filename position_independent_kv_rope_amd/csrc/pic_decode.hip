@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void dec_attn_kernel(
 // One workgroup per (request, query head): groups of D/4 lanes fold disjoint subsets
 // of the records of (request, kv head) (online log-sum-exp, 4 dims per lane, two
 // records' loads in flight per group), group 0 also the new token (score q . k_new,
-// weight v_new); the group results are combined in LDS.
+// weight v_new); the group results are combined pairwise in LDS.
 constexpr int kDecMergeThreads = 1024;
 
 template <int D>
@@ -470,12 +470,22 @@ __global__ __launch_bounds__(kDecMergeThreads) void dec_merge_kernel(
       fold(ml[u].x, ml[u].y, o);
     }
   }
+  // the group results combine pairwise in LDS, log2(groups) levels
   part_m[gi][c4] = mmax;
   part_l[gi][c4] = den;
   part_o[gi][c4] = num;
   __syncthreads();
+#pragma unroll
+  for (int half = kDecMergeGroups / 2; half >= 1; half >>= 1) {
+    if (gi < half) {
+      fold(part_m[gi + half][c4], part_l[gi + half][c4], part_o[gi + half][c4]);
+      part_m[gi][c4] = mmax;
+      part_l[gi][c4] = den;
+      part_o[gi][c4] = num;
+    }
+    __syncthreads();
+  }
   if (gi != 0) return;
-  for (int o = 1; o < kDecMergeGroups; ++o) fold(part_m[o][c4], part_l[o][c4], part_o[o][c4]);
   const float inv = 1.f / den;
   bf16x4 res;
 #pragma unroll
