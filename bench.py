@@ -100,13 +100,40 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
 
 
+def calib_lib():
+    """libpic_calib.so (include/pic_calib.h): streaming read/copy and MFMA-loop kernels."""
+    import ctypes
+    path = os.path.join(ROOT, "position_independent_kv_rope_amd", "libpic_calib.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libpic_calib.so not found at %s; build it with "
+                           "`python -m position_independent_kv_rope_amd.build`" % path)
+    L = ctypes.CDLL(path)
+    i32, i64, p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    L.pic_calib_read_sink_words.argtypes = [i64]
+    L.pic_calib_read_sink_words.restype = i64
+    L.pic_calib_read.argtypes = [p, i64, p, p]
+    L.pic_calib_read.restype = ctypes.c_int
+    L.pic_calib_copy.argtypes = [p, p, i64, p]
+    L.pic_calib_copy.restype = ctypes.c_int
+    L.pic_calib_update.argtypes = [p, i64, p]
+    L.pic_calib_update.restype = ctypes.c_int
+    L.pic_calib_mfma_flops.argtypes = [i32, i32]
+    L.pic_calib_mfma_flops.restype = i64
+    L.pic_calib_mfma.argtypes = [p, p, i32, i32, p]
+    L.pic_calib_mfma.restype = ctypes.c_int
+    return L
+
+
 def measured_peaks():
-    """Rates this GPU reaches with plain library calls, measured live (context for the
-    spec-peak fractions, never the denominator of `frac`): a 1 GiB device-to-device copy
-    (read + write bytes), a sum over 2 GiB (read bytes) and an 8192^3 bf16 GEMM of
-    random operands (vendor BLAS)."""
+    """Rates this GPU reaches, measured live (context for the spec-peak fractions, never
+    the denominator of `frac`): a plain streaming read of 2 GiB and a plain 1 GiB copy
+    (read + write bytes) with the calibration kernels, an MFMA loop on random bf16
+    operands (v_mfma_f32_32x32x16_bf16, two waves per SIMD), and an 8192^3 bf16 GEMM of
+    random operands through the vendor BLAS."""
     import torch
     dev = "cuda"
+    C = calib_lib()
+    stream = lambda: ctypes_stream(torch)
 
     def timed(fn, reps):
         fn()
@@ -119,32 +146,72 @@ def measured_peaks():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3 / reps
 
+    def ok(st, name):
+        if st != 0:
+            raise RuntimeError("%s failed: %d" % (name, st))
+
     n = 1 << 30
     src = torch.ones(n // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    t_copy = timed(lambda: dst.copy_(src), 10)
-    del dst
+    t_copy = timed(lambda: ok(C.pic_calib_copy(src.data_ptr(), dst.data_ptr(), n, stream()),
+                              "pic_calib_copy"), 10)
+    t_update = timed(lambda: ok(C.pic_calib_update(src.data_ptr(), n, stream()),
+                                "pic_calib_update"), 10)
+    del dst, src
     big = torch.ones(n // 2, dtype=torch.float32, device=dev)
-    t_read = timed(lambda: big.sum(), 10)
-    del big, src
+    sink = torch.empty(int(C.pic_calib_read_sink_words(2 * n)), dtype=torch.int32, device=dev)
+    t_read = timed(lambda: ok(C.pic_calib_read(big.data_ptr(), 2 * n, sink.data_ptr(), stream()),
+                              "pic_calib_read"), 10)
+    del big, sink
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    n_wg, iters = 2 * n_cu, 4096
+    g = torch.Generator(device="cpu").manual_seed(7)
+    ops = torch.randn(8 * 64 * 8, generator=g).to(torch.bfloat16).to(dev)
+    fsink = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    t_mfma = timed(lambda: ok(C.pic_calib_mfma(ops.data_ptr(), fsink.data_ptr(), n_wg, iters,
+                                               stream()), "pic_calib_mfma"), 10)
+    mfma_flops = float(C.pic_calib_mfma_flops(n_wg, iters))
+    del ops, fsink
     m = 8192
     a = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
     b = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
     t_gemm = timed(lambda: torch.matmul(a, b), 10)
     del a, b
     torch.cuda.empty_cache()
-    return {"copy_GB_s": round(2 * n / t_copy / 1e9, 1),
-            "read_GB_s": round(2 * n / t_read / 1e9, 1),
+    return {"read_GB_s": round(2 * n / t_read / 1e9, 1),
+            "copy_GB_s": round(2 * n / t_copy / 1e9, 1),
+            "update_GB_s": round(2 * n / t_update / 1e9, 1),
+            "mfma_loop_bf16_TFLOP_s": round(mfma_flops / t_mfma / 1e12, 1),
             "gemm_bf16_TFLOP_s": round(2.0 * m ** 3 / t_gemm / 1e12, 1),
-            "how": "torch copy_ of 1 GiB (read + write), torch sum over 2 GiB, torch.matmul "
-                   "8192^3 bf16 with random operands; 10 launches each, HIP events"}
+            "how": "libpic_calib.so: streaming read of 2 GiB, copy of 1 GiB and in-place "
+                   "update of 1 GiB (read + write bytes), MFMA loop (%d workgroups x 4 waves x %d rounds of 4 "
+                   "v_mfma_f32_32x32x16_bf16 on random operands); vendor BLAS: "
+                   "torch.matmul 8192^3 bf16 with random operands; 10 launches each, HIP "
+                   "events" % (n_wg, iters)}
+
+
+def ctypes_stream(torch):
+    return torch.cuda.current_stream().cuda_stream
 
 
 def with_measured(rec, peaks):
-    """Add the fraction of the measured GEMM rate next to the spec fraction."""
-    if peaks and rec.get("roofline", {}).get("unit") == "TFLOP/s" and rec.get("dtype") == "bf16":
-        rec["roofline"]["frac_of_measured_gemm"] = round(
-            rec["roofline"]["achieved"] / peaks["gemm_bf16_TFLOP_s"], 4)
+    """Add fractions of the measured rates next to the spec fractions: MFMA-bound records
+    against the MFMA loop and the vendor GEMM, HBM-bound ones against the streaming read
+    (a read-dominated call) and every HBM-bound kernel entry against the in-place update
+    (the rotation reads and writes its rows in place; the splice and the pool gather
+    write rows they did not read, for which the copy rate is given as well)."""
+    if not peaks:
+        return rec
+    roof = rec.get("roofline", {})
+    if roof.get("unit") == "TFLOP/s" and rec.get("dtype", "bf16") == "bf16":
+        roof["frac_of_measured_mfma"] = round(roof["achieved"] / peaks["mfma_loop_bf16_TFLOP_s"], 4)
+        roof["frac_of_measured_gemm"] = round(roof["achieved"] / peaks["gemm_bf16_TFLOP_s"], 4)
+    elif roof.get("unit") == "GB/s":
+        roof["frac_of_measured_read"] = round(roof["achieved"] / peaks["read_GB_s"], 4)
+    for kr in rec.get("kernels", {}).values():
+        if isinstance(kr, dict) and "GB_s" in kr and "hbm_frac" in kr:
+            kr["frac_of_measured_update"] = round(kr["GB_s"] / peaks["update_GB_s"], 4)
+            kr["frac_of_measured_copy"] = round(kr["GB_s"] / peaks["copy_GB_s"], 4)
     return rec
 
 
@@ -320,8 +387,11 @@ def cpu_baseline_paged(wl, pk, pv, cbp, blocks, q, kf, vf, plan, sample_rows):
 
 def bench_paged(args, wl):
     run = run_pool_gathered if args.gather else run_paged
-    print(json.dumps(run(wl, args.steps, args.warmup,
-                         None if args.no_cpu_baseline else args.cpu_sample_rows)), flush=True)
+    peaks = measured_peaks()
+    rec = with_measured(run(wl, args.steps, args.warmup,
+                            None if args.no_cpu_baseline else args.cpu_sample_rows), peaks)
+    rec["measured_peaks"] = peaks
+    print(json.dumps(rec), flush=True)
 
 
 def run_pool_gathered(wl, steps, warmup, cpu_sample_rows):
@@ -668,6 +738,9 @@ def bench_decode(args, wl):
                                          % n0, "host_cpus": os.cpu_count()}
     else:
         rec["cpu_baseline"] = None
+    peaks = measured_peaks()
+    rec = with_measured(rec, peaks)
+    rec["measured_peaks"] = peaks
     print(json.dumps(rec), flush=True)
 
 
@@ -854,6 +927,9 @@ def bench_link(args, wl):
                                "host_cpus": os.cpu_count()}
     else:
         rec["cpu_baseline"] = None
+    peaks = measured_peaks()
+    rec = with_measured(rec, peaks)
+    rec["measured_peaks"] = peaks
     print(json.dumps(rec), flush=True)
 
 

@@ -13,6 +13,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpic.so")
+# calibration kernels for the measured peaks bench.py reports (include/pic_calib.h)
+CALIB_LIB = os.path.join(PKG, "libpic_calib.so")
+CALIB_SOURCES = ["pic_calib.hip"]
 
 SOURCES = ["pic_plan.cpp", "pic_rope_splice.hip", "pic_attn.hip", "pic_attn_paged.hip",
            "pic_decode.hip", "pic_link.hip", "pic_state.hip"]
@@ -30,10 +33,9 @@ def hipcc():
     raise RuntimeError("hipcc not found; ROCm is required to build libpic.so")
 
 
-def build(verbose=False):
-    """Compile every source into libpic.so (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+def _link(sources, lib, verbose):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = lib + ".tmp"
     cmd = [hipcc()] + FLAGS + ["-I", INCLUDE, "-I", CSRC, "-o", tmp] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -43,7 +45,14 @@ def build(verbose=False):
         raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, "\n".join(errs)))
     if verbose and errs:
         print("\n".join(errs), file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    """Compile every source into libpic.so, and the calibration kernels into
+    libpic_calib.so (always recompiles)."""
+    _link(SOURCES, LIB, verbose)
+    _link(CALIB_SOURCES, CALIB_LIB, verbose)
     return LIB
 
 

@@ -27,8 +27,8 @@ def _built():
         build.build()
 
 
-def _declared_symbols():
-    with open(os.path.join(ROOT, "include", "pic.h")) as f:
+def _declared_symbols(header="pic.h"):
+    with open(os.path.join(ROOT, "include", header)) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(pic_[a-z_]+)\s*\(", text)))
@@ -65,6 +65,40 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(P.LIB_PATH)
     for s in syms:
         assert hasattr(lib, s), s
+
+
+def test_calibration_library_exports_and_host_checks():
+    # libpic_calib.so (the bench's measured peaks) exports what pic_calib.h declares; its
+    # argument checks and flop count run on the host (no launch for an invalid argument)
+    from position_independent_kv_rope_amd import build
+    if not os.path.exists(build.CALIB_LIB):
+        build.build()
+    syms = _declared_symbols("pic_calib.h")
+    assert syms == sorted(["pic_calib_copy", "pic_calib_mfma", "pic_calib_mfma_flops",
+                           "pic_calib_read", "pic_calib_read_sink_words", "pic_calib_update"])
+    lib = ctypes.CDLL(build.CALIB_LIB)
+    for s in syms:
+        assert hasattr(lib, s), s
+    i32, i64, p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.pic_calib_mfma_flops.argtypes = [i32, i32]
+    lib.pic_calib_mfma_flops.restype = i64
+    assert lib.pic_calib_mfma_flops(512, 4096) == 512 * 4 * 4096 * 4 * 2 * 32 * 32 * 16
+    lib.pic_calib_read_sink_words.argtypes = [i64]
+    lib.pic_calib_read_sink_words.restype = i64
+    assert lib.pic_calib_read_sink_words(8) == 0
+    assert lib.pic_calib_read_sink_words(16) == 4            # one workgroup, four waves
+    assert lib.pic_calib_read_sink_words(1 << 31) == 4096 * 4  # grid capped at 4096
+    lib.pic_calib_read.argtypes = [p, i64, p, p]
+    lib.pic_calib_copy.argtypes = [p, p, i64, p]
+    lib.pic_calib_mfma.argtypes = [p, p, i32, i32, p]
+    assert lib.pic_calib_read(None, 16, None, None) == -1
+    assert lib.pic_calib_read(p(16), 24, p(16), None) == -1    # not a multiple of 16
+    assert lib.pic_calib_copy(p(16), None, 16, None) == -1
+    lib.pic_calib_update.argtypes = [p, i64, p]
+    assert lib.pic_calib_update(None, 16, None) == -1
+    assert lib.pic_calib_update(p(16), 0, None) == -1
+    assert lib.pic_calib_mfma(p(16), p(16), 4, 6, None) == -1  # rounds not a multiple of 4
+    assert lib.pic_calib_mfma(p(16), p(16), 0, 4, None) == -1
 
 
 def test_strerror_and_status_codes():
