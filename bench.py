@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="recomputed rows per request whose attention the oracle times "
                          "(0 = all; the time is scaled to all rows by causal-pair count)")
+    ap.add_argument("--peaks-only", action="store_true",
+                    help="run only the measured peaks (calibration streams, MFMA loop, "
+                         "vendor GEMM) and print them as one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (5 launches) to calibrate "
                          "rocprofv3 FETCH_SIZE/WRITE_SIZE against known bytes")
@@ -1222,6 +1225,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     P.lib()
+    if args.peaks_only:
+        print(json.dumps({"measured_peaks": measured_peaks()}), flush=True)
+        return
     wl = make_workload(args.workload, args.k)
     if wl.pool_lens is not None:
         if args.state_compose:

@@ -37,7 +37,9 @@ SHORT = [("pool_rope_splice_kernel", "rope_splice_pool"), ("rope_splice_kernel",
          ("dec_attn_kernel", "dec_attn"), ("dec_merge_kernel", "dec_merge"),
          ("attn_bf16_kernel", "attn_bf16"), ("attn_f32_kernel", "attn_f32"),
          ("merge_kernel", "merge"), ("rope_delta_kernel", "rope_delta"),
-         ("splice_kernel", "splice"), ("copyBuffer", "copy (calibration)")]
+         ("splice_kernel", "splice"), ("copyBuffer", "copy (calibration)"),
+         ("calib_mfma_kernel", "calib_mfma"), ("calib_read_kernel", "calib_read"),
+         ("calib_copy_kernel", "calib_copy"), ("calib_update_kernel", "calib_update")]
 
 
 def short_name(name):
@@ -192,7 +194,7 @@ def report(args):
         out.append("- MFMA busy: %.1f%% of busy cycles (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs "
                    "over SQ_BUSY_CYCLES / 32)" % (100 * dv["mfma_busy"]))
     if "valu_per_mfma" in dv:
-        out.append("- VALU instructions per MFMA: %.2f%s" % (
+        out.append("- VALU instructions per MFMA (SQ_INSTS_VALU counts the MFMAs too): %.2f%s" % (
             dv["valu_per_mfma"], "; LDS instructions per MFMA: %.2f" % dv["lds_per_mfma"]
             if "lds_per_mfma" in dv else ""))
     if "wave_cycles_in_waitcnt" in dv:
