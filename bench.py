@@ -129,10 +129,10 @@ def calib_lib():
 
 def measured_peaks():
     """Rates this GPU reaches, measured live (context for the spec-peak fractions, never
-    the denominator of `frac`): a plain streaming read of 2 GiB and a plain 1 GiB copy
-    (read + write bytes) with the calibration kernels, an MFMA loop on random bf16
-    operands (v_mfma_f32_32x32x16_bf16, two waves per SIMD), and an 8192^3 bf16 GEMM of
-    random operands through the vendor BLAS."""
+    the denominator of `frac`): with the calibration kernels a plain streaming read of
+    2 GiB, a 1 GiB copy and a 1 GiB in-place update (read + write bytes), and an MFMA
+    loop on random bf16 operands (v_mfma_f32_32x32x16_bf16, two waves per SIMD); and an
+    8192^3 bf16 GEMM of random operands through the vendor BLAS."""
     import torch
     dev = "cuda"
     C = calib_lib()
@@ -186,11 +186,11 @@ def measured_peaks():
             "update_GB_s": round(2 * n / t_update / 1e9, 1),
             "mfma_loop_bf16_TFLOP_s": round(mfma_flops / t_mfma / 1e12, 1),
             "gemm_bf16_TFLOP_s": round(2.0 * m ** 3 / t_gemm / 1e12, 1),
-            "how": "libpic_calib.so: streaming read of 2 GiB, copy of 1 GiB and in-place "
-                   "update of 1 GiB (read + write bytes), MFMA loop (%d workgroups x 4 waves x %d rounds of 4 "
-                   "v_mfma_f32_32x32x16_bf16 on random operands); vendor BLAS: "
-                   "torch.matmul 8192^3 bf16 with random operands; 10 launches each, HIP "
-                   "events" % (n_wg, iters)}
+            "how": ("libpic_calib.so: streaming read of 2 GiB, copy of 1 GiB and in-place "
+                    "update of 1 GiB (read + write bytes), MFMA loop (%d workgroups x 4 waves "
+                    "x %d rounds of 4 v_mfma_f32_32x32x16_bf16 on random operands); vendor "
+                    "BLAS: torch.matmul 8192^3 bf16 with random operands; 10 launches each, "
+                    "HIP events" % (n_wg, iters))}
 
 
 def ctypes_stream(torch):
@@ -206,7 +206,7 @@ def with_measured(rec, peaks):
     if not peaks:
         return rec
     roof = rec.get("roofline", {})
-    if roof.get("unit") == "TFLOP/s" and rec.get("dtype", "bf16") == "bf16":
+    if roof.get("unit") == "TFLOP/s" and rec.get("dtype") == "bf16":
         roof["frac_of_measured_mfma"] = round(roof["achieved"] / peaks["mfma_loop_bf16_TFLOP_s"], 4)
         roof["frac_of_measured_gemm"] = round(roof["achieved"] / peaks["gemm_bf16_TFLOP_s"], 4)
     elif roof.get("unit") == "GB/s":
